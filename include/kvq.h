@@ -1,0 +1,315 @@
+/*
+ * kvq.h -- C ABI of a quantized paged KV-cache library for AMD Instinct MI355X
+ * (gfx950, CDNA4).
+ *
+ * The library covers the decode-time hot path that the three source pages
+ * describe:
+ *
+ *   kvq_append            quantize freshly computed key/value vectors (fp16 or
+ *                         bf16) with scales computed at run time from each
+ *                         vector's own range, and scatter the codes into
+ *                         fixed-size cache blocks through a slot mapping.
+ *                         ("Dynamic KV Cache Quantization for Fast LLM
+ *                         Inference", sections "Understanding Dynamic
+ *                         Quantization Techniques for KV Caches" and
+ *                         "Integrating Dynamic Quantization with PagedAttention";
+ *                         "KV Cache Optimization" glossary, "Technical
+ *                         Architecture", stages 2 and 3.)
+ *   kvq_decode_attention  single-query GQA attention softmax(q.K^T*scale).V of
+ *                         every sequence of a batch over its cached blocks,
+ *                         dequantizing the codes in registers ("KV Cache
+ *                         Optimization" glossary, "Technical Architecture",
+ *                         stage 4 "fused dequantization attention kernel";
+ *                         "Dynamic KV Cache Quantization ...", section "Recap
+ *                         of KV Caching", the append-then-attend loop).
+ *   kvq_bytes_per_token   the cache-size closed form ("KV Cache Optimization"
+ *                         glossary, "Technical Architecture"; "KV Cache
+ *                         Optimization: Strategies for Faster LLM Inference",
+ *                         section "What Is KV Cache and Why Does It Balloon
+ *                         Memory Usage?").
+ *   kvq_pool_init / kvq_blocks_reserve / kvq_blocks_release
+ *                         a device-side pool of physical blocks that hands
+ *                         blocks to sequences on demand and maps logical to
+ *                         physical blocks ("KV Cache Optimization: Strategies
+ *                         ...", section "How vLLM Implements KV Cache
+ *                         Optimization").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Ownership: the caller owns every buffer. Pointers named "device" must be
+ *    device memory (hipMalloc or a torch CUDA tensor); all others are host
+ *    memory. The library never allocates or frees memory and keeps no state
+ *    between calls, so every call is re-entrant.
+ *  - Streams: `stream` is a hipStream_t passed as an opaque pointer (NULL is
+ *    the null stream). Calls only enqueue work on it and return; results are
+ *    visible to later work on the same stream.
+ *  - Errors: every argument check happens on the host before any launch; a
+ *    failing check returns a negative kvq_status and enqueues nothing.
+ *    Conditions only the device can see (pool exhaustion) are written to a
+ *    caller-provided device status word. Values that the host cannot check
+ *    (block ids, slots, lengths inside device arrays) are preconditions:
+ *    breaking one gives unspecified results. Decode ignores block ids outside
+ *    [0, num_blocks) instead of reading through them.
+ *  - Alignment: every device pointer must be 16-byte aligned and every row
+ *    stride must keep rows 16-byte aligned.
+ *  - Inputs must be finite.
+ *
+ * Cache layout (one kvq_cache = one transformer layer; block tables are shared
+ * by all layers). H = num_kv_heads, d = head_dim, bs = block_size,
+ * NB = num_blocks. A token stored in slot s lives in block s / bs at offset
+ * s % bs.
+ *  codes      [NB][H][bs][row_bytes], row_bytes = d (INT8, FP8_E4M3),
+ *             d / 2 (INT4) or 2 d (NONE16, the raw fp16/bf16 value).
+ *             INT8 codes are two's complement in [-127, 127]; FP8 codes are
+ *             OCP E4M3 (bias 7, max 448, 0x7F / 0xFF never written).
+ *             INT4 codes pack two elements per byte, with the 32-element
+ *             slice interleave described at KVQ_CODE_INT4.
+ *  TOKEN_SYM scale            float [NB][H][bs]
+ *  GROUP_ASYM scale / zero    float / uint8 [NB][H][bs][d / group_size]
+ *  CHANNEL_BLOCK_SYM scale    float [NB][H][d]            (keys only)
+ *  k_stage (CHANNEL_BLOCK_SYM keys only)  src dtype [max_seqs][H][bs][d]:
+ *             raw rows of each sequence's not yet complete last block.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+typedef int32_t kvq_status;
+#define KVQ_OK 0
+#define KVQ_ERR_INVALID_ARGUMENT (-1)    /* bad pointer, size, enum or shape     */
+#define KVQ_ERR_UNSUPPORTED (-2)         /* valid request this build lacks        */
+#define KVQ_ERR_WORKSPACE_TOO_SMALL (-3) /* decode workspace below required size */
+#define KVQ_ERR_HIP (-4)                 /* a HIP launch or runtime call failed   */
+#define KVQ_ERR_OUT_OF_BLOCKS (-5)       /* pool cannot serve a reservation       */
+
+/* ---- enumerations (stored as int32 in the structs below) ---------------- */
+/* Floating-point types of inputs and outputs. */
+#define KVQ_F16 0
+#define KVQ_BF16 1
+#define KVQ_F32 2
+
+/* Code types of the cache.
+ * KVQ_CODE_NONE16: unquantized; the row is stored as given (fp16 or bf16),
+ *   no scale. Lets the same decode run on a 16-bit cache.
+ * KVQ_CODE_INT8: signed integer codes q = clamp(rne(x / s), -127, 127) with
+ *   s = max|x| / 127 ("Dynamic KV Cache Quantization ...", section
+ *   "Understanding Dynamic Quantization Techniques", the absmax scale with
+ *   2^(bits-1) - 1 in the denominator).
+ * KVQ_CODE_FP8_E4M3: the OCP E4M3 byte nearest x / s, ties to even mantissa,
+ *   saturating at +-448, with s = max|x| / 448 (FP8 KV cache named on all
+ *   three pages; the pages give no scaling rule, so the absmax rule above is
+ *   used with the format's largest finite value).
+ * KVQ_CODE_INT4: 4-bit codes, symmetric q in [-7, 7] under TOKEN_SYM (the
+ *   same absmax rule with bits = 4) or unsigned q in [0, 15] with a zero point
+ *   under GROUP_ASYM. Nibble placement inside a row of d elements, with
+ *   n = d / 32: element e = 32 i + 2 r + t (i < n, r < 16, t < 2) sits in
+ *   byte n r + i, low nibble when t = 0 and high nibble when t = 1. Signed
+ *   codes are stored as q & 0xF. */
+#define KVQ_CODE_NONE16 0
+#define KVQ_CODE_INT8 1
+#define KVQ_CODE_FP8_E4M3 2
+#define KVQ_CODE_INT4 3
+
+/* Scale granularity ("Dynamic KV Cache Quantization ...", section
+ * "Understanding Dynamic Quantization Techniques": per token or per head;
+ * "KV Cache Optimization: Strategies ...", section "KV Cache Quantization:
+ * When and How to Compress": per channel keeps more information).
+ * KVQ_SCALE_TOKEN_SYM: one fp32 scale per (token, head), zero point 0. An
+ *   all-zero row gets codes 0 and scale 1.
+ * KVQ_SCALE_GROUP_ASYM: per group of group_size consecutive elements of a
+ *   (token, head) row: mn = min(0, min x), mx = max(0, max x),
+ *   s = (mx - mn) / 15, z = clamp(rne(-mn / s), 0, 15),
+ *   q = clamp(rne(x / s) + z, 0, 15); dequantized value (q - z) s. A group
+ *   with mx == mn gets codes 0, s = 1, z = 0. INT4 only.
+ * KVQ_SCALE_CHANNEL_BLOCK_SYM: keys only, INT8 only. One fp32 scale per
+ *   (block, head, channel) from the absmax of that channel over the block's
+ *   bs tokens. Rows of a block that is not yet full wait, raw, in k_stage and
+ *   are quantized together when an append writes the block's last slot. */
+#define KVQ_SCALE_TOKEN_SYM 0
+#define KVQ_SCALE_GROUP_ASYM 1
+#define KVQ_SCALE_CHANNEL_BLOCK_SYM 2
+
+/* ---- structs (host memory, passed by pointer) ----------------------------
+ * kvq_layout: the static description of one layer's cache.
+ *   num_kv_heads  H >= 1
+ *   head_dim      d in {64, 128}
+ *   block_size    bs in {16, 32}
+ *   group_size    32 for GROUP_ASYM, ignored (set 0) otherwise
+ *   k_code/v_code KVQ_CODE_*; k_mode/v_mode KVQ_SCALE_*
+ *   src_dtype     KVQ_F16 or KVQ_BF16: the type of rows given to kvq_append
+ *                 and of the NONE16 cache and the k_stage plane
+ *   reserved      must be 0 */
+typedef struct kvq_layout {
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t group_size;
+  int32_t k_code;
+  int32_t v_code;
+  int32_t k_mode;
+  int32_t v_mode;
+  int32_t src_dtype;
+  int32_t reserved;
+} kvq_layout;
+
+/* kvq_cache: device planes of one layer (see the layout comment at the top).
+ * Pointers a layout does not use must be NULL. */
+typedef struct kvq_cache {
+  void* k_codes;
+  void* v_codes;
+  float* k_scale;
+  float* v_scale;
+  uint8_t* k_zero;
+  uint8_t* v_zero;
+  void* k_stage;
+  int64_t num_blocks; /* NB, physical blocks in every plane */
+  int32_t max_seqs;   /* rows of k_stage (0 when k_stage is unused) */
+  int32_t reserved;   /* must be 0 */
+} kvq_cache;
+
+/* ---- entry points -------------------------------------------------------- */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* kvq_status_string(kvq_status status);
+
+/* Checks a layout without touching the device: KVQ_OK, or
+ * KVQ_ERR_INVALID_ARGUMENT for malformed fields, or KVQ_ERR_UNSUPPORTED for a
+ * well-formed combination this build does not implement. */
+kvq_status kvq_layout_check(const kvq_layout* layout);
+
+/* Cache bytes per token over num_layers layers ("KV Cache Optimization"
+ * glossary, "Technical Architecture": keys and values, times layers, KV heads,
+ * head dimension and bytes per element; for 80 layers, 8 KV heads and d = 128
+ * this is 327 680 B at 16 bit, 163 840 B at 8 bit and 81 920 B at 4 bit).
+ * include_metadata = 0 counts codes only: 2 * num_layers * H * d * bits / 8
+ * summed over K and V with their own code widths. include_metadata = 1 adds,
+ * per layer and side, H * 4 (TOKEN_SYM scale), H * (d / group_size) * 5
+ * (GROUP_ASYM scale and zero point) or ceil(H * d * 4 / bs) (CHANNEL_BLOCK
+ * scales amortized over a block). Returns the byte count, or a negative
+ * kvq_status for a bad layout or num_layers < 1. Host arithmetic only. */
+int64_t kvq_bytes_per_token(const kvq_layout* layout, int32_t num_layers,
+                            int32_t include_metadata);
+
+/* Size in bytes of every plane of one layer's cache, in the order k_codes,
+ * v_codes, k_scale, v_scale, k_zero, v_zero, k_stage (0 for planes the layout
+ * does not use). out_bytes is a host array of 7 int64. Host only. */
+kvq_status kvq_cache_plane_bytes(const kvq_layout* layout, int64_t num_blocks,
+                                 int32_t max_seqs, int64_t out_bytes[7]);
+
+/* Quantize num_tokens new K and V rows and write them to their slots.
+ *  k, v          device, src_dtype; token t, head h, element e at
+ *                k[t * k_row_stride + h * d + e] (strides in elements; the H*d
+ *                elements of one token are contiguous).
+ *  slot_mapping  device int64[num_tokens]; slot of token t, or -1 to skip it.
+ *  stage_rows    device int32[num_tokens] when either side is
+ *                CHANNEL_BLOCK_SYM, else NULL: the k_stage row (the decode
+ *                batch row) of token t's sequence.
+ * Scales are computed in fp32 with correctly rounded division and codes with
+ * round-half-to-even, so the stored bytes are a pure function of the input.
+ * Preconditions: slots are distinct and inside the cache; for
+ * CHANNEL_BLOCK_SYM keys, the tokens of one sequence appear in the call
+ * contiguously and in position order, and each sequence's blocks fill from
+ * offset 0 upward across calls. Returns KVQ_OK after enqueueing. */
+kvq_status kvq_append(const kvq_layout* layout, const kvq_cache* cache,
+                      const void* k, const void* v, int64_t k_row_stride,
+                      int64_t v_row_stride, int64_t num_tokens,
+                      const int64_t* slot_mapping, const int32_t* stage_rows,
+                      void* stream);
+
+/* Device workspace bytes kvq_decode_attention needs for these sizes and this
+ * split_blocks (0 = the library's own choice), or a negative kvq_status. */
+int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch,
+                                   int32_t num_q_heads, int32_t max_context_len,
+                                   int32_t split_blocks);
+
+/* Single-query decode attention over the paged cache.
+ *  q              device [batch][num_q_heads][d] in q_dtype (F16 or BF16).
+ *  block_tables   device int32 [batch][max_blocks_per_seq]: physical block of
+ *                 each logical block of each sequence.
+ *  context_lens   device int32 [batch]: cached tokens each sequence attends
+ *                 over, 0 <= len <= max_context_len <= max_blocks_per_seq*bs.
+ *  max_context_len host bound on context_lens, sizes the launch.
+ *  sm_scale       score scale; 0 means 1/sqrt(d).
+ *  split_blocks   blocks per split-K chunk; 0 lets the library choose.
+ *  out            device [batch][num_q_heads][d] in out_dtype (F32, F16 or
+ *                 BF16), RNE-rounded from fp32.
+ *  workspace      device, at least kvq_decode_workspace_bytes(...) bytes.
+ * Query head h reads KV head h / (num_q_heads / H). out = sum_t p_t v_t /
+ * sum_t p_t with p_t = exp(s_t - max s), s_t = (q . k_t) * sm_scale, over the
+ * first context_lens[b] tokens; a sequence with no tokens gets out = 0.
+ * Keys and values are dequantized as the scale mode defines; under
+ * CHANNEL_BLOCK_SYM the partial last block is read raw from k_stage row b.
+ * The result depends on physical block ids only through the data they hold.
+ * Preconditions: num_q_heads is a multiple of H and num_q_heads / H <= 16;
+ * dequantized values v satisfy |v| / 127 < 65504 (fp16 range of the folded
+ * value scale). */
+kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache,
+                                const void* q, int32_t q_dtype, int32_t batch,
+                                int32_t num_q_heads, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t* context_lens,
+                                int32_t max_context_len, float sm_scale,
+                                int32_t split_blocks, void* out,
+                                int32_t out_dtype, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+
+/* Fill a pool: free_stack[i] = initial_order[i] (or i when initial_order is
+ * NULL) for i < num_blocks, and *free_top = num_blocks. free_stack, free_top
+ * and initial_order are device memory; initial_order must be a permutation of
+ * [0, num_blocks). */
+kvq_status kvq_pool_init(int32_t* free_stack, int32_t* free_top,
+                         const int32_t* initial_order, int64_t num_blocks,
+                         void* stream);
+
+/* Give each sequence b the blocks it needs to grow from context_lens[b] to
+ * context_lens[b] + new_tokens[b] tokens ("KV Cache Optimization: Strategies
+ * ...", section "How vLLM Implements KV Cache Optimization": blocks are
+ * handed out on demand rather than reserved for the worst case).
+ *  need_b = ceil((L_b + n_b) / bs) - ceil(L_b / bs); off_b is the exclusive
+ *  prefix sum of need in batch order; with top = *free_top, sequence b takes
+ *  free_stack[top - off_b - need_b + k], k = 0..need_b-1, as logical blocks
+ *  ceil(L_b / bs) + k of block_tables[b]; *free_top drops by sum(need).
+ *  slot_mapping_out[o_b + k] (o_b = exclusive prefix sum of new_tokens) gets
+ *  the slot of position L_b + k, k < n_b. context_lens_out (may be NULL or
+ *  alias context_lens) gets L_b + n_b.
+ * All or nothing: if sum(need) > top, or a sequence would exceed
+ * max_blocks_per_seq blocks, nothing is written except *status_flag =
+ * KVQ_ERR_OUT_OF_BLOCKS; on success *status_flag = KVQ_OK. All pointers are
+ * device memory; pool_capacity is the length of free_stack. */
+kvq_status kvq_blocks_reserve(int32_t* free_stack, int32_t* free_top,
+                              int64_t pool_capacity, int32_t* block_tables,
+                              int32_t max_blocks_per_seq,
+                              const int32_t* context_lens,
+                              const int32_t* new_tokens, int32_t batch,
+                              int32_t block_size, int64_t* slot_mapping_out,
+                              int32_t* context_lens_out, int32_t* status_flag,
+                              void* stream);
+
+/* Return the blocks of every sequence b with release_mask[b] != 0 to the
+ * pool: its ceil(context_lens[b] / bs) blocks are pushed in batch order and,
+ * within a sequence, in logical order: free_stack[top + roff_b + k] =
+ * block_tables[b][k]. context_lens_out (may be NULL or alias context_lens)
+ * gets 0 for released rows. If the pushes would exceed pool_capacity, nothing
+ * changes and *status_flag = KVQ_ERR_OUT_OF_BLOCKS; else KVQ_OK. All pointers
+ * are device memory. */
+kvq_status kvq_blocks_release(int32_t* free_stack, int32_t* free_top,
+                              int64_t pool_capacity,
+                              const int32_t* block_tables,
+                              int32_t max_blocks_per_seq,
+                              const int32_t* context_lens,
+                              const int32_t* release_mask, int32_t batch,
+                              int32_t block_size, int32_t* context_lens_out,
+                              int32_t* status_flag, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* KVQ_H_ */
