@@ -1,0 +1,12 @@
+"""Quantized paged KV-cache append and fused-dequantization decode attention
+for AMD Instinct MI355X (gfx950).
+
+The work happens in libkvq.so (hand-written HIP kernels behind the C ABI of
+include/kvq.h); `kvq` is its ctypes binding. Importing this package fails
+loudly when the library has not been built.
+"""
+from .kvq import (  # noqa: F401
+    KvqError, PagedCache, kvq_append, kvq_blocks_release, kvq_blocks_reserve,
+    kvq_bytes_per_token, kvq_cache_plane_bytes, kvq_decode_attention,
+    kvq_decode_workspace_bytes, kvq_layout_check, kvq_pool_init,
+    kvq_status_string, make_layout)

@@ -1,0 +1,332 @@
+// kvq_api.cpp -- the library's C ABI: argument checks, sizes, split planning
+// and dispatch to the HIP launchers. Every check runs on the host before any
+// launch; the library allocates nothing and keeps no state.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+// Work items (sequence x KV head x split) the split planner aims for: 16 per
+// compute unit of an MI355X (256 CUs). A constant, so that the workspace size
+// is a pure function of the arguments.
+constexpr int64_t kTargetItems = 4096;
+constexpr int64_t kMinSplitTokens = 128;
+// A split's block ids travel in one 64-lane vector load.
+constexpr int64_t kMaxSplitBlocks = 64;
+// Tokens per append launch: keeps row indices within int32 inside kernels.
+constexpr int64_t kAppendChunk = int64_t(1) << 22;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int code_bits(int32_t code) {
+  return code == KVQ_CODE_NONE16 ? 16 : code == KVQ_CODE_INT4 ? 4 : 8;
+}
+
+kvq_status check_side(const kvq_layout* L, int side) {
+  const int32_t code = side ? L->v_code : L->k_code;
+  const int32_t mode = side ? L->v_mode : L->k_mode;
+  if (code < KVQ_CODE_NONE16 || code > KVQ_CODE_INT4) return KVQ_ERR_INVALID_ARGUMENT;
+  if (mode < KVQ_SCALE_TOKEN_SYM || mode > KVQ_SCALE_CHANNEL_BLOCK_SYM)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (mode == KVQ_SCALE_TOKEN_SYM) return KVQ_OK;
+  if (mode == KVQ_SCALE_GROUP_ASYM)
+    return (code == KVQ_CODE_INT4 && L->group_size == 32) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+  return (side == 0 && code == KVQ_CODE_INT8) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+}
+
+int64_t scales_per_bh(const kvq_layout* L, int side) {
+  const int32_t code = side ? L->v_code : L->k_code;
+  const int32_t mode = side ? L->v_mode : L->k_mode;
+  if (code == KVQ_CODE_NONE16) return 0;
+  if (mode == KVQ_SCALE_TOKEN_SYM) return L->block_size;
+  if (mode == KVQ_SCALE_GROUP_ASYM) return (int64_t)L->block_size * (L->head_dim / L->group_size);
+  return L->head_dim;
+}
+
+int64_t zeros_per_bh(const kvq_layout* L, int side) {
+  const int32_t mode = side ? L->v_mode : L->k_mode;
+  return mode == KVQ_SCALE_GROUP_ASYM ? (int64_t)L->block_size * (L->head_dim / L->group_size)
+                                      : 0;
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+struct SplitPlan {
+  int32_t split_blocks;
+  int32_t num_splits;
+};
+
+SplitPlan plan_splits(const kvq_layout* L, int32_t batch, int32_t max_context_len,
+                      int32_t split_blocks) {
+  const int64_t bs = L->block_size;
+  const int64_t nblk = (max_context_len + bs - 1) / bs;
+  int64_t c = split_blocks;
+  if (c <= 0) {
+    const int64_t units = (int64_t)batch * L->num_kv_heads * nblk;
+    c = (units + kTargetItems - 1) / kTargetItems;
+    const int64_t cmin = (kMinSplitTokens + bs - 1) / bs;
+    if (c < cmin) c = cmin;
+    if (c > kMaxSplitBlocks) c = kMaxSplitBlocks;
+  }
+  if (nblk > 0 && c > nblk) c = nblk;
+  if (c < 1) c = 1;
+  int64_t ns = nblk > 0 ? (nblk + c - 1) / c : 1;
+  return {(int32_t)c, (int32_t)ns};
+}
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARGUMENT: return "KVQ_ERR_INVALID_ARGUMENT";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_WORKSPACE_TOO_SMALL: return "KVQ_ERR_WORKSPACE_TOO_SMALL";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP";
+    case KVQ_ERR_OUT_OF_BLOCKS: return "KVQ_ERR_OUT_OF_BLOCKS";
+    default: return "KVQ_UNKNOWN_STATUS";
+  }
+}
+
+kvq_status kvq_layout_check(const kvq_layout* L) {
+  if (!L) return KVQ_ERR_INVALID_ARGUMENT;
+  if (L->reserved != 0 || L->num_kv_heads < 1 || L->num_kv_heads > 4096)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (L->head_dim != 64 && L->head_dim != 128) return KVQ_ERR_INVALID_ARGUMENT;
+  if (L->block_size != 16 && L->block_size != 32) return KVQ_ERR_INVALID_ARGUMENT;
+  if (L->src_dtype != KVQ_F16 && L->src_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARGUMENT;
+  kvq_status s = check_side(L, 0);
+  if (s != KVQ_OK) return s;
+  return check_side(L, 1);
+}
+
+int64_t kvq_bytes_per_token(const kvq_layout* L, int32_t num_layers, int32_t include_metadata) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  if (num_layers < 1) return KVQ_ERR_INVALID_ARGUMENT;
+  const int64_t H = L->num_kv_heads, d = L->head_dim, bs = L->block_size;
+  int64_t per_layer = 0;
+  for (int side = 0; side < 2; ++side) {
+    const int32_t code = side ? L->v_code : L->k_code;
+    const int32_t mode = side ? L->v_mode : L->k_mode;
+    per_layer += H * d * code_bits(code) / 8;
+    if (!include_metadata || code == KVQ_CODE_NONE16) continue;
+    if (mode == KVQ_SCALE_TOKEN_SYM)
+      per_layer += H * 4;
+    else if (mode == KVQ_SCALE_GROUP_ASYM)
+      per_layer += H * (d / L->group_size) * 5;
+    else
+      per_layer += (H * d * 4 + bs - 1) / bs;
+  }
+  return per_layer * num_layers;
+}
+
+kvq_status kvq_cache_plane_bytes(const kvq_layout* L, int64_t num_blocks, int32_t max_seqs,
+                                 int64_t out_bytes[7]) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  if (!out_bytes || num_blocks < 0 || max_seqs < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  const int64_t H = L->num_kv_heads, bs = L->block_size, d = L->head_dim;
+  for (int side = 0; side < 2; ++side) {
+    const int32_t code = side ? L->v_code : L->k_code;
+    out_bytes[0 + side] = num_blocks * H * bs * d * code_bits(code) / 8;
+    out_bytes[2 + side] = num_blocks * H * scales_per_bh(L, side) * 4;
+    out_bytes[4 + side] = num_blocks * H * zeros_per_bh(L, side);
+  }
+  out_bytes[6] = L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM ? (int64_t)max_seqs * H * bs * d * 2 : 0;
+  return KVQ_OK;
+}
+
+static kvq_status check_cache(const kvq_layout* L, const kvq_cache* C) {
+  if (!C || C->reserved != 0 || C->num_blocks < 1 || C->max_seqs < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  for (int side = 0; side < 2; ++side) {
+    const void* codes = side ? C->v_codes : C->k_codes;
+    const float* scale = side ? C->v_scale : C->k_scale;
+    const uint8_t* zero = side ? C->v_zero : C->k_zero;
+    if (!codes || !aligned16(codes)) return KVQ_ERR_INVALID_ARGUMENT;
+    if ((scales_per_bh(L, side) > 0) != (scale != nullptr)) return KVQ_ERR_INVALID_ARGUMENT;
+    if (scale && !aligned16(scale)) return KVQ_ERR_INVALID_ARGUMENT;
+    if ((zeros_per_bh(L, side) > 0) != (zero != nullptr)) return KVQ_ERR_INVALID_ARGUMENT;
+    if (zero && !aligned16(zero)) return KVQ_ERR_INVALID_ARGUMENT;
+  }
+  const bool chan = L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM;
+  if (chan != (C->k_stage != nullptr)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (chan && (C->max_seqs < 1 || !aligned16(C->k_stage))) return KVQ_ERR_INVALID_ARGUMENT;
+  return KVQ_OK;
+}
+
+kvq_status kvq_append(const kvq_layout* L, const kvq_cache* C, const void* k, const void* v,
+                      int64_t k_row_stride, int64_t v_row_stride, int64_t num_tokens,
+                      const int64_t* slot_mapping, const int32_t* stage_rows, void* stream) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  s = check_cache(L, C);
+  if (s != KVQ_OK) return s;
+  if (num_tokens < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return KVQ_OK;
+  const int64_t row = (int64_t)L->num_kv_heads * L->head_dim;
+  if (!k || !v || !slot_mapping || !aligned16(k) || !aligned16(v)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (k_row_stride < row || v_row_stride < row) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((k_row_stride * 2) % 16 || (v_row_stride * 2) % 16) return KVQ_ERR_INVALID_ARGUMENT;
+  const bool chan = L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM;
+  if (chan != (stage_rows != nullptr)) return KVQ_ERR_INVALID_ARGUMENT;
+  kvq::AppendPlan p;
+  p.side[0] = {k, k_row_stride, C->k_codes, C->k_scale, C->k_zero};
+  p.side[1] = {v, v_row_stride, C->v_codes, C->v_scale, C->v_zero};
+  p.k_stage = C->k_stage;
+  p.num_blocks = C->num_blocks;
+  p.num_kv_heads = L->num_kv_heads;
+  p.head_dim = L->head_dim;
+  p.block_size = L->block_size;
+  p.src_bf16 = L->src_dtype == KVQ_BF16;
+  p.code[0] = L->k_code;
+  p.code[1] = L->v_code;
+  p.mode[0] = L->k_mode;
+  p.mode[1] = L->v_mode;
+  p.max_seqs = C->max_seqs;
+  p.cu_count = 256;
+  // Chunks keep kernel row indices small. A per-channel key append is not
+  // chunked: a chunk boundary inside one sequence's run would split the rows
+  // of a completing block between launches.
+  const int64_t chunk = chan ? num_tokens : kAppendChunk;
+  for (int64_t t0 = 0; t0 < num_tokens; t0 += chunk) {
+    const int64_t n = num_tokens - t0 < chunk ? num_tokens - t0 : chunk;
+    p.side[0].src = static_cast<const uint16_t*>(k) + t0 * k_row_stride;
+    p.side[1].src = static_cast<const uint16_t*>(v) + t0 * v_row_stride;
+    p.slots = slot_mapping + t0;
+    p.stage_rows = stage_rows ? stage_rows + t0 : nullptr;
+    p.num_tokens = n;
+    hipError_t e = kvq::launch_append(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+}
+
+int64_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t batch, int32_t num_q_heads,
+                                   int32_t max_context_len, int32_t split_blocks) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  if (batch < 0 || num_q_heads < 1 || max_context_len < 0 || split_blocks < 0 ||
+      split_blocks > kMaxSplitBlocks)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  SplitPlan sp = plan_splits(L, batch, max_context_len, split_blocks);
+  const int64_t items = (int64_t)batch * num_q_heads * sp.num_splits;
+  return round_up(items * L->head_dim * 4, 256) + round_up(items * 2 * 4, 256);
+}
+
+kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const void* q,
+                                int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len,
+                                float sm_scale, int32_t split_blocks, void* out,
+                                int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  s = check_cache(L, C);
+  if (s != KVQ_OK) return s;
+  if (batch < 0 || num_q_heads < 1 || num_q_heads % L->num_kv_heads) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_q_heads / L->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+  if (q_dtype != KVQ_F16 && q_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (max_context_len < 0 || split_blocks < 0 || split_blocks > kMaxSplitBlocks ||
+      max_blocks_per_seq < 1)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * L->block_size)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!kvq::decode_supported(L->k_code, L->v_code, L->k_mode, L->v_mode)) return KVQ_ERR_UNSUPPORTED;
+  if (batch == 0) return KVQ_OK;
+  if (!q || !out || !block_tables || !context_lens || !workspace) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_INVALID_ARGUMENT;
+  const int64_t need = kvq_decode_workspace_bytes(L, batch, num_q_heads, max_context_len, split_blocks);
+  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  SplitPlan sp = plan_splits(L, batch, max_context_len, split_blocks);
+  const int64_t items = (int64_t)batch * num_q_heads * sp.num_splits;
+  kvq::DecodePlan p;
+  p.q = q;
+  p.q_bf16 = q_dtype == KVQ_BF16;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = L->num_kv_heads;
+  p.head_dim = L->head_dim;
+  p.block_size = L->block_size;
+  p.k_code = L->k_code;
+  p.v_code = L->v_code;
+  p.k_mode = L->k_mode;
+  p.v_mode = L->v_mode;
+  p.src_bf16 = L->src_dtype == KVQ_BF16;
+  p.k_codes = C->k_codes;
+  p.v_codes = C->v_codes;
+  p.k_scale = C->k_scale;
+  p.v_scale = C->v_scale;
+  p.k_zero = C->k_zero;
+  p.v_zero = C->v_zero;
+  p.k_stage = C->k_stage;
+  p.num_blocks = C->num_blocks;
+  p.block_tables = block_tables;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.context_lens = context_lens;
+  p.split_blocks = sp.split_blocks;
+  p.num_splits = sp.num_splits;
+  p.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)L->head_dim));
+  p.out = out;
+  p.out_dtype = out_dtype;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                     round_up(items * L->head_dim * 4, 256));
+  return hip_status(kvq::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_pool_init(int32_t* free_stack, int32_t* free_top, const int32_t* initial_order,
+                         int64_t num_blocks, void* stream) {
+  if (!free_stack || !free_top || num_blocks < 1 || num_blocks > INT32_MAX)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_pool_init(free_stack, free_top, initial_order, num_blocks,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_blocks_reserve(int32_t* free_stack, int32_t* free_top, int64_t pool_capacity,
+                              int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, const int32_t* new_tokens,
+                              int32_t batch, int32_t block_size, int64_t* slot_mapping_out,
+                              int32_t* context_lens_out, int32_t* status_flag, void* stream) {
+  if (!free_stack || !free_top || !status_flag || pool_capacity < 1 || pool_capacity > INT32_MAX)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1) return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (!block_tables || !context_lens || !new_tokens || !slot_mapping_out))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_blocks_reserve(
+      free_stack, free_top, pool_capacity, block_tables, max_blocks_per_seq, context_lens,
+      new_tokens, batch, block_size, slot_mapping_out, context_lens_out, status_flag,
+      static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_blocks_release(int32_t* free_stack, int32_t* free_top, int64_t pool_capacity,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, const int32_t* release_mask,
+                              int32_t batch, int32_t block_size, int32_t* context_lens_out,
+                              int32_t* status_flag, void* stream) {
+  if (!free_stack || !free_top || !status_flag || pool_capacity < 1 || pool_capacity > INT32_MAX)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1) return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (!block_tables || !context_lens || !release_mask)) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_blocks_release(
+      free_stack, free_top, pool_capacity, block_tables, max_blocks_per_seq, context_lens,
+      release_mask, batch, block_size, context_lens_out, status_flag,
+      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

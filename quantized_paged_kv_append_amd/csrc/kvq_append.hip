@@ -1,0 +1,509 @@
+// kvq_append.hip -- quantize-on-append into paged blocks (gfx950).
+//
+// What is computed ("Dynamic KV Cache Quantization for Fast LLM Inference",
+// section "Understanding Dynamic Quantization Techniques for KV Caches"): for
+// every new (token, head) vector a scale from its own range, computed when it
+// enters the cache, then codes round(x / scale); section "Integrating Dynamic
+// Quantization with PagedAttention": each physical block stores the quantized
+// keys and values, placed through the sequence's block map (here the slot
+// mapping). The per-channel key mode follows "KV Cache Optimization:
+// Strategies for Faster LLM Inference", section "KV Cache Quantization: When
+// and How to Compress".
+//
+// Design (HBM-bound single streaming pass): a row of d 16-bit elements is
+// handled by d/8 lanes, each with one 16-byte load (or, for 4-bit codes, the
+// loads that feed whole output bytes of the slice-interleaved nibble layout);
+// the row's absmax (or per-group min/max) is a lane-group shuffle reduction;
+// the scale is one correctly rounded fp32 division per row; codes use the
+// reciprocal with a near-tie check that falls back to the exact quotient, so
+// stored bytes equal rne(x / s) exactly. Codes leave as one 8-byte (INT8/FP8)
+// or 4-byte (INT4) store per lane.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+struct SideArgs {
+  const uint16_t* src;
+  int64_t row_stride;
+  uint8_t* codes;
+  float* scale;
+  uint8_t* zero;
+};
+
+struct RowArgs {
+  SideArgs side[2];
+  const int64_t* slots;
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int32_t H;
+  int32_t bs;
+  int32_t side0;  // first side handled; blockIdx.y adds to it
+};
+
+__device__ __forceinline__ uint32_t pack_bytes(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) |
+         ((uint32_t)(c & 0xFF) << 16) | ((uint32_t)(d & 0xFF) << 24);
+}
+
+// Byte codes (INT8 / FP8 / 16-bit passthrough): lane j of a row holds
+// elements 8j .. 8j+7.
+template <int CODE, int D, bool BF16>
+__global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
+  constexpr int RL = D / 8;         // lanes per row
+  constexpr int RPW = kWave / RL;   // rows per wave
+  const SideArgs S = a.side[a.side0 + blockIdx.y];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = lane % RL;
+  const int64_t rows = a.num_tokens * a.H;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  for (int64_t base = wave * RPW; base < rows; base += nwaves * RPW) {
+    const int64_t r = base + lane / RL;
+    const bool in = r < rows;
+    const int64_t t = in ? r / a.H : 0;
+    const int h = in ? (int)(r % a.H) : 0;
+    const int64_t slot = in ? a.slots[t] : -1;
+    const int64_t blk = slot >= 0 ? slot / a.bs : 0;
+    const bool live = in && slot >= 0 && blk < a.num_blocks;
+    const int off = slot >= 0 ? (int)(slot % a.bs) : 0;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (in) {
+      w = *reinterpret_cast<const u32x4*>(S.src + t * S.row_stride + (int64_t)h * D + 8 * j);
+    }
+    const int64_t rowi = ((int64_t)blk * a.H + h) * a.bs + off;
+    if constexpr (CODE == KVQ_CODE_NONE16) {
+      if (live) *reinterpret_cast<u32x4*>(S.codes + rowi * (2 * D) + 16 * j) = w;
+      continue;
+    }
+    float x[8];
+    unpack2<BF16>(w.x, x[0], x[1]);
+    unpack2<BF16>(w.y, x[2], x[3]);
+    unpack2<BF16>(w.z, x[4], x[5]);
+    unpack2<BF16>(w.w, x[6], x[7]);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = group_max<RL>(amax);
+    constexpr float kQmax = CODE == KVQ_CODE_INT8 ? 127.0f : 448.0f;
+    const float s = amax == 0.0f ? 1.0f : div_rn(amax, kQmax);
+    const float inv = div_rn(1.0f, s);
+    uint32_t c[8];
+    bool tie = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float y = x[i] * inv;
+      if (CODE == KVQ_CODE_INT8) {
+        const float q = rne(y);
+        tie |= near_half(y, q);
+        c[i] = (uint32_t)(int)fminf(fmaxf(q, -127.0f), 127.0f);
+      } else {
+        float m, rm;
+        c[i] = e4m3_encode(y, m, rm);
+        tie |= near_half(m, rm);
+      }
+    }
+    if (tie) {  // rare: redo this lane's codes with the exact quotient
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float y = div_rn(x[i], s);
+        if (CODE == KVQ_CODE_INT8) {
+          c[i] = (uint32_t)(int)fminf(fmaxf(rne(y), -127.0f), 127.0f);
+        } else {
+          float m, rm;
+          c[i] = e4m3_encode(y, m, rm);
+        }
+      }
+    }
+    if (live) {
+      u32x2 o = {pack_bytes(c[0], c[1], c[2], c[3]), pack_bytes(c[4], c[5], c[6], c[7])};
+      *reinterpret_cast<u32x2*>(S.codes + rowi * D + 8 * j) = o;
+      if (j == 0) S.scale[rowi] = s;
+    }
+  }
+}
+
+// 4-bit codes. Nibble layout: with n = D/32 slices, element 32 i + 2 r + t
+// sits in byte n r + i (nibble t). Lane j of a row owns r in [R j, R j + R)
+// (R = 16 / RL) for every slice i, i.e. elements 32 i + 2 R j + k, k < 2R,
+// and writes the 4 contiguous bytes 4 j .. 4 j + 3.
+// MODE TOKEN_SYM: symmetric codes in [-7, 7] stored as q & 0xF.
+// MODE GROUP_ASYM: group = slice (group_size 32), unsigned codes with zero
+// point.
+template <int MODE, int D, bool BF16>
+__global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
+  constexpr int RL = D / 8;
+  constexpr int RPW = kWave / RL;
+  constexpr int NS = D / 32;  // slices (= groups)
+  constexpr int R = 16 / RL;  // r values per lane
+  constexpr int K = 2 * R;    // elements per slice per lane
+  const SideArgs S = a.side[a.side0 + blockIdx.y];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = lane % RL;
+  const int row_lane0 = lane - j;
+  const int64_t rows = a.num_tokens * a.H;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  for (int64_t base = wave * RPW; base < rows; base += nwaves * RPW) {
+    const int64_t r = base + lane / RL;
+    const bool in = r < rows;
+    const int64_t t = in ? r / a.H : 0;
+    const int h = in ? (int)(r % a.H) : 0;
+    const int64_t slot = in ? a.slots[t] : -1;
+    const int64_t blk = slot >= 0 ? slot / a.bs : 0;
+    const bool live = in && slot >= 0 && blk < a.num_blocks;
+    const int off = slot >= 0 ? (int)(slot % a.bs) : 0;
+    float x[NS][K];
+    const uint16_t* row = S.src + t * S.row_stride + (int64_t)h * D;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const uint16_t* p = row + 32 * i + K * j;
+      if constexpr (K == 2) {
+        uint32_t w = in ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+        unpack2<BF16>(w, x[i][0], x[i][1]);
+      } else {
+        u32x2 w = {0u, 0u};
+        if (in) w = *reinterpret_cast<const u32x2*>(p);
+        unpack2<BF16>(w.x, x[i][0], x[i][1]);
+        unpack2<BF16>(w.y, x[i][2], x[i][3]);
+      }
+    }
+    const int64_t rowi = ((int64_t)blk * a.H + h) * a.bs + off;
+    int q[NS][K];
+    bool tie = false;
+    if (MODE == KVQ_SCALE_TOKEN_SYM) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int k = 0; k < K; ++k) amax = fmaxf(amax, fabsf(x[i][k]));
+      amax = group_max<RL>(amax);
+      const float s = amax == 0.0f ? 1.0f : div_rn(amax, 7.0f);
+      const float inv = div_rn(1.0f, s);
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float y = x[i][k] * inv;
+          const float qq = rne(y);
+          tie |= near_half(y, qq);
+          q[i][k] = (int)fminf(fmaxf(qq, -7.0f), 7.0f);
+        }
+      if (tie) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+#pragma unroll
+          for (int k = 0; k < K; ++k)
+            q[i][k] = (int)fminf(fmaxf(rne(div_rn(x[i][k], s)), -7.0f), 7.0f);
+      }
+      if (live && j == 0) S.scale[rowi] = s;
+    } else {
+      // per-slice range, widened to contain 0
+      float mn[NS], mx[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        mn[i] = 0.0f;
+        mx[i] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          mn[i] = fminf(mn[i], x[i][k]);
+          mx[i] = fmaxf(mx[i], x[i][k]);
+        }
+        mn[i] = group_min<RL>(mn[i]);
+        mx[i] = group_max<RL>(mx[i]);
+      }
+      // lane j computes the scalars of group j % NS; the row gathers them
+      const int gown = j % NS;
+      float mno = mn[0], mxo = mx[0];
+#pragma unroll
+      for (int i = 1; i < NS; ++i)
+        if (gown == i) {
+          mno = mn[i];
+          mxo = mx[i];
+        }
+      float so = 1.0f, invo = 1.0f;
+      int zo = 0;
+      if (mxo != mno) {
+        so = div_rn(mxo - mno, 15.0f);
+        zo = (int)fminf(fmaxf(rne(div_rn(-mno, so)), 0.0f), 15.0f);
+        invo = div_rn(1.0f, so);
+      }
+      float sg[NS], ig[NS];
+      int zg[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        sg[i] = __shfl(so, row_lane0 + i, kWave);
+        ig[i] = __shfl(invo, row_lane0 + i, kWave);
+        zg[i] = __shfl(zo, row_lane0 + i, kWave);
+      }
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float y = x[i][k] * ig[i];
+          const float qq = rne(y);
+          tie |= near_half(y, qq);
+          q[i][k] = min(max((int)qq + zg[i], 0), 15);
+        }
+      if (tie) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+#pragma unroll
+          for (int k = 0; k < K; ++k)
+            q[i][k] = min(max((int)rne(div_rn(x[i][k], sg[i])) + zg[i], 0), 15);
+      }
+      if (live && j == 0) {
+        float* sp = S.scale + rowi * NS;
+        uint8_t* zp = S.zero + rowi * NS;
+        uint32_t zw = 0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          sp[i] = sg[i];
+          zw |= (uint32_t)zg[i] << (8 * i);
+        }
+        if constexpr (NS == 4) {
+          *reinterpret_cast<uint32_t*>(zp) = zw;
+        } else {
+          *reinterpret_cast<uint16_t*>(zp) = (uint16_t)zw;
+        }
+      }
+    }
+    // byte (rr, i) of this lane's 4 = n * rr + i holds elements 2 rr, 2 rr + 1
+    // of slice i (relative to this lane's run)
+    uint32_t out = 0;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const uint32_t byte = (uint32_t)(q[i][2 * rr] & 0xF) | ((uint32_t)(q[i][2 * rr + 1] & 0xF) << 4);
+        out |= byte << (8 * (NS * rr + i));
+      }
+    if (live) *reinterpret_cast<uint32_t*>(S.codes + rowi * (D / 2) + 4 * j) = out;
+  }
+}
+
+// ---- per-channel-per-block keys -----------------------------------------
+// Phase 1: every token whose slot is the last of its block completes that
+// block: the block's rows come from this call (the run of preceding tokens
+// with consecutive slots and the same stage row) and, for earlier offsets,
+// from the stage row. One wave per (completing token, head); lane l owns
+// channels 2l, 2l+1 (D = 128) or channel l (D = 64) over all bs rows.
+struct ChanArgs {
+  const uint16_t* src;
+  int64_t row_stride;
+  const int64_t* slots;
+  const int32_t* stage_rows;
+  uint16_t* stage;  // [max_seqs][H][bs][D]
+  int8_t* codes;
+  float* scale;
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int32_t H;
+  int32_t max_seqs;
+};
+
+template <int D, int BS, bool BF16>
+__global__ __launch_bounds__(256) void chan_complete_kernel(ChanArgs a) {
+  constexpr int CPL = D / kWave;  // channels per lane (1 or 2)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  const int64_t items = a.num_tokens * a.H;
+  for (int64_t it = wave; it < items; it += nwaves) {
+    const int64_t t = it / a.H;
+    const int h = (int)(it % a.H);
+    const int64_t slot = a.slots[t];
+    if (slot < 0 || slot % BS != BS - 1) continue;
+    const int64_t blk = slot / BS;
+    const int32_t srow = a.stage_rows[t];
+    if (blk >= a.num_blocks || srow < 0 || srow >= a.max_seqs) continue;
+    // rows of this block provided by this call: t - k for k < n_new
+    int n_new = 1;
+    while (n_new < BS && t - n_new >= 0 && a.slots[t - n_new] == slot - n_new &&
+           a.stage_rows[t - n_new] == srow)
+      ++n_new;
+    float x[BS][CPL];
+    float amax[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) amax[c] = 0.0f;
+#pragma unroll
+    for (int o = 0; o < BS; ++o) {
+      const int k = BS - 1 - o;  // token t - k holds offset o when k < n_new
+      const uint16_t* p;
+      if (k < n_new)
+        p = a.src + (t - k) * a.row_stride + (int64_t)h * D;
+      else
+        p = a.stage + (((int64_t)srow * a.H + h) * BS + o) * D;
+      if constexpr (CPL == 2) {
+        uint32_t w = *reinterpret_cast<const uint32_t*>(p + 2 * lane);
+        unpack2<BF16>(w, x[o][0], x[o][1]);
+      } else {
+        uint16_t w = p[lane];
+        x[o][0] = BF16 ? bf16_lo(w) : f16_lo(w);
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) amax[c] = fmaxf(amax[c], fabsf(x[o][c]));
+    }
+    float s[CPL], inv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      s[c] = amax[c] == 0.0f ? 1.0f : div_rn(amax[c], 127.0f);
+      inv[c] = div_rn(1.0f, s[c]);
+    }
+    int8_t* cb = a.codes + ((blk * a.H + h) * BS) * D;
+#pragma unroll
+    for (int o = 0; o < BS; ++o) {
+      int q[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float y = x[o][c] * inv[c];
+        float r = rne(y);
+        if (near_half(y, r)) r = rne(div_rn(x[o][c], s[c]));
+        q[c] = (int)fminf(fmaxf(r, -127.0f), 127.0f);
+      }
+      if constexpr (CPL == 2) {
+        *reinterpret_cast<uint16_t*>(cb + o * D + 2 * lane) =
+            (uint16_t)((q[0] & 0xFF) | ((q[1] & 0xFF) << 8));
+      } else {
+        cb[o * D + lane] = (int8_t)q[0];
+      }
+    }
+    float* sp = a.scale + (blk * a.H + h) * D;
+    if constexpr (CPL == 2) {
+      float2 sv = {s[0], s[1]};
+      *reinterpret_cast<float2*>(sp + 2 * lane) = sv;
+    } else {
+      sp[lane] = s[0];
+    }
+  }
+}
+
+// Phase 2: rows whose block is not completed within this call go, raw, to
+// their stage row. Runs after phase 1 (same stream), which may still read
+// stage rows of a block that this call completes. One row per D/8 lanes.
+template <int D, int BS>
+__global__ __launch_bounds__(256) void chan_stage_kernel(ChanArgs a) {
+  constexpr int RL = D / 8;
+  constexpr int RPW = kWave / RL;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = lane % RL;
+  const int64_t rows = a.num_tokens * a.H;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  for (int64_t base = wave * RPW; base < rows; base += nwaves * RPW) {
+    const int64_t r = base + lane / RL;
+    if (r >= rows) continue;
+    const int64_t t = r / a.H;
+    const int h = (int)(r % a.H);
+    const int64_t slot = a.slots[t];
+    if (slot < 0) continue;
+    const int32_t srow = a.stage_rows[t];
+    if (srow < 0 || srow >= a.max_seqs || slot / BS >= a.num_blocks) continue;
+    const int off = (int)(slot % BS);
+    // completed in this call iff the token holding the block's last offset
+    // follows in the same run
+    const int64_t tl = t + (BS - 1 - off);
+    const bool completes = tl < a.num_tokens && a.slots[tl] == slot + (BS - 1 - off) &&
+                           a.stage_rows[tl] == srow;
+    if (completes) continue;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(a.src + t * a.row_stride + (int64_t)h * D + 8 * j);
+    *reinterpret_cast<u32x4*>(a.stage + (((int64_t)srow * a.H + h) * BS + off) * D + 8 * j) = w;
+  }
+}
+
+int grid_for(int64_t waves_needed, int cu_count) {
+  int64_t blocks = (waves_needed + 3) / 4;
+  int64_t cap = (int64_t)cu_count * 16;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+template <int D, bool BF16>
+hipError_t launch_rows(const AppendPlan& p, const RowArgs& ra, int code, int mode,
+                       int nsides, hipStream_t stream) {
+  const int64_t rows = p.num_tokens * p.num_kv_heads;
+  const int64_t waves = (rows + (kWave / (D / 8)) - 1) / (kWave / (D / 8));
+  dim3 grid(grid_for(waves, p.cu_count), nsides);
+  if (code == KVQ_CODE_INT8)
+    append_bytes_kernel<KVQ_CODE_INT8, D, BF16><<<grid, 256, 0, stream>>>(ra);
+  else if (code == KVQ_CODE_FP8_E4M3)
+    append_bytes_kernel<KVQ_CODE_FP8_E4M3, D, BF16><<<grid, 256, 0, stream>>>(ra);
+  else if (code == KVQ_CODE_NONE16)
+    append_bytes_kernel<KVQ_CODE_NONE16, D, BF16><<<grid, 256, 0, stream>>>(ra);
+  else if (mode == KVQ_SCALE_TOKEN_SYM)
+    append_int4_kernel<KVQ_SCALE_TOKEN_SYM, D, BF16><<<grid, 256, 0, stream>>>(ra);
+  else
+    append_int4_kernel<KVQ_SCALE_GROUP_ASYM, D, BF16><<<grid, 256, 0, stream>>>(ra);
+  return hipGetLastError();
+}
+
+template <int D, int BS, bool BF16>
+hipError_t launch_chan(const AppendPlan& p, hipStream_t stream) {
+  ChanArgs c;
+  c.src = static_cast<const uint16_t*>(p.side[0].src);
+  c.row_stride = p.side[0].row_stride;
+  c.slots = p.slots;
+  c.stage_rows = p.stage_rows;
+  c.stage = static_cast<uint16_t*>(p.k_stage);
+  c.codes = static_cast<int8_t*>(p.side[0].codes);
+  c.scale = p.side[0].scale;
+  c.num_tokens = p.num_tokens;
+  c.num_blocks = p.num_blocks;
+  c.H = p.num_kv_heads;
+  c.max_seqs = p.max_seqs;
+  const int64_t items = p.num_tokens * p.num_kv_heads;
+  // phase 1: about one item in BS completes a block
+  chan_complete_kernel<D, BS, BF16><<<grid_for((items + 7) / 8, p.cu_count), 256, 0, stream>>>(c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t waves = (items + (kWave / (D / 8)) - 1) / (kWave / (D / 8));
+  chan_stage_kernel<D, BS><<<grid_for(waves, p.cu_count), 256, 0, stream>>>(c);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_append_d(const AppendPlan& p, hipStream_t stream) {
+  RowArgs ra;
+  for (int s = 0; s < 2; ++s) {
+    ra.side[s].src = static_cast<const uint16_t*>(p.side[s].src);
+    ra.side[s].row_stride = p.side[s].row_stride;
+    ra.side[s].codes = static_cast<uint8_t*>(p.side[s].codes);
+    ra.side[s].scale = p.side[s].scale;
+    ra.side[s].zero = p.side[s].zero;
+  }
+  ra.slots = p.slots;
+  ra.num_tokens = p.num_tokens;
+  ra.num_blocks = p.num_blocks;
+  ra.H = p.num_kv_heads;
+  ra.bs = p.block_size;
+  hipError_t e;
+  const bool chan = p.mode[0] == KVQ_SCALE_CHANNEL_BLOCK_SYM;
+  if (!chan && p.code[0] == p.code[1] && p.mode[0] == p.mode[1]) {
+    ra.side0 = 0;
+    return launch_rows<D, BF16>(p, ra, p.code[0], p.mode[0], 2, stream);
+  }
+  if (!chan) {
+    ra.side0 = 0;
+    e = launch_rows<D, BF16>(p, ra, p.code[0], p.mode[0], 1, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    e = p.block_size == 16 ? launch_chan<D, 16, BF16>(p, stream)
+                           : launch_chan<D, 32, BF16>(p, stream);
+    if (e != hipSuccess) return e;
+  }
+  ra.side0 = 1;
+  return launch_rows<D, BF16>(p, ra, p.code[1], p.mode[1], 1, stream);
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendPlan& p, hipStream_t stream) {
+  if (p.num_tokens == 0) return hipSuccess;
+  if (p.head_dim == 128)
+    return p.src_bf16 ? launch_append_d<128, true>(p, stream) : launch_append_d<128, false>(p, stream);
+  return p.src_bf16 ? launch_append_d<64, true>(p, stream) : launch_append_d<64, false>(p, stream);
+}
+
+}  // namespace kvq

@@ -1,0 +1,523 @@
+// kvq_decode.hip -- split-K paged decode attention over quantized blocks with
+// in-register dequantization (gfx950).
+//
+// What is computed ("KV Cache Optimization" glossary, "Technical
+// Architecture", stage 4: the attention kernel dequantizes KV blocks on the
+// fly while decoding; "Dynamic KV Cache Quantization for Fast LLM Inference",
+// section "Recap of KV Caching": the current query attends over its
+// sequence's cached keys and values): for each sequence b and query head h,
+// out = sum_t p_t v_t / sum_t p_t with p_t = exp(s_t - max s) and
+// s_t = (q . k_t) * sm_scale, over the first context_lens[b] tokens, keys and
+// values dequantized from their codes and scales. Online softmax across blocks
+// and a log-sum-exp merge across splits follow the Flash-Attention style named
+// in "KV Cache Optimization: Strategies for Faster LLM Inference", section
+// "Implementing KV Cache Optimization: A Practical Checklist".
+//
+// Design. Decode is HBM-bound (the same page, "Common pitfalls": decode is
+// memory-bound), so the kernel streams each code byte once:
+//  * One wave per work item (sequence b, KV head g, split j of split_blocks
+//    cache blocks). The G query heads that share KV head g are the 16 columns
+//    of the MFMA tiles (zero-padded when G < 16).
+//  * Scores: S[16 tokens x 16 heads] = K_tile . Q^T with
+//    v_mfma_f32_16x16x32_f16. Lane (r, j) = (lane % 16, lane / 16) feeds
+//    token r of the tile with elements [j d/4, (j+1) d/4) of its key row,
+//    loaded as 16-byte vectors; Q uses the same element assignment.
+//  * INT8, E4M3 and INT4 codes are all exactly representable in fp16, so
+//    codes are converted in registers (E4M3 by the hardware converter, INT8
+//    by the 0x64 exponent trick) and scales are applied after the products:
+//    the key scale multiplies the score, the value scale multiplies the
+//    probability before it is rounded to fp16.
+//  * The accumulator layout of S (lane holds tokens 4j..4j+3 of head r) is
+//    exactly the B operand of O^T[d x heads] += V^T[d x 16] . P^T[16 x heads]
+//    (v_mfma_f32_16x16x16_f16), so probabilities never leave registers. Lane
+//    (r, j) feeds value bytes [r d/16, (r+1) d/16) of tokens 4j..4j+3 and
+//    ends up owning outputs [j d/4, (j+1) d/4) of head r.
+//  * The query is pre-scaled per head by a power of two into [1, 2) before
+//    its fp16 conversion (exact for bf16 values within 2^14 of the head's
+//    largest element); the factor returns in the score scale.
+//  * A ring of three register buffers keeps two cache blocks in flight while
+//    the wave computes on a third; block ids come from one vector load per 64
+//    blocks and are read with v_readlane.
+//  * Partials (m, l, acc) per split go to the workspace; decode_reduce merges
+//    them with the log-sum-exp rule.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_acc;
+  float* ws_ml;
+  int64_t num_blocks;
+  int32_t q_bf16;
+  int32_t Hq;
+  int32_t H;
+  int32_t G;
+  int32_t max_blocks;
+  int32_t split_blocks;
+  int32_t num_splits;
+  float sm_log2;  // sm_scale * log2(e)
+};
+
+// Per-lane data of one cache block (BS tokens) for 8-bit codes.
+template <int D, int BS>
+struct Tile8 {
+  static constexpr int NT = BS / 16;     // 16-token MFMA tiles per block
+  static constexpr int KV = D / 64;      // 16-byte key vectors per lane per tile
+  static constexpr int VB = D / 16;      // value bytes per token per lane
+  u32x4 k[NT][KV];
+  uint32_t v[NT][4][VB / 4];             // [tile][token i][dword]
+  float4v sk[NT];
+  float4v sv[NT];
+};
+
+template <int D, int BS>
+__device__ __forceinline__ void load_tile8(Tile8<D, BS>& t, const DecodeArgs& a,
+                                           int64_t bh, int lane) {
+  const int r = lane & 15, j = lane >> 4;
+  const uint8_t* kb = a.k_codes + bh * BS * D;
+  const uint8_t* vb = a.v_codes + bh * BS * D;
+#pragma unroll
+  for (int nt = 0; nt < Tile8<D, BS>::NT; ++nt) {
+    const uint8_t* kr = kb + (nt * 16 + r) * D + j * (D / 4);
+#pragma unroll
+    for (int u = 0; u < Tile8<D, BS>::KV; ++u)
+      t.k[nt][u] = *reinterpret_cast<const u32x4*>(kr + 16 * u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* vr = vb + (nt * 16 + 4 * j + i) * D + r * (D / 16);
+      if constexpr (D == 128) {
+        u32x2 w = *reinterpret_cast<const u32x2*>(vr);
+        t.v[nt][i][0] = w.x;
+        t.v[nt][i][1] = w.y;
+      } else {
+        t.v[nt][i][0] = *reinterpret_cast<const uint32_t*>(vr);
+      }
+    }
+    t.sk[nt] = *reinterpret_cast<const float4v*>(a.k_scale + bh * BS + nt * 16 + 4 * j);
+    t.sv[nt] = *reinterpret_cast<const float4v*>(a.v_scale + bh * BS + nt * 16 + 4 * j);
+  }
+}
+
+// 8 code bytes (two dwords) to 8 fp16 values, in byte order.
+template <int CODE>
+__device__ __forceinline__ half8v codes8_to_h8(uint32_t lo, uint32_t hi) {
+  half2v p0, p1, p2, p3;
+  if constexpr (CODE == KVQ_CODE_FP8_E4M3) {
+    p0 = fp8x2_to_h2<false>(lo);
+    p1 = fp8x2_to_h2<true>(lo);
+    p2 = fp8x2_to_h2<false>(hi);
+    p3 = fp8x2_to_h2<true>(hi);
+  } else {
+    const uint32_t xl = lo ^ 0x80808080u, xh = hi ^ 0x80808080u;
+    p0 = i8x2_to_h2(xl, 0x04010400u);
+    p1 = i8x2_to_h2(xl, 0x04030402u);
+    p2 = i8x2_to_h2(xh, 0x04010400u);
+    p3 = i8x2_to_h2(xh, 0x04030402u);
+  }
+  half8v o;
+  o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+  o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+  return o;
+}
+
+// Value operand of MFMA c: bytes c of the lane's four token words, as fp16.
+// a01 = [t0.bX, t1.bX, t0.bY, t1.bY], a23 likewise for tokens 2, 3.
+template <int CODE, bool HI>
+__device__ __forceinline__ half4v vpair_to_h4(uint32_t a01, uint32_t a23) {
+  half2v x, y;
+  if constexpr (CODE == KVQ_CODE_FP8_E4M3) {
+    x = fp8x2_to_h2<HI>(a01);
+    y = fp8x2_to_h2<HI>(a23);
+  } else {
+    const uint32_t sel = HI ? 0x04030402u : 0x04010400u;
+    x = i8x2_to_h2(a01 ^ 0x80808080u, sel);
+    y = i8x2_to_h2(a23 ^ 0x80808080u, sel);
+  }
+  half4v o;
+  o[0] = x[0]; o[1] = x[1]; o[2] = y[0]; o[3] = y[1];
+  return o;
+}
+
+// max over the four lanes {l, l^16, l^32, l^48} (one head column), with
+// the gfx950 lane-swap instructions instead of LDS permutes.
+__device__ __forceinline__ float colmax4(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float colsum4(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <int D>
+struct SoftmaxState {
+  float m;                 // running max (log2 units) of head r
+  float l;                 // this lane's part of the running sum
+  float4v acc[D / 16];     // O^T accumulators
+};
+
+// One 16-token tile: scores, online softmax, PV. TAIL handles the tile that
+// ends past the sequence length.
+template <int CODE, int D, int BS, bool TAIL>
+__device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos0, int L,
+                                          const half8v* qop, float cscore, int j,
+                                          SoftmaxState<D>& st) {
+  constexpr int NCH = D / 32;
+  constexpr int NPV = D / 16;
+  float4v S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const u32x4& kw = t.k[nt][c / 2];
+    const uint32_t lo = (c & 1) ? kw.z : kw.x;
+    const uint32_t hi = (c & 1) ? kw.w : kw.y;
+    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_h8<CODE>(lo, hi), qop[c], S, 0, 0, 0);
+  }
+  bool ok[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ok[e] = !TAIL || pos0 + 4 * j + e < L;
+  float s[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s[e] = S[e] * t.sk[nt][e] * cscore;
+    if (TAIL && !ok[e]) s[e] = -INFINITY;
+  }
+  const float mt = colmax4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+  const float mn = fmaxf(st.m, mt);
+  const float msafe = mn == -INFINITY ? 0.0f : mn;
+  if (__any(mn > st.m)) {  // a running max grew: rescale (rare after warm-up)
+    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
+  }
+  st.m = mn;
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - msafe);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  half4v pop;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float pv = p[e] * t.sv[nt][e];
+    if (TAIL && !ok[e]) pv = 0.0f;
+    pop[e] = (half_t)pv;
+  }
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) {
+    uint32_t t0 = t.v[nt][0][w], t1 = t.v[nt][1][w];
+    uint32_t t2 = t.v[nt][2][w], t3 = t.v[nt][3][w];
+    if (TAIL) {  // zero the codes of masked tokens (E4M3 NaN bytes)
+      t0 = ok[0] ? t0 : 0u;
+      t1 = ok[1] ? t1 : 0u;
+      t2 = ok[2] ? t2 : 0u;
+      t3 = ok[3] ? t3 : 0u;
+    }
+    // [t0.b0 t1.b0 t0.b1 t1.b1], [t0.b2 t1.b2 t0.b3 t1.b3]
+    const uint32_t a01l = __builtin_amdgcn_perm(t1, t0, 0x05010400u);
+    const uint32_t a01h = __builtin_amdgcn_perm(t1, t0, 0x07030602u);
+    const uint32_t a23l = __builtin_amdgcn_perm(t3, t2, 0x05010400u);
+    const uint32_t a23h = __builtin_amdgcn_perm(t3, t2, 0x07030602u);
+    const int c0 = 4 * w;
+    st.acc[c0 + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(vpair_to_h4<CODE, false>(a01l, a23l), pop, st.acc[c0 + 0], 0, 0, 0);
+    st.acc[c0 + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vpair_to_h4<CODE, true>(a01l, a23l), pop, st.acc[c0 + 1], 0, 0, 0);
+    st.acc[c0 + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(vpair_to_h4<CODE, false>(a01h, a23h), pop, st.acc[c0 + 2], 0, 0, 0);
+    st.acc[c0 + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(vpair_to_h4<CODE, true>(a01h, a23h), pop, st.acc[c0 + 3], 0, 0, 0);
+  }
+}
+
+// A block whose BS tokens all lie before the sequence end.
+template <int CODE, int D, int BS>
+__device__ __forceinline__ void full_block_step(const Tile8<D, BS>& t, int i, int L,
+                                                const half8v* qop, float cscore, int j,
+                                                SoftmaxState<D>& st) {
+#pragma unroll
+  for (int nt = 0; nt < BS / 16; ++nt)
+    tile_step<CODE, D, BS, false>(t, nt, i * BS + nt * 16, L, qop, cscore, j, st);
+}
+
+// The sequence's last block when it is only partly filled.
+template <int CODE, int D, int BS>
+__device__ __forceinline__ void last_block_step(const Tile8<D, BS>& t, int i, int L,
+                                                const half8v* qop, float cscore, int j,
+                                                SoftmaxState<D>& st) {
+#pragma unroll
+  for (int nt = 0; nt < BS / 16; ++nt) {
+    const int pos0 = i * BS + nt * 16;
+    if (pos0 + 16 <= L)
+      tile_step<CODE, D, BS, false>(t, nt, pos0, L, qop, cscore, j, st);
+    else if (pos0 < L)
+      tile_step<CODE, D, BS, true>(t, nt, pos0, L, qop, cscore, j, st);
+  }
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ void load_query(const uint16_t* qp, float* qf) {
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 8 * u);
+    unpack2<BF16>(w.x, qf[8 * u + 0], qf[8 * u + 1]);
+    unpack2<BF16>(w.y, qf[8 * u + 2], qf[8 * u + 3]);
+    unpack2<BF16>(w.z, qf[8 * u + 4], qf[8 * u + 5]);
+    unpack2<BF16>(w.w, qf[8 * u + 6], qf[8 * u + 7]);
+  }
+}
+
+template <int CODE, int D, int BS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_kernel(DecodeArgs a) {
+  constexpr int NCH = D / 32;   // k-chunks of the score MFMA
+  constexpr int NPV = D / 16;   // output MFMAs (16 d-rows each)
+  constexpr int NBUF = BS == 16 ? 3 : 2;  // blocks in the register ring
+  const int lane = threadIdx.x;
+  const int r = lane & 15, j = lane >> 4;
+  const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x;
+  // lengths beyond the table row (a broken precondition) are cut to it
+  const int L = min(a.context_lens[b], a.max_blocks * BS);
+  const int nblk = (L + BS - 1) / BS;
+  const int i0 = sp * a.split_blocks;
+  if (i0 >= nblk) return;
+  const int i1 = min(i0 + a.split_blocks, nblk);
+  const int ilast = i1 - 1;
+
+  // ---- query: heads g*G + r, elements [j d/4, (j+1) d/4) ----------------
+  const bool hcol = r < a.G;
+  const int h = g * a.G + (hcol ? r : 0);
+  float qf[D / 4];
+  {
+    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + h) * D + j * (D / 4);
+    if (a.q_bf16)
+      load_query<true, D>(qp, qf);
+    else
+      load_query<false, D>(qp, qf);
+  }
+  float qmax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) qmax = fmaxf(qmax, fabsf(qf[e]));
+  qmax = colmax4(qmax);
+  int qe = qmax > 0.0f ? (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 : 0;
+  qe = max(qe, -126);
+  const float qdown = __uint_as_float((uint32_t)(127 - qe) << 23);  // 2^-qe
+  const float qup = __uint_as_float((uint32_t)(127 + qe) << 23);    // 2^qe
+  half8v qop[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qop[c][e] = hcol ? (half_t)(qf[8 * c + e] * qdown) : (half_t)0.0f;
+  const float cscore = hcol ? qup * a.sm_log2 : 0.0f;
+
+  SoftmaxState<D> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NPV; ++c) st.acc[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+
+  // The split's block ids (at most 64) arrive with one vector load: lane k
+  // holds the id of block i0 + k; v_readlane hands each to the scalar unit.
+  // Ids outside the pool (a broken precondition) are clamped to block 0 so
+  // that no load leaves the cache planes.
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
+  const int32_t ids = trow[min(i0 + lane, ilast)];
+  auto bh_of = [&](int i) -> int64_t {
+    const int32_t id = __builtin_amdgcn_readlane(ids, min(i, ilast) - i0);
+    return (int64_t)((id >= 0 && id < a.num_blocks) ? id : 0) * a.H + g;
+  };
+  // blocks [i0, ifull) are complete; a partial last block is handled apart
+  const bool partial = i1 == nblk && (L % BS) != 0;
+  const int ifull = partial ? i1 - 1 : i1;
+  Tile8<D, BS> buf[NBUF];
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u) load_tile8<D, BS>(buf[u], a, bh_of(i0 + u), lane);
+
+  // Steady state: every slot computes one block and refills its buffer with
+  // the block NBUF ahead (clamped to the split's last block, so the load
+  // sequence never branches and the wait counts stay exact).
+  int i = i0;
+  for (; i + NBUF <= ifull; i += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      full_block_step<CODE, D, BS>(buf[u], i + u, L, qop, cscore, j, st);
+      load_tile8<D, BS>(buf[u], a, bh_of(i + u + NBUF), lane);
+    }
+  }
+  // Remainder: fewer than NBUF complete blocks, already in buf[0 ..], then
+  // the partial block, if any, which sits in the next buffer.
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u) {
+    if (i + u < ifull) {
+      full_block_step<CODE, D, BS>(buf[u], i + u, L, qop, cscore, j, st);
+    } else if (i + u == ifull && partial) {
+      last_block_step<CODE, D, BS>(buf[u], i + u, L, qop, cscore, j, st);
+    }
+  }
+
+  // ---- partial results ---------------------------------------------------
+  const float l = colsum4(st.l);
+  if (!hcol) return;
+  const int64_t item = ((int64_t)b * a.Hq + h) * a.num_splits + sp;
+  if (j == 0) {
+    float2 ml = {st.m, l};
+    *reinterpret_cast<float2*>(a.ws_ml + item * 2) = ml;
+  }
+  // acc[c][e] holds output element (d/16) (4 j + e) + c of head r
+  float* dst = a.ws_acc + item * D + j * (D / 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (NPV == 8) {
+      float4v lo = {st.acc[0][e], st.acc[1][e], st.acc[2][e], st.acc[3][e]};
+      float4v hi = {st.acc[4][e], st.acc[5][e], st.acc[6][e], st.acc[7][e]};
+      *reinterpret_cast<float4v*>(dst + 8 * e) = lo;
+      *reinterpret_cast<float4v*>(dst + 8 * e + 4) = hi;
+    } else {
+      float4v v4 = {st.acc[0][e], st.acc[1][e], st.acc[2][e], st.acc[3][e]};
+      *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
+    }
+  }
+}
+
+// Cross-split merge: M = max m_j, out = sum_j 2^(m_j - M) acc_j /
+// sum_j 2^(m_j - M) l_j; a sequence with no tokens gets 0.
+struct ReduceArgs {
+  const float* ws_acc;
+  const float* ws_ml;
+  const int32_t* context_lens;
+  void* out;
+  int32_t out_dtype;
+  int32_t Hq;
+  int32_t BS;
+  int32_t max_blocks;
+  int32_t split_blocks;
+  int32_t num_splits;
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
+  constexpr int EPL = D / 64;  // elements per lane
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int L = min(a.context_lens[b], a.max_blocks * a.BS);
+  const int nblk = (L + a.BS - 1) / a.BS;
+  const int ns = min((nblk + a.split_blocks - 1) / a.split_blocks, a.num_splits);
+  const int64_t base = ((int64_t)b * a.Hq + h) * a.num_splits;
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
+  if (ns > 0) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
+    float den = 0.0f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = a.ws_ml[(base + s) * 2];
+      const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+      den += w * a.ws_ml[(base + s) * 2 + 1];
+      const float* ap = a.ws_acc + (base + s) * D + EPL * lane;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] += w * ap[e];
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] *= inv;
+  }
+  const int64_t ob = ((int64_t)b * a.Hq + h) * D + EPL * lane;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    if (a.out_dtype == KVQ_F32)
+      static_cast<float*>(a.out)[ob + e] = o[e];
+    else if (a.out_dtype == KVQ_F16)
+      static_cast<half_t*>(a.out)[ob + e] = (half_t)o[e];
+    else
+      static_cast<uint16_t*>(a.out)[ob + e] = f32_to_bf16_rne(o[e]);
+  }
+}
+
+template <int CODE, int D, int BS>
+hipError_t launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
+  dim3 grid(a.num_splits, a.H, batch);
+  decode_split_kernel<CODE, D, BS><<<grid, 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
+                      int32_t v_mode) {
+  if (k_code != v_code || k_mode != KVQ_SCALE_TOKEN_SYM || v_mode != KVQ_SCALE_TOKEN_SYM)
+    return false;
+  return k_code == KVQ_CODE_INT8 || k_code == KVQ_CODE_FP8_E4M3;
+}
+
+hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k_codes = static_cast<const uint8_t*>(p.k_codes);
+  a.v_codes = static_cast<const uint8_t*>(p.v_codes);
+  a.k_scale = p.k_scale;
+  a.v_scale = p.v_scale;
+  a.block_tables = p.block_tables;
+  a.context_lens = p.context_lens;
+  a.ws_acc = p.ws_acc;
+  a.ws_ml = p.ws_ml;
+  a.num_blocks = p.num_blocks;
+  a.q_bf16 = p.q_bf16;
+  a.Hq = p.num_q_heads;
+  a.H = p.num_kv_heads;
+  a.G = p.num_q_heads / p.num_kv_heads;
+  a.max_blocks = p.max_blocks_per_seq;
+  a.split_blocks = p.split_blocks;
+  a.num_splits = p.num_splits;
+  a.sm_log2 = p.sm_scale * kLog2e;
+  hipError_t e;
+  const bool fp8 = p.k_code == KVQ_CODE_FP8_E4M3;
+#define KVQ_SPLIT(CODE)                                                              \
+  if (p.head_dim == 128)                                                             \
+    e = p.block_size == 16 ? launch_split<CODE, 128, 16>(a, p.batch, stream)         \
+                           : launch_split<CODE, 128, 32>(a, p.batch, stream);        \
+  else                                                                               \
+    e = p.block_size == 16 ? launch_split<CODE, 64, 16>(a, p.batch, stream)          \
+                           : launch_split<CODE, 64, 32>(a, p.batch, stream);
+  if (fp8) {
+    KVQ_SPLIT(KVQ_CODE_FP8_E4M3)
+  } else {
+    KVQ_SPLIT(KVQ_CODE_INT8)
+  }
+#undef KVQ_SPLIT
+  if (e != hipSuccess) return e;
+  ReduceArgs ra;
+  ra.ws_acc = p.ws_acc;
+  ra.ws_ml = p.ws_ml;
+  ra.context_lens = p.context_lens;
+  ra.out = p.out;
+  ra.out_dtype = p.out_dtype;
+  ra.Hq = p.num_q_heads;
+  ra.BS = p.block_size;
+  ra.max_blocks = p.max_blocks_per_seq;
+  ra.split_blocks = p.split_blocks;
+  ra.num_splits = p.num_splits;
+  dim3 grid(p.num_q_heads, p.batch);
+  if (p.head_dim == 128)
+    decode_reduce_kernel<128><<<grid, 64, 0, stream>>>(ra);
+  else
+    decode_reduce_kernel<64><<<grid, 64, 0, stream>>>(ra);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

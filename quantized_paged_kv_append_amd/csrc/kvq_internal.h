@@ -1,0 +1,90 @@
+// kvq_internal.h -- host-side interface between the C ABI layer
+// (kvq_api.cpp) and the kernel launchers (kvq_*.hip). Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// One side (keys or values) of an append.
+struct AppendSide {
+  const void* src;     // 16-bit rows, token t head h element e at
+                       // src[t * row_stride + h * d + e]
+  int64_t row_stride;  // elements
+  void* codes;
+  float* scale;
+  uint8_t* zero;
+};
+
+struct AppendPlan {
+  AppendSide side[2];  // [0] keys, [1] values
+  const int64_t* slots;
+  const int32_t* stage_rows;
+  void* k_stage;
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t src_bf16;
+  int32_t code[2];
+  int32_t mode[2];
+  int32_t max_seqs;
+  int32_t cu_count;
+};
+
+hipError_t launch_append(const AppendPlan& p, hipStream_t stream);
+
+struct DecodePlan {
+  const void* q;
+  int32_t q_bf16;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t k_code, v_code, k_mode, v_mode;
+  int32_t src_bf16;
+  const void* k_codes;
+  const void* v_codes;
+  const float* k_scale;
+  const float* v_scale;
+  const uint8_t* k_zero;
+  const uint8_t* v_zero;
+  const void* k_stage;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  int32_t split_blocks;  // cache blocks per split
+  int32_t num_splits;    // splits per sequence in the launch grid
+  float sm_scale;
+  void* out;
+  int32_t out_dtype;
+  float* ws_acc;  // [batch][Hq][num_splits][d]
+  float* ws_ml;   // [batch][Hq][num_splits][2]
+};
+
+hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
+bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
+                      int32_t v_mode);
+
+hipError_t launch_pool_init(int32_t* stack, int32_t* top, const int32_t* order,
+                            int64_t n, hipStream_t stream);
+hipError_t launch_blocks_reserve(int32_t* stack, int32_t* top, int64_t capacity,
+                                 int32_t* tables, int32_t max_blocks,
+                                 const int32_t* lens, const int32_t* new_tokens,
+                                 int32_t batch, int32_t bs, int64_t* slots,
+                                 int32_t* lens_out, int32_t* status,
+                                 hipStream_t stream);
+hipError_t launch_blocks_release(int32_t* stack, int32_t* top,
+                                 int64_t capacity, const int32_t* tables,
+                                 int32_t max_blocks, const int32_t* lens,
+                                 const int32_t* mask, int32_t batch, int32_t bs,
+                                 int32_t* lens_out, int32_t* status,
+                                 hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,164 @@
+"""The C-ABI library loads, exports every symbol include/kvq.h declares, and
+its host-only entry points agree with the oracle and the pages' closed forms.
+Argument errors are caught on the host before any launch, so these run
+without a GPU."""
+import ctypes as C
+import json
+import re
+from pathlib import Path
+
+import pytest
+import torch
+
+from oracle import ref
+
+ROOT = Path(__file__).resolve().parents[1]
+kq = pytest.importorskip("quantized_paged_kv_append_amd.kvq")
+
+
+def _declared():
+    text = (ROOT / "include" / "kvq.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 10
+    lib = C.CDLL(kq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kq._SIGS), "binding must cover the header exactly"
+
+
+def test_binding_constants_match_header():
+    text = (ROOT / "include" / "kvq.h").read_text()
+    for name, value in re.findall(r"#define\s+(KVQ_\w+)\s+\(?(-?\d+)\)?", text):
+        assert getattr(kq, name) == int(value), name
+
+
+def test_bytes_per_token_printed_and_oracle():
+    g = json.loads((ROOT / "tests" / "golden" / "bytes_per_token.json").read_text())
+    for bits, code in (("16", "none16"), ("8", "int8"), ("8", "fp8"), ("4", "int4")):
+        L = kq.make_layout(8, 128, 16, code)
+        assert kq.kvq_bytes_per_token(L, 80) == g["bytes_per_token"][bits]
+    combos = [("int8", "token_sym", 16, 0), ("fp8", "token_sym", 32, 0),
+              ("int4", "group_asym", 32, 32), ("int4", "token_sym", 16, 0),
+              ("int8", "channel_block", 16, 0), ("none16", "token_sym", 16, 0)]
+    cmap = {"none16": ref.CODE_NONE16, "int8": ref.CODE_INT8, "fp8": ref.CODE_FP8,
+            "int4": ref.CODE_INT4}
+    mmap = {"token_sym": ref.TOKEN_SYM, "group_asym": ref.GROUP_ASYM,
+            "channel_block": ref.CHANNEL_BLOCK}
+    for code, mode, bs, gs in combos:
+        for H, d in ((8, 128), (2, 64), (5, 64)):
+            L = kq.make_layout(H, d, bs, code, k_mode=mode, group_size=gs)
+            OL = ref.layout(H, d, bs, cmap[code], k_mode=mmap[mode], group_size=gs)
+            for layers in (1, 32, 80):
+                for meta in (0, 1):
+                    assert kq.kvq_bytes_per_token(L, layers, meta) == \
+                        ref.bytes_per_token(OL, layers, meta)
+            for nb, ms in ((1, 0), (37, 3)):
+                assert kq.kvq_cache_plane_bytes(L, nb, ms) == ref.plane_bytes(OL, nb, ms)
+
+
+def test_layout_check_errors():
+    ok = kq.make_layout(8, 128, 16, "int8")
+    assert kq.kvq_layout_check(ok) == kq.KVQ_OK
+    bad = [kq.make_layout(0, 128, 16, "int8"), kq.make_layout(8, 96, 16, "int8"),
+           kq.make_layout(8, 128, 24, "int8")]
+    for L in bad:
+        assert kq.kvq_layout_check(L) == kq.KVQ_ERR_INVALID_ARGUMENT
+    L = kq.make_layout(8, 128, 16, "int8")
+    L.reserved = 1
+    assert kq.kvq_layout_check(L) == kq.KVQ_ERR_INVALID_ARGUMENT
+    L = kq.make_layout(8, 128, 16, "int8")
+    L.k_code = 9
+    assert kq.kvq_layout_check(L) == kq.KVQ_ERR_INVALID_ARGUMENT
+    unsupported = [kq.make_layout(8, 128, 16, "fp8", k_mode="group_asym", group_size=32),
+                   kq.make_layout(8, 128, 16, "int4", k_mode="group_asym", group_size=64),
+                   kq.make_layout(8, 128, 16, "int8", k_mode="token_sym", v_mode="channel_block"),
+                   kq.make_layout(8, 128, 16, "fp8", k_mode="channel_block")]
+    for L in unsupported:
+        assert kq.kvq_layout_check(L) == kq.KVQ_ERR_UNSUPPORTED
+    with pytest.raises(kq.KvqError):
+        kq.kvq_bytes_per_token(ok, 0)
+    assert kq.kvq_status_string(-5) == "KVQ_ERR_OUT_OF_BLOCKS"
+    assert kq.kvq_status_string(42) == "KVQ_UNKNOWN_STATUS"
+
+
+def test_workspace_size_is_pure_and_positive():
+    L = kq.make_layout(8, 128, 16, "fp8")
+    a = kq.kvq_decode_workspace_bytes(L, 16, 64, 32768)
+    assert a == kq.kvq_decode_workspace_bytes(L, 16, 64, 32768) and a > 0
+    assert kq.kvq_decode_workspace_bytes(L, 16, 64, 32768, 8) > a
+    assert kq._lib.kvq_decode_workspace_bytes(C.byref(L), 16, 64, 32768, 65) == \
+        kq.KVQ_ERR_INVALID_ARGUMENT
+    assert kq._lib.kvq_decode_workspace_bytes(C.byref(L), -1, 64, 32768, 0) == \
+        kq.KVQ_ERR_INVALID_ARGUMENT
+
+
+def _fake_cache(L, nb=4):
+    base = 1 << 20  # never dereferenced: the calls below fail their checks first
+    s = kq.kvq_cache()
+    s.k_codes, s.v_codes, s.k_scale, s.v_scale = base, base + 4096, base + 8192, base + 12288
+    s.num_blocks = nb
+    return s
+
+
+def test_append_and_decode_reject_bad_arguments_on_host():
+    L = kq.make_layout(8, 128, 16, "int8")
+    cs = _fake_cache(L)
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+    # misaligned input
+    assert lib.kvq_append(C.byref(L), C.byref(cs), C.c_void_p((1 << 21) + 2), p, 1024, 1024,
+                          4, p, None, None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    # stride shorter than a row
+    assert lib.kvq_append(C.byref(L), C.byref(cs), p, p, 512, 1024, 4, p, None,
+                          None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    # stage rows given for a layout without per-channel keys
+    assert lib.kvq_append(C.byref(L), C.byref(cs), p, p, 1024, 1024, 4, p, p,
+                          None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    # a zero-point plane the layout does not use
+    cz = _fake_cache(L)
+    cz.k_zero = 1 << 22
+    assert lib.kvq_append(C.byref(L), C.byref(cz), p, p, 1024, 1024, 4, p, None,
+                          None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    # nothing to do
+    assert lib.kvq_append(C.byref(L), C.byref(cs), None, None, 0, 0, 0, None, None,
+                          None) == kq.KVQ_OK
+
+    def dec(**kw):
+        a = dict(q=p, q_dtype=kq.KVQ_BF16, batch=2, hq=32, tables=p, maxb=4, lens=p,
+                 maxlen=64, sm=0.0, split=0, out=p, out_dtype=kq.KVQ_F32, ws=p,
+                 wsb=1 << 30)
+        a.update(kw)
+        return lib.kvq_decode_attention(C.byref(L), C.byref(cs), a["q"], a["q_dtype"],
+                                        a["batch"], a["hq"], a["tables"], a["maxb"],
+                                        a["lens"], a["maxlen"], a["sm"], a["split"],
+                                        a["out"], a["out_dtype"], a["ws"], a["wsb"], None)
+    assert dec(hq=30) == kq.KVQ_ERR_INVALID_ARGUMENT           # Hq % H != 0
+    assert dec(hq=8 * 17) == kq.KVQ_ERR_UNSUPPORTED             # group > 16
+    assert dec(q_dtype=kq.KVQ_F32) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert dec(out_dtype=7) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert dec(maxlen=65) == kq.KVQ_ERR_INVALID_ARGUMENT        # > maxb * bs
+    assert dec(split=65) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert dec(sm=float("nan")) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert dec(wsb=16) == kq.KVQ_ERR_WORKSPACE_TOO_SMALL
+    assert dec(tables=None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert dec(batch=0) == kq.KVQ_OK
+    L4 = kq.make_layout(8, 128, 32, "int4", k_mode="group_asym", group_size=32)
+    assert L4 is not None
+
+
+def test_pool_calls_reject_bad_arguments_on_host():
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+    assert lib.kvq_pool_init(None, p, None, 16, None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_pool_init(p, p, None, 0, None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_blocks_reserve(p, p, 16, p, 4, p, p, 2, 16, p, None, None,
+                                  None) == kq.KVQ_ERR_INVALID_ARGUMENT   # no status
+    assert lib.kvq_blocks_reserve(p, p, 16, None, 4, p, p, 2, 16, p, None, p,
+                                  None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_blocks_release(p, p, 16, p, 4, p, None, 2, 16, None, p,
+                                  None) == kq.KVQ_ERR_INVALID_ARGUMENT

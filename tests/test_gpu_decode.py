@@ -1,0 +1,152 @@
+"""kvq_decode_attention on the GPU against the oracle (fp64 attention): caches
+built by the oracle and copied to the device, so decode is tested on its own.
+Tolerance |gpu - oracle| <= 2e-3 + 1e-3 |oracle| elementwise."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import ref
+from _util import DT, OracleSeqs, bits, oracle_layout
+from _gpu_util import (DEV, assert_decode_close, decode_gpu, lib_layout, need_gpu,
+                       upload)
+
+pytestmark = pytest.mark.gpu
+
+LENS = (37, 80, 5, 1, 16, 0, 17, 300, 15, 33)
+
+
+def _setup(code="int8", d=128, bs=16, G=4, H=2, src="bfloat16", lens=LENS, seed=0,
+           permuted=True, kscale=1.0, name="tiny"):
+    w = workloads.get(name, k_code=code, v_code=code, k_mode="token_sym",
+                      v_mode="token_sym", src_dtype=src, head_dim=d, block_size=bs,
+                      num_kv_heads=H, num_q_heads=G * H, batch=len(lens),
+                      n_outliers=2, outlier_factor=8.0)
+    L, LL = oracle_layout(w), lib_layout(w)
+    lens = np.asarray(lens, np.int32)
+    nb = workloads.pool_blocks(lens, bs) + 3
+    order = workloads.pool_order(nb, seed=seed, permuted=permuted)
+    maxb = int(lens.max()) // bs + 2
+    s = OracleSeqs(L, nb, len(lens), maxb, order=order)
+    k, v = workloads.kv_rows(w, int(lens.sum()), seed=seed)
+    if kscale != 1.0:
+        k = (k.float() * kscale).to(w.torch_dtype)
+    s.append(k, v, lens)
+    q = workloads.queries(w, seed=seed)
+    return w, L, LL, s, q
+
+
+def _run(w, L, LL, s, q, out_dtype=torch.float32, sm_scale=0.0, split_blocks=0):
+    exp = ref.decode(L, s.cache, bits(q), DT[w.src_dtype], s.tables, s.lens,
+                     sm_scale=sm_scale, threads=8)
+    gc = upload(s.cache, LL)
+    got = decode_gpu(LL, gc, q.to(DEV), torch.from_numpy(s.tables).to(DEV),
+                     torch.from_numpy(s.lens).to(DEV), int(s.lens.max()), out_dtype,
+                     sm_scale, split_blocks)
+    return got, exp
+
+
+@pytest.mark.parametrize("code", ["int8", "fp8"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 16), (128, 32), (64, 32)])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_decode_matches_oracle(code, d, bs, G):
+    need_gpu()
+    w, L, LL, s, q = _setup(code, d, bs, G)
+    got, exp = _run(w, L, LL, s, q)
+    assert_decode_close(got, exp, f"{code} d{d} bs{bs} G{G}")
+    assert (got[5] == 0).all()           # empty context
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 5, 64])
+def test_decode_split_counts(split):
+    need_gpu()
+    w, L, LL, s, q = _setup("fp8", lens=(700, 1, 250, 64, 0, 333), G=8)
+    got, exp = _run(w, L, LL, s, q, split_blocks=split)
+    assert_decode_close(got, exp, f"split {split}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("src", ["float16", "bfloat16"])
+def test_decode_output_and_query_dtypes(out_dtype, src):
+    need_gpu()
+    w, L, LL, s, q = _setup("int8", src=src)
+    got, exp = _run(w, L, LL, s, q, out_dtype=out_dtype)
+    assert_decode_close(got, exp, f"{src}->{out_dtype}")
+
+
+def test_decode_custom_scale_and_peaked_softmax():
+    need_gpu()
+    w, L, LL, s, q = _setup("int8", kscale=4.0)
+    got, exp = _run(w, L, LL, s, q, sm_scale=0.4)
+    assert_decode_close(got, exp, "sm 0.4, keys x4")
+
+
+def test_decode_tiny_workload():
+    """The tiny workload exactly: 1 sequence x 256 tokens, 4 query / 2 KV heads,
+    d = 64, fp16, 2 key outlier channels x10, INT8 per-token scales, block 16."""
+    need_gpu()
+    w = workloads.get("tiny")
+    L, LL = oracle_layout(w), lib_layout(w)
+    lens = workloads.lengths(w)
+    nb = workloads.pool_blocks(lens, w.block_size)
+    s = OracleSeqs(L, nb, 1, nb, order=workloads.pool_order(nb))
+    k, v = workloads.kv_rows(w, int(lens.sum()))
+    s.append(k, v, lens)
+    q = workloads.queries(w)
+    got, exp = _run(w, L, LL, s, q)
+    assert_decode_close(got, exp, "tiny")
+
+
+def test_decode_paged_is_bit_identical_to_contiguous_and_permuted():
+    need_gpu()
+    outs = []
+    for permuted, seed_order in ((False, 0), (True, 1), (True, 2)):
+        w, L, LL, s, q = _setup("fp8", G=8, permuted=permuted, seed=0)
+        if permuted:   # same inputs, a different physical placement
+            nb = s.cache.num_blocks
+            s2 = OracleSeqs(L, nb, len(LENS), s.tables.shape[1],
+                            order=workloads.pool_order(nb, seed=seed_order))
+            k, v = workloads.kv_rows(w, int(np.sum(LENS)), seed=0)
+            s2.append(k, v, np.asarray(LENS, np.int32))
+            s = s2
+        gc = upload(s.cache, LL)
+        got = decode_gpu(LL, gc, q.to(DEV), torch.from_numpy(s.tables).to(DEV),
+                         torch.from_numpy(s.lens).to(DEV), int(s.lens.max()))
+        outs.append(got.cpu())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_decode_gqa_equals_mha_with_duplicated_heads():
+    need_gpu()
+    w, L, LL, s, q = _setup("int8", G=4, H=2, lens=(90, 17, 300))
+    got_gqa, _ = _run(w, L, LL, s, q)
+    w8 = workloads.get("tiny", k_code="int8", v_code="int8", src_dtype="bfloat16",
+                       head_dim=128, block_size=16, num_kv_heads=8, num_q_heads=8,
+                       batch=3)
+    L8, LL8 = oracle_layout(w8), lib_layout(w8)
+    lens = np.array([90, 17, 300], np.int32)
+    nb = workloads.pool_blocks(lens, 16) + 3
+    s8 = OracleSeqs(L8, nb, 3, 21)
+    k, v = workloads.kv_rows(w, int(lens.sum()), seed=0)
+    s8.append(k.repeat_interleave(4, 1), v.repeat_interleave(4, 1), lens)
+    gc = upload(s8.cache, LL8)
+    got_mha = decode_gpu(LL8, gc, q.to(DEV), torch.from_numpy(s8.tables).to(DEV),
+                         torch.from_numpy(s8.lens).to(DEV), 300)
+    assert torch.allclose(got_gqa, got_mha, atol=1e-5, rtol=1e-5)
+
+
+def test_decode_llama3_8b_workload_full():
+    """The Llama-3-8B layer workload at full size (64 sequences, lengths
+    uniform in [1024, 8192], 32 q / 8 KV heads, INT8), every output checked."""
+    need_gpu()
+    w = workloads.get("llama3_8b")
+    L, LL = oracle_layout(w), lib_layout(w)
+    lens = workloads.lengths(w)
+    nb = workloads.pool_blocks(lens, w.block_size)
+    s = OracleSeqs(L, nb, w.batch, int(lens.max()) // 16 + 1, order=workloads.pool_order(nb))
+    k, v = workloads.kv_rows(w, int(lens.sum()))
+    s.append(k, v, lens)
+    q = workloads.queries(w)
+    got, exp = _run(w, L, LL, s, q)
+    err = assert_decode_close(got, exp, "llama3_8b")
+    print(f"llama3_8b max err {err:.2e}")

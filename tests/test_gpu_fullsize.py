@@ -1,0 +1,105 @@
+"""Full-size workloads in the benchmark's launch configuration: device pool ->
+quantize-on-append -> decode, for one layer. The oracle runs its own pool
+mirror from the same initial order (its tables are checked equal to the
+device's, never read from it), appends the sampled sequences' rows and decodes
+them; the device output and planes must match on those samples."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import ref
+from _util import DT, bits, oracle_layout
+from _gpu_util import DEV, assert_decode_close, decode_gpu, kq, lib_layout, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _populate(w, seed=0, chunk=1 << 20):
+    """What bench.py does for one layer: pool init (permuted order), one
+    reservation for every sequence's context, K/V generated on the device and
+    appended in chunks."""
+    LL = lib_layout(w)
+    lens = workloads.lengths(w, seed)
+    nb = workloads.pool_blocks(lens, w.block_size, headroom_tokens=w.block_size)
+    maxb = int(lens.max()) // w.block_size + 2
+    order = workloads.pool_order(nb, seed)
+    stack = torch.empty(nb, dtype=torch.int32, device=DEV)
+    top = torch.empty(1, dtype=torch.int32, device=DEV)
+    kq.kvq_pool_init(stack, top, torch.from_numpy(order).to(DEV))
+    tables = torch.full((w.batch, maxb), -1, dtype=torch.int32, device=DEV)
+    ctx = torch.zeros(w.batch, dtype=torch.int32, device=DEV)
+    T = int(lens.sum())
+    slots = torch.empty(T, dtype=torch.int64, device=DEV)
+    status = torch.empty(1, dtype=torch.int32, device=DEV)
+    kq.kvq_blocks_reserve(stack, top, tables, ctx, torch.from_numpy(lens).to(DEV),
+                          w.block_size, slots, status, ctx)
+    cache = kq.PagedCache(LL, nb, w.batch, device=DEV)
+    k, v = workloads.kv_rows(w, T, seed=seed, device=DEV)
+    for t0 in range(0, T, chunk):
+        kq.kvq_append(LL, cache, k[t0:t0 + chunk], v[t0:t0 + chunk], slots[t0:t0 + chunk])
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    return dict(LL=LL, lens=lens, nb=nb, maxb=maxb, order=order, tables=tables, ctx=ctx,
+                cache=cache, k=k, v=v)
+
+
+def _check(w, P, sample, seed=0):
+    L = oracle_layout(w)
+    lens, nb = P["lens"], P["nb"]
+    # oracle pool mirror
+    ostack, otop = ref.pool_init(nb, P["order"])
+    otables = np.full((w.batch, P["maxb"]), -1, np.int32)
+    oslots, st = ref.blocks_reserve(ostack, otop, otables, np.zeros(w.batch, np.int32),
+                                    lens, w.block_size)
+    assert st == 0
+    assert np.array_equal(otables, P["tables"].cpu().numpy())
+    # oracle append of the sampled sequences only
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    idx = np.concatenate([starts[b] + np.arange(lens[b]) for b in sample]).astype(np.int64)
+    hc = ref.HostCache(L, nb)
+    ki = bits(P["k"][torch.from_numpy(idx).to(DEV)]).reshape(len(idx), -1)
+    vi = bits(P["v"][torch.from_numpy(idx).to(DEV)]).reshape(len(idx), -1)
+    ref.append(L, hc, ki, vi, oslots[idx])
+    # planes of the sampled sequences' blocks, bytewise
+    H, bs = w.num_kv_heads, w.block_size
+    blocks = np.concatenate([otables[b, :(lens[b] + bs - 1) // bs] for b in sample])
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
+        g = P["cache"].planes[name]
+        if g is None:
+            continue
+        per_block = g.numel() // nb
+        gb = g.view(nb, per_block)[torch.from_numpy(blocks).long().to(DEV)].cpu().numpy()
+        hb = hc.planes[name].reshape(nb, per_block)[blocks]
+        gb, hb = gb.reshape(len(blocks), H, bs, -1), hb.reshape(len(blocks), H, bs, -1)
+        o = 0
+        for b in sample:   # a partial last block: compare its written rows only
+            n = (lens[b] + bs - 1) // bs
+            tail = lens[b] - (n - 1) * bs
+            assert np.array_equal(gb[o:o + n - 1], hb[o:o + n - 1]), (name, b)
+            assert np.array_equal(gb[o + n - 1, :, :tail], hb[o + n - 1, :, :tail]), (name, b)
+            o += n
+    # decode: every query head of the sampled sequences
+    q = workloads.queries(w, seed=seed, device=DEV)
+    got = decode_gpu(P["LL"], P["cache"], q, P["tables"], P["ctx"], int(lens.max()))
+    exp = ref.decode(L, hc, bits(q[torch.as_tensor(sample, device=DEV)]), DT[w.src_dtype],
+                     otables[sample], lens[sample], threads=16)
+    return assert_decode_close(got[torch.as_tensor(sample, device=DEV)], exp, w.name)
+
+
+def test_llama3_70b_one_layer_fp8():
+    need_gpu()
+    w = workloads.get("llama3_70b")
+    P = _populate(w)
+    err = _check(w, P, sample=[0, 9, 15])
+    print(f"llama3_70b layer: max err {err:.2e}")
+
+
+def test_llama3_8b_layer_int8():
+    need_gpu()
+    w = workloads.get("llama3_8b")
+    P = _populate(w)
+    lens = P["lens"]
+    sample = [int(np.argmax(lens)), int(np.argmin(lens)), 7, 33]
+    err = _check(w, P, sample=sample)
+    print(f"llama3_8b: max err {err:.2e}")

@@ -1,0 +1,78 @@
+"""The device block pool against the oracle's pool: identical stacks, tops,
+block tables, slot mappings, lengths and status words, step after step."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from _gpu_util import DEV, kq, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+class GpuPool:
+    def __init__(self, n, B, maxb, order):
+        self.stack = torch.empty(n, dtype=torch.int32, device=DEV)
+        self.top = torch.empty(1, dtype=torch.int32, device=DEV)
+        kq.kvq_pool_init(self.stack, self.top,
+                         None if order is None else torch.from_numpy(order).to(DEV))
+        self.tables = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+        self.status = torch.full((1,), 99, dtype=torch.int32, device=DEV)
+
+
+@pytest.mark.parametrize("B,bs,n", [(5, 16, 64), (300, 16, 5000), (2500, 32, 40000)])
+def test_pool_steps_match_oracle(B, bs, n):
+    need_gpu()
+    rng = np.random.default_rng(B)
+    maxb = 96
+    order = rng.permutation(n).astype(np.int32)
+    gp = GpuPool(n, B, maxb, order)
+    ostack, otop = ref.pool_init(n, order)
+    otables = np.full((B, maxb), -1, np.int32)
+    lens = np.zeros(B, np.int32)
+    glens = torch.zeros(B, dtype=torch.int32, device=DEV)
+    saw_fail = False
+    for step in range(12):
+        if step % 4 == 3:
+            mask = (rng.random(B) < 0.3).astype(np.int32)
+            olens = lens.copy()
+            ost = ref.blocks_release(ostack, otop, otables, olens, mask, bs, olens)
+            kq.kvq_blocks_release(gp.stack, gp.top, gp.tables, glens,
+                                  torch.from_numpy(mask).to(DEV), bs, gp.status, glens)
+            lens = olens
+        else:
+            big = step == 2
+            new = rng.integers(0, 200 if big else 40, size=B).astype(np.int32)
+            if big and B < 100:
+                new[:] = 500          # forces exhaustion of the small pool
+            olens = np.zeros(B, np.int32)
+            oslots, ost = ref.blocks_reserve(ostack, otop, otables, lens, new, bs, olens)
+            gslots = torch.full((int(new.sum()),), -7, dtype=torch.int64, device=DEV)
+            kq.kvq_blocks_reserve(gp.stack, gp.top, gp.tables, glens,
+                                  torch.from_numpy(new).to(DEV), bs, gslots, gp.status, glens)
+            torch.cuda.synchronize()
+            assert np.array_equal(gslots.cpu().numpy(), oslots), step
+            if ost == 0:
+                lens = olens
+            else:
+                saw_fail = True
+        torch.cuda.synchronize()
+        assert int(gp.status.item()) == ost, step
+        assert int(gp.top.item()) == int(otop[0]), step
+        assert np.array_equal(gp.stack.cpu().numpy(), ostack), step
+        assert np.array_equal(gp.tables.cpu().numpy(), otables), step
+        assert np.array_equal(glens.cpu().numpy(), lens), step
+    if B < 100:
+        assert saw_fail
+
+
+def test_pool_release_overflow_changes_nothing():
+    need_gpu()
+    gp = GpuPool(4, 1, 4, None)
+    tables = torch.zeros((1, 4), dtype=torch.int32, device=DEV)
+    lens = torch.full((1,), 16, dtype=torch.int32, device=DEV)
+    kq.kvq_blocks_release(gp.stack, gp.top, tables, lens,
+                          torch.ones(1, dtype=torch.int32, device=DEV), 16, gp.status, lens)
+    torch.cuda.synchronize()
+    assert int(gp.status.item()) == kq.kvq.KVQ_ERR_OUT_OF_BLOCKS
+    assert int(gp.top.item()) == 4 and int(lens.item()) == 16
