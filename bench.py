@@ -1,0 +1,287 @@
+"""Decode-step benchmark of the quantized paged KV cache on one MI355X.
+
+One step is one pass of the whole hot path over a batch: the device pool
+reserves a slot for one new token per sequence, then for every layer the new
+token's K/V rows are quantized into the cache (kvq_append) and decode
+attention runs over the whole quantized context (kvq_decode_attention: split
+kernel + cross-split reduce). The default workload is the Llama-3-70B KV shape
+with all 80 layers resident: 16 sequences x 32768 tokens, 64 query / 8 KV
+heads, d = 128, FP8 E4M3 codes with fp32 per-token-per-head scales, block 16,
+bf16 inputs (synthetic, seeded; see workloads.py).
+
+Printed: one JSON line with the decode KV GB/s over the step (value), the
+split+reduce launch durations measured with HIP events on the launch stream
+(roofline), the bulk-append throughput measured while the cache is populated,
+and the CPU oracle timed on a bounded sample of the same workload
+(cpu_baseline).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_70b", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--layers", type=int, default=0, help="0 = the workload's own count")
+    ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--identity-pool", action="store_true",
+                    help="blocks in order instead of a seeded permutation")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    return ap.parse_args()
+
+
+def kv_bytes_per_token_head(w):
+    """Algorithmic bytes decode reads per (token, KV head, layer): key and
+    value codes plus their scales (and zero points)."""
+    bits = {"int8": 8, "fp8": 8, "int4": 4, "none16": 16}
+    d = w.head_dim
+    total = 0.0
+    for code, mode in ((w.k_code, w.k_mode), (w.v_code, w.v_mode)):
+        total += d * bits[code] / 8
+        if code == "none16":
+            continue
+        if mode == "token_sym":
+            total += 4
+        elif mode == "group_asym":
+            total += (d // w.group_size) * 5
+        else:  # per-channel scales amortized over a block
+            total += d * 4 / w.block_size
+    return total
+
+
+def append_bytes_per_token(w):
+    """Algorithmic bytes of a bulk append per layer-token: 16-bit K and V rows
+    in, codes and metadata out, plus the 8-byte slot."""
+    return w.num_kv_heads * (2 * w.head_dim * 2 + kv_bytes_per_token_head(w)) + 8
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import quantized_paged_kv_append_amd as kq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    w = workloads.get(args.workload)
+    layers = args.layers or w.layers
+    LL = kq.make_layout(w.num_kv_heads, w.head_dim, w.block_size, w.k_code, w.v_code,
+                        w.k_mode, w.v_mode, w.group_size, w.torch_dtype)
+    lens = workloads.lengths(w)
+    B, Hq, H, d, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    new_per_step = w.new_tokens
+    total_steps = args.warmup + args.steps
+    headroom = new_per_step * total_steps
+    nb = workloads.pool_blocks(lens, bs, headroom_tokens=headroom + bs)
+    maxb = (int(lens.max()) + headroom) // bs + 2
+    max_ctx = int(lens.max()) + headroom
+
+    # ---- pool and the prompt's placement ----------------------------------
+    order = torch.from_numpy(workloads.pool_order(nb, permuted=not args.identity_pool)).to(dev)
+    stack = torch.empty(nb, dtype=torch.int32, device=dev)
+    top = torch.empty(1, dtype=torch.int32, device=dev)
+    kq.kvq_pool_init(stack, top, order)
+    tables = torch.full((B, maxb), -1, dtype=torch.int32, device=dev)
+    ctx = torch.zeros(B, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    T0 = int(lens.sum())
+    slots0 = torch.empty(T0, dtype=torch.int64, device=dev)
+    kq.kvq_blocks_reserve(stack, top, tables, ctx, torch.from_numpy(lens).to(dev), bs,
+                          slots0, status, ctx)
+    stage_rows0 = None
+    if w.k_mode == "channel_block":
+        stage_rows0 = torch.from_numpy(np.repeat(np.arange(B, dtype=np.int32), lens)).to(dev)
+
+    # ---- populate every layer (bulk append, timed per call) ---------------
+    caches = []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    append_ms = 0.0
+    chunk = 1 << 19
+    for layer in range(layers):
+        cache = kq.PagedCache(LL, nb, B if w.k_mode == "channel_block" else 0, device=dev)
+        for c0 in range(0, T0, chunk):
+            n = min(chunk, T0 - c0)
+            k, v = workloads.kv_rows(w, n, layer=layer, device=dev, chunk=c0 // chunk)
+            ev[0].record(stream)
+            kq.kvq_append(LL, cache, k, v, slots0[c0:c0 + n],
+                          None if stage_rows0 is None else stage_rows0[c0:c0 + n])
+            ev[1].record(stream)
+            ev[1].synchronize()
+            append_ms += ev[0].elapsed_time(ev[1])
+            del k, v
+        caches.append(cache)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "pool reservation for the prompt failed"
+    append_tok_s = T0 * layers / (append_ms / 1e3)
+    append_gbs = append_tok_s * append_bytes_per_token(w) / 1e9
+
+    # ---- per-step inputs: new K/V rows and queries for every layer ---------
+    Tn = B * new_per_step
+    new_kv = [workloads.kv_rows(w, Tn, layer=layer, device=dev, chunk=999) for layer in range(layers)]
+    qs = [workloads.queries(w, device=dev, layer=layer) for layer in range(layers)]
+    new_tok = torch.full((B,), new_per_step, dtype=torch.int32, device=dev)
+    slots = torch.empty(Tn, dtype=torch.int64, device=dev)
+    stage_rows = None
+    if w.k_mode == "channel_block":
+        stage_rows = torch.from_numpy(np.repeat(np.arange(B, dtype=np.int32), new_per_step)).to(dev)
+    out = torch.empty((B, Hq, d), dtype=w.torch_dtype, device=dev)
+    ws = torch.empty(kq.kvq_decode_workspace_bytes(LL, B, Hq, max_ctx, args.split_blocks),
+                     dtype=torch.uint8, device=dev)
+    dec_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(layers)] for _ in range(args.steps)]
+
+    def step(evs=None):
+        kq.kvq_blocks_reserve(stack, top, tables, ctx, new_tok, bs, slots, status, ctx)
+        for layer in range(layers):
+            k, v = new_kv[layer]
+            kq.kvq_append(LL, caches[layer], k, v, slots, stage_rows)
+            if evs is not None:
+                evs[layer][0].record(stream)
+            kq.kvq_decode_attention(LL, caches[layer], qs[layer], tables, ctx, max_ctx, out,
+                                    ws, split_blocks=args.split_blocks)
+            if evs is not None:
+                evs[layer][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ctx_before = ctx.cpu().numpy().astype(np.int64)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dec_ms = []
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    wall0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(dec_ev[s_])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    # per-launch decode durations (events recorded on the launch stream)
+    dec_ms = [a.elapsed_time(b) for evs in dec_ev for a, b in evs]
+    wall = time.perf_counter() - wall0
+    assert int(status.item()) == 0, "pool reservation during the steps failed"
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+
+    # context attended at each timed step: before + new tokens of that step
+    ctx_tokens = [(ctx_before + new_per_step * (s + 1)).sum() for s in range(args.steps)]
+    bpth = kv_bytes_per_token_head(w)
+    kv_bytes_step = float(np.mean(ctx_tokens)) * H * bpth * layers
+    value = kv_bytes_step / (step_ms / 1e3) / 1e9
+    dec_avg_ms = float(np.mean(dec_ms))
+    dec_bytes_launch = float(np.mean(ctx_tokens)) * H * bpth
+    achieved = dec_bytes_launch / (dec_avg_ms / 1e3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, lens, args)
+
+    line = {
+        "metric": "decode-attn KV GB/s (% of 8 TB/s HBM) + append tok/s, INT8/FP8/INT4",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 codes, fp16 MFMA / fp32 accumulate" if w.k_code == "fp8" else w.k_code,
+        "data": "synthetic (seeded N(0,1) K/V/q with key outlier channels; workloads.py)",
+        "config": {
+            "workload": w.name, "layers": layers, "batch": B, "context": int(lens.max()),
+            "num_q_heads": Hq, "num_kv_heads": H, "head_dim": d, "block_size": bs,
+            "k_code": w.k_code, "v_code": w.v_code, "k_mode": w.k_mode, "v_mode": w.v_mode,
+            "new_tokens_per_step": new_per_step, "pool": "identity" if args.identity_pool else "permuted",
+            "split_blocks": args.split_blocks or "auto",
+        },
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "kv_bytes_per_step": kv_bytes_step,
+        "decode_launch_ms": round(dec_avg_ms, 5),
+        "append_tok_s": round(append_tok_s, 1),
+        "append_GBps": round(append_gbs, 2),
+        "append_bytes_per_token": append_bytes_per_token(w),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": "decode_split_kernel + decode_reduce_kernel (one kvq_decode_attention)",
+            "bytes_per_launch": dec_bytes_launch,
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line))
+
+
+def cpu_baseline(w, lens, args):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    layer 0, the first few sequences, every query head. Its own append builds
+    its cache from host copies of the same seeded inputs (the benchmark's
+    device results are never read), then its decode is timed."""
+    from oracle import ref
+    import ctypes
+
+    cmap = {"none16": ref.CODE_NONE16, "int8": ref.CODE_INT8, "fp8": ref.CODE_FP8,
+            "int4": ref.CODE_INT4}
+    mmap = {"token_sym": ref.TOKEN_SYM, "group_asym": ref.GROUP_ASYM,
+            "channel_block": ref.CHANNEL_BLOCK}
+    OL = ref.layout(w.num_kv_heads, w.head_dim, w.block_size, cmap[w.k_code], cmap[w.v_code],
+                    mmap[w.k_mode], mmap[w.v_mode], w.group_size,
+                    ref.BF16 if w.src_dtype == "bfloat16" else ref.F16)
+    nseq = min(args.cpu_sample_seqs, w.batch)
+    sl = lens[:nseq].astype(np.int32)
+    nb = workloads.pool_blocks(sl, w.block_size)
+    stack, top = ref.pool_init(nb)
+    tables = np.full((nseq, nb), -1, np.int32)
+    slots, st = ref.blocks_reserve(stack, top, tables, np.zeros(nseq, np.int32), sl, w.block_size)
+    hc = ref.HostCache(OL, nb, nseq)
+    T = int(sl.sum())
+    T0 = int(lens.sum())
+    chunk = 1 << 19
+    rows = np.repeat(np.arange(nseq, dtype=np.int32), sl)
+    for c0 in range(0, T, chunk):
+        # the same draws as the device populate of layer 0 (same chunk sizes)
+        n_gen = min(chunk, T0 - c0)
+        n = min(chunk, T - c0)
+        k, v = workloads.kv_rows(w, n_gen, layer=0, device="cuda:0", chunk=c0 // chunk)
+        kb = k[:n].cpu().contiguous().view(torch.int16).numpy().view(np.uint16).reshape(n, -1)
+        vb = v[:n].cpu().contiguous().view(torch.int16).numpy().view(np.uint16).reshape(n, -1)
+        del k, v
+        ref.append(OL, hc, kb, vb, slots[c0:c0 + n], rows[c0:c0 + n])
+    q = workloads.queries(w, device="cuda:0", layer=0)[:nseq]
+    qb = q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    threads = args.cpu_threads or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    ref.decode(OL, hc, qb, ref.BF16 if w.src_dtype == "bfloat16" else ref.F16, tables, sl,
+               threads=threads)
+    dt = time.perf_counter() - t0
+    kv_bytes = float(sl.sum()) * w.num_kv_heads * kv_bytes_per_token_head(w)
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0 of {w.name}: decode of sequences 0..{nseq - 1} "
+                      f"({int(sl.sum())} cached tokens x {w.num_kv_heads} KV heads, all "
+                      f"{w.num_q_heads} query heads), fp64 attention, {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

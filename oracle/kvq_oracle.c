@@ -68,25 +68,34 @@ float orc_e4m3_value(uint8_t c) {
   return (float)(sign ? -v : v);
 }
 
+/* Values of the 127 non-negative finite codes, filled once from
+ * orc_e4m3_value. */
+static double e4m3_table[127];
+static pthread_once_t e4m3_once = PTHREAD_ONCE_INIT;
+static void e4m3_fill(void) {
+  for (int c = 0; c < 127; ++c) e4m3_table[c] = orc_e4m3_value((uint8_t)c);
+}
+
 /* Nearest E4M3 value to y, ties to the even code (the code's last bit is the
  * mantissa's last bit), magnitudes above 448 saturate to 448, the sign is kept
  * (so -0 and negatives that round to zero give 0x80). Search over the 127
  * non-negative finite codes, whose values increase with the code. */
 uint8_t orc_e4m3_encode(float y) {
+  pthread_once(&e4m3_once, e4m3_fill);
   uint8_t sign = signbit(y) ? 0x80 : 0x00;
   double a = fabs((double)y);
   if (a >= 448.0) return sign | 0x7E;
   int lo = 0, hi = 126; /* largest k with value(k) <= a */
   while (lo < hi) {
     int mid = (lo + hi + 1) / 2;
-    if ((double)orc_e4m3_value((uint8_t)mid) <= a)
+    if (e4m3_table[mid] <= a)
       lo = mid;
     else
       hi = mid - 1;
   }
   int k = lo;
-  double below = orc_e4m3_value((uint8_t)k);
-  double above = orc_e4m3_value((uint8_t)(k + 1));
+  double below = e4m3_table[k];
+  double above = e4m3_table[k + 1];
   double twice = 2.0 * a, mid_sum = below + above; /* both exact in double */
   int pick;
   if (twice < mid_sum)

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
     const float s = amax == 0.0f ? 1.0f : div_rn(amax, kQmax);
     const float inv = div_rn(1.0f, s);
     uint32_t c[8];
-    bool tie = false;
+    bool tie = recip_unsafe(s);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float y = x[i] * inv;
@@ -181,6 +181,7 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
       amax = group_max<RL>(amax);
       const float s = amax == 0.0f ? 1.0f : div_rn(amax, 7.0f);
       const float inv = div_rn(1.0f, s);
+      tie = recip_unsafe(s);
 #pragma unroll
       for (int i = 0; i < NS; ++i)
 #pragma unroll
@@ -236,6 +237,7 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
         sg[i] = __shfl(so, row_lane0 + i, kWave);
         ig[i] = __shfl(invo, row_lane0 + i, kWave);
         zg[i] = __shfl(zo, row_lane0 + i, kWave);
+        tie |= recip_unsafe(sg[i]);
       }
 #pragma unroll
       for (int i = 0; i < NS; ++i)
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(256) void chan_complete_kernel(ChanArgs a) {
       for (int c = 0; c < CPL; ++c) {
         const float y = x[o][c] * inv[c];
         float r = rne(y);
-        if (near_half(y, r)) r = rne(div_rn(x[o][c], s[c]));
+        if (near_half(y, r) || recip_unsafe(s[c])) r = rne(div_rn(x[o][c], s[c]));
         q[c] = (int)fminf(fmaxf(r, -127.0f), 127.0f);
       }
       if constexpr (CPL == 2) {

@@ -71,6 +71,13 @@ __device__ __forceinline__ bool near_half(float y, float r) {
   return fabsf(y - r) > 0.5f - 6.103515625e-05f;  // 1/2 - 2^-14
 }
 
+// The bound above needs inv = fl(1/s) to be a normal number with relative
+// error 2^-24, i.e. s in [2^-126, 2^126]. Outside that range (scales of
+// near-denormal rows, where 1/s overflows) the exact quotient is used.
+__device__ __forceinline__ bool recip_unsafe(float s) {
+  return !(s >= 1.17549435e-38f && s <= 8.50705917e+37f);
+}
+
 // ---- OCP E4M3 encoding of a binary32 value ------------------------------
 // Nearest E4M3 value, ties to even mantissa, magnitudes above 448 saturate to
 // 448, sign kept (0x80 for -0 and for negatives that round to zero).

@@ -115,7 +115,8 @@ def test_append_every_16bit_input_at_unit_scale(code, anchor, src):
     kq.kvq_append(LL, gc, k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV))
     torch.cuda.synchronize()
     assert planes_equal(gc, hc) == []
-    s = gc.planes["k_scale"].view(torch.float32).cpu()
+    s = gc.planes["k_scale"].view(torch.float32).cpu().reshape(nb, 2, 16)
+    s = s.permute(0, 2, 1).reshape(-1, 2)[:T]        # slot order, both heads
     assert (s == 1.0).all()
 
 
