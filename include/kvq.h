@@ -224,7 +224,7 @@ kvq_status kvq_append(const kvq_layout* layout, const kvq_cache* cache,
                       void* stream);
 
 /* Device workspace bytes kvq_decode_attention needs for these sizes and this
- * split_blocks (1..64, or 0 = the library's own choice), or a negative
+ * split_blocks (1..256, or 0 = the library's own choice), or a negative
  * kvq_status. */
 int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch,
                                    int32_t num_q_heads, int32_t max_context_len,
@@ -238,7 +238,7 @@ int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch,
  *                 over, 0 <= len <= max_context_len <= max_blocks_per_seq*bs.
  *  max_context_len host bound on context_lens, sizes the launch.
  *  sm_scale       score scale; 0 means 1/sqrt(d).
- *  split_blocks   cache blocks per split-K chunk, 1..64; 0 lets the library
+ *  split_blocks   cache blocks per split-K chunk, 1..256; 0 lets the library
  *                 choose.
  *  out            device [batch][num_q_heads][d] in out_dtype (F32, F16 or
  *                 BF16), RNE-rounded from fp32.

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 
 #include "kvq.h"
@@ -12,13 +14,14 @@
 
 namespace {
 
-// Work items (sequence x KV head x split) the split planner aims for: 16 per
-// compute unit of an MI355X (256 CUs). A constant, so that the workspace size
-// is a pure function of the arguments.
-constexpr int64_t kTargetItems = 4096;
+// Work items (sequence x KV head x split, one four-wave workgroup each) the
+// split planner aims for: four per compute unit of an MI355X (256 CUs). A
+// constant, so that the workspace size is a pure function of the arguments.
+constexpr int64_t kTargetItems = 1024;
 constexpr int64_t kMinSplitTokens = 128;
-// A split's block ids travel in one 64-lane vector load.
-constexpr int64_t kMaxSplitBlocks = 64;
+// A split is shared by four waves of at most 64 blocks each (one 64-lane
+// vector load of block ids per wave).
+constexpr int64_t kMaxSplitBlocks = 256;
 // Tokens per append launch: keeps row indices within int32 inside kernels.
 constexpr int64_t kAppendChunk = int64_t(1) << 22;
 
@@ -177,6 +180,9 @@ kvq_status kvq_append(const kvq_layout* L, const kvq_cache* C, const void* k, co
   if (num_tokens == 0) return KVQ_OK;
   const int64_t row = (int64_t)L->num_kv_heads * L->head_dim;
   if (!k || !v || !slot_mapping || !aligned16(k) || !aligned16(v)) return KVQ_ERR_INVALID_ARGUMENT;
+  // per-channel keys are appended in one launch pair; row indices stay int32
+  if (L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM && num_tokens * L->num_kv_heads >= (int64_t(1) << 31))
+    return KVQ_ERR_UNSUPPORTED;
   if (k_row_stride < row || v_row_stride < row) return KVQ_ERR_INVALID_ARGUMENT;
   if ((k_row_stride * 2) % 16 || (v_row_stride * 2) % 16) return KVQ_ERR_INVALID_ARGUMENT;
   const bool chan = L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM;
@@ -199,7 +205,8 @@ kvq_status kvq_append(const kvq_layout* L, const kvq_cache* C, const void* k, co
   // Chunks keep kernel row indices small. A per-channel key append is not
   // chunked: a chunk boundary inside one sequence's run would split the rows
   // of a completing block between launches.
-  const int64_t chunk = chan ? num_tokens : kAppendChunk;
+  const int64_t max_chunk = std::min<int64_t>(kAppendChunk, (int64_t(1) << 31) / L->num_kv_heads - 1);
+  const int64_t chunk = chan ? num_tokens : max_chunk;
   for (int64_t t0 = 0; t0 < num_tokens; t0 += chunk) {
     const int64_t n = num_tokens - t0 < chunk ? num_tokens - t0 : chunk;
     p.side[0].src = static_cast<const uint16_t*>(k) + t0 * k_row_stride;

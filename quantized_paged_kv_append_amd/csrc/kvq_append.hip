@@ -39,87 +39,159 @@ struct RowArgs {
   int64_t num_blocks;
   int32_t H;
   int32_t bs;
-  int32_t side0;  // first side handled; blockIdx.y adds to it
+  int32_t side0;     // first side handled; blockIdx.y adds to it
+  uint32_t h_mul;    // t = r / H as ((mulhi(r, h_mul) + r) >> h_shift), r < 2^31
+  uint32_t h_shift;
+  uint32_t bs_shift; // log2(bs)
 };
+
+__device__ __forceinline__ uint32_t div_h(uint32_t r, const RowArgs& a) {
+  return (__umulhi(r, a.h_mul) + r) >> a.h_shift;
+}
+
+// max over the four lanes of a quad (DPP quad permutations, no LDS)
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));
+  return v;
+}
 
 __device__ __forceinline__ uint32_t pack_bytes(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) |
          ((uint32_t)(c & 0xFF) << 16) | ((uint32_t)(d & 0xFF) << 24);
 }
 
-// Byte codes (INT8 / FP8 / 16-bit passthrough): lane j of a row holds
-// elements 8j .. 8j+7.
+// E4M3 codes of four binary32 values with the hardware converter (round to
+// nearest even; every input here is below 464, so no saturation occurs).
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// True when the E4M3 rounding of y might differ from that of the exact
+// quotient. With the E4M3 step of y's binade scaled to 1, y lies within 2^-14
+// of a midpoint between neighbouring codes exactly when the low 20 bits of its
+// binary32 mantissa are within 64 of 0x80000 (the scaled magnitude is
+// 8 + (mantissa bits) / 2^20). Magnitudes below 2^-6 (subnormal codes, other
+// midpoints) always take the exact path.
+__device__ __forceinline__ bool fp8_near_tie(float y) {
+  const uint32_t low = __float_as_uint(y) & 0xFFFFFu;
+  return (low - 0x80000u + 64u) < 128u || fabsf(y) < 0.015625f;
+}
+
+// Byte codes (INT8 / FP8 / 16-bit passthrough). A wave covers 16 consecutive
+// tokens of one KV head (rows r = ((tg H + h) 16 + i), token 16 tg + i), so a
+// block's scales leave as one contiguous store when its slots are
+// consecutive. Four lanes share a row of d elements: lane k holds elements
+// 32 u + 8 k + e (u < d/32, e < 8); each 16-byte load instruction reads a
+// contiguous 64-byte piece of every row.
 template <int CODE, int D, bool BF16>
 __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
-  constexpr int RL = D / 8;         // lanes per row
-  constexpr int RPW = kWave / RL;   // rows per wave
+  constexpr int NV = D / 32;        // 16-byte vectors per lane
+  constexpr int RPW = kWave / 4;    // rows per wave (= tokens of one group)
   const SideArgs S = a.side[a.side0 + blockIdx.y];
   const int lane = threadIdx.x & (kWave - 1);
-  const int j = lane % RL;
-  const int64_t rows = a.num_tokens * a.H;
-  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
-  for (int64_t base = wave * RPW; base < rows; base += nwaves * RPW) {
-    const int64_t r = base + lane / RL;
-    const bool in = r < rows;
-    const int64_t t = in ? r / a.H : 0;
-    const int h = in ? (int)(r % a.H) : 0;
+  const int k = lane & 3;
+  const uint32_t groups = ((uint32_t)a.num_tokens + 15u) / 16u;
+  const uint32_t items = groups * (uint32_t)a.H;   // (token group, head) pairs
+  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const uint32_t nwaves = gridDim.x * blockDim.x / kWave;
+  for (uint32_t it = wave; it < items; it += nwaves) {
+    const uint32_t tg = div_h(it, a);
+    const uint32_t h = it - tg * (uint32_t)a.H;
+    const uint32_t t = tg * RPW + (uint32_t)(lane >> 2);
+    const bool in = t < (uint32_t)a.num_tokens;
     const int64_t slot = in ? a.slots[t] : -1;
-    const int64_t blk = slot >= 0 ? slot / a.bs : 0;
-    const bool live = in && slot >= 0 && blk < a.num_blocks;
-    const int off = slot >= 0 ? (int)(slot % a.bs) : 0;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (in) {
-      w = *reinterpret_cast<const u32x4*>(S.src + t * S.row_stride + (int64_t)h * D + 8 * j);
-    }
-    const int64_t rowi = ((int64_t)blk * a.H + h) * a.bs + off;
+    const int64_t blk = slot >> a.bs_shift;
+    const bool live = slot >= 0 && blk < a.num_blocks;
+    const int64_t rowi = (blk * a.H + h) * a.bs + (slot & (a.bs - 1));
+    const uint16_t* src = S.src + (int64_t)(in ? t : 0) * S.row_stride + h * D + 8 * k;
+    u32x4 w[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      w[u] = in ? *reinterpret_cast<const u32x4*>(src + 32 * u) : (u32x4){0u, 0u, 0u, 0u};
     if constexpr (CODE == KVQ_CODE_NONE16) {
-      if (live) *reinterpret_cast<u32x4*>(S.codes + rowi * (2 * D) + 16 * j) = w;
+      if (live) {
+#pragma unroll
+        for (int u = 0; u < NV; ++u)
+          *reinterpret_cast<u32x4*>(S.codes + rowi * (2 * D) + 2 * (32 * u + 8 * k)) = w[u];
+      }
       continue;
     }
-    float x[8];
-    unpack2<BF16>(w.x, x[0], x[1]);
-    unpack2<BF16>(w.y, x[2], x[3]);
-    unpack2<BF16>(w.z, x[4], x[5]);
-    unpack2<BF16>(w.w, x[6], x[7]);
+    float x[NV][8];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      unpack2<BF16>(w[u].x, x[u][0], x[u][1]);
+      unpack2<BF16>(w[u].y, x[u][2], x[u][3]);
+      unpack2<BF16>(w[u].z, x[u][4], x[u][5]);
+      unpack2<BF16>(w[u].w, x[u][6], x[u][7]);
+    }
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = group_max<RL>(amax);
+    for (int u = 0; u < NV; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[u][e]));
+    amax = quad_max(amax);
     constexpr float kQmax = CODE == KVQ_CODE_INT8 ? 127.0f : 448.0f;
     const float s = amax == 0.0f ? 1.0f : div_rn(amax, kQmax);
-    const float inv = div_rn(1.0f, s);
-    uint32_t c[8];
+    const float inv = __builtin_amdgcn_rcpf(s);   // within 1 ulp of 1/s
+    uint32_t o[NV][2];
     bool tie = recip_unsafe(s);
+    if constexpr (CODE == KVQ_CODE_INT8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float y = x[i] * inv;
-      if (CODE == KVQ_CODE_INT8) {
-        const float q = rne(y);
-        tie |= near_half(y, q);
-        c[i] = (uint32_t)(int)fminf(fmaxf(q, -127.0f), 127.0f);
-      } else {
-        float m, rm;
-        c[i] = e4m3_encode(y, m, rm);
-        tie |= near_half(m, rm);
+      for (int u = 0; u < NV; ++u) {
+        int c[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = x[u][e] * inv;
+          const float q = rne(y);
+          tie |= near_half(y, q);
+          c[e] = (int)fminf(fmaxf(q, -127.0f), 127.0f);
+        }
+        o[u][0] = pack_bytes(c[0], c[1], c[2], c[3]);
+        o[u][1] = pack_bytes(c[4], c[5], c[6], c[7]);
       }
-    }
-    if (tie) {  // rare: redo this lane's codes with the exact quotient
+      if (tie) {  // rare: redo this lane's codes with the exact quotient
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float y = div_rn(x[i], s);
-        if (CODE == KVQ_CODE_INT8) {
-          c[i] = (uint32_t)(int)fminf(fmaxf(rne(y), -127.0f), 127.0f);
-        } else {
-          float m, rm;
-          c[i] = e4m3_encode(y, m, rm);
+        for (int u = 0; u < NV; ++u) {
+          int c[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            c[e] = (int)fminf(fmaxf(rne(div_rn(x[u][e], s)), -127.0f), 127.0f);
+          o[u][0] = pack_bytes(c[0], c[1], c[2], c[3]);
+          o[u][1] = pack_bytes(c[4], c[5], c[6], c[7]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y[e] = x[u][e] * inv;
+          tie |= fp8_near_tie(y[e]);
+        }
+        o[u][0] = fp8x4(y[0], y[1], y[2], y[3]);
+        o[u][1] = fp8x4(y[4], y[5], y[6], y[7]);
+      }
+      if (tie) {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = div_rn(x[u][e], s);
+          o[u][0] = fp8x4(y[0], y[1], y[2], y[3]);
+          o[u][1] = fp8x4(y[4], y[5], y[6], y[7]);
         }
       }
     }
     if (live) {
-      u32x2 o = {pack_bytes(c[0], c[1], c[2], c[3]), pack_bytes(c[4], c[5], c[6], c[7])};
-      *reinterpret_cast<u32x2*>(S.codes + rowi * D + 8 * j) = o;
-      if (j == 0) S.scale[rowi] = s;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        u32x2 v2 = {o[u][0], o[u][1]};
+        *reinterpret_cast<u32x2*>(S.codes + rowi * D + 32 * u + 8 * k) = v2;
+      }
+      if (k == 0) S.scale[rowi] = s;
     }
   }
 }
@@ -426,7 +498,9 @@ template <int D, bool BF16>
 hipError_t launch_rows(const AppendPlan& p, const RowArgs& ra, int code, int mode,
                        int nsides, hipStream_t stream) {
   const int64_t rows = p.num_tokens * p.num_kv_heads;
-  const int64_t waves = (rows + (kWave / (D / 8)) - 1) / (kWave / (D / 8));
+  const int64_t waves = (code == KVQ_CODE_INT4)
+                            ? (rows + kWave / (D / 8) - 1) / (kWave / (D / 8))
+                            : (p.num_tokens + 15) / 16 * p.num_kv_heads;
   dim3 grid(grid_for(waves, p.cu_count), nsides);
   if (code == KVQ_CODE_INT8)
     append_bytes_kernel<KVQ_CODE_INT8, D, BF16><<<grid, 256, 0, stream>>>(ra);
@@ -480,6 +554,14 @@ hipError_t launch_append_d(const AppendPlan& p, hipStream_t stream) {
   ra.num_blocks = p.num_blocks;
   ra.H = p.num_kv_heads;
   ra.bs = p.block_size;
+  {
+    const uint32_t d = (uint32_t)p.num_kv_heads;
+    uint32_t l = 0;
+    while ((1u << l) < d) ++l;  // ceil(log2 d)
+    ra.h_shift = l;
+    ra.h_mul = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+    ra.bs_shift = p.block_size == 16 ? 4 : 5;
+  }
   hipError_t e;
   const bool chan = p.mode[0] == KVQ_SCALE_CHANNEL_BLOCK_SYM;
   if (!chan && p.code[0] == p.code[1] && p.mode[0] == p.mode[1]) {

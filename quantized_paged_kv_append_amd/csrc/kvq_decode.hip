@@ -15,9 +15,11 @@
 //
 // Design. Decode is HBM-bound (the same page, "Common pitfalls": decode is
 // memory-bound), so the kernel streams each code byte once:
-//  * One wave per work item (sequence b, KV head g, split j of split_blocks
-//    cache blocks). The G query heads that share KV head g are the 16 columns
-//    of the MFMA tiles (zero-padded when G < 16).
+//  * One workgroup of four waves per work item (sequence b, KV head g, split
+//    j of split_blocks cache blocks); each wave streams a consecutive quarter
+//    of the split and the four softmax states merge through LDS, so the
+//    global partials stay few. The G query heads that share KV head g are the
+//    16 columns of the MFMA tiles (zero-padded when G < 16).
 //  * Scores: S[16 tokens x 16 heads] = K_tile . Q^T with
 //    v_mfma_f32_16x16x32_f16. Lane (r, j) = (lane % 16, lane / 16) feeds
 //    token r of the tile with elements [j d/4, (j+1) d/4) of its key row,
@@ -37,7 +39,7 @@
 //    largest element); the factor returns in the score scale.
 //  * A ring of three register buffers keeps two cache blocks in flight while
 //    the wave computes on a third; block ids come from one vector load per 64
-//    blocks and are read with v_readlane.
+//    blocks of the split and are read with v_readlane.
 //  * Partials (m, l, acc) per split go to the workspace; decode_reduce merges
 //    them with the log-sum-exp rule.
 #include "kvq_device.h"
@@ -277,21 +279,14 @@ __device__ __forceinline__ void load_query(const uint16_t* qp, float* qf) {
   }
 }
 
+// One wave's share of a split: blocks [i0, i1) of sequence b, KV head g.
+// Leaves the running softmax state in st.
 template <int CODE, int D, int BS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_kernel(DecodeArgs a) {
+__device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, int L, int nblk,
+                                            int i0, int i1, int lane, SoftmaxState<D>& st) {
   constexpr int NCH = D / 32;   // k-chunks of the score MFMA
-  constexpr int NPV = D / 16;   // output MFMAs (16 d-rows each)
   constexpr int NBUF = BS == 16 ? 3 : 2;  // blocks in the register ring
-  const int lane = threadIdx.x;
   const int r = lane & 15, j = lane >> 4;
-  const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x;
-  // lengths beyond the table row (a broken precondition) are cut to it
-  const int L = min(a.context_lens[b], a.max_blocks * BS);
-  const int nblk = (L + BS - 1) / BS;
-  const int i0 = sp * a.split_blocks;
-  if (i0 >= nblk) return;
-  const int i1 = min(i0 + a.split_blocks, nblk);
   const int ilast = i1 - 1;
 
   // ---- query: heads g*G + r, elements [j d/4, (j+1) d/4) ----------------
@@ -320,13 +315,7 @@ void decode_split_kernel(DecodeArgs a) {
     for (int e = 0; e < 8; ++e) qop[c][e] = hcol ? (half_t)(qf[8 * c + e] * qdown) : (half_t)0.0f;
   const float cscore = hcol ? qup * a.sm_log2 : 0.0f;
 
-  SoftmaxState<D> st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NPV; ++c) st.acc[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-
-  // The split's block ids (at most 64) arrive with one vector load: lane k
+  // The wave's block ids (at most 64) arrive with one vector load: lane k
   // holds the id of block i0 + k; v_readlane hands each to the scalar unit.
   // Ids outside the pool (a broken precondition) are clamped to block 0 so
   // that no load leaves the cache planes.
@@ -365,25 +354,81 @@ void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- partial results ---------------------------------------------------
-  const float l = colsum4(st.l);
-  if (!hcol) return;
+}
+
+// A split of kNW * (per-wave share) blocks per (sequence, KV head): the
+// workgroup's waves take consecutive shares of at most 64 blocks each, merge
+// their softmax states through LDS, and wave 0 writes the split's partial.
+constexpr int kNW = 4;
+
+template <int CODE, int D, int BS>
+__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_kernel(DecodeArgs a) {
+  constexpr int NPV = D / 16;   // output MFMAs (16 d-rows each)
+  constexpr int NV = D / 4;     // accumulator values per lane
+  __shared__ float red[kNW][NV + 2][kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int r = lane & 15, j = lane >> 4;
+  const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x;
+  // lengths beyond the table row (a broken precondition) are cut to it
+  const int L = min(a.context_lens[b], a.max_blocks * BS);
+  const int nblk = (L + BS - 1) / BS;
+  const int s0 = sp * a.split_blocks;
+  if (s0 >= nblk) return;
+  const int s1 = min(s0 + a.split_blocks, nblk);
+  const int share = (a.split_blocks + kNW - 1) / kNW;
+  const int i0 = s0 + wave * share;
+  const int i1 = min(i0 + share, s1);
+
+  SoftmaxState<D> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NPV; ++c) st.acc[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  if (i0 < i1) wave_blocks<CODE, D, BS>(a, b, g, L, nblk, i0, i1, lane, st);
+
+  // ---- merge the waves' states, then write the split's partial ----------
+  const float lsum = colsum4(st.l);
+#pragma unroll
+  for (int c = 0; c < NPV; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][4 * c + e][lane] = st.acc[c][e];
+  red[wave][NV][lane] = st.m;
+  red[wave][NV + 1][lane] = lsum;
+  __syncthreads();
+  if (wave != 0) return;
+  float M = red[0][NV][lane];
+#pragma unroll
+  for (int w = 1; w < kNW; ++w) M = fmaxf(M, red[w][NV][lane]);
+  float acc[NV], l = 0.0f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    const float mw = red[w][NV][lane];
+    const float sc = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+    l += sc * red[w][NV + 1][lane];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] += sc * red[w][v][lane];
+  }
+  if (r >= a.G) return;
+  const int h = g * a.G + r;
   const int64_t item = ((int64_t)b * a.Hq + h) * a.num_splits + sp;
   if (j == 0) {
-    float2 ml = {st.m, l};
+    float2 ml = {M, l};
     *reinterpret_cast<float2*>(a.ws_ml + item * 2) = ml;
   }
-  // acc[c][e] holds output element (d/16) (4 j + e) + c of head r
+  // acc[4 c + e] holds output element (d/16) (4 j + e) + c of head r
   float* dst = a.ws_acc + item * D + j * (D / 4);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if constexpr (NPV == 8) {
-      float4v lo = {st.acc[0][e], st.acc[1][e], st.acc[2][e], st.acc[3][e]};
-      float4v hi = {st.acc[4][e], st.acc[5][e], st.acc[6][e], st.acc[7][e]};
+      float4v lo = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
+      float4v hi = {acc[16 + e], acc[20 + e], acc[24 + e], acc[28 + e]};
       *reinterpret_cast<float4v*>(dst + 8 * e) = lo;
       *reinterpret_cast<float4v*>(dst + 8 * e + 4) = hi;
     } else {
-      float4v v4 = {st.acc[0][e], st.acc[1][e], st.acc[2][e], st.acc[3][e]};
+      float4v v4 = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
       *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
     }
   }
@@ -410,33 +455,54 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
+// One wave per (sequence, query head). Lane s holds split s's (m, l); the
+// partial accumulators of up to 32 splits are loaded in the same batch, so a
+// sequence with up to 32 splits is merged after a single memory round trip.
 template <int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
-  constexpr int EPL = D / 64;  // elements per lane
+  constexpr int EPL = D / 64;  // output elements per lane
+  constexpr int KB = 32;       // splits per batch of loads
+  typedef float floatE __attribute__((ext_vector_type(EPL)));
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int L = min(a.context_lens[b], a.max_blocks * a.BS);
   const int nblk = (L + a.BS - 1) / a.BS;
   const int ns = min((nblk + a.split_blocks - 1) / a.split_blocks, a.num_splits);
   const int64_t base = ((int64_t)b * a.Hq + h) * a.num_splits;
-  float o[EPL];
+  floatE o;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
-  if (ns > 0) {
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
-    float den = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = a.ws_ml[(base + s) * 2];
-      const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-      den += w * a.ws_ml[(base + s) * 2 + 1];
-      const float* ap = a.ws_acc + (base + s) * D + EPL * lane;
+  float M = -INFINITY, den = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += KB) {
+    const int cnt = min(KB, ns - s0);
+    float2 ml = {-INFINITY, 0.0f};
+    if (lane < cnt) ml = *reinterpret_cast<const float2*>(a.ws_ml + (base + s0 + lane) * 2);
+    floatE v[KB];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] += w * ap[e];
-    }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    for (int u = 0; u < KB; ++u)
+      if (u < cnt)
+        v[u] = *reinterpret_cast<const floatE*>(a.ws_acc + (base + s0 + u) * D + EPL * lane);
+    // running merge across batches: M is the max over all splits seen so far
+    float mb = ml.x;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] *= inv;
+    for (int m = 32; m >= 1; m >>= 1) mb = fmaxf(mb, __shfl_xor(mb, m, kWave));
+    const float Mn = fmaxf(M, mb);
+    const float rescale = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    o *= rescale;
+    den *= rescale;
+    M = Mn;
+    const float w = ml.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);
+    den += w * ml.y;
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      if (u < cnt) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+        o += wu * v[u];
+      }
   }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m, kWave);
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  o *= inv;
   const int64_t ob = ((int64_t)b * a.Hq + h) * D + EPL * lane;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
@@ -452,7 +518,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
 template <int CODE, int D, int BS>
 hipError_t launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
   dim3 grid(a.num_splits, a.H, batch);
-  decode_split_kernel<CODE, D, BS><<<grid, 64, 0, stream>>>(a);
+  decode_split_kernel<CODE, D, BS><<<grid, 64 * kNW, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ def test_workspace_size_is_pure_and_positive():
     a = kq.kvq_decode_workspace_bytes(L, 16, 64, 32768)
     assert a == kq.kvq_decode_workspace_bytes(L, 16, 64, 32768) and a > 0
     assert kq.kvq_decode_workspace_bytes(L, 16, 64, 32768, 8) > a
-    assert kq._lib.kvq_decode_workspace_bytes(C.byref(L), 16, 64, 32768, 65) == \
+    assert kq._lib.kvq_decode_workspace_bytes(C.byref(L), 16, 64, 32768, 257) == \
         kq.KVQ_ERR_INVALID_ARGUMENT
     assert kq._lib.kvq_decode_workspace_bytes(C.byref(L), -1, 64, 32768, 0) == \
         kq.KVQ_ERR_INVALID_ARGUMENT
@@ -142,7 +142,7 @@ def test_append_and_decode_reject_bad_arguments_on_host():
     assert dec(q_dtype=kq.KVQ_F32) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert dec(out_dtype=7) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert dec(maxlen=65) == kq.KVQ_ERR_INVALID_ARGUMENT        # > maxb * bs
-    assert dec(split=65) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert dec(split=257) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert dec(sm=float("nan")) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert dec(wsb=16) == kq.KVQ_ERR_WORKSPACE_TOO_SMALL
     assert dec(tables=None) == kq.KVQ_ERR_INVALID_ARGUMENT

@@ -57,10 +57,10 @@ def test_decode_matches_oracle(code, d, bs, G):
     assert (got[5] == 0).all()           # empty context
 
 
-@pytest.mark.parametrize("split", [1, 2, 3, 5, 64])
+@pytest.mark.parametrize("split", [1, 2, 3, 5, 64, 65, 130, 256])
 def test_decode_split_counts(split):
     need_gpu()
-    w, L, LL, s, q = _setup("fp8", lens=(700, 1, 250, 64, 0, 333), G=8)
+    w, L, LL, s, q = _setup("fp8", lens=(7000, 1, 250, 64, 0, 4133), G=8)
     got, exp = _run(w, L, LL, s, q, split_blocks=split)
     assert_decode_close(got, exp, f"split {split}")
 
