@@ -56,6 +56,8 @@ struct DecodeArgs {
   const uint8_t* v_codes;
   const float* k_scale;
   const float* v_scale;
+  const uint8_t* k_zero;
+  const uint8_t* v_zero;
   const int32_t* block_tables;
   const int32_t* context_lens;
   float* ws_acc;
@@ -356,12 +358,302 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
 
 }
 
+// ---------------------------------------------------------------------------
+// 4-bit codes. Row layout (see the header): element 32 i + 2 r + t of a row
+// sits in byte n r + i (n = d/32 slices), nibble t. Lane (r, j) feeds the
+// score MFMA for token r with key bytes [4 n j, 4 n j + 4 n), i.e. pairs
+// r' = 4j .. 4j+3 of every slice: chunk c of the contraction is slice c, so
+// that per-slice (group) scales apply to separate accumulators. For P.V, MFMA
+// m = 2 i + t covers output rows d = 32 i + 2 r + t and lane (r, j) needs byte
+// n r + i of its four tokens.
+// ---------------------------------------------------------------------------
+template <int D, int MODE>
+struct Tile4 {
+  static constexpr int NS = D / 32;
+  static constexpr int SG = MODE == KVQ_SCALE_GROUP_ASYM ? NS : 1;
+  uint32_t k[NS];      // key bytes of token r for pairs 4j..4j+3
+  uint32_t v[4];       // value bytes n r .. n r + n - 1 of tokens 4j + e
+  float sk[4 * SG];    // key scales of tokens 4j + e, index 4 group + e
+  float sv[4 * SG];    // value scales, same order
+  uint32_t zk;         // key zero points of token r, byte c = group c
+  uint32_t zv[NS];     // value zero points of tokens 4j..4j+3 ([token][group] bytes)
+};
+
+template <int D, int BS, int MODE>
+__device__ __forceinline__ void load_tile4(Tile4<D, MODE>& t, const DecodeArgs& a, int64_t bh,
+                                           int nt, int lane) {
+  constexpr int NS = D / 32;
+  constexpr int RB = D / 2;  // bytes per row
+  const int r = lane & 15, j = lane >> 4;
+  const int64_t row0 = bh * BS + nt * 16;   // first token of the tile
+  const uint8_t* kr = a.k_codes + (row0 + r) * RB + j * (RB / 4);
+  if constexpr (NS == 4) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(kr);
+    t.k[0] = w.x; t.k[1] = w.y; t.k[2] = w.z; t.k[3] = w.w;
+  } else {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(kr);
+    t.k[0] = w.x; t.k[1] = w.y;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint8_t* vr = a.v_codes + (row0 + 4 * j + e) * RB + r * (RB / 16);
+    if constexpr (NS == 4)
+      t.v[e] = *reinterpret_cast<const uint32_t*>(vr);
+    else
+      t.v[e] = *reinterpret_cast<const uint16_t*>(vr);
+  }
+  if constexpr (MODE == KVQ_SCALE_GROUP_ASYM) {
+    // the planes hold [token][group]; the tile keeps [group][token]
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const float4v ks = *reinterpret_cast<const float4v*>(a.k_scale + (row0 + 4 * j) * NS + 4 * u);
+      const float4v vs = *reinterpret_cast<const float4v*>(a.v_scale + (row0 + 4 * j) * NS + 4 * u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int f = 4 * u + e, tok = f / NS, grp = f % NS;
+        t.sk[4 * grp + tok] = ks[e];
+        t.sv[4 * grp + tok] = vs[e];
+      }
+    }
+    if constexpr (NS == 4) {
+      t.zk = *reinterpret_cast<const uint32_t*>(a.k_zero + (row0 + r) * NS);
+      const u32x4 z = *reinterpret_cast<const u32x4*>(a.v_zero + (row0 + 4 * j) * NS);
+      t.zv[0] = z.x; t.zv[1] = z.y; t.zv[2] = z.z; t.zv[3] = z.w;
+    } else {
+      t.zk = *reinterpret_cast<const uint16_t*>(a.k_zero + (row0 + r) * NS);
+      const u32x2 z = *reinterpret_cast<const u32x2*>(a.v_zero + (row0 + 4 * j) * NS);
+      t.zv[0] = z.x; t.zv[1] = z.y;
+    }
+  } else {
+    const float4v ks = *reinterpret_cast<const float4v*>(a.k_scale + row0 + 4 * j);
+    const float4v vs = *reinterpret_cast<const float4v*>(a.v_scale + row0 + 4 * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t.sk[e] = ks[e];
+      t.sv[e] = vs[e];
+    }
+    t.zk = 0;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) t.zv[u] = 0;
+  }
+}
+
+// Byte c of each of four words w0..w3 as one word [w0.bc, w1.bc, w2.bc, w3.bc]
+// for c = 0..3 (a 4x4 byte transpose).
+__device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                             uint32_t* g) {
+  const uint32_t a0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+  const uint32_t a1 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+  const uint32_t c0 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+  const uint32_t c1 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+  g[0] = __builtin_amdgcn_perm(c0, a0, 0x05040100u);
+  g[1] = __builtin_amdgcn_perm(c0, a0, 0x07060302u);
+  g[2] = __builtin_amdgcn_perm(c1, a1, 0x05040100u);
+  g[3] = __builtin_amdgcn_perm(c1, a1, 0x07060302u);
+}
+
+// Nibble pairs of bytes 0 and 2 (shift 0 / 4) or 1 and 3 (shift 8 / 12) as
+// two fp16 values 1024 + nibble.
+template <int SHIFT>
+__device__ __forceinline__ half2v nib2(uint32_t g) {
+  return __builtin_bit_cast(half2v, ((g >> SHIFT) & 0x000F000Fu) | 0x64006400u);
+}
+
+template <int D, int MODE>
+__device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, int L, bool tail,
+                                           const half8v* qop, float cscore, int j,
+                                           SoftmaxState<D>& st) {
+  constexpr int NS = D / 32;
+  constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
+  // ---- key operands, chunk c = slice c -----------------------------------
+  uint32_t g[4];
+  if constexpr (NS == 4) {
+    transpose4x4(t.k[0], t.k[1], t.k[2], t.k[3], g);
+  } else {
+    g[0] = __builtin_amdgcn_perm(t.k[1], t.k[0], 0x06040200u);
+    g[1] = __builtin_amdgcn_perm(t.k[1], t.k[0], 0x07050301u);
+  }
+  float4v S[ASYM ? NS : 1];
+#pragma unroll
+  for (int c = 0; c < (ASYM ? NS : 1); ++c) S[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NS; ++c) {
+    uint32_t gc = g[c];
+    half2v bias;
+    if constexpr (ASYM) {
+      const uint32_t z = (t.zk >> (8 * c)) & 0xFFu;
+      bias = __builtin_bit_cast(half2v, (z | (z << 16)) | 0x64006400u);
+    } else {
+      gc ^= 0x88888888u;  // two's-complement nibble q -> q + 8
+      bias = __builtin_bit_cast(half2v, 0x64086408u);
+    }
+    const half2v h0 = nib2<0>(gc) - bias, h1 = nib2<4>(gc) - bias;
+    const half2v h2 = nib2<8>(gc) - bias, h3 = nib2<12>(gc) - bias;
+    half8v ka;
+    ka[0] = h0[0]; ka[1] = h0[1]; ka[2] = h1[0]; ka[3] = h1[1];
+    ka[4] = h2[0]; ka[5] = h2[1]; ka[6] = h3[0]; ka[7] = h3[1];
+    S[ASYM ? c : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[c], S[ASYM ? c : 0], 0, 0, 0);
+  }
+  bool ok[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ok[e] = !tail || pos0 + 4 * j + e < L;
+  float s[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = 0.0f;
+    if constexpr (ASYM) {
+#pragma unroll
+      for (int c = 0; c < NS; ++c) v += S[c][e] * t.sk[4 * c + e];
+    } else {
+      v = S[0][e] * t.sk[e];
+    }
+    s[e] = ok[e] ? v * cscore : -INFINITY;
+  }
+  const float mt = colmax4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+  const float mn = fmaxf(st.m, mt);
+  const float msafe = mn == -INFINITY ? 0.0f : mn;
+  if (__any(mn > st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) st.acc[c] *= alpha;
+  }
+  st.m = mn;
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = ok[e] ? __builtin_amdgcn_exp2f(s[e] - msafe) : 0.0f;
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  // ---- value operands: byte i of the four tokens, tokens in order 0,2,1,3
+  uint32_t G[4], Z[4];
+  if constexpr (NS == 4) {
+    transpose4x4(t.v[0], t.v[1], t.v[2], t.v[3], G);
+    if constexpr (ASYM) transpose4x4(t.zv[0], t.zv[1], t.zv[2], t.zv[3], Z);
+  } else {
+    const uint32_t v01 = t.v[0] | (t.v[1] << 16), v23 = t.v[2] | (t.v[3] << 16);
+    G[0] = __builtin_amdgcn_perm(v23, v01, 0x06040200u);
+    G[1] = __builtin_amdgcn_perm(v23, v01, 0x07050301u);
+    if constexpr (ASYM) {
+      Z[0] = __builtin_amdgcn_perm(t.zv[1], t.zv[0], 0x06040200u);
+      Z[1] = __builtin_amdgcn_perm(t.zv[1], t.zv[0], 0x07050301u);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = ok[e] ? p[e] * t.sv[ASYM ? 4 * i + e : e] : 0.0f;
+    half4v pop;
+    pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
+    uint32_t Gi = G[i];
+    half2v b02, b13;
+    if constexpr (ASYM) {
+      b02 = __builtin_bit_cast(half2v, (Z[i] & 0x00FF00FFu) | 0x64006400u);
+      b13 = __builtin_bit_cast(half2v, ((Z[i] >> 8) & 0x00FF00FFu) | 0x64006400u);
+    } else {
+      Gi ^= 0x88888888u;
+      b02 = b13 = __builtin_bit_cast(half2v, 0x64086408u);
+    }
+    const half2v x02 = nib2<0>(Gi) - b02, x13 = nib2<8>(Gi) - b13;
+    const half2v y02 = nib2<4>(Gi) - b02, y13 = nib2<12>(Gi) - b13;
+    half4v va0, va1;
+    va0[0] = x02[0]; va0[1] = x02[1]; va0[2] = x13[0]; va0[3] = x13[1];
+    va1[0] = y02[0]; va1[1] = y02[1]; va1[2] = y13[0]; va1[3] = y13[1];
+    st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va0, pop, st.acc[2 * i], 0, 0, 0);
+    st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(va1, pop, st.acc[2 * i + 1], 0, 0, 0);
+  }
+}
+
+// Query operand for 4-bit keys: chunk c holds elements 32 c + 8 j + perm8[p]
+// at position p, matching the nibble order nib2<0,4,8,12> produces.
+template <int D>
+__device__ __forceinline__ void query_int4(const DecodeArgs& a, const uint16_t* qrow, int j,
+                                           bool hcol, half8v* qop, float& cscore) {
+  constexpr int NS = D / 32;
+  float qf[NS][8];
+#pragma unroll
+  for (int c = 0; c < NS; ++c) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * j);
+    if (a.q_bf16) {
+      unpack2<true>(w.x, qf[c][0], qf[c][1]); unpack2<true>(w.y, qf[c][2], qf[c][3]);
+      unpack2<true>(w.z, qf[c][4], qf[c][5]); unpack2<true>(w.w, qf[c][6], qf[c][7]);
+    } else {
+      unpack2<false>(w.x, qf[c][0], qf[c][1]); unpack2<false>(w.y, qf[c][2], qf[c][3]);
+      unpack2<false>(w.z, qf[c][4], qf[c][5]); unpack2<false>(w.w, qf[c][6], qf[c][7]);
+    }
+  }
+  float qmax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NS; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qf[c][e]));
+  qmax = colmax4(qmax);
+  int qe = qmax > 0.0f ? (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 : 0;
+  qe = max(qe, -126);
+  const float qdown = __uint_as_float((uint32_t)(127 - qe) << 23);
+  const float qup = __uint_as_float((uint32_t)(127 + qe) << 23);
+  constexpr int perm8[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+  for (int c = 0; c < NS; ++c)
+#pragma unroll
+    for (int p = 0; p < 8; ++p) qop[c][p] = hcol ? (half_t)(qf[c][perm8[p]] * qdown) : (half_t)0.0f;
+  cscore = hcol ? qup * a.sm_log2 : 0.0f;
+}
+
+// One wave's share of a split for 4-bit codes, in 16-token tiles with a ring
+// of NBUF tiles in registers.
+template <int D, int BS, int MODE>
+__device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int g, int L,
+                                                 int nblk, int i0, int i1, int lane,
+                                                 SoftmaxState<D>& st) {
+  constexpr int TPB = BS / 16;  // tiles per block
+  constexpr int NBUF = MODE == KVQ_SCALE_GROUP_ASYM ? 2 : 3;
+  const int r = lane & 15, j = lane >> 4;
+  const int ilast = i1 - 1;
+  const bool hcol = r < a.G;
+  const int h = g * a.G + (hcol ? r : 0);
+  half8v qop[D / 32];
+  float cscore;
+  query_int4<D>(a, a.q + ((int64_t)b * a.Hq + h) * D, j, hcol, qop, cscore);
+  (void)nblk;
+
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
+  const int32_t ids = trow[min(i0 + lane, ilast)];
+  const int t0 = i0 * TPB;
+  const int t1 = min(i1 * TPB, (L + 15) / 16);   // tiles holding tokens < L
+  const int tfull = min(t1, L / 16);               // tiles wholly below L
+  const int tlast = t1 - 1;
+  auto load = [&](Tile4<D, MODE>& t, int tile) {
+    const int ti = min(tile, tlast);
+    const int32_t id = __builtin_amdgcn_readlane(ids, ti / TPB - i0);
+    const int64_t bh = (int64_t)((id >= 0 && id < a.num_blocks) ? id : 0) * a.H + g;
+    load_tile4<D, BS, MODE>(t, a, bh, ti % TPB, lane);
+  };
+  Tile4<D, MODE> buf[NBUF];
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u) load(buf[u], t0 + u);
+  int tt = t0;
+  for (; tt + NBUF <= tfull; tt += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      tile4_step<D, MODE>(buf[u], (tt + u) * 16, L, false, qop, cscore, j, st);
+      load(buf[u], tt + u + NBUF);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u) {
+    if (tt + u < tfull)
+      tile4_step<D, MODE>(buf[u], (tt + u) * 16, L, false, qop, cscore, j, st);
+    else if (tt + u < t1)
+      tile4_step<D, MODE>(buf[u], (tt + u) * 16, L, true, qop, cscore, j, st);
+  }
+}
+
 // A split of kNW * (per-wave share) blocks per (sequence, KV head): the
 // workgroup's waves take consecutive shares of at most 64 blocks each, merge
 // their softmax states through LDS, and wave 0 writes the split's partial.
 constexpr int kNW = 4;
 
-template <int CODE, int D, int BS>
+template <int CODE, int MODE, int D, int BS>
 __global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int NPV = D / 16;   // output MFMAs (16 d-rows each)
@@ -385,7 +677,12 @@ void decode_split_kernel(DecodeArgs a) {
   st.l = 0.0f;
 #pragma unroll
   for (int c = 0; c < NPV; ++c) st.acc[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-  if (i0 < i1) wave_blocks<CODE, D, BS>(a, b, g, L, nblk, i0, i1, lane, st);
+  if (i0 < i1) {
+    if constexpr (CODE == KVQ_CODE_INT4)
+      wave_blocks_int4<D, BS, MODE>(a, b, g, L, nblk, i0, i1, lane, st);
+    else
+      wave_blocks<CODE, D, BS>(a, b, g, L, nblk, i0, i1, lane, st);
+  }
 
   // ---- merge the waves' states, then write the split's partial ----------
   const float lsum = colsum4(st.l);
@@ -418,18 +715,32 @@ void decode_split_kernel(DecodeArgs a) {
     float2 ml = {M, l};
     *reinterpret_cast<float2*>(a.ws_ml + item * 2) = ml;
   }
-  // acc[4 c + e] holds output element (d/16) (4 j + e) + c of head r
-  float* dst = a.ws_acc + item * D + j * (D / 4);
+  if constexpr (CODE == KVQ_CODE_INT4) {
+    // acc[4 m + e], m = 2 i + t, holds output element 32 i + 8 j + 2 e + t
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if constexpr (NPV == 8) {
-      float4v lo = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
-      float4v hi = {acc[16 + e], acc[20 + e], acc[24 + e], acc[28 + e]};
-      *reinterpret_cast<float4v*>(dst + 8 * e) = lo;
-      *reinterpret_cast<float4v*>(dst + 8 * e + 4) = hi;
-    } else {
-      float4v v4 = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
-      *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
+    for (int i = 0; i < D / 32; ++i) {
+      float* dst = a.ws_acc + item * D + 32 * i + 8 * j;
+      const float* A0 = acc + 8 * i;      // t = 0
+      const float* A1 = acc + 8 * i + 4;  // t = 1
+      float4v lo = {A0[0], A1[0], A0[1], A1[1]};
+      float4v hi = {A0[2], A1[2], A0[3], A1[3]};
+      *reinterpret_cast<float4v*>(dst) = lo;
+      *reinterpret_cast<float4v*>(dst + 4) = hi;
+    }
+  } else {
+    // acc[4 c + e] holds output element (d/16) (4 j + e) + c of head r
+    float* dst = a.ws_acc + item * D + j * (D / 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (NPV == 8) {
+        float4v lo = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
+        float4v hi = {acc[16 + e], acc[20 + e], acc[24 + e], acc[28 + e]};
+        *reinterpret_cast<float4v*>(dst + 8 * e) = lo;
+        *reinterpret_cast<float4v*>(dst + 8 * e + 4) = hi;
+      } else {
+        float4v v4 = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
+        *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
+      }
     }
   }
 }
@@ -515,20 +826,30 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
   }
 }
 
-template <int CODE, int D, int BS>
+template <int CODE, int MODE, int D, int BS>
 hipError_t launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
   dim3 grid(a.num_splits, a.H, batch);
-  decode_split_kernel<CODE, D, BS><<<grid, 64 * kNW, 0, stream>>>(a);
+  decode_split_kernel<CODE, MODE, D, BS><<<grid, 64 * kNW, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <int CODE, int MODE>
+hipError_t launch_split_shape(const DecodeArgs& a, int d, int bs, int batch, hipStream_t stream) {
+  if (d == 128)
+    return bs == 16 ? launch_split<CODE, MODE, 128, 16>(a, batch, stream)
+                    : launch_split<CODE, MODE, 128, 32>(a, batch, stream);
+  return bs == 16 ? launch_split<CODE, MODE, 64, 16>(a, batch, stream)
+                  : launch_split<CODE, MODE, 64, 32>(a, batch, stream);
 }
 
 }  // namespace
 
 bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
                       int32_t v_mode) {
-  if (k_code != v_code || k_mode != KVQ_SCALE_TOKEN_SYM || v_mode != KVQ_SCALE_TOKEN_SYM)
-    return false;
-  return k_code == KVQ_CODE_INT8 || k_code == KVQ_CODE_FP8_E4M3;
+  if (k_code != v_code || k_mode != v_mode) return false;
+  if (k_mode == KVQ_SCALE_TOKEN_SYM)
+    return k_code == KVQ_CODE_INT8 || k_code == KVQ_CODE_FP8_E4M3 || k_code == KVQ_CODE_INT4;
+  return k_mode == KVQ_SCALE_GROUP_ASYM && k_code == KVQ_CODE_INT4;
 }
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
@@ -551,21 +872,18 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
   a.split_blocks = p.split_blocks;
   a.num_splits = p.num_splits;
   a.sm_log2 = p.sm_scale * kLog2e;
+  a.k_zero = p.k_zero;
+  a.v_zero = p.v_zero;
   hipError_t e;
-  const bool fp8 = p.k_code == KVQ_CODE_FP8_E4M3;
-#define KVQ_SPLIT(CODE)                                                              \
-  if (p.head_dim == 128)                                                             \
-    e = p.block_size == 16 ? launch_split<CODE, 128, 16>(a, p.batch, stream)         \
-                           : launch_split<CODE, 128, 32>(a, p.batch, stream);        \
-  else                                                                               \
-    e = p.block_size == 16 ? launch_split<CODE, 64, 16>(a, p.batch, stream)          \
-                           : launch_split<CODE, 64, 32>(a, p.batch, stream);
-  if (fp8) {
-    KVQ_SPLIT(KVQ_CODE_FP8_E4M3)
-  } else {
-    KVQ_SPLIT(KVQ_CODE_INT8)
-  }
-#undef KVQ_SPLIT
+  const int d = p.head_dim, bs = p.block_size;
+  if (p.k_code == KVQ_CODE_FP8_E4M3)
+    e = launch_split_shape<KVQ_CODE_FP8_E4M3, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.batch, stream);
+  else if (p.k_code == KVQ_CODE_INT8)
+    e = launch_split_shape<KVQ_CODE_INT8, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.batch, stream);
+  else if (p.k_mode == KVQ_SCALE_GROUP_ASYM)
+    e = launch_split_shape<KVQ_CODE_INT4, KVQ_SCALE_GROUP_ASYM>(a, d, bs, p.batch, stream);
+  else
+    e = launch_split_shape<KVQ_CODE_INT4, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.batch, stream);
   if (e != hipSuccess) return e;
   ReduceArgs ra;
   ra.ws_acc = p.ws_acc;

@@ -17,9 +17,10 @@ LENS = (37, 80, 5, 1, 16, 0, 17, 300, 15, 33)
 
 
 def _setup(code="int8", d=128, bs=16, G=4, H=2, src="bfloat16", lens=LENS, seed=0,
-           permuted=True, kscale=1.0, name="tiny"):
-    w = workloads.get(name, k_code=code, v_code=code, k_mode="token_sym",
-                      v_mode="token_sym", src_dtype=src, head_dim=d, block_size=bs,
+           permuted=True, kscale=1.0, name="tiny", mode="token_sym"):
+    w = workloads.get(name, k_code=code, v_code=code, k_mode=mode, v_mode=mode,
+                      group_size=32 if mode == "group_asym" else 0,
+                      src_dtype=src, head_dim=d, block_size=bs,
                       num_kv_heads=H, num_q_heads=G * H, batch=len(lens),
                       n_outliers=2, outlier_factor=8.0)
     L, LL = oracle_layout(w), lib_layout(w)
@@ -46,23 +47,25 @@ def _run(w, L, LL, s, q, out_dtype=torch.float32, sm_scale=0.0, split_blocks=0):
     return got, exp
 
 
-@pytest.mark.parametrize("code", ["int8", "fp8"])
+@pytest.mark.parametrize("code,mode", [("int8", "token_sym"), ("fp8", "token_sym"),
+                                       ("int4", "token_sym"), ("int4", "group_asym")])
 @pytest.mark.parametrize("d,bs", [(128, 16), (64, 16), (128, 32), (64, 32)])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
-def test_decode_matches_oracle(code, d, bs, G):
+def test_decode_matches_oracle(code, mode, d, bs, G):
     need_gpu()
-    w, L, LL, s, q = _setup(code, d, bs, G)
+    w, L, LL, s, q = _setup(code, d, bs, G, mode=mode)
     got, exp = _run(w, L, LL, s, q)
-    assert_decode_close(got, exp, f"{code} d{d} bs{bs} G{G}")
+    assert_decode_close(got, exp, f"{code}/{mode} d{d} bs{bs} G{G}")
     assert (got[5] == 0).all()           # empty context
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 5, 64, 65, 130, 256])
-def test_decode_split_counts(split):
+@pytest.mark.parametrize("code,mode,bs", [("fp8", "token_sym", 16), ("int4", "group_asym", 32)])
+def test_decode_split_counts(split, code, mode, bs):
     need_gpu()
-    w, L, LL, s, q = _setup("fp8", lens=(7000, 1, 250, 64, 0, 4133), G=8)
+    w, L, LL, s, q = _setup(code, lens=(7000, 1, 250, 64, 0, 4133), G=8, mode=mode, bs=bs)
     got, exp = _run(w, L, LL, s, q, split_blocks=split)
-    assert_decode_close(got, exp, f"split {split}")
+    assert_decode_close(got, exp, f"{code} split {split}")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
@@ -97,11 +100,12 @@ def test_decode_tiny_workload():
     assert_decode_close(got, exp, "tiny")
 
 
-def test_decode_paged_is_bit_identical_to_contiguous_and_permuted():
+@pytest.mark.parametrize("code,mode", [("fp8", "token_sym"), ("int4", "group_asym")])
+def test_decode_paged_is_bit_identical_to_contiguous_and_permuted(code, mode):
     need_gpu()
     outs = []
     for permuted, seed_order in ((False, 0), (True, 1), (True, 2)):
-        w, L, LL, s, q = _setup("fp8", G=8, permuted=permuted, seed=0)
+        w, L, LL, s, q = _setup(code, G=8, permuted=permuted, seed=0, mode=mode)
         if permuted:   # same inputs, a different physical placement
             nb = s.cache.num_blocks
             s2 = OracleSeqs(L, nb, len(LENS), s.tables.shape[1],

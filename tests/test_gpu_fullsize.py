@@ -103,3 +103,24 @@ def test_llama3_8b_layer_int8():
     sample = [int(np.argmax(lens)), int(np.argmin(lens)), 7, 33]
     err = _check(w, P, sample=sample)
     print(f"llama3_8b: max err {err:.2e}")
+
+
+def test_int4_long_context_one_layer():
+    """One layer of the INT4 long-context workload: one 131072-token sequence,
+    64 q / 8 KV heads, per-32-group scale and zero point, block 32."""
+    need_gpu()
+    w = workloads.get("int4_long")
+    P = _populate(w)
+    err = _check(w, P, sample=[0])
+    print(f"int4_long layer: max err {err:.2e}")
+
+
+def test_int4_batch_one_layer():
+    """One layer of the INT4 batch workload: 32 sequences with log-normal
+    lengths (median 4096, cap 65536)."""
+    need_gpu()
+    w = workloads.get("int4_batch")
+    P = _populate(w)
+    lens = P["lens"]
+    err = _check(w, P, sample=[int(np.argmax(lens)), int(np.argmin(lens)), 5])
+    print(f"int4_batch layer: max err {err:.2e}")
