@@ -14,14 +14,10 @@
 
 namespace {
 
-// Work items (sequence x KV head x split, one four-wave workgroup each) the
-// split planner aims for: four per compute unit of an MI355X (256 CUs). A
-// constant, so that the workspace size is a pure function of the arguments.
-constexpr int64_t kTargetItems = 1024;
-constexpr int64_t kMinSplitTokens = 128;
-// A split is shared by four waves of at most 64 blocks each (one 64-lane
-// vector load of block ids per wave).
-constexpr int64_t kMaxSplitBlocks = 256;
+// Explicit split sizes: a split is shared by kDecodeWaves waves of at most
+// kDecodeMaxWaveBlocks blocks each (one 64-lane vector load of block ids per
+// wave).
+constexpr int64_t kMaxSplitBlocks = (int64_t)kvq::kDecodeWaves * kvq::kDecodeMaxWaveBlocks;
 // Tokens per append launch: keeps row indices within int32 inside kernels.
 constexpr int64_t kAppendChunk = int64_t(1) << 22;
 
@@ -60,27 +56,29 @@ int64_t zeros_per_bh(const kvq_layout* L, int side) {
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
-struct SplitPlan {
-  int32_t split_blocks;
-  int32_t num_splits;
-};
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-SplitPlan plan_splits(const kvq_layout* L, int32_t batch, int32_t max_context_len,
-                      int32_t split_blocks) {
+// Upper bound on the (sequence, split) items the device plan can produce for
+// any lengths within [0, max_context_len]: sum_b ceil(n_b / S) with n_b
+// <= nmax = ceil(max_context_len / bs) blocks. For an explicit S it is
+// batch * ceil(nmax / S). For a planned S = 4w, w = clamp(ceil(H N / 2^12),
+// wmin, 64) with N = sum_b n_b: each non-empty sequence adds at most one
+// split beyond n_b / S, so the sum is at most batch + N / S, and N / S is
+// at most 2^12 / (4 H) while w is below 64 and batch nmax / 256 once it is
+// 64. Also at most batch * ceil(nmax / (4 wmin)).
+int64_t decode_item_bound(const kvq_layout* L, int64_t batch, int64_t max_context_len,
+                          int64_t split_blocks) {
   const int64_t bs = L->block_size;
-  const int64_t nblk = (max_context_len + bs - 1) / bs;
-  int64_t c = split_blocks;
-  if (c <= 0) {
-    const int64_t units = (int64_t)batch * L->num_kv_heads * nblk;
-    c = (units + kTargetItems - 1) / kTargetItems;
-    const int64_t cmin = (kMinSplitTokens + bs - 1) / bs;
-    if (c < cmin) c = cmin;
-    if (c > kMaxSplitBlocks) c = kMaxSplitBlocks;
-  }
-  if (nblk > 0 && c > nblk) c = nblk;
-  if (c < 1) c = 1;
-  int64_t ns = nblk > 0 ? (nblk + c - 1) / c : 1;
-  return {(int32_t)c, (int32_t)ns};
+  const int64_t nmax = ceil_div(max_context_len, bs);
+  if (batch == 0 || nmax == 0) return 1;
+  if (split_blocks > 0) return batch * ceil_div(nmax, split_blocks);
+  const int64_t W = kvq::kDecodeWaves;
+  const int64_t wmin = ceil_div(kvq::kDecodeMinWaveTokens, bs);
+  const int64_t a = batch * ceil_div(nmax, W * wmin);
+  const int64_t c = batch + std::max(ceil_div(int64_t(1) << kvq::kDecodeTargetWavesLog2,
+                                              W * L->num_kv_heads),
+                                     ceil_div(batch * nmax, W * kvq::kDecodeMaxWaveBlocks));
+  return std::min(a, c);
 }
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -227,8 +225,7 @@ int64_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t batch, int32_t n
   if (batch < 0 || num_q_heads < 1 || max_context_len < 0 || split_blocks < 0 ||
       split_blocks > kMaxSplitBlocks)
     return KVQ_ERR_INVALID_ARGUMENT;
-  SplitPlan sp = plan_splits(L, batch, max_context_len, split_blocks);
-  const int64_t items = (int64_t)batch * num_q_heads * sp.num_splits;
+  const int64_t items = decode_item_bound(L, batch, max_context_len, split_blocks) * num_q_heads;
   return round_up(items * L->head_dim * 4, 256) + round_up(items * 2 * 4, 256);
 }
 
@@ -255,13 +252,17 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const v
     return KVQ_ERR_INVALID_ARGUMENT;
   if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return KVQ_ERR_INVALID_ARGUMENT;
   if (!kvq::decode_supported(L->k_code, L->v_code, L->k_mode, L->v_mode)) return KVQ_ERR_UNSUPPORTED;
+  // per-channel keys: row b of the batch reads stage row b
+  if (L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM && batch > C->max_seqs)
+    return KVQ_ERR_INVALID_ARGUMENT;
   if (batch == 0) return KVQ_OK;
   if (!q || !out || !block_tables || !context_lens || !workspace) return KVQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_INVALID_ARGUMENT;
   const int64_t need = kvq_decode_workspace_bytes(L, batch, num_q_heads, max_context_len, split_blocks);
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
-  SplitPlan sp = plan_splits(L, batch, max_context_len, split_blocks);
-  const int64_t items = (int64_t)batch * num_q_heads * sp.num_splits;
+  const int64_t bound = decode_item_bound(L, batch, max_context_len, split_blocks);
+  if (bound * L->num_kv_heads > INT32_MAX) return KVQ_ERR_UNSUPPORTED;  // 1-D grid
+  const int64_t items = bound * num_q_heads;
   kvq::DecodePlan p;
   p.q = q;
   p.q_bf16 = q_dtype == KVQ_BF16;
@@ -286,8 +287,9 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const v
   p.block_tables = block_tables;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.context_lens = context_lens;
-  p.split_blocks = sp.split_blocks;
-  p.num_splits = sp.num_splits;
+  p.max_context_len = max_context_len;
+  p.split_blocks = split_blocks;
+  p.item_bound = (int32_t)bound;
   p.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)L->head_dim));
   p.out = out;
   p.out_dtype = out_dtype;

@@ -58,20 +58,161 @@ struct DecodeArgs {
   const float* v_scale;
   const uint8_t* k_zero;
   const uint8_t* v_zero;
+  const uint16_t* k_stage;  // per-channel keys: raw rows of partial blocks
   const int32_t* block_tables;
   const int32_t* context_lens;
   float* ws_acc;
   float* ws_ml;
   int64_t num_blocks;
   int32_t q_bf16;
+  int32_t stage_bf16;
   int32_t Hq;
   int32_t H;
   int32_t G;
   int32_t max_blocks;
-  int32_t split_blocks;
-  int32_t num_splits;
+  int32_t batch;
+  int32_t max_len;       // every context length is cut to this
+  int32_t split_blocks;  // 0: planned from the lengths
   float sm_log2;  // sm_scale * log2(e)
 };
+
+// ---- split planning ---------------------------------------------------------
+// Every workgroup of the split kernel and every wave of the reduce derive the
+// same plan from context_lens alone, so neither a planning launch nor a host
+// synchronization is needed:
+//   n_b  = ceil(min(len_b, max_len) / BS)          blocks of sequence b
+//   S    = split_blocks, or kDecodeWaves * clamp(ceil(H sum_b n_b / 2^12),
+//          ceil(32 / BS), 64)                        blocks per split
+//   ns_b = ceil(n_b / S)                            splits of sequence b
+// Items (b, j), j < ns_b, are numbered sequence-major. The partial of item
+// (b, j) for query head h is row Hq off_b + h ns_b + j of the workspace, with
+// off_b = sum_{b' < b} ns_b', so one head's splits are adjacent. The host
+// bounds sum_b ns_b from batch and max_len alone (the grid and workspace
+// size). Short sequences thus get few splits and the total work is cut into
+// about 4096 wave shares whatever the length mix.
+struct PlanArgs {
+  const int32_t* lens;
+  int32_t batch, max_len, bs, H, split_blocks;
+};
+
+__device__ __forceinline__ PlanArgs plan_args(const int32_t* lens, int batch, int max_len,
+                                              int bs, int H, int split_blocks) {
+  PlanArgs p;
+  p.lens = lens;
+  p.batch = batch;
+  p.max_len = max_len;
+  p.bs = bs;
+  p.H = H;
+  p.split_blocks = split_blocks;
+  return p;
+}
+
+// Cut length of sequence idx (0 past the batch).
+__device__ __forceinline__ int plan_len(const PlanArgs& p, int idx) {
+  return idx < p.batch ? min(max(p.lens[idx], 0), p.max_len) : 0;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Lengths of sequences c0 + 64 u + lane, u < 4. The first 256 are loaded
+// once (len0) and reused by both passes below.
+__device__ __forceinline__ void plan_chunk(const PlanArgs& p, int c0, int lane, const int* len0,
+                                           int* len) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) len[u] = c0 == 0 ? len0[u] : plan_len(p, c0 + u * kWave + lane);
+}
+
+__device__ __forceinline__ int plan_splits_of(const PlanArgs& p, int len, int S) {
+  return ((len + p.bs - 1) / p.bs + S - 1) / S;
+}
+
+// Blocks per split: the caller's, or planned from the total block count.
+__device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, const int* len0) {
+  if (p.split_blocks > 0) return p.split_blocks;
+  int64_t tot = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
+    int len[4];
+    plan_chunk(p, c0, lane, len0, len);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) tot += (len[u] + p.bs - 1) / p.bs;
+  }
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) tot += __shfl_xor(tot, m, kWave);
+  constexpr int64_t kRound = (int64_t(1) << kDecodeTargetWavesLog2) - 1;
+  int64_t w = (tot * p.H + kRound) >> kDecodeTargetWavesLog2;
+  const int wmin = (kDecodeMinWaveTokens + p.bs - 1) / p.bs;
+  w = w < wmin ? wmin : w > kDecodeMaxWaveBlocks ? kDecodeMaxWaveBlocks : w;
+  return kDecodeWaves * (int)w;
+}
+
+struct PlanItem {
+  int b;    // sequence
+  int len;  // its cut length
+  int j;    // split within the sequence
+  int ns;   // splits of the sequence
+  int off;  // splits of all earlier sequences
+  int S;    // blocks per split
+};
+
+// Item `item` of the plan; false past the last item.
+__device__ __forceinline__ bool plan_find_item(const PlanArgs& p, int item, int lane,
+                                               PlanItem& out) {
+  int len0[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) len0[u] = plan_len(p, u * kWave + lane);
+  const int S = plan_split_blocks(p, lane, len0);
+  out.S = S;
+  int off = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
+    int len[4];
+    plan_chunk(p, c0, lane, len0, len);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ns = plan_splits_of(p, len[u], S);
+      const int incl = wave_incl_scan(ns, lane);
+      const int tot = __shfl(incl, kWave - 1, kWave);
+      if (item < off + tot) {
+        const int f = __builtin_ctzll(__ballot(off + incl > item));
+        out.b = c0 + u * kWave + f;
+        out.len = __shfl(len[u], f, kWave);
+        out.ns = __shfl(ns, f, kWave);
+        out.off = off + __shfl(incl, f, kWave) - out.ns;
+        out.j = item - out.off;
+        return true;
+      }
+      off += tot;
+    }
+  }
+  return false;
+}
+
+// Splits of sequence b and of all sequences before it.
+__device__ __forceinline__ void plan_sequence(const PlanArgs& p, int b, int lane, int& off,
+                                              int& ns) {
+  int len0[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) len0[u] = plan_len(p, u * kWave + lane);
+  const int S = plan_split_blocks(p, lane, len0);
+  int acc = 0;
+  for (int c0 = 0; c0 < b; c0 += 4 * kWave) {
+    int len[4];
+    plan_chunk(p, c0, lane, len0, len);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc += c0 + u * kWave + lane < b ? plan_splits_of(p, len[u], S) : 0;
+  }
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+  off = acc;
+  ns = plan_splits_of(p, plan_len(p, b), S);
+}
 
 // Per-lane data of one cache block (BS tokens) for 8-bit codes.
 template <int D, int BS>
@@ -83,9 +224,12 @@ struct Tile8 {
   uint32_t v[NT][4][VB / 4];             // [tile][token i][dword]
   float4v sk[NT];
   float4v sv[NT];
+  float kc[D / 64];                      // per-channel key scales, lane's slice
 };
 
-template <int D, int BS>
+// KCH: keys carry one scale per channel for the whole block
+// (CHANNEL_BLOCK_SYM), loaded as D/64 consecutive floats per lane.
+template <int D, int BS, bool KCH>
 __device__ __forceinline__ void load_tile8(Tile8<D, BS>& t, const DecodeArgs& a,
                                            int64_t bh, int lane) {
   const int r = lane & 15, j = lane >> 4;
@@ -108,8 +252,19 @@ __device__ __forceinline__ void load_tile8(Tile8<D, BS>& t, const DecodeArgs& a,
         t.v[nt][i][0] = *reinterpret_cast<const uint32_t*>(vr);
       }
     }
-    t.sk[nt] = *reinterpret_cast<const float4v*>(a.k_scale + bh * BS + nt * 16 + 4 * j);
+    if constexpr (!KCH)
+      t.sk[nt] = *reinterpret_cast<const float4v*>(a.k_scale + bh * BS + nt * 16 + 4 * j);
     t.sv[nt] = *reinterpret_cast<const float4v*>(a.v_scale + bh * BS + nt * 16 + 4 * j);
+  }
+  if constexpr (KCH) {
+    const float* kc = a.k_scale + bh * D + lane * (D / 64);
+    if constexpr (D == 128) {
+      const float2 w = *reinterpret_cast<const float2*>(kc);
+      t.kc[0] = w.x;
+      t.kc[1] = w.y;
+    } else {
+      t.kc[0] = *kc;
+    }
   }
 }
 
@@ -175,21 +330,50 @@ struct SoftmaxState {
   float4v acc[D / 16];     // O^T accumulators
 };
 
+// Eight raw 16-bit key values to fp16 operands: bf16 values are exact in
+// fp16 within its range (the same bound as for value scales).
+__device__ __forceinline__ half8v raw8_to_h8(const u32x4& w, bool bf16) {
+  if (!bf16) return __builtin_bit_cast(half8v, w);
+  half8v o;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    o[2 * u] = (half_t)bf16_lo(w[u]);
+    o[2 * u + 1] = (half_t)bf16_hi(w[u]);
+  }
+  return o;
+}
+
+// Where the keys of a tile come from.
+enum KeySource {
+  kKeyTokenScale = 0,  // codes; the score takes the token's key scale
+  kKeyChannel = 1,     // codes; per-channel scales are already in the query
+  kKeyRaw = 2,         // raw staged rows, kraw[c] = elements of chunk c
+};
+
 // One 16-token tile: scores, online softmax, PV. TAIL handles the tile that
 // ends past the sequence length.
-template <int CODE, int D, int BS, bool TAIL>
+template <int CODE, int D, int BS, bool TAIL, int KSRC = kKeyTokenScale>
 __device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos0, int L,
                                           const half8v* qop, float cscore, int j,
-                                          SoftmaxState<D>& st) {
+                                          SoftmaxState<D>& st, const u32x4* kraw = nullptr,
+                                          bool raw_bf16 = false, const half8v* qlo = nullptr) {
   constexpr int NCH = D / 32;
   constexpr int NPV = D / 16;
   float4v S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const u32x4& kw = t.k[nt][c / 2];
-    const uint32_t lo = (c & 1) ? kw.z : kw.x;
-    const uint32_t hi = (c & 1) ? kw.w : kw.y;
-    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_h8<CODE>(lo, hi), qop[c], S, 0, 0, 0);
+    half8v kop;
+    if constexpr (KSRC == kKeyRaw) {
+      kop = raw8_to_h8(kraw[c], raw_bf16);
+    } else {
+      const u32x4& kw = t.k[nt][c / 2];
+      const uint32_t lo = (c & 1) ? kw.z : kw.x;
+      const uint32_t hi = (c & 1) ? kw.w : kw.y;
+      kop = codes8_to_h8<CODE>(lo, hi);
+    }
+    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[c], S, 0, 0, 0);
+    if constexpr (KSRC == kKeyChannel)  // low half of the split query
+      S = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo[c], S, 0, 0, 0);
   }
   bool ok[4];
 #pragma unroll
@@ -197,7 +381,7 @@ __device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos
   float s[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    s[e] = S[e] * t.sk[nt][e] * cscore;
+    s[e] = KSRC == kKeyTokenScale ? S[e] * t.sk[nt][e] * cscore : S[e] * cscore;
     if (TAIL && !ok[e]) s[e] = -INFINITY;
   }
   const float mt = colmax4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
@@ -245,27 +429,67 @@ __device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos
 }
 
 // A block whose BS tokens all lie before the sequence end.
-template <int CODE, int D, int BS>
+template <int CODE, int D, int BS, int KSRC = kKeyTokenScale>
 __device__ __forceinline__ void full_block_step(const Tile8<D, BS>& t, int i, int L,
                                                 const half8v* qop, float cscore, int j,
-                                                SoftmaxState<D>& st) {
+                                                SoftmaxState<D>& st,
+                                                const half8v* qlo = nullptr) {
 #pragma unroll
   for (int nt = 0; nt < BS / 16; ++nt)
-    tile_step<CODE, D, BS, false>(t, nt, i * BS + nt * 16, L, qop, cscore, j, st);
+    tile_step<CODE, D, BS, false, KSRC>(t, nt, i * BS + nt * 16, L, qop, cscore, j, st,
+                                        nullptr, false, qlo);
 }
 
-// The sequence's last block when it is only partly filled.
-template <int CODE, int D, int BS>
+// Per-channel keys: the block's scales fold into the query,
+// q'[c] = (q[c] 2^-e) sK[c] in fp32, which enters the MFMA as the sum of two
+// fp16 operands, hi = fp16(q') and lo = fp16(q' - hi): one fp16 rounding of
+// q' would cost 2^-12 relative per term, as much as the whole error budget
+// when a few outlier channels dominate the score. Each lane holds D/64
+// scales of the block; the wave trades them through its own LDS slice `x`
+// (D floats) so that lane (r, j) gets channels [j D/4, (j+1) D/4). The fences
+// only keep the compiler from moving LDS accesses across them: a wave's LDS
+// operations complete in issue order.
+template <int D, int BS>
+__device__ __forceinline__ void channel_query(const Tile8<D, BS>& t, float* x, const float* qs,
+                                              int lane, half8v* qop, half8v* qlo) {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if constexpr (D == 128)
+    *reinterpret_cast<float2*>(x + 2 * lane) = make_float2(t.kc[0], t.kc[1]);
+  else
+    x[lane] = t.kc[0];
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const float* src = x + (lane >> 4) * (D / 4);
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const float4v s0 = *reinterpret_cast<const float4v*>(src + 8 * c);
+    const float4v s1 = *reinterpret_cast<const float4v*>(src + 8 * c + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qp = qs[8 * c + e] * (e < 4 ? s0[e] : s1[e - 4]);
+      const half_t hi = (half_t)qp;
+      qop[c][e] = hi;
+      qlo[c][e] = (half_t)(qp - (float)hi);
+    }
+  }
+}
+
+// The sequence's last block when it is only partly filled. With KRAW the
+// keys come from the staged rows kraw[tile][chunk] instead of the codes.
+template <int CODE, int D, int BS, bool KRAW = false>
 __device__ __forceinline__ void last_block_step(const Tile8<D, BS>& t, int i, int L,
                                                 const half8v* qop, float cscore, int j,
-                                                SoftmaxState<D>& st) {
+                                                SoftmaxState<D>& st,
+                                                const u32x4 (*kraw)[D / 32] = nullptr,
+                                                bool raw_bf16 = false) {
+  constexpr int KS = KRAW ? kKeyRaw : kKeyTokenScale;
 #pragma unroll
   for (int nt = 0; nt < BS / 16; ++nt) {
     const int pos0 = i * BS + nt * 16;
+    const u32x4* kr = KRAW ? kraw[nt] : nullptr;
     if (pos0 + 16 <= L)
-      tile_step<CODE, D, BS, false>(t, nt, pos0, L, qop, cscore, j, st);
+      tile_step<CODE, D, BS, false, KS>(t, nt, pos0, L, qop, cscore, j, st, kr, raw_bf16);
     else if (pos0 < L)
-      tile_step<CODE, D, BS, true>(t, nt, pos0, L, qop, cscore, j, st);
+      tile_step<CODE, D, BS, true, KS>(t, nt, pos0, L, qop, cscore, j, st, kr, raw_bf16);
   }
 }
 
@@ -282,10 +506,13 @@ __device__ __forceinline__ void load_query(const uint16_t* qp, float* qf) {
 }
 
 // One wave's share of a split: blocks [i0, i1) of sequence b, KV head g.
-// Leaves the running softmax state in st.
-template <int CODE, int D, int BS>
+// Leaves the running softmax state in st. KCH: per-channel key scales
+// (CHANNEL_BLOCK_SYM), the partial last block's keys read raw from stage
+// row b; `lds` is the wave's own scratch of at least D floats.
+template <int CODE, int D, int BS, bool KCH = false>
 __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, int L, int nblk,
-                                            int i0, int i1, int lane, SoftmaxState<D>& st) {
+                                            int i0, int i1, int lane, SoftmaxState<D>& st,
+                                            float* lds) {
   constexpr int NCH = D / 32;   // k-chunks of the score MFMA
   constexpr int NBUF = BS == 16 ? 3 : 2;  // blocks in the register ring
   const int r = lane & 15, j = lane >> 4;
@@ -310,11 +537,18 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   qe = max(qe, -126);
   const float qdown = __uint_as_float((uint32_t)(127 - qe) << 23);  // 2^-qe
   const float qup = __uint_as_float((uint32_t)(127 + qe) << 23);    // 2^qe
+  // qs: the scaled query in fp32; qop: its fp16 operand (with per-channel
+  // keys it is only needed for the raw partial block, so it is made there)
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) qf[e] = hcol ? qf[e] * qdown : 0.0f;
+  const float* qs = qf;
   half8v qop[NCH];
+  if constexpr (!KCH) {
 #pragma unroll
-  for (int c = 0; c < NCH; ++c)
+    for (int c = 0; c < NCH; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qop[c][e] = hcol ? (half_t)(qf[8 * c + e] * qdown) : (half_t)0.0f;
+      for (int e = 0; e < 8; ++e) qop[c][e] = (half_t)qs[8 * c + e];
+  }
   const float cscore = hcol ? qup * a.sm_log2 : 0.0f;
 
   // The wave's block ids (at most 64) arrive with one vector load: lane k
@@ -327,12 +561,21 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
     const int32_t id = __builtin_amdgcn_readlane(ids, min(i, ilast) - i0);
     return (int64_t)((id >= 0 && id < a.num_blocks) ? id : 0) * a.H + g;
   };
+  auto block = [&](const Tile8<D, BS>& t, int i) {
+    if constexpr (KCH) {
+      half8v qb[NCH], ql[NCH];
+      channel_query<D, BS>(t, lds, qs, lane, qb, ql);
+      full_block_step<CODE, D, BS, kKeyChannel>(t, i, L, qb, cscore, j, st, ql);
+    } else {
+      full_block_step<CODE, D, BS>(t, i, L, qop, cscore, j, st);
+    }
+  };
   // blocks [i0, ifull) are complete; a partial last block is handled apart
   const bool partial = i1 == nblk && (L % BS) != 0;
   const int ifull = partial ? i1 - 1 : i1;
   Tile8<D, BS> buf[NBUF];
 #pragma unroll
-  for (int u = 0; u < NBUF; ++u) load_tile8<D, BS>(buf[u], a, bh_of(i0 + u), lane);
+  for (int u = 0; u < NBUF; ++u) load_tile8<D, BS, KCH>(buf[u], a, bh_of(i0 + u), lane);
 
   // Steady state: every slot computes one block and refills its buffer with
   // the block NBUF ahead (clamped to the split's last block, so the load
@@ -341,21 +584,43 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   for (; i + NBUF <= ifull; i += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
-      full_block_step<CODE, D, BS>(buf[u], i + u, L, qop, cscore, j, st);
-      load_tile8<D, BS>(buf[u], a, bh_of(i + u + NBUF), lane);
+      block(buf[u], i + u);
+      load_tile8<D, BS, KCH>(buf[u], a, bh_of(i + u + NBUF), lane);
     }
   }
   // Remainder: fewer than NBUF complete blocks, already in buf[0 ..], then
-  // the partial block, if any, which sits in the next buffer.
+  // the partial block, if any, which sits in the next buffer. Per-channel
+  // keys of the partial block are the staged rows of sequence b (rows past
+  // the length are masked).
+  u32x4 kraw[BS / 16][NCH];
+  if constexpr (KCH) {
+    if (partial) {
+#pragma unroll
+      for (int nt = 0; nt < BS / 16; ++nt) {
+        const uint16_t* sp =
+            a.k_stage + (((int64_t)b * a.H + g) * BS + nt * 16 + r) * D + j * (D / 4);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) kraw[nt][c] = *reinterpret_cast<const u32x4*>(sp + 8 * c);
+      }
+    }
+  }
 #pragma unroll
   for (int u = 0; u < NBUF; ++u) {
     if (i + u < ifull) {
-      full_block_step<CODE, D, BS>(buf[u], i + u, L, qop, cscore, j, st);
+      block(buf[u], i + u);
     } else if (i + u == ifull && partial) {
-      last_block_step<CODE, D, BS>(buf[u], i + u, L, qop, cscore, j, st);
+      if constexpr (KCH) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qop[c][e] = (half_t)qs[8 * c + e];
+        last_block_step<CODE, D, BS, true>(buf[u], i + u, L, qop, cscore, j, st, kraw,
+                                           a.stage_bf16 != 0);
+      } else {
+        last_block_step<CODE, D, BS>(buf[u], i + u, L, qop, cscore, j, st);
+      }
     }
   }
-
 }
 
 // ---------------------------------------------------------------------------
@@ -648,10 +913,11 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   }
 }
 
-// A split of kNW * (per-wave share) blocks per (sequence, KV head): the
-// workgroup's waves take consecutive shares of at most 64 blocks each, merge
-// their softmax states through LDS, and wave 0 writes the split's partial.
-constexpr int kNW = 4;
+// One item of the plan per workgroup and KV head: the split's S blocks are
+// cut into kNW consecutive shares of at most 64 blocks, one per wave; the
+// waves merge their softmax states through LDS and wave 0 writes the split's
+// partial.
+constexpr int kNW = kDecodeWaves;
 
 template <int CODE, int MODE, int D, int BS>
 __global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
@@ -661,14 +927,19 @@ void decode_split_kernel(DecodeArgs a) {
   __shared__ float red[kNW][NV + 2][kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, j = lane >> 4;
-  const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x;
-  // lengths beyond the table row (a broken precondition) are cut to it
-  const int L = min(a.context_lens[b], a.max_blocks * BS);
+  // KV head fastest: the H workgroups of one item read the same blocks
+  // (whose heads are adjacent in memory) at about the same time
+  const int g = blockIdx.x % a.H;
+  // every wave derives the same plan, so the early exit is workgroup-uniform
+  const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, BS, a.H, a.split_blocks);
+  PlanItem it;
+  if (!plan_find_item(pa, blockIdx.x / a.H, lane, it)) return;
+  const int S = it.S;
+  const int b = it.b, L = it.len;
   const int nblk = (L + BS - 1) / BS;
-  const int s0 = sp * a.split_blocks;
-  if (s0 >= nblk) return;
-  const int s1 = min(s0 + a.split_blocks, nblk);
-  const int share = (a.split_blocks + kNW - 1) / kNW;
+  const int s0 = it.j * S;
+  const int s1 = min(s0 + S, nblk);
+  const int share = (S + kNW - 1) / kNW;
   const int i0 = s0 + wave * share;
   const int i1 = min(i0 + share, s1);
 
@@ -681,7 +952,8 @@ void decode_split_kernel(DecodeArgs a) {
     if constexpr (CODE == KVQ_CODE_INT4)
       wave_blocks_int4<D, BS, MODE>(a, b, g, L, nblk, i0, i1, lane, st);
     else
-      wave_blocks<CODE, D, BS>(a, b, g, L, nblk, i0, i1, lane, st);
+      wave_blocks<CODE, D, BS, MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM>(a, b, g, L, nblk, i0, i1,
+                                                                     lane, st, &red[wave][0][0]);
   }
 
   // ---- merge the waves' states, then write the split's partial ----------
@@ -710,7 +982,7 @@ void decode_split_kernel(DecodeArgs a) {
   }
   if (r >= a.G) return;
   const int h = g * a.G + r;
-  const int64_t item = ((int64_t)b * a.Hq + h) * a.num_splits + sp;
+  const int64_t item = (int64_t)a.Hq * it.off + (int64_t)h * it.ns + it.j;
   if (j == 0) {
     float2 ml = {M, l};
     *reinterpret_cast<float2*>(a.ws_ml + item * 2) = ml;
@@ -754,10 +1026,11 @@ struct ReduceArgs {
   void* out;
   int32_t out_dtype;
   int32_t Hq;
+  int32_t H;
   int32_t BS;
-  int32_t max_blocks;
+  int32_t batch;
+  int32_t max_len;
   int32_t split_blocks;
-  int32_t num_splits;
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -775,10 +1048,10 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
   constexpr int KB = 32;       // splits per batch of loads
   typedef float floatE __attribute__((ext_vector_type(EPL)));
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int L = min(a.context_lens[b], a.max_blocks * a.BS);
-  const int nblk = (L + a.BS - 1) / a.BS;
-  const int ns = min((nblk + a.split_blocks - 1) / a.split_blocks, a.num_splits);
-  const int64_t base = ((int64_t)b * a.Hq + h) * a.num_splits;
+  const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, a.BS, a.H, a.split_blocks);
+  int off, ns;
+  plan_sequence(pa, b, lane, off, ns);
+  const int64_t base = (int64_t)a.Hq * off + (int64_t)h * ns;
   floatE o;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
@@ -827,25 +1100,27 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
 }
 
 template <int CODE, int MODE, int D, int BS>
-hipError_t launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
-  dim3 grid(a.num_splits, a.H, batch);
+hipError_t launch_split(const DecodeArgs& a, int items, hipStream_t stream) {
+  dim3 grid(items * a.H);
   decode_split_kernel<CODE, MODE, D, BS><<<grid, 64 * kNW, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int CODE, int MODE>
-hipError_t launch_split_shape(const DecodeArgs& a, int d, int bs, int batch, hipStream_t stream) {
+hipError_t launch_split_shape(const DecodeArgs& a, int d, int bs, int items, hipStream_t stream) {
   if (d == 128)
-    return bs == 16 ? launch_split<CODE, MODE, 128, 16>(a, batch, stream)
-                    : launch_split<CODE, MODE, 128, 32>(a, batch, stream);
-  return bs == 16 ? launch_split<CODE, MODE, 64, 16>(a, batch, stream)
-                  : launch_split<CODE, MODE, 64, 32>(a, batch, stream);
+    return bs == 16 ? launch_split<CODE, MODE, 128, 16>(a, items, stream)
+                    : launch_split<CODE, MODE, 128, 32>(a, items, stream);
+  return bs == 16 ? launch_split<CODE, MODE, 64, 16>(a, items, stream)
+                  : launch_split<CODE, MODE, 64, 32>(a, items, stream);
 }
 
 }  // namespace
 
 bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
                       int32_t v_mode) {
+  if (k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM)
+    return k_code == KVQ_CODE_INT8 && v_code == KVQ_CODE_INT8 && v_mode == KVQ_SCALE_TOKEN_SYM;
   if (k_code != v_code || k_mode != v_mode) return false;
   if (k_mode == KVQ_SCALE_TOKEN_SYM)
     return k_code == KVQ_CODE_INT8 || k_code == KVQ_CODE_FP8_E4M3 || k_code == KVQ_CODE_INT4;
@@ -869,21 +1144,27 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
   a.H = p.num_kv_heads;
   a.G = p.num_q_heads / p.num_kv_heads;
   a.max_blocks = p.max_blocks_per_seq;
+  a.batch = p.batch;
+  a.max_len = p.max_context_len;
   a.split_blocks = p.split_blocks;
-  a.num_splits = p.num_splits;
   a.sm_log2 = p.sm_scale * kLog2e;
   a.k_zero = p.k_zero;
   a.v_zero = p.v_zero;
+  a.k_stage = static_cast<const uint16_t*>(p.k_stage);
+  a.stage_bf16 = p.src_bf16;
   hipError_t e;
   const int d = p.head_dim, bs = p.block_size;
   if (p.k_code == KVQ_CODE_FP8_E4M3)
-    e = launch_split_shape<KVQ_CODE_FP8_E4M3, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.batch, stream);
+    e = launch_split_shape<KVQ_CODE_FP8_E4M3, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.item_bound, stream);
+  else if (p.k_code == KVQ_CODE_INT8 && p.k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM)
+    e = launch_split_shape<KVQ_CODE_INT8, KVQ_SCALE_CHANNEL_BLOCK_SYM>(a, d, bs, p.item_bound,
+                                                                      stream);
   else if (p.k_code == KVQ_CODE_INT8)
-    e = launch_split_shape<KVQ_CODE_INT8, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.batch, stream);
+    e = launch_split_shape<KVQ_CODE_INT8, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.item_bound, stream);
   else if (p.k_mode == KVQ_SCALE_GROUP_ASYM)
-    e = launch_split_shape<KVQ_CODE_INT4, KVQ_SCALE_GROUP_ASYM>(a, d, bs, p.batch, stream);
+    e = launch_split_shape<KVQ_CODE_INT4, KVQ_SCALE_GROUP_ASYM>(a, d, bs, p.item_bound, stream);
   else
-    e = launch_split_shape<KVQ_CODE_INT4, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.batch, stream);
+    e = launch_split_shape<KVQ_CODE_INT4, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.item_bound, stream);
   if (e != hipSuccess) return e;
   ReduceArgs ra;
   ra.ws_acc = p.ws_acc;
@@ -892,10 +1173,11 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
   ra.out = p.out;
   ra.out_dtype = p.out_dtype;
   ra.Hq = p.num_q_heads;
+  ra.H = p.num_kv_heads;
   ra.BS = p.block_size;
-  ra.max_blocks = p.max_blocks_per_seq;
+  ra.batch = p.batch;
+  ra.max_len = p.max_context_len;
   ra.split_blocks = p.split_blocks;
-  ra.num_splits = p.num_splits;
   dim3 grid(p.num_q_heads, p.batch);
   if (p.head_dim == 128)
     decode_reduce_kernel<128><<<grid, 64, 0, stream>>>(ra);

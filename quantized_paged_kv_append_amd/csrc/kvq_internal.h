@@ -59,14 +59,26 @@ struct DecodePlan {
   const int32_t* block_tables;
   int32_t max_blocks_per_seq;
   const int32_t* context_lens;
-  int32_t split_blocks;  // cache blocks per split
-  int32_t num_splits;    // splits per sequence in the launch grid
+  int32_t max_context_len;
+  int32_t split_blocks;  // cache blocks per split, 0 = planned on the device
+  int32_t item_bound;    // upper bound on (sequence, split) items: grid size
   float sm_scale;
   void* out;
   int32_t out_dtype;
-  float* ws_acc;  // [batch][Hq][num_splits][d]
-  float* ws_ml;   // [batch][Hq][num_splits][2]
+  float* ws_acc;  // [item_bound][Hq][d]
+  float* ws_ml;   // [item_bound][Hq][2]
 };
+
+// Split planning constants, shared by the host (grid and workspace bounds)
+// and the device (the plan itself). A workgroup of kDecodeWaves waves takes
+// one (sequence, KV head, split) item; each wave streams at most
+// kDecodeMaxWaveBlocks blocks. When the caller leaves split_blocks at 0 the
+// per-wave share is ceil(H * total_blocks / 2^kDecodeTargetWavesLog2),
+// clamped to [ceil(kDecodeMinWaveTokens / bs), kDecodeMaxWaveBlocks].
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeMaxWaveBlocks = 64;
+constexpr int kDecodeTargetWavesLog2 = 12;
+constexpr int kDecodeMinWaveTokens = 32;
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
 bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,

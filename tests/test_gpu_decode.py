@@ -17,8 +17,8 @@ LENS = (37, 80, 5, 1, 16, 0, 17, 300, 15, 33)
 
 
 def _setup(code="int8", d=128, bs=16, G=4, H=2, src="bfloat16", lens=LENS, seed=0,
-           permuted=True, kscale=1.0, name="tiny", mode="token_sym"):
-    w = workloads.get(name, k_code=code, v_code=code, k_mode=mode, v_mode=mode,
+           permuted=True, kscale=1.0, name="tiny", mode="token_sym", vmode=None, fill=0):
+    w = workloads.get(name, k_code=code, v_code=code, k_mode=mode, v_mode=vmode or mode,
                       group_size=32 if mode == "group_asym" else 0,
                       src_dtype=src, head_dim=d, block_size=bs,
                       num_kv_heads=H, num_q_heads=G * H, batch=len(lens),
@@ -29,6 +29,8 @@ def _setup(code="int8", d=128, bs=16, G=4, H=2, src="bfloat16", lens=LENS, seed=
     order = workloads.pool_order(nb, seed=seed, permuted=permuted)
     maxb = int(lens.max()) // bs + 2
     s = OracleSeqs(L, nb, len(lens), maxb, order=order)
+    if fill:
+        s.cache = ref.HostCache(L, nb, len(lens), fill=fill)
     k, v = workloads.kv_rows(w, int(lens.sum()), seed=seed)
     if kscale != 1.0:
         k = (k.float() * kscale).to(w.torch_dtype)
@@ -37,12 +39,14 @@ def _setup(code="int8", d=128, bs=16, G=4, H=2, src="bfloat16", lens=LENS, seed=
     return w, L, LL, s, q
 
 
-def _run(w, L, LL, s, q, out_dtype=torch.float32, sm_scale=0.0, split_blocks=0):
+def _run(w, L, LL, s, q, out_dtype=torch.float32, sm_scale=0.0, split_blocks=0,
+         max_len=None):
     exp = ref.decode(L, s.cache, bits(q), DT[w.src_dtype], s.tables, s.lens,
                      sm_scale=sm_scale, threads=8)
     gc = upload(s.cache, LL)
     got = decode_gpu(LL, gc, q.to(DEV), torch.from_numpy(s.tables).to(DEV),
-                     torch.from_numpy(s.lens).to(DEV), int(s.lens.max()), out_dtype,
+                     torch.from_numpy(s.lens).to(DEV),
+                     int(s.lens.max()) if max_len is None else max_len, out_dtype,
                      sm_scale, split_blocks)
     return got, exp
 
@@ -59,6 +63,31 @@ def test_decode_matches_oracle(code, mode, d, bs, G):
     assert (got[5] == 0).all()           # empty context
 
 
+@pytest.mark.parametrize("src", ["bfloat16", "float16"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 16), (128, 32), (64, 32)])
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
+def test_decode_channel_block_keys(src, d, bs, G):
+    """INT8 keys with one scale per channel per block, the partial last block
+    read raw from the sequence's stage row, INT8 per-token values. Every byte
+    the appends left unwritten is 0xFF (NaN in the float planes and stage),
+    which the decode must never let through."""
+    need_gpu()
+    w, L, LL, s, q = _setup("int8", d, bs, G, src=src, mode="channel_block",
+                            vmode="token_sym", fill=0xFF)
+    got, exp = _run(w, L, LL, s, q)
+    assert_decode_close(got, exp, f"channel keys {src} d{d} bs{bs} G{G}")
+    assert (got[5] == 0).all()
+
+
+@pytest.mark.parametrize("split", [1, 3, 64, 256])
+def test_decode_channel_block_split_counts(split):
+    need_gpu()
+    w, L, LL, s, q = _setup("int8", lens=(7000, 1, 250, 64, 0, 4133), G=8, mode="channel_block",
+                            vmode="token_sym", fill=0xFF)
+    got, exp = _run(w, L, LL, s, q, split_blocks=split)
+    assert_decode_close(got, exp, f"channel keys split {split}")
+
+
 @pytest.mark.parametrize("split", [1, 2, 3, 5, 64, 65, 130, 256])
 @pytest.mark.parametrize("code,mode,bs", [("fp8", "token_sym", 16), ("int4", "group_asym", 32)])
 def test_decode_split_counts(split, code, mode, bs):
@@ -66,6 +95,23 @@ def test_decode_split_counts(split, code, mode, bs):
     w, L, LL, s, q = _setup(code, lens=(7000, 1, 250, 64, 0, 4133), G=8, mode=mode, bs=bs)
     got, exp = _run(w, L, LL, s, q, split_blocks=split)
     assert_decode_close(got, exp, f"{code} split {split}")
+
+
+@pytest.mark.parametrize("split", [0, 3, 40])
+@pytest.mark.parametrize("code,mode,bs", [("int8", "token_sym", 16), ("int4", "group_asym", 32)])
+def test_decode_skewed_batch_over_planning_chunks(split, code, mode, bs):
+    """300 sequences (past one 256-sequence chunk of the split planner): most
+    short, three long, some empty, and a max_context_len above every length,
+    so the launch holds more workgroups than the plan has items."""
+    need_gpu()
+    rng = np.random.default_rng(7)
+    lens = rng.integers(0, 40, 300)
+    lens[[3, 150, 299]] = [5000, 2600, 4100]
+    lens[[0, 256, 257, 298]] = 0
+    w, L, LL, s, q = _setup(code, lens=tuple(int(x) for x in lens), G=4, mode=mode, bs=bs)
+    got, exp = _run(w, L, LL, s, q, split_blocks=split, max_len=int(lens.max()) + bs)
+    assert_decode_close(got, exp, f"{code} skewed split {split}")
+    assert (got[[0, 256, 257, 298]] == 0).all()
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])

@@ -36,12 +36,16 @@ def _populate(w, seed=0, chunk=1 << 20):
                           w.block_size, slots, status, ctx)
     cache = kq.PagedCache(LL, nb, w.batch, device=DEV)
     k, v = workloads.kv_rows(w, T, seed=seed, device=DEV)
+    rows = None
+    if w.k_mode == "channel_block":   # stage row of each token: its sequence
+        rows = torch.from_numpy(np.repeat(np.arange(w.batch, dtype=np.int32), lens)).to(DEV)
     for t0 in range(0, T, chunk):
-        kq.kvq_append(LL, cache, k[t0:t0 + chunk], v[t0:t0 + chunk], slots[t0:t0 + chunk])
+        kq.kvq_append(LL, cache, k[t0:t0 + chunk], v[t0:t0 + chunk], slots[t0:t0 + chunk],
+                      stage_rows=None if rows is None else rows[t0:t0 + chunk])
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     return dict(LL=LL, lens=lens, nb=nb, maxb=maxb, order=order, tables=tables, ctx=ctx,
-                cache=cache, k=k, v=v)
+                cache=cache, k=k, v=v, stack=stack, top=top)
 
 
 def _check(w, P, sample, seed=0):
@@ -54,15 +58,17 @@ def _check(w, P, sample, seed=0):
                                     lens, w.block_size)
     assert st == 0
     assert np.array_equal(otables, P["tables"].cpu().numpy())
-    # oracle append of the sampled sequences only
+    # oracle append of the sampled sequences only (stage row = sequence)
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
     idx = np.concatenate([starts[b] + np.arange(lens[b]) for b in sample]).astype(np.int64)
-    hc = ref.HostCache(L, nb)
+    rows = np.concatenate([np.full(lens[b], b, np.int32) for b in sample])
+    hc = ref.HostCache(L, nb, w.batch)
     ki = bits(P["k"][torch.from_numpy(idx).to(DEV)]).reshape(len(idx), -1)
     vi = bits(P["v"][torch.from_numpy(idx).to(DEV)]).reshape(len(idx), -1)
-    ref.append(L, hc, ki, vi, oslots[idx])
+    ref.append(L, hc, ki, vi, oslots[idx], rows)
     # planes of the sampled sequences' blocks, bytewise
-    H, bs = w.num_kv_heads, w.block_size
+    H, bs, d = w.num_kv_heads, w.block_size, w.head_dim
+    chan = w.k_mode == "channel_block"
     blocks = np.concatenate([otables[b, :(lens[b] + bs - 1) // bs] for b in sample])
     for name in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
         g = P["cache"].planes[name]
@@ -71,20 +77,33 @@ def _check(w, P, sample, seed=0):
         per_block = g.numel() // nb
         gb = g.view(nb, per_block)[torch.from_numpy(blocks).long().to(DEV)].cpu().numpy()
         hb = hc.planes[name].reshape(nb, per_block)[blocks]
+        # per-channel keys: a block's codes and scales exist once it is full
+        chan_k = chan and name in ("k_codes", "k_scale")
         gb, hb = gb.reshape(len(blocks), H, bs, -1), hb.reshape(len(blocks), H, bs, -1)
         o = 0
         for b in sample:   # a partial last block: compare its written rows only
             n = (lens[b] + bs - 1) // bs
             tail = lens[b] - (n - 1) * bs
-            assert np.array_equal(gb[o:o + n - 1], hb[o:o + n - 1]), (name, b)
-            assert np.array_equal(gb[o + n - 1, :, :tail], hb[o + n - 1, :, :tail]), (name, b)
+            full = n if tail == bs else n - 1
+            assert np.array_equal(gb[o:o + full], hb[o:o + full]), (name, b)
+            if full < n and not chan_k:
+                assert np.array_equal(gb[o + n - 1, :, :tail], hb[o + n - 1, :, :tail]), (name, b)
             o += n
-    # decode: every query head of the sampled sequences
+    if chan:   # staged rows of the partial last blocks
+        gs = P["cache"].planes["k_stage"].cpu().numpy().reshape(w.batch, H, bs, d * 2)
+        hs = hc.planes["k_stage"].reshape(w.batch, H, bs, d * 2)
+        for b in sample:
+            tail = lens[b] % bs
+            assert np.array_equal(gs[b, :, :tail], hs[b, :, :tail]), ("k_stage", b)
+    # decode: every query head of the sampled sequences (the oracle attends
+    # over the sampled sequences only; the others get length 0)
     q = workloads.queries(w, seed=seed, device=DEV)
     got = decode_gpu(P["LL"], P["cache"], q, P["tables"], P["ctx"], int(lens.max()))
-    exp = ref.decode(L, hc, bits(q[torch.as_tensor(sample, device=DEV)]), DT[w.src_dtype],
-                     otables[sample], lens[sample], threads=16)
-    return assert_decode_close(got[torch.as_tensor(sample, device=DEV)], exp, w.name)
+    olens = np.zeros_like(lens)
+    olens[sample] = lens[sample]
+    exp = ref.decode(L, hc, bits(q), DT[w.src_dtype], otables, olens, threads=16)
+    P["oracle"] = dict(hc=hc, stack=ostack, top=otop, tables=otables)
+    return assert_decode_close(got[torch.as_tensor(sample, device=DEV)], exp[sample], w.name)
 
 
 def test_llama3_70b_one_layer_fp8():
@@ -124,3 +143,47 @@ def test_int4_batch_one_layer():
     lens = P["lens"]
     err = _check(w, P, sample=[int(np.argmax(lens)), int(np.argmin(lens)), 5])
     print(f"int4_batch layer: max err {err:.2e}")
+
+
+def test_mixed_continuous_step_one_layer():
+    """The mixed workload at full size (256 sequences, log-normal lengths
+    median 2048, cap 32768, INT8 per-channel-per-block keys with staging, INT8
+    per-token values), then one continuous step: 8 new tokens per sequence
+    reserved, appended and decoded."""
+    need_gpu()
+    w = workloads.get("mixed")
+    P = _populate(w)
+    lens = P["lens"]
+    sample = [int(np.argmax(lens)), int(np.argmin(lens)), 3, 100, 255]
+    err = _check(w, P, sample=sample)
+    print(f"mixed populate: max err {err:.2e}")
+
+    # one step: reserve, append (stage rows = sequence), decode
+    B, n, bs = w.batch, w.new_tokens, w.block_size
+    L = oracle_layout(w)
+    O = P["oracle"]
+    new_tok = np.full(B, n, np.int32)
+    slots = torch.empty(B * n, dtype=torch.int64, device=DEV)
+    status = torch.empty(1, dtype=torch.int32, device=DEV)
+    kq.kvq_blocks_reserve(P["stack"], P["top"], P["tables"], P["ctx"],
+                          torch.from_numpy(new_tok).to(DEV), bs, slots, status, P["ctx"])
+    k2, v2 = workloads.kv_rows(w, B * n, seed=0, device=DEV, chunk=7)
+    rows = torch.from_numpy(np.repeat(np.arange(B, dtype=np.int32), n)).to(DEV)
+    kq.kvq_append(P["LL"], P["cache"], k2, v2, slots, stage_rows=rows)
+    oslots, st = ref.blocks_reserve(O["stack"], O["top"], O["tables"], lens, new_tok, bs)
+    torch.cuda.synchronize()
+    assert st == 0 and int(status.item()) == 0
+    assert np.array_equal(O["tables"], P["tables"].cpu().numpy())
+    assert np.array_equal(oslots, slots.cpu().numpy())
+    idx = np.concatenate([b * n + np.arange(n) for b in sample]).astype(np.int64)
+    ref.append(L, O["hc"], bits(k2.cpu()[idx]).reshape(len(idx), -1),
+               bits(v2.cpu()[idx]).reshape(len(idx), -1), oslots[idx],
+               np.repeat(np.asarray(sample, np.int32), n))
+    lens2 = lens + n
+    q = workloads.queries(w, seed=0, device=DEV, step=1)
+    got = decode_gpu(P["LL"], P["cache"], q, P["tables"], P["ctx"], int(lens2.max()))
+    olens = np.zeros_like(lens2)
+    olens[sample] = lens2[sample]
+    exp = ref.decode(L, O["hc"], bits(q), DT[w.src_dtype], O["tables"], olens, threads=16)
+    err = assert_decode_close(got[torch.as_tensor(sample, device=DEV)], exp[sample], "mixed step")
+    print(f"mixed step: max err {err:.2e}")
