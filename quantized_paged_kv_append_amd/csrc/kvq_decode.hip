@@ -112,6 +112,19 @@ __device__ __forceinline__ int plan_len(const PlanArgs& p, int idx) {
   return idx < p.batch ? min(max(p.lens[idx], 0), p.max_len) : 0;
 }
 
+// Cut lengths of sequences c0 + 64 u + lane, u < 4, with the four loads
+// issued back to back (clamped indices; the empty asm keeps the compiler
+// from moving each load into its own branch and wait).
+__device__ __forceinline__ void plan_len4(const PlanArgs& p, int c0, int lane, int* len) {
+  int v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = p.lens[min(c0 + u * kWave + lane, p.batch - 1)];
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    len[u] = c0 + u * kWave + lane < p.batch ? min(max(v[u], 0), p.max_len) : 0;
+}
+
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
@@ -125,8 +138,12 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // once (len0) and reused by both passes below.
 __device__ __forceinline__ void plan_chunk(const PlanArgs& p, int c0, int lane, const int* len0,
                                            int* len) {
+  if (c0 == 0) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) len[u] = c0 == 0 ? len0[u] : plan_len(p, c0 + u * kWave + lane);
+    for (int u = 0; u < 4; ++u) len[u] = len0[u];
+  } else {
+    plan_len4(p, c0, lane, len);
+  }
 }
 
 __device__ __forceinline__ int plan_splits_of(const PlanArgs& p, int len, int S) {
@@ -165,8 +182,7 @@ struct PlanItem {
 __device__ __forceinline__ bool plan_find_item(const PlanArgs& p, int item, int lane,
                                                PlanItem& out) {
   int len0[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) len0[u] = plan_len(p, u * kWave + lane);
+  plan_len4(p, 0, lane, len0);
   const int S = plan_split_blocks(p, lane, len0);
   out.S = S;
   int off = 0;
@@ -197,8 +213,7 @@ __device__ __forceinline__ bool plan_find_item(const PlanArgs& p, int item, int 
 __device__ __forceinline__ void plan_sequence(const PlanArgs& p, int b, int lane, int& off,
                                               int& ns) {
   int len0[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) len0[u] = plan_len(p, u * kWave + lane);
+  plan_len4(p, 0, lane, len0);
   const int S = plan_split_blocks(p, lane, len0);
   int acc = 0;
   for (int c0 = 0; c0 < b; c0 += 4 * kWave) {
