@@ -734,15 +734,32 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
 
 // Nibble pairs of bytes 0 and 2 (shift 0 / 4) or 1 and 3 (shift 8 / 12) as
 // two fp16 values 1024 + nibble.
+// Nibbles SHIFT/4 and SHIFT/4 + 4 of g as the fp16 pair 1024 + q:
+// ((g >> SHIFT) & m) | o with m = 0x000F000F and o = 0x64006400 held in
+// registers by the caller, so that the and-or is one instruction (a VOP3
+// encoding takes no two literal constants on gfx9).
 template <int SHIFT>
-__device__ __forceinline__ half2v nib2(uint32_t g) {
-  return __builtin_bit_cast(half2v, ((g >> SHIFT) & 0x000F000Fu) | 0x64006400u);
+__device__ __forceinline__ half2v nib2(uint32_t g, uint32_t m, uint32_t o) {
+  return __builtin_bit_cast(half2v, ((g >> SHIFT) & m) | o);
 }
 
-template <int D, int MODE>
-__device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, int L, bool tail,
+// Register-resident constants of the 4-bit conversions.
+struct Nib4Consts {
+  uint32_t m;    // 0x000F000F
+  uint32_t o;    // 0x64006400
+  uint32_t m64;  // 0x64646464, the fp16 exponent byte for v_perm
+};
+__device__ __forceinline__ Nib4Consts nib4_consts() {
+  Nib4Consts k{0x000F000Fu, 0x64006400u, 0x64646464u};
+  asm volatile("" : "+v"(k.m), "+v"(k.o), "+v"(k.m64));
+  return k;
+}
+
+template <int D, int MODE, bool TAIL>
+__device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, int L,
                                            const half8v* qop, float cscore, int j,
-                                           SoftmaxState<D>& st) {
+                                           SoftmaxState<D>& st, const Nib4Consts& kc) {
+  constexpr bool tail = TAIL;
   constexpr int NS = D / 32;
   constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
   // ---- key operands, chunk c = slice c -----------------------------------
@@ -760,15 +777,15 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
   for (int c = 0; c < NS; ++c) {
     uint32_t gc = g[c];
     half2v bias;
-    if constexpr (ASYM) {
-      const uint32_t z = (t.zk >> (8 * c)) & 0xFFu;
-      bias = __builtin_bit_cast(half2v, (z | (z << 16)) | 0x64006400u);
+    if constexpr (ASYM) {  // fp16 pair 1024 + z, z = byte c of zk
+      const uint32_t sel = (uint32_t)c | (4u << 8) | ((uint32_t)c << 16) | (4u << 24);
+      bias = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kc.m64, t.zk, sel));
     } else {
       gc ^= 0x88888888u;  // two's-complement nibble q -> q + 8
       bias = __builtin_bit_cast(half2v, 0x64086408u);
     }
-    const half2v h0 = nib2<0>(gc) - bias, h1 = nib2<4>(gc) - bias;
-    const half2v h2 = nib2<8>(gc) - bias, h3 = nib2<12>(gc) - bias;
+    const half2v h0 = nib2<0>(gc, kc.m, kc.o) - bias, h1 = nib2<4>(gc, kc.m, kc.o) - bias;
+    const half2v h2 = nib2<8>(gc, kc.m, kc.o) - bias, h3 = nib2<12>(gc, kc.m, kc.o) - bias;
     half8v ka;
     ka[0] = h0[0]; ka[1] = h0[1]; ka[2] = h1[0]; ka[3] = h1[1];
     ka[4] = h2[0]; ka[5] = h2[1]; ka[6] = h3[0]; ka[7] = h3[1];
@@ -783,7 +800,7 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
     float v = 0.0f;
     if constexpr (ASYM) {
 #pragma unroll
-      for (int c = 0; c < NS; ++c) v += S[c][e] * t.sk[4 * c + e];
+      for (int c = 0; c < NS; ++c) v = __builtin_fmaf(S[c][e], t.sk[4 * c + e], v);
     } else {
       v = S[0][e] * t.sk[e];
     }
@@ -826,15 +843,15 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
     pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
     uint32_t Gi = G[i];
     half2v b02, b13;
-    if constexpr (ASYM) {
-      b02 = __builtin_bit_cast(half2v, (Z[i] & 0x00FF00FFu) | 0x64006400u);
-      b13 = __builtin_bit_cast(half2v, ((Z[i] >> 8) & 0x00FF00FFu) | 0x64006400u);
+    if constexpr (ASYM) {  // fp16 pairs 1024 + z: bytes 0, 2 and bytes 1, 3 of Z[i]
+      b02 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kc.m64, Z[i], 0x04020400u));
+      b13 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kc.m64, Z[i], 0x04030401u));
     } else {
       Gi ^= 0x88888888u;
       b02 = b13 = __builtin_bit_cast(half2v, 0x64086408u);
     }
-    const half2v x02 = nib2<0>(Gi) - b02, x13 = nib2<8>(Gi) - b13;
-    const half2v y02 = nib2<4>(Gi) - b02, y13 = nib2<12>(Gi) - b13;
+    const half2v x02 = nib2<0>(Gi, kc.m, kc.o) - b02, x13 = nib2<8>(Gi, kc.m, kc.o) - b13;
+    const half2v y02 = nib2<4>(Gi, kc.m, kc.o) - b02, y13 = nib2<12>(Gi, kc.m, kc.o) - b13;
     half4v va0, va1;
     va0[0] = x02[0]; va0[1] = x02[1]; va0[2] = x13[0]; va0[3] = x13[1];
     va1[0] = y02[0]; va1[1] = y02[1]; va1[2] = y13[0]; va1[3] = y13[1];
@@ -894,6 +911,7 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   half8v qop[D / 32];
   float cscore;
   query_int4<D>(a, a.q + ((int64_t)b * a.Hq + h) * D, j, hcol, qop, cscore);
+  const Nib4Consts kc = nib4_consts();
   (void)nblk;
 
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
@@ -915,16 +933,16 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   for (; tt + NBUF <= tfull; tt += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
-      tile4_step<D, MODE>(buf[u], (tt + u) * 16, L, false, qop, cscore, j, st);
+      tile4_step<D, MODE, false>(buf[u], (tt + u) * 16, L, qop, cscore, j, st, kc);
       load(buf[u], tt + u + NBUF);
     }
   }
 #pragma unroll
   for (int u = 0; u < NBUF; ++u) {
     if (tt + u < tfull)
-      tile4_step<D, MODE>(buf[u], (tt + u) * 16, L, false, qop, cscore, j, st);
+      tile4_step<D, MODE, false>(buf[u], (tt + u) * 16, L, qop, cscore, j, st, kc);
     else if (tt + u < t1)
-      tile4_step<D, MODE>(buf[u], (tt + u) * 16, L, true, qop, cscore, j, st);
+      tile4_step<D, MODE, true>(buf[u], (tt + u) * 16, L, qop, cscore, j, st, kc);
   }
 }
 
