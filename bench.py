@@ -16,6 +16,7 @@ and the CPU oracle timed on a bounded sample of the same workload
 (cpu_baseline).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,35 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+HERE = os.path.dirname(os.path.abspath(__file__))
+# sources whose change invalidates committed decode counters
+DECODE_SOURCES = ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_api.cpp")
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(HERE, "quantized_paged_kv_append_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per kvq_decode_attention launch (split + reduce kernels)
+    from the committed rocprofv3 counter summary of this workload, when it
+    was taken on the current decode sources; None otherwise."""
+    path = os.path.join(HERE, "profiles", f"decode_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            key, sep, val = line.strip().strip("`").partition(": ")
+            if sep:
+                fields[key] = val.strip()
+    if fields.get("source_hash") != decode_source_hash():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -250,7 +280,7 @@ def main():
         "append_bytes_per_token": append_bytes_per_token(w),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": committed_traffic(w.name),
             "kernel": "decode_split_kernel + decode_reduce_kernel (one kvq_decode_attention)",
             "bytes_per_launch": dec_bytes_launch,
         },
