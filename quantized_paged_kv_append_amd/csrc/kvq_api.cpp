@@ -260,8 +260,11 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const v
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_INVALID_ARGUMENT;
   const int64_t need = kvq_decode_workspace_bytes(L, batch, num_q_heads, max_context_len, split_blocks);
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  // the device planner counts blocks in int32
+  if ((int64_t)batch * ceil_div(max_context_len, L->block_size) > INT32_MAX)
+    return KVQ_ERR_UNSUPPORTED;
   const int64_t bound = decode_item_bound(L, batch, max_context_len, split_blocks);
-  if (bound * L->num_kv_heads > INT32_MAX) return KVQ_ERR_UNSUPPORTED;  // 1-D grid
+  if (bound * L->num_kv_heads > INT32_MAX - 16) return KVQ_ERR_UNSUPPORTED;  // 1-D grid
   const int64_t items = bound * num_q_heads;
   kvq::DecodePlan p;
   p.q = q;

@@ -125,13 +125,23 @@ __device__ __forceinline__ void plan_len4(const PlanArgs& p, int c0, int lane, i
     len[u] = c0 + u * kWave + lane < p.batch ? min(max(v[u], 0), p.max_len) : 0;
 }
 
+// Inclusive prefix sum over the wave with DPP moves (no LDS round trips):
+// shifts 1, 2, 4, 8 within each row of 16 lanes, then the last lane of row 0
+// and row 2 into rows 1 and 3, then lane 31 into rows 2 and 3. Lanes with no
+// source read 0 (the `old` operand).
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+  (void)lane;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x, int lane) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x, lane), kWave - 1);
 }
 
 // Lengths of sequences c0 + 64 u + lane, u < 4. The first 256 are loaded
@@ -153,15 +163,15 @@ __device__ __forceinline__ int plan_splits_of(const PlanArgs& p, int len, int S)
 // Blocks per split: the caller's, or planned from the total block count.
 __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, const int* len0) {
   if (p.split_blocks > 0) return p.split_blocks;
-  int64_t tot = 0;
+  // block counts fit in int32: the host bounds batch * ceil(max_len / bs)
+  int tot32 = 0;
   for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
     int len[4];
     plan_chunk(p, c0, lane, len0, len);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) tot += (len[u] + p.bs - 1) / p.bs;
+    for (int u = 0; u < 4; ++u) tot32 += (len[u] + p.bs - 1) / p.bs;
   }
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) tot += __shfl_xor(tot, m, kWave);
+  const int64_t tot = wave_sum(tot32, lane);
   constexpr int64_t kRound = (int64_t(1) << kDecodeTargetWavesLog2) - 1;
   int64_t w = (tot * p.H + kRound) >> kDecodeTargetWavesLog2;
   const int wmin = (kDecodeMinWaveTokens + p.bs - 1) / p.bs;
@@ -193,15 +203,15 @@ __device__ __forceinline__ bool plan_find_item(const PlanArgs& p, int item, int 
     for (int u = 0; u < 4; ++u) {
       const int ns = plan_splits_of(p, len[u], S);
       const int incl = wave_incl_scan(ns, lane);
-      const int tot = __shfl(incl, kWave - 1, kWave);
+      const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
       if (item < off + tot) {
         const int f = __builtin_ctzll(__ballot(off + incl > item));
         out.b = c0 + u * kWave + f;
-        out.len = __shfl(len[u], f, kWave);
-        out.ns = __shfl(ns, f, kWave);
-        out.off = off + __shfl(incl, f, kWave) - out.ns;
+        out.len = __builtin_amdgcn_readlane(len[u], f);
+        out.ns = __builtin_amdgcn_readlane(ns, f);
+        out.off = off + __builtin_amdgcn_readlane(incl, f) - out.ns;
         out.j = item - out.off;
-        return true;
+        return out.b < p.batch;   // always, for consistent lengths
       }
       off += tot;
     }
@@ -223,9 +233,7 @@ __device__ __forceinline__ void plan_sequence(const PlanArgs& p, int b, int lane
     for (int u = 0; u < 4; ++u)
       acc += c0 + u * kWave + lane < b ? plan_splits_of(p, len[u], S) : 0;
   }
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
-  off = acc;
+  off = wave_sum(acc, lane);
   ns = plan_splits_of(p, plan_len(p, b), S);
 }
 
@@ -572,9 +580,13 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   // that no load leaves the cache planes.
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
   const int32_t ids = trow[min(i0 + lane, ilast)];
+  // Prefetches past the share's last block (the ring's final refills, never
+  // computed on) read physical block 0, which every wave shares, so they hit
+  // in cache instead of fetching a block from HBM again.
   auto bh_of = [&](int i) -> int64_t {
     const int32_t id = __builtin_amdgcn_readlane(ids, min(i, ilast) - i0);
-    return (int64_t)((id >= 0 && id < a.num_blocks) ? id : 0) * a.H + g;
+    const bool ok = i <= ilast && id >= 0 && id < a.num_blocks;
+    return (int64_t)(ok ? id : 0) * a.H + g;
   };
   auto block = [&](const Tile8<D, BS>& t, int i) {
     if constexpr (KCH) {
@@ -921,9 +933,12 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   const int tfull = min(t1, L / 16);               // tiles wholly below L
   const int tlast = t1 - 1;
   auto load = [&](Tile4<D, MODE>& t, int tile) {
-    const int ti = min(tile, tlast);
-    const int32_t id = __builtin_amdgcn_readlane(ids, ti / TPB - i0);
-    const int64_t bh = (int64_t)((id >= 0 && id < a.num_blocks) ? id : 0) * a.H + g;
+    // refills past the last tile read tile 0 of the shared block 0
+    const bool past = tile > tlast;
+    const int ti = past ? 0 : tile;
+    const int32_t id = __builtin_amdgcn_readlane(ids, past ? 0 : ti / TPB - i0);
+    const bool ok = !past && id >= 0 && id < a.num_blocks;
+    const int64_t bh = (int64_t)(ok ? id : 0) * a.H + g;
     load_tile4<D, BS, MODE>(t, a, bh, ti % TPB, lane);
   };
   Tile4<D, MODE> buf[NBUF];
@@ -946,6 +961,25 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   }
 }
 
+// Workgroup -> (item, KV head). The KV head varies fastest, so the H
+// workgroups of one item read the same blocks (whose heads are adjacent in
+// memory) at about the same time. Consecutive workgroups go to the 8 XCDs in
+// turn, and each XCD has its own L2; with H dividing 16 the order within
+// each run of 16 workgroups also puts heads 2m and 2m + 1 of an item on the
+// same XCD (workgroups q and q + 8), so that a 128-byte line holding both
+// heads' 64-byte scale tiles (block 16) is fetched by one L2, not two.
+__device__ __forceinline__ void workgroup_item(int H, int w, int& item, int& g) {
+  if ((H & 1) == 0 && 16 % H == 0) {
+    const int per = H >> 1;                  // head pairs per item
+    const int x = w & 7, slot = (w >> 3) & 1;
+    item = (w >> 4) * (8 / per) + x / per;
+    g = 2 * (x % per) + slot;
+  } else {
+    item = w / H;
+    g = w % H;
+  }
+}
+
 // One item of the plan per workgroup and KV head: the split's S blocks are
 // cut into kNW consecutive shares of at most 64 blocks, one per wave; the
 // waves merge their softmax states through LDS and wave 0 writes the split's
@@ -960,13 +994,12 @@ void decode_split_kernel(DecodeArgs a) {
   __shared__ float red[kNW][NV + 2][kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, j = lane >> 4;
-  // KV head fastest: the H workgroups of one item read the same blocks
-  // (whose heads are adjacent in memory) at about the same time
-  const int g = blockIdx.x % a.H;
+  int wg_item, g;
+  workgroup_item(a.H, blockIdx.x, wg_item, g);
   // every wave derives the same plan, so the early exit is workgroup-uniform
   const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, BS, a.H, a.split_blocks);
   PlanItem it;
-  if (!plan_find_item(pa, blockIdx.x / a.H, lane, it)) return;
+  if (!plan_find_item(pa, wg_item, lane, it)) return;
   const int S = it.S;
   const int b = it.b, L = it.len;
   const int nblk = (L + BS - 1) / BS;
@@ -1134,7 +1167,8 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
 
 template <int CODE, int MODE, int D, int BS>
 hipError_t launch_split(const DecodeArgs& a, int items, hipStream_t stream) {
-  dim3 grid(items * a.H);
+  // whole runs of 16 workgroups (see workgroup_item); the extra ones find no item
+  dim3 grid((items * a.H + 15) / 16 * 16);
   decode_split_kernel<CODE, MODE, D, BS><<<grid, 64 * kNW, 0, stream>>>(a);
   return hipGetLastError();
 }
