@@ -1005,7 +1005,9 @@ void decode_split_kernel(DecodeArgs a) {
   const int nblk = (L + BS - 1) / BS;
   const int s0 = it.j * S;
   const int s1 = min(s0 + S, nblk);
-  const int share = (S + kNW - 1) / kNW;
+  // the item's blocks split evenly over the waves (a short last split or a
+  // short sequence keeps every wave busy)
+  const int share = (s1 - s0 + kNW - 1) / kNW;
   const int i0 = s0 + wave * share;
   const int i1 = min(i0 + share, s1);
 
