@@ -247,11 +247,16 @@ int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch,
  * sum_t p_t with p_t = exp(s_t - max s), s_t = (q . k_t) * sm_scale, over the
  * first context_lens[b] tokens; a sequence with no tokens gets out = 0.
  * Keys and values are dequantized as the scale mode defines; under
- * CHANNEL_BLOCK_SYM the partial last block is read raw from k_stage row b.
+ * CHANNEL_BLOCK_SYM the partial last block is read raw from k_stage row b;
+ * a NONE16 cache is read as stored.
  * The result depends on physical block ids only through the data they hold.
+ * Supported: both sides INT8, E4M3 or INT4 under TOKEN_SYM, both INT4 under
+ * GROUP_ASYM, INT8 CHANNEL_BLOCK_SYM keys with INT8 TOKEN_SYM values, and
+ * both NONE16; other layouts return KVQ_ERR_UNSUPPORTED.
  * Preconditions: num_q_heads is a multiple of H and num_q_heads / H <= 16;
  * dequantized values v satisfy |v| / 127 < 65504 (fp16 range of the folded
- * value scale). */
+ * value scale); bf16 keys and values read raw (NONE16, staged rows) lie
+ * within fp16's range. */
 kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache,
                                 const void* q, int32_t q_dtype, int32_t batch,
                                 int32_t num_q_heads, const int32_t* block_tables,

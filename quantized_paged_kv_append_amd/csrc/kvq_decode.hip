@@ -42,6 +42,8 @@
 //    blocks of the split and are read with v_readlane.
 //  * Partials (m, l, acc) per split go to the workspace; decode_reduce merges
 //    them with the log-sum-exp rule.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -142,6 +144,25 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 
 __device__ __forceinline__ int wave_sum(int x, int lane) {
   return __builtin_amdgcn_readlane(wave_incl_scan(x, lane), kWave - 1);
+}
+
+// Max and sum of a float over the wave by the same DPP pattern, with -inf
+// (max) or 0 (sum) in lanes that have no source; the result is lane 63's.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce_f(float x) {
+  const int idle = MAX ? __float_as_int(-INFINITY) : 0;
+  auto step = [&](float v, float w) { return MAX ? fmaxf(v, w) : v + w; };
+#define KVQ_DPP_STEP(ctrl, rmask)                                                       \
+  x = step(x, __int_as_float(__builtin_amdgcn_update_dpp(idle, __float_as_int(x), ctrl, \
+                                                          rmask, 0xF, false)))
+  KVQ_DPP_STEP(0x111, 0xF);
+  KVQ_DPP_STEP(0x112, 0xF);
+  KVQ_DPP_STEP(0x114, 0xF);
+  KVQ_DPP_STEP(0x118, 0xF);
+  KVQ_DPP_STEP(0x142, 0xA);
+  KVQ_DPP_STEP(0x143, 0xC);
+#undef KVQ_DPP_STEP
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
 }
 
 // Lengths of sequences c0 + 64 u + lane, u < 4. The first 256 are loaded
@@ -528,6 +549,124 @@ __device__ __forceinline__ void load_query(const uint16_t* qp, float* qf) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit passthrough (KVQ_CODE_NONE16): rows hold the source values. Keys
+// enter the score MFMA as fp16 like the staged rows above (lane (r, j):
+// elements [j d/4, (j+1) d/4) of token r). Values: lane (r, j) loads
+// elements [r d/16, (r+1) d/16) of tokens 4j..4j+3, and the operand of PV
+// MFMA c is element c of those four tokens -- the same output mapping as
+// the 8-bit codes. bf16 values convert to fp16 exactly within fp16's range.
+// ---------------------------------------------------------------------------
+template <int D, int BS>
+struct TileRaw {
+  static constexpr int NT = BS / 16;
+  static constexpr int NCH = D / 32;   // 16-byte key vectors per lane per tile
+  static constexpr int VW = D / 32;    // 32-bit value words per token per lane
+  u32x4 k[NT][NCH];
+  uint32_t v[NT][4][VW];               // [tile][token i][word]
+};
+
+template <int D, int BS>
+__device__ __forceinline__ void load_tile_raw(TileRaw<D, BS>& t, const DecodeArgs& a,
+                                              int64_t bh, int lane) {
+  const int r = lane & 15, j = lane >> 4;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_codes) + bh * BS * D;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_codes) + bh * BS * D;
+#pragma unroll
+  for (int nt = 0; nt < TileRaw<D, BS>::NT; ++nt) {
+    const uint16_t* kr = kb + (nt * 16 + r) * D + j * (D / 4);
+#pragma unroll
+    for (int c = 0; c < TileRaw<D, BS>::NCH; ++c)
+      t.k[nt][c] = *reinterpret_cast<const u32x4*>(kr + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* vr = vb + (nt * 16 + 4 * j + i) * D + r * (D / 16);
+      if constexpr (D == 128) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(vr);
+        t.v[nt][i][0] = w.x; t.v[nt][i][1] = w.y; t.v[nt][i][2] = w.z; t.v[nt][i][3] = w.w;
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vr);
+        t.v[nt][i][0] = w.x; t.v[nt][i][1] = w.y;
+      }
+    }
+  }
+}
+
+// Element c (0 or 1 of word w) of four tokens' value words as fp16.
+__device__ __forceinline__ half4v raw_vop(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                          bool hi, bool bf16) {
+  half4v o;
+  if (bf16) {
+    o[0] = (half_t)(hi ? bf16_hi(w0) : bf16_lo(w0));
+    o[1] = (half_t)(hi ? bf16_hi(w1) : bf16_lo(w1));
+    o[2] = (half_t)(hi ? bf16_hi(w2) : bf16_lo(w2));
+    o[3] = (half_t)(hi ? bf16_hi(w3) : bf16_lo(w3));
+  } else {
+    const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+    const uint32_t x = __builtin_amdgcn_perm(w1, w0, sel), y = __builtin_amdgcn_perm(w3, w2, sel);
+    o = __builtin_bit_cast(half4v, (u32x2){x, y});
+  }
+  return o;
+}
+
+template <int D, int BS, bool TAIL>
+__device__ __forceinline__ void tile_step_raw(const TileRaw<D, BS>& t, int nt, int pos0, int L,
+                                              const half8v* qop, float cscore, int j,
+                                              SoftmaxState<D>& st, bool bf16) {
+  constexpr int NCH = D / 32;
+  constexpr int NPV = D / 16;
+  float4v S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(raw8_to_h8(t.k[nt][c], bf16), qop[c], S, 0, 0, 0);
+  bool ok[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ok[e] = !TAIL || pos0 + 4 * j + e < L;
+  float s[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[e] = (TAIL && !ok[e]) ? -INFINITY : S[e] * cscore;
+  const float mt = colmax4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+  const float mn = fmaxf(st.m, mt);
+  const float msafe = mn == -INFINITY ? 0.0f : mn;
+  if (__any(mn > st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
+  }
+  st.m = mn;
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = (TAIL && !ok[e]) ? 0.0f : __builtin_amdgcn_exp2f(s[e] - msafe);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  half4v pop;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pop[e] = (half_t)p[e];
+#pragma unroll
+  for (int c = 0; c < NPV; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = t.v[nt][i][c / 2];
+      if (TAIL && !ok[i]) w[i] = 0u;   // rows past the length may hold NaN
+    }
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(raw_vop(w[0], w[1], w[2], w[3], c & 1, bf16),
+                                                      pop, st.acc[c], 0, 0, 0);
+  }
+}
+
+// Tile-type dispatch for the block streaming below.
+template <int D, int BS, bool KCH>
+__device__ __forceinline__ void load_tile(Tile8<D, BS>& t, const DecodeArgs& a, int64_t bh,
+                                          int lane) {
+  load_tile8<D, BS, KCH>(t, a, bh, lane);
+}
+template <int D, int BS, bool KCH>
+__device__ __forceinline__ void load_tile(TileRaw<D, BS>& t, const DecodeArgs& a, int64_t bh,
+                                          int lane) {
+  load_tile_raw<D, BS>(t, a, bh, lane);
+}
+
 // One wave's share of a split: blocks [i0, i1) of sequence b, KV head g.
 // Leaves the running softmax state in st. KCH: per-channel key scales
 // (CHANNEL_BLOCK_SYM), the partial last block's keys read raw from stage
@@ -588,8 +727,15 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
     const bool ok = i <= ilast && id >= 0 && id < a.num_blocks;
     return (int64_t)(ok ? id : 0) * a.H + g;
   };
-  auto block = [&](const Tile8<D, BS>& t, int i) {
-    if constexpr (KCH) {
+  constexpr bool RAW = CODE == KVQ_CODE_NONE16;
+  using TileT = typename std::conditional<RAW, TileRaw<D, BS>, Tile8<D, BS>>::type;
+  const bool raw_bf16 = a.stage_bf16 != 0;
+  auto block = [&](const TileT& t, int i) {
+    if constexpr (RAW) {
+#pragma unroll
+      for (int nt = 0; nt < BS / 16; ++nt)
+        tile_step_raw<D, BS, false>(t, nt, i * BS + nt * 16, L, qop, cscore, j, st, raw_bf16);
+    } else if constexpr (KCH) {
       half8v qb[NCH], ql[NCH];
       channel_query<D, BS>(t, lds, qs, lane, qb, ql);
       full_block_step<CODE, D, BS, kKeyChannel>(t, i, L, qb, cscore, j, st, ql);
@@ -600,9 +746,9 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   // blocks [i0, ifull) are complete; a partial last block is handled apart
   const bool partial = i1 == nblk && (L % BS) != 0;
   const int ifull = partial ? i1 - 1 : i1;
-  Tile8<D, BS> buf[NBUF];
+  TileT buf[NBUF];
 #pragma unroll
-  for (int u = 0; u < NBUF; ++u) load_tile8<D, BS, KCH>(buf[u], a, bh_of(i0 + u), lane);
+  for (int u = 0; u < NBUF; ++u) load_tile<D, BS, KCH>(buf[u], a, bh_of(i0 + u), lane);
 
   // Steady state: every slot computes one block and refills its buffer with
   // the block NBUF ahead (clamped to the split's last block, so the load
@@ -612,7 +758,7 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       block(buf[u], i + u);
-      load_tile8<D, BS, KCH>(buf[u], a, bh_of(i + u + NBUF), lane);
+      load_tile<D, BS, KCH>(buf[u], a, bh_of(i + u + NBUF), lane);
     }
   }
   // Remainder: fewer than NBUF complete blocks, already in buf[0 ..], then
@@ -636,7 +782,16 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
     if (i + u < ifull) {
       block(buf[u], i + u);
     } else if (i + u == ifull && partial) {
-      if constexpr (KCH) {
+      if constexpr (RAW) {
+#pragma unroll
+        for (int nt = 0; nt < BS / 16; ++nt) {
+          const int pos0 = (i + u) * BS + nt * 16;
+          if (pos0 + 16 <= L)
+            tile_step_raw<D, BS, false>(buf[u], nt, pos0, L, qop, cscore, j, st, raw_bf16);
+          else if (pos0 < L)
+            tile_step_raw<D, BS, true>(buf[u], nt, pos0, L, qop, cscore, j, st, raw_bf16);
+        }
+      } else if constexpr (KCH) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
 #pragma unroll
@@ -1134,9 +1289,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
       if (u < cnt)
         v[u] = *reinterpret_cast<const floatE*>(a.ws_acc + (base + s0 + u) * D + EPL * lane);
     // running merge across batches: M is the max over all splits seen so far
-    float mb = ml.x;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mb = fmaxf(mb, __shfl_xor(mb, m, kWave));
+    const float mb = wave_reduce_f<true>(ml.x);
     const float Mn = fmaxf(M, mb);
     const float rescale = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
     o *= rescale;
@@ -1151,8 +1304,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
         o += wu * v[u];
       }
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m, kWave);
+  den = wave_reduce_f<false>(den);
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   o *= inv;
   const int64_t ob = ((int64_t)b * a.Hq + h) * D + EPL * lane;
@@ -1191,6 +1343,7 @@ bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
   if (k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM)
     return k_code == KVQ_CODE_INT8 && v_code == KVQ_CODE_INT8 && v_mode == KVQ_SCALE_TOKEN_SYM;
   if (k_code != v_code || k_mode != v_mode) return false;
+  if (k_code == KVQ_CODE_NONE16) return true;
   if (k_mode == KVQ_SCALE_TOKEN_SYM)
     return k_code == KVQ_CODE_INT8 || k_code == KVQ_CODE_FP8_E4M3 || k_code == KVQ_CODE_INT4;
   return k_mode == KVQ_SCALE_GROUP_ASYM && k_code == KVQ_CODE_INT4;
@@ -1223,7 +1376,9 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
   a.stage_bf16 = p.src_bf16;
   hipError_t e;
   const int d = p.head_dim, bs = p.block_size;
-  if (p.k_code == KVQ_CODE_FP8_E4M3)
+  if (p.k_code == KVQ_CODE_NONE16)
+    e = launch_split_shape<KVQ_CODE_NONE16, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.item_bound, stream);
+  else if (p.k_code == KVQ_CODE_FP8_E4M3)
     e = launch_split_shape<KVQ_CODE_FP8_E4M3, KVQ_SCALE_TOKEN_SYM>(a, d, bs, p.item_bound, stream);
   else if (p.k_code == KVQ_CODE_INT8 && p.k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM)
     e = launch_split_shape<KVQ_CODE_INT8, KVQ_SCALE_CHANNEL_BLOCK_SYM>(a, d, bs, p.item_bound,

@@ -147,8 +147,14 @@ def test_append_and_decode_reject_bad_arguments_on_host():
     assert dec(wsb=16) == kq.KVQ_ERR_WORKSPACE_TOO_SMALL
     assert dec(tables=None) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert dec(batch=0) == kq.KVQ_OK
-    L4 = kq.make_layout(8, 128, 32, "int4", k_mode="group_asym", group_size=32)
-    assert L4 is not None
+    # a valid layout whose decode this library does not build: FP8 keys with
+    # INT8 values
+    Lmix = kq.make_layout(8, 128, 16, "fp8", v_code="int8")
+    assert kq.kvq_layout_check(Lmix) == kq.KVQ_OK
+    cmix = _fake_cache(Lmix)
+    assert lib.kvq_decode_attention(C.byref(Lmix), C.byref(cmix), p, kq.KVQ_BF16, 2, 32, p, 4,
+                                    p, 64, 0.0, 0, p, kq.KVQ_F32, p, 1 << 30,
+                                    None) == kq.KVQ_ERR_UNSUPPORTED
 
 
 def test_pool_calls_reject_bad_arguments_on_host():

@@ -52,7 +52,8 @@ def _run(w, L, LL, s, q, out_dtype=torch.float32, sm_scale=0.0, split_blocks=0,
 
 
 @pytest.mark.parametrize("code,mode", [("int8", "token_sym"), ("fp8", "token_sym"),
-                                       ("int4", "token_sym"), ("int4", "group_asym")])
+                                       ("int4", "token_sym"), ("int4", "group_asym"),
+                                       ("none16", "token_sym")])
 @pytest.mark.parametrize("d,bs", [(128, 16), (64, 16), (128, 32), (64, 32)])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 def test_decode_matches_oracle(code, mode, d, bs, G):
@@ -61,6 +62,18 @@ def test_decode_matches_oracle(code, mode, d, bs, G):
     got, exp = _run(w, L, LL, s, q)
     assert_decode_close(got, exp, f"{code}/{mode} d{d} bs{bs} G{G}")
     assert (got[5] == 0).all()           # empty context
+
+
+@pytest.mark.parametrize("src", ["bfloat16", "float16"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 32)])
+def test_decode_passthrough_16bit(src, d, bs):
+    """NONE16: rows read as stored (fp16, or bf16 converted to fp16); every
+    byte the appends left unwritten is 0xFF, a NaN pattern in both formats."""
+    need_gpu()
+    w, L, LL, s, q = _setup("none16", d, bs, 8, src=src, fill=0xFF)
+    got, exp = _run(w, L, LL, s, q)
+    assert_decode_close(got, exp, f"none16 {src} d{d} bs{bs}")
+    assert (got[5] == 0).all()
 
 
 @pytest.mark.parametrize("src", ["bfloat16", "float16"])

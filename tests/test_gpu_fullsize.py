@@ -114,6 +114,15 @@ def test_llama3_70b_one_layer_fp8():
     print(f"llama3_70b layer: max err {err:.2e}")
 
 
+def test_llama3_70b_one_layer_bf16_passthrough():
+    """The 70B layer shape with the 16-bit passthrough cache."""
+    need_gpu()
+    w = workloads.get("llama3_70b_bf16")
+    P = _populate(w)
+    err = _check(w, P, sample=[0, 7, 15])
+    print(f"llama3_70b_bf16 layer: max err {err:.2e}")
+
+
 def test_llama3_8b_layer_int8():
     need_gpu()
     w = workloads.get("llama3_8b")

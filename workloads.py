@@ -15,6 +15,8 @@ Strategies ...", "How vLLM Implements KV Cache Optimization"):
               8 KV heads, d 128, bf16, 4 key outlier channels x8, INT8, bs 16
   llama3_70b  80 layers, 16 sequences x 32768 tokens, 64 q / 8 KV heads, d 128,
               bf16, FP8 E4M3, bs 16
+  llama3_70b_bf16  the same shape with the 16-bit passthrough cache (the
+              unquantized baseline the quantized codes are measured against)
   int4_long   80 layers, 1 sequence of 131072 tokens, INT4 with per-32 group
               scale and zero point, bs 32
   int4_batch  80 layers, 32 sequences, log-normal lengths (median 4096, cap
@@ -80,6 +82,10 @@ WORKLOADS = {
                            "fp8", "token_sym", "token_sym",
                            lengths=("fixed", 32768), n_outliers=4,
                            outlier_factor=8.0),
+    "llama3_70b_bf16": Workload("llama3_70b_bf16", 80, 16, 64, 8, 128, 16, "bfloat16",
+                                "none16", "none16", "token_sym", "token_sym",
+                                lengths=("fixed", 32768), n_outliers=4,
+                                outlier_factor=8.0),
     "int4_long": Workload("int4_long", 80, 1, 64, 8, 128, 32, "bfloat16", "int4",
                           "int4", "group_asym", "group_asym", group_size=32,
                           lengths=("fixed", 131072), n_outliers=4,
