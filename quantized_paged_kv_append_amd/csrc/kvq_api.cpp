@@ -14,10 +14,8 @@
 
 namespace {
 
-// Explicit split sizes: a split is shared by kDecodeWaves waves of at most
-// kDecodeMaxWaveBlocks blocks each (one 64-lane vector load of block ids per
-// wave).
-constexpr int64_t kMaxSplitBlocks = (int64_t)kvq::kDecodeWaves * kvq::kDecodeMaxWaveBlocks;
+// Largest caller-given split (cache blocks shared by a workgroup's waves).
+constexpr int64_t kMaxSplitBlocks = 256;
 // Tokens per append launch: keeps row indices within int32 inside kernels.
 constexpr int64_t kAppendChunk = int64_t(1) << 22;
 
@@ -65,7 +63,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // wmin, 64) with N = sum_b n_b: each non-empty sequence adds at most one
 // split beyond n_b / S, so the sum is at most batch + N / S, and N / S is
 // at most 2^12 / (4 H) while w is below 64 and batch nmax / 256 once it is
-// 64. Also at most batch * ceil(nmax / (4 wmin)).
+// 64. Also at most batch * ceil(nmax / (4 wmin)). The plan for nearly equal
+// lengths, w = clamp(ceil(H N / 2^11), wmin, 128), gives fewer items than
+// either term.
 int64_t decode_item_bound(const kvq_layout* L, int64_t batch, int64_t max_context_len,
                           int64_t split_blocks) {
   const int64_t bs = L->block_size;
@@ -77,7 +77,7 @@ int64_t decode_item_bound(const kvq_layout* L, int64_t batch, int64_t max_contex
   const int64_t a = batch * ceil_div(nmax, W * wmin);
   const int64_t c = batch + std::max(ceil_div(int64_t(1) << kvq::kDecodeTargetWavesLog2,
                                               W * L->num_kv_heads),
-                                     ceil_div(batch * nmax, W * kvq::kDecodeMaxWaveBlocks));
+                                     ceil_div(batch * nmax, W * 64));
   return std::min(a, c);
 }
 

@@ -182,21 +182,56 @@ __device__ __forceinline__ int plan_splits_of(const PlanArgs& p, int len, int S)
 }
 
 // Blocks per split: the caller's, or planned from the total block count.
+// Max over the wave of non-negative ints (DPP, as wave_incl_scan).
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_i(int x) {
+  const int idle = MAX ? 0 : INT32_MAX;
+#define KVQ_DPP_STEP(ctrl, rmask)                                                         \
+  {                                                                                        \
+    const int y = __builtin_amdgcn_update_dpp(idle, x, ctrl, rmask, 0xF, false);          \
+    x = MAX ? max(x, y) : min(x, y);                                                       \
+  }
+  KVQ_DPP_STEP(0x111, 0xF);
+  KVQ_DPP_STEP(0x112, 0xF);
+  KVQ_DPP_STEP(0x114, 0xF);
+  KVQ_DPP_STEP(0x118, 0xF);
+  KVQ_DPP_STEP(0x142, 0xA);
+  KVQ_DPP_STEP(0x143, 0xC);
+#undef KVQ_DPP_STEP
+  return __builtin_amdgcn_readlane(x, kWave - 1);
+}
+
+// Blocks per split: the caller's, or planned from the block counts. A batch
+// whose non-empty sequences have nearly equal block counts (max <= 9/8 min)
+// is cut into one round of shares (2^kDecodeUniformWavesLog2 waves: two
+// workgroups per CU, up to kDecodeMaxWaveBlocks blocks each), since equal
+// items need no balancing and fewer, longer shares pay the start-up chain
+// less often; any other batch into twice as many shorter shares (at most 64
+// blocks), which the dispatcher balances.
 __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, const int* len0) {
   if (p.split_blocks > 0) return p.split_blocks;
   // block counts fit in int32: the host bounds batch * ceil(max_len / bs)
-  int tot32 = 0;
+  int tot32 = 0, nmax = 0, nmin = INT32_MAX;
   for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
     int len[4];
     plan_chunk(p, c0, lane, len0, len);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) tot32 += (len[u] + p.bs - 1) / p.bs;
+    for (int u = 0; u < 4; ++u) {
+      const int n = (len[u] + p.bs - 1) / p.bs;
+      tot32 += n;
+      nmax = max(nmax, n);
+      if (n > 0) nmin = min(nmin, n);
+    }
   }
   const int64_t tot = wave_sum(tot32, lane);
-  constexpr int64_t kRound = (int64_t(1) << kDecodeTargetWavesLog2) - 1;
-  int64_t w = (tot * p.H + kRound) >> kDecodeTargetWavesLog2;
+  nmax = wave_reduce_i<true>(nmax);
+  nmin = wave_reduce_i<false>(nmin);
+  const bool uniform = (int64_t)nmax * 8 <= (int64_t)nmin * 9;
+  const int lg = uniform ? kDecodeUniformWavesLog2 : kDecodeTargetWavesLog2;
+  const int cap = uniform ? kDecodeMaxWaveBlocks : 64;
+  int64_t w = (tot * p.H + (int64_t(1) << lg) - 1) >> lg;
   const int wmin = (kDecodeMinWaveTokens + p.bs - 1) / p.bs;
-  w = w < wmin ? wmin : w > kDecodeMaxWaveBlocks ? kDecodeMaxWaveBlocks : w;
+  w = w < wmin ? wmin : w > cap ? cap : w;
   return kDecodeWaves * (int)w;
 }
 
@@ -257,6 +292,33 @@ __device__ __forceinline__ void plan_sequence(const PlanArgs& p, int b, int lane
   off = wave_sum(acc, lane);
   ns = plan_splits_of(p, plan_len(p, b), S);
 }
+
+// Block ids of blocks [i0, ilast] of one sequence, 64 at a time: lane k of
+// `cur` holds the id of block base + k and lane k of `nxt` that of block
+// base + 64 + k (indices past ilast read ilast). A wave asks only for blocks
+// in [base, base + 128) and calls advance() once it has passed base + 64, so
+// each 64-id load is issued 64 blocks before its first use.
+struct IdWindow {
+  const int32_t* row;
+  int base, ilast;
+  int32_t cur, nxt;
+  __device__ __forceinline__ void init(const int32_t* trow, int i0, int il, int lane) {
+    row = trow;
+    base = i0;
+    ilast = il;
+    cur = row[min(i0 + lane, il)];
+    nxt = row[min(i0 + kWave + lane, il)];
+  }
+  __device__ __forceinline__ int32_t id(int i) const {
+    const int k = min(i, ilast) - base;
+    return __builtin_amdgcn_readlane(k < kWave ? cur : nxt, k & (kWave - 1));
+  }
+  __device__ __forceinline__ void advance(int lane) {
+    base += kWave;
+    cur = nxt;
+    nxt = row[min(base + kWave + lane, ilast)];
+  }
+};
 
 // Per-lane data of one cache block (BS tokens) for 8-bit codes.
 template <int D, int BS>
@@ -713,17 +775,16 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   }
   const float cscore = hcol ? qup * a.sm_log2 : 0.0f;
 
-  // The wave's block ids (at most 64) arrive with one vector load: lane k
-  // holds the id of block i0 + k; v_readlane hands each to the scalar unit.
-  // Ids outside the pool (a broken precondition) are clamped to block 0 so
-  // that no load leaves the cache planes.
-  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
-  const int32_t ids = trow[min(i0 + lane, ilast)];
+  // Block ids arrive 64 at a time with one vector load and reach the scalar
+  // unit through v_readlane. Ids outside the pool (a broken precondition)
+  // are clamped to block 0 so that no load leaves the cache planes.
+  IdWindow ids;
+  ids.init(a.block_tables + (int64_t)b * a.max_blocks, i0, ilast, lane);
   // Prefetches past the share's last block (the ring's final refills, never
   // computed on) read physical block 0, which every wave shares, so they hit
   // in cache instead of fetching a block from HBM again.
   auto bh_of = [&](int i) -> int64_t {
-    const int32_t id = __builtin_amdgcn_readlane(ids, min(i, ilast) - i0);
+    const int32_t id = ids.id(i);
     const bool ok = i <= ilast && id >= 0 && id < a.num_blocks;
     return (int64_t)(ok ? id : 0) * a.H + g;
   };
@@ -755,6 +816,7 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   // sequence never branches and the wait counts stay exact).
   int i = i0;
   for (; i + NBUF <= ifull; i += NBUF) {
+    if (i - ids.base >= kWave) ids.advance(lane);
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       block(buf[u], i + u);
@@ -1081,8 +1143,8 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   const Nib4Consts kc = nib4_consts();
   (void)nblk;
 
-  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
-  const int32_t ids = trow[min(i0 + lane, ilast)];
+  IdWindow ids;
+  ids.init(a.block_tables + (int64_t)b * a.max_blocks, i0, ilast, lane);
   const int t0 = i0 * TPB;
   const int t1 = min(i1 * TPB, (L + 15) / 16);   // tiles holding tokens < L
   const int tfull = min(t1, L / 16);               // tiles wholly below L
@@ -1091,7 +1153,7 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
     // refills past the last tile read tile 0 of the shared block 0
     const bool past = tile > tlast;
     const int ti = past ? 0 : tile;
-    const int32_t id = __builtin_amdgcn_readlane(ids, past ? 0 : ti / TPB - i0);
+    const int32_t id = ids.id(past ? ids.base : ti / TPB);
     const bool ok = !past && id >= 0 && id < a.num_blocks;
     const int64_t bh = (int64_t)(ok ? id : 0) * a.H + g;
     load_tile4<D, BS, MODE>(t, a, bh, ti % TPB, lane);
@@ -1101,6 +1163,7 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   for (int u = 0; u < NBUF; ++u) load(buf[u], t0 + u);
   int tt = t0;
   for (; tt + NBUF <= tfull; tt += NBUF) {
+    if (tt / TPB - ids.base >= kWave) ids.advance(lane);
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       tile4_step<D, MODE, false>(buf[u], (tt + u) * 16, L, qop, cscore, j, st, kc);

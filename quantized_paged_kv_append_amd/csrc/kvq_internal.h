@@ -71,13 +71,16 @@ struct DecodePlan {
 
 // Split planning constants, shared by the host (grid and workspace bounds)
 // and the device (the plan itself). A workgroup of kDecodeWaves waves takes
-// one (sequence, KV head, split) item; each wave streams at most
-// kDecodeMaxWaveBlocks blocks. When the caller leaves split_blocks at 0 the
-// per-wave share is ceil(H * total_blocks / 2^kDecodeTargetWavesLog2),
-// clamped to [ceil(kDecodeMinWaveTokens / bs), kDecodeMaxWaveBlocks].
+// one (sequence, KV head, split) item. When the caller leaves split_blocks
+// at 0 the per-wave share is ceil(H * total_blocks / 2^lg) blocks, clamped to
+// [ceil(kDecodeMinWaveTokens / bs), cap], with lg, cap =
+// kDecodeUniformWavesLog2, kDecodeMaxWaveBlocks for a batch of nearly equal
+// lengths and kDecodeTargetWavesLog2, 64 otherwise. The host's item bound
+// assumes the second pair, which yields more items for any lengths.
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeMaxWaveBlocks = 64;
+constexpr int kDecodeMaxWaveBlocks = 128;
 constexpr int kDecodeTargetWavesLog2 = 12;
+constexpr int kDecodeUniformWavesLog2 = 11;
 constexpr int kDecodeMinWaveTokens = 32;
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
