@@ -196,81 +196,88 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
   }
 }
 
-// 4-bit codes. Nibble layout: with n = D/32 slices, element 32 i + 2 r + t
-// sits in byte n r + i (nibble t). Lane j of a row owns r in [R j, R j + R)
-// (R = 16 / RL) for every slice i, i.e. elements 32 i + 2 R j + k, k < 2R,
-// and writes the 4 contiguous bytes 4 j .. 4 j + 3.
+// min over the four lanes of a quad (DPP quad permutations, no LDS)
+__device__ __forceinline__ float quad_min(float v) {
+  v = fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));
+  v = fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));
+  return v;
+}
+
+// the value of lane `src` of each quad, in every lane of that quad
+template <int SRC>
+__device__ __forceinline__ float quad_bcast(float v) {
+  constexpr int ctrl = SRC | (SRC << 2) | (SRC << 4) | (SRC << 6);
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+}
+
+// 4-bit codes. Nibble layout: with n = D/32 slices (= 32-element groups),
+// element 32 i + 2 r + t sits in byte n r + i (nibble t). A wave covers 16
+// consecutive tokens of one head, four lanes per row; lane k of a row loads
+// elements [32 i + 8 k, 32 i + 8 k + 8) of every slice i (16-byte loads) and
+// so owns pairs r in [4 k, 4 k + 4), i.e. the n * 4 contiguous output bytes
+// starting at byte 4 n k.
 // MODE TOKEN_SYM: symmetric codes in [-7, 7] stored as q & 0xF.
-// MODE GROUP_ASYM: group = slice (group_size 32), unsigned codes with zero
-// point.
+// MODE GROUP_ASYM: unsigned codes with a zero point per slice; lane k of a
+// quad computes slice k's scale and zero point (k < n) and the quad shares
+// them by DPP broadcasts.
 template <int MODE, int D, bool BF16>
 __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
-  constexpr int RL = D / 8;
-  constexpr int RPW = kWave / RL;
-  constexpr int NS = D / 32;  // slices (= groups)
-  constexpr int R = 16 / RL;  // r values per lane
-  constexpr int K = 2 * R;    // elements per slice per lane
+  constexpr int NS = D / 32;       // slices per row, one 16-byte load each
+  constexpr int RPW = kWave / 4;   // rows per wave (tokens of one group)
   const SideArgs S = a.side[a.side0 + blockIdx.y];
   const int lane = threadIdx.x & (kWave - 1);
-  const int j = lane % RL;
-  const int row_lane0 = lane - j;
-  const int64_t rows = a.num_tokens * a.H;
-  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
-  for (int64_t base = wave * RPW; base < rows; base += nwaves * RPW) {
-    const int64_t r = base + lane / RL;
-    const bool in = r < rows;
-    const int64_t t = in ? r / a.H : 0;
-    const int h = in ? (int)(r % a.H) : 0;
+  const int k = lane & 3;
+  const uint32_t groups = ((uint32_t)a.num_tokens + 15u) / 16u;
+  const uint32_t items = groups * (uint32_t)a.H;   // (token group, head) pairs
+  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const uint32_t nwaves = gridDim.x * blockDim.x / kWave;
+  for (uint32_t it = wave; it < items; it += nwaves) {
+    const uint32_t tg = div_h(it, a);
+    const uint32_t h = it - tg * (uint32_t)a.H;
+    const uint32_t t = tg * RPW + (uint32_t)(lane >> 2);
+    const bool in = t < (uint32_t)a.num_tokens;
     const int64_t slot = in ? a.slots[t] : -1;
-    const int64_t blk = slot >= 0 ? slot / a.bs : 0;
-    const bool live = in && slot >= 0 && blk < a.num_blocks;
-    const int off = slot >= 0 ? (int)(slot % a.bs) : 0;
-    float x[NS][K];
-    const uint16_t* row = S.src + t * S.row_stride + (int64_t)h * D;
+    const int64_t blk = slot >> a.bs_shift;
+    const bool live = slot >= 0 && blk < a.num_blocks;
+    const int64_t rowi = (blk * a.H + h) * a.bs + (slot & (a.bs - 1));
+    const uint16_t* src = S.src + (int64_t)(in ? t : 0) * S.row_stride + h * D + 8 * k;
+    float x[NS][8];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const uint16_t* p = row + 32 * i + K * j;
-      if constexpr (K == 2) {
-        uint32_t w = in ? *reinterpret_cast<const uint32_t*>(p) : 0u;
-        unpack2<BF16>(w, x[i][0], x[i][1]);
-      } else {
-        u32x2 w = {0u, 0u};
-        if (in) w = *reinterpret_cast<const u32x2*>(p);
-        unpack2<BF16>(w.x, x[i][0], x[i][1]);
-        unpack2<BF16>(w.y, x[i][2], x[i][3]);
-      }
+      const u32x4 w = in ? *reinterpret_cast<const u32x4*>(src + 32 * i) : (u32x4){0u, 0u, 0u, 0u};
+      unpack2<BF16>(w.x, x[i][0], x[i][1]);
+      unpack2<BF16>(w.y, x[i][2], x[i][3]);
+      unpack2<BF16>(w.z, x[i][4], x[i][5]);
+      unpack2<BF16>(w.w, x[i][6], x[i][7]);
     }
-    const int64_t rowi = ((int64_t)blk * a.H + h) * a.bs + off;
-    int q[NS][K];
-    bool tie = false;
-    if (MODE == KVQ_SCALE_TOKEN_SYM) {
+    int q[NS][8];
+    if constexpr (MODE == KVQ_SCALE_TOKEN_SYM) {
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < NS; ++i)
 #pragma unroll
-        for (int k = 0; k < K; ++k) amax = fmaxf(amax, fabsf(x[i][k]));
-      amax = group_max<RL>(amax);
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+      amax = quad_max(amax);
       const float s = amax == 0.0f ? 1.0f : div_rn(amax, 7.0f);
-      const float inv = div_rn(1.0f, s);
-      tie = recip_unsafe(s);
+      const float inv = __builtin_amdgcn_rcpf(s);   // within 1 ulp of 1/s
+      bool tie = recip_unsafe(s);
 #pragma unroll
       for (int i = 0; i < NS; ++i)
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const float y = x[i][k] * inv;
+        for (int e = 0; e < 8; ++e) {
+          const float y = x[i][e] * inv;
           const float qq = rne(y);
           tie |= near_half(y, qq);
-          q[i][k] = (int)fminf(fmaxf(qq, -7.0f), 7.0f);
+          q[i][e] = (int)fminf(fmaxf(qq, -7.0f), 7.0f);
         }
-      if (tie) {
+      if (tie) {  // rare: this lane's codes from the exact quotient
 #pragma unroll
         for (int i = 0; i < NS; ++i)
 #pragma unroll
-          for (int k = 0; k < K; ++k)
-            q[i][k] = (int)fminf(fmaxf(rne(div_rn(x[i][k], s)), -7.0f), 7.0f);
+          for (int e = 0; e < 8; ++e)
+            q[i][e] = (int)fminf(fmaxf(rne(div_rn(x[i][e], s)), -7.0f), 7.0f);
       }
-      if (live && j == 0) S.scale[rowi] = s;
+      if (live && k == 0) S.scale[rowi] = s;
     } else {
       // per-slice range, widened to contain 0
       float mn[NS], mx[NS];
@@ -279,81 +286,91 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
         mn[i] = 0.0f;
         mx[i] = 0.0f;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          mn[i] = fminf(mn[i], x[i][k]);
-          mx[i] = fmaxf(mx[i], x[i][k]);
+        for (int e = 0; e < 8; ++e) {
+          mn[i] = fminf(mn[i], x[i][e]);
+          mx[i] = fmaxf(mx[i], x[i][e]);
         }
-        mn[i] = group_min<RL>(mn[i]);
-        mx[i] = group_max<RL>(mx[i]);
+        mn[i] = quad_min(mn[i]);
+        mx[i] = quad_max(mx[i]);
       }
-      // lane j computes the scalars of group j % NS; the row gathers them
-      const int gown = j % NS;
+      // lane k computes slice k's scalars (k < NS), the quad shares them
       float mno = mn[0], mxo = mx[0];
 #pragma unroll
       for (int i = 1; i < NS; ++i)
-        if (gown == i) {
+        if (k == i) {
           mno = mn[i];
           mxo = mx[i];
         }
-      float so = 1.0f, invo = 1.0f;
-      int zo = 0;
+      float so = 1.0f, zf = 0.0f;
       if (mxo != mno) {
         so = div_rn(mxo - mno, 15.0f);
-        zo = (int)fminf(fmaxf(rne(div_rn(-mno, so)), 0.0f), 15.0f);
-        invo = div_rn(1.0f, so);
+        zf = fminf(fmaxf(rne(div_rn(-mno, so)), 0.0f), 15.0f);
       }
-      float sg[NS], ig[NS];
+      float sg[NS];
       int zg[NS];
+      bool tie = false;
+      sg[0] = quad_bcast<0>(so);
+      zg[0] = (int)quad_bcast<0>(zf);
+      sg[1] = quad_bcast<1>(so);
+      zg[1] = (int)quad_bcast<1>(zf);
+      if constexpr (NS == 4) {
+        sg[2] = quad_bcast<2>(so);
+        zg[2] = (int)quad_bcast<2>(zf);
+        sg[3] = quad_bcast<3>(so);
+        zg[3] = (int)quad_bcast<3>(zf);
+      }
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        sg[i] = __shfl(so, row_lane0 + i, kWave);
-        ig[i] = __shfl(invo, row_lane0 + i, kWave);
-        zg[i] = __shfl(zo, row_lane0 + i, kWave);
         tie |= recip_unsafe(sg[i]);
-      }
+        const float inv = __builtin_amdgcn_rcpf(sg[i]);
 #pragma unroll
-      for (int i = 0; i < NS; ++i)
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const float y = x[i][k] * ig[i];
+        for (int e = 0; e < 8; ++e) {
+          const float y = x[i][e] * inv;
           const float qq = rne(y);
           tie |= near_half(y, qq);
-          q[i][k] = min(max((int)qq + zg[i], 0), 15);
+          q[i][e] = min(max((int)qq + zg[i], 0), 15);
         }
+      }
       if (tie) {
 #pragma unroll
         for (int i = 0; i < NS; ++i)
 #pragma unroll
-          for (int k = 0; k < K; ++k)
-            q[i][k] = min(max((int)rne(div_rn(x[i][k], sg[i])) + zg[i], 0), 15);
+          for (int e = 0; e < 8; ++e)
+            q[i][e] = min(max((int)rne(div_rn(x[i][e], sg[i])) + zg[i], 0), 15);
       }
-      if (live && j == 0) {
+      if (live && k == 0) {
         float* sp = S.scale + rowi * NS;
         uint8_t* zp = S.zero + rowi * NS;
-        uint32_t zw = 0;
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          sp[i] = sg[i];
-          zw |= (uint32_t)zg[i] << (8 * i);
-        }
         if constexpr (NS == 4) {
-          *reinterpret_cast<uint32_t*>(zp) = zw;
+          *reinterpret_cast<float4v*>(sp) = (float4v){sg[0], sg[1], sg[2], sg[3]};
+          *reinterpret_cast<uint32_t*>(zp) = (uint32_t)zg[0] | ((uint32_t)zg[1] << 8) |
+                                             ((uint32_t)zg[2] << 16) | ((uint32_t)zg[3] << 24);
         } else {
-          *reinterpret_cast<uint16_t*>(zp) = (uint16_t)zw;
+          *reinterpret_cast<float2*>(sp) = make_float2(sg[0], sg[1]);
+          *reinterpret_cast<uint16_t*>(zp) = (uint16_t)(zg[0] | (zg[1] << 8));
         }
       }
     }
-    // byte (rr, i) of this lane's 4 = n * rr + i holds elements 2 rr, 2 rr + 1
-    // of slice i (relative to this lane's run)
-    uint32_t out = 0;
+    // output byte NS r' + i (r' = r - 4 k) holds elements 2 r', 2 r' + 1 of
+    // this lane's run of slice i
+    uint32_t out[NS];
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr)
+    for (int wd = 0; wd < NS; ++wd) {
+      uint32_t v = 0;
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const uint32_t byte = (uint32_t)(q[i][2 * rr] & 0xF) | ((uint32_t)(q[i][2 * rr + 1] & 0xF) << 4);
-        out |= byte << (8 * (NS * rr + i));
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const int byte = 4 * wd + b4, rr = byte / NS, i = byte % NS;
+        v |= ((uint32_t)(q[i][2 * rr] & 0xF) | ((uint32_t)(q[i][2 * rr + 1] & 0xF) << 4)) << (8 * b4);
       }
-    if (live) *reinterpret_cast<uint32_t*>(S.codes + rowi * (D / 2) + 4 * j) = out;
+      out[wd] = v;
+    }
+    if (live) {
+      uint8_t* dst = S.codes + rowi * (D / 2) + 4 * NS * k;
+      if constexpr (NS == 4)
+        *reinterpret_cast<u32x4*>(dst) = (u32x4){out[0], out[1], out[2], out[3]};
+      else
+        *reinterpret_cast<u32x2*>(dst) = (u32x2){out[0], out[1]};
+    }
   }
 }
 
@@ -497,10 +514,8 @@ int grid_for(int64_t waves_needed, int cu_count) {
 template <int D, bool BF16>
 hipError_t launch_rows(const AppendPlan& p, const RowArgs& ra, int code, int mode,
                        int nsides, hipStream_t stream) {
-  const int64_t rows = p.num_tokens * p.num_kv_heads;
-  const int64_t waves = (code == KVQ_CODE_INT4)
-                            ? (rows + kWave / (D / 8) - 1) / (kWave / (D / 8))
-                            : (p.num_tokens + 15) / 16 * p.num_kv_heads;
+  // every row kernel: one wave per (16-token group, head)
+  const int64_t waves = (p.num_tokens + 15) / 16 * p.num_kv_heads;
   dim3 grid(grid_for(waves, p.cu_count), nsides);
   if (code == KVQ_CODE_INT8)
     append_bytes_kernel<KVQ_CODE_INT8, D, BF16><<<grid, 256, 0, stream>>>(ra);
