@@ -195,6 +195,40 @@ void orc_quant_asym4(const float* x, int n, uint8_t* q, float* s, uint8_t* z) {
   *z = (uint8_t)zi;
 }
 
+/* Static scales [P1, opening section and "Understanding Dynamic Quantization
+ * Techniques for KV Caches": static quantization applies a fixed scaling
+ * factor (and zero point) determined in advance, where dynamic quantization
+ * derives them from each new vector]. The code rules are those above with
+ * the caller's scale s (> 0, finite) and zero point z in place of the ones
+ * taken from the vector's range; since the range no longer bounds x / s,
+ * the codes saturate: [-qmax, qmax] for the symmetric integers, +-448 for
+ * E4M3 (the encoder saturates), [0, 15] for the asymmetric nibbles. The
+ * clamps are applied to rne(x / s) before any integer conversion. */
+void orc_quant_sym_static(const float* x, int n, int qmax, float s, int8_t* q) {
+  for (int i = 0; i < n; ++i) {
+    float r = rintf(x[i] / s);
+    if (r > (float)qmax) r = (float)qmax;
+    if (r < (float)-qmax) r = (float)-qmax;
+    q[i] = (int8_t)r;
+  }
+}
+
+void orc_quant_fp8_static(const float* x, int n, float s, uint8_t* q) {
+  for (int i = 0; i < n; ++i) q[i] = orc_e4m3_encode(x[i] / s);
+}
+
+void orc_quant_asym4_static(const float* x, int n, float s, uint8_t z, uint8_t* q) {
+  for (int i = 0; i < n; ++i) {
+    float r = rintf(x[i] / s);
+    if (r > 15.0f) r = 15.0f;
+    if (r < -15.0f) r = -15.0f;
+    int qi = (int)r + (int)z;
+    if (qi < 0) qi = 0;
+    if (qi > 15) qi = 15;
+    q[i] = (uint8_t)qi;
+  }
+}
+
 /* Per-channel keys [P3, "KV Cache Quantization: When and How to Compress":
  * per-channel scales keep more information than a single scale]. One block of
  * bs rows x[t][c] (c < d): channel c gets the symmetric INT8 rule of
@@ -443,6 +477,79 @@ int orc_append(const orc_layout* L, const orc_cache* C, const void* k,
           store_key_channel_block(L, C, raw, blk, h, off, stage_rows[t]);
         } else {
           store_row(L, C, side, x, raw, blk, h, off);
+        }
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* Append with static scales: as orc_append, with side X's codes from the
+ * caller's per-KV-head parameters -- TOKEN_SYM: scale x_scale[h]; GROUP_ASYM:
+ * scale x_scale[h * ng + g] and zero point x_zero[h * ng + g] for group g of
+ * ng = d / group_size. The metadata planes receive those values, so that
+ * dequantization is unchanged. NONE16 sides are passthrough as in
+ * orc_append; CHANNEL_BLOCK keys are not a static mode (their staging exists
+ * to find the scale) and are rejected. */
+int orc_append_static(const orc_layout* L, const orc_cache* C, const void* k,
+                      const void* v, int64_t k_row_stride, int64_t v_row_stride,
+                      int64_t num_tokens, const int64_t* slot_mapping,
+                      const float* k_scale, const uint8_t* k_zero,
+                      const float* v_scale, const uint8_t* v_zero) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (L->k_mode == ORC_CHANNEL_BLOCK || L->v_mode == ORC_CHANNEL_BLOCK) return ORC_ERR_INVALID;
+  int H = L->num_kv_heads, d = L->head_dim, bs = L->block_size;
+  float x[128];
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    int64_t blk = slot / bs;
+    int off = (int)(slot % bs);
+    if (blk >= C->num_blocks) return ORC_ERR_INVALID;
+    for (int side = 0; side < 2; ++side) {
+      const void* src = side ? v : k;
+      int64_t stride = side ? v_row_stride : k_row_stride;
+      const float* sst = side ? v_scale : k_scale;
+      const uint8_t* zst = side ? v_zero : k_zero;
+      int code = side_code(L, side), mode = side_mode(L, side);
+      for (int h = 0; h < H; ++h) {
+        int64_t base = t * stride + (int64_t)h * d;
+        int64_t bh = blk * H + h;
+        int64_t rb = row_bytes(L, side);
+        uint8_t* dst = (uint8_t*)(side ? C->v_codes : C->k_codes) + (bh * bs + off) * rb;
+        if (code == ORC_CODE_NONE16) {
+          memcpy(dst, (const uint16_t*)src + base, (size_t)rb);
+          continue;
+        }
+        for (int e = 0; e < d; ++e) x[e] = src_to_f32(src, base + e, L->src_dtype);
+        float* scale = side ? C->v_scale : C->k_scale;
+        if (mode == ORC_TOKEN_SYM) {
+          float sh = sst[h];
+          if (code == ORC_CODE_INT8) {
+            orc_quant_sym_static(x, d, 127, sh, (int8_t*)dst);
+          } else if (code == ORC_CODE_FP8) {
+            orc_quant_fp8_static(x, d, sh, dst);
+          } else {
+            int8_t q[128];
+            uint8_t nib[128];
+            orc_quant_sym_static(x, d, 7, sh, q);
+            for (int e = 0; e < d; ++e) nib[e] = (uint8_t)(q[e] & 0xF);
+            orc_int4_pack(nib, d, dst);
+          }
+          scale[bh * bs + off] = sh;
+        } else { /* GROUP_ASYM */
+          int gs = L->group_size, ng = d / gs;
+          uint8_t nib[128];
+          uint8_t* zero = side ? C->v_zero : C->k_zero;
+          for (int g = 0; g < ng; ++g) {
+            float sg = sst[h * ng + g];
+            uint8_t zg = zst[h * ng + g];
+            orc_quant_asym4_static(x + g * gs, gs, sg, zg, nib + g * gs);
+            scale[(bh * bs + off) * ng + g] = sg;
+            zero[(bh * bs + off) * ng + g] = zg;
+          }
+          orc_int4_pack(nib, d, dst);
         }
       }
     }

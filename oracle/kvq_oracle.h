@@ -65,6 +65,9 @@ void orc_quant_sym(const float* x, int n, int qmax, int8_t* q, float* s);
 void orc_quant_fp8(const float* x, int n, uint8_t* q, float* s);
 void orc_quant_asym4(const float* x, int n, uint8_t* q, float* s, uint8_t* z);
 void orc_quant_channel_block(const float* x, int bs, int d, int8_t* q, float* s);
+void orc_quant_sym_static(const float* x, int n, int qmax, float s, int8_t* q);
+void orc_quant_fp8_static(const float* x, int n, float s, uint8_t* q);
+void orc_quant_asym4_static(const float* x, int n, float s, uint8_t z, uint8_t* q);
 void orc_int4_pack(const uint8_t* nib, int d, uint8_t* out);
 void orc_int4_unpack(const uint8_t* in, int d, uint8_t* nib);
 
@@ -79,6 +82,11 @@ int orc_append(const orc_layout* L, const orc_cache* C, const void* k,
                const void* v, int64_t k_row_stride, int64_t v_row_stride,
                int64_t num_tokens, const int64_t* slot_mapping,
                const int32_t* stage_rows);
+int orc_append_static(const orc_layout* L, const orc_cache* C, const void* k,
+                      const void* v, int64_t k_row_stride, int64_t v_row_stride,
+                      int64_t num_tokens, const int64_t* slot_mapping,
+                      const float* k_scale, const uint8_t* k_zero,
+                      const float* v_scale, const uint8_t* v_zero);
 int orc_dequant_token(const orc_layout* L, const orc_cache* C, int side,
                       const int32_t* table_row, int32_t context_len,
                       int32_t stage_row, int32_t pos, int32_t head, float* out);

@@ -54,6 +54,10 @@ def _load():
         "orc_quant_fp8": (None, [vp, C.c_int, vp, vp]),
         "orc_quant_asym4": (None, [vp, C.c_int, vp, vp, vp]),
         "orc_quant_channel_block": (None, [vp, C.c_int, C.c_int, vp, vp]),
+        "orc_quant_sym_static": (None, [vp, C.c_int, C.c_int, f32, vp]),
+        "orc_quant_fp8_static": (None, [vp, C.c_int, f32, vp]),
+        "orc_quant_asym4_static": (None, [vp, C.c_int, f32, C.c_uint8, vp]),
+        "orc_append_static": (C.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
         "orc_int4_pack": (None, [vp, C.c_int, vp]),
         "orc_int4_unpack": (None, [vp, C.c_int, vp]),
         "orc_bytes_per_token": (i64, [vp, i32, i32]),
@@ -145,6 +149,46 @@ def append(L, cache, k_bits, v_bits, slots, stage_rows=None,
                         ks, vs, T, _ptr(slots), _ptr(sr))
     if rc:
         raise ValueError(f"orc_append: {rc}")
+
+
+def append_static(L, cache, k_bits, v_bits, slots, k_scale, v_scale, k_zero=None,
+                  v_zero=None):
+    """Append with static scales: k_scale / v_scale float32 [H] (TOKEN_SYM)
+    or [H][d/gs] (GROUP_ASYM, with uint8 zero points of the same shape)."""
+    k_bits, v_bits = _u16(k_bits), _u16(v_bits)
+    T = k_bits.shape[0]
+    ks, vs = k_bits.size // max(T, 1), v_bits.size // max(T, 1)
+    slots = np.ascontiguousarray(slots, np.int64)
+    arr = lambda a, t: None if a is None else np.ascontiguousarray(a, t)
+    k_scale, v_scale = arr(k_scale, np.float32), arr(v_scale, np.float32)
+    k_zero, v_zero = arr(k_zero, np.uint8), arr(v_zero, np.uint8)
+    cs = cache.struct()
+    rc = lib.orc_append_static(C.byref(L), C.byref(cs), _ptr(k_bits), _ptr(v_bits),
+                               ks, vs, T, _ptr(slots), _ptr(k_scale), _ptr(k_zero),
+                               _ptr(v_scale), _ptr(v_zero))
+    if rc:
+        raise ValueError(f"orc_append_static: {rc}")
+
+
+def quant_sym_static(x, qmax, s):
+    x = np.ascontiguousarray(x, np.float32)
+    q = np.zeros(x.size, np.int8)
+    lib.orc_quant_sym_static(_ptr(x), x.size, qmax, s, _ptr(q))
+    return q
+
+
+def quant_fp8_static(x, s):
+    x = np.ascontiguousarray(x, np.float32)
+    q = np.zeros(x.size, np.uint8)
+    lib.orc_quant_fp8_static(_ptr(x), x.size, s, _ptr(q))
+    return q
+
+
+def quant_asym4_static(x, s, z):
+    x = np.ascontiguousarray(x, np.float32)
+    q = np.zeros(x.size, np.uint8)
+    lib.orc_quant_asym4_static(_ptr(x), x.size, s, z, _ptr(q))
+    return q
 
 
 def dequant_token(L, cache, side, table_row, context_len, stage_row, pos, head):
