@@ -487,18 +487,24 @@ int orc_append(const orc_layout* L, const orc_cache* C, const void* k,
 /* Append with static scales: as orc_append, with side X's codes from the
  * caller's per-KV-head parameters -- TOKEN_SYM: scale x_scale[h]; GROUP_ASYM:
  * scale x_scale[h * ng + g] and zero point x_zero[h * ng + g] for group g of
- * ng = d / group_size. The metadata planes receive those values, so that
- * dequantization is unchanged. NONE16 sides are passthrough as in
- * orc_append; CHANNEL_BLOCK keys are not a static mode (their staging exists
- * to find the scale) and are rejected. */
+ * ng = d / group_size; CHANNEL_BLOCK keys: scale k_scale[h * d + c] for
+ * channel c. The metadata planes receive those values, so that
+ * dequantization is unchanged; NONE16 sides are passthrough as in orc_append.
+ * Static per-channel keys (P3, "KV Cache Quantization: When and How to
+ * Compress", per-channel scales, here fixed in advance) need no wait for the
+ * block: each row is coded at once, and the block's scale row is written with
+ * its first slot (offset 0; blocks fill from offset 0 upward). The raw row
+ * still goes to the sequence's stage row, because decode reads a sequence's
+ * partial last block from there in this mode. */
 int orc_append_static(const orc_layout* L, const orc_cache* C, const void* k,
                       const void* v, int64_t k_row_stride, int64_t v_row_stride,
                       int64_t num_tokens, const int64_t* slot_mapping,
-                      const float* k_scale, const uint8_t* k_zero,
-                      const float* v_scale, const uint8_t* v_zero) {
+                      const int32_t* stage_rows, const float* k_scale,
+                      const uint8_t* k_zero, const float* v_scale,
+                      const uint8_t* v_zero) {
   int rc = check_layout(L);
   if (rc) return rc;
-  if (L->k_mode == ORC_CHANNEL_BLOCK || L->v_mode == ORC_CHANNEL_BLOCK) return ORC_ERR_INVALID;
+  if ((L->k_mode == ORC_CHANNEL_BLOCK) != (stage_rows != NULL)) return ORC_ERR_INVALID;
   int H = L->num_kv_heads, d = L->head_dim, bs = L->block_size;
   float x[128];
   for (int64_t t = 0; t < num_tokens; ++t) {
@@ -524,7 +530,15 @@ int orc_append_static(const orc_layout* L, const orc_cache* C, const void* k,
         }
         for (int e = 0; e < d; ++e) x[e] = src_to_f32(src, base + e, L->src_dtype);
         float* scale = side ? C->v_scale : C->k_scale;
-        if (mode == ORC_TOKEN_SYM) {
+        if (mode == ORC_CHANNEL_BLOCK) {
+          uint16_t* srow = (uint16_t*)C->k_stage +
+                           (((int64_t)stage_rows[t] * H + h) * bs + off) * d;
+          memcpy(srow, (const uint16_t*)src + base, sizeof(uint16_t) * (size_t)d);
+          for (int c = 0; c < d; ++c)
+            orc_quant_sym_static(x + c, 1, 127, sst[h * d + c], (int8_t*)dst + c);
+          if (off == 0)
+            memcpy(scale + bh * d, sst + (int64_t)h * d, sizeof(float) * (size_t)d);
+        } else if (mode == ORC_TOKEN_SYM) {
           float sh = sst[h];
           if (code == ORC_CODE_INT8) {
             orc_quant_sym_static(x, d, 127, sh, (int8_t*)dst);

@@ -85,8 +85,9 @@ int orc_append(const orc_layout* L, const orc_cache* C, const void* k,
 int orc_append_static(const orc_layout* L, const orc_cache* C, const void* k,
                       const void* v, int64_t k_row_stride, int64_t v_row_stride,
                       int64_t num_tokens, const int64_t* slot_mapping,
-                      const float* k_scale, const uint8_t* k_zero,
-                      const float* v_scale, const uint8_t* v_zero);
+                      const int32_t* stage_rows, const float* k_scale,
+                      const uint8_t* k_zero, const float* v_scale,
+                      const uint8_t* v_zero);
 int orc_dequant_token(const orc_layout* L, const orc_cache* C, int side,
                       const int32_t* table_row, int32_t context_len,
                       int32_t stage_row, int32_t pos, int32_t head, float* out);

@@ -57,7 +57,7 @@ def _load():
         "orc_quant_sym_static": (None, [vp, C.c_int, C.c_int, f32, vp]),
         "orc_quant_fp8_static": (None, [vp, C.c_int, f32, vp]),
         "orc_quant_asym4_static": (None, [vp, C.c_int, f32, C.c_uint8, vp]),
-        "orc_append_static": (C.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
+        "orc_append_static": (C.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
         "orc_int4_pack": (None, [vp, C.c_int, vp]),
         "orc_int4_unpack": (None, [vp, C.c_int, vp]),
         "orc_bytes_per_token": (i64, [vp, i32, i32]),
@@ -152,9 +152,10 @@ def append(L, cache, k_bits, v_bits, slots, stage_rows=None,
 
 
 def append_static(L, cache, k_bits, v_bits, slots, k_scale, v_scale, k_zero=None,
-                  v_zero=None):
-    """Append with static scales: k_scale / v_scale float32 [H] (TOKEN_SYM)
-    or [H][d/gs] (GROUP_ASYM, with uint8 zero points of the same shape)."""
+                  v_zero=None, stage_rows=None):
+    """Append with static scales: k_scale / v_scale float32 [H] (TOKEN_SYM),
+    [H][d/gs] (GROUP_ASYM, with uint8 zero points of the same shape) or
+    [H][d] (CHANNEL_BLOCK keys, with stage_rows as for append)."""
     k_bits, v_bits = _u16(k_bits), _u16(v_bits)
     T = k_bits.shape[0]
     ks, vs = k_bits.size // max(T, 1), v_bits.size // max(T, 1)
@@ -162,10 +163,11 @@ def append_static(L, cache, k_bits, v_bits, slots, k_scale, v_scale, k_zero=None
     arr = lambda a, t: None if a is None else np.ascontiguousarray(a, t)
     k_scale, v_scale = arr(k_scale, np.float32), arr(v_scale, np.float32)
     k_zero, v_zero = arr(k_zero, np.uint8), arr(v_zero, np.uint8)
+    rows = None if stage_rows is None else np.ascontiguousarray(stage_rows, np.int32)
     cs = cache.struct()
     rc = lib.orc_append_static(C.byref(L), C.byref(cs), _ptr(k_bits), _ptr(v_bits),
-                               ks, vs, T, _ptr(slots), _ptr(k_scale), _ptr(k_zero),
-                               _ptr(v_scale), _ptr(v_zero))
+                               ks, vs, T, _ptr(slots), _ptr(rows), _ptr(k_scale),
+                               _ptr(k_zero), _ptr(v_scale), _ptr(v_zero))
     if rc:
         raise ValueError(f"orc_append_static: {rc}")
 

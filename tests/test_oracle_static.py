@@ -1,5 +1,6 @@
 """Pins of the oracle's static-scale quantizers and append (a fixed, caller-given
-scale and zero point in place of the ones taken from each vector's range):
+scale and zero point in place of the ones taken from each vector's or block's
+range):
 hand-worked values, saturation, the reduction to the dynamic quantizers when
 the given scale is the one they would compute, round-trip bounds, and brute
 force over a small cache. No GPU."""
@@ -45,6 +46,10 @@ def test_asym4_static_hand_worked():
     assert ref.quant_asym4_static(x, 0.5, 3).tolist() == [0, 3, 7, 15, 0, 3, 15]
     assert ref.quant_asym4_static(x, 0.5, 0).tolist() == [0, 0, 4, 15, 0, 0, 12]
     assert ref.quant_asym4_static(x, 0.5, 15).tolist() == [12, 15, 15, 15, 0, 15, 15]
+    # quotients beyond the int32 range still saturate on the right side
+    big = f32([3e9, -3e9, 1e38, -1e38])
+    assert ref.quant_asym4_static(big, 1.0, 3).tolist() == [15, 0, 15, 0]
+    assert ref.quant_sym_static(big, 127, 1.0).tolist() == [127, -127, 127, -127]
 
 
 @pytest.mark.parametrize("qmax", [127, 7])
@@ -165,9 +170,66 @@ def test_append_static_places_codes_and_static_metadata(code, mode):
             assert (scale[slot // 16, :, slot % 16] == ks).all()
 
 
+def test_append_static_channel_keys_equal_dynamic_at_the_block_scales():
+    # One full block per sequence: static per-channel scales equal to the
+    # block's own dynamic scales give the dynamic codes and scale row; the
+    # stage row holds the raw rows either way.
+    w = workloads.get("mixed", batch=2)
+    L = oracle_layout(w)
+    H, d, bs = w.num_kv_heads, w.head_dim, w.block_size
+    k, v = workloads.kv_rows(w, 2 * bs, seed=8)
+    dyn = OracleSeqs(L, 6, 2, 2, order=np.arange(6, dtype=np.int32), max_seqs=2)
+    dyn.append(k, v, [bs, bs])
+    blocks = dyn.tables[:, 0]
+    sc = dyn.cache.scale(0).reshape(6, H, d)
+    for b in range(2):
+        st = OracleSeqs(L, 6, 2, 2, order=np.arange(6, dtype=np.int32), max_seqs=2)
+        slots, rows = st.grow([bs, bs])
+        ref.append_static(L, st.cache, bits(k).reshape(2 * bs, -1), bits(v).reshape(2 * bs, -1),
+                          slots, np.ascontiguousarray(sc[blocks[b]]),
+                          f32(np.full(H, 0.05)), stage_rows=rows)
+        kc_d = dyn.cache.planes["k_codes"].reshape(6, H, bs, d)
+        kc_s = st.cache.planes["k_codes"].reshape(6, H, bs, d)
+        assert (kc_s[blocks[b]] == kc_d[blocks[b]]).all()
+        assert (st.cache.scale(0).reshape(6, H, d)[blocks[b]] == sc[blocks[b]]).all()
+        assert (st.cache.planes["k_stage"] == dyn.cache.planes["k_stage"]).all()
+
+
+def test_append_static_channel_keys_brute_force_and_tail():
+    # Every key element is rne(x / s_c) clipped to [-127, 127]; a block's scale
+    # row is the given one from its first slot on; the partial tail reads back
+    # raw from the stage row.
+    w = workloads.get("mixed", batch=2)
+    L = oracle_layout(w)
+    H, d, bs = w.num_kv_heads, w.head_dim, w.block_size
+    lens = np.array([21, 9], np.int32)
+    k, v = workloads.kv_rows(w, 30, seed=2)
+    ks = f32(10.0 ** rng.uniform(-2.5, -1.0, (H, d)))
+    s = OracleSeqs(L, 6, 2, 2, order=rng.permutation(6).astype(np.int32), max_seqs=2)
+    slots, rows = s.grow(lens)
+    ref.append_static(L, s.cache, bits(k).reshape(30, -1), bits(v).reshape(30, -1), slots,
+                      ks, f32(np.full(H, 0.05)), stage_rows=rows)
+    codes = s.cache.planes["k_codes"].view(np.int8).reshape(6, H, bs, d)
+    for t, slot in enumerate(slots):
+        for h in range(H):
+            want = [ref.quant_sym_static(f32([xe]), 127, float(se))[0]
+                    for xe, se in zip(k[t, h].float().numpy(), ks[h])]
+            assert (codes[slot // bs, h, slot % bs] == want).all()
+    scale = s.cache.scale(0).reshape(6, H, d)
+    for b in range(2):
+        for j in range((lens[b] + bs - 1) // bs):
+            assert (scale[s.tables[b, j]] == ks).all()
+    # sequence 0: positions 16..20 are the partial tail, read raw
+    for pos in (16, 20):
+        got = ref.dequant_token(L, s.cache, 0, s.tables[0], 21, 0, pos, 1)
+        assert (got == k[pos, 1].float().numpy()).all()
+    got = ref.dequant_token(L, s.cache, 0, s.tables[0], 21, 0, 3, 1)
+    assert (got == codes[slots[3] // bs, 1, slots[3] % bs].astype(np.float32) * ks[1]).all()
+
+
 def test_append_static_passthrough_side_and_rejections():
     # INT8 keys with static scales next to 16-bit values: the value rows are
-    # stored as given. Per-channel keys have no static form and are rejected.
+    # stored as given. Per-channel keys need their stage rows.
     w = workloads.get("tiny", k_code="int8", v_code="none16", src_dtype="float16",
                       head_dim=64, block_size=16, num_kv_heads=2, num_q_heads=2, batch=1)
     L = oracle_layout(w)
@@ -186,4 +248,5 @@ def test_append_static_passthrough_side_and_rejections():
     kc, vc = workloads.kv_rows(wc, 3, seed=0)
     with pytest.raises(ValueError):
         ref.append_static(Lc, sc.cache, bits(kc).reshape(3, -1), bits(vc).reshape(3, -1),
-                          slots, f32(np.ones(wc.num_kv_heads)), f32(np.ones(wc.num_kv_heads)))
+                          slots, f32(np.ones((wc.num_kv_heads, wc.head_dim))),
+                          f32(np.ones(wc.num_kv_heads)))
