@@ -15,6 +15,9 @@
  *                         "Integrating Dynamic Quantization with PagedAttention";
  *                         "KV Cache Optimization" glossary, "Technical
  *                         Architecture", stages 2 and 3.)
+ *   kvq_append_static     the same with scales (and zero points) fixed in
+ *                         advance by the caller ("Dynamic KV Cache
+ *                         Quantization ...", static versus dynamic scales).
  *   kvq_decode_attention  single-query GQA attention softmax(q.K^T*scale).V of
  *                         every sequence of a batch over its cached blocks,
  *                         dequantizing the codes in registers ("KV Cache
@@ -222,6 +225,40 @@ kvq_status kvq_append(const kvq_layout* layout, const kvq_cache* cache,
                       int64_t v_row_stride, int64_t num_tokens,
                       const int64_t* slot_mapping, const int32_t* stage_rows,
                       void* stream);
+
+/* kvq_append with static scales: the scale (and zero point) of each code is
+ * given by the caller, fixed in advance, instead of being computed from each
+ * new vector's range ("Dynamic KV Cache Quantization for Fast LLM Inference",
+ * opening section and section "Understanding Dynamic Quantization Techniques
+ * for KV Caches", the static scheme that dynamic quantization is set against).
+ *  k_scales, v_scales  device float: TOKEN_SYM [H], one per KV head;
+ *                GROUP_ASYM [H][d / group_size], one per head and group;
+ *                CHANNEL_BLOCK_SYM keys [H][d], one per head and channel
+ *                (16-byte aligned). Positive and finite. NULL exactly for a
+ *                NONE16 side.
+ *  k_zeros, v_zeros    device uint8 [H][d / group_size] zero points in
+ *                [0, 15] for a GROUP_ASYM side; NULL otherwise.
+ * The other arguments are those of kvq_append, stage_rows included. Codes are
+ * rne(x / s), or rne(x / s) + z, with x / s in fp32 and correctly rounded,
+ * then saturated at the code range: [-127, 127] (INT8), [-7, 7] (INT4
+ * symmetric), +-448 (E4M3), [0, 15] (INT4 asymmetric, the quotient clipped to
+ * [-15, 15] first). Each token's metadata entries receive the given values,
+ * so the cache reads back through kvq_decode_attention unchanged. Per-channel
+ * keys are coded at once (the scale is known, so rows need not wait for their
+ * block); a block's scale row is written with its offset-0 slot, and the
+ * rows of each sequence's not yet complete last block still go, raw, to its
+ * stage row, where decode reads them.
+ * Scale and zero arrays other than per-channel ones need only their element
+ * alignment.
+ * Errors: KVQ_ERR_INVALID_ARGUMENT if a pointer is NULL where one is required
+ * or given where none is, or for kvq_append's argument errors. */
+kvq_status kvq_append_static(const kvq_layout* layout, const kvq_cache* cache,
+                             const void* k, const void* v, int64_t k_row_stride,
+                             int64_t v_row_stride, int64_t num_tokens,
+                             const int64_t* slot_mapping, const int32_t* stage_rows,
+                             const float* k_scales, const uint8_t* k_zeros,
+                             const float* v_scales, const uint8_t* v_zeros,
+                             void* stream);
 
 /* Device workspace bytes kvq_decode_attention needs for these sizes and this
  * split_blocks (1..256, or 0 = the library's own choice), or a negative

@@ -167,9 +167,15 @@ static kvq_status check_cache(const kvq_layout* L, const kvq_cache* C) {
   return KVQ_OK;
 }
 
-kvq_status kvq_append(const kvq_layout* L, const kvq_cache* C, const void* k, const void* v,
-                      int64_t k_row_stride, int64_t v_row_stride, int64_t num_tokens,
-                      const int64_t* slot_mapping, const int32_t* stage_rows, void* stream) {
+namespace {
+
+// Both append entry points: st[side] / sz[side] are the static parameters
+// (null on the dynamic path).
+kvq_status append_common(const kvq_layout* L, const kvq_cache* C, const void* k, const void* v,
+                         int64_t k_row_stride, int64_t v_row_stride, int64_t num_tokens,
+                         const int64_t* slot_mapping, const int32_t* stage_rows,
+                         const float* const st[2], const uint8_t* const sz[2], bool is_static,
+                         void* stream) {
   kvq_status s = kvq_layout_check(L);
   if (s != KVQ_OK) return s;
   s = check_cache(L, C);
@@ -186,8 +192,9 @@ kvq_status kvq_append(const kvq_layout* L, const kvq_cache* C, const void* k, co
   const bool chan = L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM;
   if (chan != (stage_rows != nullptr)) return KVQ_ERR_INVALID_ARGUMENT;
   kvq::AppendPlan p;
-  p.side[0] = {k, k_row_stride, C->k_codes, C->k_scale, C->k_zero};
-  p.side[1] = {v, v_row_stride, C->v_codes, C->v_scale, C->v_zero};
+  p.side[0] = {k, k_row_stride, C->k_codes, C->k_scale, C->k_zero, st[0], sz[0]};
+  p.side[1] = {v, v_row_stride, C->v_codes, C->v_scale, C->v_zero, st[1], sz[1]};
+  p.is_static = is_static;
   p.k_stage = C->k_stage;
   p.num_blocks = C->num_blocks;
   p.num_kv_heads = L->num_kv_heads;
@@ -216,6 +223,43 @@ kvq_status kvq_append(const kvq_layout* L, const kvq_cache* C, const void* k, co
     if (e != hipSuccess) return KVQ_ERR_HIP;
   }
   return KVQ_OK;
+}
+
+}  // namespace
+
+kvq_status kvq_append(const kvq_layout* L, const kvq_cache* C, const void* k, const void* v,
+                      int64_t k_row_stride, int64_t v_row_stride, int64_t num_tokens,
+                      const int64_t* slot_mapping, const int32_t* stage_rows, void* stream) {
+  const float* const st[2] = {nullptr, nullptr};
+  const uint8_t* const sz[2] = {nullptr, nullptr};
+  return append_common(L, C, k, v, k_row_stride, v_row_stride, num_tokens, slot_mapping,
+                       stage_rows, st, sz, false, stream);
+}
+
+kvq_status kvq_append_static(const kvq_layout* L, const kvq_cache* C, const void* k,
+                             const void* v, int64_t k_row_stride, int64_t v_row_stride,
+                             int64_t num_tokens, const int64_t* slot_mapping,
+                             const int32_t* stage_rows, const float* k_scales,
+                             const uint8_t* k_zeros, const float* v_scales,
+                             const uint8_t* v_zeros, void* stream) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  const float* const st[2] = {k_scales, v_scales};
+  const uint8_t* const sz[2] = {k_zeros, v_zeros};
+  const int32_t code[2] = {L->k_code, L->v_code}, mode[2] = {L->k_mode, L->v_mode};
+  for (int i = 0; i < 2; ++i) {
+    // a passthrough side takes no parameters; a quantized one its scales,
+    // and zero points exactly when it is asymmetric
+    const bool quant = code[i] != KVQ_CODE_NONE16;
+    const bool asym = quant && mode[i] == KVQ_SCALE_GROUP_ASYM;
+    if ((st[i] != nullptr) != quant || (sz[i] != nullptr) != asym)
+      return KVQ_ERR_INVALID_ARGUMENT;
+    // per-channel scales are read as 16-byte vectors
+    const uintptr_t align = mode[i] == KVQ_SCALE_CHANNEL_BLOCK_SYM ? 16 : 4;
+    if (st[i] && reinterpret_cast<uintptr_t>(st[i]) % align) return KVQ_ERR_INVALID_ARGUMENT;
+  }
+  return append_common(L, C, k, v, k_row_stride, v_row_stride, num_tokens, slot_mapping,
+                       stage_rows, st, sz, true, stream);
 }
 
 int64_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t batch, int32_t num_q_heads,

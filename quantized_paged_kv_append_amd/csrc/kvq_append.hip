@@ -18,6 +18,13 @@
 // reciprocal with a near-tie check that falls back to the exact quotient, so
 // stored bytes equal rne(x / s) exactly. Codes leave as one 8-byte (INT8/FP8)
 // or 4-byte (INT4) store per lane.
+//
+// Static scales (same pages, "Understanding Dynamic Quantization Techniques
+// for KV Caches", the static alternative): the STATIC kernels take the scale
+// (and zero point) of each head, or head and group, from the caller instead
+// of the row's range, skip the range reduction, and saturate the codes at the
+// code range, since the range no longer bounds x / s; the metadata planes
+// receive the given values.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -30,15 +37,20 @@ struct SideArgs {
   uint8_t* codes;
   float* scale;
   uint8_t* zero;
+  const float* st_scale;   // static parameters (STATIC kernels only)
+  const uint8_t* st_zero;
 };
 
 struct RowArgs {
   SideArgs side[2];
   const int64_t* slots;
+  const int32_t* stage_rows;  // static per-channel keys only
+  uint16_t* stage;
   int64_t num_tokens;
   int64_t num_blocks;
   int32_t H;
   int32_t bs;
+  int32_t max_seqs;
   int32_t side0;     // first side handled; blockIdx.y adds to it
   uint32_t h_mul;    // t = r / H as ((mulhi(r, h_mul) + r) >> h_shift), r < 2^31
   uint32_t h_shift;
@@ -62,11 +74,17 @@ __device__ __forceinline__ uint32_t pack_bytes(int a, int b, int c, int d) {
 }
 
 // E4M3 codes of four binary32 values with the hardware converter (round to
-// nearest even; every input here is below 464, so no saturation occurs).
+// nearest even). Every input here is below 464 in magnitude: dynamic scales
+// bound it, static ones are clamped to +-448 first, so no saturation occurs.
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
+
+// Saturation to the largest finite E4M3 magnitude. Every y in (448, 464)
+// rounds to 448 anyway, so clamping first leaves the rounding of in-range
+// values unchanged and sends the rest to +-448.
+__device__ __forceinline__ float sat448(float y) { return fminf(fmaxf(y, -448.0f), 448.0f); }
 
 // True when the E4M3 rounding of y might differ from that of the exact
 // quotient. With the E4M3 step of y's binade scaled to 1, y lies within 2^-14
@@ -85,7 +103,7 @@ __device__ __forceinline__ bool fp8_near_tie(float y) {
 // consecutive. Four lanes share a row of d elements: lane k holds elements
 // 32 u + 8 k + e (u < d/32, e < 8); each 16-byte load instruction reads a
 // contiguous 64-byte piece of every row.
-template <int CODE, int D, bool BF16>
+template <int CODE, int D, bool BF16, bool STATIC>
 __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
   constexpr int NV = D / 32;        // 16-byte vectors per lane
   constexpr int RPW = kWave / 4;    // rows per wave (= tokens of one group)
@@ -126,14 +144,19 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
       unpack2<BF16>(w[u].z, x[u][4], x[u][5]);
       unpack2<BF16>(w[u].w, x[u][6], x[u][7]);
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int u = 0; u < NV; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[u][e]));
-    amax = quad_max(amax);
     constexpr float kQmax = CODE == KVQ_CODE_INT8 ? 127.0f : 448.0f;
-    const float s = amax == 0.0f ? 1.0f : div_rn(amax, kQmax);
+    float s;
+    if constexpr (STATIC) {
+      s = S.st_scale[h];
+    } else {
+      float amax = 0.0f;
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[u][e]));
+      amax = quad_max(amax);
+      s = amax == 0.0f ? 1.0f : div_rn(amax, kQmax);
+    }
     const float inv = __builtin_amdgcn_rcpf(s);   // within 1 ulp of 1/s
     uint32_t o[NV][2];
     bool tie = recip_unsafe(s);
@@ -170,6 +193,7 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
         for (int e = 0; e < 8; ++e) {
           y[e] = x[u][e] * inv;
           tie |= fp8_near_tie(y[e]);
+          if constexpr (STATIC) y[e] = sat448(y[e]);
         }
         o[u][0] = fp8x4(y[0], y[1], y[2], y[3]);
         o[u][1] = fp8x4(y[4], y[5], y[6], y[7]);
@@ -179,7 +203,10 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
         for (int u = 0; u < NV; ++u) {
           float y[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = div_rn(x[u][e], s);
+          for (int e = 0; e < 8; ++e) {
+            y[e] = div_rn(x[u][e], s);
+            if constexpr (STATIC) y[e] = sat448(y[e]);
+          }
           o[u][0] = fp8x4(y[0], y[1], y[2], y[3]);
           o[u][1] = fp8x4(y[4], y[5], y[6], y[7]);
         }
@@ -220,7 +247,7 @@ __device__ __forceinline__ float quad_bcast(float v) {
 // MODE GROUP_ASYM: unsigned codes with a zero point per slice; lane k of a
 // quad computes slice k's scale and zero point (k < n) and the quad shares
 // them by DPP broadcasts.
-template <int MODE, int D, bool BF16>
+template <int MODE, int D, bool BF16, bool STATIC>
 __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
   constexpr int NS = D / 32;       // slices per row, one 16-byte load each
   constexpr int RPW = kWave / 4;   // rows per wave (tokens of one group)
@@ -252,13 +279,18 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
     }
     int q[NS][8];
     if constexpr (MODE == KVQ_SCALE_TOKEN_SYM) {
-      float amax = 0.0f;
+      float s;
+      if constexpr (STATIC) {
+        s = S.st_scale[h];
+      } else {
+        float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < NS; ++i)
+        for (int i = 0; i < NS; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
-      amax = quad_max(amax);
-      const float s = amax == 0.0f ? 1.0f : div_rn(amax, 7.0f);
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+        amax = quad_max(amax);
+        s = amax == 0.0f ? 1.0f : div_rn(amax, 7.0f);
+      }
       const float inv = __builtin_amdgcn_rcpf(s);   // within 1 ulp of 1/s
       bool tie = recip_unsafe(s);
 #pragma unroll
@@ -279,6 +311,15 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
       }
       if (live && k == 0) S.scale[rowi] = s;
     } else {
+      float sg[NS];
+      int zg[NS];
+      if constexpr (STATIC) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          sg[i] = S.st_scale[h * NS + i];
+          zg[i] = S.st_zero[h * NS + i];
+        }
+      } else {
       // per-slice range, widened to contain 0
       float mn[NS], mx[NS];
 #pragma unroll
@@ -306,9 +347,6 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
         so = div_rn(mxo - mno, 15.0f);
         zf = fminf(fmaxf(rne(div_rn(-mno, so)), 0.0f), 15.0f);
       }
-      float sg[NS];
-      int zg[NS];
-      bool tie = false;
       sg[0] = quad_bcast<0>(so);
       zg[0] = (int)quad_bcast<0>(zf);
       sg[1] = quad_bcast<1>(so);
@@ -319,6 +357,10 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
         sg[3] = quad_bcast<3>(so);
         zg[3] = (int)quad_bcast<3>(zf);
       }
+      }
+      // A dynamic range bounds |x / s| by 15; static scales do not, so the
+      // rounded quotient is clipped to +-15 before the integer conversion.
+      bool tie = false;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         tie |= recip_unsafe(sg[i]);
@@ -326,8 +368,9 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float y = x[i][e] * inv;
-          const float qq = rne(y);
+          float qq = rne(y);
           tie |= near_half(y, qq);
+          if constexpr (STATIC) qq = fminf(fmaxf(qq, -15.0f), 15.0f);
           q[i][e] = min(max((int)qq + zg[i], 0), 15);
         }
       }
@@ -335,8 +378,11 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
 #pragma unroll
         for (int i = 0; i < NS; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            q[i][e] = min(max((int)rne(div_rn(x[i][e], sg[i])) + zg[i], 0), 15);
+          for (int e = 0; e < 8; ++e) {
+            float qq = rne(div_rn(x[i][e], sg[i]));
+            if constexpr (STATIC) qq = fminf(fmaxf(qq, -15.0f), 15.0f);
+            q[i][e] = min(max((int)qq + zg[i], 0), 15);
+          }
       }
       if (live && k == 0) {
         float* sp = S.scale + rowi * NS;
@@ -470,6 +516,88 @@ __global__ __launch_bounds__(256) void chan_complete_kernel(ChanArgs a) {
   }
 }
 
+// Static per-channel keys: channel c of head h has the caller's scale
+// s[h d + c], so a row is coded as soon as it arrives (no wait for its block).
+// Lane layout as in append_bytes_kernel (16 tokens of one head per wave, four
+// lanes per row); each lane also reads the scales of its 8 D/32 channels, and
+// writes them as the block's scale row when its token holds offset 0. Rows of
+// a block that this call does not complete still go, raw, to the stage row,
+// where decode reads a partial last block (at most one such row per stage
+// position per call, so no two writes race).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void append_chan_static_kernel(RowArgs a) {
+  constexpr int NV = D / 32;
+  constexpr int RPW = kWave / 4;
+  const SideArgs S = a.side[0];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int k = lane & 3;
+  const uint32_t groups = ((uint32_t)a.num_tokens + 15u) / 16u;
+  const uint32_t items = groups * (uint32_t)a.H;
+  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const uint32_t nwaves = gridDim.x * blockDim.x / kWave;
+  for (uint32_t it = wave; it < items; it += nwaves) {
+    const uint32_t tg = div_h(it, a);
+    const uint32_t h = it - tg * (uint32_t)a.H;
+    const uint32_t t = tg * RPW + (uint32_t)(lane >> 2);
+    const bool in = t < (uint32_t)a.num_tokens;
+    const int64_t slot = in ? a.slots[t] : -1;
+    const int32_t srow = in ? a.stage_rows[t] : -1;
+    const int64_t blk = slot >> a.bs_shift;
+    const int off = (int)(slot & (a.bs - 1));
+    const bool live = slot >= 0 && blk < a.num_blocks && srow >= 0 && srow < a.max_seqs;
+    const int64_t rowi = (blk * a.H + h) * a.bs + off;
+    const uint16_t* src = S.src + (int64_t)(in ? t : 0) * S.row_stride + h * D + 8 * k;
+    const float* sp = S.st_scale + h * D + 8 * k;
+    u32x4 w[NV];
+    float4v sv[NV][2];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      w[u] = in ? *reinterpret_cast<const u32x4*>(src + 32 * u) : (u32x4){0u, 0u, 0u, 0u};
+      sv[u][0] = *reinterpret_cast<const float4v*>(sp + 32 * u);
+      sv[u][1] = *reinterpret_cast<const float4v*>(sp + 32 * u + 4);
+    }
+    uint32_t o[NV][2];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      float x[8];
+      unpack2<BF16>(w[u].x, x[0], x[1]);
+      unpack2<BF16>(w[u].y, x[2], x[3]);
+      unpack2<BF16>(w[u].z, x[4], x[5]);
+      unpack2<BF16>(w[u].w, x[6], x[7]);
+      int c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float sc = sv[u][e >> 2][e & 3];
+        const float y = x[e] * __builtin_amdgcn_rcpf(sc);
+        float q = rne(y);
+        if (near_half(y, q) || recip_unsafe(sc)) q = rne(div_rn(x[e], sc));  // rare
+        c[e] = (int)fminf(fmaxf(q, -127.0f), 127.0f);
+      }
+      o[u][0] = pack_bytes(c[0], c[1], c[2], c[3]);
+      o[u][1] = pack_bytes(c[4], c[5], c[6], c[7]);
+    }
+    if (live) {
+      // completed in this call iff the token holding the block's last offset
+      // follows in the same run
+      const int64_t tl = (int64_t)t + (a.bs - 1 - off);
+      const bool completes = tl < a.num_tokens && a.slots[tl] == slot + (a.bs - 1 - off) &&
+                             a.stage_rows[tl] == srow;
+      uint16_t* st = a.stage + (((int64_t)srow * a.H + h) * a.bs + off) * D + 8 * k;
+      int8_t* cd = reinterpret_cast<int8_t*>(S.codes) + rowi * D + 8 * k;
+      float* sd = S.scale + (blk * a.H + h) * D + 8 * k;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        *reinterpret_cast<u32x2*>(cd + 32 * u) = (u32x2){o[u][0], o[u][1]};
+        if (!completes) *reinterpret_cast<u32x4*>(st + 32 * u) = w[u];
+        if (off == 0) {
+          *reinterpret_cast<float4v*>(sd + 32 * u) = sv[u][0];
+          *reinterpret_cast<float4v*>(sd + 32 * u + 4) = sv[u][1];
+        }
+      }
+    }
+  }
+}
+
 // Phase 2: rows whose block is not completed within this call go, raw, to
 // their stage row. Runs after phase 1 (same stream), which may still read
 // stage rows of a block that this call completes. One row per D/8 lanes.
@@ -511,22 +639,30 @@ int grid_for(int64_t waves_needed, int cu_count) {
   return (int)blocks;
 }
 
+template <int D, bool BF16, bool STATIC>
+void launch_rows_t(dim3 grid, const RowArgs& ra, int code, int mode, hipStream_t stream) {
+  if (code == KVQ_CODE_INT8)
+    append_bytes_kernel<KVQ_CODE_INT8, D, BF16, STATIC><<<grid, 256, 0, stream>>>(ra);
+  else if (code == KVQ_CODE_FP8_E4M3)
+    append_bytes_kernel<KVQ_CODE_FP8_E4M3, D, BF16, STATIC><<<grid, 256, 0, stream>>>(ra);
+  else if (code == KVQ_CODE_NONE16)
+    append_bytes_kernel<KVQ_CODE_NONE16, D, BF16, false><<<grid, 256, 0, stream>>>(ra);
+  else if (mode == KVQ_SCALE_TOKEN_SYM)
+    append_int4_kernel<KVQ_SCALE_TOKEN_SYM, D, BF16, STATIC><<<grid, 256, 0, stream>>>(ra);
+  else
+    append_int4_kernel<KVQ_SCALE_GROUP_ASYM, D, BF16, STATIC><<<grid, 256, 0, stream>>>(ra);
+}
+
 template <int D, bool BF16>
 hipError_t launch_rows(const AppendPlan& p, const RowArgs& ra, int code, int mode,
                        int nsides, hipStream_t stream) {
   // every row kernel: one wave per (16-token group, head)
   const int64_t waves = (p.num_tokens + 15) / 16 * p.num_kv_heads;
   dim3 grid(grid_for(waves, p.cu_count), nsides);
-  if (code == KVQ_CODE_INT8)
-    append_bytes_kernel<KVQ_CODE_INT8, D, BF16><<<grid, 256, 0, stream>>>(ra);
-  else if (code == KVQ_CODE_FP8_E4M3)
-    append_bytes_kernel<KVQ_CODE_FP8_E4M3, D, BF16><<<grid, 256, 0, stream>>>(ra);
-  else if (code == KVQ_CODE_NONE16)
-    append_bytes_kernel<KVQ_CODE_NONE16, D, BF16><<<grid, 256, 0, stream>>>(ra);
-  else if (mode == KVQ_SCALE_TOKEN_SYM)
-    append_int4_kernel<KVQ_SCALE_TOKEN_SYM, D, BF16><<<grid, 256, 0, stream>>>(ra);
+  if (p.is_static)
+    launch_rows_t<D, BF16, true>(grid, ra, code, mode, stream);
   else
-    append_int4_kernel<KVQ_SCALE_GROUP_ASYM, D, BF16><<<grid, 256, 0, stream>>>(ra);
+    launch_rows_t<D, BF16, false>(grid, ra, code, mode, stream);
   return hipGetLastError();
 }
 
@@ -563,8 +699,13 @@ hipError_t launch_append_d(const AppendPlan& p, hipStream_t stream) {
     ra.side[s].codes = static_cast<uint8_t*>(p.side[s].codes);
     ra.side[s].scale = p.side[s].scale;
     ra.side[s].zero = p.side[s].zero;
+    ra.side[s].st_scale = p.side[s].st_scale;
+    ra.side[s].st_zero = p.side[s].st_zero;
   }
   ra.slots = p.slots;
+  ra.stage_rows = p.stage_rows;
+  ra.stage = static_cast<uint16_t*>(p.k_stage);
+  ra.max_seqs = p.max_seqs;
   ra.num_tokens = p.num_tokens;
   ra.num_blocks = p.num_blocks;
   ra.H = p.num_kv_heads;
@@ -586,6 +727,12 @@ hipError_t launch_append_d(const AppendPlan& p, hipStream_t stream) {
   if (!chan) {
     ra.side0 = 0;
     e = launch_rows<D, BF16>(p, ra, p.code[0], p.mode[0], 1, stream);
+    if (e != hipSuccess) return e;
+  } else if (p.is_static) {
+    ra.side0 = 0;
+    const int64_t waves = (p.num_tokens + 15) / 16 * p.num_kv_heads;
+    append_chan_static_kernel<D, BF16><<<grid_for(waves, p.cu_count), 256, 0, stream>>>(ra);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
     e = p.block_size == 16 ? launch_chan<D, 16, BF16>(p, stream)

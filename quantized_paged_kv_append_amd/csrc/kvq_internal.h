@@ -17,6 +17,8 @@ struct AppendSide {
   void* codes;
   float* scale;
   uint8_t* zero;
+  const float* st_scale;   // static scales ([H] or [H][d/32]); null: dynamic
+  const uint8_t* st_zero;  // static zero points ([H][d/32], GROUP_ASYM)
 };
 
 struct AppendPlan {
@@ -34,6 +36,7 @@ struct AppendPlan {
   int32_t mode[2];
   int32_t max_seqs;
   int32_t cu_count;
+  int32_t is_static;   // codes from the sides' st_scale / st_zero
 };
 
 hipError_t launch_append(const AppendPlan& p, hipStream_t stream);

@@ -62,6 +62,8 @@ _SIGS = {
     "kvq_bytes_per_token": (_i64, [_LP, _i32, _i32]),
     "kvq_cache_plane_bytes": (_i32, [_LP, _i64, _i32, _vp]),
     "kvq_append": (_i32, [_LP, _CP, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "kvq_append_static": (_i32, [_LP, _CP, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp]),
     "kvq_decode_workspace_bytes": (_i64, [_LP, _i32, _i32, _i32, _i32]),
     "kvq_decode_attention": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
                                     _i32, _f32, _i32, _vp, _i32, _vp, _i64, _vp]),
@@ -157,6 +159,20 @@ def kvq_append(layout, cache: PagedCache, k, v, slot_mapping, stage_rows=None,
         C.byref(layout), C.byref(cache.struct), _ptr(k), _ptr(v),
         k.stride(0) if T else 0, v.stride(0) if T else 0, T, _ptr(slot_mapping),
         _ptr(stage_rows), _stream(stream)))
+
+
+def kvq_append_static(layout, cache: PagedCache, k, v, slot_mapping, k_scales,
+                      v_scales, k_zeros=None, v_zeros=None, stage_rows=None, stream=None):
+    """kvq_append with caller-given scales: k_scales / v_scales device float32
+    [H] (TOKEN_SYM), [H][d/32] (GROUP_ASYM, with uint8 zero points of that
+    shape) or [H][d] (per-channel keys, with stage_rows as for kvq_append);
+    None for a 16-bit passthrough side."""
+    T = k.shape[0]
+    _check("kvq_append_static", _lib.kvq_append_static(
+        C.byref(layout), C.byref(cache.struct), _ptr(k), _ptr(v),
+        k.stride(0) if T else 0, v.stride(0) if T else 0, T, _ptr(slot_mapping),
+        _ptr(stage_rows), _ptr(k_scales), _ptr(k_zeros), _ptr(v_scales), _ptr(v_zeros),
+        _stream(stream)))
 
 
 def kvq_decode_workspace_bytes(layout, batch, num_q_heads, max_context_len,

@@ -157,6 +157,43 @@ def test_append_and_decode_reject_bad_arguments_on_host():
                                     None) == kq.KVQ_ERR_UNSUPPORTED
 
 
+def test_append_static_rejects_bad_arguments_on_host():
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+    sc, zp = C.c_void_p(1 << 23), C.c_void_p(1 << 24)
+
+    def app(L, cs, ks, kz, vs, vz, T=4, rows=None):
+        return lib.kvq_append_static(C.byref(L), C.byref(cs), p, p, 1024, 1024, T, p,
+                                     rows, ks, kz, vs, vz, None)
+    L = kq.make_layout(8, 128, 16, "int8")
+    cs = _fake_cache(L)
+    assert app(L, cs, sc, None, sc, None, T=0) == kq.KVQ_OK
+    assert app(L, cs, None, None, sc, None) == kq.KVQ_ERR_INVALID_ARGUMENT   # no key scales
+    assert app(L, cs, sc, zp, sc, None) == kq.KVQ_ERR_INVALID_ARGUMENT       # zero for symmetric
+    assert app(L, cs, C.c_void_p((1 << 23) + 2), None, sc, None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert app(L, cs, sc, None, sc, None, T=-1) == kq.KVQ_ERR_INVALID_ARGUMENT
+    La = kq.make_layout(8, 128, 32, "int4", k_mode="group_asym", group_size=32)
+    ca = _fake_cache(La)
+    ca.k_zero, ca.v_zero = 1 << 25, (1 << 25) + 4096
+    assert app(La, ca, sc, zp, sc, zp, T=0) == kq.KVQ_OK
+    assert app(La, ca, sc, None, sc, zp) == kq.KVQ_ERR_INVALID_ARGUMENT      # asym needs zeros
+    # a 16-bit side takes no parameters
+    Ln = kq.make_layout(8, 128, 16, "fp8", v_code="none16")
+    cn = _fake_cache(Ln)
+    cn.v_scale = None
+    assert app(Ln, cn, sc, None, None, None, T=0) == kq.KVQ_OK
+    assert app(Ln, cn, sc, None, sc, None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    # per-channel keys: stage rows required, [H][d] scales 16-byte aligned
+    Lc = kq.make_layout(8, 128, 16, "int8", k_mode="channel_block")
+    cc = _fake_cache(Lc)
+    cc.k_stage, cc.max_seqs = 1 << 26, 4
+    assert app(Lc, cc, sc, None, sc, None, T=0, rows=p) == kq.KVQ_OK
+    assert app(Lc, cc, sc, None, sc, None) == kq.KVQ_ERR_INVALID_ARGUMENT          # no rows
+    assert app(Lc, cc, C.c_void_p((1 << 23) + 4), None, sc, None,
+               rows=p) == kq.KVQ_ERR_INVALID_ARGUMENT                              # alignment
+    assert app(L, cs, sc, None, sc, None, rows=p) == kq.KVQ_ERR_INVALID_ARGUMENT   # rows unused
+
+
 def test_pool_calls_reject_bad_arguments_on_host():
     lib = kq._lib
     p = C.c_void_p(1 << 21)
