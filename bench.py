@@ -77,6 +77,13 @@ def parse():
                     help="sequences of layer 0 the oracle decodes (0: enough for about "
                          "16 s of CPU work, at most the whole batch)")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--flush-mb", type=int, default=-1,
+                    help="MiB of scratch read before every timed step so that no KV "
+                         "bytes stay in L2 / the Infinity Cache between steps (-1: 1024 "
+                         "when a step reads under 2 GB of KV, else 0)")
+    ap.add_argument("--flush-write", action="store_true",
+                    help="flush by writing the scratch instead of reading it (the "
+                         "dirty lines are then written back during the next step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (reference kernel for "
                          "the FETCH_SIZE / WRITE_SIZE counter scale) and exit")
@@ -223,24 +230,42 @@ def main():
             if evs is not None:
                 evs[layer][1].record(stream)
 
+    # working sets that fit in the caches are flushed between steps
+    kv_step_est = float(lens.sum()) * H * kv_bytes_per_token_head(w) * layers
+    flush_mb = args.flush_mb if args.flush_mb >= 0 else (1024 if kv_step_est < 2e9 else 0)
+    flush_buf = torch.ones(flush_mb << 20, dtype=torch.uint8, device=dev) if flush_mb else None
+    flush_sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ctx_before = ctx.cpu().numpy().astype(np.int64)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dec_ms = []
     torch.cuda.synchronize()
     t_start.record(stream)
     wall0 = time.perf_counter()
     for s_ in range(args.steps):
+        if flush_buf is not None:
+            if args.flush_write:
+                flush_buf.fill_(s_ & 0xFF)
+            else:   # a read leaves clean lines: nothing to write back later
+                flush_sink[s_ % 2] = flush_buf.view(torch.int64).sum()
+        step_ev[s_][0].record(stream)
         step(dec_ev[s_])
+        step_ev[s_][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     # per-launch decode durations (events recorded on the launch stream)
     dec_ms = [a.elapsed_time(b) for evs in dec_ev for a, b in evs]
     wall = time.perf_counter() - wall0
     assert int(status.item()) == 0, "pool reservation during the steps failed"
-    step_ms = t_start.elapsed_time(t_end) / args.steps
+    bracket_ms = t_start.elapsed_time(t_end) / args.steps
+    # with a flush, a step is timed from its own events (the flush between
+    # steps is not part of the work); otherwise the whole bracket counts
+    step_ms = (float(np.mean([a.elapsed_time(b) for a, b in step_ev])) if flush_buf is not None
+               else bracket_ms)
 
     # context attended at each timed step: before + new tokens of that step
     ctx_tokens = [(ctx_before + new_per_step * (s + 1)).sum() for s in range(args.steps)]
@@ -280,6 +305,11 @@ def main():
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "kv_bytes_per_step": kv_bytes_step,
         "decode_launch_ms": round(dec_avg_ms, 5),
+        "decode_launch_ms_p10_p50_p90": [round(float(x), 5)
+                                         for x in np.percentile(dec_ms, [10, 50, 90])],
+        "ms_per_step_bracket": round(bracket_ms, 4),
+        "cache_flush_mb": flush_mb,
+        "cache_flush": ("write" if args.flush_write else "read") if flush_mb else None,
         "append_tok_s": round(append_tok_s, 1),
         "append_GBps": round(append_gbs, 2),
         "append_bytes_per_token": append_bytes_per_token(w),
@@ -340,16 +370,26 @@ def cpu_baseline(w, lens, args):
     q = workloads.queries(w, device="cuda:0", layer=0)[:nseq]
     qb = q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     threads = args.cpu_threads or len(os.sched_getaffinity(0))
+    qdt = ref.BF16 if w.src_dtype == "bfloat16" else ref.F16
     t0 = time.perf_counter()
-    ref.decode(OL, hc, qb, ref.BF16 if w.src_dtype == "bfloat16" else ref.F16, tables, sl,
-               threads=threads)
+    ref.decode(OL, hc, qb, qdt, tables, sl, threads=threads)
     dt = time.perf_counter() - t0
     kv_bytes = float(sl.sum()) * w.num_kv_heads * kv_bytes_per_token_head(w)
+    # the same oracle on one core, over the first sequences (about 4 s)
+    n1 = max(1, min(nseq, int(np.searchsorted(
+        np.cumsum(sl.astype(np.float64) * w.num_q_heads), 4.0 / 1.8e-6)) + 1))
+    t0 = time.perf_counter()
+    ref.decode(OL, hc, qb[:n1], qdt, tables[:n1], sl[:n1], threads=1)
+    dt1 = time.perf_counter() - t0
+    kv1 = float(sl[:n1].sum()) * w.num_kv_heads * kv_bytes_per_token_head(w)
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
+            "value_1core": round(kv1 / dt1 / 1e9, 4),
             "sample": f"layer 0 of {w.name}: decode of sequences 0..{nseq - 1} "
                       f"({int(sl.sum())} cached tokens x {w.num_kv_heads} KV heads, all "
-                      f"{w.num_q_heads} query heads), fp64 attention, {dt:.2f} s"}
+                      f"{w.num_q_heads} query heads), fp64 attention, {dt:.2f} s on "
+                      f"{threads} threads; value_1core: sequences 0..{n1 - 1} on one "
+                      f"thread, {dt1:.2f} s"}
 
 
 if __name__ == "__main__":
