@@ -777,6 +777,133 @@ int orc_decode(const orc_layout* L, const orc_cache* C, const void* q,
   return J.rc;
 }
 
+/* Multi-query (prefill) attention [P3, "Why KV Cache Is Essential for
+ * Efficient LLM Inference": the prompt's tokens are processed together before
+ * decoding; P3, "Implementing KV Cache Optimization: A Practical Checklist",
+ * common pitfalls: that phase is compute-bound, unlike decode]. Sequence b
+ * has nq = query_start[b+1] - query_start[b] query tokens, the last nq of its
+ * context_lens[b] = L cached positions (their keys and values are already
+ * appended): query i sits at position p = L - nq + i and attends causally to
+ * positions 0..p. Query row r = query_start[b] + i, head h (KV head h / G):
+ * out[r][h] = sum_{t<=p} e_t v_t / sum_{t<=p} e_t, e_t = exp(s_t - max s),
+ * s_t = (q . k_t) sm, in binary64 from the binary32 dequantized rows. Which
+ * positions are read raw from the stage (per-channel keys) is decided by the
+ * full length L, as in decode. nq = 1 is decode. */
+typedef struct {
+  const orc_layout* L;
+  const orc_cache* C;
+  const void* q;
+  int32_t q_dtype, batch, Hq, max_blocks;
+  const int32_t* qstart;
+  const int32_t* tables;
+  const int32_t* lens;
+  double sm;
+  double* out;
+  int64_t next;
+  int rc;
+  pthread_mutex_t mu;
+} prefill_job;
+
+static int prefill_one(const prefill_job* J, int b, int i, int h, double* o) {
+  const orc_layout* L = J->L;
+  int H = L->num_kv_heads, d = L->head_dim, G = J->Hq / H;
+  int len = J->lens[b], nq = J->qstart[b + 1] - J->qstart[b];
+  int64_t qrow = J->qstart[b] + i;
+  int p = len - nq + i; /* the query's own position */
+  const int32_t* table_row = J->tables + (int64_t)b * J->max_blocks;
+  double qv[128];
+  float row[128];
+  for (int e = 0; e < d; ++e) qv[e] = q_elem(J->q, J->q_dtype, (qrow * J->Hq + h) * d + e);
+  for (int e = 0; e < d; ++e) o[e] = 0.0;
+  if (p < 0) return ORC_OK;
+  double* sc = (double*)malloc(sizeof(double) * (size_t)(p + 1));
+  double m = -INFINITY;
+  for (int t = 0; t <= p; ++t) {
+    int rc = orc_dequant_token(L, J->C, 0, table_row, len, b, t, h / G, row);
+    if (rc) {
+      free(sc);
+      return rc;
+    }
+    double dot = 0.0;
+    for (int e = 0; e < d; ++e) dot += qv[e] * (double)row[e];
+    sc[t] = dot * J->sm;
+    if (sc[t] > m) m = sc[t];
+  }
+  double l = 0.0;
+  for (int t = 0; t <= p; ++t) {
+    double w = exp(sc[t] - m);
+    l += w;
+    int rc = orc_dequant_token(L, J->C, 1, table_row, len, b, t, h / G, row);
+    if (rc) {
+      free(sc);
+      return rc;
+    }
+    for (int e = 0; e < d; ++e) o[e] += w * (double)row[e];
+  }
+  free(sc);
+  for (int e = 0; e < d; ++e) o[e] /= l;
+  return ORC_OK;
+}
+
+static void* prefill_worker(void* arg) {
+  prefill_job* J = (prefill_job*)arg;
+  int64_t rows = J->qstart[J->batch];
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int64_t item = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (item >= rows * J->Hq) break;
+    int64_t r = item / J->Hq;
+    int h = (int)(item % J->Hq);
+    int b = 0;
+    while (J->qstart[b + 1] <= r) ++b; /* the sequence holding row r */
+    int rc = prefill_one(J, b, (int)(r - J->qstart[b]), h, J->out + item * J->L->head_dim);
+    if (rc) {
+      pthread_mutex_lock(&J->mu);
+      J->rc = rc;
+      pthread_mutex_unlock(&J->mu);
+    }
+  }
+  return NULL;
+}
+
+int orc_prefill(const orc_layout* L, const orc_cache* C, const void* q, int32_t q_dtype,
+                int32_t batch, int32_t num_q_heads, const int32_t* query_start,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, double sm_scale, double* out,
+                int32_t num_threads) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (num_q_heads % L->num_kv_heads) return ORC_ERR_INVALID;
+  for (int b = 0; b < batch; ++b) {
+    int nq = query_start[b + 1] - query_start[b];
+    if (nq < 0 || nq > context_lens[b]) return ORC_ERR_INVALID;
+  }
+  prefill_job J;
+  J.L = L;
+  J.C = C;
+  J.q = q;
+  J.q_dtype = q_dtype;
+  J.batch = batch;
+  J.Hq = num_q_heads;
+  J.max_blocks = max_blocks_per_seq;
+  J.qstart = query_start;
+  J.tables = block_tables;
+  J.lens = context_lens;
+  J.sm = sm_scale != 0.0 ? sm_scale : 1.0 / sqrt((double)L->head_dim);
+  J.out = out;
+  J.next = 0;
+  J.rc = ORC_OK;
+  pthread_mutex_init(&J.mu, NULL);
+  if (num_threads < 1) num_threads = 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)num_threads);
+  for (int i = 0; i < num_threads; ++i) pthread_create(&th[i], NULL, prefill_worker, &J);
+  for (int i = 0; i < num_threads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  pthread_mutex_destroy(&J.mu);
+  return J.rc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Block pool [P3, "How vLLM Implements KV Cache Optimization": small fixed- */
 /* size blocks handed to sequences on demand; P1, "Integrating Dynamic       */

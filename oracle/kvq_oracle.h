@@ -88,6 +88,11 @@ int orc_append_static(const orc_layout* L, const orc_cache* C, const void* k,
                       const int32_t* stage_rows, const float* k_scale,
                       const uint8_t* k_zero, const float* v_scale,
                       const uint8_t* v_zero);
+int orc_prefill(const orc_layout* L, const orc_cache* C, const void* q, int32_t q_dtype,
+                int32_t batch, int32_t num_q_heads, const int32_t* query_start,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, double sm_scale, double* out,
+                int32_t num_threads);
 int orc_dequant_token(const orc_layout* L, const orc_cache* C, int side,
                       const int32_t* table_row, int32_t context_len,
                       int32_t stage_row, int32_t pos, int32_t head, float* out);

@@ -57,6 +57,7 @@ def _load():
         "orc_quant_sym_static": (None, [vp, C.c_int, C.c_int, f32, vp]),
         "orc_quant_fp8_static": (None, [vp, C.c_int, f32, vp]),
         "orc_quant_asym4_static": (None, [vp, C.c_int, f32, C.c_uint8, vp]),
+        "orc_prefill": (C.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, f64, vp, i32]),
         "orc_append_static": (C.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
         "orc_int4_pack": (None, [vp, C.c_int, vp]),
         "orc_int4_unpack": (None, [vp, C.c_int, vp]),
@@ -218,6 +219,27 @@ def decode(L, cache, q, q_dtype, block_tables, context_lens, sm_scale=0.0,
                         _ptr(out), threads)
     if rc:
         raise ValueError(f"orc_decode: {rc}")
+    return out
+
+
+def prefill(L, cache, q, q_dtype, query_start, block_tables, context_lens, sm_scale=0.0,
+            threads=1):
+    """Multi-query attention: q uint16 bits [Tq][Hq][d], query_start int32
+    [B+1] (sequence b's queries are its last query_start[b+1]-query_start[b]
+    positions). Returns fp64 [Tq][Hq][d]."""
+    q = np.ascontiguousarray(q)
+    Tq, Hq, d = q.shape
+    qs = np.ascontiguousarray(query_start, np.int32)
+    tables = np.ascontiguousarray(block_tables, np.int32)
+    lens = np.ascontiguousarray(context_lens, np.int32)
+    assert qs[-1] == Tq
+    out = np.zeros((Tq, Hq, d), np.float64)
+    cs = cache.struct()
+    rc = lib.orc_prefill(C.byref(L), C.byref(cs), _ptr(q), q_dtype, len(lens), Hq, _ptr(qs),
+                         _ptr(tables), tables.shape[1], _ptr(lens), sm_scale, _ptr(out),
+                         threads)
+    if rc:
+        raise ValueError(f"orc_prefill: {rc}")
     return out
 
 
