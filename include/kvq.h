@@ -25,6 +25,8 @@
  *                         stage 4 "fused dequantization attention kernel";
  *                         "Dynamic KV Cache Quantization ...", section "Recap
  *                         of KV Caching", the append-then-attend loop).
+ *   kvq_prefill_attention several causal queries per sequence at once
+ *                         (prompt chunks, checking several new tokens).
  *   kvq_bytes_per_token   the cache-size closed form ("KV Cache Optimization"
  *                         glossary, "Technical Architecture"; "KV Cache
  *                         Optimization: Strategies for Faster LLM Inference",
@@ -303,6 +305,47 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache
                                 int32_t split_blocks, void* out,
                                 int32_t out_dtype, void* workspace,
                                 int64_t workspace_bytes, void* stream);
+
+/* Device workspace bytes kvq_prefill_attention needs for these sizes and this
+ * split_blocks (>= 1, or 0 = the library's own choice), or a negative
+ * kvq_status. */
+int64_t kvq_prefill_workspace_bytes(const kvq_layout* layout, int32_t batch,
+                                    int32_t num_q_heads, int32_t max_query_len,
+                                    int32_t max_context_len, int32_t split_blocks);
+
+/* Multi-query (prefill) attention over the paged cache: several query
+ * tokens per sequence at once, causally, as when a prompt chunk is processed
+ * or several new tokens are checked together ("KV Cache Optimization:
+ * Strategies for Faster LLM Inference", sections "Why KV Cache Is Essential
+ * for Efficient LLM Inference" and "Implementing KV Cache Optimization: A
+ * Practical Checklist", prefill versus decode).
+ *  q              device [Tq][num_q_heads][d] in q_dtype (F16 or BF16),
+ *                 Tq = query_start[batch].
+ *  query_start    device int32 [batch + 1], non-decreasing, query_start[0] =
+ *                 0: sequence b's queries are rows query_start[b] ..
+ *                 query_start[b + 1] - 1, nq_b of them, and they are its last
+ *                 nq_b cached positions (their keys and values already
+ *                 appended): query i sits at position context_lens[b] - nq_b
+ *                 + i and attends to positions 0 .. that position.
+ *  max_query_len  host bound on every nq_b (sizes the launch).
+ *  split_blocks   cache blocks per split-K chunk (>= 1); 0 lets the library
+ *                 choose.
+ *  out            device [Tq][num_q_heads][d] in out_dtype.
+ * The other arguments are those of kvq_decode_attention; nq_b = 1 computes
+ * the same function as decode. Under CHANNEL_BLOCK_SYM the positions of the
+ * partial last block (decided by context_lens[b]) are read raw from k_stage
+ * row b. Supported: both sides INT8 or E4M3 under TOKEN_SYM, INT8
+ * CHANNEL_BLOCK_SYM keys with INT8 TOKEN_SYM values, and both NONE16; other
+ * layouts return KVQ_ERR_UNSUPPORTED. Preconditions: nq_b <= context_lens[b]
+ * <= max_context_len; the value-range preconditions of decode. */
+kvq_status kvq_prefill_attention(const kvq_layout* layout, const kvq_cache* cache,
+                                 const void* q, int32_t q_dtype, int32_t batch,
+                                 int32_t num_q_heads, const int32_t* query_start,
+                                 int32_t max_query_len, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, float sm_scale,
+                                 int32_t split_blocks, void* out, int32_t out_dtype,
+                                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Fill a pool: free_stack[i] = initial_order[i] (or i when initial_order is
  * NULL) for i < num_blocks, and *free_top = num_blocks. free_stack, free_top

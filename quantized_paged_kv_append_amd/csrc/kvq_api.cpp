@@ -346,6 +346,122 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const v
   return hip_status(kvq::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Multi-query splits: S blocks per split (the caller's, else an eighth of the
+// longest context, at least 16), J = splits of the longest context, CT =
+// 16-column tiles of max_query_len queries times G heads.
+struct PrefillShape {
+  int64_t S, J, CT, partials;
+};
+
+PrefillShape prefill_shape(const kvq_layout* L, int64_t batch, int64_t num_q_heads,
+                           int64_t max_query_len, int64_t max_context_len, int64_t split_blocks) {
+  PrefillShape sh;
+  const int64_t maxblk = std::max<int64_t>(1, ceil_div(max_context_len, L->block_size));
+  sh.S = split_blocks > 0 ? split_blocks : std::max<int64_t>(16, ceil_div(maxblk, 8));
+  sh.J = ceil_div(maxblk, sh.S);
+  sh.CT = ceil_div(max_query_len * (num_q_heads / L->num_kv_heads), 16);
+  sh.partials = batch * sh.J * L->num_kv_heads * sh.CT * 16;
+  return sh;
+}
+
+}  // namespace
+
+int64_t kvq_prefill_workspace_bytes(const kvq_layout* L, int32_t batch, int32_t num_q_heads,
+                                    int32_t max_query_len, int32_t max_context_len,
+                                    int32_t split_blocks) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  if (batch < 0 || num_q_heads < 1 || num_q_heads % L->num_kv_heads || max_query_len < 0 ||
+      max_context_len < max_query_len || split_blocks < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  const PrefillShape sh = prefill_shape(L, batch, num_q_heads, max_query_len, max_context_len,
+                                        split_blocks);
+  return round_up(sh.partials * L->head_dim * 4, 256) + round_up(sh.partials * 2 * 4, 256);
+}
+
+kvq_status kvq_prefill_attention(const kvq_layout* L, const kvq_cache* C, const void* q,
+                                 int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                 const int32_t* query_start, int32_t max_query_len,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t max_context_len,
+                                 float sm_scale, int32_t split_blocks, void* out,
+                                 int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  s = check_cache(L, C);
+  if (s != KVQ_OK) return s;
+  if (batch < 0 || num_q_heads < 1 || num_q_heads % L->num_kv_heads) return KVQ_ERR_INVALID_ARGUMENT;
+  if (q_dtype != KVQ_F16 && q_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (max_query_len < 0 || max_context_len < max_query_len || split_blocks < 0 ||
+      max_blocks_per_seq < 1)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * L->block_size)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!kvq::prefill_supported(L->k_code, L->v_code, L->k_mode, L->v_mode))
+    return KVQ_ERR_UNSUPPORTED;
+  if (L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM && batch > C->max_seqs)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || max_query_len == 0) return KVQ_OK;
+  if (!q || !out || !query_start || !block_tables || !context_lens || !workspace)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_INVALID_ARGUMENT;
+  const int64_t need = kvq_prefill_workspace_bytes(L, batch, num_q_heads, max_query_len,
+                                                   max_context_len, split_blocks);
+  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  const PrefillShape sh = prefill_shape(L, batch, num_q_heads, max_query_len, max_context_len,
+                                        split_blocks);
+  // one wave per unit in a 1-D grid of 4-wave workgroups; the reduce grid is
+  // (heads, queries, sequences)
+  if (sh.partials / 16 > 4 * (int64_t)INT32_MAX || max_query_len > 65535 || batch > 65535)
+    return KVQ_ERR_UNSUPPORTED;
+  kvq::PrefillPlan pp;
+  kvq::DecodePlan& p = pp.d;
+  p.q = q;
+  p.q_bf16 = q_dtype == KVQ_BF16;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = L->num_kv_heads;
+  p.head_dim = L->head_dim;
+  p.block_size = L->block_size;
+  p.k_code = L->k_code;
+  p.v_code = L->v_code;
+  p.k_mode = L->k_mode;
+  p.v_mode = L->v_mode;
+  p.src_bf16 = L->src_dtype == KVQ_BF16;
+  p.k_codes = C->k_codes;
+  p.v_codes = C->v_codes;
+  p.k_scale = C->k_scale;
+  p.v_scale = C->v_scale;
+  p.k_zero = C->k_zero;
+  p.v_zero = C->v_zero;
+  p.k_stage = C->k_stage;
+  p.num_blocks = C->num_blocks;
+  p.block_tables = block_tables;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.context_lens = context_lens;
+  p.max_context_len = max_context_len;
+  p.split_blocks = (int32_t)sh.S;
+  p.item_bound = 0;
+  p.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)L->head_dim));
+  p.out = out;
+  p.out_dtype = out_dtype;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                     round_up(sh.partials * L->head_dim * 4, 256));
+  pp.query_start = query_start;
+  pp.max_query_len = max_query_len;
+  pp.splits = (int32_t)sh.J;
+  pp.split_blocks = (int32_t)sh.S;
+  pp.col_tiles = (int32_t)sh.CT;
+  return hip_status(kvq::launch_prefill(pp, static_cast<hipStream_t>(stream)));
+}
+
 kvq_status kvq_pool_init(int32_t* free_stack, int32_t* free_top, const int32_t* initial_order,
                          int64_t num_blocks, void* stream) {
   if (!free_stack || !free_top || num_blocks < 1 || num_blocks > INT32_MAX)

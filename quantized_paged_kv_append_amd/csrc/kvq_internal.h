@@ -90,6 +90,21 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
 bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
                       int32_t v_mode);
 
+// Multi-query (prefill) attention: the decode fields (q is [Tq][Hq][d], out
+// [Tq][Hq][d], the workspace [batch][splits][H][col_tiles * 16] partials)
+// plus the query rows of each sequence.
+struct PrefillPlan {
+  DecodePlan d;
+  const int32_t* query_start;  // [batch + 1]
+  int32_t max_query_len;
+  int32_t splits;              // J: splits per sequence (upper bound)
+  int32_t split_blocks;        // S: cache blocks per split
+  int32_t col_tiles;           // CT: 16-column tiles per (sequence, KV head)
+};
+
+hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream);
+bool prefill_supported(int32_t k_code, int32_t v_code, int32_t k_mode, int32_t v_mode);
+
 hipError_t launch_pool_init(int32_t* stack, int32_t* top, const int32_t* order,
                             int64_t n, hipStream_t stream);
 hipError_t launch_blocks_reserve(int32_t* stack, int32_t* top, int64_t capacity,

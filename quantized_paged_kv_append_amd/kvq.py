@@ -67,6 +67,9 @@ _SIGS = {
     "kvq_decode_workspace_bytes": (_i64, [_LP, _i32, _i32, _i32, _i32]),
     "kvq_decode_attention": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
                                     _i32, _f32, _i32, _vp, _i32, _vp, _i64, _vp]),
+    "kvq_prefill_workspace_bytes": (_i64, [_LP, _i32, _i32, _i32, _i32, _i32]),
+    "kvq_prefill_attention": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
+                                     _vp, _i32, _f32, _i32, _vp, _i32, _vp, _i64, _vp]),
     "kvq_pool_init": (_i32, [_vp, _vp, _vp, _i64, _vp]),
     "kvq_blocks_reserve": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32,
                                   _vp, _vp, _vp, _vp]),
@@ -197,6 +200,33 @@ def kvq_decode_attention(layout, cache: PagedCache, q, block_tables, context_len
         int(max_context_len), float(sm_scale), int(split_blocks), _ptr(out),
         DTYPES[out.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def kvq_prefill_workspace_bytes(layout, batch, num_q_heads, max_query_len, max_context_len,
+                                split_blocks=0) -> int:
+    n = _lib.kvq_prefill_workspace_bytes(C.byref(layout), batch, num_q_heads, max_query_len,
+                                         max_context_len, split_blocks)
+    if n < 0:
+        raise KvqError("kvq_prefill_workspace_bytes", n)
+    return n
+
+
+def kvq_prefill_attention(layout, cache: PagedCache, q, query_start, max_query_len,
+                          block_tables, context_lens, max_context_len, out, workspace,
+                          sm_scale=0.0, split_blocks=0, stream=None):
+    """q: device [Tq][Hq][d] fp16/bf16; query_start: int32 [B+1] (sequence b's
+    queries are its last query_start[b+1]-query_start[b] positions);
+    block_tables: int32 [B][max_blocks]; context_lens: int32 [B]; out: device
+    [Tq][Hq][d]; workspace: device uint8 tensor of
+    kvq_prefill_workspace_bytes(...)."""
+    _, Hq, _ = q.shape
+    B = context_lens.numel()
+    _check("kvq_prefill_attention", _lib.kvq_prefill_attention(
+        C.byref(layout), C.byref(cache.struct), _ptr(q), DTYPES[q.dtype], B, Hq,
+        _ptr(query_start), int(max_query_len), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), int(max_context_len), float(sm_scale), int(split_blocks),
+        _ptr(out), DTYPES[out.dtype], _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def kvq_pool_init(free_stack, free_top, initial_order=None, stream=None):

@@ -194,6 +194,40 @@ def test_append_static_rejects_bad_arguments_on_host():
     assert app(L, cs, sc, None, sc, None, rows=p) == kq.KVQ_ERR_INVALID_ARGUMENT   # rows unused
 
 
+def test_prefill_rejects_bad_arguments_on_host():
+    L = kq.make_layout(8, 128, 16, "int8")
+    cs = _fake_cache(L)
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+
+    def pre(**kw):
+        a = dict(q=p, q_dtype=kq.KVQ_BF16, batch=2, hq=32, qs=p, maxq=8, tables=p, maxb=4,
+                 lens=p, maxlen=64, sm=0.0, split=0, out=p, out_dtype=kq.KVQ_F32, ws=p,
+                 wsb=1 << 30, L=L, cs=cs)
+        a.update(kw)
+        return lib.kvq_prefill_attention(C.byref(a["L"]), C.byref(a["cs"]), a["q"], a["q_dtype"],
+                                         a["batch"], a["hq"], a["qs"], a["maxq"], a["tables"],
+                                         a["maxb"], a["lens"], a["maxlen"], a["sm"], a["split"],
+                                         a["out"], a["out_dtype"], a["ws"], a["wsb"], None)
+    assert pre(hq=30) == kq.KVQ_ERR_INVALID_ARGUMENT            # Hq % H
+    assert pre(maxq=65) == kq.KVQ_ERR_INVALID_ARGUMENT          # more queries than context
+    assert pre(maxlen=65) == kq.KVQ_ERR_INVALID_ARGUMENT        # > maxb * bs
+    assert pre(split=-1) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert pre(qs=None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert pre(q=C.c_void_p((1 << 21) + 2)) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert pre(wsb=16) == kq.KVQ_ERR_WORKSPACE_TOO_SMALL
+    assert pre(sm=float("inf")) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert pre(batch=0) == kq.KVQ_OK and pre(maxq=0) == kq.KVQ_OK
+    L4 = kq.make_layout(8, 128, 32, "int4", k_mode="group_asym", group_size=32)
+    c4 = _fake_cache(L4)
+    c4.k_zero, c4.v_zero = 1 << 25, (1 << 25) + 4096
+    assert pre(L=L4, cs=c4) == kq.KVQ_ERR_UNSUPPORTED
+    # workspace grows with the query count and shrinks with longer splits
+    w1 = kq.kvq_prefill_workspace_bytes(L, 2, 32, 8, 4096, 0)
+    assert kq.kvq_prefill_workspace_bytes(L, 2, 32, 16, 4096, 0) > w1
+    assert kq.kvq_prefill_workspace_bytes(L, 2, 32, 8, 4096, 256) < w1
+
+
 def test_pool_calls_reject_bad_arguments_on_host():
     lib = kq._lib
     p = C.c_void_p(1 << 21)
