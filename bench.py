@@ -31,9 +31,10 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_F16_TFLOPS = 2500.0   # dense fp16 MFMA, MI355X
 HERE = os.path.dirname(os.path.abspath(__file__))
 # sources whose change invalidates committed decode counters
-DECODE_SOURCES = ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_api.cpp")
+DECODE_SOURCES = ("kvq_decode.hip", "kvq_attn_tiles.h", "kvq_device.h", "kvq_internal.h")
 
 
 def decode_source_hash():
@@ -70,6 +71,11 @@ def parse():
     ap.add_argument("--workload", default="llama3_70b", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's own count")
     ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=0, help="0 = the workload's own batch")
+    ap.add_argument("--prefill-queries", type=int, default=0,
+                    help="append this many tokens per sequence per step and attend with "
+                         "all of them at once through kvq_prefill_attention (0: one "
+                         "decode query per sequence)")
     ap.add_argument("--identity-pool", action="store_true",
                     help="blocks in order instead of a seeded permutation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -144,12 +150,15 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     w = workloads.get(args.workload)
+    if args.batch:
+        w = workloads.get(args.workload, batch=args.batch)
     layers = args.layers or w.layers
+    nq = args.prefill_queries
     LL = kq.make_layout(w.num_kv_heads, w.head_dim, w.block_size, w.k_code, w.v_code,
                         w.k_mode, w.v_mode, w.group_size, w.torch_dtype)
     lens = workloads.lengths(w)
     B, Hq, H, d, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
-    new_per_step = w.new_tokens
+    new_per_step = nq if nq else w.new_tokens
     total_steps = args.warmup + args.steps
     headroom = new_per_step * total_steps
     nb = workloads.pool_blocks(lens, bs, headroom_tokens=headroom + bs)
@@ -206,15 +215,24 @@ def main():
     # ---- per-step inputs: new K/V rows and queries for every layer ---------
     Tn = B * new_per_step
     new_kv = [workloads.kv_rows(w, Tn, layer=layer, device=dev, chunk=999) for layer in range(layers)]
-    qs = [workloads.queries(w, device=dev, layer=layer) for layer in range(layers)]
+    if nq:
+        qs = [workloads.query_rows(w, B * nq, device=dev, layer=layer) for layer in range(layers)]
+        qstart = torch.arange(0, B * nq + 1, nq, dtype=torch.int32, device=dev)
+    else:
+        qs = [workloads.queries(w, device=dev, layer=layer) for layer in range(layers)]
     new_tok = torch.full((B,), new_per_step, dtype=torch.int32, device=dev)
     slots = torch.empty(Tn, dtype=torch.int64, device=dev)
     stage_rows = None
     if w.k_mode == "channel_block":
         stage_rows = torch.from_numpy(np.repeat(np.arange(B, dtype=np.int32), new_per_step)).to(dev)
-    out = torch.empty((B, Hq, d), dtype=w.torch_dtype, device=dev)
-    ws = torch.empty(kq.kvq_decode_workspace_bytes(LL, B, Hq, max_ctx, args.split_blocks),
-                     dtype=torch.uint8, device=dev)
+    if nq:
+        out = torch.empty((B * nq, Hq, d), dtype=w.torch_dtype, device=dev)
+        ws = torch.empty(kq.kvq_prefill_workspace_bytes(LL, B, Hq, nq, max_ctx, args.split_blocks),
+                         dtype=torch.uint8, device=dev)
+    else:
+        out = torch.empty((B, Hq, d), dtype=w.torch_dtype, device=dev)
+        ws = torch.empty(kq.kvq_decode_workspace_bytes(LL, B, Hq, max_ctx, args.split_blocks),
+                         dtype=torch.uint8, device=dev)
     dec_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(layers)] for _ in range(args.steps)]
 
@@ -225,8 +243,12 @@ def main():
             kq.kvq_append(LL, caches[layer], k, v, slots, stage_rows)
             if evs is not None:
                 evs[layer][0].record(stream)
-            kq.kvq_decode_attention(LL, caches[layer], qs[layer], tables, ctx, max_ctx, out,
-                                    ws, split_blocks=args.split_blocks)
+            if nq:
+                kq.kvq_prefill_attention(LL, caches[layer], qs[layer], qstart, nq, tables, ctx,
+                                         max_ctx, out, ws, split_blocks=args.split_blocks)
+            else:
+                kq.kvq_decode_attention(LL, caches[layer], qs[layer], tables, ctx, max_ctx, out,
+                                        ws, split_blocks=args.split_blocks)
             if evs is not None:
                 evs[layer][1].record(stream)
 
@@ -277,11 +299,32 @@ def main():
     achieved = dec_bytes_launch / (dec_avg_ms / 1e3) / 1e9
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not nq:
         cpu = cpu_baseline(w, lens, args)
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": committed_traffic(w.name),
+            "kernel": "decode_split_kernel + decode_reduce_kernel (one kvq_decode_attention)",
+            "bytes_per_launch": dec_bytes_launch}
+    prefill = None
+    if nq:
+        # MFMA work per launch: every (query, head) pair takes 4 d flops per
+        # position it sees (QK and PV, a multiply and an add each)
+        vis = [sum(int(c) - nq + i + 1 for c in (ctx_before + nq * (s + 1)) for i in range(nq))
+               for s in range(args.steps)]
+        flops = float(np.mean(vis)) * Hq * 4 * d
+        tflops = flops / (dec_avg_ms / 1e3) / 1e12
+        prefill = {"queries_per_sequence": nq, "flops_per_launch": flops,
+                   "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
+                   "hbm_frac": roof["frac"]}
+        roof = ({"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
+                 "traffic": None, "flops_per_launch": flops}
+                if tflops / PEAK_MFMA_F16_TFLOPS > roof["frac"] else dict(roof, traffic=None))
+        roof["kernel"] = "prefill_split_kernel + prefill_reduce_kernel (one kvq_prefill_attention)"
 
     line = {
-        "metric": "decode-attn KV GB/s (% of 8 TB/s HBM) + append tok/s, INT8/FP8/INT4",
+        "metric": ("prefill-attn KV GB/s (multi-query, causal) + MFMA TFLOP/s" if nq else
+                   "decode-attn KV GB/s (% of 8 TB/s HBM) + append tok/s, INT8/FP8/INT4"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -301,6 +344,7 @@ def main():
             "k_code": w.k_code, "v_code": w.v_code, "k_mode": w.k_mode, "v_mode": w.v_mode,
             "new_tokens_per_step": new_per_step, "pool": "identity" if args.identity_pool else "permuted",
             "split_blocks": args.split_blocks or "auto",
+            "prefill_queries": nq or None,
         },
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "kv_bytes_per_step": kv_bytes_step,
@@ -313,12 +357,8 @@ def main():
         "append_tok_s": round(append_tok_s, 1),
         "append_GBps": round(append_gbs, 2),
         "append_bytes_per_token": append_bytes_per_token(w),
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": committed_traffic(w.name),
-            "kernel": "decode_split_kernel + decode_reduce_kernel (one kvq_decode_attention)",
-            "bytes_per_launch": dec_bytes_launch,
-        },
+        "roofline": roof,
+        "prefill": prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

@@ -348,9 +348,11 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const v
 
 namespace {
 
-// Multi-query splits: S blocks per split (the caller's, else an eighth of the
-// longest context, at least 16), J = splits of the longest context, CT =
-// 16-column tiles of max_query_len queries times G heads.
+// Multi-query splits: S blocks per split (the caller's, else a sixteenth of
+// the longest context within [32, 64]: four waves share a split, and longer
+// splits leave skewed batches waiting on their longest sequences), J =
+// splits of the longest context, CT = 16-column tiles of max_query_len
+// queries times G heads.
 struct PrefillShape {
   int64_t S, J, CT, partials;
 };
@@ -359,7 +361,8 @@ PrefillShape prefill_shape(const kvq_layout* L, int64_t batch, int64_t num_q_hea
                            int64_t max_query_len, int64_t max_context_len, int64_t split_blocks) {
   PrefillShape sh;
   const int64_t maxblk = std::max<int64_t>(1, ceil_div(max_context_len, L->block_size));
-  sh.S = split_blocks > 0 ? split_blocks : std::max<int64_t>(16, ceil_div(maxblk, 8));
+  sh.S = split_blocks > 0 ? split_blocks
+                         : std::min<int64_t>(64, std::max<int64_t>(32, ceil_div(maxblk, 16)));
   sh.J = ceil_div(maxblk, sh.S);
   sh.CT = ceil_div(max_query_len * (num_q_heads / L->num_kv_heads), 16);
   sh.partials = batch * sh.J * L->num_kv_heads * sh.CT * 16;
@@ -416,9 +419,9 @@ kvq_status kvq_prefill_attention(const kvq_layout* L, const kvq_cache* C, const 
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   const PrefillShape sh = prefill_shape(L, batch, num_q_heads, max_query_len, max_context_len,
                                         split_blocks);
-  // one wave per unit in a 1-D grid of 4-wave workgroups; the reduce grid is
-  // (heads, queries, sequences)
-  if (sh.partials / 16 > 4 * (int64_t)INT32_MAX || max_query_len > 65535 || batch > 65535)
+  // one workgroup per unit in a 1-D grid; the reduce grid is (heads,
+  // queries, sequences)
+  if (sh.partials / 16 > (int64_t)INT32_MAX || max_query_len > 65535 || batch > 65535)
     return KVQ_ERR_UNSUPPORTED;
   kvq::PrefillPlan pp;
   kvq::DecodePlan& p = pp.d;

@@ -1,0 +1,488 @@
+// kvq_attn_tiles.h -- the attention tile machinery shared by decode
+// (kvq_decode.hip) and multi-query attention (kvq_prefill.hip): cache-tile
+// loads, exact code-to-fp16 conversion, the 16-token MFMA tile step with
+// online softmax, per-channel query folding, and small wave reductions.
+// Device code for gfx950, internal to the library.
+#pragma once
+
+#include <type_traits>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* k_scale;
+  const float* v_scale;
+  const uint8_t* k_zero;
+  const uint8_t* v_zero;
+  const uint16_t* k_stage;  // per-channel keys: raw rows of partial blocks
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_acc;
+  float* ws_ml;
+  int64_t num_blocks;
+  int32_t q_bf16;
+  int32_t stage_bf16;
+  int32_t Hq;
+  int32_t H;
+  int32_t G;
+  int32_t max_blocks;
+  int32_t batch;
+  int32_t max_len;       // every context length is cut to this
+  int32_t split_blocks;  // 0: planned from the lengths
+  float sm_log2;  // sm_scale * log2(e)
+};
+
+// Max and sum of a float over the wave by the same DPP pattern, with -inf
+// (max) or 0 (sum) in lanes that have no source; the result is lane 63's.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce_f(float x) {
+  const int idle = MAX ? __float_as_int(-INFINITY) : 0;
+  auto step = [&](float v, float w) { return MAX ? fmaxf(v, w) : v + w; };
+#define KVQ_DPP_STEP(ctrl, rmask)                                                       \
+  x = step(x, __int_as_float(__builtin_amdgcn_update_dpp(idle, __float_as_int(x), ctrl, \
+                                                          rmask, 0xF, false)))
+  KVQ_DPP_STEP(0x111, 0xF);
+  KVQ_DPP_STEP(0x112, 0xF);
+  KVQ_DPP_STEP(0x114, 0xF);
+  KVQ_DPP_STEP(0x118, 0xF);
+  KVQ_DPP_STEP(0x142, 0xA);
+  KVQ_DPP_STEP(0x143, 0xC);
+#undef KVQ_DPP_STEP
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+
+template <int D, int BS>
+struct Tile8 {
+  static constexpr int NT = BS / 16;     // 16-token MFMA tiles per block
+  static constexpr int KV = D / 64;      // 16-byte key vectors per lane per tile
+  static constexpr int VB = D / 16;      // value bytes per token per lane
+  u32x4 k[NT][KV];
+  uint32_t v[NT][4][VB / 4];             // [tile][token i][dword]
+  float4v sk[NT];
+  float4v sv[NT];
+  float kc[D / 64];                      // per-channel key scales, lane's slice
+};
+
+// KCH: keys carry one scale per channel for the whole block
+// (CHANNEL_BLOCK_SYM), loaded as D/64 consecutive floats per lane.
+template <int D, int BS, bool KCH>
+__device__ __forceinline__ void load_tile8(Tile8<D, BS>& t, const DecodeArgs& a,
+                                           int64_t bh, int lane) {
+  const int r = lane & 15, j = lane >> 4;
+  const uint8_t* kb = a.k_codes + bh * BS * D;
+  const uint8_t* vb = a.v_codes + bh * BS * D;
+#pragma unroll
+  for (int nt = 0; nt < Tile8<D, BS>::NT; ++nt) {
+    const uint8_t* kr = kb + (nt * 16 + r) * D + j * (D / 4);
+#pragma unroll
+    for (int u = 0; u < Tile8<D, BS>::KV; ++u)
+      t.k[nt][u] = *reinterpret_cast<const u32x4*>(kr + 16 * u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* vr = vb + (nt * 16 + 4 * j + i) * D + r * (D / 16);
+      if constexpr (D == 128) {
+        u32x2 w = *reinterpret_cast<const u32x2*>(vr);
+        t.v[nt][i][0] = w.x;
+        t.v[nt][i][1] = w.y;
+      } else {
+        t.v[nt][i][0] = *reinterpret_cast<const uint32_t*>(vr);
+      }
+    }
+    if constexpr (!KCH)
+      t.sk[nt] = *reinterpret_cast<const float4v*>(a.k_scale + bh * BS + nt * 16 + 4 * j);
+    t.sv[nt] = *reinterpret_cast<const float4v*>(a.v_scale + bh * BS + nt * 16 + 4 * j);
+  }
+  if constexpr (KCH) {
+    const float* kc = a.k_scale + bh * D + lane * (D / 64);
+    if constexpr (D == 128) {
+      const float2 w = *reinterpret_cast<const float2*>(kc);
+      t.kc[0] = w.x;
+      t.kc[1] = w.y;
+    } else {
+      t.kc[0] = *kc;
+    }
+  }
+}
+
+// 8 code bytes (two dwords) to 8 fp16 values, in byte order.
+template <int CODE>
+__device__ __forceinline__ half8v codes8_to_h8(uint32_t lo, uint32_t hi) {
+  half2v p0, p1, p2, p3;
+  if constexpr (CODE == KVQ_CODE_FP8_E4M3) {
+    p0 = fp8x2_to_h2<false>(lo);
+    p1 = fp8x2_to_h2<true>(lo);
+    p2 = fp8x2_to_h2<false>(hi);
+    p3 = fp8x2_to_h2<true>(hi);
+  } else {
+    const uint32_t xl = lo ^ 0x80808080u, xh = hi ^ 0x80808080u;
+    p0 = i8x2_to_h2(xl, 0x04010400u);
+    p1 = i8x2_to_h2(xl, 0x04030402u);
+    p2 = i8x2_to_h2(xh, 0x04010400u);
+    p3 = i8x2_to_h2(xh, 0x04030402u);
+  }
+  half8v o;
+  o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+  o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+  return o;
+}
+
+// Value operand of MFMA c: bytes c of the lane's four token words, as fp16.
+// a01 = [t0.bX, t1.bX, t0.bY, t1.bY], a23 likewise for tokens 2, 3.
+template <int CODE, bool HI>
+__device__ __forceinline__ half4v vpair_to_h4(uint32_t a01, uint32_t a23) {
+  half2v x, y;
+  if constexpr (CODE == KVQ_CODE_FP8_E4M3) {
+    x = fp8x2_to_h2<HI>(a01);
+    y = fp8x2_to_h2<HI>(a23);
+  } else {
+    const uint32_t sel = HI ? 0x04030402u : 0x04010400u;
+    x = i8x2_to_h2(a01 ^ 0x80808080u, sel);
+    y = i8x2_to_h2(a23 ^ 0x80808080u, sel);
+  }
+  half4v o;
+  o[0] = x[0]; o[1] = x[1]; o[2] = y[0]; o[3] = y[1];
+  return o;
+}
+
+// max over the four lanes {l, l^16, l^32, l^48} (one head column), with
+// the gfx950 lane-swap instructions instead of LDS permutes.
+__device__ __forceinline__ float colmax4(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float colsum4(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <int D>
+struct SoftmaxState {
+  float m;                 // running max (log2 units) of head r
+  float l;                 // this lane's part of the running sum
+  float4v acc[D / 16];     // O^T accumulators
+};
+
+// Eight raw 16-bit key values to fp16 operands: bf16 values are exact in
+// fp16 within its range (the same bound as for value scales).
+__device__ __forceinline__ half8v raw8_to_h8(const u32x4& w, bool bf16) {
+  if (!bf16) return __builtin_bit_cast(half8v, w);
+  half8v o;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    o[2 * u] = (half_t)bf16_lo(w[u]);
+    o[2 * u + 1] = (half_t)bf16_hi(w[u]);
+  }
+  return o;
+}
+
+// Where the keys of a tile come from.
+enum KeySource {
+  kKeyTokenScale = 0,  // codes; the score takes the token's key scale
+  kKeyChannel = 1,     // codes; per-channel scales are already in the query
+  kKeyRaw = 2,         // raw staged rows, kraw[c] = elements of chunk c
+};
+
+// One 16-token tile: scores, online softmax, PV. TAIL handles the tile that
+// ends past the sequence length: scores of tokens at or past L (this lane's
+// column limit) are masked, and value codes of tokens at or past Lv (the rows
+// that hold data; Lv < 0 means L) are zeroed, since they may hold NaN bytes.
+// In decode both limits are the length; causal multi-query columns differ in
+// L while sharing the value operand, so only rows past the data are zeroed.
+template <int CODE, int D, int BS, bool TAIL, int KSRC = kKeyTokenScale>
+__device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos0, int L,
+                                          const half8v* qop, float cscore, int j,
+                                          SoftmaxState<D>& st, const u32x4* kraw = nullptr,
+                                          bool raw_bf16 = false, const half8v* qlo = nullptr,
+                                          int Lv = -1) {
+  constexpr int NCH = D / 32;
+  constexpr int NPV = D / 16;
+  const int Ld = Lv < 0 ? L : Lv;
+  float4v S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    half8v kop;
+    if constexpr (KSRC == kKeyRaw) {
+      kop = raw8_to_h8(kraw[c], raw_bf16);
+    } else {
+      const u32x4& kw = t.k[nt][c / 2];
+      const uint32_t lo = (c & 1) ? kw.z : kw.x;
+      const uint32_t hi = (c & 1) ? kw.w : kw.y;
+      kop = codes8_to_h8<CODE>(lo, hi);
+    }
+    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[c], S, 0, 0, 0);
+    if constexpr (KSRC == kKeyChannel)  // low half of the split query
+      S = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo[c], S, 0, 0, 0);
+  }
+  bool ok[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ok[e] = !TAIL || pos0 + 4 * j + e < L;
+  float s[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s[e] = KSRC == kKeyTokenScale ? S[e] * t.sk[nt][e] * cscore : S[e] * cscore;
+    if (TAIL && !ok[e]) s[e] = -INFINITY;
+  }
+  const float mt = colmax4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+  const float mn = fmaxf(st.m, mt);
+  const float msafe = mn == -INFINITY ? 0.0f : mn;
+  if (__any(mn > st.m)) {  // a running max grew: rescale (rare after warm-up)
+    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
+  }
+  st.m = mn;
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - msafe);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  half4v pop;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float pv = p[e] * t.sv[nt][e];
+    if (TAIL && !ok[e]) pv = 0.0f;
+    pop[e] = (half_t)pv;
+  }
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) {
+    uint32_t t0 = t.v[nt][0][w], t1 = t.v[nt][1][w];
+    uint32_t t2 = t.v[nt][2][w], t3 = t.v[nt][3][w];
+    if (TAIL) {  // zero the codes of rows past the data (E4M3 NaN bytes)
+      const int pv0 = pos0 + 4 * j;
+      t0 = pv0 + 0 < Ld ? t0 : 0u;
+      t1 = pv0 + 1 < Ld ? t1 : 0u;
+      t2 = pv0 + 2 < Ld ? t2 : 0u;
+      t3 = pv0 + 3 < Ld ? t3 : 0u;
+    }
+    // [t0.b0 t1.b0 t0.b1 t1.b1], [t0.b2 t1.b2 t0.b3 t1.b3]
+    const uint32_t a01l = __builtin_amdgcn_perm(t1, t0, 0x05010400u);
+    const uint32_t a01h = __builtin_amdgcn_perm(t1, t0, 0x07030602u);
+    const uint32_t a23l = __builtin_amdgcn_perm(t3, t2, 0x05010400u);
+    const uint32_t a23h = __builtin_amdgcn_perm(t3, t2, 0x07030602u);
+    const int c0 = 4 * w;
+    st.acc[c0 + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(vpair_to_h4<CODE, false>(a01l, a23l), pop, st.acc[c0 + 0], 0, 0, 0);
+    st.acc[c0 + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vpair_to_h4<CODE, true>(a01l, a23l), pop, st.acc[c0 + 1], 0, 0, 0);
+    st.acc[c0 + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(vpair_to_h4<CODE, false>(a01h, a23h), pop, st.acc[c0 + 2], 0, 0, 0);
+    st.acc[c0 + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(vpair_to_h4<CODE, true>(a01h, a23h), pop, st.acc[c0 + 3], 0, 0, 0);
+  }
+}
+
+// A block whose BS tokens all lie before the sequence end.
+template <int CODE, int D, int BS, int KSRC = kKeyTokenScale>
+__device__ __forceinline__ void full_block_step(const Tile8<D, BS>& t, int i, int L,
+                                                const half8v* qop, float cscore, int j,
+                                                SoftmaxState<D>& st,
+                                                const half8v* qlo = nullptr) {
+#pragma unroll
+  for (int nt = 0; nt < BS / 16; ++nt)
+    tile_step<CODE, D, BS, false, KSRC>(t, nt, i * BS + nt * 16, L, qop, cscore, j, st,
+                                        nullptr, false, qlo);
+}
+
+// Per-channel keys: the block's scales fold into the query,
+// q'[c] = (q[c] 2^-e) sK[c] in fp32, which enters the MFMA as the sum of two
+// fp16 operands, hi = fp16(q') and lo = fp16(q' - hi): one fp16 rounding of
+// q' would cost 2^-12 relative per term, as much as the whole error budget
+// when a few outlier channels dominate the score. Each lane holds D/64
+// scales of the block; the wave trades them through its own LDS slice `x`
+// (D floats) so that lane (r, j) gets channels [j D/4, (j+1) D/4). The fences
+// only keep the compiler from moving LDS accesses across them: a wave's LDS
+// operations complete in issue order.
+template <int D, int BS>
+__device__ __forceinline__ void channel_query(const Tile8<D, BS>& t, float* x, const float* qs,
+                                              int lane, half8v* qop, half8v* qlo) {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if constexpr (D == 128)
+    *reinterpret_cast<float2*>(x + 2 * lane) = make_float2(t.kc[0], t.kc[1]);
+  else
+    x[lane] = t.kc[0];
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const float* src = x + (lane >> 4) * (D / 4);
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const float4v s0 = *reinterpret_cast<const float4v*>(src + 8 * c);
+    const float4v s1 = *reinterpret_cast<const float4v*>(src + 8 * c + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qp = qs[8 * c + e] * (e < 4 ? s0[e] : s1[e - 4]);
+      const half_t hi = (half_t)qp;
+      qop[c][e] = hi;
+      qlo[c][e] = (half_t)(qp - (float)hi);
+    }
+  }
+}
+
+// The sequence's last block when it is only partly filled. With KRAW the
+// keys come from the staged rows kraw[tile][chunk] instead of the codes.
+template <int CODE, int D, int BS, bool KRAW = false>
+__device__ __forceinline__ void last_block_step(const Tile8<D, BS>& t, int i, int L,
+                                                const half8v* qop, float cscore, int j,
+                                                SoftmaxState<D>& st,
+                                                const u32x4 (*kraw)[D / 32] = nullptr,
+                                                bool raw_bf16 = false) {
+  constexpr int KS = KRAW ? kKeyRaw : kKeyTokenScale;
+#pragma unroll
+  for (int nt = 0; nt < BS / 16; ++nt) {
+    const int pos0 = i * BS + nt * 16;
+    const u32x4* kr = KRAW ? kraw[nt] : nullptr;
+    if (pos0 + 16 <= L)
+      tile_step<CODE, D, BS, false, KS>(t, nt, pos0, L, qop, cscore, j, st, kr, raw_bf16);
+    else if (pos0 < L)
+      tile_step<CODE, D, BS, true, KS>(t, nt, pos0, L, qop, cscore, j, st, kr, raw_bf16);
+  }
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ void load_query(const uint16_t* qp, float* qf) {
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 8 * u);
+    unpack2<BF16>(w.x, qf[8 * u + 0], qf[8 * u + 1]);
+    unpack2<BF16>(w.y, qf[8 * u + 2], qf[8 * u + 3]);
+    unpack2<BF16>(w.z, qf[8 * u + 4], qf[8 * u + 5]);
+    unpack2<BF16>(w.w, qf[8 * u + 6], qf[8 * u + 7]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit passthrough (KVQ_CODE_NONE16): rows hold the source values. Keys
+// enter the score MFMA as fp16 like the staged rows above (lane (r, j):
+// elements [j d/4, (j+1) d/4) of token r). Values: lane (r, j) loads
+// elements [r d/16, (r+1) d/16) of tokens 4j..4j+3, and the operand of PV
+// MFMA c is element c of those four tokens -- the same output mapping as
+// the 8-bit codes. bf16 values convert to fp16 exactly within fp16's range.
+// ---------------------------------------------------------------------------
+template <int D, int BS>
+struct TileRaw {
+  static constexpr int NT = BS / 16;
+  static constexpr int NCH = D / 32;   // 16-byte key vectors per lane per tile
+  static constexpr int VW = D / 32;    // 32-bit value words per token per lane
+  u32x4 k[NT][NCH];
+  uint32_t v[NT][4][VW];               // [tile][token i][word]
+};
+
+template <int D, int BS>
+__device__ __forceinline__ void load_tile_raw(TileRaw<D, BS>& t, const DecodeArgs& a,
+                                              int64_t bh, int lane) {
+  const int r = lane & 15, j = lane >> 4;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_codes) + bh * BS * D;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_codes) + bh * BS * D;
+#pragma unroll
+  for (int nt = 0; nt < TileRaw<D, BS>::NT; ++nt) {
+    const uint16_t* kr = kb + (nt * 16 + r) * D + j * (D / 4);
+#pragma unroll
+    for (int c = 0; c < TileRaw<D, BS>::NCH; ++c)
+      t.k[nt][c] = *reinterpret_cast<const u32x4*>(kr + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* vr = vb + (nt * 16 + 4 * j + i) * D + r * (D / 16);
+      if constexpr (D == 128) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(vr);
+        t.v[nt][i][0] = w.x; t.v[nt][i][1] = w.y; t.v[nt][i][2] = w.z; t.v[nt][i][3] = w.w;
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vr);
+        t.v[nt][i][0] = w.x; t.v[nt][i][1] = w.y;
+      }
+    }
+  }
+}
+
+// Element c (0 or 1 of word w) of four tokens' value words as fp16.
+__device__ __forceinline__ half4v raw_vop(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                          bool hi, bool bf16) {
+  half4v o;
+  if (bf16) {
+    o[0] = (half_t)(hi ? bf16_hi(w0) : bf16_lo(w0));
+    o[1] = (half_t)(hi ? bf16_hi(w1) : bf16_lo(w1));
+    o[2] = (half_t)(hi ? bf16_hi(w2) : bf16_lo(w2));
+    o[3] = (half_t)(hi ? bf16_hi(w3) : bf16_lo(w3));
+  } else {
+    const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+    const uint32_t x = __builtin_amdgcn_perm(w1, w0, sel), y = __builtin_amdgcn_perm(w3, w2, sel);
+    o = __builtin_bit_cast(half4v, (u32x2){x, y});
+  }
+  return o;
+}
+
+template <int D, int BS, bool TAIL>
+__device__ __forceinline__ void tile_step_raw(const TileRaw<D, BS>& t, int nt, int pos0, int L,
+                                              const half8v* qop, float cscore, int j,
+                                              SoftmaxState<D>& st, bool bf16, int Lv = -1) {
+  constexpr int NCH = D / 32;
+  constexpr int NPV = D / 16;
+  const int Ld = Lv < 0 ? L : Lv;   // as in tile_step
+  float4v S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(raw8_to_h8(t.k[nt][c], bf16), qop[c], S, 0, 0, 0);
+  bool ok[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ok[e] = !TAIL || pos0 + 4 * j + e < L;
+  float s[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[e] = (TAIL && !ok[e]) ? -INFINITY : S[e] * cscore;
+  const float mt = colmax4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+  const float mn = fmaxf(st.m, mt);
+  const float msafe = mn == -INFINITY ? 0.0f : mn;
+  if (__any(mn > st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
+  }
+  st.m = mn;
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = (TAIL && !ok[e]) ? 0.0f : __builtin_amdgcn_exp2f(s[e] - msafe);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  half4v pop;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pop[e] = (half_t)p[e];
+#pragma unroll
+  for (int c = 0; c < NPV; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = t.v[nt][i][c / 2];
+      if (TAIL && pos0 + 4 * j + i >= Ld) w[i] = 0u;   // rows past the data may hold NaN
+    }
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(raw_vop(w[0], w[1], w[2], w[3], c & 1, bf16),
+                                                      pop, st.acc[c], 0, 0, 0);
+  }
+}
+
+// Tile-type dispatch for the block streaming below.
+template <int D, int BS, bool KCH>
+__device__ __forceinline__ void load_tile(Tile8<D, BS>& t, const DecodeArgs& a, int64_t bh,
+                                          int lane) {
+  load_tile8<D, BS, KCH>(t, a, bh, lane);
+}
+template <int D, int BS, bool KCH>
+__device__ __forceinline__ void load_tile(TileRaw<D, BS>& t, const DecodeArgs& a, int64_t bh,
+                                          int lane) {
+  load_tile_raw<D, BS>(t, a, bh, lane);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// waves per decode / multi-query workgroup
+constexpr int kNW = kDecodeWaves;
+
+}  // namespace
+}  // namespace kvq

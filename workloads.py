@@ -162,6 +162,16 @@ def queries(w: Workload, seed: int = 0, device="cpu", step: int = 0,
     return q.to(w.torch_dtype)
 
 
+def query_rows(w: Workload, num_rows: int, seed: int = 0, device="cpu", step: int = 0,
+               layer: int = 0):
+    """Multi-query rows [num_rows][Hq][d] in the source dtype (a draw of its
+    own, independent of the decode queries)."""
+    g = _gen(device, seed, ROLE_Q, layer, 50000 + step)
+    q = torch.randn((num_rows, w.num_q_heads, w.head_dim), generator=g,
+                    device=device, dtype=torch.float32)
+    return q.to(w.torch_dtype)
+
+
 def pool_order(num_blocks: int, seed: int = 0, permuted: bool = True) -> np.ndarray:
     """Initial free-stack order: a seeded permutation (a fragmented pool) or
     the identity."""
