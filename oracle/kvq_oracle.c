@@ -964,6 +964,161 @@ int orc_blocks_reserve(int32_t* stack, int32_t* top, int64_t capacity,
   return ORC_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Prefix sharing [P3, "How vLLM Implements KV Cache Optimization": requests */
+/* sharing a system prompt keep one copy of its cached prefix; P2 glossary, */
+/* "Evolution & History" and "Enterprise Use Cases": common prompt prefixes */
+/* reused across requests]. refcount[id] counts the table entries that hold  */
+/* block id (0 for a free block). A forked sequence shares its source's       */
+/* blocks; a shared block that is only partly filled is copied before a     */
+/* sequence appends into it (copy on write); a block returns to the free     */
+/* stack when its last reference goes.                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Fork k (in order): row dst[k] takes row src[k]'s length and its first
+ * ceil(len / bs) table entries, each block's count growing by one.
+ * Preconditions: destination rows are empty, distinct and not sources. */
+int orc_blocks_fork(int32_t* refcount, int32_t* tables, int32_t max_blocks,
+                    int32_t* lens, const int32_t* src, const int32_t* dst,
+                    int32_t num_forks, int32_t bs) {
+  for (int k = 0; k < num_forks; ++k) {
+    int64_t nb = ceil_div(lens[src[k]], bs);
+    for (int64_t i = 0; i < nb; ++i) {
+      int32_t id = tables[(int64_t)src[k] * max_blocks + i];
+      tables[(int64_t)dst[k] * max_blocks + i] = id;
+      refcount[id] += 1;
+    }
+    lens[dst[k]] = lens[src[k]];
+  }
+  return ORC_OK;
+}
+
+/* Reservation with counts. Sequence b copies its last block first when it
+ * appends (n > 0) into a partly filled block (L % bs != 0) whose count, at
+ * the start of the call, exceeds one: need_b = (1 if it copies) +
+ * ceil((L+n)/bs) - ceil(L/bs). Needs are served as in orc_blocks_reserve
+ * (all or nothing, batch order, increasing stack position); a copying
+ * sequence's first block replaces its last table entry and the pair (old,
+ * new) is reported (in batch order) for the caller to copy the block's
+ * contents. Every block taken gets count 1. After the allocation the copied
+ * blocks lose one reference each, in batch order, and a block whose count
+ * reaches zero is pushed back onto the stack. */
+int orc_blocks_reserve_shared(int32_t* stack, int32_t* top, int64_t capacity,
+                              int32_t* refcount, int32_t* tables, int32_t max_blocks,
+                              const int32_t* lens, const int32_t* new_tokens,
+                              int32_t batch, int32_t bs, int64_t* slots,
+                              int32_t* lens_out, int32_t* cow_src, int32_t* cow_dst,
+                              int32_t* cow_count, int32_t* status) {
+  (void)capacity;
+  int64_t total = 0;
+  int fits = 1;
+  int* cow = (int*)malloc(sizeof(int) * (size_t)(batch > 0 ? batch : 1));
+  for (int b = 0; b < batch; ++b) {
+    int64_t have = ceil_div(lens[b], bs);
+    int64_t want = ceil_div((int64_t)lens[b] + new_tokens[b], bs);
+    if (want > max_blocks) fits = 0;
+    cow[b] = new_tokens[b] > 0 && lens[b] % bs != 0 &&
+             refcount[tables[(int64_t)b * max_blocks + lens[b] / bs]] > 1;
+    total += want - have + cow[b];
+  }
+  if (!fits || total > *top) {
+    free(cow);
+    *status = ORC_ERR_OUT_OF_BLOCKS;
+    return ORC_OK;
+  }
+  int64_t off = 0, tok = 0;
+  int ncow = 0;
+  for (int b = 0; b < batch; ++b) {
+    int64_t have = ceil_div(lens[b], bs);
+    int64_t grow = ceil_div((int64_t)lens[b] + new_tokens[b], bs) - have;
+    int64_t need = grow + cow[b];
+    int32_t* row = tables + (int64_t)b * max_blocks;
+    int64_t first = *top - off - need; /* the sequence's lowest stack position */
+    if (cow[b]) {
+      int32_t fresh = stack[first];
+      cow_src[ncow] = row[lens[b] / bs];
+      cow_dst[ncow] = fresh;
+      ++ncow;
+      row[lens[b] / bs] = fresh;
+      refcount[fresh] = 1;
+    }
+    for (int64_t k = 0; k < grow; ++k) {
+      row[have + k] = stack[first + cow[b] + k];
+      refcount[row[have + k]] = 1;
+    }
+    off += need;
+    for (int64_t k = 0; k < new_tokens[b]; ++k) {
+      int64_t pos = lens[b] + k;
+      slots[tok++] = (int64_t)row[pos / bs] * bs + pos % bs;
+    }
+  }
+  *top -= (int32_t)total;
+  for (int c = 0; c < ncow; ++c) {
+    refcount[cow_src[c]] -= 1;
+    if (refcount[cow_src[c]] == 0) stack[(*top)++] = cow_src[c];
+  }
+  *cow_count = ncow;
+  if (lens_out)
+    for (int b = 0; b < batch; ++b) lens_out[b] = lens[b] + new_tokens[b];
+  free(cow);
+  *status = ORC_OK;
+  return ORC_OK;
+}
+
+/* Release with counts: the masked rows' blocks lose one reference each, in
+ * batch order and, within a row, in logical order; a block whose count
+ * reaches zero is pushed onto the stack at that moment. */
+int orc_blocks_release_shared(int32_t* stack, int32_t* top, int64_t capacity,
+                              int32_t* refcount, const int32_t* tables,
+                              int32_t max_blocks, const int32_t* lens,
+                              const int32_t* mask, int32_t batch, int32_t bs,
+                              int32_t* lens_out, int32_t* status) {
+  (void)capacity;
+  for (int b = 0; b < batch; ++b) {
+    if (!mask[b]) continue;
+    int64_t nb = ceil_div(lens[b], bs);
+    for (int64_t i = 0; i < nb; ++i) {
+      int32_t id = tables[(int64_t)b * max_blocks + i];
+      refcount[id] -= 1;
+      if (refcount[id] == 0) stack[(*top)++] = id;
+    }
+  }
+  if (lens_out)
+    for (int b = 0; b < batch; ++b)
+      if (mask[b]) lens_out[b] = 0;
+  *status = ORC_OK;
+  return ORC_OK;
+}
+
+/* Copy every plane of block src[k] to block dst[k] (one layer): codes,
+ * scales and zero points; per-channel key scales per block. */
+int orc_copy_blocks(const orc_layout* L, const orc_cache* C, const int32_t* src,
+                    const int32_t* dst, int32_t n) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  int64_t H = L->num_kv_heads, bs = L->block_size, d = L->head_dim;
+  for (int k = 0; k < n; ++k) {
+    for (int side = 0; side < 2; ++side) {
+      int64_t rb = row_bytes(L, side);
+      uint8_t* codes = (uint8_t*)(side ? C->v_codes : C->k_codes);
+      memcpy(codes + (int64_t)dst[k] * H * bs * rb, codes + (int64_t)src[k] * H * bs * rb,
+             (size_t)(H * bs * rb));
+      int code = side_code(L, side), mode = side_mode(L, side);
+      if (code == ORC_CODE_NONE16) continue;
+      float* scale = side ? C->v_scale : C->k_scale;
+      int64_t per = mode == ORC_CHANNEL_BLOCK ? H * d
+                    : mode == ORC_GROUP_ASYM ? H * bs * (d / L->group_size)
+                                             : H * bs;
+      memcpy(scale + dst[k] * per, scale + src[k] * per, sizeof(float) * (size_t)per);
+      if (mode == ORC_GROUP_ASYM) {
+        uint8_t* zero = side ? C->v_zero : C->k_zero;
+        memcpy(zero + dst[k] * per, zero + src[k] * per, (size_t)per);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
 /* Released sequences push their blocks back in batch order, each in logical
  * order. All or nothing when the pushes would overflow the stack. */
 int orc_blocks_release(int32_t* stack, int32_t* top, int64_t capacity,

@@ -93,6 +93,22 @@ int orc_prefill(const orc_layout* L, const orc_cache* C, const void* q, int32_t 
                 const int32_t* block_tables, int32_t max_blocks_per_seq,
                 const int32_t* context_lens, double sm_scale, double* out,
                 int32_t num_threads);
+int orc_blocks_fork(int32_t* refcount, int32_t* tables, int32_t max_blocks,
+                    int32_t* lens, const int32_t* src, const int32_t* dst,
+                    int32_t num_forks, int32_t bs);
+int orc_blocks_reserve_shared(int32_t* stack, int32_t* top, int64_t capacity,
+                              int32_t* refcount, int32_t* tables, int32_t max_blocks,
+                              const int32_t* lens, const int32_t* new_tokens,
+                              int32_t batch, int32_t bs, int64_t* slots,
+                              int32_t* lens_out, int32_t* cow_src, int32_t* cow_dst,
+                              int32_t* cow_count, int32_t* status);
+int orc_blocks_release_shared(int32_t* stack, int32_t* top, int64_t capacity,
+                              int32_t* refcount, const int32_t* tables,
+                              int32_t max_blocks, const int32_t* lens,
+                              const int32_t* mask, int32_t batch, int32_t bs,
+                              int32_t* lens_out, int32_t* status);
+int orc_copy_blocks(const orc_layout* L, const orc_cache* C, const int32_t* src,
+                    const int32_t* dst, int32_t n);
 int orc_dequant_token(const orc_layout* L, const orc_cache* C, int side,
                       const int32_t* table_row, int32_t context_len,
                       int32_t stage_row, int32_t pos, int32_t head, float* out);

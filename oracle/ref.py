@@ -69,6 +69,12 @@ def _load():
         "orc_decode_range": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32,
                                         i32, i32, f64, vp, vp, vp]),
         "orc_pool_init": (C.c_int, [vp, vp, vp, i64]),
+        "orc_blocks_fork": (C.c_int, [vp, vp, i32, vp, vp, vp, i32, i32]),
+        "orc_blocks_reserve_shared": (C.c_int, [vp, vp, i64, vp, vp, i32, vp, vp, i32, i32,
+                                                vp, vp, vp, vp, vp, vp]),
+        "orc_blocks_release_shared": (C.c_int, [vp, vp, i64, vp, vp, i32, vp, vp, i32, i32,
+                                                vp, vp]),
+        "orc_copy_blocks": (C.c_int, [vp, vp, vp, vp, i32]),
         "orc_blocks_reserve": (C.c_int, [vp, vp, i64, vp, i32, vp, vp, i32, i32,
                                           vp, vp, vp]),
         "orc_blocks_release": (C.c_int, [vp, vp, i64, vp, i32, vp, vp, i32, i32,
@@ -354,3 +360,54 @@ def blocks_release(stack, top, tables, lens, mask, bs, lens_out=None):
                                 bs, _ptr(lens_out), _ptr(status))
     assert rc == 0
     return int(status[0])
+
+
+# ---- prefix sharing (block reference counts) ---------------------------------
+
+def blocks_fork(refcount, tables, lens, src, dst, bs):
+    """Mutates refcount, tables and lens (int32 numpy, in place)."""
+    src = np.ascontiguousarray(src, np.int32)
+    dst = np.ascontiguousarray(dst, np.int32)
+    assert lens.dtype == np.int32 and lens.flags.c_contiguous
+    rc = lib.orc_blocks_fork(_ptr(refcount), _ptr(tables), tables.shape[1], _ptr(lens),
+                             _ptr(src), _ptr(dst), src.size, bs)
+    assert rc == 0
+
+
+def blocks_reserve_shared(stack, top, refcount, tables, lens, new_tokens, bs, lens_out=None):
+    """Mutates stack, top, refcount, tables in place; returns (slots, status,
+    cow_src, cow_dst) with the copy-on-write pairs in batch order."""
+    lens = np.ascontiguousarray(lens, np.int32)
+    new_tokens = np.ascontiguousarray(new_tokens, np.int32)
+    slots = np.full(int(new_tokens.sum()), -7, np.int64)
+    status = np.zeros(1, np.int32)
+    cs = np.full(max(lens.size, 1), -7, np.int32)
+    cd = np.full(max(lens.size, 1), -7, np.int32)
+    cnt = np.zeros(1, np.int32)
+    rc = lib.orc_blocks_reserve_shared(_ptr(stack), _ptr(top), stack.size, _ptr(refcount),
+                                       _ptr(tables), tables.shape[1], _ptr(lens),
+                                       _ptr(new_tokens), lens.size, bs, _ptr(slots),
+                                       _ptr(lens_out), _ptr(cs), _ptr(cd), _ptr(cnt),
+                                       _ptr(status))
+    assert rc == 0
+    n = int(cnt[0]) if status[0] == 0 else 0
+    return slots, int(status[0]), cs[:n].copy(), cd[:n].copy()
+
+
+def blocks_release_shared(stack, top, refcount, tables, lens, mask, bs, lens_out=None):
+    lens = np.ascontiguousarray(lens, np.int32)
+    mask = np.ascontiguousarray(mask, np.int32)
+    status = np.zeros(1, np.int32)
+    rc = lib.orc_blocks_release_shared(_ptr(stack), _ptr(top), stack.size, _ptr(refcount),
+                                       _ptr(tables), tables.shape[1], _ptr(lens), _ptr(mask),
+                                       lens.size, bs, _ptr(lens_out), _ptr(status))
+    assert rc == 0
+    return int(status[0])
+
+
+def copy_blocks(L, cache, src, dst):
+    src = np.ascontiguousarray(src, np.int32)
+    dst = np.ascontiguousarray(dst, np.int32)
+    cs = cache.struct()
+    rc = lib.orc_copy_blocks(C.byref(L), C.byref(cs), _ptr(src), _ptr(dst), src.size)
+    assert rc == 0
