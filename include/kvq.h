@@ -38,6 +38,10 @@
  *                         physical blocks ("KV Cache Optimization: Strategies
  *                         ...", section "How vLLM Implements KV Cache
  *                         Optimization").
+ *   kvq_blocks_fork / kvq_blocks_reserve_shared / kvq_blocks_release_shared /
+ *   kvq_copy_blocks       prefix sharing: reference-counted blocks, copy on
+ *                         write of a shared, partly filled block (same
+ *                         section, prefix caching).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -394,6 +398,71 @@ kvq_status kvq_blocks_release(int32_t* free_stack, int32_t* free_top,
                               const int32_t* release_mask, int32_t batch,
                               int32_t block_size, int32_t* context_lens_out,
                               int32_t* status_flag, void* stream);
+
+/* ---- prefix sharing ("KV Cache Optimization: Strategies ...", section "How
+ * vLLM Implements KV Cache Optimization": requests that share a system prompt
+ * keep one cached copy of its prefix; "KV Cache Optimization" glossary,
+ * "Evolution & History" and "Enterprise Use Cases": common prompt prefixes
+ * reused across requests). A pool used with these calls also keeps
+ * refcount, a device int32 [pool_capacity]: the number of table entries
+ * holding each block, 0 for a free block (all zero after kvq_pool_init; the
+ * caller zero-fills it). Use the _shared reserve and release with such a
+ * pool; the plain ones do not keep the counts. */
+
+/* Fork k (k < num_forks): row dst_rows[k] takes row src_rows[k]'s length and
+ * its first ceil(len / bs) table entries, each block gaining one reference.
+ * Destination rows must be empty (length 0), distinct, and not sources of
+ * the same call. With CHANNEL_BLOCK_SYM keys the destination's k_stage row
+ * must also be given the source's (a plain device copy), since a partly
+ * filled last block lives there. All pointers are device memory. */
+kvq_status kvq_blocks_fork(int32_t* refcount, int64_t pool_capacity,
+                           int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t* context_lens, int32_t batch,
+                           const int32_t* src_rows, const int32_t* dst_rows,
+                           int32_t num_forks, int32_t block_size, void* stream);
+
+/* kvq_blocks_reserve for a pool with counts, with copy on write: a sequence
+ * that appends (n_b > 0) into a partly filled last block (L_b % bs != 0)
+ * held by more than one table (count > 1 at the start of the call) first
+ * takes one extra block, the lowest of its stack positions, which replaces
+ * that table entry; the pair (old, new) goes to cow_src[c], cow_dst[c]
+ * (c in batch order, *cow_count pairs; arrays of at least batch entries) and
+ * the caller must copy each pair's contents in every layer
+ * (kvq_copy_blocks) before appending. need_b counts the extra block; taken
+ * blocks get count 1; after the allocation each copied block loses one
+ * reference and one left at zero is pushed onto the stack (in the order of
+ * its last copy). Otherwise as kvq_blocks_reserve, all or nothing. */
+kvq_status kvq_blocks_reserve_shared(int32_t* free_stack, int32_t* free_top,
+                                     int64_t pool_capacity, int32_t* refcount,
+                                     int32_t* block_tables,
+                                     int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens,
+                                     const int32_t* new_tokens, int32_t batch,
+                                     int32_t block_size, int64_t* slot_mapping_out,
+                                     int32_t* context_lens_out, int32_t* cow_src,
+                                     int32_t* cow_dst, int32_t* cow_count,
+                                     int32_t* status_flag, void* stream);
+
+/* kvq_blocks_release for a pool with counts: every table entry of a masked
+ * row drops one reference (rows in batch order, entries in logical order)
+ * and a block left at zero is pushed onto the stack in the order of its
+ * last entry. */
+kvq_status kvq_blocks_release_shared(int32_t* free_stack, int32_t* free_top,
+                                     int64_t pool_capacity, int32_t* refcount,
+                                     const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens,
+                                     const int32_t* release_mask, int32_t batch,
+                                     int32_t block_size, int32_t* context_lens_out,
+                                     int32_t* status_flag, void* stream);
+
+/* Copy every plane of block src_ids[k] onto block dst_ids[k] in one layer's
+ * cache (codes, scales, zero points; not k_stage), for k < *count (device
+ * int32, at most max_pairs): the copy-on-write pairs of
+ * kvq_blocks_reserve_shared. Ids outside [0, num_blocks) are skipped. */
+kvq_status kvq_copy_blocks(const kvq_layout* layout, const kvq_cache* cache,
+                           const int32_t* src_ids, const int32_t* dst_ids,
+                           const int32_t* count, int32_t max_pairs, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -11,6 +11,7 @@
 
 #include "kvq.h"
 #include "kvq_internal.h"
+#include "kvq_sharing.h"
 
 namespace {
 
@@ -502,6 +503,82 @@ kvq_status kvq_blocks_release(int32_t* free_stack, int32_t* free_top, int64_t po
       free_stack, free_top, pool_capacity, block_tables, max_blocks_per_seq, context_lens,
       release_mask, batch, block_size, context_lens_out, status_flag,
       static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_blocks_fork(int32_t* refcount, int64_t pool_capacity, int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t* context_lens, int32_t batch,
+                           const int32_t* src_rows, const int32_t* dst_rows, int32_t num_forks,
+                           int32_t block_size, void* stream) {
+  if (!refcount || pool_capacity < 1 || pool_capacity > INT32_MAX || batch < 0 ||
+      max_blocks_per_seq < 1 || block_size < 1 || num_forks < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_forks == 0) return KVQ_OK;
+  if (!block_tables || !context_lens || !src_rows || !dst_rows) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_blocks_fork(refcount, pool_capacity, block_tables,
+                                            max_blocks_per_seq, context_lens, batch, src_rows,
+                                            dst_rows, num_forks, block_size,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_blocks_reserve_shared(int32_t* free_stack, int32_t* free_top,
+                                     int64_t pool_capacity, int32_t* refcount,
+                                     int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, const int32_t* new_tokens,
+                                     int32_t batch, int32_t block_size,
+                                     int64_t* slot_mapping_out, int32_t* context_lens_out,
+                                     int32_t* cow_src, int32_t* cow_dst, int32_t* cow_count,
+                                     int32_t* status_flag, void* stream) {
+  if (!free_stack || !free_top || !status_flag || !refcount || !cow_count ||
+      pool_capacity < 1 || pool_capacity > INT32_MAX)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1) return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (!block_tables || !context_lens || !new_tokens || !slot_mapping_out ||
+                    !cow_src || !cow_dst))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_blocks_reserve_shared(
+      free_stack, free_top, pool_capacity, refcount, block_tables, max_blocks_per_seq,
+      context_lens, new_tokens, batch, block_size, slot_mapping_out, context_lens_out, cow_src,
+      cow_dst, cow_count, status_flag, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_blocks_release_shared(int32_t* free_stack, int32_t* free_top,
+                                     int64_t pool_capacity, int32_t* refcount,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, const int32_t* release_mask,
+                                     int32_t batch, int32_t block_size,
+                                     int32_t* context_lens_out, int32_t* status_flag,
+                                     void* stream) {
+  if (!free_stack || !free_top || !status_flag || !refcount || pool_capacity < 1 ||
+      pool_capacity > INT32_MAX)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1) return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (!block_tables || !context_lens || !release_mask)) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_blocks_release_shared(
+      free_stack, free_top, pool_capacity, refcount, block_tables, max_blocks_per_seq,
+      context_lens, release_mask, batch, block_size, context_lens_out, status_flag,
+      static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_copy_blocks(const kvq_layout* L, const kvq_cache* C, const int32_t* src_ids,
+                           const int32_t* dst_ids, const int32_t* count, int32_t max_pairs,
+                           void* stream) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  s = check_cache(L, C);
+  if (s != KVQ_OK) return s;
+  if (max_pairs < 0 || max_pairs > 65535 * 1024) return KVQ_ERR_INVALID_ARGUMENT;
+  if (max_pairs == 0) return KVQ_OK;
+  if (!src_ids || !dst_ids || !count) return KVQ_ERR_INVALID_ARGUMENT;
+  int64_t planes[7];
+  s = kvq_cache_plane_bytes(L, C->num_blocks, C->max_seqs, planes);
+  if (s != KVQ_OK) return s;
+  uint8_t* const base[6] = {static_cast<uint8_t*>(C->k_codes), static_cast<uint8_t*>(C->v_codes),
+                            reinterpret_cast<uint8_t*>(C->k_scale),
+                            reinterpret_cast<uint8_t*>(C->v_scale), C->k_zero, C->v_zero};
+  int64_t per_block[6];
+  for (int i = 0; i < 6; ++i) per_block[i] = planes[i] / C->num_blocks;
+  return hip_status(kvq::launch_copy_blocks(base, per_block, src_ids, dst_ids, count, max_pairs,
+                                            C->num_blocks, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

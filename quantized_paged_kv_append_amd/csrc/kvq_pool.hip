@@ -11,6 +11,7 @@
 // a pure function of the inputs. Latency-bound (a few microseconds per step).
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_sharing.h"
 
 namespace kvq {
 namespace {
@@ -152,6 +153,270 @@ __global__ __launch_bounds__(kThreads) void release_kernel(
   }
 }
 
+// ---- prefix sharing --------------------------------------------------------
+// refcount[id] counts the table entries holding block id; a free block has 0.
+// Fork: one workgroup per fork copies the source row's entries to the
+// destination row and counts them (device-scope atomics, so forks sharing a
+// source may run at once).
+__global__ __launch_bounds__(256) void fork_kernel(int32_t* refcount, int64_t capacity,
+                                                   int32_t* tables, int32_t max_blocks,
+                                                   int32_t* lens, int32_t batch,
+                                                   const int32_t* src, const int32_t* dst,
+                                                   int32_t bs) {
+  const int k = blockIdx.x;
+  const int s = src[k], d = dst[k];
+  if (s < 0 || s >= batch || d < 0 || d >= batch || s == d) return;
+  const int32_t L = lens[s];
+  const int64_t nb = min(ceil_div(max(L, 0), bs), (int64_t)max_blocks);
+  for (int64_t i = threadIdx.x; i < nb; i += blockDim.x) {
+    const int32_t id = tables[(int64_t)s * max_blocks + i];
+    tables[(int64_t)d * max_blocks + i] = id;
+    if (id >= 0 && id < capacity) atomicAdd(&refcount[id], 1);
+  }
+  if (threadIdx.x == 0) lens[d] = L;
+}
+
+// A count after other waves' atomics on it: an L2-coherent load (a plain load
+// could hit a line this CU cached before the atomics).
+__device__ __forceinline__ int32_t count_now(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Copy on write of a shared, partly filled last block: whether sequence b
+// copies, read from the counts at the start of the call.
+__device__ __forceinline__ int cow_needed(const int32_t* refcount, int64_t capacity,
+                                          const int32_t* tables, int32_t max_blocks,
+                                          int b, int32_t L, int32_t n, int32_t bs) {
+  if (n <= 0 || L % bs == 0 || L / bs >= max_blocks) return 0;
+  const int32_t id = tables[(int64_t)b * max_blocks + L / bs];
+  return id >= 0 && id < capacity && refcount[id] > 1;
+}
+
+// Reservation with counts (one workgroup): the plain reservation's scans plus
+// one extra block per copying sequence, taken first; new blocks get count 1;
+// then the copied blocks lose a reference each and those that reach zero are
+// pushed in the order of their last copy. The last-copy test uses the count
+// itself as scratch: after the decrements, every copy c of a block left at
+// zero lowers its count to -(c + 1) with atomicMin, so the copy that finds
+// -(c + 1) there is the last one; the counts are then reset to zero.
+__global__ __launch_bounds__(kThreads) void reserve_shared_kernel(
+    int32_t* stack, int32_t* top, int64_t capacity, int32_t* refcount, int32_t* tables,
+    int32_t max_blocks, const int32_t* lens, const int32_t* new_tokens, int32_t batch,
+    int32_t bs, int64_t* slots, int32_t* lens_out, int32_t* cow_src, int32_t* cow_dst,
+    int32_t* cow_count, int32_t* status) {
+  __shared__ int64_t sh[kThreads];
+  __shared__ int ok_sh;
+  const int tid = threadIdx.x;
+  const int64_t top0 = min(max((int64_t)*top, (int64_t)0), capacity);
+  if (tid == 0) ok_sh = 1;
+  __syncthreads();
+  int64_t total_need = 0;
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    int64_t need = 0;
+    if (b < batch) {
+      const int64_t have = ceil_div(lens[b], bs);
+      const int64_t want = ceil_div((int64_t)lens[b] + new_tokens[b], bs);
+      if (want > max_blocks) ok_sh = 0;
+      need = want - have +
+             cow_needed(refcount, capacity, tables, max_blocks, b, lens[b], new_tokens[b], bs);
+    }
+    int64_t chunk_total;
+    block_exclusive_scan(need, &chunk_total, sh);
+    total_need += chunk_total;
+  }
+  __syncthreads();
+  if (!ok_sh || total_need > top0) {
+    if (tid == 0) *status = KVQ_ERR_OUT_OF_BLOCKS;
+    return;
+  }
+  // the copy decisions are taken before any count changes (pass 2 only sets
+  // the counts of blocks taken from the stack, which no table holds)
+  int64_t boff = 0, toff = 0, coff = 0;
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    int64_t have = 0, grow = 0, n = 0, L = 0;
+    int cow = 0;
+    if (b < batch) {
+      L = lens[b];
+      n = new_tokens[b];
+      have = ceil_div(L, bs);
+      grow = ceil_div(L + n, bs) - have;
+      cow = cow_needed(refcount, capacity, tables, max_blocks, b, (int32_t)L, (int32_t)n, bs);
+    }
+    const int64_t need = grow + cow;
+    int64_t ctot, ttot, wtot;
+    const int64_t bpre = block_exclusive_scan(need, &ctot, sh) + boff;
+    const int64_t tpre = block_exclusive_scan(n, &ttot, sh) + toff;
+    const int64_t cpre = block_exclusive_scan(cow, &wtot, sh) + coff;
+    __syncthreads();   // every copy decision of this chunk is read before counts change
+    if (b < batch) {
+      int32_t* row = tables + (int64_t)b * max_blocks;
+      const int64_t first = top0 - bpre - need;
+      if (cow) {
+        const int32_t fresh = stack[first];
+        cow_src[cpre] = row[L / bs];
+        cow_dst[cpre] = fresh;
+        row[L / bs] = fresh;
+        if (fresh >= 0 && fresh < capacity) refcount[fresh] = 1;
+      }
+      for (int64_t k = 0; k < grow; ++k) {
+        const int32_t id = stack[first + cow + k];
+        row[have + k] = id;
+        if (id >= 0 && id < capacity) refcount[id] = 1;
+      }
+      for (int64_t k = 0; k < n; ++k) {
+        const int64_t pos = L + k;
+        slots[tpre + k] = (int64_t)row[pos / bs] * bs + pos % bs;
+      }
+      if (lens_out) lens_out[b] = (int32_t)(L + n);
+    }
+    boff += ctot;
+    toff += ttot;
+    coff += wtot;
+    __syncthreads();
+  }
+  const int64_t ncow = coff;
+  const int64_t top1 = top0 - total_need;
+  // copied blocks lose a reference
+  for (int64_t c = tid; c < ncow; c += kThreads) {
+    const int32_t id = cow_src[c];
+    if (id >= 0 && id < capacity) atomicSub(&refcount[id], 1);
+  }
+  __syncthreads();
+  for (int64_t c = tid; c < ncow; c += kThreads) {
+    const int32_t id = cow_src[c];
+    if (id >= 0 && id < capacity && count_now(&refcount[id]) <= 0)
+      atomicMin(&refcount[id], (int32_t)(-(c + 1)));
+  }
+  __syncthreads();
+  int64_t poff = 0;
+  for (int64_t base = 0; base < ncow; base += kThreads) {
+    const int64_t c = base + tid;
+    const int32_t id = c < ncow ? cow_src[c] : -1;
+    const int last = id >= 0 && id < capacity && count_now(&refcount[id]) == (int32_t)(-(c + 1));
+    int64_t ptot;
+    const int64_t pre = block_exclusive_scan(last, &ptot, sh) + poff;
+    if (last && top1 + pre < capacity) stack[top1 + pre] = id;
+    poff += ptot;
+    __syncthreads();   // every test of this chunk is done before any reset
+    if (last) refcount[id] = 0;
+  }
+  if (tid == 0) {
+    *top = (int32_t)min(top1 + poff, capacity);
+    *cow_count = (int32_t)ncow;
+    *status = KVQ_OK;
+  }
+}
+
+// Release with counts (one workgroup): the masked rows' table entries, in
+// (row, logical block) order, are enumerated chunk by chunk (a scan of the
+// rows' block counts, then a binary search per entry); every entry drops a
+// reference; a block left at zero is pushed in the order of its last entry
+// (the same atomicMin marking as in reserve_shared_kernel).
+__device__ __forceinline__ int find_row(const int64_t* incl, int n, int64_t e) {
+  int lo = 0, hi = n - 1;   // first row whose inclusive prefix exceeds e
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (incl[mid] > e) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+template <int PHASE>
+__device__ void release_entries(int32_t* stack, int64_t top0, int64_t capacity,
+                                int32_t* refcount, const int32_t* tables, int32_t max_blocks,
+                                const int32_t* lens, const int32_t* mask, int32_t batch,
+                                int32_t bs, int64_t* sh, int64_t* sh2, int64_t* pushed) {
+  const int tid = threadIdx.x;
+  int64_t ebase = 0;
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    const int64_t nb = (b < batch && mask[b]) ? min(ceil_div(max(lens[b], 0), bs), (int64_t)max_blocks) : 0;
+    int64_t total;
+    const int64_t pre = block_exclusive_scan(nb, &total, sh2);
+    sh[tid] = pre + nb;   // inclusive prefix of this chunk's rows
+    __syncthreads();
+    const int rows = min(kThreads, batch - base);
+    for (int64_t e0 = 0; e0 < total; e0 += kThreads) {
+      const int64_t e = e0 + tid;
+      int32_t id = -1;
+      if (e < total) {
+        const int r = find_row(sh, rows, e);
+        const int64_t i = e - (r ? sh[r - 1] : 0);
+        id = tables[(int64_t)(base + r) * max_blocks + i];
+        if (id < 0 || id >= capacity) id = -1;
+      }
+      const int64_t E = ebase + e;   // entry index over the whole call
+      if (PHASE == 0) {
+        if (id >= 0) atomicSub(&refcount[id], 1);
+      } else if (PHASE == 1) {
+        if (id >= 0 && count_now(&refcount[id]) <= 0) atomicMin(&refcount[id], (int32_t)(-(E + 1)));
+      } else {
+        const int last = id >= 0 && count_now(&refcount[id]) == (int32_t)(-(E + 1));
+        int64_t ptot;
+        const int64_t p = block_exclusive_scan(last, &ptot, sh2) + *pushed;
+        if (last && top0 + p < capacity) stack[top0 + p] = id;
+        __syncthreads();   // every test of this batch of entries is done
+        if (last) refcount[id] = 0;
+        *pushed += ptot;
+      }
+    }
+    ebase += total;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void release_shared_kernel(
+    int32_t* stack, int32_t* top, int64_t capacity, int32_t* refcount, const int32_t* tables,
+    int32_t max_blocks, const int32_t* lens, const int32_t* mask, int32_t batch, int32_t bs,
+    int32_t* lens_out, int32_t* status) {
+  __shared__ int64_t sh[kThreads];
+  __shared__ int64_t sh2[kThreads];
+  const int tid = threadIdx.x;
+  const int64_t top0 = min(max((int64_t)*top, (int64_t)0), capacity);
+  int64_t pushed = 0;
+  release_entries<0>(stack, top0, capacity, refcount, tables, max_blocks, lens, mask, batch, bs,
+                     sh, sh2, &pushed);
+  __syncthreads();
+  release_entries<1>(stack, top0, capacity, refcount, tables, max_blocks, lens, mask, batch, bs,
+                     sh, sh2, &pushed);
+  __syncthreads();
+  release_entries<2>(stack, top0, capacity, refcount, tables, max_blocks, lens, mask, batch, bs,
+                     sh, sh2, &pushed);
+  __syncthreads();
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    if (lens_out && b < batch && mask[b]) lens_out[b] = 0;
+  }
+  if (tid == 0) {
+    *top = (int32_t)min(top0 + pushed, capacity);
+    *status = top0 + pushed <= capacity ? KVQ_OK : KVQ_ERR_OUT_OF_BLOCKS;
+  }
+}
+
+// Copy of one layer's planes for each (src, dst) block pair: workgroup
+// (pair, plane), 16-byte vectors; pairs past *count are skipped.
+struct CopyPlanes {
+  uint8_t* base[6];
+  int64_t per_block[6];   // bytes of each plane per block (0: plane unused)
+};
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyPlanes cp, const int32_t* src,
+                                                          const int32_t* dst,
+                                                          const int32_t* count,
+                                                          int64_t num_blocks) {
+  const int k = blockIdx.x, plane = blockIdx.y;
+  if (k >= *count || cp.per_block[plane] == 0) return;
+  const int32_t s = src[k], d = dst[k];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  const int64_t per = cp.per_block[plane];
+  const u32x4* from = reinterpret_cast<const u32x4*>(cp.base[plane] + s * per);
+  u32x4* to = reinterpret_cast<u32x4*>(cp.base[plane] + d * per);
+  for (int64_t i = threadIdx.x; i < per / 16; i += blockDim.x) to[i] = from[i];
+}
+
 }  // namespace
 
 hipError_t launch_pool_init(int32_t* stack, int32_t* top, const int32_t* order,
@@ -183,6 +448,53 @@ hipError_t launch_blocks_release(int32_t* stack, int32_t* top,
                                  hipStream_t stream) {
   release_kernel<<<1, kThreads, 0, stream>>>(stack, top, capacity, tables, max_blocks,
                                              lens, mask, batch, bs, lens_out, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_blocks_fork(int32_t* refcount, int64_t capacity, int32_t* tables,
+                              int32_t max_blocks, int32_t* lens, int32_t batch,
+                              const int32_t* src, const int32_t* dst, int32_t num_forks,
+                              int32_t bs, hipStream_t stream) {
+  fork_kernel<<<num_forks, 256, 0, stream>>>(refcount, capacity, tables, max_blocks, lens,
+                                             batch, src, dst, bs);
+  return hipGetLastError();
+}
+
+hipError_t launch_blocks_reserve_shared(int32_t* stack, int32_t* top, int64_t capacity,
+                                        int32_t* refcount, int32_t* tables, int32_t max_blocks,
+                                        const int32_t* lens, const int32_t* new_tokens,
+                                        int32_t batch, int32_t bs, int64_t* slots,
+                                        int32_t* lens_out, int32_t* cow_src, int32_t* cow_dst,
+                                        int32_t* cow_count, int32_t* status,
+                                        hipStream_t stream) {
+  reserve_shared_kernel<<<1, kThreads, 0, stream>>>(stack, top, capacity, refcount, tables,
+                                                    max_blocks, lens, new_tokens, batch, bs,
+                                                    slots, lens_out, cow_src, cow_dst,
+                                                    cow_count, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_blocks_release_shared(int32_t* stack, int32_t* top, int64_t capacity,
+                                        int32_t* refcount, const int32_t* tables,
+                                        int32_t max_blocks, const int32_t* lens,
+                                        const int32_t* mask, int32_t batch, int32_t bs,
+                                        int32_t* lens_out, int32_t* status,
+                                        hipStream_t stream) {
+  release_shared_kernel<<<1, kThreads, 0, stream>>>(stack, top, capacity, refcount, tables,
+                                                    max_blocks, lens, mask, batch, bs, lens_out,
+                                                    status);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(uint8_t* const base[6], const int64_t per_block[6],
+                              const int32_t* src, const int32_t* dst, const int32_t* count,
+                              int32_t max_pairs, int64_t num_blocks, hipStream_t stream) {
+  CopyPlanes cp;
+  for (int i = 0; i < 6; ++i) {
+    cp.base[i] = base[i];
+    cp.per_block[i] = base[i] ? per_block[i] : 0;
+  }
+  copy_blocks_kernel<<<dim3(max_pairs, 6), 256, 0, stream>>>(cp, src, dst, count, num_blocks);
   return hipGetLastError();
 }
 

@@ -71,6 +71,12 @@ _SIGS = {
     "kvq_prefill_attention": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
                                      _vp, _i32, _f32, _i32, _vp, _i32, _vp, _i64, _vp]),
     "kvq_pool_init": (_i32, [_vp, _vp, _vp, _i64, _vp]),
+    "kvq_blocks_fork": (_i32, [_vp, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _vp]),
+    "kvq_blocks_reserve_shared": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "kvq_blocks_release_shared": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                         _vp, _vp, _vp]),
+    "kvq_copy_blocks": (_i32, [_LP, _CP, _vp, _vp, _vp, _i32, _vp]),
     "kvq_blocks_reserve": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32,
                                   _vp, _vp, _vp, _vp]),
     "kvq_blocks_release": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32,
@@ -252,3 +258,40 @@ def kvq_blocks_release(free_stack, free_top, block_tables, context_lens, release
         block_tables.shape[1], _ptr(context_lens), _ptr(release_mask),
         context_lens.numel(), block_size, _ptr(context_lens_out), _ptr(status_flag),
         _stream(stream)))
+
+
+def kvq_blocks_fork(refcount, block_tables, context_lens, src_rows, dst_rows, block_size,
+                    stream=None):
+    """Rows dst_rows[k] take rows src_rows[k]'s blocks (device int32 tensors)."""
+    _check("kvq_blocks_fork", _lib.kvq_blocks_fork(
+        _ptr(refcount), refcount.numel(), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), context_lens.numel(), _ptr(src_rows), _ptr(dst_rows),
+        src_rows.numel(), block_size, _stream(stream)))
+
+
+def kvq_blocks_reserve_shared(free_stack, free_top, refcount, block_tables, context_lens,
+                              new_tokens, block_size, slot_mapping_out, cow_src, cow_dst,
+                              cow_count, status_flag, context_lens_out=None, stream=None):
+    _check("kvq_blocks_reserve_shared", _lib.kvq_blocks_reserve_shared(
+        _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(refcount),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(new_tokens),
+        context_lens.numel(), block_size, _ptr(slot_mapping_out), _ptr(context_lens_out),
+        _ptr(cow_src), _ptr(cow_dst), _ptr(cow_count), _ptr(status_flag), _stream(stream)))
+
+
+def kvq_blocks_release_shared(free_stack, free_top, refcount, block_tables, context_lens,
+                              release_mask, block_size, status_flag, context_lens_out=None,
+                              stream=None):
+    _check("kvq_blocks_release_shared", _lib.kvq_blocks_release_shared(
+        _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(refcount),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(release_mask),
+        context_lens.numel(), block_size, _ptr(context_lens_out), _ptr(status_flag),
+        _stream(stream)))
+
+
+def kvq_copy_blocks(layout, cache: PagedCache, src_ids, dst_ids, count, max_pairs=None,
+                    stream=None):
+    """Copy block src_ids[k] onto dst_ids[k] in one layer, k < count[0] (device)."""
+    _check("kvq_copy_blocks", _lib.kvq_copy_blocks(
+        C.byref(layout), C.byref(cache.struct), _ptr(src_ids), _ptr(dst_ids), _ptr(count),
+        src_ids.numel() if max_pairs is None else max_pairs, _stream(stream)))

@@ -228,6 +228,27 @@ def test_prefill_rejects_bad_arguments_on_host():
     assert kq.kvq_prefill_workspace_bytes(L, 2, 32, 8, 4096, 256) < w1
 
 
+def test_sharing_calls_reject_bad_arguments_on_host():
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+    assert lib.kvq_blocks_fork(None, 64, p, 4, p, 2, p, p, 1, 16, None) == \
+        kq.KVQ_ERR_INVALID_ARGUMENT                                  # no counts
+    assert lib.kvq_blocks_fork(p, 64, p, 4, p, 2, p, p, 0, 16, None) == kq.KVQ_OK
+    assert lib.kvq_blocks_fork(p, 64, None, 4, p, 2, p, p, 1, 16, None) == \
+        kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_blocks_reserve_shared(p, p, 64, p, p, 4, p, p, 2, 16, p, None, None, p, p, p,
+                                         None) == kq.KVQ_ERR_INVALID_ARGUMENT   # no copy pairs
+    assert lib.kvq_blocks_reserve_shared(p, p, 64, None, p, 4, p, p, 2, 16, p, None, p, p, p, p,
+                                         None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_blocks_release_shared(p, p, 0, p, p, 4, p, p, 2, 16, None, p, None) == \
+        kq.KVQ_ERR_INVALID_ARGUMENT                                  # empty pool
+    L = kq.make_layout(8, 128, 16, "int8")
+    cs = _fake_cache(L)
+    assert lib.kvq_copy_blocks(C.byref(L), C.byref(cs), p, p, p, 0, None) == kq.KVQ_OK
+    assert lib.kvq_copy_blocks(C.byref(L), C.byref(cs), None, p, p, 4, None) == \
+        kq.KVQ_ERR_INVALID_ARGUMENT
+
+
 def test_pool_calls_reject_bad_arguments_on_host():
     lib = kq._lib
     p = C.c_void_p(1 << 21)
