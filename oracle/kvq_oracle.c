@@ -788,7 +788,13 @@ int orc_decode(const orc_layout* L, const orc_cache* C, const void* q,
  * out[r][h] = sum_{t<=p} e_t v_t / sum_{t<=p} e_t, e_t = exp(s_t - max s),
  * s_t = (q . k_t) sm, in binary64 from the binary32 dequantized rows. Which
  * positions are read raw from the stage (per-channel keys) is decided by the
- * full length L, as in decode. nq = 1 is decode. */
+ * full length L, as in decode. nq = 1 is decode.
+ * Sliding window with attention sinks [P3, "Cache Eviction and Compression
+ * Strategies": a sliding window keeps only the most recent tokens; a few
+ * first tokens kept as sinks next to the window allow unbounded context]:
+ * with window > 0 the query at position p sees only positions t <= p with
+ * t >= p + 1 - window (its last `window` positions, itself included) or
+ * t < sink. window = 0 is full causal attention. */
 typedef struct {
   const orc_layout* L;
   const orc_cache* C;
@@ -797,12 +803,17 @@ typedef struct {
   const int32_t* qstart;
   const int32_t* tables;
   const int32_t* lens;
+  int32_t window, sink;
   double sm;
   double* out;
   int64_t next;
   int rc;
   pthread_mutex_t mu;
 } prefill_job;
+
+static int prefill_sees(const prefill_job* J, int p, int t) {
+  return t <= p && (J->window <= 0 || t >= p + 1 - J->window || t < J->sink);
+}
 
 static int prefill_one(const prefill_job* J, int b, int i, int h, double* o) {
   const orc_layout* L = J->L;
@@ -819,6 +830,7 @@ static int prefill_one(const prefill_job* J, int b, int i, int h, double* o) {
   double* sc = (double*)malloc(sizeof(double) * (size_t)(p + 1));
   double m = -INFINITY;
   for (int t = 0; t <= p; ++t) {
+    if (!prefill_sees(J, p, t)) continue;
     int rc = orc_dequant_token(L, J->C, 0, table_row, len, b, t, h / G, row);
     if (rc) {
       free(sc);
@@ -831,6 +843,7 @@ static int prefill_one(const prefill_job* J, int b, int i, int h, double* o) {
   }
   double l = 0.0;
   for (int t = 0; t <= p; ++t) {
+    if (!prefill_sees(J, p, t)) continue;
     double w = exp(sc[t] - m);
     l += w;
     int rc = orc_dequant_token(L, J->C, 1, table_row, len, b, t, h / G, row);
@@ -870,8 +883,8 @@ static void* prefill_worker(void* arg) {
 int orc_prefill(const orc_layout* L, const orc_cache* C, const void* q, int32_t q_dtype,
                 int32_t batch, int32_t num_q_heads, const int32_t* query_start,
                 const int32_t* block_tables, int32_t max_blocks_per_seq,
-                const int32_t* context_lens, double sm_scale, double* out,
-                int32_t num_threads) {
+                const int32_t* context_lens, int32_t window, int32_t sink,
+                double sm_scale, double* out, int32_t num_threads) {
   int rc = check_layout(L);
   if (rc) return rc;
   if (num_q_heads % L->num_kv_heads) return ORC_ERR_INVALID;
@@ -890,6 +903,8 @@ int orc_prefill(const orc_layout* L, const orc_cache* C, const void* q, int32_t 
   J.qstart = query_start;
   J.tables = block_tables;
   J.lens = context_lens;
+  J.window = window;
+  J.sink = sink;
   J.sm = sm_scale != 0.0 ? sm_scale : 1.0 / sqrt((double)L->head_dim);
   J.out = out;
   J.next = 0;
@@ -1116,6 +1131,47 @@ int orc_copy_blocks(const orc_layout* L, const orc_cache* C, const int32_t* src,
       }
     }
   }
+  return ORC_OK;
+}
+
+/* Block recycling under a sliding window [P3, "Cache Eviction and Compression
+ * Strategies": with a window of the last N tokens, older tokens are dropped;
+ * with sinks, the first tokens stay]. Queries from position L = lens[b] on
+ * see positions t >= L + 1 - window and t < sink only, so block i of
+ * sequence b is no longer needed when it holds no sink position
+ * (i >= ceil(sink / bs)) and ends before the window ((i + 1) bs <=
+ * L + 1 - window). Such blocks still in the table are pushed onto the
+ * stack (batch order, logical order) and their entries set to -1. All or
+ * nothing when the pushes would overflow the stack. */
+int orc_blocks_trim(int32_t* stack, int32_t* top, int64_t capacity, int32_t* tables,
+                    int32_t max_blocks, const int32_t* lens, int32_t window, int32_t sink,
+                    int32_t batch, int32_t bs, int32_t* status) {
+  int64_t total = 0;
+  if (window > 0) {
+    for (int b = 0; b < batch; ++b) {
+      int64_t lo = ceil_div(sink, bs), hi = ((int64_t)lens[b] + 1 - window) / bs;
+      if (lens[b] + 1 - window < 0) hi = 0;
+      for (int64_t i = lo; i < hi && i < max_blocks; ++i)
+        total += tables[(int64_t)b * max_blocks + i] >= 0;
+    }
+  }
+  if (*top + total > capacity) {
+    *status = ORC_ERR_OUT_OF_BLOCKS;
+    return ORC_OK;
+  }
+  if (window > 0) {
+    for (int b = 0; b < batch; ++b) {
+      int64_t lo = ceil_div(sink, bs), hi = ((int64_t)lens[b] + 1 - window) / bs;
+      if (lens[b] + 1 - window < 0) hi = 0;
+      for (int64_t i = lo; i < hi && i < max_blocks; ++i) {
+        int32_t* e = &tables[(int64_t)b * max_blocks + i];
+        if (*e < 0) continue;
+        stack[(*top)++] = *e;
+        *e = -1;
+      }
+    }
+  }
+  *status = ORC_OK;
   return ORC_OK;
 }
 

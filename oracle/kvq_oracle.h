@@ -91,8 +91,11 @@ int orc_append_static(const orc_layout* L, const orc_cache* C, const void* k,
 int orc_prefill(const orc_layout* L, const orc_cache* C, const void* q, int32_t q_dtype,
                 int32_t batch, int32_t num_q_heads, const int32_t* query_start,
                 const int32_t* block_tables, int32_t max_blocks_per_seq,
-                const int32_t* context_lens, double sm_scale, double* out,
-                int32_t num_threads);
+                const int32_t* context_lens, int32_t window, int32_t sink,
+                double sm_scale, double* out, int32_t num_threads);
+int orc_blocks_trim(int32_t* stack, int32_t* top, int64_t capacity, int32_t* tables,
+                    int32_t max_blocks, const int32_t* lens, int32_t window, int32_t sink,
+                    int32_t batch, int32_t bs, int32_t* status);
 int orc_blocks_fork(int32_t* refcount, int32_t* tables, int32_t max_blocks,
                     int32_t* lens, const int32_t* src, const int32_t* dst,
                     int32_t num_forks, int32_t bs);

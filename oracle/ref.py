@@ -57,7 +57,9 @@ def _load():
         "orc_quant_sym_static": (None, [vp, C.c_int, C.c_int, f32, vp]),
         "orc_quant_fp8_static": (None, [vp, C.c_int, f32, vp]),
         "orc_quant_asym4_static": (None, [vp, C.c_int, f32, C.c_uint8, vp]),
-        "orc_prefill": (C.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, f64, vp, i32]),
+        "orc_prefill": (C.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, i32, f64, vp,
+                                 i32]),
+        "orc_blocks_trim": (C.c_int, [vp, vp, i64, vp, i32, vp, i32, i32, i32, i32, vp]),
         "orc_append_static": (C.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
         "orc_int4_pack": (None, [vp, C.c_int, vp]),
         "orc_int4_unpack": (None, [vp, C.c_int, vp]),
@@ -229,10 +231,11 @@ def decode(L, cache, q, q_dtype, block_tables, context_lens, sm_scale=0.0,
 
 
 def prefill(L, cache, q, q_dtype, query_start, block_tables, context_lens, sm_scale=0.0,
-            threads=1):
+            threads=1, window=0, sink=0):
     """Multi-query attention: q uint16 bits [Tq][Hq][d], query_start int32
     [B+1] (sequence b's queries are its last query_start[b+1]-query_start[b]
-    positions). Returns fp64 [Tq][Hq][d]."""
+    positions); window > 0 limits each query to its last `window` positions
+    plus the first `sink`. Returns fp64 [Tq][Hq][d]."""
     q = np.ascontiguousarray(q)
     Tq, Hq, d = q.shape
     qs = np.ascontiguousarray(query_start, np.int32)
@@ -242,8 +245,8 @@ def prefill(L, cache, q, q_dtype, query_start, block_tables, context_lens, sm_sc
     out = np.zeros((Tq, Hq, d), np.float64)
     cs = cache.struct()
     rc = lib.orc_prefill(C.byref(L), C.byref(cs), _ptr(q), q_dtype, len(lens), Hq, _ptr(qs),
-                         _ptr(tables), tables.shape[1], _ptr(lens), sm_scale, _ptr(out),
-                         threads)
+                         _ptr(tables), tables.shape[1], _ptr(lens), window, sink, sm_scale,
+                         _ptr(out), threads)
     if rc:
         raise ValueError(f"orc_prefill: {rc}")
     return out
@@ -411,3 +414,13 @@ def copy_blocks(L, cache, src, dst):
     cs = cache.struct()
     rc = lib.orc_copy_blocks(C.byref(L), C.byref(cs), _ptr(src), _ptr(dst), src.size)
     assert rc == 0
+
+
+def blocks_trim(stack, top, tables, lens, window, sink, bs):
+    """Mutates stack, top, tables in place; returns the status."""
+    lens = np.ascontiguousarray(lens, np.int32)
+    status = np.zeros(1, np.int32)
+    rc = lib.orc_blocks_trim(_ptr(stack), _ptr(top), stack.size, _ptr(tables), tables.shape[1],
+                             _ptr(lens), window, sink, lens.size, bs, _ptr(status))
+    assert rc == 0
+    return int(status[0])
