@@ -332,6 +332,14 @@ int64_t kvq_prefill_workspace_bytes(const kvq_layout* layout, int32_t batch,
  *                 appended): query i sits at position context_lens[b] - nq_b
  *                 + i and attends to positions 0 .. that position.
  *  max_query_len  host bound on every nq_b (sizes the launch).
+ *  window, sink   sliding-window attention with attention sinks ("KV Cache
+ *                 Optimization: Strategies ...", section "Cache Eviction and
+ *                 Compression Strategies"): with window > 0 the query at
+ *                 position p sees only positions t <= p with
+ *                 t >= p + 1 - window or t < sink; window = 0 (sink
+ *                 ignored) is full causal attention. Positions no query
+ *                 sees are never read, so their table entries may be -1
+ *                 (kvq_blocks_trim).
  *  split_blocks   cache blocks per split-K chunk (>= 1); 0 lets the library
  *                 choose.
  *  out            device [Tq][num_q_heads][d] in out_dtype.
@@ -347,9 +355,10 @@ kvq_status kvq_prefill_attention(const kvq_layout* layout, const kvq_cache* cach
                                  int32_t num_q_heads, const int32_t* query_start,
                                  int32_t max_query_len, const int32_t* block_tables,
                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                 int32_t max_context_len, float sm_scale,
-                                 int32_t split_blocks, void* out, int32_t out_dtype,
-                                 void* workspace, int64_t workspace_bytes, void* stream);
+                                 int32_t max_context_len, float sm_scale, int32_t window,
+                                 int32_t sink, int32_t split_blocks, void* out,
+                                 int32_t out_dtype, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
 
 /* Fill a pool: free_stack[i] = initial_order[i] (or i when initial_order is
  * NULL) for i < num_blocks, and *free_top = num_blocks. free_stack, free_top
@@ -408,6 +417,23 @@ kvq_status kvq_blocks_release(int32_t* free_stack, int32_t* free_top,
  * holding each block, 0 for a free block (all zero after kvq_pool_init; the
  * caller zero-fills it). Use the _shared reserve and release with such a
  * pool; the plain ones do not keep the counts. */
+
+/* Block recycling under a sliding window ("KV Cache Optimization:
+ * Strategies ...", section "Cache Eviction and Compression Strategies": only
+ * the recent tokens, and the sinks, are kept). Queries from position
+ * L = context_lens[b] on see only t >= L + 1 - window and t < sink, so the
+ * blocks i of sequence b with ceil(sink / bs) <= i and (i + 1) bs <=
+ * L + 1 - window that are still in its table are pushed onto the stack
+ * (batch order, logical order) and their entries set to -1. window = 0 trims
+ * nothing. For the plain pool (no counts); a trimmed table is for windowed
+ * kvq_prefill_attention only (decode reads every block). All or nothing if
+ * the pushes would overflow the stack (*status_flag = KVQ_ERR_OUT_OF_BLOCKS).
+ * All pointers are device memory. */
+kvq_status kvq_blocks_trim(int32_t* free_stack, int32_t* free_top, int64_t pool_capacity,
+                           int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t window, int32_t sink,
+                           int32_t batch, int32_t block_size, int32_t* status_flag,
+                           void* stream);
 
 /* Fork k (k < num_forks): row dst_rows[k] takes row src_rows[k]'s length and
  * its first ceil(len / bs) table entries, each block gaining one reference.

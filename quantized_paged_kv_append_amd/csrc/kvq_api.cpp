@@ -390,14 +390,15 @@ kvq_status kvq_prefill_attention(const kvq_layout* L, const kvq_cache* C, const 
                                  const int32_t* query_start, int32_t max_query_len,
                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
                                  const int32_t* context_lens, int32_t max_context_len,
-                                 float sm_scale, int32_t split_blocks, void* out,
-                                 int32_t out_dtype, void* workspace, int64_t workspace_bytes,
-                                 void* stream) {
+                                 float sm_scale, int32_t window, int32_t sink,
+                                 int32_t split_blocks, void* out, int32_t out_dtype,
+                                 void* workspace, int64_t workspace_bytes, void* stream) {
   kvq_status s = kvq_layout_check(L);
   if (s != KVQ_OK) return s;
   s = check_cache(L, C);
   if (s != KVQ_OK) return s;
   if (batch < 0 || num_q_heads < 1 || num_q_heads % L->num_kv_heads) return KVQ_ERR_INVALID_ARGUMENT;
+  if (window < 0 || sink < 0) return KVQ_ERR_INVALID_ARGUMENT;
   if (q_dtype != KVQ_F16 && q_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARGUMENT;
   if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
     return KVQ_ERR_INVALID_ARGUMENT;
@@ -463,6 +464,8 @@ kvq_status kvq_prefill_attention(const kvq_layout* L, const kvq_cache* C, const 
   pp.splits = (int32_t)sh.J;
   pp.split_blocks = (int32_t)sh.S;
   pp.col_tiles = (int32_t)sh.CT;
+  pp.window = window;
+  pp.sink = window > 0 ? sink : 0;
   return hip_status(kvq::launch_prefill(pp, static_cast<hipStream_t>(stream)));
 }
 
@@ -503,6 +506,22 @@ kvq_status kvq_blocks_release(int32_t* free_stack, int32_t* free_top, int64_t po
       free_stack, free_top, pool_capacity, block_tables, max_blocks_per_seq, context_lens,
       release_mask, batch, block_size, context_lens_out, status_flag,
       static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_blocks_trim(int32_t* free_stack, int32_t* free_top, int64_t pool_capacity,
+                           int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t window, int32_t sink,
+                           int32_t batch, int32_t block_size, int32_t* status_flag,
+                           void* stream) {
+  if (!free_stack || !free_top || !status_flag || pool_capacity < 1 || pool_capacity > INT32_MAX)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1 || window < 0 || sink < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (!block_tables || !context_lens)) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_blocks_trim(free_stack, free_top, pool_capacity, block_tables,
+                                            max_blocks_per_seq, context_lens, window, sink,
+                                            batch, block_size, status_flag,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_blocks_fork(int32_t* refcount, int64_t pool_capacity, int32_t* block_tables,

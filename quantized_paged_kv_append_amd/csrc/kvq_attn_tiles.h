@@ -195,18 +195,20 @@ enum KeySource {
   kKeyRaw = 2,         // raw staged rows, kraw[c] = elements of chunk c
 };
 
-// One 16-token tile: scores, online softmax, PV. TAIL handles the tile that
-// ends past the sequence length: scores of tokens at or past L (this lane's
-// column limit) are masked, and value codes of tokens at or past Lv (the rows
-// that hold data; Lv < 0 means L) are zeroed, since they may hold NaN bytes.
-// In decode both limits are the length; causal multi-query columns differ in
-// L while sharing the value operand, so only rows past the data are zeroed.
+// One 16-token tile: scores, online softmax, PV. TAIL handles a tile with
+// masked tokens: the lane's column sees token t only if t < L and (t >= lo
+// or t < sk) -- L its causal limit, lo the start of its window and sk the
+// number of sink tokens (lo = 0: no window) -- and value codes of tokens at
+// or past Lv (the rows that hold data; Lv < 0 means L) are zeroed, since
+// they may hold NaN bytes. In decode L is the length for every column; the
+// columns of multi-query attention differ in L and lo while sharing the
+// value operand, so only rows past the data are zeroed.
 template <int CODE, int D, int BS, bool TAIL, int KSRC = kKeyTokenScale>
 __device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos0, int L,
                                           const half8v* qop, float cscore, int j,
                                           SoftmaxState<D>& st, const u32x4* kraw = nullptr,
                                           bool raw_bf16 = false, const half8v* qlo = nullptr,
-                                          int Lv = -1) {
+                                          int Lv = -1, int lo = 0, int sk = 0) {
   constexpr int NCH = D / 32;
   constexpr int NPV = D / 16;
   const int Ld = Lv < 0 ? L : Lv;
@@ -228,7 +230,10 @@ __device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos
   }
   bool ok[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ok[e] = !TAIL || pos0 + 4 * j + e < L;
+  for (int e = 0; e < 4; ++e) {
+    const int tk = pos0 + 4 * j + e;
+    ok[e] = !TAIL || (tk < L && (tk >= lo || tk < sk));
+  }
   float s[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -420,7 +425,8 @@ __device__ __forceinline__ half4v raw_vop(uint32_t w0, uint32_t w1, uint32_t w2,
 template <int D, int BS, bool TAIL>
 __device__ __forceinline__ void tile_step_raw(const TileRaw<D, BS>& t, int nt, int pos0, int L,
                                               const half8v* qop, float cscore, int j,
-                                              SoftmaxState<D>& st, bool bf16, int Lv = -1) {
+                                              SoftmaxState<D>& st, bool bf16, int Lv = -1,
+                                              int lo = 0, int sk = 0) {
   constexpr int NCH = D / 32;
   constexpr int NPV = D / 16;
   const int Ld = Lv < 0 ? L : Lv;   // as in tile_step
@@ -428,9 +434,12 @@ __device__ __forceinline__ void tile_step_raw(const TileRaw<D, BS>& t, int nt, i
 #pragma unroll
   for (int c = 0; c < NCH; ++c)
     S = __builtin_amdgcn_mfma_f32_16x16x32_f16(raw8_to_h8(t.k[nt][c], bf16), qop[c], S, 0, 0, 0);
-  bool ok[4];
+  bool ok[4];   // as in tile_step
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ok[e] = !TAIL || pos0 + 4 * j + e < L;
+  for (int e = 0; e < 4; ++e) {
+    const int tk = pos0 + 4 * j + e;
+    ok[e] = !TAIL || (tk < L && (tk >= lo || tk < sk));
+  }
   float s[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) s[e] = (TAIL && !ok[e]) ? -INFINITY : S[e] * cscore;

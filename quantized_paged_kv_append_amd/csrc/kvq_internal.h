@@ -100,6 +100,8 @@ struct PrefillPlan {
   int32_t splits;              // J: splits per sequence (upper bound)
   int32_t split_blocks;        // S: cache blocks per split
   int32_t col_tiles;           // CT: 16-column tiles per (sequence, KV head)
+  int32_t window;              // > 0: sliding window of the last `window` positions
+  int32_t sink;                // sink positions kept next to the window
 };
 
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream);

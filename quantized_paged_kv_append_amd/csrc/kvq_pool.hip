@@ -396,6 +396,68 @@ __global__ __launch_bounds__(kThreads) void release_shared_kernel(
   }
 }
 
+// Window trimming (one workgroup): sequence b's blocks i in
+// [ceil(sink / bs), floor((L + 1 - window) / bs)) that are still in its table
+// are pushed (batch order, logical order) and their entries cleared; all or
+// nothing if the pushes would overflow the stack.
+__device__ __forceinline__ void trim_range(int32_t L, int32_t window, int32_t sink, int32_t bs,
+                                           int32_t max_blocks, int64_t& lo, int64_t& hi) {
+  lo = ceil_div(max(sink, 0), bs);
+  hi = (int64_t)L + 1 - window >= 0 ? ((int64_t)L + 1 - window) / bs : 0;
+  hi = min(hi, (int64_t)max_blocks);
+}
+
+__global__ __launch_bounds__(kThreads) void trim_kernel(int32_t* stack, int32_t* top,
+                                                        int64_t capacity, int32_t* tables,
+                                                        int32_t max_blocks, const int32_t* lens,
+                                                        int32_t window, int32_t sink,
+                                                        int32_t batch, int32_t bs,
+                                                        int32_t* status) {
+  __shared__ int64_t sh[kThreads];
+  const int tid = threadIdx.x;
+  const int64_t top0 = min(max((int64_t)*top, (int64_t)0), capacity);
+  int64_t total = 0;
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    int64_t nb = 0;
+    if (b < batch && window > 0) {
+      int64_t lo, hi;
+      trim_range(lens[b], window, sink, bs, max_blocks, lo, hi);
+      for (int64_t i = lo; i < hi; ++i) nb += tables[(int64_t)b * max_blocks + i] >= 0;
+    }
+    int64_t t;
+    block_exclusive_scan(nb, &t, sh);
+    total += t;
+  }
+  if (top0 + total > capacity) {
+    if (tid == 0) *status = KVQ_ERR_OUT_OF_BLOCKS;
+    return;
+  }
+  int64_t off = 0;
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    int64_t nb = 0, lo = 0, hi = 0;
+    if (b < batch && window > 0) {
+      trim_range(lens[b], window, sink, bs, max_blocks, lo, hi);
+      for (int64_t i = lo; i < hi; ++i) nb += tables[(int64_t)b * max_blocks + i] >= 0;
+    }
+    int64_t t;
+    int64_t pos = top0 + block_exclusive_scan(nb, &t, sh) + off;
+    for (int64_t i = lo; i < hi; ++i) {
+      int32_t* e = &tables[(int64_t)b * max_blocks + i];
+      if (*e < 0) continue;
+      stack[pos++] = *e;
+      *e = -1;
+    }
+    off += t;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    *top = (int32_t)(top0 + total);
+    *status = KVQ_OK;
+  }
+}
+
 // Copy of one layer's planes for each (src, dst) block pair: workgroup
 // (pair, plane), 16-byte vectors; pairs past *count are skipped.
 struct CopyPlanes {
@@ -448,6 +510,15 @@ hipError_t launch_blocks_release(int32_t* stack, int32_t* top,
                                  hipStream_t stream) {
   release_kernel<<<1, kThreads, 0, stream>>>(stack, top, capacity, tables, max_blocks,
                                              lens, mask, batch, bs, lens_out, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_blocks_trim(int32_t* stack, int32_t* top, int64_t capacity, int32_t* tables,
+                              int32_t max_blocks, const int32_t* lens, int32_t window,
+                              int32_t sink, int32_t batch, int32_t bs, int32_t* status,
+                              hipStream_t stream) {
+  trim_kernel<<<1, kThreads, 0, stream>>>(stack, top, capacity, tables, max_blocks, lens, window,
+                                          sink, batch, bs, status);
   return hipGetLastError();
 }
 

@@ -32,6 +32,8 @@ struct PrefillArgs {
   int32_t S;    // blocks per split
   int32_t CT;   // column tiles per (sequence, KV head)
   int32_t TW;   // column tiles per workgroup: 1, 2 or 4 (4 / TW waves per tile)
+  int32_t window;   // > 0: each query sees its last `window` positions ...
+  int32_t sink;     // ... and the first `sink` positions
 };
 
 template <int CODE, int MODE, int D, int BS>
@@ -80,11 +82,25 @@ void prefill_split_kernel(PrefillArgs pa) {
   const int Lr = valid ? L - nq + qi + 1 : 0;                 // this column's limit
   const int Lmin = L - nq + cbase / a.G + 1;                  // over the tile's columns
   const int Lmax = active ? L - nq + (min(ncol, cbase + 16) - 1) / a.G + 1 : 0;
-  // the tile's blocks (none past what any of its columns sees), in shares
+  // sliding window with sinks: the lane's column sees t >= lo_r (and t < SK);
+  // lo_min / lo_max bound the window starts over the tile's columns
+  const int W = pa.window, SK = pa.window > 0 ? pa.sink : 0;
+  const int lo_r = W > 0 ? Lr - W : 0;
+  const int lo_min = W > 0 ? Lmin - W : 0;
+  const int lo_max = W > 0 ? Lmax - W : 0;
+  // the tile's visible blocks of the split (none past what any of its columns
+  // sees): the sink blocks A = [s0, a_end) and the window's blocks
+  // B = [bstart, s1), with nothing between them read
   const int s1 = min(min(s0 + pa.S, nblk), (Lmax + BS - 1) / BS);
-  const int share = max(s1 - s0 + nshare - 1, 0) / nshare;
-  const int i0 = s0 + (wave / pa.TW) * share;
-  const int i1 = min(i0 + share, s1);
+  const int nsb = (SK + BS - 1) / BS;
+  const int wb0 = max(lo_min, 0) / BS;   // first block any window reaches
+  const bool gap = wb0 > nsb;
+  const int a_end = gap ? max(s0, min(s1, nsb)) : s0;
+  const int bstart = gap ? max(a_end, max(s0, wb0)) : s0;
+  const int nA = a_end - s0, nV = nA + max(s1 - bstart, 0);
+  // the wave's share of the visible blocks, as positions x in A then B
+  const int share = (nV + nshare - 1) / nshare;
+  const int x0 = (wave / pa.TW) * share, x1 = min(x0 + share, nV);
 
   float qf[D / 4];
   {
@@ -122,24 +138,28 @@ void prefill_split_kernel(PrefillArgs pa) {
 #pragma unroll
   for (int cc = 0; cc < NPV; ++cc) st.acc[cc] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (i0 < i1) {
+  if (x0 < x1) {
     // per-channel keys: a partly filled last block is read raw from stage row b
     const bool staged = KCH && (L % BS) != 0;
     // the wave's LDS slice for the per-channel query (the merge area, unused
     // until the waves have finished streaming)
     float* xs = &red[wave][0][0];
     const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
-    // refills past the share read physical block 0 (shared, cached); ids
-    // outside the pool (a broken precondition) are read as block 0 too
+    // ids outside the pool (a broken precondition, or a block dropped from a
+    // window) are read as block 0, which every wave shares
     auto bh_of = [&](int i) -> int64_t {
-      const int32_t id = i < i1 ? trow[i] : 0;
+      const int32_t id = trow[i];
       return (int64_t)(id >= 0 && id < a.num_blocks ? id : 0) * a.H + g;
     };
-    // blocks [i0, ifull) are seen whole by every column (and hold codes);
-    // the rest of the share, at most two blocks per column tile plus a staged
-    // one, needs per-column masks
+    // the share's blocks of B: [b0, b1); of those, [ra, rb) are seen whole by
+    // every column (and hold codes) and stream through the register ring;
+    // the rest -- sink blocks, the first blocks of the window, the last one
+    // or two of the context, a staged one -- take per-column masks
+    const int b0 = bstart + max(x0, nA) - nA, b1 = bstart + x1 - nA;
     const int iseen = (KCH && staged) ? min(Lmin / BS, nblk - 1) : Lmin / BS;
-    const int ifull = max(i0, min(i1, iseen));
+    const int wf0 = W > 0 ? (max(lo_max, 0) + BS - 1) / BS : 0;
+    const int ra = min(max(wf0, b0), max(b1, b0));
+    const int rb = min(max(iseen, ra), max(b1, ra));
     auto full_block = [&](const TileT& t, int i) {
       if constexpr (RAW) {
 #pragma unroll
@@ -178,24 +198,28 @@ void prefill_split_kernel(PrefillArgs pa) {
 #pragma unroll
       for (int nt = 0; nt < BS / 16; ++nt) {
         const int pos0 = i * BS + nt * 16;
-        if (pos0 >= Lmax) continue;
-        const bool masked = pos0 + 16 > Lmin;
+        // no column sees the tile: past every limit, or between the sinks
+        // and every window
+        if (pos0 >= Lmax || (W > 0 && pos0 >= SK && pos0 + 16 <= lo_min)) continue;
+        const bool masked =
+            pos0 + 16 > Lmin || (W > 0 && pos0 < lo_max && pos0 + 16 > SK);
         if constexpr (RAW) {
           if (masked)
-            tile_step_raw<D, BS, true>(t, nt, pos0, Lr, qop, cscore, jj, st, raw_bf16, L);
+            tile_step_raw<D, BS, true>(t, nt, pos0, Lr, qop, cscore, jj, st, raw_bf16, L,
+                                       lo_r, SK);
           else
             tile_step_raw<D, BS, false>(t, nt, pos0, Lr, qop, cscore, jj, st, raw_bf16, L);
         } else if constexpr (KCH) {
           if (rawk) {   // qb holds the plain fp16 query here
             if (masked)
               tile_step<CODE, D, BS, true, kKeyRaw>(t, nt, pos0, Lr, qb, cscore, jj, st,
-                                                    kraw[nt], raw_bf16, nullptr, L);
+                                                    kraw[nt], raw_bf16, nullptr, L, lo_r, SK);
             else
               tile_step<CODE, D, BS, false, kKeyRaw>(t, nt, pos0, Lr, qb, cscore, jj, st,
                                                      kraw[nt], raw_bf16, nullptr, L);
           } else if (masked) {
             tile_step<CODE, D, BS, true, kKeyChannel>(t, nt, pos0, Lr, qb, cscore, jj, st,
-                                                      nullptr, false, ql, L);
+                                                      nullptr, false, ql, L, lo_r, SK);
           } else {
             tile_step<CODE, D, BS, false, kKeyChannel>(t, nt, pos0, Lr, qb, cscore, jj, st,
                                                        nullptr, false, ql, L);
@@ -203,33 +227,38 @@ void prefill_split_kernel(PrefillArgs pa) {
         } else {
           if (masked)
             tile_step<CODE, D, BS, true>(t, nt, pos0, Lr, qop, cscore, jj, st, nullptr, false,
-                                         nullptr, L);
+                                         nullptr, L, lo_r, SK);
           else
             tile_step<CODE, D, BS, false>(t, nt, pos0, Lr, qop, cscore, jj, st, nullptr, false,
                                           nullptr, L);
         }
       }
     };
+    auto edge_run = [&](int e0, int e1) {
+      for (int i = e0; i < e1; ++i) {
+        TileT t;
+        load_tile<D, BS, KCH>(t, a, bh_of(i), lane);
+        edge_block(t, i);
+      }
+    };
+    edge_run(s0 + x0, s0 + min(x1, nA));   // sink blocks
+    edge_run(b0, ra);
     // register ring over the whole blocks: every slot computes one block and
-    // refills its buffer with the block NBUF ahead (past ifull: block 0)
-    if (i0 < ifull) {
-      auto bh_full = [&](int i) -> int64_t { return bh_of(i < ifull ? i : i1); };
+    // refills its buffer with the block NBUF ahead (past rb: block 0)
+    if (ra < rb) {
+      auto bh_full = [&](int i) -> int64_t { return i < rb ? bh_of(i) : (int64_t)g; };
       TileT buf[NBUF];
 #pragma unroll
-      for (int v = 0; v < NBUF; ++v) load_tile<D, BS, KCH>(buf[v], a, bh_full(i0 + v), lane);
-      for (int i = i0; i < ifull; i += NBUF) {
+      for (int v = 0; v < NBUF; ++v) load_tile<D, BS, KCH>(buf[v], a, bh_full(ra + v), lane);
+      for (int i = ra; i < rb; i += NBUF) {
 #pragma unroll
         for (int v = 0; v < NBUF; ++v) {
-          if (i + v < ifull) full_block(buf[v], i + v);
+          if (i + v < rb) full_block(buf[v], i + v);
           load_tile<D, BS, KCH>(buf[v], a, bh_full(i + v + NBUF), lane);
         }
       }
     }
-    for (int i = ifull; i < i1; ++i) {
-      TileT t;
-      load_tile<D, BS, KCH>(t, a, bh_of(i), lane);
-      edge_block(t, i);
-    }
+    edge_run(rb, b1);
   }
 
   // ---- merge the waves' states, then write one partial per column ---------
@@ -404,6 +433,8 @@ hipError_t launch_prefill(const PrefillPlan& pp, hipStream_t stream) {
   pa.J = pp.splits;
   pa.S = pp.split_blocks;
   pa.CT = pp.col_tiles;
+  pa.window = pp.window;
+  pa.sink = pp.sink;
   // the column tiles of a split share a workgroup (one tile per wave or
   // pair of waves), so that their reads of the same blocks meet in L1
   pa.TW = pp.col_tiles >= 4 ? 4 : (pp.col_tiles >= 2 ? 2 : 1);

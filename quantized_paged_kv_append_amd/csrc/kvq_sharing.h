@@ -1,5 +1,6 @@
 // kvq_sharing.h -- host-side interface between the C ABI layer (kvq_api.cpp)
-// and the prefix-sharing pool kernels (kvq_pool.hip). Internal.
+// and the pool kernels for prefix sharing and window trimming (kvq_pool.hip).
+// Internal.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,5 +30,10 @@ hipError_t launch_blocks_release_shared(int32_t* stack, int32_t* top, int64_t ca
 hipError_t launch_copy_blocks(uint8_t* const base[6], const int64_t per_block[6],
                               const int32_t* src, const int32_t* dst, const int32_t* count,
                               int32_t max_pairs, int64_t num_blocks, hipStream_t stream);
+
+hipError_t launch_blocks_trim(int32_t* stack, int32_t* top, int64_t capacity, int32_t* tables,
+                              int32_t max_blocks, const int32_t* lens, int32_t window,
+                              int32_t sink, int32_t batch, int32_t bs, int32_t* status,
+                              hipStream_t stream);
 
 }  // namespace kvq

@@ -69,7 +69,10 @@ _SIGS = {
                                     _i32, _f32, _i32, _vp, _i32, _vp, _i64, _vp]),
     "kvq_prefill_workspace_bytes": (_i64, [_LP, _i32, _i32, _i32, _i32, _i32]),
     "kvq_prefill_attention": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
-                                     _vp, _i32, _f32, _i32, _vp, _i32, _vp, _i64, _vp]),
+                                     _vp, _i32, _f32, _i32, _i32, _i32, _vp, _i32, _vp, _i64,
+                                     _vp]),
+    "kvq_blocks_trim": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
+                               _vp]),
     "kvq_pool_init": (_i32, [_vp, _vp, _vp, _i64, _vp]),
     "kvq_blocks_fork": (_i32, [_vp, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _vp]),
     "kvq_blocks_reserve_shared": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
@@ -219,7 +222,7 @@ def kvq_prefill_workspace_bytes(layout, batch, num_q_heads, max_query_len, max_c
 
 def kvq_prefill_attention(layout, cache: PagedCache, q, query_start, max_query_len,
                           block_tables, context_lens, max_context_len, out, workspace,
-                          sm_scale=0.0, split_blocks=0, stream=None):
+                          sm_scale=0.0, split_blocks=0, window=0, sink=0, stream=None):
     """q: device [Tq][Hq][d] fp16/bf16; query_start: int32 [B+1] (sequence b's
     queries are its last query_start[b+1]-query_start[b] positions);
     block_tables: int32 [B][max_blocks]; context_lens: int32 [B]; out: device
@@ -230,8 +233,8 @@ def kvq_prefill_attention(layout, cache: PagedCache, q, query_start, max_query_l
     _check("kvq_prefill_attention", _lib.kvq_prefill_attention(
         C.byref(layout), C.byref(cache.struct), _ptr(q), DTYPES[q.dtype], B, Hq,
         _ptr(query_start), int(max_query_len), _ptr(block_tables), block_tables.shape[1],
-        _ptr(context_lens), int(max_context_len), float(sm_scale), int(split_blocks),
-        _ptr(out), DTYPES[out.dtype], _ptr(workspace),
+        _ptr(context_lens), int(max_context_len), float(sm_scale), int(window), int(sink),
+        int(split_blocks), _ptr(out), DTYPES[out.dtype], _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
@@ -295,3 +298,12 @@ def kvq_copy_blocks(layout, cache: PagedCache, src_ids, dst_ids, count, max_pair
     _check("kvq_copy_blocks", _lib.kvq_copy_blocks(
         C.byref(layout), C.byref(cache.struct), _ptr(src_ids), _ptr(dst_ids), _ptr(count),
         src_ids.numel() if max_pairs is None else max_pairs, _stream(stream)))
+
+
+def kvq_blocks_trim(free_stack, free_top, block_tables, context_lens, window, sink, block_size,
+                    status_flag, stream=None):
+    """Return the blocks no query past context_lens can see under the window."""
+    _check("kvq_blocks_trim", _lib.kvq_blocks_trim(
+        _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), int(window), int(sink),
+        context_lens.numel(), block_size, _ptr(status_flag), _stream(stream)))

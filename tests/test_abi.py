@@ -207,7 +207,8 @@ def test_prefill_rejects_bad_arguments_on_host():
         a.update(kw)
         return lib.kvq_prefill_attention(C.byref(a["L"]), C.byref(a["cs"]), a["q"], a["q_dtype"],
                                          a["batch"], a["hq"], a["qs"], a["maxq"], a["tables"],
-                                         a["maxb"], a["lens"], a["maxlen"], a["sm"], a["split"],
+                                         a["maxb"], a["lens"], a["maxlen"], a["sm"],
+                                         a.get("window", 0), a.get("sink", 0), a["split"],
                                          a["out"], a["out_dtype"], a["ws"], a["wsb"], None)
     assert pre(hq=30) == kq.KVQ_ERR_INVALID_ARGUMENT            # Hq % H
     assert pre(maxq=65) == kq.KVQ_ERR_INVALID_ARGUMENT          # more queries than context
@@ -218,6 +219,10 @@ def test_prefill_rejects_bad_arguments_on_host():
     assert pre(wsb=16) == kq.KVQ_ERR_WORKSPACE_TOO_SMALL
     assert pre(sm=float("inf")) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert pre(batch=0) == kq.KVQ_OK and pre(maxq=0) == kq.KVQ_OK
+    assert pre(window=-1) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert pre(window=8, sink=-2) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_blocks_trim(p, p, 64, p, 4, p, -1, 0, 2, 16, p, None) == \
+        kq.KVQ_ERR_INVALID_ARGUMENT
     L4 = kq.make_layout(8, 128, 32, "int4", k_mode="group_asym", group_size=32)
     c4 = _fake_cache(L4)
     c4.k_zero, c4.v_zero = 1 << 25, (1 << 25) + 4096

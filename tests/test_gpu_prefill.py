@@ -39,26 +39,28 @@ def _setup(code="int8", d=128, bs=16, G=4, H=2, src="bfloat16", lens=LENS, nq=NQ
 
 
 def prefill_gpu(LL, gc, q, qs, tables, lens, max_q, max_len, out_dtype=torch.float32,
-                split_blocks=0, sm_scale=0.0):
+                split_blocks=0, sm_scale=0.0, window=0, sink=0):
     Tq, Hq, d = q.shape
     B = lens.numel()
     ws = torch.empty(kq.kvq_prefill_workspace_bytes(LL, B, Hq, max_q, max_len, split_blocks),
                      dtype=torch.uint8, device=DEV)
     out = torch.full((Tq, Hq, d), float("nan"), dtype=out_dtype, device=DEV)
     kq.kvq_prefill_attention(LL, gc, q, qs, max_q, tables, lens, max_len, out, ws,
-                             sm_scale=sm_scale, split_blocks=split_blocks)
+                             sm_scale=sm_scale, split_blocks=split_blocks, window=window,
+                             sink=sink)
     torch.cuda.synchronize()
     return out
 
 
-def _run(w, L, LL, s, q, qs, split_blocks=0, out_dtype=torch.float32, sm_scale=0.0):
+def _run(w, L, LL, s, q, qs, split_blocks=0, out_dtype=torch.float32, sm_scale=0.0, window=0,
+         sink=0):
     exp = ref.prefill(L, s.cache, bits(q), DT[w.src_dtype], qs, s.tables, s.lens,
-                      sm_scale=sm_scale, threads=8)
+                      sm_scale=sm_scale, threads=8, window=window, sink=sink)
     gc = upload(s.cache, LL)
     got = prefill_gpu(LL, gc, q.to(DEV), torch.from_numpy(qs).to(DEV),
                       torch.from_numpy(s.tables).to(DEV), torch.from_numpy(s.lens).to(DEV),
                       int(np.diff(qs).max()), int(s.lens.max()), out_dtype, split_blocks,
-                      sm_scale)
+                      sm_scale, window, sink)
     return got, exp
 
 
@@ -133,3 +135,76 @@ def test_prefill_chunk_of_a_long_prompt_sampled():
         ln = np.array([4096 - 512 + r0 + 1], np.int32)
         exp = ref.decode(L, s.cache, bits(q[r0:r0 + 1]), ref.BF16, s.tables, ln, threads=8)
         assert_decode_close(got[r0:r0 + 1], exp, f"row {r0}")
+
+
+@pytest.mark.parametrize("window,sink", [(1, 0), (7, 3), (16, 16), (40, 20), (100, 1), (33, 0)])
+@pytest.mark.parametrize("code,mode", [("int8", "token_sym"), ("fp8", "token_sym"),
+                                       ("none16", "token_sym"), ("int8", "channel_block")])
+@pytest.mark.parametrize("G,bs", [(4, 16), (8, 32)])
+def test_prefill_sliding_window_and_sinks(window, sink, code, mode, G, bs):
+    need_gpu()
+    w, L, LL, s, q, qs = _setup(code, 128, bs, G, mode=mode)
+    got, exp = _run(w, L, LL, s, q, qs, window=window, sink=sink)
+    assert_decode_close(got, exp, f"{code}/{mode} window {window} sink {sink}")
+
+
+@pytest.mark.parametrize("split", [1, 5, 64])
+def test_prefill_window_split_counts(split):
+    need_gpu()
+    w, L, LL, s, q, qs = _setup("fp8", G=8, lens=(700, 1, 250, 64, 0, 413),
+                                nq=(40, 1, 250, 9, 0, 17))
+    got, exp = _run(w, L, LL, s, q, qs, split_blocks=split, window=100, sink=4)
+    assert_decode_close(got, exp, f"window split {split}")
+
+
+@pytest.mark.parametrize("code", ["int8", "fp8"])
+def test_windowed_stream_with_trimming(code):
+    """Each step: reserve, append (GPU and oracle), windowed attention with
+    the new tokens, then trim the blocks no later query sees. Pools and
+    tables stay equal to the oracle's; the trimmed blocks are handed to
+    other sequences and overwritten, and the answers still match."""
+    need_gpu()
+    bs, window, sink, B, n = 16, 40, 3, 3, 40
+    w = workloads.get("tiny", k_code=code, v_code=code, block_size=bs, src_dtype="bfloat16",
+                      num_q_heads=8, num_kv_heads=2, head_dim=128, batch=B)
+    L, LL = oracle_layout(w), lib_layout(w)
+    order = np.random.default_rng(1).permutation(n).astype(np.int32)
+    s = OracleSeqs(L, n, B, 16, order=order)
+    gstack = torch.empty(n, dtype=torch.int32, device=DEV)
+    gtop = torch.empty(1, dtype=torch.int32, device=DEV)
+    kq.kvq_pool_init(gstack, gtop, torch.from_numpy(order).to(DEV))
+    gtab = torch.full((B, 16), -1, dtype=torch.int32, device=DEV)
+    glens = torch.zeros(B, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gc = kq.PagedCache(LL, n, device=DEV)
+    for t in gc.planes.values():
+        if t is not None:
+            t.fill_(0xFF)
+    rng = np.random.default_rng(5)
+    trimmed = 0
+    for step in range(8):
+        new = rng.integers(1, 30, B).astype(np.int32)
+        k, v = workloads.kv_rows(w, int(new.sum()), seed=step)
+        slots, _ = s.grow(new)
+        ref.append(L, s.cache, bits(k).reshape(len(slots), -1), bits(v).reshape(len(slots), -1),
+                   slots)
+        gsl = torch.empty(int(new.sum()), dtype=torch.int64, device=DEV)
+        kq.kvq_blocks_reserve(gstack, gtop, gtab, glens, torch.from_numpy(new).to(DEV), bs, gsl,
+                              status, glens)
+        kq.kvq_append(LL, gc, k.to(DEV), v.to(DEV), gsl)
+        qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+        q = workloads.query_rows(w, int(new.sum()), step=step)
+        exp = ref.prefill(L, s.cache, bits(q), ref.BF16, qs, s.tables, s.lens, threads=8,
+                          window=window, sink=sink)
+        got = prefill_gpu(LL, gc, q.to(DEV), torch.from_numpy(qs).to(DEV), gtab, glens,
+                          int(new.max()), int(s.lens.max()), window=window, sink=sink)
+        assert_decode_close(got, exp, f"windowed step {step}")
+        before = int(s.top[0])
+        assert ref.blocks_trim(s.stack, s.top, s.tables, s.lens, window, sink, bs) == 0
+        trimmed += int(s.top[0]) - before
+        kq.kvq_blocks_trim(gstack, gtop, gtab, glens, window, sink, bs, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert np.array_equal(gtab.cpu().numpy(), s.tables), step
+        assert np.array_equal(gstack.cpu().numpy(), s.stack) and int(gtop.item()) == int(s.top[0])
+    assert trimmed > 0
