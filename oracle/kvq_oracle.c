@@ -1175,6 +1175,74 @@ int orc_blocks_trim(int32_t* stack, int32_t* top, int64_t capacity, int32_t* tab
   return ORC_OK;
 }
 
+/* Offload of quantized blocks [P3, "KV Cache Offloading: Moving Data Between
+ * GPU and CPU": inactive cache is moved to CPU memory and brought back when
+ * needed, limited by the link's bandwidth; "quantize first": quantized blocks
+ * cross the link in 2-4x fewer bytes]. A packed block is the block's slice
+ * of every plane of one layer, in the order k_codes, v_codes, k_scale,
+ * v_scale, k_zero, v_zero (planes the layout does not have take no bytes);
+ * block k of a pack starts at k * orc_block_pack_bytes. */
+static int64_t plane_block_bytes(const orc_layout* L, int plane) {
+  int64_t H = L->num_kv_heads, bs = L->block_size, d = L->head_dim;
+  int side = plane & 1;
+  int code = side_code(L, side), mode = side_mode(L, side);
+  if (plane < 2) return H * bs * row_bytes(L, side);
+  if (code == ORC_CODE_NONE16) return 0;
+  int64_t per = mode == ORC_CHANNEL_BLOCK ? H * d
+                : mode == ORC_GROUP_ASYM ? H * bs * (d / L->group_size)
+                                         : H * bs;
+  if (plane < 4) return per * 4;
+  return mode == ORC_GROUP_ASYM ? per : 0;
+}
+
+int64_t orc_block_pack_bytes(const orc_layout* L) {
+  if (check_layout(L)) return ORC_ERR_INVALID;
+  int64_t total = 0;
+  for (int p = 0; p < 6; ++p) total += plane_block_bytes(L, p);
+  return total;
+}
+
+static uint8_t* plane_base(const orc_cache* C, int plane) {
+  void* b[6] = {C->k_codes, C->v_codes, C->k_scale, C->v_scale, C->k_zero, C->v_zero};
+  return (uint8_t*)b[plane];
+}
+
+int orc_pack_blocks(const orc_layout* L, const orc_cache* C, const int32_t* ids, int32_t n,
+                    uint8_t* dst) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  int64_t pack = orc_block_pack_bytes(L);
+  for (int k = 0; k < n; ++k) {
+    if (ids[k] < 0 || ids[k] >= C->num_blocks) return ORC_ERR_INVALID;
+    uint8_t* out = dst + (int64_t)k * pack;
+    for (int p = 0; p < 6; ++p) {
+      int64_t per = plane_block_bytes(L, p);
+      if (!per) continue;
+      memcpy(out, plane_base(C, p) + (int64_t)ids[k] * per, (size_t)per);
+      out += per;
+    }
+  }
+  return ORC_OK;
+}
+
+int orc_unpack_blocks(const orc_layout* L, const orc_cache* C, const uint8_t* src,
+                      const int32_t* ids, int32_t n) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  int64_t pack = orc_block_pack_bytes(L);
+  for (int k = 0; k < n; ++k) {
+    if (ids[k] < 0 || ids[k] >= C->num_blocks) return ORC_ERR_INVALID;
+    const uint8_t* in = src + (int64_t)k * pack;
+    for (int p = 0; p < 6; ++p) {
+      int64_t per = plane_block_bytes(L, p);
+      if (!per) continue;
+      memcpy(plane_base(C, p) + (int64_t)ids[k] * per, in, (size_t)per);
+      in += per;
+    }
+  }
+  return ORC_OK;
+}
+
 /* Released sequences push their blocks back in batch order, each in logical
  * order. All or nothing when the pushes would overflow the stack. */
 int orc_blocks_release(int32_t* stack, int32_t* top, int64_t capacity,

@@ -112,6 +112,11 @@ int orc_blocks_release_shared(int32_t* stack, int32_t* top, int64_t capacity,
                               int32_t* lens_out, int32_t* status);
 int orc_copy_blocks(const orc_layout* L, const orc_cache* C, const int32_t* src,
                     const int32_t* dst, int32_t n);
+int64_t orc_block_pack_bytes(const orc_layout* L);
+int orc_pack_blocks(const orc_layout* L, const orc_cache* C, const int32_t* ids, int32_t n,
+                    uint8_t* dst);
+int orc_unpack_blocks(const orc_layout* L, const orc_cache* C, const uint8_t* src,
+                      const int32_t* ids, int32_t n);
 int orc_dequant_token(const orc_layout* L, const orc_cache* C, int side,
                       const int32_t* table_row, int32_t context_len,
                       int32_t stage_row, int32_t pos, int32_t head, float* out);

@@ -77,6 +77,9 @@ def _load():
         "orc_blocks_release_shared": (C.c_int, [vp, vp, i64, vp, vp, i32, vp, vp, i32, i32,
                                                 vp, vp]),
         "orc_copy_blocks": (C.c_int, [vp, vp, vp, vp, i32]),
+        "orc_block_pack_bytes": (i64, [vp]),
+        "orc_pack_blocks": (C.c_int, [vp, vp, vp, i32, vp]),
+        "orc_unpack_blocks": (C.c_int, [vp, vp, vp, vp, i32]),
         "orc_blocks_reserve": (C.c_int, [vp, vp, i64, vp, i32, vp, vp, i32, i32,
                                           vp, vp, vp]),
         "orc_blocks_release": (C.c_int, [vp, vp, i64, vp, i32, vp, vp, i32, i32,
@@ -424,3 +427,26 @@ def blocks_trim(stack, top, tables, lens, window, sink, bs):
                              _ptr(lens), window, sink, lens.size, bs, _ptr(status))
     assert rc == 0
     return int(status[0])
+
+
+def block_pack_bytes(L):
+    return int(lib.orc_block_pack_bytes(C.byref(L)))
+
+
+def pack_blocks(L, cache, ids):
+    ids = np.ascontiguousarray(ids, np.int32)
+    out = np.zeros(block_pack_bytes(L) * ids.size, np.uint8)
+    cs = cache.struct()
+    rc = lib.orc_pack_blocks(C.byref(L), C.byref(cs), _ptr(ids), ids.size, _ptr(out))
+    if rc:
+        raise ValueError(f"orc_pack_blocks: {rc}")
+    return out
+
+
+def unpack_blocks(L, cache, packed, ids):
+    ids = np.ascontiguousarray(ids, np.int32)
+    packed = np.ascontiguousarray(packed, np.uint8)
+    cs = cache.struct()
+    rc = lib.orc_unpack_blocks(C.byref(L), C.byref(cs), _ptr(packed), _ptr(ids), ids.size)
+    if rc:
+        raise ValueError(f"orc_unpack_blocks: {rc}")
