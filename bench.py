@@ -90,6 +90,10 @@ def parse():
     ap.add_argument("--flush-write", action="store_true",
                     help="flush by writing the scratch instead of reading it (the "
                          "dirty lines are then written back during the next step)")
+    ap.add_argument("--offload-blocks", type=int, default=0,
+                    help="only time packing this many blocks of the workload's layout, the "
+                         "copy of the pack to pinned host memory and back, and the unpack, "
+                         "then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (reference kernel for "
                          "the FETCH_SIZE / WRITE_SIZE counter scale) and exit")
@@ -108,6 +112,58 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "repeats": 3}))
+
+
+def offload_bench(args):
+    """Offload of quantized blocks: kvq_pack_blocks into a device buffer,
+    that buffer to pinned host memory and back (hipMemcpyAsync through torch),
+    kvq_unpack_blocks into other blocks; one JSON line with each rate and the
+    packed bytes per block against the 16-bit cache's."""
+    import quantized_paged_kv_append_amd as kq
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.workload)
+    LL = kq.make_layout(w.num_kv_heads, w.head_dim, w.block_size, w.k_code, w.v_code,
+                        w.k_mode, w.v_mode, w.group_size, w.torch_dtype)
+    L16 = kq.make_layout(w.num_kv_heads, w.head_dim, w.block_size, "none16", "none16",
+                         "token_sym", "token_sym", 0, w.torch_dtype)
+    n = args.offload_blocks
+    cache = kq.PagedCache(LL, 2 * n, w.batch if w.k_mode == "channel_block" else 0, device=dev)
+    for t in cache.planes.values():
+        if t is not None:
+            t.random_(0, 256)   # the bytes' values do not matter for the copies
+    per = kq.kvq_block_pack_bytes(LL)
+    ids = torch.randperm(n, device=dev).to(torch.int32)
+    back_ids = (ids + n).to(torch.int32)
+    packed = torch.empty(per * n, dtype=torch.uint8, device=dev)
+    host = torch.empty(per * n, dtype=torch.uint8, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    times = {"pack": [], "d2h": [], "h2d": [], "unpack": []}
+    for it in range(args.warmup + args.steps):
+        ev[0].record(stream)
+        kq.kvq_pack_blocks(LL, cache, ids, packed)
+        ev[1].record(stream)
+        host.copy_(packed, non_blocking=True)
+        ev[2].record(stream)
+        packed.copy_(host, non_blocking=True)
+        ev[3].record(stream)
+        kq.kvq_unpack_blocks(LL, cache, packed, back_ids)
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            for k, (a, b) in zip(times, zip(ev[:-1], ev[1:])):
+                times[k].append(a.elapsed_time(b))
+    nbytes = per * n
+    rate = {k: round(nbytes / (float(np.median(v)) / 1e3) / 1e9, 2) for k, v in times.items()}
+    print(json.dumps({"metric": "quantized block offload GB/s (pack, to host, from host, unpack)",
+                      "value": rate["d2h"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "higher_is_better": True,
+                      "config": {"workload": w.name, "blocks": n, "k_code": w.k_code,
+                                 "k_mode": w.k_mode, "block_size": w.block_size},
+                      "rates_GBps": rate, "bytes_per_block": per,
+                      "bytes_per_block_16bit": kq.kvq_block_pack_bytes(L16),
+                      "link_bytes_ratio_vs_16bit": round(kq.kvq_block_pack_bytes(L16) / per, 3),
+                      "ms_median": {k: round(float(np.median(v)), 4) for k, v in times.items()}}))
 
 
 def kv_bytes_per_token_head(w):
@@ -139,6 +195,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.offload_blocks:
+        offload_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "

@@ -38,6 +38,12 @@
  *                         physical blocks ("KV Cache Optimization: Strategies
  *                         ...", section "How vLLM Implements KV Cache
  *                         Optimization").
+ *   kvq_pack_blocks / kvq_unpack_blocks
+ *                         quantized blocks packed for offload to host memory
+ *                         and back ("KV Cache Optimization: Strategies ...",
+ *                         section "KV Cache Offloading ...").
+ *   kvq_blocks_trim       blocks a sliding window no longer reaches go back
+ *                         to the pool (section "Cache Eviction ...").
  *   kvq_blocks_fork / kvq_blocks_reserve_shared / kvq_blocks_release_shared /
  *   kvq_copy_blocks       prefix sharing: reference-counted blocks, copy on
  *                         write of a shared, partly filled block (same
@@ -489,6 +495,32 @@ kvq_status kvq_blocks_release_shared(int32_t* free_stack, int32_t* free_top,
 kvq_status kvq_copy_blocks(const kvq_layout* layout, const kvq_cache* cache,
                            const int32_t* src_ids, const int32_t* dst_ids,
                            const int32_t* count, int32_t max_pairs, void* stream);
+
+/* ---- block offload ("KV Cache Optimization: Strategies ...", section "KV
+ * Cache Offloading: Moving Data Between GPU and CPU": inactive cache moves to
+ * CPU memory and back, bounded by the link; quantized blocks cross it in 2-4x
+ * fewer bytes than 16-bit ones). A packed block is the block's slice of every
+ * plane of one layer, in the order k_codes, v_codes, k_scale, v_scale,
+ * k_zero, v_zero (absent planes take no bytes; k_stage is not part of it);
+ * block k of a pack starts at k * kvq_block_pack_bytes(layout). The pack
+ * lives in device memory, or in host memory the device can address
+ * (hipHostMalloc); the caller moves it across the link (hipMemcpyAsync). */
+
+/* Bytes of one packed block of this layout = kvq_bytes_per_token(layout, 1, 1)
+ * * block_size (per-channel key scales are per block), or a negative
+ * kvq_status. Host only. */
+int64_t kvq_block_pack_bytes(const kvq_layout* layout);
+
+/* Pack blocks ids[0 .. n) (device int32) of one layer into dst, 16-byte
+ * aligned, n * kvq_block_pack_bytes bytes. Ids outside [0, num_blocks) are
+ * skipped (their slot in dst is left as it was). */
+kvq_status kvq_pack_blocks(const kvq_layout* layout, const kvq_cache* cache,
+                           const int32_t* ids, int32_t n, void* dst, void* stream);
+
+/* The inverse: write packed block k of src into block ids[k] of one layer. */
+kvq_status kvq_unpack_blocks(const kvq_layout* layout, const kvq_cache* cache,
+                             const void* src, const int32_t* ids, int32_t n,
+                             void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -600,4 +600,63 @@ kvq_status kvq_copy_blocks(const kvq_layout* L, const kvq_cache* C, const int32_
                                             C->num_blocks, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// The six planes of one layer (k_codes, v_codes, k_scale, v_scale, k_zero,
+// v_zero) and their bytes per block.
+kvq_status block_planes(const kvq_layout* L, const kvq_cache* C, uint8_t* base[6],
+                        int64_t per_block[6]) {
+  int64_t planes[7];
+  kvq_status s = kvq_cache_plane_bytes(L, C->num_blocks, C->max_seqs, planes);
+  if (s != KVQ_OK) return s;
+  uint8_t* const b[6] = {static_cast<uint8_t*>(C->k_codes), static_cast<uint8_t*>(C->v_codes),
+                         reinterpret_cast<uint8_t*>(C->k_scale),
+                         reinterpret_cast<uint8_t*>(C->v_scale), C->k_zero, C->v_zero};
+  for (int i = 0; i < 6; ++i) {
+    base[i] = b[i];
+    per_block[i] = b[i] ? planes[i] / C->num_blocks : 0;
+  }
+  return KVQ_OK;
+}
+
+kvq_status pack_common(const kvq_layout* L, const kvq_cache* C, const int32_t* ids, int32_t n,
+                       void* packed, bool pack, void* stream) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  s = check_cache(L, C);
+  if (s != KVQ_OK) return s;
+  if (n < 0 || n > 65535 * 1024) return KVQ_ERR_INVALID_ARGUMENT;
+  if (n == 0) return KVQ_OK;
+  if (!ids || !packed || !aligned16(packed)) return KVQ_ERR_INVALID_ARGUMENT;
+  uint8_t* base[6];
+  int64_t per[6];
+  s = block_planes(L, C, base, per);
+  if (s != KVQ_OK) return s;
+  return hip_status(kvq::launch_pack_blocks(base, per, ids, n, static_cast<uint8_t*>(packed),
+                                            pack, C->num_blocks,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int64_t kvq_block_pack_bytes(const kvq_layout* L) {
+  kvq_status s = kvq_layout_check(L);
+  if (s != KVQ_OK) return s;
+  int64_t planes[7];
+  kvq_cache_plane_bytes(L, 1, 0, planes);
+  int64_t total = 0;
+  for (int i = 0; i < 6; ++i) total += planes[i];
+  return total;
+}
+
+kvq_status kvq_pack_blocks(const kvq_layout* L, const kvq_cache* C, const int32_t* ids,
+                           int32_t n, void* dst, void* stream) {
+  return pack_common(L, C, ids, n, dst, true, stream);
+}
+
+kvq_status kvq_unpack_blocks(const kvq_layout* L, const kvq_cache* C, const void* src,
+                             const int32_t* ids, int32_t n, void* stream) {
+  return pack_common(L, C, ids, n, const_cast<void*>(src), false, stream);
+}
+
 }  // extern "C"

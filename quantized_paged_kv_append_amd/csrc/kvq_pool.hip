@@ -458,6 +458,34 @@ __global__ __launch_bounds__(kThreads) void trim_kernel(int32_t* stack, int32_t*
   }
 }
 
+// Pack / unpack of blocks for offload: workgroup (block k, plane), 16-byte
+// vectors between the plane's slice of block ids[k] and its place in the
+// pack (block k at k * pack_bytes, planes in order).
+struct PackPlanes {
+  uint8_t* base[6];
+  int64_t per_block[6];   // 0: plane unused
+  int64_t offset[6];      // the plane's offset inside a packed block
+  int64_t pack_bytes;
+};
+
+template <bool PACK>
+__global__ __launch_bounds__(256) void pack_kernel(PackPlanes pp, const int32_t* ids,
+                                                   uint8_t* packed, int64_t num_blocks) {
+  const int k = blockIdx.x, plane = blockIdx.y;
+  const int64_t per = pp.per_block[plane];
+  if (per == 0) return;
+  const int32_t id = ids[k];
+  if (id < 0 || id >= num_blocks) return;
+  u32x4* cache = reinterpret_cast<u32x4*>(pp.base[plane] + id * per);
+  u32x4* pk = reinterpret_cast<u32x4*>(packed + k * pp.pack_bytes + pp.offset[plane]);
+  for (int64_t i = threadIdx.x; i < per / 16; i += blockDim.x) {
+    if (PACK)
+      pk[i] = cache[i];
+    else
+      cache[i] = pk[i];
+  }
+}
+
 // Copy of one layer's planes for each (src, dst) block pair: workgroup
 // (pair, plane), 16-byte vectors; pairs past *count are skipped.
 struct CopyPlanes {
@@ -566,6 +594,25 @@ hipError_t launch_copy_blocks(uint8_t* const base[6], const int64_t per_block[6]
     cp.per_block[i] = base[i] ? per_block[i] : 0;
   }
   copy_blocks_kernel<<<dim3(max_pairs, 6), 256, 0, stream>>>(cp, src, dst, count, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_blocks(uint8_t* const base[6], const int64_t per_block[6],
+                              const int32_t* ids, int32_t n, uint8_t* packed, bool pack,
+                              int64_t num_blocks, hipStream_t stream) {
+  PackPlanes pp;
+  int64_t off = 0;
+  for (int i = 0; i < 6; ++i) {
+    pp.base[i] = base[i];
+    pp.per_block[i] = base[i] ? per_block[i] : 0;
+    pp.offset[i] = off;
+    off += pp.per_block[i];
+  }
+  pp.pack_bytes = off;
+  if (pack)
+    pack_kernel<true><<<dim3(n, 6), 256, 0, stream>>>(pp, ids, packed, num_blocks);
+  else
+    pack_kernel<false><<<dim3(n, 6), 256, 0, stream>>>(pp, ids, packed, num_blocks);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // kvq_sharing.h -- host-side interface between the C ABI layer (kvq_api.cpp)
-// and the pool kernels for prefix sharing and window trimming (kvq_pool.hip).
+// and the pool kernels for prefix sharing, window trimming and block offload
+// (kvq_pool.hip).
 // Internal.
 #pragma once
 
@@ -35,5 +36,11 @@ hipError_t launch_blocks_trim(int32_t* stack, int32_t* top, int64_t capacity, in
                               int32_t max_blocks, const int32_t* lens, int32_t window,
                               int32_t sink, int32_t batch, int32_t bs, int32_t* status,
                               hipStream_t stream);
+
+// pack (pack = true) or unpack the six planes of blocks ids[0 .. n) to / from
+// `packed` (block k at k * sum(per_block), planes in order)
+hipError_t launch_pack_blocks(uint8_t* const base[6], const int64_t per_block[6],
+                              const int32_t* ids, int32_t n, uint8_t* packed, bool pack,
+                              int64_t num_blocks, hipStream_t stream);
 
 }  // namespace kvq

@@ -80,6 +80,9 @@ _SIGS = {
     "kvq_blocks_release_shared": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                          _vp, _vp, _vp]),
     "kvq_copy_blocks": (_i32, [_LP, _CP, _vp, _vp, _vp, _i32, _vp]),
+    "kvq_block_pack_bytes": (_i64, [_LP]),
+    "kvq_pack_blocks": (_i32, [_LP, _CP, _vp, _i32, _vp, _vp]),
+    "kvq_unpack_blocks": (_i32, [_LP, _CP, _vp, _vp, _i32, _vp]),
     "kvq_blocks_reserve": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32,
                                   _vp, _vp, _vp, _vp]),
     "kvq_blocks_release": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32,
@@ -307,3 +310,23 @@ def kvq_blocks_trim(free_stack, free_top, block_tables, context_lens, window, si
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), int(window), int(sink),
         context_lens.numel(), block_size, _ptr(status_flag), _stream(stream)))
+
+
+def kvq_block_pack_bytes(layout) -> int:
+    n = _lib.kvq_block_pack_bytes(C.byref(layout))
+    if n < 0:
+        raise KvqError("kvq_block_pack_bytes", n)
+    return n
+
+
+def kvq_pack_blocks(layout, cache: PagedCache, ids, dst, stream=None):
+    """Pack blocks ids (device int32) of one layer into dst (uint8 tensor)."""
+    _check("kvq_pack_blocks", _lib.kvq_pack_blocks(
+        C.byref(layout), C.byref(cache.struct), _ptr(ids), ids.numel(), _ptr(dst),
+        _stream(stream)))
+
+
+def kvq_unpack_blocks(layout, cache: PagedCache, src, ids, stream=None):
+    _check("kvq_unpack_blocks", _lib.kvq_unpack_blocks(
+        C.byref(layout), C.byref(cache.struct), _ptr(src), _ptr(ids), ids.numel(),
+        _stream(stream)))

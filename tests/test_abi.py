@@ -254,6 +254,25 @@ def test_sharing_calls_reject_bad_arguments_on_host():
         kq.KVQ_ERR_INVALID_ARGUMENT
 
 
+def test_block_pack_bytes_match_oracle():
+    from itertools import product
+    for code, mode, bs, d in product(["none16", "int8", "fp8", "int4"],
+                                     ["token_sym", "group_asym", "channel_block"], [16, 32],
+                                     [64, 128]):
+        if mode == "group_asym" and code != "int4":
+            continue
+        if mode == "channel_block" and code != "int8":
+            continue
+        vmode = "token_sym" if mode == "channel_block" else mode
+        L = kq.make_layout(4, d, bs, code, k_mode=mode, v_mode=vmode,
+                           group_size=32 if mode == "group_asym" else 0)
+        OL = ref.layout(4, d, bs, {"none16": 0, "int8": 1, "fp8": 2, "int4": 3}[code],
+                        None, {"token_sym": 0, "group_asym": 1, "channel_block": 2}[mode],
+                        {"token_sym": 0, "group_asym": 1}[vmode],
+                        32 if mode == "group_asym" else 0, ref.BF16)
+        assert kq.kvq_block_pack_bytes(L) == ref.block_pack_bytes(OL), (code, mode, bs, d)
+
+
 def test_pool_calls_reject_bad_arguments_on_host():
     lib = kq._lib
     p = C.c_void_p(1 << 21)
