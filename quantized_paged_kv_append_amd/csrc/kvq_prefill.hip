@@ -14,16 +14,17 @@ namespace {
 // are its last nq positions; query i (position L - nq + i) sees positions
 // 0 .. L - nq + i.
 //
-// The 16 MFMA columns of a wave are 16 consecutive (query, head) pairs
-// c = i G + r of one KV head g, a column tile: the G heads of a query are
-// adjacent, a tile spans 16 / G queries (or a query G / 16 tiles). A
-// workgroup takes one unit (sequence b, split j of S blocks, KV head g,
-// column tile ct); its four waves stream consecutive quarters of the split
-// through the decode's register ring and tile steps, with a causal limit
-// per lane (column), and merge their softmax states through LDS. Every block
-// a wave loads serves 16 columns; the units of one (b, j, g) are adjacent in
-// the grid, so their repeated block reads meet in L2. Each unit writes a
-// partial (m, l, acc) per column; prefill_reduce merges the splits.
+// The 16 MFMA columns of a tile are 16 consecutive (query, head) pairs
+// c = i G + r of one KV head g: the G heads of a query are adjacent, a tile
+// spans 16 / G queries (or a query G / 16 tiles). A wave serves one or two
+// tiles (each block it loads and converts then serves 16 or 32 columns), with
+// a causal limit (and window start) per lane and tile. A workgroup takes one
+// unit (sequence b, split j of S blocks, KV head g, group of up to four
+// waves' tiles); waves on the same tiles stream consecutive shares of the
+// split through the decode's register ring and tile steps and merge their
+// softmax states through LDS. The waves of a workgroup read the same blocks,
+// which meet in L1. Each unit writes a partial (m, l, acc) per column;
+// prefill_reduce merges the splits.
 // ---------------------------------------------------------------------------
 struct PrefillArgs {
   DecodeArgs a;
@@ -36,7 +37,10 @@ struct PrefillArgs {
   int32_t sink;     // ... and the first `sink` positions
 };
 
-template <int CODE, int MODE, int D, int BS>
+// NC: 16-column tiles per wave. With NC = 2 a block's codes are loaded and
+// converted once for 32 columns (per-channel keys keep NC = 1: their
+// per-block query folding needs the fp32 query of every column).
+template <int CODE, int MODE, int D, int BS, int NC>
 __global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_split_kernel(PrefillArgs pa) {
   constexpr int NCH = D / 32;
@@ -45,14 +49,16 @@ void prefill_split_kernel(PrefillArgs pa) {
   constexpr int NBUF = BS == 16 ? 3 : 2;  // blocks in the register ring
   constexpr bool KCH = MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM;
   constexpr bool RAW = CODE == KVQ_CODE_NONE16;
+  static_assert(!KCH || NC == 1, "per-channel keys take one column tile per wave");
   using TileT = typename std::conditional<RAW, TileRaw<D, BS>, Tile8<D, BS>>::type;
   __shared__ float red[kNW][NV + 2][kWave];
   const DecodeArgs& a = pa.a;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, jj = lane >> 4;
-  // unit (b, j, g, tile group); wave w serves column tile tg TW + w % TW and
-  // the (w / TW)-th of the 4 / TW shares of the split's blocks
-  const int ctg = (pa.CT + pa.TW - 1) / pa.TW;
+  // unit (b, j, g, tile group); wave w serves column tiles NC (tg TW + w % TW)
+  // .. + NC - 1 and the (w / TW)-th of the 4 / TW shares of the split's blocks
+  const int cts = (pa.CT + NC - 1) / NC;
+  const int ctg = (cts + pa.TW - 1) / pa.TW;
   int64_t u = blockIdx.x;
   const int tg = (int)(u % ctg);
   u /= ctg;
@@ -68,27 +74,29 @@ void prefill_split_kernel(PrefillArgs pa) {
   const int nblk = (L + BS - 1) / BS;
   const int s0 = j * pa.S;
   // workgroup-uniform exits: no split here, or no column in the tile group
-  if (s0 >= nblk || tg * pa.TW * 16 >= ncol) return;
+  if (s0 >= nblk || tg * pa.TW * NC * 16 >= ncol) return;
   const int nshare = kNW / pa.TW;
-  const int ct = tg * pa.TW + wave % pa.TW;
-  const int cbase = ct * 16;
-  const bool active = cbase < ncol;   // a tile past the columns only joins the merge
+  const int cbase = (tg * pa.TW + wave % pa.TW) * NC * 16;
+  const bool active = cbase < ncol;   // tiles past the columns only join the merge
 
-  // ---- columns: lane (r, jj) serves column c = cbase + r -------------------
-  const int c = cbase + r;
-  const bool valid = c < ncol;
-  const int qi = valid ? c / a.G : 0;
-  const int hq = g * a.G + (valid ? c % a.G : 0);
-  const int Lr = valid ? L - nq + qi + 1 : 0;                 // this column's limit
-  const int Lmin = L - nq + cbase / a.G + 1;                  // over the tile's columns
-  const int Lmax = active ? L - nq + (min(ncol, cbase + 16) - 1) / a.G + 1 : 0;
-  // sliding window with sinks: the lane's column sees t >= lo_r (and t < SK);
-  // lo_min / lo_max bound the window starts over the tile's columns
+  // ---- columns: lane (r, jj) serves columns cbase + 16 c + r, c < NC -------
+  int col[NC], Lr[NC], lo_r[NC];
+  bool valid[NC];
+  float cscore[NC];
   const int W = pa.window, SK = pa.window > 0 ? pa.sink : 0;
-  const int lo_r = W > 0 ? Lr - W : 0;
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    col[cc] = cbase + 16 * cc + r;
+    valid[cc] = col[cc] < ncol;
+    Lr[cc] = valid[cc] ? L - nq + col[cc] / a.G + 1 : 0;   // the column's limit
+    lo_r[cc] = W > 0 ? Lr[cc] - W : 0;                       // its window start
+  }
+  // bounds over the wave's columns
+  const int Lmin = L - nq + cbase / a.G + 1;
+  const int Lmax = active ? L - nq + (min(ncol, cbase + 16 * NC) - 1) / a.G + 1 : 0;
   const int lo_min = W > 0 ? Lmin - W : 0;
   const int lo_max = W > 0 ? Lmax - W : 0;
-  // the tile's visible blocks of the split (none past what any of its columns
+  // the visible blocks of the split (none past what any of the columns
   // sees): the sink blocks A = [s0, a_end) and the window's blocks
   // B = [bstart, s1), with nothing between them read
   const int s1 = min(min(s0 + pa.S, nblk), (Lmax + BS - 1) / BS);
@@ -102,41 +110,46 @@ void prefill_split_kernel(PrefillArgs pa) {
   const int share = (nV + nshare - 1) / nshare;
   const int x0 = (wave / pa.TW) * share, x1 = min(x0 + share, nV);
 
-  float qf[D / 4];
-  {
+  // ---- queries, each column pre-scaled by a power of two (as in decode) ---
+  float qf[D / 4];      // the last column's fp32 query (per-channel keys: NC = 1)
+  half8v qop[NC][NCH];  // fp16 operands (made later with per-channel keys)
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    const int qi = valid[cc] ? col[cc] / a.G : 0;
+    const int hq = g * a.G + (valid[cc] ? col[cc] % a.G : 0);
     const uint16_t* qp = a.q + ((int64_t)(q0 + qi) * a.Hq + hq) * D + jj * (D / 4);
     if (a.q_bf16)
       load_query<true, D>(qp, qf);
     else
       load_query<false, D>(qp, qf);
+    float qmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) qmax = fmaxf(qmax, fabsf(qf[e]));
+    qmax = colmax4(qmax);
+    int qe = qmax > 0.0f ? (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 : 0;
+    qe = max(qe, -126);
+    const float qdown = __uint_as_float((uint32_t)(127 - qe) << 23);
+    const float qup = __uint_as_float((uint32_t)(127 + qe) << 23);
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) qf[e] = valid[cc] ? qf[e] * qdown : 0.0f;
+    if constexpr (!KCH) {
+#pragma unroll
+      for (int k8 = 0; k8 < NCH; ++k8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qop[cc][k8][e] = (half_t)qf[8 * k8 + e];
+    }
+    cscore[cc] = valid[cc] ? qup * a.sm_log2 : 0.0f;
   }
-  float qmax = 0.0f;
-#pragma unroll
-  for (int e = 0; e < D / 4; ++e) qmax = fmaxf(qmax, fabsf(qf[e]));
-  qmax = colmax4(qmax);
-  int qe = qmax > 0.0f ? (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 : 0;
-  qe = max(qe, -126);
-  const float qdown = __uint_as_float((uint32_t)(127 - qe) << 23);
-  const float qup = __uint_as_float((uint32_t)(127 + qe) << 23);
-#pragma unroll
-  for (int e = 0; e < D / 4; ++e) qf[e] = valid ? qf[e] * qdown : 0.0f;
-  // fp16 query operand; with per-channel keys it is made where it is needed
-  // (the staged block), to keep registers for the ring
-  half8v qop[NCH];
-  if constexpr (!KCH) {
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qop[cc][e] = (half_t)qf[8 * cc + e];
-  }
-  const float cscore = valid ? qup * a.sm_log2 : 0.0f;
   const bool raw_bf16 = a.stage_bf16 != 0;
 
-  SoftmaxState<D> st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
+  SoftmaxState<D> st[NC];
 #pragma unroll
-  for (int cc = 0; cc < NPV; ++cc) st.acc[cc] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int cc = 0; cc < NC; ++cc) {
+    st[cc].m = -INFINITY;
+    st[cc].l = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NPV; ++k) st[cc].acc[k] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   if (x0 < x1) {
     // per-channel keys: a partly filled last block is read raw from stage row b
@@ -161,16 +174,20 @@ void prefill_split_kernel(PrefillArgs pa) {
     const int ra = min(max(wf0, b0), max(b1, b0));
     const int rb = min(max(iseen, ra), max(b1, ra));
     auto full_block = [&](const TileT& t, int i) {
-      if constexpr (RAW) {
 #pragma unroll
-        for (int nt = 0; nt < BS / 16; ++nt)
-          tile_step_raw<D, BS, false>(t, nt, i * BS + nt * 16, L, qop, cscore, jj, st, raw_bf16);
-      } else if constexpr (KCH) {
-        half8v qb[NCH], ql[NCH];
-        channel_query<D, BS>(t, xs, qf, lane, qb, ql);
-        full_block_step<CODE, D, BS, kKeyChannel>(t, i, L, qb, cscore, jj, st, ql);
-      } else {
-        full_block_step<CODE, D, BS>(t, i, L, qop, cscore, jj, st);
+      for (int cc = 0; cc < NC; ++cc) {
+        if constexpr (RAW) {
+#pragma unroll
+          for (int nt = 0; nt < BS / 16; ++nt)
+            tile_step_raw<D, BS, false>(t, nt, i * BS + nt * 16, L, qop[cc], cscore[cc], jj,
+                                        st[cc], raw_bf16);
+        } else if constexpr (KCH) {
+          half8v qb[NCH], ql[NCH];
+          channel_query<D, BS>(t, xs, qf, lane, qb, ql);
+          full_block_step<CODE, D, BS, kKeyChannel>(t, i, L, qb, cscore[cc], jj, st[cc], ql);
+        } else {
+          full_block_step<CODE, D, BS>(t, i, L, qop[cc], cscore[cc], jj, st[cc]);
+        }
       }
     };
     auto edge_block = [&](const TileT& t, int i) {
@@ -186,13 +203,13 @@ void prefill_split_kernel(PrefillArgs pa) {
             const uint16_t* sp =
                 a.k_stage + (((int64_t)b * a.H + g) * BS + nt * 16 + r) * D + jj * (D / 4);
 #pragma unroll
-            for (int cc = 0; cc < NCH; ++cc)
-              kraw[nt][cc] = *reinterpret_cast<const u32x4*>(sp + 8 * cc);
+            for (int k8 = 0; k8 < NCH; ++k8)
+              kraw[nt][k8] = *reinterpret_cast<const u32x4*>(sp + 8 * k8);
           }
 #pragma unroll
-          for (int cc = 0; cc < NCH; ++cc)
+          for (int k8 = 0; k8 < NCH; ++k8)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qb[cc][e] = (half_t)qf[8 * cc + e];
+            for (int e = 0; e < 8; ++e) qb[k8][e] = (half_t)qf[8 * k8 + e];
         }
       }
 #pragma unroll
@@ -203,34 +220,40 @@ void prefill_split_kernel(PrefillArgs pa) {
         if (pos0 >= Lmax || (W > 0 && pos0 >= SK && pos0 + 16 <= lo_min)) continue;
         const bool masked =
             pos0 + 16 > Lmin || (W > 0 && pos0 < lo_max && pos0 + 16 > SK);
-        if constexpr (RAW) {
-          if (masked)
-            tile_step_raw<D, BS, true>(t, nt, pos0, Lr, qop, cscore, jj, st, raw_bf16, L,
-                                       lo_r, SK);
-          else
-            tile_step_raw<D, BS, false>(t, nt, pos0, Lr, qop, cscore, jj, st, raw_bf16, L);
-        } else if constexpr (KCH) {
-          if (rawk) {   // qb holds the plain fp16 query here
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          if constexpr (RAW) {
             if (masked)
-              tile_step<CODE, D, BS, true, kKeyRaw>(t, nt, pos0, Lr, qb, cscore, jj, st,
-                                                    kraw[nt], raw_bf16, nullptr, L, lo_r, SK);
+              tile_step_raw<D, BS, true>(t, nt, pos0, Lr[cc], qop[cc], cscore[cc], jj, st[cc],
+                                         raw_bf16, L, lo_r[cc], SK);
             else
-              tile_step<CODE, D, BS, false, kKeyRaw>(t, nt, pos0, Lr, qb, cscore, jj, st,
-                                                     kraw[nt], raw_bf16, nullptr, L);
-          } else if (masked) {
-            tile_step<CODE, D, BS, true, kKeyChannel>(t, nt, pos0, Lr, qb, cscore, jj, st,
-                                                      nullptr, false, ql, L, lo_r, SK);
+              tile_step_raw<D, BS, false>(t, nt, pos0, Lr[cc], qop[cc], cscore[cc], jj, st[cc],
+                                          raw_bf16, L);
+          } else if constexpr (KCH) {
+            if (rawk) {   // qb holds the plain fp16 query here
+              if (masked)
+                tile_step<CODE, D, BS, true, kKeyRaw>(t, nt, pos0, Lr[cc], qb, cscore[cc], jj,
+                                                      st[cc], kraw[nt], raw_bf16, nullptr, L,
+                                                      lo_r[cc], SK);
+              else
+                tile_step<CODE, D, BS, false, kKeyRaw>(t, nt, pos0, Lr[cc], qb, cscore[cc], jj,
+                                                       st[cc], kraw[nt], raw_bf16, nullptr, L);
+            } else if (masked) {
+              tile_step<CODE, D, BS, true, kKeyChannel>(t, nt, pos0, Lr[cc], qb, cscore[cc], jj,
+                                                        st[cc], nullptr, false, ql, L, lo_r[cc],
+                                                        SK);
+            } else {
+              tile_step<CODE, D, BS, false, kKeyChannel>(t, nt, pos0, Lr[cc], qb, cscore[cc],
+                                                         jj, st[cc], nullptr, false, ql, L);
+            }
           } else {
-            tile_step<CODE, D, BS, false, kKeyChannel>(t, nt, pos0, Lr, qb, cscore, jj, st,
-                                                       nullptr, false, ql, L);
+            if (masked)
+              tile_step<CODE, D, BS, true>(t, nt, pos0, Lr[cc], qop[cc], cscore[cc], jj, st[cc],
+                                           nullptr, false, nullptr, L, lo_r[cc], SK);
+            else
+              tile_step<CODE, D, BS, false>(t, nt, pos0, Lr[cc], qop[cc], cscore[cc], jj,
+                                            st[cc], nullptr, false, nullptr, L);
           }
-        } else {
-          if (masked)
-            tile_step<CODE, D, BS, true>(t, nt, pos0, Lr, qop, cscore, jj, st, nullptr, false,
-                                         nullptr, L, lo_r, SK);
-          else
-            tile_step<CODE, D, BS, false>(t, nt, pos0, Lr, qop, cscore, jj, st, nullptr, false,
-                                          nullptr, L);
         }
       }
     };
@@ -262,43 +285,48 @@ void prefill_split_kernel(PrefillArgs pa) {
   }
 
   // ---- merge the waves' states, then write one partial per column ---------
-  const float lsum = colsum4(st.l);
-  __syncthreads();   // every wave is done with its LDS slice
+  // one column tile at a time through the same LDS area
 #pragma unroll
-  for (int cc = 0; cc < NPV; ++cc)
+  for (int cc = 0; cc < NC; ++cc) {
+    const float lsum = colsum4(st[cc].l);
+    __syncthreads();   // every wave is done with the LDS area
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][4 * cc + e][lane] = st.acc[cc][e];
-  red[wave][NV][lane] = st.m;
-  red[wave][NV + 1][lane] = lsum;
-  __syncthreads();
-  // waves w < TW merge the shares of their tile: waves w, w + TW, ...
-  if (wave >= pa.TW || !valid) return;
-  float M = -INFINITY;
-  for (int w = wave; w < kNW; w += pa.TW) M = fmaxf(M, red[w][NV][lane]);
-  float acc[NV], l = 0.0f;
+    for (int k = 0; k < NPV; ++k)
 #pragma unroll
-  for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
-  for (int w = wave; w < kNW; w += pa.TW) {
-    const float mw = red[w][NV][lane];
-    const float sc = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-    l += sc * red[w][NV + 1][lane];
+      for (int e = 0; e < 4; ++e) red[wave][4 * k + e][lane] = st[cc].acc[k][e];
+    red[wave][NV][lane] = st[cc].m;
+    red[wave][NV + 1][lane] = lsum;
+    __syncthreads();
+    // waves w < TW merge the shares of their columns: waves w, w + TW, ...
+    if (wave < pa.TW && valid[cc]) {
+      float M = -INFINITY;
+      for (int w = wave; w < kNW; w += pa.TW) M = fmaxf(M, red[w][NV][lane]);
+      float acc[NV], l = 0.0f;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] += sc * red[w][v][lane];
-  }
-  const int64_t pidx = (((int64_t)b * pa.J + j) * a.H + g) * (pa.CT * 16) + c;
-  if (jj == 0) *reinterpret_cast<float2*>(a.ws_ml + pidx * 2) = make_float2(M, l);
-  // acc[4 cc + e] holds output element (d/16) (4 jj + e) + cc of column c
-  float* dst = a.ws_acc + pidx * D + jj * (D / 4);
+      for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
+      for (int w = wave; w < kNW; w += pa.TW) {
+        const float mw = red[w][NV][lane];
+        const float sc = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        l += sc * red[w][NV + 1][lane];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if constexpr (NPV == 8) {
-      float4v lo = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
-      float4v hi = {acc[16 + e], acc[20 + e], acc[24 + e], acc[28 + e]};
-      *reinterpret_cast<float4v*>(dst + 8 * e) = lo;
-      *reinterpret_cast<float4v*>(dst + 8 * e + 4) = hi;
-    } else {
-      float4v v4 = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
-      *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
+        for (int v = 0; v < NV; ++v) acc[v] += sc * red[w][v][lane];
+      }
+      const int64_t pidx = (((int64_t)b * pa.J + j) * a.H + g) * (pa.CT * 16) + col[cc];
+      if (jj == 0) *reinterpret_cast<float2*>(a.ws_ml + pidx * 2) = make_float2(M, l);
+      // acc[4 k + e] holds output element (d/16) (4 jj + e) + k of the column
+      float* dst = a.ws_acc + pidx * D + jj * (D / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (NPV == 8) {
+          float4v lo = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
+          float4v hi = {acc[16 + e], acc[20 + e], acc[24 + e], acc[28 + e]};
+          *reinterpret_cast<float4v*>(dst + 8 * e) = lo;
+          *reinterpret_cast<float4v*>(dst + 8 * e + 4) = hi;
+        } else {
+          float4v v4 = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
+          *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
+        }
+      }
     }
   }
 }
@@ -373,22 +401,43 @@ __global__ __launch_bounds__(64) void prefill_reduce_kernel(PrefillReduceArgs a)
   }
 }
 
-template <int CODE, int MODE>
-hipError_t launch_prefill_shape(const PrefillArgs& pa, int d, int bs, int64_t units,
-                                hipStream_t stream) {
+template <int CODE, int MODE, int NC>
+hipError_t launch_prefill_nc(const PrefillArgs& pa, int d, int bs, int64_t units,
+                             hipStream_t stream) {
   const dim3 grid((unsigned)units);   // one workgroup per unit
   if (d == 128) {
     if (bs == 16)
-      prefill_split_kernel<CODE, MODE, 128, 16><<<grid, 64 * kNW, 0, stream>>>(pa);
+      prefill_split_kernel<CODE, MODE, 128, 16, NC><<<grid, 64 * kNW, 0, stream>>>(pa);
     else
-      prefill_split_kernel<CODE, MODE, 128, 32><<<grid, 64 * kNW, 0, stream>>>(pa);
+      prefill_split_kernel<CODE, MODE, 128, 32, NC><<<grid, 64 * kNW, 0, stream>>>(pa);
   } else {
     if (bs == 16)
-      prefill_split_kernel<CODE, MODE, 64, 16><<<grid, 64 * kNW, 0, stream>>>(pa);
+      prefill_split_kernel<CODE, MODE, 64, 16, NC><<<grid, 64 * kNW, 0, stream>>>(pa);
     else
-      prefill_split_kernel<CODE, MODE, 64, 32><<<grid, 64 * kNW, 0, stream>>>(pa);
+      prefill_split_kernel<CODE, MODE, 64, 32, NC><<<grid, 64 * kNW, 0, stream>>>(pa);
   }
   return hipGetLastError();
+}
+
+// Two column tiles per wave whenever there are two and the second set of
+// accumulators fits in registers next to the ring without spilling (d 64;
+// d 128 with 16-token blocks of 8-bit codes); per-channel keys: one.
+template <int CODE, int MODE>
+hipError_t launch_prefill_shape(PrefillArgs pa, int d, int bs, int64_t units_per_tg,
+                                hipStream_t stream) {
+  const bool fits = d == 64 || (bs == 16 && CODE != KVQ_CODE_NONE16);
+  const int nc = (MODE != KVQ_SCALE_CHANNEL_BLOCK_SYM && pa.CT >= 2 && fits) ? 2 : 1;
+  const int cts = (pa.CT + nc - 1) / nc;
+  // the column tiles of a split share a workgroup (one wave or pair of waves
+  // each), so that their reads of the same blocks meet in L1
+  pa.TW = cts >= 4 ? 4 : (cts >= 2 ? 2 : 1);
+  const int64_t units = units_per_tg * ((cts + pa.TW - 1) / pa.TW);
+  if constexpr (MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM) {
+    return launch_prefill_nc<CODE, MODE, 1>(pa, d, bs, units, stream);
+  } else {
+    if (nc == 2) return launch_prefill_nc<CODE, MODE, 2>(pa, d, bs, units, stream);
+    return launch_prefill_nc<CODE, MODE, 1>(pa, d, bs, units, stream);
+  }
 }
 
 }  // namespace
@@ -435,11 +484,8 @@ hipError_t launch_prefill(const PrefillPlan& pp, hipStream_t stream) {
   pa.CT = pp.col_tiles;
   pa.window = pp.window;
   pa.sink = pp.sink;
-  // the column tiles of a split share a workgroup (one tile per wave or
-  // pair of waves), so that their reads of the same blocks meet in L1
-  pa.TW = pp.col_tiles >= 4 ? 4 : (pp.col_tiles >= 2 ? 2 : 1);
-  const int64_t units = (int64_t)p.batch * pp.splits * p.num_kv_heads *
-                        ((pp.col_tiles + pa.TW - 1) / pa.TW);
+  pa.TW = 1;   // set per launch shape
+  const int64_t units = (int64_t)p.batch * pp.splits * p.num_kv_heads;
   const int d = p.head_dim, bs = p.block_size;
   hipError_t e;
   if (p.k_code == KVQ_CODE_NONE16)
