@@ -424,8 +424,11 @@ struct Tile4 {
   static constexpr int SG = MODE == KVQ_SCALE_GROUP_ASYM ? NS : 1;
   uint32_t k[NS];      // key bytes of token r for pairs 4j..4j+3
   uint32_t v[4];       // value bytes n r .. n r + n - 1 of tokens 4j + e
-  float sk[4 * SG];    // key scales of tokens 4j + e, index 4 group + e
-  float sv[4 * SG];    // value scales, same order
+  // The 4 SG scales of tokens 4j..4j+3 ([token][group]) are spread over the
+  // 16 lanes of row j: lane r holds entry r mod 4 SG, read by the others
+  // through a row broadcast.
+  float sk;            // key scale
+  float sv;            // value scale
   uint32_t zk;         // key zero points of token r, byte c = group c
   uint32_t zv[NS];     // value zero points of tokens 4j..4j+3 ([token][group] bytes)
 };
@@ -453,19 +456,13 @@ __device__ __forceinline__ void load_tile4(Tile4<D, MODE>& t, const DecodeArgs& 
     else
       t.v[e] = *reinterpret_cast<const uint16_t*>(vr);
   }
+  {
+    constexpr int SG = Tile4<D, MODE>::SG;
+    const int64_t f = (row0 + 4 * j) * SG + (r & (4 * SG - 1));
+    t.sk = a.k_scale[f];
+    t.sv = a.v_scale[f];
+  }
   if constexpr (MODE == KVQ_SCALE_GROUP_ASYM) {
-    // the planes hold [token][group]; the tile keeps [group][token]
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const float4v ks = *reinterpret_cast<const float4v*>(a.k_scale + (row0 + 4 * j) * NS + 4 * u);
-      const float4v vs = *reinterpret_cast<const float4v*>(a.v_scale + (row0 + 4 * j) * NS + 4 * u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int f = 4 * u + e, tok = f / NS, grp = f % NS;
-        t.sk[4 * grp + tok] = ks[e];
-        t.sv[4 * grp + tok] = vs[e];
-      }
-    }
     if constexpr (NS == 4) {
       t.zk = *reinterpret_cast<const uint32_t*>(a.k_zero + (row0 + r) * NS);
       const u32x4 z = *reinterpret_cast<const u32x4*>(a.v_zero + (row0 + 4 * j) * NS);
@@ -476,16 +473,78 @@ __device__ __forceinline__ void load_tile4(Tile4<D, MODE>& t, const DecodeArgs& 
       t.zv[0] = z.x; t.zv[1] = z.y;
     }
   } else {
-    const float4v ks = *reinterpret_cast<const float4v*>(a.k_scale + row0 + 4 * j);
-    const float4v vs = *reinterpret_cast<const float4v*>(a.v_scale + row0 + 4 * j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t.sk[e] = ks[e];
-      t.sv[e] = vs[e];
-    }
     t.zk = 0;
 #pragma unroll
     for (int u = 0; u < NS; ++u) t.zv[u] = 0;
+  }
+}
+
+// Lane F of the caller's row of 16 lanes, for every lane of the row (DPP
+// row_newbcast). The compiler folds the move into a following multiply.
+template <int F>
+__device__ __forceinline__ float row_bcast(float x) {
+  static_assert(F >= 0 && F < 16, "a lane within the row");
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + F, 0xF, 0xF, true));
+}
+
+// Group combination of the 4-bit asymmetric scores: for each token e of the
+// lane, v_e = sum over groups c of S_c[e] times the key scale of (token e,
+// group c), which lane NS e + c of the row holds, as one multiply and NS - 1
+// multiply-accumulates with a row-broadcast operand (the compiler folds a DPP
+// move into a multiply but not into v_fmac). The block reads the score MFMA
+// results and a DPP source, hazards the compiler does not track through
+// inline assembly, so it opens with 24 wait states: more than an XDL result
+// read needs after a 16-pass MFMA and more than a DPP read after a VALU write.
+#define KVQ_ROWB(F) " row_newbcast:" #F " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+__device__ __forceinline__ void combine_groups(const float4v* S, float sk, float* v,
+                                               std::integral_constant<int, 4>) {
+  asm("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+      "v_mul_f32_dpp %0, %4, %5" KVQ_ROWB(0)
+      "v_mul_f32_dpp %1, %4, %6" KVQ_ROWB(4)
+      "v_mul_f32_dpp %2, %4, %7" KVQ_ROWB(8)
+      "v_mul_f32_dpp %3, %4, %8" KVQ_ROWB(12)
+      "v_fmac_f32_dpp %0, %4, %9" KVQ_ROWB(1)
+      "v_fmac_f32_dpp %1, %4, %10" KVQ_ROWB(5)
+      "v_fmac_f32_dpp %2, %4, %11" KVQ_ROWB(9)
+      "v_fmac_f32_dpp %3, %4, %12" KVQ_ROWB(13)
+      "v_fmac_f32_dpp %0, %4, %13" KVQ_ROWB(2)
+      "v_fmac_f32_dpp %1, %4, %14" KVQ_ROWB(6)
+      "v_fmac_f32_dpp %2, %4, %15" KVQ_ROWB(10)
+      "v_fmac_f32_dpp %3, %4, %16" KVQ_ROWB(14)
+      "v_fmac_f32_dpp %0, %4, %17" KVQ_ROWB(3)
+      "v_fmac_f32_dpp %1, %4, %18" KVQ_ROWB(7)
+      "v_fmac_f32_dpp %2, %4, %19" KVQ_ROWB(11)
+      "v_fmac_f32_dpp %3, %4, %20" KVQ_ROWB(15)
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(sk), "v"(S[0][0]), "v"(S[0][1]), "v"(S[0][2]), "v"(S[0][3]),
+        "v"(S[1][0]), "v"(S[1][1]), "v"(S[1][2]), "v"(S[1][3]),
+        "v"(S[2][0]), "v"(S[2][1]), "v"(S[2][2]), "v"(S[2][3]),
+        "v"(S[3][0]), "v"(S[3][1]), "v"(S[3][2]), "v"(S[3][3]));
+}
+__device__ __forceinline__ void combine_groups(const float4v* S, float sk, float* v,
+                                               std::integral_constant<int, 2>) {
+  asm("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+      "v_mul_f32_dpp %0, %4, %5" KVQ_ROWB(0)
+      "v_mul_f32_dpp %1, %4, %6" KVQ_ROWB(2)
+      "v_mul_f32_dpp %2, %4, %7" KVQ_ROWB(4)
+      "v_mul_f32_dpp %3, %4, %8" KVQ_ROWB(6)
+      "v_fmac_f32_dpp %0, %4, %9" KVQ_ROWB(1)
+      "v_fmac_f32_dpp %1, %4, %10" KVQ_ROWB(3)
+      "v_fmac_f32_dpp %2, %4, %11" KVQ_ROWB(5)
+      "v_fmac_f32_dpp %3, %4, %12" KVQ_ROWB(7)
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(sk), "v"(S[0][0]), "v"(S[0][1]), "v"(S[0][2]), "v"(S[0][3]),
+        "v"(S[1][0]), "v"(S[1][1]), "v"(S[1][2]), "v"(S[1][3]));
+}
+#undef KVQ_ROWB
+
+// f(std::integral_constant<int, I>) for I = B .. E - 1, in order.
+template <int B, int E, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
@@ -565,18 +624,20 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
   bool ok[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) ok[e] = !tail || pos0 + 4 * j + e < L;
-  float s[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v = 0.0f;
-    if constexpr (ASYM) {
-#pragma unroll
-      for (int c = 0; c < NS; ++c) v = __builtin_fmaf(S[c][e], t.sk[4 * c + e], v);
-    } else {
-      v = S[0][e] * t.sk[e];
-    }
-    s[e] = ok[e] ? v * cscore : -INFINITY;
+  // score of token 4j + e: sum over groups c of S[c][e] times the key scale
+  // of (token e, group c), held by lane SG e + c of the row
+  constexpr int SG = Tile4<D, MODE>::SG;
+  float v[4], s[4];
+  if constexpr (ASYM) {
+    combine_groups(S, t.sk, v, std::integral_constant<int, NS>{});
+  } else {
+    static_for<0, 4>([&](auto E) {
+      constexpr int e = decltype(E)::value;
+      v[e] = row_bcast<e>(t.sk) * S[0][e];
+    });
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[e] = ok[e] ? v[e] * cscore : -INFINITY;
   const float mt = colmax4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
   const float mn = fmaxf(st.m, mt);
   const float msafe = mn == -INFINITY ? 0.0f : mn;
@@ -605,11 +666,13 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
       Z[1] = __builtin_amdgcn_perm(t.zv[1], t.zv[0], 0x07050301u);
     }
   }
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
+  static_for<0, NS>([&](auto I) {
+    constexpr int i = decltype(I)::value;
     float pv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = ok[e] ? p[e] * t.sv[ASYM ? 4 * i + e : e] : 0.0f;
+    static_for<0, 4>([&](auto E) {
+      constexpr int e = decltype(E)::value;
+      pv[e] = ok[e] ? row_bcast<SG * e + (ASYM ? i : 0)>(t.sv) * p[e] : 0.0f;
+    });
     half4v pop;
     pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
     uint32_t Gi = G[i];
@@ -628,7 +691,7 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
     va1[0] = y02[0]; va1[1] = y02[1]; va1[2] = y13[0]; va1[3] = y13[1];
     st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va0, pop, st.acc[2 * i], 0, 0, 0);
     st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(va1, pop, st.acc[2 * i + 1], 0, 0, 0);
-  }
+  });
 }
 
 // Query operand for 4-bit keys: chunk c holds elements 32 c + 8 j + perm8[p]
