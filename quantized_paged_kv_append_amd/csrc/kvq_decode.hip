@@ -569,19 +569,25 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
 // registers by the caller, so that the and-or is one instruction (a VOP3
 // encoding takes no two literal constants on gfx9).
 template <int SHIFT>
+__device__ __forceinline__ uint32_t nib2u(uint32_t g, uint32_t m, uint32_t o) {
+  return ((g >> SHIFT) & m) | o;
+}
+template <int SHIFT>
 __device__ __forceinline__ half2v nib2(uint32_t g, uint32_t m, uint32_t o) {
-  return __builtin_bit_cast(half2v, ((g >> SHIFT) & m) | o);
+  return __builtin_bit_cast(half2v, nib2u<SHIFT>(g, m, o));
 }
 
 // Register-resident constants of the 4-bit conversions.
 struct Nib4Consts {
   uint32_t m;    // 0x000F000F
   uint32_t o;    // 0x64006400
-  uint32_t m64;  // 0x64646464, the fp16 exponent byte for v_perm
+  uint32_t m64;  // 0x64646464, the fp16 exponent byte of 1024 + x for v_perm
+  uint32_t e4;   // 0xE4E4E4E4, the same for -(1024 + x)
+  uint32_t nb;   // 0xE408E408, the fp16 pair -(1024 + 8)
 };
 __device__ __forceinline__ Nib4Consts nib4_consts() {
-  Nib4Consts k{0x000F000Fu, 0x64006400u, 0x64646464u};
-  asm volatile("" : "+v"(k.m), "+v"(k.o), "+v"(k.m64));
+  Nib4Consts k{0x000F000Fu, 0x64006400u, 0x64646464u, 0xE4E4E4E4u, 0xE408E408u};
+  asm volatile("" : "+v"(k.m), "+v"(k.o), "+v"(k.m64), "+v"(k.e4), "+v"(k.nb));
   return k;
 }
 
@@ -675,22 +681,29 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
     });
     half4v pop;
     pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
+    // The value operands are the raw codes 1024 + n; a second product with
+    // -(1024 + z) (zero point, or 8 for the symmetric offset) on the same
+    // accumulator removes the offset. Both are exact in fp16 and the two
+    // terms cancel in the fp32 accumulator within the tile, which replaces
+    // four fp16 subtractions per group with one more MFMA per output tile.
     uint32_t Gi = G[i];
-    half2v b02, b13;
-    if constexpr (ASYM) {  // fp16 pairs 1024 + z: bytes 0, 2 and bytes 1, 3 of Z[i]
-      b02 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kc.m64, Z[i], 0x04020400u));
-      b13 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kc.m64, Z[i], 0x04030401u));
+    half4v corr;  // -(1024 + z) of the tokens in pop's order
+    if constexpr (ASYM) {
+      const uint32_t c02 = __builtin_amdgcn_perm(kc.e4, Z[i], 0x04020400u);
+      const uint32_t c13 = __builtin_amdgcn_perm(kc.e4, Z[i], 0x04030401u);
+      corr = __builtin_bit_cast(half4v, (u32x2){c02, c13});
     } else {
       Gi ^= 0x88888888u;
-      b02 = b13 = __builtin_bit_cast(half2v, 0x64086408u);
+      corr = __builtin_bit_cast(half4v, (u32x2){kc.nb, kc.nb});
     }
-    const half2v x02 = nib2<0>(Gi, kc.m, kc.o) - b02, x13 = nib2<8>(Gi, kc.m, kc.o) - b13;
-    const half2v y02 = nib2<4>(Gi, kc.m, kc.o) - b02, y13 = nib2<12>(Gi, kc.m, kc.o) - b13;
-    half4v va0, va1;
-    va0[0] = x02[0]; va0[1] = x02[1]; va0[2] = x13[0]; va0[3] = x13[1];
-    va1[0] = y02[0]; va1[1] = y02[1]; va1[2] = y13[0]; va1[3] = y13[1];
+    const half4v va0 = __builtin_bit_cast(
+        half4v, (u32x2){nib2u<0>(Gi, kc.m, kc.o), nib2u<8>(Gi, kc.m, kc.o)});
+    const half4v va1 = __builtin_bit_cast(
+        half4v, (u32x2){nib2u<4>(Gi, kc.m, kc.o), nib2u<12>(Gi, kc.m, kc.o)});
     st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va0, pop, st.acc[2 * i], 0, 0, 0);
     st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(va1, pop, st.acc[2 * i + 1], 0, 0, 0);
+    st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(corr, pop, st.acc[2 * i], 0, 0, 0);
+    st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(corr, pop, st.acc[2 * i + 1], 0, 0, 0);
   });
 }
 
