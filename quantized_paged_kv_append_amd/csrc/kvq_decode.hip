@@ -433,43 +433,82 @@ struct Tile4 {
   uint32_t zv[NS];     // value zero points of tokens 4j..4j+3 ([token][group] bytes)
 };
 
-template <int D, int BS, int MODE>
-__device__ __forceinline__ void load_tile4(Tile4<D, MODE>& t, const DecodeArgs& a, int64_t bh,
-                                           int nt, int lane) {
+// x, known to be equal in every lane, held in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Byte offsets of a lane's loads within a tile's rows, fixed for the wave:
+// each load is a wave-uniform base (scalar registers) plus one of these, so
+// the loop spends no vector instructions on addresses.
+struct Lane4 {
+  uint32_t k;   // key bytes [j n, (j + 1) n) of token r, n = d / 8
+  uint32_t v;   // value bytes of token 4j (+ e rows for token 4j + e) at r d / 32
+  uint32_t s;   // scale entry r mod 4 SG of tokens 4j..4j+3
+  uint32_t zk;  // key zero points of token r
+  uint32_t zv;  // value zero points of tokens 4j..4j+3
+};
+template <int D, int MODE>
+__device__ __forceinline__ Lane4 lane4_offsets(int lane) {
   constexpr int NS = D / 32;
   constexpr int RB = D / 2;  // bytes per row
+  constexpr int SG = Tile4<D, MODE>::SG;
   const int r = lane & 15, j = lane >> 4;
-  const int64_t row0 = bh * BS + nt * 16;   // first token of the tile
-  const uint8_t* kr = a.k_codes + (row0 + r) * RB + j * (RB / 4);
+  Lane4 o;
+  o.k = (uint32_t)(r * RB + j * (RB / 4));
+  o.v = (uint32_t)(4 * j * RB + r * (RB / 16));
+  o.s = (uint32_t)(4 * (4 * j * SG + (r & (4 * SG - 1))));
+  o.zk = (uint32_t)(r * NS);
+  o.zv = (uint32_t)(4 * j * NS);
+  return o;
+}
+
+// Buffer resource over `base`: raw (untyped) loads at 32-bit byte offsets;
+// the record count only bounds the offsets, which stay within a tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+template <int D, int BS, int MODE>
+__device__ __forceinline__ void load_tile4(Tile4<D, MODE>& t, const DecodeArgs& a, int64_t bh,
+                                           int nt, const Lane4& o) {
+  constexpr int NS = D / 32;
+  constexpr int RB = D / 2;  // bytes per row
+  constexpr int SG = Tile4<D, MODE>::SG;
+  // first token of the tile: wave-uniform, kept in scalar registers so that
+  // each plane's buffer resource is scalar and every load is a buffer load
+  // at the lane's fixed 32-bit offset
+  const int64_t row0 = uniform64(bh * BS + nt * 16);
+  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(a.k_codes + row0 * RB);
+  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v_codes + row0 * RB);
   if constexpr (NS == 4) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(kr);
+    const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 0, 0));
     t.k[0] = w.x; t.k[1] = w.y; t.k[2] = w.z; t.k[3] = w.w;
   } else {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(kr);
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(kr, o.k, 0, 0));
     t.k[0] = w.x; t.k[1] = w.y;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint8_t* vr = a.v_codes + (row0 + 4 * j + e) * RB + r * (RB / 16);
     if constexpr (NS == 4)
-      t.v[e] = *reinterpret_cast<const uint32_t*>(vr);
+      t.v[e] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.v + e * RB, 0, 0);
     else
-      t.v[e] = *reinterpret_cast<const uint16_t*>(vr);
+      t.v[e] = __builtin_amdgcn_raw_buffer_load_b16(vr, o.v + e * RB, 0, 0);
   }
-  {
-    constexpr int SG = Tile4<D, MODE>::SG;
-    const int64_t f = (row0 + 4 * j) * SG + (r & (4 * SG - 1));
-    t.sk = a.k_scale[f];
-    t.sv = a.v_scale[f];
-  }
+  t.sk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(a.k_scale + row0 * SG), o.s, 0, 0));
+  t.sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(a.v_scale + row0 * SG), o.s, 0, 0));
   if constexpr (MODE == KVQ_SCALE_GROUP_ASYM) {
+    const __amdgpu_buffer_rsrc_t zkr = tile_rsrc(a.k_zero + row0 * NS);
+    const __amdgpu_buffer_rsrc_t zvr = tile_rsrc(a.v_zero + row0 * NS);
     if constexpr (NS == 4) {
-      t.zk = *reinterpret_cast<const uint32_t*>(a.k_zero + (row0 + r) * NS);
-      const u32x4 z = *reinterpret_cast<const u32x4*>(a.v_zero + (row0 + 4 * j) * NS);
+      t.zk = __builtin_amdgcn_raw_buffer_load_b32(zkr, o.zk, 0, 0);
+      const u32x4 z = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zvr, o.zv, 0, 0));
       t.zv[0] = z.x; t.zv[1] = z.y; t.zv[2] = z.z; t.zv[3] = z.w;
     } else {
-      t.zk = *reinterpret_cast<const uint16_t*>(a.k_zero + (row0 + r) * NS);
-      const u32x2 z = *reinterpret_cast<const u32x2*>(a.v_zero + (row0 + 4 * j) * NS);
+      t.zk = __builtin_amdgcn_raw_buffer_load_b16(zkr, o.zk, 0, 0);
+      const u32x2 z = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(zvr, o.zv, 0, 0));
       t.zv[0] = z.x; t.zv[1] = z.y;
     }
   } else {
@@ -767,6 +806,7 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   const int t1 = min(i1 * TPB, (L + 15) / 16);   // tiles holding tokens < L
   const int tfull = min(t1, L / 16);               // tiles wholly below L
   const int tlast = t1 - 1;
+  const Lane4 lo4 = lane4_offsets<D, MODE>(lane);
   auto load = [&](Tile4<D, MODE>& t, int tile) {
     // refills past the last tile read tile 0 of the shared block 0
     const bool past = tile > tlast;
@@ -774,7 +814,7 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
     const int32_t id = ids.id(past ? ids.base : ti / TPB);
     const bool ok = !past && id >= 0 && id < a.num_blocks;
     const int64_t bh = (int64_t)(ok ? id : 0) * a.H + g;
-    load_tile4<D, BS, MODE>(t, a, bh, ti % TPB, lane);
+    load_tile4<D, BS, MODE>(t, a, bh, ti % TPB, lo4);
   };
   Tile4<D, MODE> buf[NBUF];
 #pragma unroll
