@@ -630,14 +630,15 @@ __device__ __forceinline__ Nib4Consts nib4_consts() {
   return k;
 }
 
-template <int D, int MODE, bool TAIL>
-__device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, int L,
-                                           const half8v* qop, float cscore, int j,
-                                           SoftmaxState<D>& st, const Nib4Consts& kc) {
-  constexpr bool tail = TAIL;
+// Per-token scores of one tile before the column scale: the score MFMAs
+// (chunk c = slice c; one accumulator per 32-element group for asymmetric
+// codes) and, for token 4j + e, the sum over groups c of S[c][e] times the
+// key scale of (token e, group c), held by lane SG e + c of the row.
+template <int D, int MODE>
+__device__ __forceinline__ void tile4_scores(const Tile4<D, MODE>& t, const half8v* qop,
+                                             const Nib4Consts& kc, float* v) {
   constexpr int NS = D / 32;
   constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
-  // ---- key operands, chunk c = slice c -----------------------------------
   uint32_t g[4];
   if constexpr (NS == 4) {
     transpose4x4(t.k[0], t.k[1], t.k[2], t.k[3], g);
@@ -666,13 +667,6 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
     ka[4] = h2[0]; ka[5] = h2[1]; ka[6] = h3[0]; ka[7] = h3[1];
     S[ASYM ? c : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[c], S[ASYM ? c : 0], 0, 0, 0);
   }
-  bool ok[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) ok[e] = !tail || pos0 + 4 * j + e < L;
-  // score of token 4j + e: sum over groups c of S[c][e] times the key scale
-  // of (token e, group c), held by lane SG e + c of the row
-  constexpr int SG = Tile4<D, MODE>::SG;
-  float v[4], s[4];
   if constexpr (ASYM) {
     combine_groups(S, t.sk, v, std::integral_constant<int, NS>{});
   } else {
@@ -681,24 +675,14 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
       v[e] = row_bcast<e>(t.sk) * S[0][e];
     });
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) s[e] = ok[e] ? v[e] * cscore : -INFINITY;
-  const float mt = colmax4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-  const float mn = fmaxf(st.m, mt);
-  const float msafe = mn == -INFINITY ? 0.0f : mn;
-  if (__any(mn > st.m)) {
-    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
-    st.l *= alpha;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) st.acc[c] *= alpha;
-  }
-  st.m = mn;
-  float p[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) p[e] = ok[e] ? __builtin_amdgcn_exp2f(s[e] - msafe) : 0.0f;
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  // ---- value operands: byte i of the four tokens, tokens in order 0,2,1,3
-  uint32_t G[4], Z[4];
+}
+
+// Value bytes of a tile regrouped for the PV operands: G[i] (and the zero
+// points Z[i]) hold byte i of the four tokens 4j..4j+3.
+template <int D, int MODE>
+__device__ __forceinline__ void tile4_vbytes(const Tile4<D, MODE>& t, uint32_t* G, uint32_t* Z) {
+  constexpr int NS = D / 32;
+  constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
   if constexpr (NS == 4) {
     transpose4x4(t.v[0], t.v[1], t.v[2], t.v[3], G);
     if constexpr (ASYM) transpose4x4(t.zv[0], t.zv[1], t.zv[2], t.zv[3], Z);
@@ -711,6 +695,76 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
       Z[1] = __builtin_amdgcn_perm(t.zv[1], t.zv[0], 0x07050301u);
     }
   }
+}
+
+// PV operand words of group i of one tile, tokens in the order 0, 2, 1, 3:
+// x (low nibbles) and y (high nibbles) are the raw codes 1024 + n, c the
+// pairs -(1024 + z) (zero point, or 8 for the symmetric offset). A second
+// product with c on the same accumulator removes the offset: both are exact
+// in fp16 and the two terms cancel in the fp32 accumulator within the step,
+// which replaces four fp16 subtractions per group by one more MFMA per
+// output tile.
+struct VWords4 {
+  uint32_t x[2], y[2], c[2];
+};
+template <bool ASYM>
+__device__ __forceinline__ VWords4 vgroup_words(uint32_t Gi, uint32_t Zi, const Nib4Consts& kc) {
+  VWords4 w;
+  if constexpr (ASYM) {
+    w.c[0] = __builtin_amdgcn_perm(kc.e4, Zi, 0x04020400u);
+    w.c[1] = __builtin_amdgcn_perm(kc.e4, Zi, 0x04030401u);
+  } else {
+    Gi ^= 0x88888888u;
+    w.c[0] = w.c[1] = kc.nb;
+  }
+  w.x[0] = nib2u<0>(Gi, kc.m, kc.o);
+  w.x[1] = nib2u<8>(Gi, kc.m, kc.o);
+  w.y[0] = nib2u<4>(Gi, kc.m, kc.o);
+  w.y[1] = nib2u<12>(Gi, kc.m, kc.o);
+  return w;
+}
+
+// Online-softmax update for N scores per lane (already in log2 units, -inf
+// where masked): returns the max to subtract and rescales the state when a
+// column's max grows.
+template <int D, int N>
+__device__ __forceinline__ float softmax_update(const float* s, SoftmaxState<D>& st) {
+  float m = s[0];
+#pragma unroll
+  for (int e = 1; e < N; ++e) m = fmaxf(m, s[e]);
+  const float mn = fmaxf(st.m, colmax4(m));
+  const float msafe = mn == -INFINITY ? 0.0f : mn;
+  if (__any(mn > st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) st.acc[c] *= alpha;
+  }
+  st.m = mn;
+  return msafe;
+}
+
+template <int D, int MODE, bool TAIL>
+__device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, int L,
+                                           const half8v* qop, float cscore, int j,
+                                           SoftmaxState<D>& st, const Nib4Consts& kc) {
+  constexpr int NS = D / 32;
+  constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
+  constexpr int SG = Tile4<D, MODE>::SG;
+  float v[4], s[4];
+  tile4_scores(t, qop, kc, v);
+  bool ok[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ok[e] = !TAIL || pos0 + 4 * j + e < L;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[e] = ok[e] ? v[e] * cscore : -INFINITY;
+  const float msafe = softmax_update<D, 4>(s, st);
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = ok[e] ? __builtin_amdgcn_exp2f(s[e] - msafe) : 0.0f;
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  uint32_t G[4], Z[4] = {0u, 0u, 0u, 0u};
+  tile4_vbytes(t, G, Z);
   static_for<0, NS>([&](auto I) {
     constexpr int i = decltype(I)::value;
     float pv[4];
@@ -720,29 +774,61 @@ __device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, in
     });
     half4v pop;
     pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
-    // The value operands are the raw codes 1024 + n; a second product with
-    // -(1024 + z) (zero point, or 8 for the symmetric offset) on the same
-    // accumulator removes the offset. Both are exact in fp16 and the two
-    // terms cancel in the fp32 accumulator within the tile, which replaces
-    // four fp16 subtractions per group with one more MFMA per output tile.
-    uint32_t Gi = G[i];
-    half4v corr;  // -(1024 + z) of the tokens in pop's order
-    if constexpr (ASYM) {
-      const uint32_t c02 = __builtin_amdgcn_perm(kc.e4, Z[i], 0x04020400u);
-      const uint32_t c13 = __builtin_amdgcn_perm(kc.e4, Z[i], 0x04030401u);
-      corr = __builtin_bit_cast(half4v, (u32x2){c02, c13});
-    } else {
-      Gi ^= 0x88888888u;
-      corr = __builtin_bit_cast(half4v, (u32x2){kc.nb, kc.nb});
-    }
-    const half4v va0 = __builtin_bit_cast(
-        half4v, (u32x2){nib2u<0>(Gi, kc.m, kc.o), nib2u<8>(Gi, kc.m, kc.o)});
-    const half4v va1 = __builtin_bit_cast(
-        half4v, (u32x2){nib2u<4>(Gi, kc.m, kc.o), nib2u<12>(Gi, kc.m, kc.o)});
+    const VWords4 w = vgroup_words<ASYM>(G[i], Z[i], kc);
+    const half4v va0 = __builtin_bit_cast(half4v, (u32x2){w.x[0], w.x[1]});
+    const half4v va1 = __builtin_bit_cast(half4v, (u32x2){w.y[0], w.y[1]});
+    const half4v corr = __builtin_bit_cast(half4v, (u32x2){w.c[0], w.c[1]});
     st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va0, pop, st.acc[2 * i], 0, 0, 0);
     st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(va1, pop, st.acc[2 * i + 1], 0, 0, 0);
     st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(corr, pop, st.acc[2 * i], 0, 0, 0);
     st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(corr, pop, st.acc[2 * i + 1], 0, 0, 0);
+  });
+}
+
+// Two consecutive whole tiles (32 tokens) in one step: one softmax update
+// for both, and the PV products on 16x16x32 MFMAs whose contraction runs over
+// the 32 tokens (k = 8j + 4T + e' for tile T, token 4j + e' in the order
+// 0, 2, 1, 3, the same in the value and probability operands).
+template <int D, int MODE>
+__device__ __forceinline__ void tile4_pair_step(const Tile4<D, MODE>& t0, const Tile4<D, MODE>& t1,
+                                                const half8v* qop, float cscore,
+                                                SoftmaxState<D>& st, const Nib4Consts& kc) {
+  constexpr int NS = D / 32;
+  constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
+  constexpr int SG = Tile4<D, MODE>::SG;
+  float v[8], s[8];
+  tile4_scores(t0, qop, kc, v);
+  tile4_scores(t1, qop, kc, v + 4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = v[e] * cscore;
+  const float msafe = softmax_update<D, 8>(s, st);
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - msafe);
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  uint32_t G0[4], Z0[4] = {0u, 0u, 0u, 0u}, G1[4], Z1[4] = {0u, 0u, 0u, 0u};
+  tile4_vbytes(t0, G0, Z0);
+  tile4_vbytes(t1, G1, Z1);
+  static_for<0, NS>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    float pv[8];
+    static_for<0, 4>([&](auto E) {
+      constexpr int e = decltype(E)::value;
+      pv[e] = row_bcast<SG * e + (ASYM ? i : 0)>(t0.sv) * p[e];
+      pv[4 + e] = row_bcast<SG * e + (ASYM ? i : 0)>(t1.sv) * p[4 + e];
+    });
+    half8v pop;
+    pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
+    pop[4] = (half_t)pv[4]; pop[5] = (half_t)pv[6]; pop[6] = (half_t)pv[5]; pop[7] = (half_t)pv[7];
+    const VWords4 w0 = vgroup_words<ASYM>(G0[i], Z0[i], kc);
+    const VWords4 w1 = vgroup_words<ASYM>(G1[i], Z1[i], kc);
+    const half8v va0 = __builtin_bit_cast(half8v, (u32x4){w0.x[0], w0.x[1], w1.x[0], w1.x[1]});
+    const half8v va1 = __builtin_bit_cast(half8v, (u32x4){w0.y[0], w0.y[1], w1.y[0], w1.y[1]});
+    const half8v corr = __builtin_bit_cast(half8v, (u32x4){w0.c[0], w0.c[1], w1.c[0], w1.c[1]});
+    st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0, pop, st.acc[2 * i], 0, 0, 0);
+    st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va1, pop, st.acc[2 * i + 1], 0, 0, 0);
+    st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(corr, pop, st.acc[2 * i], 0, 0, 0);
+    st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(corr, pop, st.acc[2 * i + 1], 0, 0, 0);
   });
 }
 
@@ -782,14 +868,14 @@ __device__ __forceinline__ void query_int4(const DecodeArgs& a, const uint16_t* 
   cscore = hcol ? qup * a.sm_log2 : 0.0f;
 }
 
-// One wave's share of a split for 4-bit codes, in 16-token tiles with a ring
-// of NBUF tiles in registers.
+// One wave's share of a split for 4-bit codes, in pairs of 16-token tiles
+// from a ring of NBUF tiles in registers; the last tiles go one at a time.
 template <int D, int BS, int MODE>
 __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int g, int L,
                                                  int nblk, int i0, int i1, int lane,
                                                  SoftmaxState<D>& st) {
   constexpr int TPB = BS / 16;  // tiles per block
-  constexpr int NBUF = MODE == KVQ_SCALE_GROUP_ASYM ? 2 : 3;
+  constexpr int NBUF = 4;  // tiles in the register ring: two pairs
   const int r = lane & 15, j = lane >> 4;
   const int ilast = i1 - 1;
   const bool hcol = r < a.G;
@@ -822,11 +908,12 @@ __device__ __forceinline__ void wave_blocks_int4(const DecodeArgs& a, int b, int
   int tt = t0;
   for (; tt + NBUF <= tfull; tt += NBUF) {
     if (tt / TPB - ids.base >= kWave) ids.advance(lane);
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      tile4_step<D, MODE, false>(buf[u], (tt + u) * 16, L, qop, cscore, j, st, kc);
-      load(buf[u], tt + u + NBUF);
-    }
+    tile4_pair_step<D, MODE>(buf[0], buf[1], qop, cscore, st, kc);
+    load(buf[0], tt + NBUF);
+    load(buf[1], tt + NBUF + 1);
+    tile4_pair_step<D, MODE>(buf[2], buf[3], qop, cscore, st, kc);
+    load(buf[2], tt + NBUF + 2);
+    load(buf[3], tt + NBUF + 3);
   }
 #pragma unroll
   for (int u = 0; u < NBUF; ++u) {

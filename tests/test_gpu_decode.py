@@ -110,6 +110,22 @@ def test_decode_split_counts(split, code, mode, bs):
     assert_decode_close(got, exp, f"{code} split {split}")
 
 
+@pytest.mark.parametrize("split", [0, 21, 40])
+@pytest.mark.parametrize("mode", ["token_sym", "group_asym"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 16), (128, 32), (64, 32)])
+def test_decode_int4_long_shares(d, bs, mode, split):
+    """INT4 with wave shares of many tiles, so that the kernel takes pairs of
+    whole 16-token tiles from its ring and the last tiles of a share one at a
+    time (whole or ragged), for both scale modes, both head sizes and both
+    block sizes."""
+    need_gpu()
+    w, L, LL, s, q = _setup("int4", d=d, bs=bs, lens=(3001, 700, 93, 1, 0, 1290), G=8,
+                            mode=mode)
+    got, exp = _run(w, L, LL, s, q, split_blocks=split)
+    assert_decode_close(got, exp, f"int4/{mode} d{d} bs{bs} split {split}")
+    assert (got[4] == 0).all()
+
+
 @pytest.mark.parametrize("split", [0, 3, 40])
 @pytest.mark.parametrize("code,mode,bs", [("int8", "token_sym", 16), ("int4", "group_asym", 32)])
 def test_decode_skewed_batch_over_planning_chunks(split, code, mode, bs):
