@@ -34,7 +34,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_F16_TFLOPS = 2500.0   # dense fp16 MFMA, MI355X
 HERE = os.path.dirname(os.path.abspath(__file__))
 # sources whose change invalidates committed decode counters
-DECODE_SOURCES = ("kvq_decode.hip", "kvq_attn_tiles.h", "kvq_device.h", "kvq_internal.h")
+DECODE_SOURCES = ("kvq_decode.hip", "kvq_attn_tiles.h", "kvq_int4_tiles.h", "kvq_device.h",
+                  "kvq_internal.h")
 
 
 def decode_source_hash():

@@ -352,9 +352,10 @@ int64_t kvq_prefill_workspace_bytes(const kvq_layout* layout, int32_t batch,
  * The other arguments are those of kvq_decode_attention; nq_b = 1 computes
  * the same function as decode. Under CHANNEL_BLOCK_SYM the positions of the
  * partial last block (decided by context_lens[b]) are read raw from k_stage
- * row b. Supported: both sides INT8 or E4M3 under TOKEN_SYM, INT8
- * CHANNEL_BLOCK_SYM keys with INT8 TOKEN_SYM values, and both NONE16; other
- * layouts return KVQ_ERR_UNSUPPORTED. Preconditions: nq_b <= context_lens[b]
+ * row b. Supported: both sides INT8, E4M3 or INT4 under TOKEN_SYM, both INT4
+ * under GROUP_ASYM, INT8 CHANNEL_BLOCK_SYM keys with INT8 TOKEN_SYM values,
+ * and both NONE16 (the layouts decode supports); other layouts return
+ * KVQ_ERR_UNSUPPORTED. Preconditions: nq_b <= context_lens[b]
  * <= max_context_len; the value-range preconditions of decode. */
 kvq_status kvq_prefill_attention(const kvq_layout* layout, const kvq_cache* cache,
                                  const void* q, int32_t q_dtype, int32_t batch,

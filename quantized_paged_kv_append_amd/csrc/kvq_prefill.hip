@@ -1,6 +1,7 @@
 // kvq_prefill.hip -- multi-query (prefill) attention over the quantized
 // paged cache (gfx950): several causal queries per sequence at once.
 #include "kvq_attn_tiles.h"
+#include "kvq_int4_tiles.h"
 
 namespace kvq {
 namespace {
@@ -40,6 +41,87 @@ struct PrefillArgs {
 // NC: 16-column tiles per wave. With NC = 2 a block's codes are loaded and
 // converted once for 32 columns (per-channel keys keep NC = 1: their
 // per-block query folding needs the fp32 query of every column).
+// A wave's share of a split over 4-bit codes for one column tile: the
+// visible blocks as positions [x0, x1) in the sink blocks A = [s0, s0 + nA)
+// then the window's blocks from bstart. Blocks seen whole by every column
+// stream through a four-tile register ring in pairs of tiles; the others
+// (sink blocks, the window's first blocks, the context's last one or two)
+// go tile by tile with this lane's column masks (limit Lr, window start lo,
+// sink count).
+template <int D, int BS, int MODE>
+__device__ __forceinline__ void prefill_blocks_int4(const PrefillArgs& pa, int b, int g, int L,
+                                                    int s0, int x0, int x1, int nA, int bstart,
+                                                    int Lmin, int Lmax, int lo_min, int lo_max,
+                                                    int Lr, int lo, const half8v* qop,
+                                                    float cscore, int lane, SoftmaxState<D>& st) {
+  constexpr int TPB = BS / 16;  // tiles per block
+  constexpr int NBUF = 4;       // tiles in the ring: two pairs
+  const DecodeArgs& a = pa.a;
+  const int jj = lane >> 4;
+  const int W = pa.window, SK = pa.window > 0 ? pa.sink : 0;
+  const Nib4Consts kc = nib4_consts();
+  const Lane4 lo4 = lane4_offsets<D, MODE>(lane);
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
+  // ids outside the pool (a broken precondition, or a block dropped from a
+  // window) are read as block 0, which every wave shares
+  auto bh_of = [&](int i) -> int64_t {
+    const int32_t id = trow[i];
+    return (int64_t)(id >= 0 && id < a.num_blocks ? id : 0) * a.H + g;
+  };
+  const int b0 = bstart + max(x0, nA) - nA, b1 = bstart + x1 - nA;
+  const int iseen = Lmin / BS;
+  const int wf0 = W > 0 ? (max(lo_max, 0) + BS - 1) / BS : 0;
+  const int ra = min(max(wf0, b0), max(b1, b0));
+  const int rb = min(max(iseen, ra), max(b1, ra));
+  auto edge_run = [&](int e0, int e1) {
+    for (int i = e0; i < e1; ++i) {
+      const int64_t bh = bh_of(i);
+#pragma unroll
+      for (int nt = 0; nt < TPB; ++nt) {
+        const int pos0 = i * BS + nt * 16;
+        // no column sees the tile: past every limit, or between the sinks
+        // and every window
+        if (pos0 >= Lmax || (W > 0 && pos0 >= SK && pos0 + 16 <= lo_min)) continue;
+        const bool masked = pos0 + 16 > Lmin || (W > 0 && pos0 < lo_max && pos0 + 16 > SK);
+        Tile4<D, MODE> t;
+        load_tile4<D, BS, MODE>(t, a, bh, nt, lo4);
+        if (masked)
+          tile4_step<D, MODE, true>(t, pos0, Lr, qop, cscore, jj, st, kc, lo, SK);
+        else
+          tile4_step<D, MODE, false>(t, pos0, Lr, qop, cscore, jj, st, kc);
+      }
+    }
+  };
+  edge_run(s0 + x0, s0 + min(x1, nA));   // sink blocks
+  edge_run(b0, ra);
+  if (ra < rb) {
+    // tiles [T0, T1) of the whole blocks; refills past T1 read tile 0 of
+    // block 0, which every wave shares
+    const int T0 = ra * TPB, T1 = rb * TPB;
+    auto load = [&](Tile4<D, MODE>& t, int tile) {
+      const bool past = tile >= T1;
+      load_tile4<D, BS, MODE>(t, a, past ? (int64_t)g : bh_of(tile / TPB), past ? 0 : tile % TPB,
+                              lo4);
+    };
+    Tile4<D, MODE> buf[NBUF];
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) load(buf[u], T0 + u);
+    int tt = T0;
+    for (; tt + NBUF <= T1; tt += NBUF) {
+      tile4_pair_step<D, MODE>(buf[0], buf[1], qop, cscore, st, kc);
+      load(buf[0], tt + NBUF);
+      load(buf[1], tt + NBUF + 1);
+      tile4_pair_step<D, MODE>(buf[2], buf[3], qop, cscore, st, kc);
+      load(buf[2], tt + NBUF + 2);
+      load(buf[3], tt + NBUF + 3);
+    }
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u)
+      if (tt + u < T1) tile4_step<D, MODE, false>(buf[u], (tt + u) * 16, L, qop, cscore, jj, st, kc);
+  }
+  edge_run(rb, b1);
+}
+
 template <int CODE, int MODE, int D, int BS, int NC>
 __global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_split_kernel(PrefillArgs pa) {
@@ -49,7 +131,9 @@ void prefill_split_kernel(PrefillArgs pa) {
   constexpr int NBUF = BS == 16 ? 3 : 2;  // blocks in the register ring
   constexpr bool KCH = MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM;
   constexpr bool RAW = CODE == KVQ_CODE_NONE16;
+  constexpr bool I4 = CODE == KVQ_CODE_INT4;
   static_assert(!KCH || NC == 1, "per-channel keys take one column tile per wave");
+  static_assert(!I4 || NC == 1, "4-bit codes take one column tile per wave");
   using TileT = typename std::conditional<RAW, TileRaw<D, BS>, Tile8<D, BS>>::type;
   __shared__ float red[kNW][NV + 2][kWave];
   const DecodeArgs& a = pa.a;
@@ -117,6 +201,11 @@ void prefill_split_kernel(PrefillArgs pa) {
   for (int cc = 0; cc < NC; ++cc) {
     const int qi = valid[cc] ? col[cc] / a.G : 0;
     const int hq = g * a.G + (valid[cc] ? col[cc] % a.G : 0);
+    if constexpr (I4) {   // the 4-bit operand order, made from the whole row
+      query_int4<D>(a, a.q + ((int64_t)(q0 + qi) * a.Hq + hq) * D, jj, valid[cc], qop[cc],
+                    cscore[cc]);
+      continue;
+    }
     const uint16_t* qp = a.q + ((int64_t)(q0 + qi) * a.Hq + hq) * D + jj * (D / 4);
     if (a.q_bf16)
       load_query<true, D>(qp, qf);
@@ -151,7 +240,11 @@ void prefill_split_kernel(PrefillArgs pa) {
     for (int k = 0; k < NPV; ++k) st[cc].acc[k] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  if (x0 < x1) {
+  if constexpr (I4) {
+    if (x0 < x1) prefill_blocks_int4<D, BS, MODE>(pa, b, g, L, s0, x0, x1, nA, bstart, Lmin, Lmax,
+                                                  lo_min, lo_max, Lr[0], lo_r[0], qop[0],
+                                                  cscore[0], lane, st[0]);
+  } else if (x0 < x1) {
     // per-channel keys: a partly filled last block is read raw from stage row b
     const bool staged = KCH && (L % BS) != 0;
     // the wave's LDS slice for the per-channel query (the merge area, unused
@@ -313,6 +406,18 @@ void prefill_split_kernel(PrefillArgs pa) {
       }
       const int64_t pidx = (((int64_t)b * pa.J + j) * a.H + g) * (pa.CT * 16) + col[cc];
       if (jj == 0) *reinterpret_cast<float2*>(a.ws_ml + pidx * 2) = make_float2(M, l);
+      if constexpr (I4) {
+        // acc[4 m + e], m = 2 i + t, holds output element 32 i + 8 jj + 2 e + t
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+          float* dst = a.ws_acc + pidx * D + 32 * i + 8 * jj;
+          const float* A0 = acc + 8 * i;      // t = 0
+          const float* A1 = acc + 8 * i + 4;  // t = 1
+          *reinterpret_cast<float4v*>(dst) = (float4v){A0[0], A1[0], A0[1], A1[1]};
+          *reinterpret_cast<float4v*>(dst + 4) = (float4v){A0[2], A1[2], A0[3], A1[3]};
+        }
+        continue;
+      }
       // acc[4 k + e] holds output element (d/16) (4 jj + e) + k of the column
       float* dst = a.ws_acc + pidx * D + jj * (D / 4);
 #pragma unroll
@@ -421,18 +526,20 @@ hipError_t launch_prefill_nc(const PrefillArgs& pa, int d, int bs, int64_t units
 
 // Two column tiles per wave whenever there are two and the second set of
 // accumulators fits in registers next to the ring without spilling (d 64;
-// d 128 with 16-token blocks of 8-bit codes); per-channel keys: one.
+// d 128 with 16-token blocks of 8-bit codes); per-channel keys and 4-bit
+// codes: one.
 template <int CODE, int MODE>
 hipError_t launch_prefill_shape(PrefillArgs pa, int d, int bs, int64_t units_per_tg,
                                 hipStream_t stream) {
   const bool fits = d == 64 || (bs == 16 && CODE != KVQ_CODE_NONE16);
-  const int nc = (MODE != KVQ_SCALE_CHANNEL_BLOCK_SYM && pa.CT >= 2 && fits) ? 2 : 1;
+  const int nc = (MODE != KVQ_SCALE_CHANNEL_BLOCK_SYM && CODE != KVQ_CODE_INT4 && pa.CT >= 2 &&
+                  fits) ? 2 : 1;
   const int cts = (pa.CT + nc - 1) / nc;
   // the column tiles of a split share a workgroup (one wave or pair of waves
   // each), so that their reads of the same blocks meet in L1
   pa.TW = cts >= 4 ? 4 : (cts >= 2 ? 2 : 1);
   const int64_t units = units_per_tg * ((cts + pa.TW - 1) / pa.TW);
-  if constexpr (MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM) {
+  if constexpr (MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM || CODE == KVQ_CODE_INT4) {
     return launch_prefill_nc<CODE, MODE, 1>(pa, d, bs, units, stream);
   } else {
     if (nc == 2) return launch_prefill_nc<CODE, MODE, 2>(pa, d, bs, units, stream);
@@ -447,6 +554,8 @@ bool prefill_supported(int32_t k_code, int32_t v_code, int32_t k_mode, int32_t v
     return k_code == KVQ_CODE_INT8 && v_code == KVQ_CODE_INT8 && v_mode == KVQ_SCALE_TOKEN_SYM;
   if (k_code != v_code || k_mode != v_mode) return false;
   if (k_code == KVQ_CODE_NONE16) return true;
+  if (k_code == KVQ_CODE_INT4)
+    return k_mode == KVQ_SCALE_TOKEN_SYM || k_mode == KVQ_SCALE_GROUP_ASYM;
   return k_mode == KVQ_SCALE_TOKEN_SYM &&
          (k_code == KVQ_CODE_INT8 || k_code == KVQ_CODE_FP8_E4M3);
 }
@@ -494,6 +603,10 @@ hipError_t launch_prefill(const PrefillPlan& pp, hipStream_t stream) {
     e = launch_prefill_shape<KVQ_CODE_INT8, KVQ_SCALE_CHANNEL_BLOCK_SYM>(pa, d, bs, units, stream);
   else if (p.k_code == KVQ_CODE_FP8_E4M3)
     e = launch_prefill_shape<KVQ_CODE_FP8_E4M3, KVQ_SCALE_TOKEN_SYM>(pa, d, bs, units, stream);
+  else if (p.k_code == KVQ_CODE_INT4 && p.k_mode == KVQ_SCALE_GROUP_ASYM)
+    e = launch_prefill_shape<KVQ_CODE_INT4, KVQ_SCALE_GROUP_ASYM>(pa, d, bs, units, stream);
+  else if (p.k_code == KVQ_CODE_INT4)
+    e = launch_prefill_shape<KVQ_CODE_INT4, KVQ_SCALE_TOKEN_SYM>(pa, d, bs, units, stream);
   else
     e = launch_prefill_shape<KVQ_CODE_INT8, KVQ_SCALE_TOKEN_SYM>(pa, d, bs, units, stream);
   if (e != hipSuccess) return e;

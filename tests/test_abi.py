@@ -223,10 +223,9 @@ def test_prefill_rejects_bad_arguments_on_host():
     assert pre(window=8, sink=-2) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert lib.kvq_blocks_trim(p, p, 64, p, 4, p, -1, 0, 2, 16, p, None) == \
         kq.KVQ_ERR_INVALID_ARGUMENT
-    L4 = kq.make_layout(8, 128, 32, "int4", k_mode="group_asym", group_size=32)
-    c4 = _fake_cache(L4)
-    c4.k_zero, c4.v_zero = 1 << 25, (1 << 25) + 4096
-    assert pre(L=L4, cs=c4) == kq.KVQ_ERR_UNSUPPORTED
+    Lm = kq.make_layout(8, 128, 16, "int8", v_code="fp8")   # mixed codes: no kernel
+    assert kq.kvq_layout_check(Lm) == kq.KVQ_OK
+    assert pre(L=Lm, cs=_fake_cache(Lm)) == kq.KVQ_ERR_UNSUPPORTED
     # workspace grows with the query count and shrinks with longer splits
     w1 = kq.kvq_prefill_workspace_bytes(L, 2, 32, 8, 4096, 0)
     assert kq.kvq_prefill_workspace_bytes(L, 2, 32, 16, 4096, 0) > w1

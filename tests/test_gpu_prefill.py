@@ -22,6 +22,7 @@ def _setup(code="int8", d=128, bs=16, G=4, H=2, src="bfloat16", lens=LENS, nq=NQ
            mode="token_sym", fill=0xFF):
     w = workloads.get("tiny", k_code=code, v_code=code, k_mode=mode,
                       v_mode="token_sym" if mode == "channel_block" else mode,
+                      group_size=32 if mode == "group_asym" else 0,
                       src_dtype=src, head_dim=d, block_size=bs, num_kv_heads=H,
                       num_q_heads=G * H, batch=len(lens), n_outliers=2, outlier_factor=8.0)
     L, LL = oracle_layout(w), lib_layout(w)
@@ -65,7 +66,8 @@ def _run(w, L, LL, s, q, qs, split_blocks=0, out_dtype=torch.float32, sm_scale=0
 
 
 @pytest.mark.parametrize("code,mode", [("int8", "token_sym"), ("fp8", "token_sym"),
-                                       ("none16", "token_sym"), ("int8", "channel_block")])
+                                       ("none16", "token_sym"), ("int8", "channel_block"),
+                                       ("int4", "token_sym"), ("int4", "group_asym")])
 @pytest.mark.parametrize("d,bs", [(128, 16), (64, 32), (128, 32)])
 @pytest.mark.parametrize("G", [1, 4, 8, 16])
 def test_prefill_matches_oracle(code, mode, d, bs, G):
@@ -76,7 +78,8 @@ def test_prefill_matches_oracle(code, mode, d, bs, G):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 7, 64])
-@pytest.mark.parametrize("code,mode", [("fp8", "token_sym"), ("int8", "channel_block")])
+@pytest.mark.parametrize("code,mode", [("fp8", "token_sym"), ("int8", "channel_block"),
+                                       ("int4", "group_asym"), ("int4", "token_sym")])
 def test_prefill_split_counts(split, code, mode):
     need_gpu()
     w, L, LL, s, q, qs = _setup(code, G=8, mode=mode, lens=(700, 1, 250, 64, 0, 413),
@@ -94,7 +97,8 @@ def test_prefill_output_and_query_dtypes(out_dtype, src):
     assert_decode_close(got, exp, f"{src}->{out_dtype}")
 
 
-@pytest.mark.parametrize("code,mode", [("int8", "token_sym"), ("int8", "channel_block")])
+@pytest.mark.parametrize("code,mode", [("int8", "token_sym"), ("int8", "channel_block"),
+                                       ("int4", "group_asym")])
 def test_prefill_single_queries_match_decode(code, mode):
     """One query per sequence is decode: both GPU paths agree with each other
     and with the oracle."""
@@ -139,7 +143,8 @@ def test_prefill_chunk_of_a_long_prompt_sampled():
 
 @pytest.mark.parametrize("window,sink", [(1, 0), (7, 3), (16, 16), (40, 20), (100, 1), (33, 0)])
 @pytest.mark.parametrize("code,mode", [("int8", "token_sym"), ("fp8", "token_sym"),
-                                       ("none16", "token_sym"), ("int8", "channel_block")])
+                                       ("none16", "token_sym"), ("int8", "channel_block"),
+                                       ("int4", "group_asym")])
 @pytest.mark.parametrize("G,bs", [(4, 16), (8, 32)])
 def test_prefill_sliding_window_and_sinks(window, sink, code, mode, G, bs):
     need_gpu()
