@@ -233,3 +233,28 @@ def test_decode_llama3_8b_workload_full():
     got, exp = _run(w, L, LL, s, q)
     err = assert_decode_close(got, exp, "llama3_8b")
     print(f"llama3_8b max err {err:.2e}")
+
+
+def test_decode_reuses_one_workspace_across_shapes():
+    """One workspace serves calls of growing and shrinking batch and split
+    counts, each matching the oracle: no call depends on what an earlier one
+    left in the workspace."""
+    need_gpu()
+    import quantized_paged_kv_append_amd as kq
+    shapes = [((37, 80, 5, 1), 3), ((300, 0, 17, 16, 64, 15, 33, 2, 1, 90), 2),
+              ((37, 80), 0), ((513, 1, 260), 1), ((0, 3, 0), 0), ((700, 3), 5)]
+    ws = None
+    for lens, split in shapes:
+        w, L, LL, s, q = _setup("fp8", lens=lens)
+        need = kq.kvq_decode_workspace_bytes(LL, len(lens), q.shape[1], int(max(lens)), split)
+        if ws is None:
+            ws = torch.full((1 << 22,), 0xFF, dtype=torch.uint8, device=DEV)
+        assert need <= ws.numel()
+        exp = ref.decode(L, s.cache, bits(q), DT[w.src_dtype], s.tables, s.lens, threads=8)
+        gc = upload(s.cache, LL)
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        kq.kvq_decode_attention(LL, gc, q.to(DEV), torch.from_numpy(s.tables).to(DEV),
+                                torch.from_numpy(s.lens).to(DEV), int(max(lens)), out, ws,
+                                split_blocks=split)
+        torch.cuda.synchronize()
+        assert_decode_close(out, exp, f"lens {lens} split {split}")
