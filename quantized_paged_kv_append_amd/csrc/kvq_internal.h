@@ -81,7 +81,7 @@ struct DecodePlan {
 // lengths and kDecodeTargetWavesLog2, 64 otherwise. The host's item bound
 // assumes the second pair, which yields more items for any lengths.
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeMaxWaveBlocks = 128;
+constexpr int kDecodeMaxWaveBlocks = 256;
 constexpr int kDecodeTargetWavesLog2 = 12;
 constexpr int kDecodeUniformWavesLog2 = 11;
 constexpr int kDecodeMinWaveTokens = 32;
