@@ -97,6 +97,15 @@ __device__ __forceinline__ bool fp8_near_tie(float y) {
   return (low - 0x80000u + 64u) < 128u || fabsf(y) < 0.015625f;
 }
 
+// Eight 16-bit inputs (one 16-byte piece) as floats, exactly.
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const u32x4& w, float* x) {
+  unpack2<BF16>(w.x, x[0], x[1]);
+  unpack2<BF16>(w.y, x[2], x[3]);
+  unpack2<BF16>(w.z, x[4], x[5]);
+  unpack2<BF16>(w.w, x[6], x[7]);
+}
+
 // Byte codes (INT8 / FP8 / 16-bit passthrough). A wave covers 16 consecutive
 // tokens of one KV head (rows r = ((tg H + h) 16 + i), token 16 tg + i), so a
 // block's scales leave as one contiguous store when its slots are
@@ -114,36 +123,47 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
   const uint32_t items = groups * (uint32_t)a.H;   // (token group, head) pairs
   const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const uint32_t nwaves = gridDim.x * blockDim.x / kWave;
-  for (uint32_t it = wave; it < items; it += nwaves) {
+  // The inputs of one (token group, head) item: the lane row's slot and its
+  // 16-byte pieces. For E4M3 and 16-bit codes each wave loads its next item
+  // before it codes the current one, so two items' loads are in flight while
+  // it computes (measured: +9% on E4M3); INT8 keeps one item at a time, whose
+  // lower register use holds eight waves per SIMD instead of six (the
+  // prefetch cost it 4%).
+  struct Rows {
+    int64_t slot;
+    u32x4 w[NV];
+  };
+  auto fetch = [&](uint32_t it, Rows& R) {
     const uint32_t tg = div_h(it, a);
     const uint32_t h = it - tg * (uint32_t)a.H;
     const uint32_t t = tg * RPW + (uint32_t)(lane >> 2);
-    const bool in = t < (uint32_t)a.num_tokens;
-    const int64_t slot = in ? a.slots[t] : -1;
+    const bool in = it < items && t < (uint32_t)a.num_tokens;
+    R.slot = in ? a.slots[t] : -1;
+    const uint16_t* src = S.src + (int64_t)(in ? t : 0) * S.row_stride + h * D + 8 * k;
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      R.w[u] = in ? *reinterpret_cast<const u32x4*>(src + 32 * u) : (u32x4){0u, 0u, 0u, 0u};
+  };
+  auto code = [&](uint32_t it, const Rows& R) {
+    const uint32_t tg = div_h(it, a);
+    const uint32_t h = it - tg * (uint32_t)a.H;
+    const int64_t slot = R.slot;
     const int64_t blk = slot >> a.bs_shift;
     const bool live = slot >= 0 && blk < a.num_blocks;
     const int64_t rowi = (blk * a.H + h) * a.bs + (slot & (a.bs - 1));
-    const uint16_t* src = S.src + (int64_t)(in ? t : 0) * S.row_stride + h * D + 8 * k;
-    u32x4 w[NV];
-#pragma unroll
-    for (int u = 0; u < NV; ++u)
-      w[u] = in ? *reinterpret_cast<const u32x4*>(src + 32 * u) : (u32x4){0u, 0u, 0u, 0u};
+    const u32x4* w = R.w;
     if constexpr (CODE == KVQ_CODE_NONE16) {
       if (live) {
 #pragma unroll
         for (int u = 0; u < NV; ++u)
           *reinterpret_cast<u32x4*>(S.codes + rowi * (2 * D) + 2 * (32 * u + 8 * k)) = w[u];
       }
-      continue;
+      return;
     }
+    // the exact-quotient paths unpack the inputs again rather than keep them
     float x[NV][8];
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      unpack2<BF16>(w[u].x, x[u][0], x[u][1]);
-      unpack2<BF16>(w[u].y, x[u][2], x[u][3]);
-      unpack2<BF16>(w[u].z, x[u][4], x[u][5]);
-      unpack2<BF16>(w[u].w, x[u][6], x[u][7]);
-    }
+    for (int u = 0; u < NV; ++u) unpack8<BF16>(w[u], x[u]);
     constexpr float kQmax = CODE == KVQ_CODE_INT8 ? 127.0f : 448.0f;
     float s;
     if constexpr (STATIC) {
@@ -177,10 +197,12 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
       if (tie) {  // rare: redo this lane's codes with the exact quotient
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
+          float xe[8];
+          unpack8<BF16>(w[u], xe);
           int c[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            c[e] = (int)fminf(fmaxf(rne(div_rn(x[u][e], s)), -127.0f), 127.0f);
+            c[e] = (int)fminf(fmaxf(rne(div_rn(xe[e], s)), -127.0f), 127.0f);
           o[u][0] = pack_bytes(c[0], c[1], c[2], c[3]);
           o[u][1] = pack_bytes(c[4], c[5], c[6], c[7]);
         }
@@ -201,10 +223,12 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
       if (tie) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
+          float xe[8];
+          unpack8<BF16>(w[u], xe);
           float y[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            y[e] = div_rn(x[u][e], s);
+            y[e] = div_rn(xe[e], s);
             if constexpr (STATIC) y[e] = sat448(y[e]);
           }
           o[u][0] = fp8x4(y[0], y[1], y[2], y[3]);
@@ -219,6 +243,22 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
         *reinterpret_cast<u32x2*>(S.codes + rowi * D + 32 * u + 8 * k) = v2;
       }
       if (k == 0) S.scale[rowi] = s;
+    }
+  };
+  if constexpr (CODE == KVQ_CODE_INT8) {
+    for (uint32_t it = wave; it < items; it += nwaves) {
+      Rows cur;
+      fetch(it, cur);
+      code(it, cur);
+    }
+  } else {
+    if (wave >= items) return;
+    Rows cur, nxt;
+    fetch(wave, cur);
+    for (uint32_t it = wave; it < items; it += nwaves) {
+      fetch(it + nwaves, nxt);
+      code(it, cur);
+      cur = nxt;
     }
   }
 }
