@@ -77,6 +77,9 @@ def parse():
                     help="append this many tokens per sequence per step and attend with "
                          "all of them at once through kvq_prefill_attention (0: one "
                          "decode query per sequence)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager steps only (default: also one step captured in a "
+                         "HIP graph, replayed; its time is the line's value)")
     ap.add_argument("--identity-pool", action="store_true",
                     help="blocks in order instead of a seeded permutation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,7 +222,8 @@ def main():
     lens = workloads.lengths(w)
     B, Hq, H, d, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     new_per_step = nq if nq else w.new_tokens
-    total_steps = args.warmup + args.steps
+    # eager steps, then (unless --eager) as many graph replays
+    total_steps = (args.warmup + args.steps) * (1 if args.eager else 2)
     headroom = new_per_step * total_steps
     nb = workloads.pool_blocks(lens, bs, headroom_tokens=headroom + bs)
     maxb = (int(lens.max()) + headroom) // bs + 2
@@ -354,6 +358,44 @@ def main():
     bpth = kv_bytes_per_token_head(w)
     kv_bytes_step = float(np.mean(ctx_tokens)) * H * bpth * layers
     value = kv_bytes_step / (step_ms / 1e3) / 1e9
+    eager_ms, eager_value = step_ms, value
+
+    # ---- the same step captured once in a HIP graph, replayed -------------
+    # (the library makes no allocation, memset or host synchronization, so
+    # the graph holds its kernels only; per-launch figures stay the eager ones)
+    graph_ms = None
+    if not args.eager:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ctx_g = ctx.cpu().numpy().astype(np.int64)
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for s_ in range(args.steps):
+            if flush_buf is not None:
+                flush_sink[s_ % 2] = flush_buf.view(torch.int64).sum()
+            gev[s_][0].record(stream)
+            g.replay()
+            gev[s_][1].record(stream)
+        g1.record(stream)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, "pool reservation during the graph replays failed"
+        graph_ms = (float(np.mean([a.elapsed_time(b) for a, b in gev])) if flush_buf is not None
+                    else g0.elapsed_time(g1) / args.steps)
+        ctx_tokens_g = [(ctx_g + new_per_step * (s + 1)).sum() for s in range(args.steps)]
+        kv_bytes_step = float(np.mean(ctx_tokens_g)) * H * bpth * layers
+        step_ms = graph_ms
+        value = kv_bytes_step / (step_ms / 1e3) / 1e9
     dec_avg_ms = float(np.mean(dec_ms))
     dec_bytes_launch = float(np.mean(ctx_tokens)) * H * bpth
     achieved = dec_bytes_launch / (dec_avg_ms / 1e3) / 1e9
@@ -405,6 +447,7 @@ def main():
             "new_tokens_per_step": new_per_step, "pool": "identity" if args.identity_pool else "permuted",
             "split_blocks": args.split_blocks or "auto",
             "prefill_queries": nq or None,
+            "step": "eager" if args.eager else "hip graph replay",
         },
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "kv_bytes_per_step": kv_bytes_step,
@@ -412,6 +455,8 @@ def main():
         "decode_launch_ms_p10_p50_p90": [round(float(x), 5)
                                          for x in np.percentile(dec_ms, [10, 50, 90])],
         "ms_per_step_bracket": round(bracket_ms, 4),
+        "ms_per_step_eager": round(eager_ms, 4),
+        "value_eager": round(eager_value, 2),
         "cache_flush_mb": flush_mb,
         "cache_flush": ("write" if args.flush_write else "read") if flush_mb else None,
         "append_tok_s": round(append_tok_s, 1),
