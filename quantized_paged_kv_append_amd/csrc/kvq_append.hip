@@ -464,8 +464,9 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
 // Phase 1: every token whose slot is the last of its block completes that
 // block: the block's rows come from this call (the run of preceding tokens
 // with consecutive slots and the same stage row) and, for earlier offsets,
-// from the stage row. One wave per (completing token, head); lane l owns
-// channels 2l, 2l+1 (D = 128) or channel l (D = 64) over all bs rows.
+// from the stage row. One wave per (token, head) item (items whose token
+// completes no block end after reading its slot); lane l owns channels
+// 2l, 2l+1 (D = 128) or channel l (D = 64) over all bs rows.
 struct ChanArgs {
   const uint16_t* src;
   int64_t row_stride;
@@ -495,11 +496,16 @@ __global__ __launch_bounds__(256) void chan_complete_kernel(ChanArgs a) {
     const int64_t blk = slot / BS;
     const int32_t srow = a.stage_rows[t];
     if (blk >= a.num_blocks || srow < 0 || srow >= a.max_seqs) continue;
-    // rows of this block provided by this call: t - k for k < n_new
-    int n_new = 1;
-    while (n_new < BS && t - n_new >= 0 && a.slots[t - n_new] == slot - n_new &&
-           a.stage_rows[t - n_new] == srow)
-      ++n_new;
+    // rows of this block provided by this call: t - k for k < n_new, the
+    // run of preceding tokens with consecutive slots and the same stage row;
+    // lane l checks token t - 1 - l, all lanes at once
+    bool match = false;
+    if (lane < BS - 1 && t - 1 - lane >= 0) {
+      const int64_t tp = t - 1 - lane;
+      match = a.slots[tp] == slot - 1 - lane && a.stage_rows[tp] == srow;
+    }
+    // at most BS - 1 < 64 bits are set, so the complement is never 0
+    const int n_new = 1 + __builtin_ctzll(~(uint64_t)__ballot(match));
     float x[BS][CPL];
     float amax[CPL];
 #pragma unroll
@@ -721,8 +727,10 @@ hipError_t launch_chan(const AppendPlan& p, hipStream_t stream) {
   c.H = p.num_kv_heads;
   c.max_seqs = p.max_seqs;
   const int64_t items = p.num_tokens * p.num_kv_heads;
-  // phase 1: about one item in BS completes a block
-  chan_complete_kernel<D, BS, BF16><<<grid_for((items + 7) / 8, p.cu_count), 256, 0, stream>>>(c);
+  // phase 1: one wave per (token, head) item while the grid allows, so
+  // that the items that complete no block (all but about one in BS) cost a
+  // single slot load each, side by side
+  chan_complete_kernel<D, BS, BF16><<<grid_for(items, p.cu_count), 256, 0, stream>>>(c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t waves = (items + (kWave / (D / 8)) - 1) / (kWave / (D / 8));
