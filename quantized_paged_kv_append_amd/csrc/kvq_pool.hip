@@ -95,10 +95,17 @@ __global__ __launch_bounds__(kThreads) void reserve_kernel(
     const int64_t tpre = block_exclusive_scan(n, &ttot, sh) + toff;
     if (b < batch) {
       int32_t* row = tables + (int64_t)b * max_blocks;
-      for (int64_t k = 0; k < need; ++k) row[have + k] = stack[top0 - bpre - need + k];
-      for (int64_t k = 0; k < n; ++k) {
-        const int64_t pos = L + k;
-        slots[tpre + k] = (int64_t)row[pos / bs] * bs + pos % bs;
+      const int64_t take0 = top0 - bpre - need;   // this row's first popped entry
+      for (int64_t k = 0; k < need; ++k) row[have + k] = stack[take0 + k];
+      // slots block by block: one id per block the new tokens touch, from
+      // the row's existing entries or the popped ones (never a re-read of
+      // the entries just written), then its run of consecutive slots
+      for (int64_t k = 0; k < n;) {
+        const int64_t pos = L + k, blk = pos / bs, off = pos % bs;
+        const int64_t id = blk < have ? row[blk] : stack[take0 + (blk - have)];
+        const int64_t m = min(n - k, (int64_t)bs - off);
+        for (int64_t u = 0; u < m; ++u) slots[tpre + k + u] = id * bs + off + u;
+        k += m;
       }
       if (lens_out) lens_out[b] = (int32_t)(L + n);
     }
