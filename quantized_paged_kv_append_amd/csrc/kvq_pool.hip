@@ -19,21 +19,46 @@ namespace {
 constexpr int kThreads = 1024;
 
 // Block-wide exclusive scan of one int64 per thread; returns the prefix and
-// writes the total to *total (all threads).
+// writes the total to *total (all threads). Each wave scans its 64 values
+// with shuffles, the wave totals meet in sh[0 .. kThreads / 64), and the
+// trailing barrier frees sh for the next call: two barriers per scan.
 __device__ int64_t block_exclusive_scan(int64_t v, int64_t* total, int64_t* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int64_t add = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+  constexpr int kWaves = kThreads / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  int64_t x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const int64_t incl = sh[tid];
-  *total = sh[kThreads - 1];
+  if (lane == kWave - 1) sh[wave] = x;
   __syncthreads();
-  return incl - v;
+  // lane w < kWaves holds wave w's total; sums over the first kWaves lanes
+  const int64_t t = lane < kWaves ? sh[lane] : 0;
+  int64_t before = lane < wave ? t : 0, all = t;
+#pragma unroll
+  for (int off = 1; off < kWaves; off <<= 1) {
+    before += __shfl_xor(before, off);
+    all += __shfl_xor(all, off);
+  }
+  *total = __shfl(all, 0);
+  before = __shfl(before, 0);
+  __syncthreads();
+  return before + x - v;
+}
+
+// Largest i < cnt with pre[i] <= f, for a non-decreasing pre with pre[0] = 0
+// <= f: the entry whose run [pre[i], pre[i + 1]) holds f.
+__device__ __forceinline__ int find_run(const int64_t* pre, int cnt, int64_t f) {
+  int lo = 0, hi = cnt - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= f)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
 }
 
 __global__ __launch_bounds__(kThreads) void pool_init_kernel(int32_t* stack, int32_t* top,
@@ -53,6 +78,8 @@ __global__ __launch_bounds__(kThreads) void reserve_kernel(
     const int32_t* lens, const int32_t* new_tokens, int32_t batch, int32_t bs,
     int64_t* slots, int32_t* lens_out, int32_t* status, int64_t capacity) {
   __shared__ int64_t sh[kThreads];
+  __shared__ int64_t s_bpre[kThreads], s_wpre[kThreads], s_tout[kThreads];
+  __shared__ int32_t s_L[kThreads], s_n[kThreads];
   __shared__ int ok_sh;
   const int tid = threadIdx.x;
   // a top outside [0, capacity] (a broken precondition) is cut to it
@@ -79,39 +106,65 @@ __global__ __launch_bounds__(kThreads) void reserve_kernel(
     if (tid == 0) *status = KVQ_ERR_OUT_OF_BLOCKS;
     return;
   }
-  // pass 2: take blocks and write slots
+  // pass 2, chunk by chunk: every thread of the workgroup writes table
+  // entries and slots of any sequence of the chunk (runs found by a binary
+  // search over the chunk's prefix sums), so a long prompt is placed in
+  // parallel rather than by its own thread
   int64_t boff = 0, toff = 0;
   for (int base = 0; base < batch; base += kThreads) {
     const int b = base + tid;
-    int64_t have = 0, need = 0, n = 0, L = 0;
+    const int cnt = min(kThreads, batch - base);
+    int64_t L = 0, n = 0, need = 0, touched = 0;
     if (b < batch) {
       L = lens[b];
       n = new_tokens[b];
-      have = ceil_div(L, bs);
-      need = ceil_div(L + n, bs) - have;
+      need = ceil_div(L + n, bs) - ceil_div(L, bs);
+      touched = n > 0 ? (L + n - 1) / bs - L / bs + 1 : 0;   // blocks the new tokens fall in
     }
-    int64_t ctot, ttot;
-    const int64_t bpre = block_exclusive_scan(need, &ctot, sh) + boff;
-    const int64_t tpre = block_exclusive_scan(n, &ttot, sh) + toff;
-    if (b < batch) {
-      int32_t* row = tables + (int64_t)b * max_blocks;
-      const int64_t take0 = top0 - bpre - need;   // this row's first popped entry
-      for (int64_t k = 0; k < need; ++k) row[have + k] = stack[take0 + k];
-      // slots block by block: one id per block the new tokens touch, from
-      // the row's existing entries or the popped ones (never a re-read of
-      // the entries just written), then its run of consecutive slots
-      for (int64_t k = 0; k < n;) {
-        const int64_t pos = L + k, blk = pos / bs, off = pos % bs;
-        const int64_t id = blk < have ? row[blk] : stack[take0 + (blk - have)];
-        const int64_t m = min(n - k, (int64_t)bs - off);
-        for (int64_t u = 0; u < m; ++u) slots[tpre + k + u] = id * bs + off + u;
-        k += m;
-      }
-      if (lens_out) lens_out[b] = (int32_t)(L + n);
+    int64_t ctot, ttot, wtot;
+    const int64_t bpre = block_exclusive_scan(need, &ctot, sh);
+    const int64_t tpre = block_exclusive_scan(n, &ttot, sh);
+    const int64_t wpre = block_exclusive_scan(touched, &wtot, sh);
+    s_bpre[tid] = bpre;
+    s_wpre[tid] = wpre;
+    s_tout[tid] = toff + tpre;
+    s_L[tid] = (int32_t)L;
+    s_n[tid] = (int32_t)n;
+    __syncthreads();
+    // lengths may alias lens_out: each thread has read its own already
+    if (b < batch && lens_out) lens_out[b] = (int32_t)(L + n);
+    // sequence i takes the popped entries take0 .. take0 + need - 1, with
+    // take0 = top0 - (boff + bpre_i) - need_i, as table entries have .. have + need - 1
+    auto seq = [&](int i, int64_t& Li, int64_t& ni, int64_t& hi, int64_t& take0) {
+      Li = s_L[i];
+      ni = s_n[i];
+      hi = ceil_div(Li, bs);
+      take0 = top0 - (boff + s_bpre[i]) - (ceil_div(Li + ni, bs) - hi);
+    };
+    for (int64_t f = tid; f < ctot; f += kThreads) {
+      const int i = find_run(s_bpre, cnt, f);
+      int64_t Li, ni, hi, take0;
+      seq(i, Li, ni, hi, take0);
+      const int64_t k = f - s_bpre[i];
+      tables[(int64_t)(base + i) * max_blocks + hi + k] = stack[take0 + k];
+    }
+    // slots, one touched block per iteration: its id from the row's existing
+    // entries or the popped ones (never the entries written just above),
+    // then its run of consecutive slots
+    for (int64_t f = tid; f < wtot; f += kThreads) {
+      const int i = find_run(s_wpre, cnt, f);
+      int64_t Li, ni, hi, take0;
+      seq(i, Li, ni, hi, take0);
+      const int64_t blk = Li / bs + (f - s_wpre[i]);
+      const int64_t id =
+          blk < hi ? tables[(int64_t)(base + i) * max_blocks + blk] : stack[take0 + (blk - hi)];
+      const int64_t p0 = max(Li, blk * bs), p1 = min(Li + ni, (blk + 1) * bs);
+      int64_t* out = slots + s_tout[i] - Li;
+      for (int64_t pos = p0; pos < p1; ++pos) out[pos] = id * bs + (pos - blk * bs);
     }
     boff += ctot;
     toff += ttot;
-    __syncthreads();
+    __syncthreads();   // the chunk's arrays are read before the next chunk writes them
   }
   if (tid == 0) {
     *top = (int32_t)(top0 - total_need);
