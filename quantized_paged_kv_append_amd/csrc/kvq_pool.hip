@@ -177,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void release_kernel(
     int32_t max_blocks, const int32_t* lens, const int32_t* mask, int32_t batch,
     int32_t bs, int32_t* lens_out, int32_t* status) {
   __shared__ int64_t sh[kThreads];
+  __shared__ int64_t s_pre[kThreads];
   const int tid = threadIdx.x;
   const int64_t top0 = min(max((int64_t)*top, (int64_t)0), capacity);
   int64_t total = 0;
@@ -191,14 +192,21 @@ __global__ __launch_bounds__(kThreads) void release_kernel(
     if (tid == 0) *status = KVQ_ERR_OUT_OF_BLOCKS;
     return;
   }
+  // the chunk's released entries are spread over the whole workgroup (entry
+  // f of the chunk belongs to the sequence whose prefix run holds it)
   int64_t off = 0;
   for (int base = 0; base < batch; base += kThreads) {
     const int b = base + tid;
+    const int cnt = min(kThreads, batch - base);
     const bool rel = b < batch && mask[b];
     const int64_t nb = rel ? min(ceil_div(lens[b], bs), (int64_t)max_blocks) : 0;
     int64_t t;
-    const int64_t pre = block_exclusive_scan(nb, &t, sh) + off;
-    for (int64_t k = 0; k < nb; ++k) stack[top0 + pre + k] = tables[(int64_t)b * max_blocks + k];
+    s_pre[tid] = block_exclusive_scan(nb, &t, sh);
+    __syncthreads();
+    for (int64_t f = tid; f < t; f += kThreads) {
+      const int i = find_run(s_pre, cnt, f);
+      stack[top0 + off + f] = tables[(int64_t)(base + i) * max_blocks + (f - s_pre[i])];
+    }
     off += t;
     __syncthreads();
   }
