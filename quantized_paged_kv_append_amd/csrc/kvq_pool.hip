@@ -273,6 +273,8 @@ __global__ __launch_bounds__(kThreads) void reserve_shared_kernel(
     int32_t bs, int64_t* slots, int32_t* lens_out, int32_t* cow_src, int32_t* cow_dst,
     int32_t* cow_count, int32_t* status) {
   __shared__ int64_t sh[kThreads];
+  __shared__ int64_t s_first[kThreads], s_gpre[kThreads], s_xpre[kThreads], s_tout[kThreads];
+  __shared__ int32_t s_L[kThreads], s_n[kThreads], s_cow[kThreads];
   __shared__ int ok_sh;
   const int tid = threadIdx.x;
   const int64_t top0 = min(max((int64_t)*top, (int64_t)0), capacity);
@@ -299,28 +301,41 @@ __global__ __launch_bounds__(kThreads) void reserve_shared_kernel(
     return;
   }
   // the copy decisions are taken before any count changes (pass 2 only sets
-  // the counts of blocks taken from the stack, which no table holds)
+  // the counts of blocks taken from the stack, which no table holds). Table
+  // entries and slots are spread over the workgroup as in reserve_kernel.
   int64_t boff = 0, toff = 0, coff = 0;
   for (int base = 0; base < batch; base += kThreads) {
     const int b = base + tid;
-    int64_t have = 0, grow = 0, n = 0, L = 0;
+    const int cnt = min(kThreads, batch - base);
+    int64_t grow = 0, n = 0, L = 0, touched = 0;
     int cow = 0;
     if (b < batch) {
       L = lens[b];
       n = new_tokens[b];
-      have = ceil_div(L, bs);
-      grow = ceil_div(L + n, bs) - have;
+      grow = ceil_div(L + n, bs) - ceil_div(L, bs);
       cow = cow_needed(refcount, capacity, tables, max_blocks, b, (int32_t)L, (int32_t)n, bs);
+      touched = n > 0 ? (L + n - 1) / bs - L / bs + 1 : 0;
     }
     const int64_t need = grow + cow;
-    int64_t ctot, ttot, wtot;
+    int64_t ctot, ttot, wtot, gtot, xtot;
     const int64_t bpre = block_exclusive_scan(need, &ctot, sh) + boff;
     const int64_t tpre = block_exclusive_scan(n, &ttot, sh) + toff;
     const int64_t cpre = block_exclusive_scan(cow, &wtot, sh) + coff;
+    const int64_t gpre = block_exclusive_scan(grow, &gtot, sh);
+    const int64_t xpre = block_exclusive_scan(touched, &xtot, sh);
+    // sequence i of the chunk takes stack entries first .. first + need - 1:
+    // the copy's fresh block (if any), then its grown blocks
+    const int64_t first = top0 - bpre - need;
+    s_first[tid] = first;
+    s_gpre[tid] = gpre;
+    s_xpre[tid] = xpre;
+    s_tout[tid] = tpre;
+    s_L[tid] = (int32_t)L;
+    s_n[tid] = (int32_t)n;
+    s_cow[tid] = cow;
     __syncthreads();   // every copy decision of this chunk is read before counts change
     if (b < batch) {
       int32_t* row = tables + (int64_t)b * max_blocks;
-      const int64_t first = top0 - bpre - need;
       if (cow) {
         const int32_t fresh = stack[first];
         cow_src[cpre] = row[L / bs];
@@ -328,16 +343,32 @@ __global__ __launch_bounds__(kThreads) void reserve_shared_kernel(
         row[L / bs] = fresh;
         if (fresh >= 0 && fresh < capacity) refcount[fresh] = 1;
       }
-      for (int64_t k = 0; k < grow; ++k) {
-        const int32_t id = stack[first + cow + k];
-        row[have + k] = id;
-        if (id >= 0 && id < capacity) refcount[id] = 1;
-      }
-      for (int64_t k = 0; k < n; ++k) {
-        const int64_t pos = L + k;
-        slots[tpre + k] = (int64_t)row[pos / bs] * bs + pos % bs;
-      }
       if (lens_out) lens_out[b] = (int32_t)(L + n);
+    }
+    for (int64_t f = tid; f < gtot; f += kThreads) {
+      const int i = find_run(s_gpre, cnt, f);
+      const int64_t k = f - s_gpre[i];
+      const int32_t id = stack[s_first[i] + s_cow[i] + k];
+      tables[(int64_t)(base + i) * max_blocks + ceil_div(s_L[i], bs) + k] = id;
+      if (id >= 0 && id < capacity) refcount[id] = 1;
+    }
+    // slots block by block; a block's id is the row's existing entry, the
+    // copy's fresh block (the partial block of a copying row) or a grown
+    // one, never a re-read of an entry written in this pass
+    for (int64_t f = tid; f < xtot; f += kThreads) {
+      const int i = find_run(s_xpre, cnt, f);
+      const int64_t Li = s_L[i], ni = s_n[i], hi = ceil_div(Li, bs);
+      const int64_t blk = Li / bs + (f - s_xpre[i]);
+      int64_t id;
+      if (s_cow[i] && blk == Li / bs)
+        id = stack[s_first[i]];
+      else if (blk < hi)
+        id = tables[(int64_t)(base + i) * max_blocks + blk];
+      else
+        id = stack[s_first[i] + s_cow[i] + (blk - hi)];
+      const int64_t p0 = max(Li, blk * bs), p1 = min(Li + ni, (blk + 1) * bs);
+      int64_t* out = slots + s_tout[i] - Li;
+      for (int64_t pos = p0; pos < p1; ++pos) out[pos] = id * bs + (pos - blk * bs);
     }
     boff += ctot;
     toff += ttot;
