@@ -506,6 +506,48 @@ __device__ __forceinline__ void trim_range(int32_t L, int32_t window, int32_t si
   hi = min(hi, (int64_t)max_blocks);
 }
 
+// Entries [lo, hi) of every row of a chunk are enumerated by the whole
+// workgroup in (row, block) order: entry e of the chunk belongs to the row
+// whose run in the chunk's prefix sums holds it. PUSH = false counts the live
+// (non-negative) entries; PUSH = true moves them to the stack from `pos` on,
+// in that order, and clears them.
+template <bool PUSH>
+__device__ int64_t trim_entries(int32_t* stack, int64_t pos, int32_t* tables, int32_t max_blocks,
+                                const int32_t* lens, int32_t window, int32_t sink, int32_t batch,
+                                int32_t bs, int64_t* sh, int64_t* s_pre, int64_t* s_lo) {
+  const int tid = threadIdx.x;
+  int64_t live = 0;
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    const int cnt = min(kThreads, batch - base);
+    int64_t lo = 0, hi = 0;
+    if (b < batch && window > 0) trim_range(lens[b], window, sink, bs, max_blocks, lo, hi);
+    int64_t etot;
+    s_pre[tid] = block_exclusive_scan(max(hi - lo, (int64_t)0), &etot, sh);
+    s_lo[tid] = lo;
+    __syncthreads();
+    for (int64_t e0 = 0; e0 < etot; e0 += kThreads) {
+      const int64_t e = e0 + tid;
+      int32_t* ent = nullptr;
+      int32_t id = -1;
+      if (e < etot) {
+        const int r = find_run(s_pre, cnt, e);
+        ent = &tables[(int64_t)(base + r) * max_blocks + s_lo[r] + (e - s_pre[r])];
+        id = *ent;
+      }
+      int64_t ktot;
+      const int64_t k = block_exclusive_scan(id >= 0 ? 1 : 0, &ktot, sh);
+      if (PUSH && id >= 0) {
+        stack[pos + live + k] = id;
+        *ent = -1;
+      }
+      live += ktot;
+    }
+    __syncthreads();   // the chunk's arrays are read before the next chunk writes them
+  }
+  return live;
+}
+
 __global__ __launch_bounds__(kThreads) void trim_kernel(int32_t* stack, int32_t* top,
                                                         int64_t capacity, int32_t* tables,
                                                         int32_t max_blocks, const int32_t* lens,
@@ -513,45 +555,17 @@ __global__ __launch_bounds__(kThreads) void trim_kernel(int32_t* stack, int32_t*
                                                         int32_t batch, int32_t bs,
                                                         int32_t* status) {
   __shared__ int64_t sh[kThreads];
-  const int tid = threadIdx.x;
+  __shared__ int64_t s_pre[kThreads], s_lo[kThreads];
   const int64_t top0 = min(max((int64_t)*top, (int64_t)0), capacity);
-  int64_t total = 0;
-  for (int base = 0; base < batch; base += kThreads) {
-    const int b = base + tid;
-    int64_t nb = 0;
-    if (b < batch && window > 0) {
-      int64_t lo, hi;
-      trim_range(lens[b], window, sink, bs, max_blocks, lo, hi);
-      for (int64_t i = lo; i < hi; ++i) nb += tables[(int64_t)b * max_blocks + i] >= 0;
-    }
-    int64_t t;
-    block_exclusive_scan(nb, &t, sh);
-    total += t;
-  }
+  const int64_t total = trim_entries<false>(stack, top0, tables, max_blocks, lens, window, sink,
+                                            batch, bs, sh, s_pre, s_lo);
   if (top0 + total > capacity) {
-    if (tid == 0) *status = KVQ_ERR_OUT_OF_BLOCKS;
+    if (threadIdx.x == 0) *status = KVQ_ERR_OUT_OF_BLOCKS;
     return;
   }
-  int64_t off = 0;
-  for (int base = 0; base < batch; base += kThreads) {
-    const int b = base + tid;
-    int64_t nb = 0, lo = 0, hi = 0;
-    if (b < batch && window > 0) {
-      trim_range(lens[b], window, sink, bs, max_blocks, lo, hi);
-      for (int64_t i = lo; i < hi; ++i) nb += tables[(int64_t)b * max_blocks + i] >= 0;
-    }
-    int64_t t;
-    int64_t pos = top0 + block_exclusive_scan(nb, &t, sh) + off;
-    for (int64_t i = lo; i < hi; ++i) {
-      int32_t* e = &tables[(int64_t)b * max_blocks + i];
-      if (*e < 0) continue;
-      stack[pos++] = *e;
-      *e = -1;
-    }
-    off += t;
-    __syncthreads();
-  }
-  if (tid == 0) {
+  trim_entries<true>(stack, top0, tables, max_blocks, lens, window, sink, batch, bs, sh, s_pre,
+                     s_lo);
+  if (threadIdx.x == 0) {
     *top = (int32_t)(top0 + total);
     *status = KVQ_OK;
   }

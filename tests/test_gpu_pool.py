@@ -76,3 +76,48 @@ def test_pool_release_overflow_changes_nothing():
     torch.cuda.synchronize()
     assert int(gp.status.item()) == kq.kvq.KVQ_ERR_OUT_OF_BLOCKS
     assert int(gp.top.item()) == 4 and int(lens.item()) == 16
+
+
+@pytest.mark.parametrize("B,window,sink", [(1500, 40, 20), (3, 70, 0), (1100, 1, 33)])
+def test_trim_large_batches_match_oracle(B, window, sink):
+    """Trim after placing long contexts: chunks of 1024 rows, many more
+    entries per chunk than threads, rows partly trimmed already (a second
+    trim after growth), and rows with nothing to trim; stack, top, tables and
+    status equal to the oracle's."""
+    need_gpu()
+    bs = 16
+    rng = np.random.default_rng(B + window)
+    lens = rng.integers(0, 2000 if B > 10 else 30000, size=B).astype(np.int32)
+    maxb = int(lens.max()) // bs + 40
+    n = int(sum((int(x) + 200) // bs + 2 for x in lens))
+    order = rng.permutation(n).astype(np.int32)
+    gp = GpuPool(n, B, maxb, order)
+    ostack, otop = ref.pool_init(n, order)
+    otables = np.full((B, maxb), -1, np.int32)
+    zero = np.zeros(B, np.int32)
+    glens = torch.zeros(B, dtype=torch.int32, device=DEV)
+    oslots, ost = ref.blocks_reserve(ostack, otop, otables, zero, lens, bs)
+    assert ost == 0
+    gslots = torch.empty(int(lens.sum()), dtype=torch.int64, device=DEV)
+    kq.kvq_blocks_reserve(gp.stack, gp.top, gp.tables, glens, torch.from_numpy(lens).to(DEV),
+                          bs, gslots, gp.status, glens)
+    cur = lens.copy()
+    for rnd in range(2):
+        ost = ref.blocks_trim(ostack, otop, otables, cur, window, sink, bs)
+        kq.kvq_blocks_trim(gp.stack, gp.top, gp.tables, torch.from_numpy(cur).to(DEV), window,
+                           sink, bs, gp.status)
+        torch.cuda.synchronize()
+        assert int(gp.status.item()) == ost, rnd
+        assert int(gp.top.item()) == int(otop[0]), rnd
+        assert np.array_equal(gp.stack.cpu().numpy(), ostack), rnd
+        assert np.array_equal(gp.tables.cpu().numpy(), otables), rnd
+        # grow every row by up to 180 tokens, then trim again
+        new = rng.integers(0, 180, size=B).astype(np.int32)
+        olens = np.zeros(B, np.int32)
+        _, ost = ref.blocks_reserve(ostack, otop, otables, cur, new, bs, olens)
+        assert ost == 0
+        gs = torch.empty(int(new.sum()), dtype=torch.int64, device=DEV)
+        g_cur = torch.from_numpy(cur).to(DEV)
+        kq.kvq_blocks_reserve(gp.stack, gp.top, gp.tables, g_cur, torch.from_numpy(new).to(DEV),
+                              bs, gs, gp.status, g_cur)
+        cur = olens
