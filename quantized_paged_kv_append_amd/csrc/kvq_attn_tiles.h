@@ -492,6 +492,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 // waves per decode / multi-query workgroup
 constexpr int kNW = kDecodeWaves;
+// Query heads (one wave each) per workgroup of the cross-split merges: up
+// to kReduceHeads when the merges number kReduceGroupWaves or more (one-wave
+// workgroups by the ten thousand cost dispatch time), else one, which
+// spreads a small merge over more CUs.
+constexpr int kReduceHeads = 4;
+constexpr int64_t kReduceGroupWaves = 4096;
+inline int reduce_heads_per_group(int64_t waves) {
+  return waves >= kReduceGroupWaves ? kReduceHeads : 1;
+}
 
 }  // namespace
 }  // namespace kvq

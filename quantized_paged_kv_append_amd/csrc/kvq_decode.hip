@@ -606,15 +606,19 @@ struct ReduceArgs {
 };
 
 
-// One wave per (sequence, query head). Lane s holds split s's (m, l); the
-// partial accumulators of up to 32 splits are loaded in the same batch, so a
-// sequence with up to 32 splits is merged after a single memory round trip.
+// One wave per (sequence, query head), one or kReduceHeads heads per
+// workgroup.
+// Lane s holds split s's (m, l); the partial accumulators of up to 32
+// splits are loaded in the same batch, so a sequence with up to 32 splits is
+// merged after a single memory round trip.
 template <int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(ReduceArgs a) {
+__global__ __launch_bounds__(64 * kReduceHeads) void decode_reduce_kernel(ReduceArgs a) {
   constexpr int EPL = D / 64;  // output elements per lane
   constexpr int KB = 32;       // splits per batch of loads
   typedef float floatE __attribute__((ext_vector_type(EPL)));
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int h = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, b = blockIdx.y;
+  if (h >= a.Hq) return;
   const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, a.BS, a.H, a.split_blocks);
   int off, ns;
   plan_sequence(pa, b, lane, off, ns);
@@ -746,11 +750,12 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
   ra.batch = p.batch;
   ra.max_len = p.max_context_len;
   ra.split_blocks = p.split_blocks;
-  dim3 grid(p.num_q_heads, p.batch);
+  const int hpg = reduce_heads_per_group((int64_t)p.num_q_heads * p.batch);
+  dim3 grid((p.num_q_heads + hpg - 1) / hpg, p.batch);
   if (p.head_dim == 128)
-    decode_reduce_kernel<128><<<grid, 64, 0, stream>>>(ra);
+    decode_reduce_kernel<128><<<grid, kWave * hpg, 0, stream>>>(ra);
   else
-    decode_reduce_kernel<64><<<grid, 64, 0, stream>>>(ra);
+    decode_reduce_kernel<64><<<grid, kWave * hpg, 0, stream>>>(ra);
   return hipGetLastError();
 }
 

@@ -437,7 +437,9 @@ void prefill_split_kernel(PrefillArgs pa) {
 }
 
 // Cross-split merge for multi-query attention, as decode_reduce: one wave
-// per (query head, query i, sequence b); split j's partial of column
+// per (query head, query i, sequence b), one or kReduceHeads heads per
+// workgroup;
+// split j's partial of column
 // c = i G + h % G sits at ((b J + j) H + g) CT16 + c.
 struct PrefillReduceArgs {
   const float* ws_acc;
@@ -450,11 +452,14 @@ struct PrefillReduceArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(64) void prefill_reduce_kernel(PrefillReduceArgs a) {
+__global__ __launch_bounds__(64 * kReduceHeads) void prefill_reduce_kernel(PrefillReduceArgs a) {
   constexpr int EPL = D / 64;
   constexpr int KB = 32;
   typedef float floatE __attribute__((ext_vector_type(EPL)));
-  const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int h = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, i = blockIdx.y,
+            b = blockIdx.z;
+  if (h >= a.Hq) return;
   const int L = min(a.context_lens[b], a.max_len);
   const int q0 = a.qstart[b];
   const int nq = min(a.qstart[b + 1] - q0, L);
@@ -625,11 +630,13 @@ hipError_t launch_prefill(const PrefillPlan& pp, hipStream_t stream) {
   ra.J = pp.splits;
   ra.S = pp.split_blocks;
   ra.CT = pp.col_tiles;
-  const dim3 grid(p.num_q_heads, pp.max_query_len, p.batch);
+  const int hpg =
+      reduce_heads_per_group((int64_t)p.num_q_heads * pp.max_query_len * p.batch);
+  const dim3 grid((p.num_q_heads + hpg - 1) / hpg, pp.max_query_len, p.batch);
   if (d == 128)
-    prefill_reduce_kernel<128><<<grid, 64, 0, stream>>>(ra);
+    prefill_reduce_kernel<128><<<grid, kWave * hpg, 0, stream>>>(ra);
   else
-    prefill_reduce_kernel<64><<<grid, 64, 0, stream>>>(ra);
+    prefill_reduce_kernel<64><<<grid, kWave * hpg, 0, stream>>>(ra);
   return hipGetLastError();
 }
 
