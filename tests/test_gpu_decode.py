@@ -258,3 +258,20 @@ def test_decode_reuses_one_workspace_across_shapes():
                                 split_blocks=split)
         torch.cuda.synchronize()
         assert_decode_close(out, exp, f"lens {lens} split {split}")
+
+
+@pytest.mark.parametrize("code,mode,bs,split", [("fp8", "token_sym", 16, 0),
+                                                ("int4", "group_asym", 32, 3)])
+def test_decode_many_merges_grouped(code, mode, bs, split):
+    """700 sequences x 6 query heads: 4200 cross-split merges, so the merge
+    runs four heads per workgroup and its last workgroup of every sequence
+    has two heads past the end; skewed short contexts, empty ones included,
+    with several splits each."""
+    need_gpu()
+    rng = np.random.default_rng(7)
+    lens = tuple(int(x) for x in rng.integers(0, 200, size=700))
+    w, L, LL, s, q = _setup(code, lens=lens, G=3, H=2, mode=mode, bs=bs, d=64)
+    got, exp = _run(w, L, LL, s, q, split_blocks=split)
+    assert_decode_close(got, exp, f"{code} grouped merges")
+    empty = np.nonzero(np.asarray(lens) == 0)[0]
+    assert (got[torch.from_numpy(empty).to(got.device)] == 0).all()
