@@ -78,7 +78,7 @@ int64_t decode_item_bound(const kvq_layout* L, int64_t batch, int64_t max_contex
   const int64_t a = batch * ceil_div(nmax, W * wmin);
   const int64_t c = batch + std::max(ceil_div(int64_t(1) << kvq::kDecodeTargetWavesLog2,
                                               W * L->num_kv_heads),
-                                     ceil_div(batch * nmax, W * 64));
+                                     ceil_div(batch * nmax, W * kvq::kDecodeSkewWaveBlocks));
   return std::min(a, c);
 }
 

@@ -54,7 +54,7 @@ namespace {
 // synchronization is needed:
 //   n_b  = ceil(min(len_b, max_len) / BS)          blocks of sequence b
 //   S    = split_blocks, or kDecodeWaves * clamp(ceil(H sum_b n_b / 2^12),
-//          ceil(32 / BS), 64)                        blocks per split
+//          ceil(32 / BS), 32)                        blocks per split
 //   ns_b = ceil(n_b / S)                            splits of sequence b
 // Items (b, j), j < ns_b, are numbered sequence-major. The partial of item
 // (b, j) for query head h is row Hq off_b + h ns_b + j of the workspace, with
@@ -157,8 +157,8 @@ __device__ __forceinline__ int wave_reduce_i(int x) {
 // is cut into one round of shares (2^kDecodeUniformWavesLog2 waves: two
 // workgroups per CU, up to kDecodeMaxWaveBlocks blocks each), since equal
 // items need no balancing and fewer, longer shares pay the start-up chain
-// less often; any other batch into twice as many shorter shares (at most 64
-// blocks), which the dispatcher balances.
+// less often; any other batch into twice as many shorter shares (at most
+// kDecodeSkewWaveBlocks blocks), which the dispatcher balances.
 __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, const int* len0) {
   if (p.split_blocks > 0) return p.split_blocks;
   // block counts fit in int32: the host bounds batch * ceil(max_len / bs)
@@ -179,7 +179,7 @@ __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, co
   nmin = wave_reduce_i<false>(nmin);
   const bool uniform = (int64_t)nmax * 8 <= (int64_t)nmin * 9;
   const int lg = uniform ? kDecodeUniformWavesLog2 : kDecodeTargetWavesLog2;
-  const int cap = uniform ? kDecodeMaxWaveBlocks : 64;
+  const int cap = uniform ? kDecodeMaxWaveBlocks : kDecodeSkewWaveBlocks;
   int64_t w = (tot * p.H + (int64_t(1) << lg) - 1) >> lg;
   const int wmin = (kDecodeMinWaveTokens + p.bs - 1) / p.bs;
   w = w < wmin ? wmin : w > cap ? cap : w;
@@ -486,7 +486,7 @@ __device__ __forceinline__ void workgroup_item(int H, int w, int& item, int& g) 
 }
 
 // One item of the plan per workgroup and KV head: the split's S blocks are
-// cut into kNW consecutive shares of at most 64 blocks, one per wave; the
+// cut into kNW consecutive shares, one per wave; the
 // waves merge their softmax states through LDS and wave 0 writes the split's
 // partial.
 

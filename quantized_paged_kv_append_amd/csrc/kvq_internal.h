@@ -78,13 +78,15 @@ struct DecodePlan {
 // at 0 the per-wave share is ceil(H * total_blocks / 2^lg) blocks, clamped to
 // [ceil(kDecodeMinWaveTokens / bs), cap], with lg, cap =
 // kDecodeUniformWavesLog2, kDecodeMaxWaveBlocks for a batch of nearly equal
-// lengths and kDecodeTargetWavesLog2, 64 otherwise. The host's item bound
-// assumes the second pair, which yields more items for any lengths.
+// lengths and kDecodeTargetWavesLog2, kDecodeSkewWaveBlocks otherwise. The
+// host's item bound assumes the second pair, which yields more items for any
+// lengths.
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeMaxWaveBlocks = 256;
 constexpr int kDecodeTargetWavesLog2 = 12;
 constexpr int kDecodeUniformWavesLog2 = 11;
 constexpr int kDecodeMinWaveTokens = 32;
+constexpr int kDecodeSkewWaveBlocks = 32;
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
 bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
