@@ -1,0 +1,85 @@
+"""The decode's split plan is made on the device from the context lengths; the
+grid and the workspace are sized on the host from batch and max_context_len
+alone. This checks, for many length mixes, that the plan's item count (its
+rule replayed here from the planning constants in the library's internal
+header) never exceeds the bound the host sizes the workspace for (read back
+from kvq_decode_workspace_bytes), so that no split is left out and no partial
+lands outside the workspace. Host-only; no GPU."""
+import math
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = Path(__file__).resolve().parents[1]
+kq = pytest.importorskip("quantized_paged_kv_append_amd")
+
+
+def _constants():
+    text = (ROOT / "quantized_paged_kv_append_amd" / "csrc" / "kvq_internal.h").read_text()
+    names = ("kDecodeWaves", "kDecodeMaxWaveBlocks", "kDecodeTargetWavesLog2",
+             "kDecodeUniformWavesLog2", "kDecodeMinWaveTokens", "kDecodeSkewWaveBlocks")
+    out = {}
+    for n in names:
+        m = re.search(rf"constexpr int {n} = (\d+);", text)
+        assert m, n
+        out[n] = int(m.group(1))
+    return out
+
+
+def _plan_items(lens, max_len, bs, H, c):
+    """Items of the device plan (the rule the split kernel and the reduce
+    derive from the lengths): every non-empty or empty sequence's splits."""
+    n = (np.minimum(np.maximum(lens, 0), max_len) + bs - 1) // bs
+    tot = int(n.sum())
+    nonzero = n[n > 0]
+    uniform = len(nonzero) > 0 and int(n.max()) * 8 <= int(nonzero.min()) * 9
+    lg = c["kDecodeUniformWavesLog2"] if uniform else c["kDecodeTargetWavesLog2"]
+    cap = c["kDecodeMaxWaveBlocks"] if uniform else c["kDecodeSkewWaveBlocks"]
+    wmin = math.ceil(c["kDecodeMinWaveTokens"] / bs)
+    w = min(max(math.ceil(tot * H / 2 ** lg), wmin), cap)
+    S = c["kDecodeWaves"] * w
+    return int(((n + S - 1) // S).sum())
+
+
+def _host_bound(L, batch, Hq, max_len, d):
+    """Items the workspace holds: kvq_decode_workspace_bytes is
+    round_up(items d 4, 256) + round_up(items 2 4, 256) for items = bound Hq."""
+    total = kq.kvq_decode_workspace_bytes(L, batch, Hq, max_len)
+    lo, hi = 0, 1 << 40
+    while lo < hi:   # largest bound whose workspace fits in `total`
+        mid = (lo + hi + 1) // 2
+        items = mid * Hq
+        need = -(-items * d * 4 // 256) * 256 + -(-items * 8 // 256) * 256
+        if need <= total:
+            lo = mid
+        else:
+            hi = mid - 1
+    return lo
+
+
+@pytest.mark.parametrize("H,Hq,d,bs", [(8, 64, 128, 16), (8, 32, 128, 32), (2, 4, 64, 16),
+                                       (1, 8, 128, 16)])
+def test_plan_items_never_exceed_the_host_bound(H, Hq, d, bs):
+    c = _constants()
+    L = kq.make_layout(H, d, bs, "int8", src_dtype=torch.bfloat16)
+    rng = np.random.default_rng(H * 1000 + bs)
+    cases = []
+    for batch in (1, 2, 3, 16, 64, 255, 256, 257, 1000, 3000):
+        for max_len in (1, 15, 16, 17, 1000, 32768, 131072):
+            cases.append((batch, max_len, np.full(batch, max_len)))          # equal
+            cases.append((batch, max_len, rng.integers(0, max_len + 1, batch)))
+            skew = np.zeros(batch, np.int64)
+            skew[0] = max_len                                               # one long
+            cases.append((batch, max_len, skew))
+            ln = np.minimum(np.round(max(max_len // 16, 1) * np.exp(rng.normal(0, 1, batch))),
+                            max_len)
+            cases.append((batch, max_len, ln.astype(np.int64)))             # log-normal
+    for batch, max_len, lens in cases:
+        if batch * ((max_len + bs - 1) // bs) > 2 ** 31 - 1:
+            continue
+        items = _plan_items(lens.astype(np.int64), max_len, bs, H, c)
+        bound = _host_bound(L, batch, Hq, max_len, d)
+        assert items <= bound, (batch, max_len, items, bound)
