@@ -197,16 +197,16 @@ def append_bytes_per_token(w):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
     if args.offload_blocks:
         offload_bench(args)
         return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
     import quantized_paged_kv_append_amd as kq
 
     dev = torch.device("cuda:0")
