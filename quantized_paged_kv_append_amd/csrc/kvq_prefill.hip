@@ -454,7 +454,10 @@ struct PrefillReduceArgs {
 template <int D>
 __global__ __launch_bounds__(64 * kReduceHeads) void prefill_reduce_kernel(PrefillReduceArgs a) {
   constexpr int EPL = D / 64;
-  constexpr int KB = 32;
+  // splits per batch of loads: 16 holds the kernel at 80 VGPRs (six waves
+  // per SIMD; with 32, each load's 64-bit address among them, 144 and three),
+  // at one more round trip per 16 splits past the first 16
+  constexpr int KB = 16;
   typedef float floatE __attribute__((ext_vector_type(EPL)));
   const int lane = threadIdx.x & (kWave - 1);
   const int h = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, i = blockIdx.y,
