@@ -332,23 +332,18 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
         s = amax == 0.0f ? 1.0f : div_rn(amax, 7.0f);
       }
       const float inv = __builtin_amdgcn_rcpf(s);   // within 1 ulp of 1/s
-      bool tie = recip_unsafe(s);
+      const bool unsafe = recip_unsafe(s);
+      // an element near a rounding boundary (rare) takes the exact quotient
+      // on its own, so a wave redoes only the elements some lane needs
 #pragma unroll
       for (int i = 0; i < NS; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float y = x[i][e] * inv;
-          const float qq = rne(y);
-          tie |= near_half(y, qq);
+          float qq = rne(y);
+          if (unsafe || near_half(y, qq)) qq = rne(div_rn(x[i][e], s));
           q[i][e] = (int)fminf(fmaxf(qq, -7.0f), 7.0f);
         }
-      if (tie) {  // rare: this lane's codes from the exact quotient
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            q[i][e] = (int)fminf(fmaxf(rne(div_rn(x[i][e], s)), -7.0f), 7.0f);
-      }
       if (live && k == 0) S.scale[rowi] = s;
     } else {
       float sg[NS];
@@ -400,29 +395,20 @@ __global__ __launch_bounds__(256) void append_int4_kernel(RowArgs a) {
       }
       // A dynamic range bounds |x / s| by 15; static scales do not, so the
       // rounded quotient is clipped to +-15 before the integer conversion.
-      bool tie = false;
+      // an element near a rounding boundary (rare) takes the exact quotient
+      // on its own, so a wave redoes only the elements some lane needs
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        tie |= recip_unsafe(sg[i]);
+        const bool unsafe = recip_unsafe(sg[i]);
         const float inv = __builtin_amdgcn_rcpf(sg[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float y = x[i][e] * inv;
           float qq = rne(y);
-          tie |= near_half(y, qq);
+          if (unsafe || near_half(y, qq)) qq = rne(div_rn(x[i][e], sg[i]));
           if constexpr (STATIC) qq = fminf(fmaxf(qq, -15.0f), 15.0f);
           q[i][e] = min(max((int)qq + zg[i], 0), 15);
         }
-      }
-      if (tie) {
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float qq = rne(div_rn(x[i][e], sg[i]));
-            if constexpr (STATIC) qq = fminf(fmaxf(qq, -15.0f), 15.0f);
-            q[i][e] = min(max((int)qq + zg[i], 0), 15);
-          }
       }
       if (live && k == 0) {
         float* sp = S.scale + rowi * NS;
