@@ -160,7 +160,6 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
       }
       return;
     }
-    // the exact-quotient paths unpack the inputs again rather than keep them
     float x[NV][8];
 #pragma unroll
     for (int u = 0; u < NV; ++u) unpack8<BF16>(w[u], x[u]);
@@ -179,7 +178,9 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
     }
     const float inv = __builtin_amdgcn_rcpf(s);   // within 1 ulp of 1/s
     uint32_t o[NV][2];
-    bool tie = recip_unsafe(s);
+    // an element near a rounding boundary (rare) takes the exact quotient on
+    // its own, so a wave redoes only the elements some lane needs
+    const bool unsafe = recip_unsafe(s);
     if constexpr (CODE == KVQ_CODE_INT8) {
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
@@ -187,25 +188,12 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float y = x[u][e] * inv;
-          const float q = rne(y);
-          tie |= near_half(y, q);
+          float q = rne(y);
+          if (unsafe || near_half(y, q)) q = rne(div_rn(x[u][e], s));
           c[e] = (int)fminf(fmaxf(q, -127.0f), 127.0f);
         }
         o[u][0] = pack_bytes(c[0], c[1], c[2], c[3]);
         o[u][1] = pack_bytes(c[4], c[5], c[6], c[7]);
-      }
-      if (tie) {  // rare: redo this lane's codes with the exact quotient
-#pragma unroll
-        for (int u = 0; u < NV; ++u) {
-          float xe[8];
-          unpack8<BF16>(w[u], xe);
-          int c[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            c[e] = (int)fminf(fmaxf(rne(div_rn(xe[e], s)), -127.0f), 127.0f);
-          o[u][0] = pack_bytes(c[0], c[1], c[2], c[3]);
-          o[u][1] = pack_bytes(c[4], c[5], c[6], c[7]);
-        }
       }
     } else {
 #pragma unroll
@@ -214,26 +202,11 @@ __global__ __launch_bounds__(256) void append_bytes_kernel(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           y[e] = x[u][e] * inv;
-          tie |= fp8_near_tie(y[e]);
+          if (unsafe || fp8_near_tie(y[e])) y[e] = div_rn(x[u][e], s);
           if constexpr (STATIC) y[e] = sat448(y[e]);
         }
         o[u][0] = fp8x4(y[0], y[1], y[2], y[3]);
         o[u][1] = fp8x4(y[4], y[5], y[6], y[7]);
-      }
-      if (tie) {
-#pragma unroll
-        for (int u = 0; u < NV; ++u) {
-          float xe[8];
-          unpack8<BF16>(w[u], xe);
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            y[e] = div_rn(xe[e], s);
-            if constexpr (STATIC) y[e] = sat448(y[e]);
-          }
-          o[u][0] = fp8x4(y[0], y[1], y[2], y[3]);
-          o[u][1] = fp8x4(y[4], y[5], y[6], y[7]);
-        }
       }
     }
     if (live) {
