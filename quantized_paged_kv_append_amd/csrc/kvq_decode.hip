@@ -54,7 +54,7 @@ namespace {
 // synchronization is needed:
 //   n_b  = ceil(min(len_b, max_len) / BS)          blocks of sequence b
 //   S    = split_blocks, or kDecodeWaves * clamp(ceil(H sum_b n_b / 2^12),
-//          ceil(32 / BS), 32)                        blocks per split
+//          ceil(32 / BS), 32 or 64)                  blocks per split
 //   ns_b = ceil(n_b / S)                            splits of sequence b
 // Items (b, j), j < ns_b, are numbered sequence-major. The partial of item
 // (b, j) for query head h is row Hq off_b + h ns_b + j of the workspace, with
@@ -65,10 +65,11 @@ namespace {
 struct PlanArgs {
   const int32_t* lens;
   int32_t batch, max_len, bs, H, split_blocks;
+  int32_t skew_cap;  // per-wave share cap for batches of unequal lengths
 };
 
 __device__ __forceinline__ PlanArgs plan_args(const int32_t* lens, int batch, int max_len,
-                                              int bs, int H, int split_blocks) {
+                                              int bs, int H, int split_blocks, int skew_cap) {
   PlanArgs p;
   p.lens = lens;
   p.batch = batch;
@@ -76,6 +77,7 @@ __device__ __forceinline__ PlanArgs plan_args(const int32_t* lens, int batch, in
   p.bs = bs;
   p.H = H;
   p.split_blocks = split_blocks;
+  p.skew_cap = skew_cap;
   return p;
 }
 
@@ -158,7 +160,7 @@ __device__ __forceinline__ int wave_reduce_i(int x) {
 // workgroups per CU, up to kDecodeMaxWaveBlocks blocks each), since equal
 // items need no balancing and fewer, longer shares pay the start-up chain
 // less often; any other batch into twice as many shorter shares (at most
-// kDecodeSkewWaveBlocks blocks), which the dispatcher balances.
+// decode_skew_cap(key mode) blocks), which the dispatcher balances.
 __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, const int* len0) {
   if (p.split_blocks > 0) return p.split_blocks;
   // block counts fit in int32: the host bounds batch * ceil(max_len / bs)
@@ -179,7 +181,7 @@ __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, co
   nmin = wave_reduce_i<false>(nmin);
   const bool uniform = (int64_t)nmax * 8 <= (int64_t)nmin * 9;
   const int lg = uniform ? kDecodeUniformWavesLog2 : kDecodeTargetWavesLog2;
-  const int cap = uniform ? kDecodeMaxWaveBlocks : kDecodeSkewWaveBlocks;
+  const int cap = uniform ? kDecodeMaxWaveBlocks : p.skew_cap;
   int64_t w = (tot * p.H + (int64_t(1) << lg) - 1) >> lg;
   const int wmin = (kDecodeMinWaveTokens + p.bs - 1) / p.bs;
   w = w < wmin ? wmin : w > cap ? cap : w;
@@ -501,7 +503,8 @@ void decode_split_kernel(DecodeArgs a) {
   int wg_item, g;
   workgroup_item(a.H, blockIdx.x, wg_item, g);
   // every wave derives the same plan, so the early exit is workgroup-uniform
-  const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, BS, a.H, a.split_blocks);
+  const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, BS, a.H, a.split_blocks,
+                                decode_skew_cap(MODE));
   PlanItem it;
   if (!plan_find_item(pa, wg_item, lane, it)) return;
   const int S = it.S;
@@ -603,6 +606,7 @@ struct ReduceArgs {
   int32_t batch;
   int32_t max_len;
   int32_t split_blocks;
+  int32_t skew_cap;  // the split kernel's plan: decode_skew_cap of the key mode
 };
 
 
@@ -619,7 +623,8 @@ __global__ __launch_bounds__(64 * kReduceHeads) void decode_reduce_kernel(Reduce
   const int lane = threadIdx.x & (kWave - 1);
   const int h = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, b = blockIdx.y;
   if (h >= a.Hq) return;
-  const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, a.BS, a.H, a.split_blocks);
+  const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, a.BS, a.H, a.split_blocks,
+                                a.skew_cap);
   int off, ns;
   plan_sequence(pa, b, lane, off, ns);
   const int64_t base = (int64_t)a.Hq * off + (int64_t)h * ns;
@@ -750,6 +755,7 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
   ra.batch = p.batch;
   ra.max_len = p.max_context_len;
   ra.split_blocks = p.split_blocks;
+  ra.skew_cap = decode_skew_cap(p.k_mode);
   const int hpg = reduce_heads_per_group((int64_t)p.num_q_heads * p.batch);
   dim3 grid((p.num_q_heads + hpg - 1) / hpg, p.batch);
   if (p.head_dim == 128)

@@ -86,7 +86,16 @@ constexpr int kDecodeMaxWaveBlocks = 256;
 constexpr int kDecodeTargetWavesLog2 = 12;
 constexpr int kDecodeUniformWavesLog2 = 11;
 constexpr int kDecodeMinWaveTokens = 32;
+// Per-wave share cap for batches of unequal lengths: 32 blocks, or 64 with
+// per-channel keys, whose items cost more to start (each block folds its
+// scales into the query); the host bound takes the smaller, which yields
+// more items.
 constexpr int kDecodeSkewWaveBlocks = 32;
+constexpr int kDecodeSkewWaveBlocksChannel = 64;
+__host__ __device__ constexpr int decode_skew_cap(int32_t k_mode) {
+  return k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM ? kDecodeSkewWaveBlocksChannel
+                                               : kDecodeSkewWaveBlocks;
+}
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
 bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,

@@ -20,7 +20,8 @@ kq = pytest.importorskip("quantized_paged_kv_append_amd")
 def _constants():
     text = (ROOT / "quantized_paged_kv_append_amd" / "csrc" / "kvq_internal.h").read_text()
     names = ("kDecodeWaves", "kDecodeMaxWaveBlocks", "kDecodeTargetWavesLog2",
-             "kDecodeUniformWavesLog2", "kDecodeMinWaveTokens", "kDecodeSkewWaveBlocks")
+             "kDecodeUniformWavesLog2", "kDecodeMinWaveTokens", "kDecodeSkewWaveBlocks",
+             "kDecodeSkewWaveBlocksChannel")
     out = {}
     for n in names:
         m = re.search(rf"constexpr int {n} = (\d+);", text)
@@ -37,7 +38,8 @@ def _plan_items(lens, max_len, bs, H, c):
     nonzero = n[n > 0]
     uniform = len(nonzero) > 0 and int(n.max()) * 8 <= int(nonzero.min()) * 9
     lg = c["kDecodeUniformWavesLog2"] if uniform else c["kDecodeTargetWavesLog2"]
-    cap = c["kDecodeMaxWaveBlocks"] if uniform else c["kDecodeSkewWaveBlocks"]
+    cap = c["kDecodeMaxWaveBlocks"] if uniform else min(c["kDecodeSkewWaveBlocks"],
+                                                        c["kDecodeSkewWaveBlocksChannel"])
     wmin = math.ceil(c["kDecodeMinWaveTokens"] / bs)
     w = min(max(math.ceil(tot * H / 2 ** lg), wmin), cap)
     S = c["kDecodeWaves"] * w
