@@ -33,6 +33,7 @@ struct PrefillArgs {
   int32_t J;    // splits per sequence in the grid
   int32_t S;    // blocks per split
   int32_t CT;   // column tiles per (sequence, KV head)
+  int32_t max_q;  // bound on every sequence's query count (sizes CT and the grid)
   int32_t TW;   // column tiles per workgroup: 1, 2 or 4 (4 / TW waves per tile)
   int32_t window;   // > 0: each query sees its last `window` positions ...
   int32_t sink;     // ... and the first `sink` positions
@@ -153,7 +154,8 @@ void prefill_split_kernel(PrefillArgs pa) {
   if (b >= a.batch) return;
   const int L = min(a.context_lens[b], a.max_len);
   const int q0 = pa.qstart[b];
-  const int nq = min(pa.qstart[b + 1] - q0, L);
+  // queries past max_q would index past the CT * 16 columns of a partial row
+  const int nq = min(min(pa.qstart[b + 1] - q0, L), pa.max_q);
   const int ncol = nq * a.G;
   const int nblk = (L + BS - 1) / BS;
   const int s0 = j * pa.S;
@@ -449,6 +451,7 @@ struct PrefillReduceArgs {
   void* out;
   int32_t out_dtype;
   int32_t Hq, H, G, BS, max_len, J, S, CT;
+  int32_t max_q;  // as in PrefillArgs
 };
 
 template <int D>
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(64 * kReduceHeads) void prefill_reduce_kernel(Prefi
   if (h >= a.Hq) return;
   const int L = min(a.context_lens[b], a.max_len);
   const int q0 = a.qstart[b];
-  const int nq = min(a.qstart[b + 1] - q0, L);
+  const int nq = min(min(a.qstart[b + 1] - q0, L), a.max_q);
   if (i >= nq) return;
   const int ns = ((L + a.BS - 1) / a.BS + a.S - 1) / a.S;
   const int64_t cols = (int64_t)a.CT * 16;
@@ -599,6 +602,7 @@ hipError_t launch_prefill(const PrefillPlan& pp, hipStream_t stream) {
   pa.J = pp.splits;
   pa.S = pp.split_blocks;
   pa.CT = pp.col_tiles;
+  pa.max_q = pp.max_query_len;
   pa.window = pp.window;
   pa.sink = pp.sink;
   pa.TW = 1;   // set per launch shape
@@ -633,6 +637,7 @@ hipError_t launch_prefill(const PrefillPlan& pp, hipStream_t stream) {
   ra.J = pp.splits;
   ra.S = pp.split_blocks;
   ra.CT = pp.col_tiles;
+  ra.max_q = pp.max_query_len;
   const int hpg =
       reduce_heads_per_group((int64_t)p.num_q_heads * pp.max_query_len * p.batch);
   const dim3 grid((p.num_q_heads + hpg - 1) / hpg, pp.max_query_len, p.batch);

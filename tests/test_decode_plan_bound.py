@@ -85,3 +85,43 @@ def test_plan_items_never_exceed_the_host_bound(H, Hq, d, bs):
         items = _plan_items(lens.astype(np.int64), max_len, bs, H, c)
         bound = _host_bound(L, batch, Hq, max_len, d)
         assert items <= bound, (batch, max_len, items, bound)
+
+
+def test_prefill_partial_index_stays_in_the_workspace():
+    """Multi-query attention: split j of sequence b writes column c's partial
+    at ((b J + j) H + g) CT16 + c for c < nq_b G, with CT = ceil(max_query_len
+    G / 16) and J from max_context_len; the kernels cut nq_b to
+    min(query_start[b+1] - query_start[b], len_b, max_query_len). A sequence
+    with more queries than max_query_len (a broken precondition) must not
+    reach past the workspace. The rule is replayed here; the kernels' own
+    expression is checked for the same cut."""
+    src = (ROOT / "quantized_paged_kv_append_amd" / "csrc" / "kvq_prefill.hip").read_text()
+    assert src.count("min(min(pa.qstart[b + 1] - q0, L), pa.max_q)") == 1
+    assert src.count("min(min(a.qstart[b + 1] - q0, L), a.max_q)") == 1
+    rng = np.random.default_rng(7)
+    for H, Hq, d, bs in ((8, 64, 128, 16), (2, 4, 64, 32), (8, 32, 128, 16)):
+        G = Hq // H
+        L = kq.make_layout(H, d, bs, "int8", src_dtype=torch.bfloat16)
+        for _ in range(200):
+            B = int(rng.integers(1, 9))
+            max_q = int(rng.integers(1, 40))
+            max_len = int(rng.integers(max_q, 3000))
+            lens = rng.integers(0, max_len + 1, B)
+            # query counts up to 3x the bound: the clamp must hold them
+            nq_raw = rng.integers(0, 3 * max_q + 1, B)
+            total = kq.kvq_prefill_workspace_bytes(L, B, Hq, max_q, max_len)
+            S = min(64, max(32, -(-max(1, -(-max_len // bs)) // 16)))
+            J = -(-max(1, -(-max_len // bs)) // S)
+            CT = -(-max_q * G // 16)
+            partials = B * J * H * CT * 16
+            need = -(-partials * d * 4 // 256) * 256 + -(-partials * 8 // 256) * 256
+            assert need <= total
+            worst = -1
+            for b in range(B):
+                nq = min(int(nq_raw[b]), int(lens[b]), max_q)
+                nblk = -(-int(lens[b]) // bs)
+                for j in range(J):
+                    if j * S >= nblk or nq == 0:
+                        continue
+                    worst = max(worst, ((b * J + j) * H + (H - 1)) * CT * 16 + nq * G - 1)
+            assert worst < partials, (B, max_q, max_len, worst, partials)
