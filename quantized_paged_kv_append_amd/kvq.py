@@ -109,6 +109,99 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+# ---- argument validation ----------------------------------------------------
+# The C ABI sees raw pointers only: a tensor of the wrong dtype, on the host,
+# too small or with a strided inner dimension would be read or written as if
+# it were right. Every entry point below checks its tensors first, in the
+# order dtype, shape and size, layout in memory, then device, and raises
+# ValueError naming the argument before anything reaches the library.
+
+_SRC_DTYPES = {KVQ_F16: torch.float16, KVQ_BF16: torch.bfloat16}
+
+
+def _need(t, name, dtypes, numel=None, min_numel=None, ndim=None, contiguous=True,
+          optional=False):
+    """Check one tensor argument; returns it unchanged."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name}: a tensor is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        want = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name}: dtype {str(t.dtype).replace('torch.', '')}, expected {want}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: {t.dim()}-D, expected {ndim}-D")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _on_device(**tensors):
+    """Last check of every entry point: all tensor arguments on the GPU."""
+    for name, t in tensors.items():
+        if isinstance(t, PagedCache):
+            for n, p in t.planes.items():
+                if p is not None and not p.is_cuda:
+                    raise ValueError(f"{name} plane {n}: must be a CUDA (HIP) device tensor")
+        elif t is not None and not t.is_cuda:
+            raise ValueError(f"{name}: must be a CUDA (HIP) device tensor")
+
+
+_LAYOUT_FIELDS = ("num_kv_heads", "head_dim", "block_size", "group_size", "k_code", "v_code",
+                  "k_mode", "v_mode", "src_dtype")
+
+
+def _need_cache(layout, cache):
+    """The cache's planes were sized for this layout."""
+    if not isinstance(cache, PagedCache):
+        raise ValueError(f"cache: expected a PagedCache, got {type(cache).__name__}")
+    for f in _LAYOUT_FIELDS:
+        if getattr(cache.layout, f) != getattr(layout, f):
+            raise ValueError(f"cache: made for a layout with {f} = "
+                             f"{getattr(cache.layout, f)}, called with {getattr(layout, f)}")
+
+
+def _need_rows(t, name, layout, T=None):
+    """K or V rows: [T][H][d] or [T][H*d] in the layout's source dtype, each
+    row's H*d elements contiguous (rows themselves may be strided)."""
+    H, d = layout.num_kv_heads, layout.head_dim
+    want = _SRC_DTYPES.get(layout.src_dtype)
+    if want is None:
+        raise ValueError(f"layout.src_dtype {layout.src_dtype} is not F16 or BF16")
+    _need(t, name, want, contiguous=False)
+    if t.dim() == 3:
+        if tuple(t.shape[1:]) != (H, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{name}: shape {tuple(t.shape)} strides {t.stride()}, expected "
+                             f"[T][{H}][{d}] with contiguous rows")
+    elif t.dim() == 2:
+        if t.shape[1] != H * d or t.stride(1) != 1:
+            raise ValueError(f"{name}: shape {tuple(t.shape)} strides {t.stride()}, expected "
+                             f"[T][{H * d}] with contiguous rows")
+    else:
+        raise ValueError(f"{name}: {t.dim()}-D, expected [T][H][d] or [T][H*d]")
+    if T is not None and t.shape[0] != T:
+        raise ValueError(f"{name}: {t.shape[0]} rows, expected {T} (as k)")
+    if t.shape[0] > 1 and t.stride(0) < H * d:
+        raise ValueError(f"{name}: row stride {t.stride(0)} below H*d = {H * d}")
+    return t
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _capturing():
+    return torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -169,7 +262,16 @@ def kvq_append(layout, cache: PagedCache, k, v, slot_mapping, stage_rows=None,
     """k, v: device [T][H][d] (or [T][H*d], rows may be strided) in the layout's
     source dtype; slot_mapping: device int64 [T]; stage_rows: device int32 [T]
     for per-channel keys."""
+    _need_rows(k, "k", layout)
     T = k.shape[0]
+    _need_rows(v, "v", layout, T)
+    _need(slot_mapping, "slot_mapping", torch.int64, numel=T)
+    chan = layout.k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM
+    _need(stage_rows, "stage_rows", torch.int32, numel=T, optional=not chan)
+    if not chan and stage_rows is not None:
+        raise ValueError("stage_rows: only for per-channel keys (channel_block)")
+    _need_cache(layout, cache)
+    _on_device(cache=cache, k=k, v=v, slot_mapping=slot_mapping, stage_rows=stage_rows)
     _check("kvq_append", _lib.kvq_append(
         C.byref(layout), C.byref(cache.struct), _ptr(k), _ptr(v),
         k.stride(0) if T else 0, v.stride(0) if T else 0, T, _ptr(slot_mapping),
@@ -182,7 +284,32 @@ def kvq_append_static(layout, cache: PagedCache, k, v, slot_mapping, k_scales,
     [H] (TOKEN_SYM), [H][d/32] (GROUP_ASYM, with uint8 zero points of that
     shape) or [H][d] (per-channel keys, with stage_rows as for kvq_append);
     None for a 16-bit passthrough side."""
+    _need_rows(k, "k", layout)
     T = k.shape[0]
+    _need_rows(v, "v", layout, T)
+    _need(slot_mapping, "slot_mapping", torch.int64, numel=T)
+    chan = layout.k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM
+    _need(stage_rows, "stage_rows", torch.int32, numel=T, optional=not chan)
+    if not chan and stage_rows is not None:
+        raise ValueError("stage_rows: only for per-channel keys (channel_block)")
+    H, d, gs = layout.num_kv_heads, layout.head_dim, layout.group_size
+    for side, sc, zp in (("k", k_scales, k_zeros), ("v", v_scales, v_zeros)):
+        code = layout.k_code if side == "k" else layout.v_code
+        mode = layout.k_mode if side == "k" else layout.v_mode
+        if code == KVQ_CODE_NONE16:
+            n = 0
+        elif mode == KVQ_SCALE_TOKEN_SYM:
+            n = H
+        elif mode == KVQ_SCALE_GROUP_ASYM:
+            n = H * (d // gs if gs else 0)
+        else:
+            n = H * d
+        _need(sc, f"{side}_scales", torch.float32, numel=n, optional=n == 0)
+        asym = code != KVQ_CODE_NONE16 and mode == KVQ_SCALE_GROUP_ASYM
+        _need(zp, f"{side}_zeros", torch.uint8, numel=n, optional=not asym)
+    _need_cache(layout, cache)
+    _on_device(cache=cache, k=k, v=v, slot_mapping=slot_mapping, stage_rows=stage_rows, k_scales=k_scales,
+               k_zeros=k_zeros, v_scales=v_scales, v_zeros=v_zeros)
     _check("kvq_append_static", _lib.kvq_append_static(
         C.byref(layout), C.byref(cache.struct), _ptr(k), _ptr(v),
         k.stride(0) if T else 0, v.stride(0) if T else 0, T, _ptr(slot_mapping),
@@ -199,13 +326,39 @@ def kvq_decode_workspace_bytes(layout, batch, num_q_heads, max_context_len,
     return n
 
 
+def _decode_checks(layout, q, block_tables, context_lens, out, workspace, rows=None):
+    """Shared checks of decode and multi-query attention: q [rows][Hq][d]
+    fp16/bf16, out of q's shape in fp32/fp16/bf16, int32 tables [B][max] and
+    lengths [B], a workspace of bytes. Returns (B, Hq)."""
+    _need(q, "q", (torch.float16, torch.bfloat16), ndim=3)
+    if q.shape[2] != layout.head_dim:
+        raise ValueError(f"q: head dim {q.shape[2]}, layout has {layout.head_dim}")
+    Hq = q.shape[1]
+    _need(context_lens, "context_lens", torch.int32, ndim=1)
+    B = context_lens.numel()
+    if rows is None and q.shape[0] != B:
+        raise ValueError(f"q: {q.shape[0]} rows, context_lens has {B}")
+    _need(block_tables, "block_tables", torch.int32, ndim=2)
+    if block_tables.shape[0] < B:
+        raise ValueError(f"block_tables: {block_tables.shape[0]} rows, batch is {B}")
+    _need(out, "out", (torch.float32, torch.float16, torch.bfloat16), ndim=3)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out: shape {tuple(out.shape)}, expected {tuple(q.shape)} (as q)")
+    if workspace is not None:
+        _need(workspace, "workspace", tuple(DTYPES) + (torch.uint8, torch.int32, torch.int64))
+    return B, Hq
+
+
 def kvq_decode_attention(layout, cache: PagedCache, q, block_tables, context_lens,
                          max_context_len, out, workspace, sm_scale=0.0,
                          split_blocks=0, stream=None):
     """q: device [B][Hq][d] fp16/bf16; block_tables: int32 [B][max_blocks];
     context_lens: int32 [B]; out: device [B][Hq][d] fp32/fp16/bf16;
     workspace: device uint8 tensor of kvq_decode_workspace_bytes(...)."""
-    B, Hq, _ = q.shape
+    B, Hq = _decode_checks(layout, q, block_tables, context_lens, out, workspace)
+    _need_cache(layout, cache)
+    _on_device(cache=cache, q=q, block_tables=block_tables, context_lens=context_lens, out=out,
+               workspace=workspace)
     _check("kvq_decode_attention", _lib.kvq_decode_attention(
         C.byref(layout), C.byref(cache.struct), _ptr(q), DTYPES[q.dtype], B, Hq,
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
@@ -231,8 +384,11 @@ def kvq_prefill_attention(layout, cache: PagedCache, q, query_start, max_query_l
     block_tables: int32 [B][max_blocks]; context_lens: int32 [B]; out: device
     [Tq][Hq][d]; workspace: device uint8 tensor of
     kvq_prefill_workspace_bytes(...)."""
-    _, Hq, _ = q.shape
-    B = context_lens.numel()
+    B, Hq = _decode_checks(layout, q, block_tables, context_lens, out, workspace, rows=True)
+    _need(query_start, "query_start", torch.int32, numel=B + 1)
+    _need_cache(layout, cache)
+    _on_device(cache=cache, q=q, query_start=query_start, block_tables=block_tables,
+               context_lens=context_lens, out=out, workspace=workspace)
     _check("kvq_prefill_attention", _lib.kvq_prefill_attention(
         C.byref(layout), C.byref(cache.struct), _ptr(q), DTYPES[q.dtype], B, Hq,
         _ptr(query_start), int(max_query_len), _ptr(block_tables), block_tables.shape[1],
@@ -241,7 +397,23 @@ def kvq_prefill_attention(layout, cache: PagedCache, q, query_start, max_query_l
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def _need_pool(free_stack, free_top):
+    _need(free_stack, "free_stack", torch.int32, ndim=1)
+    _need(free_top, "free_top", torch.int32, min_numel=1)
+
+
+def _need_status(status_flag):
+    _need(status_flag, "status_flag", torch.int32, min_numel=1)
+
+
+def _need_lens_out(context_lens_out, B):
+    _need(context_lens_out, "context_lens_out", torch.int32, numel=B, optional=True)
+
+
 def kvq_pool_init(free_stack, free_top, initial_order=None, stream=None):
+    _need_pool(free_stack, free_top)
+    _need(initial_order, "initial_order", torch.int32, numel=free_stack.numel(), optional=True)
+    _on_device(free_stack=free_stack, free_top=free_top, initial_order=initial_order)
     _check("kvq_pool_init", _lib.kvq_pool_init(
         _ptr(free_stack), _ptr(free_top), _ptr(initial_order), free_stack.numel(),
         _stream(stream)))
@@ -250,6 +422,27 @@ def kvq_pool_init(free_stack, free_top, initial_order=None, stream=None):
 def kvq_blocks_reserve(free_stack, free_top, block_tables, context_lens, new_tokens,
                        block_size, slot_mapping_out, status_flag,
                        context_lens_out=None, stream=None):
+    """slot_mapping_out: int64, at least sum(new_tokens) entries (checked on
+    the host when the stream is not being captured into a graph)."""
+    _need_pool(free_stack, free_top)
+    _need(context_lens, "context_lens", torch.int32, ndim=1)
+    B = context_lens.numel()
+    _need(block_tables, "block_tables", torch.int32, ndim=2)
+    if block_tables.shape[0] < B:
+        raise ValueError(f"block_tables: {block_tables.shape[0]} rows, batch is {B}")
+    _need(new_tokens, "new_tokens", torch.int32, numel=B)
+    _need(slot_mapping_out, "slot_mapping_out", torch.int64, ndim=1)
+    _need_status(status_flag)
+    _need_lens_out(context_lens_out, B)
+    if B and not _capturing():
+        total = int(new_tokens.sum().item())
+        if slot_mapping_out.numel() < total:
+            raise ValueError(f"slot_mapping_out: {slot_mapping_out.numel()} entries, the "
+                             f"reservation writes {total}")
+    _on_device(free_stack=free_stack, free_top=free_top, block_tables=block_tables,
+               context_lens=context_lens, new_tokens=new_tokens,
+               slot_mapping_out=slot_mapping_out, status_flag=status_flag,
+               context_lens_out=context_lens_out)
     _check("kvq_blocks_reserve", _lib.kvq_blocks_reserve(
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(new_tokens),
@@ -259,6 +452,18 @@ def kvq_blocks_reserve(free_stack, free_top, block_tables, context_lens, new_tok
 
 def kvq_blocks_release(free_stack, free_top, block_tables, context_lens, release_mask,
                        block_size, status_flag, context_lens_out=None, stream=None):
+    _need_pool(free_stack, free_top)
+    _need(context_lens, "context_lens", torch.int32, ndim=1)
+    B = context_lens.numel()
+    _need(block_tables, "block_tables", torch.int32, ndim=2)
+    if block_tables.shape[0] < B:
+        raise ValueError(f"block_tables: {block_tables.shape[0]} rows, batch is {B}")
+    _need(release_mask, "release_mask", torch.int32, numel=B)
+    _need_status(status_flag)
+    _need_lens_out(context_lens_out, B)
+    _on_device(free_stack=free_stack, free_top=free_top, block_tables=block_tables,
+               context_lens=context_lens, release_mask=release_mask, status_flag=status_flag,
+               context_lens_out=context_lens_out)
     _check("kvq_blocks_release", _lib.kvq_blocks_release(
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(release_mask),
@@ -269,6 +474,15 @@ def kvq_blocks_release(free_stack, free_top, block_tables, context_lens, release
 def kvq_blocks_fork(refcount, block_tables, context_lens, src_rows, dst_rows, block_size,
                     stream=None):
     """Rows dst_rows[k] take rows src_rows[k]'s blocks (device int32 tensors)."""
+    _need(refcount, "refcount", torch.int32, ndim=1)
+    _need(context_lens, "context_lens", torch.int32, ndim=1)
+    _need(block_tables, "block_tables", torch.int32, ndim=2)
+    if block_tables.shape[0] < context_lens.numel():
+        raise ValueError("block_tables: fewer rows than context_lens")
+    _need(src_rows, "src_rows", torch.int32, ndim=1)
+    _need(dst_rows, "dst_rows", torch.int32, numel=src_rows.numel())
+    _on_device(refcount=refcount, block_tables=block_tables, context_lens=context_lens,
+               src_rows=src_rows, dst_rows=dst_rows)
     _check("kvq_blocks_fork", _lib.kvq_blocks_fork(
         _ptr(refcount), refcount.numel(), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), context_lens.numel(), _ptr(src_rows), _ptr(dst_rows),
@@ -278,6 +492,29 @@ def kvq_blocks_fork(refcount, block_tables, context_lens, src_rows, dst_rows, bl
 def kvq_blocks_reserve_shared(free_stack, free_top, refcount, block_tables, context_lens,
                               new_tokens, block_size, slot_mapping_out, cow_src, cow_dst,
                               cow_count, status_flag, context_lens_out=None, stream=None):
+    _need_pool(free_stack, free_top)
+    _need(refcount, "refcount", torch.int32, numel=free_stack.numel())
+    _need(context_lens, "context_lens", torch.int32, ndim=1)
+    B = context_lens.numel()
+    _need(block_tables, "block_tables", torch.int32, ndim=2)
+    if block_tables.shape[0] < B:
+        raise ValueError(f"block_tables: {block_tables.shape[0]} rows, batch is {B}")
+    _need(new_tokens, "new_tokens", torch.int32, numel=B)
+    _need(slot_mapping_out, "slot_mapping_out", torch.int64, ndim=1)
+    _need(cow_src, "cow_src", torch.int32, min_numel=B)
+    _need(cow_dst, "cow_dst", torch.int32, min_numel=B)
+    _need(cow_count, "cow_count", torch.int32, min_numel=1)
+    _need_status(status_flag)
+    _need_lens_out(context_lens_out, B)
+    if B and not _capturing():
+        total = int(new_tokens.sum().item())
+        if slot_mapping_out.numel() < total:
+            raise ValueError(f"slot_mapping_out: {slot_mapping_out.numel()} entries, the "
+                             f"reservation writes {total}")
+    _on_device(free_stack=free_stack, free_top=free_top, refcount=refcount,
+               block_tables=block_tables, context_lens=context_lens, new_tokens=new_tokens,
+               slot_mapping_out=slot_mapping_out, cow_src=cow_src, cow_dst=cow_dst,
+               cow_count=cow_count, status_flag=status_flag, context_lens_out=context_lens_out)
     _check("kvq_blocks_reserve_shared", _lib.kvq_blocks_reserve_shared(
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(refcount),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(new_tokens),
@@ -288,6 +525,19 @@ def kvq_blocks_reserve_shared(free_stack, free_top, refcount, block_tables, cont
 def kvq_blocks_release_shared(free_stack, free_top, refcount, block_tables, context_lens,
                               release_mask, block_size, status_flag, context_lens_out=None,
                               stream=None):
+    _need_pool(free_stack, free_top)
+    _need(refcount, "refcount", torch.int32, numel=free_stack.numel())
+    _need(context_lens, "context_lens", torch.int32, ndim=1)
+    B = context_lens.numel()
+    _need(block_tables, "block_tables", torch.int32, ndim=2)
+    if block_tables.shape[0] < B:
+        raise ValueError(f"block_tables: {block_tables.shape[0]} rows, batch is {B}")
+    _need(release_mask, "release_mask", torch.int32, numel=B)
+    _need_status(status_flag)
+    _need_lens_out(context_lens_out, B)
+    _on_device(free_stack=free_stack, free_top=free_top, refcount=refcount,
+               block_tables=block_tables, context_lens=context_lens, release_mask=release_mask,
+               status_flag=status_flag, context_lens_out=context_lens_out)
     _check("kvq_blocks_release_shared", _lib.kvq_blocks_release_shared(
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(refcount),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(release_mask),
@@ -298,6 +548,12 @@ def kvq_blocks_release_shared(free_stack, free_top, refcount, block_tables, cont
 def kvq_copy_blocks(layout, cache: PagedCache, src_ids, dst_ids, count, max_pairs=None,
                     stream=None):
     """Copy block src_ids[k] onto dst_ids[k] in one layer, k < count[0] (device)."""
+    n = src_ids.numel() if max_pairs is None else max_pairs
+    _need(src_ids, "src_ids", torch.int32, min_numel=n)
+    _need(dst_ids, "dst_ids", torch.int32, min_numel=n)
+    _need(count, "count", torch.int32, min_numel=1)
+    _need_cache(layout, cache)
+    _on_device(cache=cache, src_ids=src_ids, dst_ids=dst_ids, count=count)
     _check("kvq_copy_blocks", _lib.kvq_copy_blocks(
         C.byref(layout), C.byref(cache.struct), _ptr(src_ids), _ptr(dst_ids), _ptr(count),
         src_ids.numel() if max_pairs is None else max_pairs, _stream(stream)))
@@ -306,6 +562,14 @@ def kvq_copy_blocks(layout, cache: PagedCache, src_ids, dst_ids, count, max_pair
 def kvq_blocks_trim(free_stack, free_top, block_tables, context_lens, window, sink, block_size,
                     status_flag, stream=None):
     """Return the blocks no query past context_lens can see under the window."""
+    _need_pool(free_stack, free_top)
+    _need(context_lens, "context_lens", torch.int32, ndim=1)
+    _need(block_tables, "block_tables", torch.int32, ndim=2)
+    if block_tables.shape[0] < context_lens.numel():
+        raise ValueError("block_tables: fewer rows than context_lens")
+    _need_status(status_flag)
+    _on_device(free_stack=free_stack, free_top=free_top, block_tables=block_tables,
+               context_lens=context_lens, status_flag=status_flag)
     _check("kvq_blocks_trim", _lib.kvq_blocks_trim(
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), int(window), int(sink),
@@ -321,12 +585,26 @@ def kvq_block_pack_bytes(layout) -> int:
 
 def kvq_pack_blocks(layout, cache: PagedCache, ids, dst, stream=None):
     """Pack blocks ids (device int32) of one layer into dst (uint8 tensor)."""
+    _need(ids, "ids", torch.int32, ndim=1)
+    _need(dst, "dst", (torch.uint8, torch.int8), ndim=1, contiguous=True)
+    if _nbytes(dst) < ids.numel() * kvq_block_pack_bytes(layout):
+        raise ValueError(f"dst: {_nbytes(dst)} bytes, {ids.numel()} packed blocks need "
+                         f"{ids.numel() * kvq_block_pack_bytes(layout)}")
+    _need_cache(layout, cache)
+    _on_device(cache=cache, ids=ids, dst=dst)
     _check("kvq_pack_blocks", _lib.kvq_pack_blocks(
         C.byref(layout), C.byref(cache.struct), _ptr(ids), ids.numel(), _ptr(dst),
         _stream(stream)))
 
 
 def kvq_unpack_blocks(layout, cache: PagedCache, src, ids, stream=None):
+    _need(ids, "ids", torch.int32, ndim=1)
+    _need(src, "src", (torch.uint8, torch.int8), ndim=1)
+    if _nbytes(src) < ids.numel() * kvq_block_pack_bytes(layout):
+        raise ValueError(f"src: {_nbytes(src)} bytes, {ids.numel()} packed blocks need "
+                         f"{ids.numel() * kvq_block_pack_bytes(layout)}")
+    _need_cache(layout, cache)
+    _on_device(cache=cache, src=src, ids=ids)
     _check("kvq_unpack_blocks", _lib.kvq_unpack_blocks(
         C.byref(layout), C.byref(cache.struct), _ptr(src), _ptr(ids), ids.numel(),
         _stream(stream)))
