@@ -119,27 +119,60 @@ def test_sym_zero_row_and_sign_and_power_of_two():
         assert sk == np.float32(s * 2.0 ** k) and (qk == q).all()
 
 
-def test_pages_toy_int8_procedure_in_fp32():
-    # The toy quantizer printed on "Dynamic KV Cache Quantization for Fast LLM
-    # Inference" (section "Understanding Dynamic Quantization Techniques"),
-    # run by torch in fp32 on the CPU: abs-max, divide by 127, torch.round
-    # (half to even), cast to int8.
-    for _ in range(50):
-        t = torch.randn(1, 10, 128, dtype=torch.float32) * 10
-        abs_max = t.abs().max()
-        scale = abs_max / 127.0
-        q_t = torch.round(t / scale).to(torch.int8)
-        for i in range(10):
-            q, s = ref.quant_sym(t[0, i].numpy(), 127)
-            # the toy takes one scale over the whole tensor; per row, compare
-            # with rows re-quantized at that row's own scale
-            row = t[0, i]
-            rs = row.abs().max() / 127.0
-            assert s == rs.item()
-            assert (q == torch.round(row / rs).to(torch.int8).numpy()).all()
-        whole_q, whole_s = ref.quant_sym(t.reshape(-1).numpy(), 127)
-        assert whole_s == scale.item()
-        assert (whole_q == q_t.reshape(-1).numpy()).all()
+@pytest.mark.parametrize("bits", [8, 4])
+def test_absmax_rule_hand_worked(bits):
+    # "Dynamic KV Cache Quantization for Fast LLM Inference", section
+    # "Understanding Dynamic Quantization Techniques for KV Caches": the scale
+    # is the row's largest magnitude over 2^(bits-1) - 1 and a code is the
+    # value over the scale, rounded. Rows chosen so that the scale is a power
+    # of two (exact), with the expected codes worked out by hand; halves go
+    # to the even neighbour.
+    qmax = 2 ** (bits - 1) - 1
+    if bits == 8:
+        # max 15.875 = 127 / 8 -> scale 1/8; x * 8 = 0.5, 1.5, 2.5, -3.5, 127, 8, 40.48
+        x = [0.0625, 0.1875, 0.3125, -0.4375, 15.875, 1.0, 5.06]
+        want = [0, 2, 2, -4, 127, 8, 40]
+        scale = 0.125
+    else:
+        # max 1.75 = 7 / 4 -> scale 1/4; x * 4 = 0.5, 1.5, -2.5, 7, -4, 1.2, -6.5
+        x = [0.125, 0.375, -0.625, 1.75, -1.0, 0.3, -1.625]
+        want = [0, 2, -2, 7, -4, 1, -6]
+        scale = 0.25
+    q, s = ref.quant_sym(f32(x), qmax)
+    assert float(s) == scale
+    assert q.tolist() == want
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_absmax_rule_against_exact_rationals(bits):
+    # The same rule checked with exact rational arithmetic on heavy-tailed
+    # (Laplace) rows of 48 elements: the fp32 scale is the correctly rounded
+    # quotient max|x| / (2^(bits-1) - 1), and each code is the integer nearest
+    # to the exact ratio x / scale (halves to even). Elements whose exact
+    # ratio lies within 2^-18 of a rounding boundary are skipped: there the
+    # fp32 rounding of the quotient itself decides, which the hand-worked
+    # ties above cover.
+    from fractions import Fraction
+    qmax = 2 ** (bits - 1) - 1
+    r = np.random.default_rng(77 + bits)
+    for _ in range(40):
+        x = f32(r.laplace(0.0, 10.0 ** r.uniform(-2, 2), 48))
+        q, s = ref.quant_sym(x, qmax)
+        a = max(abs(Fraction(float(v))) for v in x)
+        s_exact = a / qmax
+        # a correctly rounded fp32 scale lies within half an ulp (2^-24
+        # relative) of the exact quotient
+        s32 = Fraction(float(s))
+        assert abs(s32 - s_exact) <= s_exact * Fraction(1, 2 ** 24)
+        for xi, qi in zip(x, q):
+            y = Fraction(float(xi)) / s32
+            fl = y.numerator // y.denominator
+            frac = y - fl
+            if abs(frac - Fraction(1, 2)) < Fraction(1, 2 ** 18):
+                continue
+            nearest = fl + 1 if frac > Fraction(1, 2) else fl
+            nearest = max(-qmax, min(qmax, nearest))
+            assert int(qi) == nearest, (float(xi), float(s), int(qi), nearest)
 
 
 # ---------------------------------------------------------------------------
