@@ -316,6 +316,31 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache
                                 int32_t out_dtype, void* workspace,
                                 int64_t workspace_bytes, void* stream);
 
+/* kvq_decode_attention for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace: the partials go to a fixed array the
+ * library holds in each GPU's memory (KVQ_DECODE_SCRATCH_BYTES per GPU, kept
+ * until the process ends, its address looked up once per device on the first
+ * call). The call allocates nothing: no hipMalloc, no hipFree, no allocating
+ * library routine.
+ *  Arguments, results and errors are those of kvq_decode_attention, minus
+ *  workspace and workspace_bytes. The stream must belong to the current
+ *  device. A call whose kvq_decode_workspace_bytes(...) exceeds
+ *  KVQ_DECODE_SCRATCH_BYTES returns KVQ_ERR_WORKSPACE_TOO_SMALL before
+ *  touching the device; KVQ_ERR_HIP if the array's address cannot be had.
+ *  Every call on one GPU shares that GPU's array: calls that may overlap on
+ *  one GPU (different streams, or threads) race and must be serialized by
+ *  the caller. Nothing in the array needs to start at any value. */
+#define KVQ_DECODE_SCRATCH_BYTES 134217728 /* 128 MiB */
+kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const kvq_cache* cache,
+                                        const void* q, int32_t q_dtype, int32_t batch,
+                                        int32_t num_q_heads, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens,
+                                        int32_t max_context_len, float sm_scale,
+                                        int32_t split_blocks, void* out, int32_t out_dtype,
+                                        void* stream);
+
 /* Device workspace bytes kvq_prefill_attention needs for these sizes and this
  * split_blocks (>= 1, or 0 = the library's own choice), or a negative
  * kvq_status. */

@@ -274,13 +274,16 @@ int64_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t batch, int32_t n
   return round_up(items * L->head_dim * 4, 256) + round_up(items * 2 * 4, 256);
 }
 
-kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const void* q,
-                                int32_t q_dtype, int32_t batch, int32_t num_q_heads,
-                                const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                const int32_t* context_lens, int32_t max_context_len,
-                                float sm_scale, int32_t split_blocks, void* out,
-                                int32_t out_dtype, void* workspace, int64_t workspace_bytes,
-                                void* stream) {
+namespace {
+
+// Host checks shared by both decode entry points (every check before any
+// launch); on success *need is the workspace the call needs.
+kvq_status decode_check(const kvq_layout* L, const kvq_cache* C, const void* q, int32_t q_dtype,
+                        int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t max_context_len, float sm_scale, int32_t split_blocks,
+                        void* out, int32_t out_dtype, int64_t* need) {
+  *need = 0;
   kvq_status s = kvq_layout_check(L);
   if (s != KVQ_OK) return s;
   s = check_cache(L, C);
@@ -301,15 +304,24 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const v
   if (L->k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM && batch > C->max_seqs)
     return KVQ_ERR_INVALID_ARGUMENT;
   if (batch == 0) return KVQ_OK;
-  if (!q || !out || !block_tables || !context_lens || !workspace) return KVQ_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_INVALID_ARGUMENT;
-  const int64_t need = kvq_decode_workspace_bytes(L, batch, num_q_heads, max_context_len, split_blocks);
-  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  if (!q || !out || !block_tables || !context_lens) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARGUMENT;
   // the device planner counts blocks in int32
   if ((int64_t)batch * ceil_div(max_context_len, L->block_size) > INT32_MAX)
     return KVQ_ERR_UNSUPPORTED;
   const int64_t bound = decode_item_bound(L, batch, max_context_len, split_blocks);
   if (bound * L->num_kv_heads > INT32_MAX - 16) return KVQ_ERR_UNSUPPORTED;  // 1-D grid
+  *need = kvq_decode_workspace_bytes(L, batch, num_q_heads, max_context_len, split_blocks);
+  return KVQ_OK;
+}
+
+// Enqueue the split and reduce kernels; the arguments passed decode_check.
+kvq_status decode_launch(const kvq_layout* L, const kvq_cache* C, const void* q, int32_t q_dtype,
+                         int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t max_context_len, float sm_scale, int32_t split_blocks,
+                         void* out, int32_t out_dtype, void* workspace, void* stream) {
+  const int64_t bound = decode_item_bound(L, batch, max_context_len, split_blocks);
   const int64_t items = bound * num_q_heads;
   kvq::DecodePlan p;
   p.q = q;
@@ -345,6 +357,47 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const v
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                      round_up(items * L->head_dim * 4, 256));
   return hip_status(kvq::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const void* q,
+                                int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len,
+                                float sm_scale, int32_t split_blocks, void* out,
+                                int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+  int64_t need = 0;
+  kvq_status s = decode_check(L, C, q, q_dtype, batch, num_q_heads, block_tables,
+                              max_blocks_per_seq, context_lens, max_context_len, sm_scale,
+                              split_blocks, out, out_dtype, &need);
+  if (s != KVQ_OK || batch == 0) return s;
+  if (!workspace || !aligned16(workspace)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  return decode_launch(L, C, q, q_dtype, batch, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, sm_scale, split_blocks, out, out_dtype,
+                       workspace, stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_layout* L, const kvq_cache* C, const void* q,
+                                        int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t max_context_len,
+                                        float sm_scale, int32_t split_blocks, void* out,
+                                        int32_t out_dtype, void* stream) {
+  int64_t need = 0;
+  kvq_status s = decode_check(L, C, q, q_dtype, batch, num_q_heads, block_tables,
+                              max_blocks_per_seq, context_lens, max_context_len, sm_scale,
+                              split_blocks, out, out_dtype, &need);
+  if (s != KVQ_OK || batch == 0) return s;
+  // sizes beyond the library's scratch are refused before the device is touched
+  if (need > (int64_t)KVQ_DECODE_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  void* scratch = nullptr;
+  if (kvq::decode_scratch(&scratch) != hipSuccess || !scratch) return KVQ_ERR_HIP;
+  return decode_launch(L, C, q, q_dtype, batch, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, sm_scale, split_blocks, out, out_dtype,
+                       scratch, stream);
 }
 
 namespace {

@@ -42,8 +42,17 @@
 //    blocks of the split and are read with v_readlane.
 //  * Partials (m, l, acc) per split go to the workspace; decode_reduce merges
 //    them with the log-sum-exp rule.
+#include <atomic>
+#include <mutex>
+
 #include "kvq_attn_tiles.h"
 #include "kvq_int4_tiles.h"
+
+// Partials of kvq_decode_attention_noalloc: a fixed array in device memory
+// (one copy per GPU, held until the process ends), so that callers that cannot
+// allocate still get a workspace. Host code never names it in a launch: its
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[KVQ_DECODE_SCRATCH_BYTES];
 
 namespace kvq {
 namespace {
@@ -690,6 +699,34 @@ hipError_t launch_split_shape(const DecodeArgs& a, int d, int bs, int items, hip
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      // with `dev` current: each GPU holds its own copy at its own address
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
                       int32_t v_mode) {

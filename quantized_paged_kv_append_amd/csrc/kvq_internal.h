@@ -98,6 +98,9 @@ __host__ __device__ constexpr int decode_skew_cap(int32_t k_mode) {
 }
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
+// Device address of the current device's decode scratch array
+// (KVQ_DECODE_SCRATCH_BYTES, 256-byte aligned), looked up once per device.
+hipError_t decode_scratch(void** ptr);
 bool decode_supported(int32_t k_code, int32_t v_code, int32_t k_mode,
                       int32_t v_mode);
 

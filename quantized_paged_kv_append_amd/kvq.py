@@ -28,6 +28,7 @@ KVQ_ERR_UNSUPPORTED = -2
 KVQ_ERR_WORKSPACE_TOO_SMALL = -3
 KVQ_ERR_HIP = -4
 KVQ_ERR_OUT_OF_BLOCKS = -5
+KVQ_DECODE_SCRATCH_BYTES = 134217728   # the allocation-free decode's per-GPU array
 
 KVQ_F16, KVQ_BF16, KVQ_F32 = 0, 1, 2
 KVQ_CODE_NONE16, KVQ_CODE_INT8, KVQ_CODE_FP8_E4M3, KVQ_CODE_INT4 = 0, 1, 2, 3
@@ -67,6 +68,8 @@ _SIGS = {
     "kvq_decode_workspace_bytes": (_i64, [_LP, _i32, _i32, _i32, _i32]),
     "kvq_decode_attention": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
                                     _i32, _f32, _i32, _vp, _i32, _vp, _i64, _vp]),
+    "kvq_decode_attention_noalloc": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
+                                            _i32, _f32, _i32, _vp, _i32, _vp]),
     "kvq_prefill_workspace_bytes": (_i64, [_LP, _i32, _i32, _i32, _i32, _i32]),
     "kvq_prefill_attention": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
                                      _vp, _i32, _f32, _i32, _i32, _i32, _vp, _i32, _vp, _i64,
@@ -365,6 +368,22 @@ def kvq_decode_attention(layout, cache: PagedCache, q, block_tables, context_len
         int(max_context_len), float(sm_scale), int(split_blocks), _ptr(out),
         DTYPES[out.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def kvq_decode_attention_noalloc(layout, cache: PagedCache, q, block_tables, context_lens,
+                                 max_context_len, out, sm_scale=0.0, split_blocks=0,
+                                 stream=None):
+    """kvq_decode_attention without a workspace argument: the library's fixed
+    per-GPU array (KVQ_DECODE_SCRATCH_BYTES) holds the partials, and the call
+    allocates nothing. Calls that overlap on one GPU race on that array."""
+    B, Hq = _decode_checks(layout, q, block_tables, context_lens, out, None)
+    _need_cache(layout, cache)
+    _on_device(cache=cache, q=q, block_tables=block_tables, context_lens=context_lens, out=out)
+    _check("kvq_decode_attention_noalloc", _lib.kvq_decode_attention_noalloc(
+        C.byref(layout), C.byref(cache.struct), _ptr(q), DTYPES[q.dtype], B, Hq,
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        int(max_context_len), float(sm_scale), int(split_blocks), _ptr(out),
+        DTYPES[out.dtype], _stream(stream)))
 
 
 def kvq_prefill_workspace_bytes(layout, batch, num_q_heads, max_query_len, max_context_len,

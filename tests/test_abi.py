@@ -157,6 +157,35 @@ def test_append_and_decode_reject_bad_arguments_on_host():
                                     None) == kq.KVQ_ERR_UNSUPPORTED
 
 
+def test_decode_noalloc_rejects_bad_arguments_on_host():
+    """The allocation-free decode takes kvq_decode_attention's checks, and
+    refuses sizes whose workspace exceeds its fixed per-GPU array before it
+    touches the device."""
+    L = kq.make_layout(8, 128, 16, "int8")
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+
+    def dec(**kw):
+        a = dict(batch=2, hq=32, maxb=4, maxlen=64, tables=p)
+        a.update(kw)
+        cs = _fake_cache(L)
+        return lib.kvq_decode_attention_noalloc(C.byref(L), C.byref(cs), p, kq.KVQ_BF16,
+                                                a["batch"], a["hq"], a["tables"], a["maxb"], p,
+                                                a["maxlen"], 0.0, 0, p, kq.KVQ_F32, None)
+    assert dec(hq=30) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert dec(tables=None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert dec(batch=0) == kq.KVQ_OK
+    # a batch whose workspace bound is past KVQ_DECODE_SCRATCH_BYTES
+    big_b, big_len = 4096, 1 << 20
+    need = kq.kvq_decode_workspace_bytes(L, big_b, 32, big_len)
+    assert need > kq.KVQ_DECODE_SCRATCH_BYTES
+    assert dec(batch=big_b, maxb=big_len // 16, maxlen=big_len) == \
+        kq.KVQ_ERR_WORKSPACE_TOO_SMALL
+    # the workloads' shapes fit (the mixed step's 256 sequences of up to 32K
+    # tokens is the largest)
+    assert kq.kvq_decode_workspace_bytes(L, 256, 32, 33000) <= kq.KVQ_DECODE_SCRATCH_BYTES
+
+
 def test_append_static_rejects_bad_arguments_on_host():
     lib = kq._lib
     p = C.c_void_p(1 << 21)
