@@ -3,6 +3,9 @@ quantize-on-append -> decode, for one layer. The oracle runs its own pool
 mirror from the same initial order (its tables are checked equal to the
 device's, never read from it), appends the sampled sequences' rows and decodes
 them; the device output and planes must match on those samples."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -15,10 +18,10 @@ from _gpu_util import DEV, assert_decode_close, decode_gpu, kq, lib_layout, need
 pytestmark = pytest.mark.gpu
 
 
-def _populate(w, seed=0, chunk=1 << 20):
+def _populate(w, seed=0, chunk=1 << 20, layer=0):
     """What bench.py does for one layer: pool init (permuted order), one
     reservation for every sequence's context, K/V generated on the device and
-    appended in chunks."""
+    appended in chunks (layer selects that layer's draw)."""
     LL = lib_layout(w)
     lens = workloads.lengths(w, seed)
     nb = workloads.pool_blocks(lens, w.block_size, headroom_tokens=w.block_size)
@@ -35,7 +38,7 @@ def _populate(w, seed=0, chunk=1 << 20):
     kq.kvq_blocks_reserve(stack, top, tables, ctx, torch.from_numpy(lens).to(DEV),
                           w.block_size, slots, status, ctx)
     cache = kq.PagedCache(LL, nb, w.batch, device=DEV)
-    k, v = workloads.kv_rows(w, T, seed=seed, device=DEV)
+    k, v = workloads.kv_rows(w, T, seed=seed, device=DEV, layer=layer)
     rows = None
     if w.k_mode == "channel_block":   # stage row of each token: its sequence
         rows = torch.from_numpy(np.repeat(np.arange(w.batch, dtype=np.int32), lens)).to(DEV)
@@ -48,9 +51,16 @@ def _populate(w, seed=0, chunk=1 << 20):
                 cache=cache, k=k, v=v, stack=stack, top=top)
 
 
-def _check(w, P, sample, seed=0):
+def _threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _check(w, P, sample=None, seed=0, layer=0):
+    """sample: the sequences compared (None: every sequence)."""
     L = oracle_layout(w)
     lens, nb = P["lens"], P["nb"]
+    if sample is None:
+        sample = list(range(w.batch))
     # oracle pool mirror
     ostack, otop = ref.pool_init(nb, P["order"])
     otables = np.full((w.batch, P["maxb"]), -1, np.int32)
@@ -58,14 +68,21 @@ def _check(w, P, sample, seed=0):
                                     lens, w.block_size)
     assert st == 0
     assert np.array_equal(otables, P["tables"].cpu().numpy())
-    # oracle append of the sampled sequences only (stage row = sequence)
+    # oracle append of the sampled sequences only (stage row = sequence), one
+    # call per sequence on a thread pool: sequences own disjoint blocks and
+    # stage rows, and the oracle's C code runs outside the interpreter lock
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
-    idx = np.concatenate([starts[b] + np.arange(lens[b]) for b in sample]).astype(np.int64)
-    rows = np.concatenate([np.full(lens[b], b, np.int32) for b in sample])
     hc = ref.HostCache(L, nb, w.batch)
-    ki = bits(P["k"][torch.from_numpy(idx).to(DEV)]).reshape(len(idx), -1)
-    vi = bits(P["v"][torch.from_numpy(idx).to(DEV)]).reshape(len(idx), -1)
-    ref.append(L, hc, ki, vi, oslots[idx], rows)
+
+    def one(b):
+        idx = (starts[b] + np.arange(lens[b])).astype(np.int64)
+        ti = torch.from_numpy(idx).to(DEV)
+        ki = bits(P["k"][ti]).reshape(len(idx), -1)
+        vi = bits(P["v"][ti]).reshape(len(idx), -1)
+        ref.append(L, hc, ki, vi, oslots[idx], np.full(lens[b], b, np.int32))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, sample))
     # planes of the sampled sequences' blocks, bytewise
     H, bs, d = w.num_kv_heads, w.block_size, w.head_dim
     chan = w.k_mode == "channel_block"
@@ -97,21 +114,47 @@ def _check(w, P, sample, seed=0):
             assert np.array_equal(gs[b, :, :tail], hs[b, :, :tail]), ("k_stage", b)
     # decode: every query head of the sampled sequences (the oracle attends
     # over the sampled sequences only; the others get length 0)
-    q = workloads.queries(w, seed=seed, device=DEV)
+    q = workloads.queries(w, seed=seed, device=DEV, layer=layer)
     got = decode_gpu(P["LL"], P["cache"], q, P["tables"], P["ctx"], int(lens.max()))
     olens = np.zeros_like(lens)
     olens[sample] = lens[sample]
-    exp = ref.decode(L, hc, bits(q), DT[w.src_dtype], otables, olens, threads=16)
+    exp = ref.decode(L, hc, bits(q), DT[w.src_dtype], otables, olens, threads=_threads())
     P["oracle"] = dict(hc=hc, stack=ostack, top=otop, tables=otables)
     return assert_decode_close(got[torch.as_tensor(sample, device=DEV)], exp[sample], w.name)
 
 
-def test_llama3_70b_one_layer_fp8():
+def _other_layers(w, n=2, seed=0):
+    """Layer 1 and n seeded layers among the rest of the workload's layers."""
+    g = np.random.default_rng([seed, 80])
+    return [1] + sorted(int(x) for x in g.choice(np.arange(2, w.layers), n, replace=False))
+
+
+@pytest.mark.parametrize("name", ["llama3_70b", "llama3_70b_int8"])
+def test_llama3_70b_every_sequence_of_layer_0(name):
+    """The 70B KV shape (16 x 32768 tokens, 64 q / 8 KV heads, block 16) with
+    E4M3 or INT8 per-token codes: every sequence's planes and every query
+    head's output of layer 0."""
     need_gpu()
-    w = workloads.get("llama3_70b")
+    w = workloads.get(name)
     P = _populate(w)
-    err = _check(w, P, sample=[0, 9, 15])
-    print(f"llama3_70b layer: max err {err:.2e}")
+    err = _check(w, P)
+    print(f"{name} layer 0, all 16 sequences: max err {err:.2e}")
+
+
+@pytest.mark.parametrize("name", ["llama3_70b", "llama3_70b_int8"])
+def test_llama3_70b_seeded_rows_of_other_layers(name):
+    """Layer 1 and two seeded layers of the 80 (each its own K/V/q draw): two
+    seeded sequences each."""
+    need_gpu()
+    w = workloads.get(name)
+    g = np.random.default_rng([0, 81])
+    for layer in _other_layers(w):
+        P = _populate(w, layer=layer)
+        sample = sorted(int(x) for x in g.choice(w.batch, 2, replace=False))
+        err = _check(w, P, sample=sample, layer=layer)
+        print(f"{name} layer {layer}, sequences {sample}: max err {err:.2e}")
+        del P
+        torch.cuda.empty_cache()
 
 
 def test_llama3_70b_one_layer_bf16_passthrough():
@@ -144,14 +187,21 @@ def test_int4_long_context_one_layer():
 
 
 def test_int4_batch_one_layer():
-    """One layer of the INT4 batch workload: 32 sequences with log-normal
-    lengths (median 4096, cap 65536)."""
+    """One layer of the INT4 batch workload: all 32 sequences (log-normal
+    lengths, median 4096, cap 65536), then seeded sequences of other layers."""
     need_gpu()
     w = workloads.get("int4_batch")
     P = _populate(w)
-    lens = P["lens"]
-    err = _check(w, P, sample=[int(np.argmax(lens)), int(np.argmin(lens)), 5])
-    print(f"int4_batch layer: max err {err:.2e}")
+    err = _check(w, P)
+    print(f"int4_batch layer 0, all 32 sequences: max err {err:.2e}")
+    del P
+    g = np.random.default_rng([0, 82])
+    for layer in _other_layers(w, n=1):
+        P = _populate(w, layer=layer)
+        sample = sorted(int(x) for x in g.choice(w.batch, 3, replace=False))
+        err = _check(w, P, sample=sample, layer=layer)
+        print(f"int4_batch layer {layer}, sequences {sample}: max err {err:.2e}")
+        del P
 
 
 def test_mixed_continuous_step_one_layer():

@@ -15,6 +15,7 @@ Strategies ...", "How vLLM Implements KV Cache Optimization"):
               8 KV heads, d 128, bf16, 4 key outlier channels x8, INT8, bs 16
   llama3_70b  80 layers, 16 sequences x 32768 tokens, 64 q / 8 KV heads, d 128,
               bf16, FP8 E4M3, bs 16
+  llama3_70b_int8  the same shape with INT8 per-token-per-head codes
   llama3_70b_bf16  the same shape with the 16-bit passthrough cache (the
               unquantized baseline the quantized codes are measured against)
   int4_long   80 layers, 1 sequence of 131072 tokens, INT4 with per-32 group
@@ -82,6 +83,10 @@ WORKLOADS = {
                            "fp8", "token_sym", "token_sym",
                            lengths=("fixed", 32768), n_outliers=4,
                            outlier_factor=8.0),
+    "llama3_70b_int8": Workload("llama3_70b_int8", 80, 16, 64, 8, 128, 16, "bfloat16", "int8",
+                                "int8", "token_sym", "token_sym",
+                                lengths=("fixed", 32768), n_outliers=4,
+                                outlier_factor=8.0),
     "llama3_70b_bf16": Workload("llama3_70b_bf16", 80, 16, 64, 8, 128, 16, "bfloat16",
                                 "none16", "none16", "token_sym", "token_sym",
                                 lengths=("fixed", 32768), n_outliers=4,
