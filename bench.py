@@ -35,7 +35,7 @@ PEAK_MFMA_F16_TFLOPS = 2500.0   # dense fp16 MFMA, MI355X
 HERE = os.path.dirname(os.path.abspath(__file__))
 # sources whose change invalidates committed decode counters
 DECODE_SOURCES = ("kvq_decode.hip", "kvq_attn_tiles.h", "kvq_int4_tiles.h", "kvq_device.h",
-                  "kvq_internal.h")
+                  "kvq_internal.h", "kvq_api.cpp")
 
 
 def decode_source_hash():
@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_70b", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-extras", action="store_true",
+                    help="measure only --workload (by default, the default llama3_70b line "
+                         "also carries short runs of the other workloads under 'workloads')")
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's own count")
     ap.add_argument("--split-blocks", type=int, default=0)
     ap.add_argument("--batch", type=int, default=0, help="0 = the workload's own batch")
@@ -207,14 +210,46 @@ def main():
     if args.offload_blocks:
         offload_bench(args)
         return
+    torch.cuda.set_device(torch.device("cuda:0"))
+    line = run(args, args.workload)
+    explicit = any(a == "--workload" or a.startswith("--workload=") for a in sys.argv[1:])
+    if not (args.no_extras or explicit or args.prefill_queries or args.batch or args.layers
+            or args.split_blocks):
+        # the other workloads, each on its own caches (freed in between), with
+        # fewer steps: their per-launch decode and append figures
+        extras = {}
+        for name in EXTRA_WORKLOADS:
+            sub = argparse.Namespace(**vars(args))
+            sub.steps, sub.warmup, sub.no_cpu_baseline = min(args.steps, 10), 2, True
+            torch.cuda.empty_cache()
+            r = run(sub, name)
+            extras[name] = {k: r[k] for k in ("value", "ms_per_step", "pct_of_hbm_peak",
+                                               "decode_launch_ms",
+                                               "decode_launch_ms_p10_p50_p90",
+                                               "append_tok_s", "append_GBps", "dtype")}
+            extras[name]["roofline"] = {k: r["roofline"][k] for k in
+                                        ("achieved", "frac", "traffic", "bytes_per_launch")}
+            extras[name]["config"] = {k: r["config"][k] for k in
+                                      ("layers", "batch", "context", "num_q_heads",
+                                       "k_code", "v_code", "k_mode", "v_mode", "block_size")}
+        line["workloads"] = extras
+    print(json.dumps(line))
+
+
+# measured after the headline workload in a default run
+EXTRA_WORKLOADS = ("llama3_70b_int8", "llama3_8b", "int4_long", "int4_batch", "mixed")
+
+
+def run(args, wname):
+    """Populate one workload's caches, time its steps and return the JSON
+    line's fields (the caches are freed on return)."""
     import quantized_paged_kv_append_amd as kq
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    w = workloads.get(args.workload)
+    w = workloads.get(wname)
     if args.batch:
-        w = workloads.get(args.workload, batch=args.batch)
+        w = workloads.get(wname, batch=args.batch)
     layers = args.layers or w.layers
     nq = args.prefill_queries
     LL = kq.make_layout(w.num_kv_heads, w.head_dim, w.block_size, w.k_code, w.v_code,
@@ -467,7 +502,7 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
-    print(json.dumps(line))
+    return line
 
 
 def cpu_baseline(w, lens, args):
