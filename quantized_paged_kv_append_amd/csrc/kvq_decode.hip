@@ -363,7 +363,7 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   const int ifull = partial ? i1 - 1 : i1;
   TileT buf[NBUF];
 #pragma unroll
-  for (int u = 0; u < NBUF; ++u) load_tile<D, BS, KCH>(buf[u], a, bh_of(i0 + u), lane);
+  for (int u = 0; u < NBUF; ++u) load_tile<D, BS, KCH, true>(buf[u], a, bh_of(i0 + u), lane);
 
   // Steady state: every slot computes one block and refills its buffer with
   // the block NBUF ahead (clamped to the split's last block, so the load
@@ -374,7 +374,7 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       block(buf[u], i + u);
-      load_tile<D, BS, KCH>(buf[u], a, bh_of(i + u + NBUF), lane);
+      load_tile<D, BS, KCH, true>(buf[u], a, bh_of(i + u + NBUF), lane);
     }
   }
   // Remainder: fewer than NBUF complete blocks, already in buf[0 ..], then
