@@ -440,9 +440,96 @@ struct ChanArgs {
   int32_t max_seqs;
 };
 
+// Quantize the block completed by token t (its slot, the block's last, is
+// `slot`; its stage row `srow`) for head h: the whole wave, lane l owning
+// channels CPL l .. CPL l + CPL - 1 over all BS rows.
+template <int D, int BS, bool BF16>
+__device__ __forceinline__ void chan_block(const ChanArgs& a, int64_t t, int h, int64_t slot,
+                                           int32_t srow, int lane) {
+  constexpr int CPL = D / kWave;  // channels per lane (1 or 2)
+  const int64_t blk = slot / BS;
+  // rows of this block provided by this call: t - k for k < n_new, the
+  // run of preceding tokens with consecutive slots and the same stage row;
+  // lane l checks token t - 1 - l, all lanes at once
+  bool match = false;
+  if (lane < BS - 1 && t - 1 - lane >= 0) {
+    const int64_t tp = t - 1 - lane;
+    match = a.slots[tp] == slot - 1 - lane && a.stage_rows[tp] == srow;
+  }
+  // at most BS - 1 < 64 bits are set, so the complement is never 0
+  const int n_new = 1 + __builtin_ctzll(~(uint64_t)__ballot(match));
+  float x[BS][CPL];
+  float amax[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) amax[c] = 0.0f;
+#pragma unroll
+  for (int o = 0; o < BS; ++o) {
+    const int k = BS - 1 - o;  // token t - k holds offset o when k < n_new
+    const uint16_t* p;
+    if (k < n_new)
+      p = a.src + (t - k) * a.row_stride + (int64_t)h * D;
+    else
+      p = a.stage + (((int64_t)srow * a.H + h) * BS + o) * D;
+    if constexpr (CPL == 2) {
+      uint32_t w = *reinterpret_cast<const uint32_t*>(p + 2 * lane);
+      unpack2<BF16>(w, x[o][0], x[o][1]);
+    } else {
+      uint16_t w = p[lane];
+      x[o][0] = BF16 ? bf16_lo(w) : f16_lo(w);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) amax[c] = fmaxf(amax[c], fabsf(x[o][c]));
+  }
+  float s[CPL], inv[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    s[c] = amax[c] == 0.0f ? 1.0f : div_rn(amax[c], 127.0f);
+    inv[c] = div_rn(1.0f, s[c]);
+  }
+  int8_t* cb = a.codes + ((blk * a.H + h) * BS) * D;
+#pragma unroll
+  for (int o = 0; o < BS; ++o) {
+    int q[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float y = x[o][c] * inv[c];
+      float r = rne(y);
+      if (near_half(y, r) || recip_unsafe(s[c])) r = rne(div_rn(x[o][c], s[c]));
+      q[c] = (int)fminf(fmaxf(r, -127.0f), 127.0f);
+    }
+    if constexpr (CPL == 2) {
+      *reinterpret_cast<uint16_t*>(cb + o * D + 2 * lane) =
+          (uint16_t)((q[0] & 0xFF) | ((q[1] & 0xFF) << 8));
+    } else {
+      cb[o * D + lane] = (int8_t)q[0];
+    }
+  }
+  float* sp = a.scale + (blk * a.H + h) * D;
+  if constexpr (CPL == 2) {
+    float2 sv = {s[0], s[1]};
+    *reinterpret_cast<float2*>(sp + 2 * lane) = sv;
+  } else {
+    sp[lane] = s[0];
+  }
+}
+
+// The slot and stage row of token t, when they complete a block (else
+// slot = -1).
+template <int BS>
+__device__ __forceinline__ void chan_completing(const ChanArgs& a, int64_t t, int64_t& slot,
+                                                int32_t& srow) {
+  slot = a.slots[t];
+  srow = a.stage_rows[t];
+  if (slot < 0 || slot % BS != BS - 1 || slot / BS >= a.num_blocks || srow < 0 ||
+      srow >= a.max_seqs)
+    slot = -1;
+}
+
+// Small appends (a decode step's few tokens per sequence): one wave per
+// (token, head) item, so that the items that complete no block (all but about
+// one in BS) cost a single slot load each, side by side.
 template <int D, int BS, bool BF16>
 __global__ __launch_bounds__(256) void chan_complete_kernel(ChanArgs a) {
-  constexpr int CPL = D / kWave;  // channels per lane (1 or 2)
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
@@ -450,73 +537,34 @@ __global__ __launch_bounds__(256) void chan_complete_kernel(ChanArgs a) {
   for (int64_t it = wave; it < items; it += nwaves) {
     const int64_t t = it / a.H;
     const int h = (int)(it % a.H);
-    const int64_t slot = a.slots[t];
-    if (slot < 0 || slot % BS != BS - 1) continue;
-    const int64_t blk = slot / BS;
-    const int32_t srow = a.stage_rows[t];
-    if (blk >= a.num_blocks || srow < 0 || srow >= a.max_seqs) continue;
-    // rows of this block provided by this call: t - k for k < n_new, the
-    // run of preceding tokens with consecutive slots and the same stage row;
-    // lane l checks token t - 1 - l, all lanes at once
-    bool match = false;
-    if (lane < BS - 1 && t - 1 - lane >= 0) {
-      const int64_t tp = t - 1 - lane;
-      match = a.slots[tp] == slot - 1 - lane && a.stage_rows[tp] == srow;
-    }
-    // at most BS - 1 < 64 bits are set, so the complement is never 0
-    const int n_new = 1 + __builtin_ctzll(~(uint64_t)__ballot(match));
-    float x[BS][CPL];
-    float amax[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) amax[c] = 0.0f;
-#pragma unroll
-    for (int o = 0; o < BS; ++o) {
-      const int k = BS - 1 - o;  // token t - k holds offset o when k < n_new
-      const uint16_t* p;
-      if (k < n_new)
-        p = a.src + (t - k) * a.row_stride + (int64_t)h * D;
-      else
-        p = a.stage + (((int64_t)srow * a.H + h) * BS + o) * D;
-      if constexpr (CPL == 2) {
-        uint32_t w = *reinterpret_cast<const uint32_t*>(p + 2 * lane);
-        unpack2<BF16>(w, x[o][0], x[o][1]);
-      } else {
-        uint16_t w = p[lane];
-        x[o][0] = BF16 ? bf16_lo(w) : f16_lo(w);
-      }
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) amax[c] = fmaxf(amax[c], fabsf(x[o][c]));
-    }
-    float s[CPL], inv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      s[c] = amax[c] == 0.0f ? 1.0f : div_rn(amax[c], 127.0f);
-      inv[c] = div_rn(1.0f, s[c]);
-    }
-    int8_t* cb = a.codes + ((blk * a.H + h) * BS) * D;
-#pragma unroll
-    for (int o = 0; o < BS; ++o) {
-      int q[CPL];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float y = x[o][c] * inv[c];
-        float r = rne(y);
-        if (near_half(y, r) || recip_unsafe(s[c])) r = rne(div_rn(x[o][c], s[c]));
-        q[c] = (int)fminf(fmaxf(r, -127.0f), 127.0f);
-      }
-      if constexpr (CPL == 2) {
-        *reinterpret_cast<uint16_t*>(cb + o * D + 2 * lane) =
-            (uint16_t)((q[0] & 0xFF) | ((q[1] & 0xFF) << 8));
-      } else {
-        cb[o * D + lane] = (int8_t)q[0];
-      }
-    }
-    float* sp = a.scale + (blk * a.H + h) * D;
-    if constexpr (CPL == 2) {
-      float2 sv = {s[0], s[1]};
-      *reinterpret_cast<float2*>(sp + 2 * lane) = sv;
-    } else {
-      sp[lane] = s[0];
+    int64_t slot;
+    int32_t srow;
+    chan_completing<BS>(a, t, slot, srow);
+    if (slot >= 0) chan_block<D, BS, BF16>(a, t, h, slot, srow, lane);
+  }
+}
+
+// Bulk appends (prompts): one wave per (64-token chunk, head): lane l reads
+// token 64 c + l's slot and stage row, and the wave quantizes the blocks the
+// chunk's tokens complete, one after another, instead of paying a dependent
+// slot load per (token, head).
+template <int D, int BS, bool BF16>
+__global__ __launch_bounds__(256) void chan_complete_chunked_kernel(ChanArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  const int64_t items = (a.num_tokens + kWave - 1) / kWave * a.H;
+  for (int64_t it = wave; it < items; it += nwaves) {
+    const int64_t t0 = it / a.H * kWave;
+    const int h = (int)(it % a.H);
+    int64_t slot = -1;
+    int32_t srow = -1;
+    if (t0 + lane < a.num_tokens) chan_completing<BS>(a, t0 + lane, slot, srow);
+    for (uint64_t m = __ballot(slot >= 0); m; m &= m - 1) {
+      const int i = __builtin_ctzll(m);
+      const int64_t st = ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), i) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)slot, i);
+      chan_block<D, BS, BF16>(a, t0 + i, h, st, __builtin_amdgcn_readlane(srow, i), lane);
     }
   }
 }
@@ -636,6 +684,67 @@ __global__ __launch_bounds__(256) void chan_stage_kernel(ChanArgs a) {
   }
 }
 
+// Phase 2 for bulk appends: lane l of a wave holds the metadata of row
+// 64 c + l (row = token H + head), and the wave copies the rows that need the
+// stage, four at a time (16 lanes of 16 bytes per row at D = 128, eight per
+// row at D = 64).
+template <int D, int BS>
+__global__ __launch_bounds__(256) void chan_stage_chunked_kernel(ChanArgs a) {
+  constexpr int RL = D / 8;          // lanes per row
+  constexpr int RPW = kWave / RL;    // rows per copy step
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = lane % RL;
+  const int64_t rows = a.num_tokens * a.H;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  for (int64_t base = wave * kWave; base < rows; base += nwaves * kWave) {
+    const int64_t r = base + lane;
+    bool need = false;
+    int64_t dst = 0;
+    if (r < rows) {
+      const int64_t t = r / a.H;
+      const int h = (int)(r % a.H);
+      const int64_t slot = a.slots[t];
+      const int32_t srow = a.stage_rows[t];
+      if (slot >= 0 && srow >= 0 && srow < a.max_seqs && slot / BS < a.num_blocks) {
+        const int off = (int)(slot % BS);
+        const int64_t tl = t + (BS - 1 - off);
+        const bool completes = tl < a.num_tokens && a.slots[tl] == slot + (BS - 1 - off) &&
+                               a.stage_rows[tl] == srow;
+        need = !completes;
+        dst = (((int64_t)srow * a.H + h) * BS + off) * D;
+      }
+    }
+    // the rows that need the stage, RPW at a time: lane group q copies the
+    // row of the q-th lowest remaining set bit (the picks are wave-uniform)
+    uint64_t rem = __ballot(need);
+    const int q = lane / RL;
+    while (rem) {
+      int src = -1;
+#pragma unroll
+      for (int z = 0; z < RPW; ++z) {
+        const int b = rem ? __builtin_ctzll(rem) : -1;
+        rem &= rem - 1;   // rem = 0 stays 0
+        if (z == q) src = b;
+      }
+      const int64_t dd = __shfl(dst, src < 0 ? 0 : src);
+      if (src >= 0) {
+        const int64_t rr = base + src;
+        const int64_t t = rr / a.H;
+        const int h = (int)(rr % a.H);
+        const u32x4 w =
+            *reinterpret_cast<const u32x4*>(a.src + t * a.row_stride + (int64_t)h * D + 8 * j);
+        *reinterpret_cast<u32x4*>(a.stage + dd + 8 * j) = w;
+      }
+    }
+  }
+}
+
+// (token, head) items above which a per-channel key append takes the chunked
+// kernels: two items per wave of the largest grid (256 CUs x 16 workgroups of
+// four waves).
+constexpr int64_t kChanBulkItems = 2 * 256 * 16 * 4;
+
 int grid_for(int64_t waves_needed, int cu_count) {
   int64_t blocks = (waves_needed + 3) / 4;
   int64_t cap = (int64_t)cu_count * 16;
@@ -686,14 +795,27 @@ hipError_t launch_chan(const AppendPlan& p, hipStream_t stream) {
   c.H = p.num_kv_heads;
   c.max_seqs = p.max_seqs;
   const int64_t items = p.num_tokens * p.num_kv_heads;
-  // phase 1: one wave per (token, head) item while the grid allows, so
-  // that the items that complete no block (all but about one in BS) cost a
-  // single slot load each, side by side
-  chan_complete_kernel<D, BS, BF16><<<grid_for(items, p.cu_count), 256, 0, stream>>>(c);
-  hipError_t e = hipGetLastError();
+  // Up to a few items per wave of the full grid (a decode step's append),
+  // one wave per (token, head) item; beyond, the chunked kernels, whose
+  // waves read 64 tokens' slots at once
+  const bool bulk = items > kChanBulkItems;
+  hipError_t e;
+  if (bulk) {
+    const int64_t chunk_items = (p.num_tokens + kWave - 1) / kWave * p.num_kv_heads;
+    chan_complete_chunked_kernel<D, BS, BF16>
+        <<<grid_for(chunk_items, p.cu_count), 256, 0, stream>>>(c);
+  } else {
+    chan_complete_kernel<D, BS, BF16><<<grid_for(items, p.cu_count), 256, 0, stream>>>(c);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t waves = (items + (kWave / (D / 8)) - 1) / (kWave / (D / 8));
-  chan_stage_kernel<D, BS><<<grid_for(waves, p.cu_count), 256, 0, stream>>>(c);
+  if (bulk) {
+    chan_stage_chunked_kernel<D, BS>
+        <<<grid_for((items + kWave - 1) / kWave, p.cu_count), 256, 0, stream>>>(c);
+  } else {
+    const int64_t waves = (items + (kWave / (D / 8)) - 1) / (kWave / (D / 8));
+    chan_stage_kernel<D, BS><<<grid_for(waves, p.cu_count), 256, 0, stream>>>(c);
+  }
   return hipGetLastError();
 }
 

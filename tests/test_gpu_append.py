@@ -173,3 +173,45 @@ def test_append_channel_block_keys_in_chunks():
     for b, Lb in enumerate(lens_final):
         tail = Lb % 16
         assert np.array_equal(st_g[b, :, :tail], st_h[b, :, :tail]), b
+
+
+def test_append_channel_block_keys_bulk_then_step():
+    """Per-channel keys through both append paths: two bulk calls (more than
+    131072 (token, head) items each, taken 64 tokens at a time per wave) that
+    leave every sequence with a partial block, whose rows the second call and
+    then a small call (one wave per (token, head)) complete; completed
+    blocks, value planes and staged rows equal the oracle's."""
+    need_gpu()
+    B = 48
+    w = workloads.get("mixed", batch=B)
+    L, LL = oracle_layout(w), lib_layout(w)
+    g = np.random.default_rng(21)
+    lens_final = g.integers(500, 1500, B).astype(np.int32)
+    c1 = (lens_final * g.uniform(0.45, 0.65, B)).astype(np.int32)
+    c2 = ((lens_final - c1) * g.uniform(0.7, 0.95, B)).astype(np.int32)
+    c3 = lens_final - c1 - c2
+    assert c1.sum() * w.num_kv_heads > 131072 and c2.sum() * w.num_kv_heads > 131072
+    starts = np.concatenate([[0], np.cumsum(lens_final)[:-1]])
+    k, v = workloads.kv_rows(w, int(lens_final.sum()), seed=11)
+    nb = workloads.pool_blocks(lens_final, 16) + 8
+    maxb = int(lens_final.max()) // 16 + 2
+    seqs = OracleSeqs(L, nb, B, maxb, order=workloads.pool_order(nb, seed=3), max_seqs=B)
+    seqs.cache = ref.HostCache(L, nb, B, fill=0)
+    gc = gpu_cache(LL, nb, B, fill=0)
+    done = np.zeros(B, np.int64)
+    for ch in (c1, c2, c3):
+        idx = np.concatenate([starts[b] + done[b] + np.arange(ch[b]) for b in range(B)]).astype(np.int64)
+        slots, rows = seqs.grow(ch)
+        kk, vv = k[idx], v[idx]
+        ref.append(L, seqs.cache, bits(kk).reshape(len(idx), -1), bits(vv).reshape(len(idx), -1),
+                   slots, rows)
+        kq.kvq_append(LL, gc, kk.to(DEV), vv.to(DEV), torch.from_numpy(slots).to(DEV),
+                      stage_rows=torch.from_numpy(rows).to(DEV))
+        done += ch
+        torch.cuda.synchronize()
+        assert planes_equal(gc, seqs.cache, ["k_codes", "k_scale", "v_codes", "v_scale"]) == []
+        st_g = gc.planes["k_stage"].cpu().numpy().reshape(B, 8, 16, 256)
+        st_h = seqs.cache.planes["k_stage"].reshape(B, 8, 16, 256)
+        for b in range(B):
+            tail = int(done[b]) % 16
+            assert np.array_equal(st_g[b, :, :tail], st_h[b, :, :tail]), b
