@@ -170,8 +170,8 @@ __device__ __forceinline__ int wave_reduce_i(int x) {
 // items need no balancing and fewer, longer shares pay the start-up chain
 // less often; any other batch into twice as many shorter shares (at most
 // decode_skew_cap(key mode) blocks), which the dispatcher balances.
-__device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, const int* len0) {
-  if (p.split_blocks > 0) return p.split_blocks;
+__device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, const int* len0,
+                                                 bool& uniform) {
   // block counts fit in int32: the host bounds batch * ceil(max_len / bs)
   int tot32 = 0, nmax = 0, nmin = INT32_MAX;
   for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
@@ -188,7 +188,8 @@ __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, co
   const int64_t tot = wave_sum(tot32, lane);
   nmax = wave_reduce_i<true>(nmax);
   nmin = wave_reduce_i<false>(nmin);
-  const bool uniform = (int64_t)nmax * 8 <= (int64_t)nmin * 9;
+  uniform = (int64_t)nmax * 8 <= (int64_t)nmin * 9;
+  if (p.split_blocks > 0) return p.split_blocks;
   const int lg = uniform ? kDecodeUniformWavesLog2 : kDecodeTargetWavesLog2;
   const int cap = uniform ? kDecodeMaxWaveBlocks : p.skew_cap;
   int64_t w = (tot * p.H + (int64_t(1) << lg) - 1) >> lg;
@@ -206,43 +207,10 @@ struct PlanItem {
   int S;    // blocks per split
 };
 
-// Item `item` of the plan; false past the last item.
-__device__ __forceinline__ bool plan_find_item(const PlanArgs& p, int item, int lane,
-                                               PlanItem& out) {
-  int len0[4];
-  plan_len4(p, 0, lane, len0);
-  const int S = plan_split_blocks(p, lane, len0);
-  out.S = S;
-  int off = 0;
-  for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
-    int len[4];
-    plan_chunk(p, c0, lane, len0, len);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ns = plan_splits_of(p, len[u], S);
-      const int incl = wave_incl_scan(ns, lane);
-      const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
-      if (item < off + tot) {
-        const int f = __builtin_ctzll(__ballot(off + incl > item));
-        out.b = c0 + u * kWave + f;
-        out.len = __builtin_amdgcn_readlane(len[u], f);
-        out.ns = __builtin_amdgcn_readlane(ns, f);
-        out.off = off + __builtin_amdgcn_readlane(incl, f) - out.ns;
-        out.j = item - out.off;
-        return out.b < p.batch;   // always, for consistent lengths
-      }
-      off += tot;
-    }
-  }
-  return false;
-}
-
-// Splits of sequence b and of all sequences before it.
-__device__ __forceinline__ void plan_sequence(const PlanArgs& p, int b, int lane, int& off,
-                                              int& ns) {
-  int len0[4];
-  plan_len4(p, 0, lane, len0);
-  const int S = plan_split_blocks(p, lane, len0);
+// Splits of sequence b (ns) and of all sequences before it (off), for S
+// blocks per split; len0 holds the first 256 lengths (plan_len4).
+__device__ __forceinline__ void plan_sequence_of(const PlanArgs& p, int b, int lane,
+                                                 const int* len0, int S, int& off, int& ns) {
   int acc = 0;
   for (int c0 = 0; c0 < b; c0 += 4 * kWave) {
     int len[4];
@@ -253,6 +221,180 @@ __device__ __forceinline__ void plan_sequence(const PlanArgs& p, int b, int lane
   }
   off = wave_sum(acc, lane);
   ns = plan_splits_of(p, plan_len(p, b), S);
+}
+
+// Sequences (of the batch) whose last split is partial with at least r of
+// its S blocks (r >= 1).
+__device__ __forceinline__ int plan_partials_from(const PlanArgs& p, const int* len0, int S,
+                                                  int r, int lane) {
+  int cnt = 0;
+#pragma unroll 1
+  for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
+    int len[4];
+    plan_chunk(p, c0, lane, len0, len);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      cnt += __builtin_popcountll(__ballot(((len[u] + p.bs - 1) / p.bs) % S >= r));
+  }
+  return cnt;
+}
+
+// What every item lookup of one launch shares: the first 256 lengths, the
+// blocks per split and whether the batch has nearly equal lengths.
+struct PlanCtx {
+  int len0[4];
+  int S;
+  bool uniform;
+};
+
+__device__ __forceinline__ PlanCtx plan_ctx(const PlanArgs& p, int lane) {
+  PlanCtx c;
+  plan_len4(p, 0, lane, c.len0);
+  c.S = plan_split_blocks(p, lane, c.len0, c.uniform);
+  return c;
+}
+
+// Workgroups the plan occupies: its items times the KV heads, in whole runs
+// of 16 (see workgroup_item).
+__device__ __forceinline__ int plan_workgroups(const PlanArgs& p, const PlanCtx& c, int lane) {
+  int total = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
+    int len[4];
+    plan_chunk(p, c0, lane, c.len0, len);
+    int t4 = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t4 += plan_splits_of(p, len[u], c.S);
+    total += wave_sum(t4, lane);
+  }
+  return (total * p.H + 15) / 16 * 16;
+}
+
+// Item `item` of the plan; false past the last item. The partial row of
+// item (b, j) is fixed by (b, j) alone (see plan_sequence); only which
+// workgroup computes it depends on the order here. A batch of nearly equal
+// lengths is taken sequence-major. Any other batch is taken longest first,
+// so that its short splits, not long ones, close the launch: first every
+// full split (S blocks) in sequence order, then the sequences' partial last
+// splits by size, largest first, in sequence order among equal sizes.
+__device__ __forceinline__ bool plan_find_item(const PlanArgs& p, const PlanCtx& ctx, int item,
+                                               int lane, PlanItem& out) {
+  const int* len0 = ctx.len0;
+  const bool uniform = ctx.uniform;
+  const int S = ctx.S;
+  out.S = S;
+  if (uniform) {
+    int off = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
+      int len[4];
+      plan_chunk(p, c0, lane, len0, len);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ns = plan_splits_of(p, len[u], S);
+        const int incl = wave_incl_scan(ns, lane);
+        const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+        if (item < off + tot) {
+          const int f = __builtin_ctzll(__ballot(off + incl > item));
+          out.b = c0 + u * kWave + f;
+          out.len = __builtin_amdgcn_readlane(len[u], f);
+          out.ns = __builtin_amdgcn_readlane(ns, f);
+          out.off = off + __builtin_amdgcn_readlane(incl, f) - out.ns;
+          out.j = item - out.off;
+          return out.b < p.batch;   // always, for consistent lengths
+        }
+        off += tot;
+      }
+    }
+    return false;
+  }
+  // counts of full splits and of all splits: the grid is sized for the
+  // longest possible contexts, so most workgroups of a skewed batch find no
+  // item and leave here
+  int full = 0, total = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 4 * kWave) {
+    int len[4];
+    plan_chunk(p, c0, lane, len0, len);
+    int f4 = 0, t4 = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = (len[u] + p.bs - 1) / p.bs;
+      f4 += n / S;
+      t4 += (n + S - 1) / S;
+    }
+    full += wave_sum(f4, lane);
+    total += wave_sum(t4, lane);
+  }
+  if (item >= total) return false;
+  int b = -1, j = 0;
+  if (item < full) {   // the item-th full split, sequence order
+    int off = 0;
+#pragma unroll 1
+    for (int c0 = 0; c0 < p.batch && b < 0; c0 += 4 * kWave) {
+      int len[4];
+      plan_chunk(p, c0, lane, len0, len);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int F = (len[u] + p.bs - 1) / p.bs / S;
+        const int incl = wave_incl_scan(F, lane);
+        const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+        if (b < 0 && item < off + tot) {
+          const int f = __builtin_ctzll(__ballot(off + incl > item));
+          b = c0 + u * kWave + f;
+          j = item - (off + __builtin_amdgcn_readlane(incl, f) - __builtin_amdgcn_readlane(F, f));
+        }
+        off += tot;
+      }
+    }
+  } else {             // a partial last split: its size r, then its rank there
+    const int w = item - full;
+    // the largest r with more than w partial splits of at least r blocks
+    int lo = 1, hi = S - 1;
+#pragma unroll 1
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (plan_partials_from(p, len0, S, mid, lane) > w)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int r = lo;
+    int k = w - (r + 1 < S ? plan_partials_from(p, len0, S, r + 1, lane) : 0);
+#pragma unroll 1
+    for (int c0 = 0; c0 < p.batch && b < 0; c0 += 4 * kWave) {
+      int len[4];
+      plan_chunk(p, c0, lane, len0, len);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int n = (len[u] + p.bs - 1) / p.bs;
+        const uint64_t m = __ballot(n % S == r);
+        const int pc = __builtin_popcountll(m);
+        if (b < 0 && k < pc) {
+          // the lane holding the k-th set bit of m
+          const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+          const int f = __builtin_ctzll(__ballot(((m >> lane) & 1) && rank == k));
+          b = c0 + u * kWave + f;
+          j = __builtin_amdgcn_readlane(n / S, f);   // the last split
+        }
+        if (b < 0) k -= pc;
+      }
+    }
+  }
+  if (b < 0 || b >= p.batch) return false;
+  out.b = b;
+  plan_sequence_of(p, b, lane, len0, S, out.off, out.ns);
+  out.len = plan_len(p, b);
+  out.j = j;
+  return true;
+}
+
+// Splits of sequence b and of all sequences before it.
+__device__ __forceinline__ void plan_sequence(const PlanArgs& p, int b, int lane, int& off,
+                                              int& ns) {
+  int len0[4];
+  plan_len4(p, 0, lane, len0);
+  bool uniform;
+  const int S = plan_split_blocks(p, lane, len0, uniform);
+  plan_sequence_of(p, b, lane, len0, S, off, ns);
 }
 
 // Block ids of blocks [i0, ilast] of one sequence, 64 at a time: lane k of
@@ -496,60 +638,13 @@ __device__ __forceinline__ void workgroup_item(int H, int w, int& item, int& g) 
   }
 }
 
-// One item of the plan per workgroup and KV head: the split's S blocks are
-// cut into kNW consecutive shares, one per wave; the
-// waves merge their softmax states through LDS and wave 0 writes the split's
-// partial.
-
-template <int CODE, int MODE, int D, int BS>
-__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_kernel(DecodeArgs a) {
-  constexpr int NPV = D / 16;   // output MFMAs (16 d-rows each)
-  constexpr int NV = D / 4;     // accumulator values per lane
-  __shared__ float red[kNW][NV + 2][kWave];
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+// Wave 0: merge the kNW wave states in red and write the split's partial.
+template <int CODE, int D>
+__device__ __forceinline__ void split_write(const DecodeArgs& a, const PlanItem& it, int g,
+                                            int lane, float (*red)[D / 4 + 2][kWave]) {
+  constexpr int NPV = D / 16;
+  constexpr int NV = D / 4;
   const int r = lane & 15, j = lane >> 4;
-  int wg_item, g;
-  workgroup_item(a.H, blockIdx.x, wg_item, g);
-  // every wave derives the same plan, so the early exit is workgroup-uniform
-  const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, BS, a.H, a.split_blocks,
-                                decode_skew_cap(MODE));
-  PlanItem it;
-  if (!plan_find_item(pa, wg_item, lane, it)) return;
-  const int S = it.S;
-  const int b = it.b, L = it.len;
-  const int nblk = (L + BS - 1) / BS;
-  const int s0 = it.j * S;
-  const int s1 = min(s0 + S, nblk);
-  // the item's blocks split evenly over the waves (a short last split or a
-  // short sequence keeps every wave busy)
-  const int share = (s1 - s0 + kNW - 1) / kNW;
-  const int i0 = s0 + wave * share;
-  const int i1 = min(i0 + share, s1);
-
-  SoftmaxState<D> st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NPV; ++c) st.acc[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-  if (i0 < i1) {
-    if constexpr (CODE == KVQ_CODE_INT4)
-      wave_blocks_int4<D, BS, MODE>(a, b, g, L, nblk, i0, i1, lane, st);
-    else
-      wave_blocks<CODE, D, BS, MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM>(a, b, g, L, nblk, i0, i1,
-                                                                     lane, st, &red[wave][0][0]);
-  }
-
-  // ---- merge the waves' states, then write the split's partial ----------
-  const float lsum = colsum4(st.l);
-#pragma unroll
-  for (int c = 0; c < NPV; ++c)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][4 * c + e][lane] = st.acc[c][e];
-  red[wave][NV][lane] = st.m;
-  red[wave][NV + 1][lane] = lsum;
-  __syncthreads();
-  if (wave != 0) return;
   float M = red[0][NV][lane];
 #pragma unroll
   for (int w = 1; w < kNW; ++w) M = fmaxf(M, red[w][NV][lane]);
@@ -597,6 +692,99 @@ void decode_split_kernel(DecodeArgs a) {
         float4v v4 = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
         *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
       }
+    }
+  }
+}
+
+// One item of the plan: the split's S blocks are cut into kNW consecutive
+// shares, one per wave; the waves merge their softmax states through LDS and
+// wave 0 writes the split's partial. Every wave calls this (it holds
+// workgroup barriers); with ROUNDS the waves wait for wave 0 at the end, so
+// that a next item may reuse red.
+template <int CODE, int MODE, int D, int BS, bool ROUNDS>
+__device__ __forceinline__ void split_item(const DecodeArgs& a, const PlanItem& it, int g,
+                                           int lane, int wave,
+                                           float (*red)[D / 4 + 2][kWave]) {
+  constexpr int NPV = D / 16;   // output MFMAs (16 d-rows each)
+  constexpr int NV = D / 4;     // accumulator values per lane
+  const int S = it.S;
+  const int b = it.b, L = it.len;
+  const int nblk = (L + BS - 1) / BS;
+  const int s0 = it.j * S;
+  const int s1 = min(s0 + S, nblk);
+  // the item's blocks split evenly over the waves (a short last split or a
+  // short sequence keeps every wave busy)
+  const int share = (s1 - s0 + kNW - 1) / kNW;
+  const int i0 = s0 + wave * share;
+  const int i1 = min(i0 + share, s1);
+
+  SoftmaxState<D> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NPV; ++c) st.acc[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  if (i0 < i1) {
+    if constexpr (CODE == KVQ_CODE_INT4)
+      wave_blocks_int4<D, BS, MODE>(a, b, g, L, nblk, i0, i1, lane, st);
+    else
+      wave_blocks<CODE, D, BS, MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM>(a, b, g, L, nblk, i0, i1,
+                                                                     lane, st, &red[wave][0][0]);
+  }
+
+  // ---- merge the waves' states, then write the split's partial ----------
+  const float lsum = colsum4(st.l);
+#pragma unroll
+  for (int c = 0; c < NPV; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][4 * c + e][lane] = st.acc[c][e];
+  red[wave][NV][lane] = st.m;
+  red[wave][NV + 1][lane] = lsum;
+  __syncthreads();
+  if (wave == 0) split_write<CODE, D>(a, it, g, lane, red);
+  // the next item's waves write red only after wave 0 has read it
+  if constexpr (ROUNDS) __syncthreads();
+}
+
+// Workgroup w takes the plan's (item, KV head) pair w. ROUNDS (a grid of
+// kDecodeMaxGrid workgroups, for plans the host can only bound above that,
+// i.e. large skewed batches whose bound assumes every context at its
+// longest): the workgroups take the pairs x = 0, 1, ... in rounds of the grid
+// size G, round 0 pair w and later rounds pair x0 + w or x0 + G - 1 - w (odd
+// rounds), so that the extra pairs go first to the workgroups dispatched
+// last, which hold the shortest items; without it such a batch would launch
+// thousands of workgroups that find no item. Only scalars cross the rounds
+// (each derives the plan again from the cached lengths): the rounds cost
+// registers, so plans within the bound take the single-pair kernel.
+template <int CODE, int MODE, int D, int BS, bool ROUNDS>
+__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_kernel(DecodeArgs a) {
+  constexpr int NV = D / 4;
+  __shared__ float red[kNW][NV + 2][kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  // every wave derives the same plan, so every branch below is
+  // workgroup-uniform
+  const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, BS, a.H, a.split_blocks,
+                                decode_skew_cap(MODE));
+  if constexpr (!ROUNDS) {
+    int wg_item, g;
+    workgroup_item(a.H, blockIdx.x, wg_item, g);
+    const PlanCtx ctx = plan_ctx(pa, lane);
+    PlanItem it;
+    if (!plan_find_item(pa, ctx, wg_item, lane, it)) return;
+    split_item<CODE, MODE, D, BS, false>(a, it, g, lane, wave, red);
+  } else {
+    const int G = (int)gridDim.x, w = (int)blockIdx.x;
+    int need = 0;
+    for (int x0 = 0, odd = 0; x0 == 0 || x0 < need; x0 += G, odd ^= 1) {
+      const PlanCtx ctx = plan_ctx(pa, lane);
+      need = __builtin_amdgcn_readfirstlane(plan_workgroups(pa, ctx, lane));
+      const int x = x0 + (odd ? G - 1 - w : w);
+      if (x >= need) continue;
+      int wg_item, g;
+      workgroup_item(a.H, x, wg_item, g);
+      PlanItem it;
+      if (!plan_find_item(pa, ctx, wg_item, lane, it)) continue;
+      split_item<CODE, MODE, D, BS, true>(a, it, g, lane, wave, red);
     }
   }
 }
@@ -683,9 +871,13 @@ __global__ __launch_bounds__(64 * kReduceHeads) void decode_reduce_kernel(Reduce
 
 template <int CODE, int MODE, int D, int BS>
 hipError_t launch_split(const DecodeArgs& a, int items, hipStream_t stream) {
-  // whole runs of 16 workgroups (see workgroup_item); the extra ones find no item
-  dim3 grid((items * a.H + 15) / 16 * 16);
-  decode_split_kernel<CODE, MODE, D, BS><<<grid, 64 * kNW, 0, stream>>>(a);
+  // whole runs of 16 workgroups (see workgroup_item); the extra ones find no
+  // item. Beyond kDecodeMaxGrid workgroups, the grid is capped and takes rounds.
+  const int64_t pairs = ((int64_t)items * a.H + 15) / 16 * 16;
+  if (pairs <= kDecodeMaxGrid)
+    decode_split_kernel<CODE, MODE, D, BS, false><<<dim3((unsigned)pairs), 64 * kNW, 0, stream>>>(a);
+  else
+    decode_split_kernel<CODE, MODE, D, BS, true><<<dim3(kDecodeMaxGrid), 64 * kNW, 0, stream>>>(a);
   return hipGetLastError();
 }
 

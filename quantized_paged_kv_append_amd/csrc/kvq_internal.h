@@ -97,6 +97,11 @@ __host__ __device__ constexpr int decode_skew_cap(int32_t k_mode) {
                                                : kDecodeSkewWaveBlocks;
 }
 
+// Largest decode split grid: sixteen workgroups of kDecodeWaves waves per
+// CU of a 256-CU chip, a multiple of 16; when the host's bound on the (item,
+// KV head) pairs is larger, a grid of this size takes the pairs in rounds.
+constexpr int kDecodeMaxGrid = 4096;
+
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
 // Device address of the current device's decode scratch array
 // (KVQ_DECODE_SCRATCH_BYTES, 256-byte aligned), looked up once per device.
