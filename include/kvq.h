@@ -304,8 +304,9 @@ int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch,
  * both NONE16; other layouts return KVQ_ERR_UNSUPPORTED.
  * Preconditions: num_q_heads is a multiple of H and num_q_heads / H <= 16;
  * dequantized values v satisfy |v| / 127 < 65504 (fp16 range of the folded
- * value scale); bf16 keys and values read raw (NONE16, staged rows) lie
- * within fp16's range. */
+ * value scale). Rows read raw (NONE16, staged rows) enter the matrix
+ * instructions in their own 16-bit format, so bf16 rows keep bf16's range;
+ * only sums past fp32's range overflow. */
 kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache,
                                 const void* q, int32_t q_dtype, int32_t batch,
                                 int32_t num_q_heads, const int32_t* block_tables,

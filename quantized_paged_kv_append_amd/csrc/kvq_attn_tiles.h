@@ -192,17 +192,38 @@ struct SoftmaxState {
   float4v acc[D / 16];     // O^T accumulators
 };
 
-// Eight raw 16-bit key values to fp16 operands: bf16 values are exact in
-// fp16 within its range (the same bound as for value scales).
-__device__ __forceinline__ half8v raw8_to_h8(const u32x4& w, bool bf16) {
-  if (!bf16) return __builtin_bit_cast(half8v, w);
-  half8v o;
+// Raw 16-bit rows (the passthrough cache, staged per-channel key rows) enter
+// the MFMA in their own format: fp16 rows through the f16 instructions, bf16
+// rows through the bf16 ones, so that no element is rounded or leaves its
+// range on the way. The other operand (the power-of-two-scaled query, the
+// softmax weights) is fp32 and goes to the bf16 instructions as a pair
+// hi + lo of bf16 values: hi = x rounded to bf16, lo = (x - hi) rounded to
+// bf16 (x - hi is exact in fp32), which holds x to a relative 2^-17.
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void bf16_split8(const float* x, half8v& hi, half8v& lo) {
+  bf16x8v h, l;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    o[2 * u] = (half_t)bf16_lo(w[u]);
-    o[2 * u + 1] = (half_t)bf16_hi(w[u]);
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
   }
-  return o;
+  hi = __builtin_bit_cast(half8v, h);
+  lo = __builtin_bit_cast(half8v, l);
+}
+
+// S += rows (eight raw 16-bit elements per lane) x query. bf16: the query is
+// the pair qhi + qlo of bf16_split8; fp16: qhi is the fp16 query.
+__device__ __forceinline__ float4v raw_scores(const u32x4& rows, const half8v& qhi,
+                                              const half8v& qlo, float4v S, bool bf16) {
+  if (bf16) {
+    const bf16x8v k = __builtin_bit_cast(bf16x8v, rows);
+    S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, __builtin_bit_cast(bf16x8v, qhi), S, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, __builtin_bit_cast(bf16x8v, qlo), S, 0, 0,
+                                                   0);
+  }
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8v, rows), qhi, S, 0, 0, 0);
 }
 
 // Where the keys of a tile come from.
@@ -232,15 +253,14 @@ __device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos
   float4v S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    half8v kop;
-    if constexpr (KSRC == kKeyRaw) {
-      kop = raw8_to_h8(kraw[c], raw_bf16);
-    } else {
-      const u32x4& kw = t.k[nt][c / 2];
-      const uint32_t lo = (c & 1) ? kw.z : kw.x;
-      const uint32_t hi = (c & 1) ? kw.w : kw.y;
-      kop = codes8_to_h8<CODE>(lo, hi);
+    if constexpr (KSRC == kKeyRaw) {   // bf16 rows: qop/qlo are the bf16 pair
+      S = raw_scores(kraw[c], qop[c], raw_bf16 ? qlo[c] : qop[c], S, raw_bf16);
+      continue;
     }
+    const u32x4& kw = t.k[nt][c / 2];
+    const uint32_t lo = (c & 1) ? kw.z : kw.x;
+    const uint32_t hi = (c & 1) ? kw.w : kw.y;
+    const half8v kop = codes8_to_h8<CODE>(lo, hi);
     S = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[c], S, 0, 0, 0);
     if constexpr (KSRC == kKeyChannel)  // low half of the split query
       S = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo[c], S, 0, 0, 0);
@@ -354,16 +374,17 @@ __device__ __forceinline__ void last_block_step(const Tile8<D, BS>& t, int i, in
                                                 const half8v* qop, float cscore, int j,
                                                 SoftmaxState<D>& st,
                                                 const u32x4 (*kraw)[D / 32] = nullptr,
-                                                bool raw_bf16 = false) {
+                                                bool raw_bf16 = false,
+                                                const half8v* qlo = nullptr) {
   constexpr int KS = KRAW ? kKeyRaw : kKeyTokenScale;
 #pragma unroll
   for (int nt = 0; nt < BS / 16; ++nt) {
     const int pos0 = i * BS + nt * 16;
     const u32x4* kr = KRAW ? kraw[nt] : nullptr;
     if (pos0 + 16 <= L)
-      tile_step<CODE, D, BS, false, KS>(t, nt, pos0, L, qop, cscore, j, st, kr, raw_bf16);
+      tile_step<CODE, D, BS, false, KS>(t, nt, pos0, L, qop, cscore, j, st, kr, raw_bf16, qlo);
     else if (pos0 < L)
-      tile_step<CODE, D, BS, true, KS>(t, nt, pos0, L, qop, cscore, j, st, kr, raw_bf16);
+      tile_step<CODE, D, BS, true, KS>(t, nt, pos0, L, qop, cscore, j, st, kr, raw_bf16, qlo);
   }
 }
 
@@ -380,12 +401,13 @@ __device__ __forceinline__ void load_query(const uint16_t* qp, float* qf) {
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit passthrough (KVQ_CODE_NONE16): rows hold the source values. Keys
-// enter the score MFMA as fp16 like the staged rows above (lane (r, j):
-// elements [j d/4, (j+1) d/4) of token r). Values: lane (r, j) loads
-// elements [r d/16, (r+1) d/16) of tokens 4j..4j+3, and the operand of PV
-// MFMA c is element c of those four tokens -- the same output mapping as
-// the 8-bit codes. bf16 values convert to fp16 exactly within fp16's range.
+// 16-bit passthrough (KVQ_CODE_NONE16): rows hold the source values and
+// enter both MFMAs in their own format, as the staged rows above do. Keys:
+// lane (r, j) holds elements [j d/4, (j+1) d/4) of token r. Values: lane
+// (r, j) loads elements [r d/16, (r+1) d/16) of tokens 4j..4j+3, and the
+// operand of PV MFMA c is element c of those four tokens -- the same output
+// mapping as the 8-bit codes. bf16 rows take two MFMAs per step (the hi and
+// lo halves of the query or of the weights).
 // ---------------------------------------------------------------------------
 template <int D, int BS>
 struct TileRaw {
@@ -423,35 +445,25 @@ __device__ __forceinline__ void load_tile_raw(TileRaw<D, BS>& t, const DecodeArg
   }
 }
 
-// Element c (0 or 1 of word w) of four tokens' value words as fp16.
-__device__ __forceinline__ half4v raw_vop(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
-                                          bool hi, bool bf16) {
-  half4v o;
-  if (bf16) {
-    o[0] = (half_t)(hi ? bf16_hi(w0) : bf16_lo(w0));
-    o[1] = (half_t)(hi ? bf16_hi(w1) : bf16_lo(w1));
-    o[2] = (half_t)(hi ? bf16_hi(w2) : bf16_lo(w2));
-    o[3] = (half_t)(hi ? bf16_hi(w3) : bf16_lo(w3));
-  } else {
-    const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
-    const uint32_t x = __builtin_amdgcn_perm(w1, w0, sel), y = __builtin_amdgcn_perm(w3, w2, sel);
-    o = __builtin_bit_cast(half4v, (u32x2){x, y});
-  }
-  return o;
+// Element c (0 or 1 of word w) of four tokens' value words, as the four
+// 16-bit elements of a PV operand (fp16 or bf16 alike).
+__device__ __forceinline__ u32x2 raw_vop(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                         bool hi) {
+  const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+  return (u32x2){__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
 }
 
 template <int D, int BS, bool TAIL>
 __device__ __forceinline__ void tile_step_raw(const TileRaw<D, BS>& t, int nt, int pos0, int L,
-                                              const half8v* qop, float cscore, int j,
-                                              SoftmaxState<D>& st, bool bf16, int Lv = -1,
+                                              const half8v* qop, const half8v* qlo, float cscore,
+                                              int j, SoftmaxState<D>& st, bool bf16, int Lv = -1,
                                               int lo = 0, int sk = 0) {
   constexpr int NCH = D / 32;
   constexpr int NPV = D / 16;
   const int Ld = Lv < 0 ? L : Lv;   // as in tile_step
   float4v S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int c = 0; c < NCH; ++c)
-    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(raw8_to_h8(t.k[nt][c], bf16), qop[c], S, 0, 0, 0);
+  for (int c = 0; c < NCH; ++c) S = raw_scores(t.k[nt][c], qop[c], bf16 ? qlo[c] : qop[c], S, bf16);
   bool ok[4];   // as in tile_step
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -475,9 +487,19 @@ __device__ __forceinline__ void tile_step_raw(const TileRaw<D, BS>& t, int nt, i
 #pragma unroll
   for (int e = 0; e < 4; ++e) p[e] = (TAIL && !ok[e]) ? 0.0f : __builtin_amdgcn_exp2f(s[e] - msafe);
   st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  // weights: fp16 for fp16 rows, the bf16 pair hi + lo for bf16 rows
   half4v pop;
+  short4v phi, plo;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) pop[e] = (half_t)p[e];
+  for (int e = 0; e < 4; ++e) {
+    if (bf16) {
+      const __bf16 h = (__bf16)p[e];
+      phi[e] = __builtin_bit_cast(short, h);
+      plo[e] = __builtin_bit_cast(short, (__bf16)(p[e] - (float)h));
+    } else {
+      pop[e] = (half_t)p[e];
+    }
+  }
 #pragma unroll
   for (int c = 0; c < NPV; ++c) {
     uint32_t w[4];
@@ -486,8 +508,15 @@ __device__ __forceinline__ void tile_step_raw(const TileRaw<D, BS>& t, int nt, i
       w[i] = t.v[nt][i][c / 2];
       if (TAIL && pos0 + 4 * j + i >= Ld) w[i] = 0u;   // rows past the data may hold NaN
     }
-    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(raw_vop(w[0], w[1], w[2], w[3], c & 1, bf16),
-                                                      pop, st.acc[c], 0, 0, 0);
+    const u32x2 vw = raw_vop(w[0], w[1], w[2], w[3], c & 1);
+    if (bf16) {
+      const short4v vop = __builtin_bit_cast(short4v, vw);
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, phi, st.acc[c], 0, 0, 0);
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, plo, st.acc[c], 0, 0, 0);
+    } else {
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4v, vw), pop,
+                                                        st.acc[c], 0, 0, 0);
+    }
   }
 }
 

@@ -457,18 +457,27 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   qe = max(qe, -126);
   const float qdown = __uint_as_float((uint32_t)(127 - qe) << 23);  // 2^-qe
   const float qup = __uint_as_float((uint32_t)(127 + qe) << 23);    // 2^qe
-  // qs: the scaled query in fp32; qop: its fp16 operand (with per-channel
-  // keys it is only needed for the raw partial block, so it is made there)
+  // qs: the scaled query in fp32; qop: its fp16 operand, or for bf16 raw
+  // rows the bf16 pair qop + qlo (with per-channel keys it is only needed
+  // for the raw partial block, so it is made there)
 #pragma unroll
   for (int e = 0; e < D / 4; ++e) qf[e] = hcol ? qf[e] * qdown : 0.0f;
   const float* qs = qf;
-  half8v qop[NCH];
-  if constexpr (!KCH) {
+  constexpr bool RAW = CODE == KVQ_CODE_NONE16;
+  const bool raw_bf16 = a.stage_bf16 != 0;
+  half8v qop[NCH], qlo[NCH];
+  auto make_qop = [&](bool pair) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
+    for (int c = 0; c < NCH; ++c) {
+      if (pair) {
+        bf16_split8(qs + 8 * c, qop[c], qlo[c]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qop[c][e] = (half_t)qs[8 * c + e];
-  }
+        for (int e = 0; e < 8; ++e) qop[c][e] = (half_t)qs[8 * c + e];
+      }
+    }
+  };
+  if constexpr (!KCH) make_qop(RAW && raw_bf16);
   const float cscore = hcol ? qup * a.sm_log2 : 0.0f;
 
   // Block ids arrive 64 at a time with one vector load and reach the scalar
@@ -484,14 +493,13 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
     const bool ok = i <= ilast && id >= 0 && id < a.num_blocks;
     return (int64_t)(ok ? id : 0) * a.H + g;
   };
-  constexpr bool RAW = CODE == KVQ_CODE_NONE16;
   using TileT = typename std::conditional<RAW, TileRaw<D, BS>, Tile8<D, BS>>::type;
-  const bool raw_bf16 = a.stage_bf16 != 0;
   auto block = [&](const TileT& t, int i) {
     if constexpr (RAW) {
 #pragma unroll
       for (int nt = 0; nt < BS / 16; ++nt)
-        tile_step_raw<D, BS, false>(t, nt, i * BS + nt * 16, L, qop, cscore, j, st, raw_bf16);
+        tile_step_raw<D, BS, false>(t, nt, i * BS + nt * 16, L, qop, qlo, cscore, j, st,
+                                    raw_bf16);
     } else if constexpr (KCH) {
       half8v qb[NCH], ql[NCH];
       channel_query<D, BS>(t, lds, qs, lane, qb, ql);
@@ -545,17 +553,14 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
         for (int nt = 0; nt < BS / 16; ++nt) {
           const int pos0 = (i + u) * BS + nt * 16;
           if (pos0 + 16 <= L)
-            tile_step_raw<D, BS, false>(buf[u], nt, pos0, L, qop, cscore, j, st, raw_bf16);
+            tile_step_raw<D, BS, false>(buf[u], nt, pos0, L, qop, qlo, cscore, j, st, raw_bf16);
           else if (pos0 < L)
-            tile_step_raw<D, BS, true>(buf[u], nt, pos0, L, qop, cscore, j, st, raw_bf16);
+            tile_step_raw<D, BS, true>(buf[u], nt, pos0, L, qop, qlo, cscore, j, st, raw_bf16);
         }
       } else if constexpr (KCH) {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qop[c][e] = (half_t)qs[8 * c + e];
-        last_block_step<CODE, D, BS, true>(buf[u], i + u, L, qop, cscore, j, st, kraw,
-                                           a.stage_bf16 != 0);
+        make_qop(raw_bf16);
+        last_block_step<CODE, D, BS, true>(buf[u], i + u, L, qop, cscore, j, st, kraw, raw_bf16,
+                                           qlo);
       } else {
         last_block_step<CODE, D, BS>(buf[u], i + u, L, qop, cscore, j, st);
       }

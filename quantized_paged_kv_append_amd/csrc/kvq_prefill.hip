@@ -198,7 +198,9 @@ void prefill_split_kernel(PrefillArgs pa) {
 
   // ---- queries, each column pre-scaled by a power of two (as in decode) ---
   float qf[D / 4];      // the last column's fp32 query (per-channel keys: NC = 1)
-  half8v qop[NC][NCH];  // fp16 operands (made later with per-channel keys)
+  half8v qop[NC][NCH];  // fp16 operands (made later with per-channel keys), or
+  half8v qlo[NC][NCH];  // for bf16 raw rows the bf16 pairs qop + qlo
+  const bool raw_bf16 = a.stage_bf16 != 0;
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
     const int qi = valid[cc] ? col[cc] / a.G : 0;
@@ -225,13 +227,17 @@ void prefill_split_kernel(PrefillArgs pa) {
     for (int e = 0; e < D / 4; ++e) qf[e] = valid[cc] ? qf[e] * qdown : 0.0f;
     if constexpr (!KCH) {
 #pragma unroll
-      for (int k8 = 0; k8 < NCH; ++k8)
+      for (int k8 = 0; k8 < NCH; ++k8) {
+        if (RAW && raw_bf16) {
+          bf16_split8(qf + 8 * k8, qop[cc][k8], qlo[cc][k8]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qop[cc][k8][e] = (half_t)qf[8 * k8 + e];
+          for (int e = 0; e < 8; ++e) qop[cc][k8][e] = (half_t)qf[8 * k8 + e];
+        }
+      }
     }
     cscore[cc] = valid[cc] ? qup * a.sm_log2 : 0.0f;
   }
-  const bool raw_bf16 = a.stage_bf16 != 0;
 
   SoftmaxState<D> st[NC];
 #pragma unroll
@@ -274,8 +280,8 @@ void prefill_split_kernel(PrefillArgs pa) {
         if constexpr (RAW) {
 #pragma unroll
           for (int nt = 0; nt < BS / 16; ++nt)
-            tile_step_raw<D, BS, false>(t, nt, i * BS + nt * 16, L, qop[cc], cscore[cc], jj,
-                                        st[cc], raw_bf16);
+            tile_step_raw<D, BS, false>(t, nt, i * BS + nt * 16, L, qop[cc], qlo[cc],
+                                        cscore[cc], jj, st[cc], raw_bf16);
         } else if constexpr (KCH) {
           half8v qb[NCH], ql[NCH];
           channel_query<D, BS>(t, xs, qf, lane, qb, ql);
@@ -302,9 +308,14 @@ void prefill_split_kernel(PrefillArgs pa) {
               kraw[nt][k8] = *reinterpret_cast<const u32x4*>(sp + 8 * k8);
           }
 #pragma unroll
-          for (int k8 = 0; k8 < NCH; ++k8)
+          for (int k8 = 0; k8 < NCH; ++k8) {
+            if (raw_bf16) {
+              bf16_split8(qf + 8 * k8, qb[k8], ql[k8]);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qb[k8][e] = (half_t)qf[8 * k8 + e];
+              for (int e = 0; e < 8; ++e) qb[k8][e] = (half_t)qf[8 * k8 + e];
+            }
+          }
         }
       }
 #pragma unroll
@@ -319,20 +330,20 @@ void prefill_split_kernel(PrefillArgs pa) {
         for (int cc = 0; cc < NC; ++cc) {
           if constexpr (RAW) {
             if (masked)
-              tile_step_raw<D, BS, true>(t, nt, pos0, Lr[cc], qop[cc], cscore[cc], jj, st[cc],
-                                         raw_bf16, L, lo_r[cc], SK);
+              tile_step_raw<D, BS, true>(t, nt, pos0, Lr[cc], qop[cc], qlo[cc], cscore[cc], jj,
+                                         st[cc], raw_bf16, L, lo_r[cc], SK);
             else
-              tile_step_raw<D, BS, false>(t, nt, pos0, Lr[cc], qop[cc], cscore[cc], jj, st[cc],
-                                          raw_bf16, L);
+              tile_step_raw<D, BS, false>(t, nt, pos0, Lr[cc], qop[cc], qlo[cc], cscore[cc], jj,
+                                          st[cc], raw_bf16, L);
           } else if constexpr (KCH) {
-            if (rawk) {   // qb holds the plain fp16 query here
+            if (rawk) {   // qb holds the plain fp16 query here, or qb + ql the bf16 pair
               if (masked)
                 tile_step<CODE, D, BS, true, kKeyRaw>(t, nt, pos0, Lr[cc], qb, cscore[cc], jj,
-                                                      st[cc], kraw[nt], raw_bf16, nullptr, L,
+                                                      st[cc], kraw[nt], raw_bf16, ql, L,
                                                       lo_r[cc], SK);
               else
                 tile_step<CODE, D, BS, false, kKeyRaw>(t, nt, pos0, Lr[cc], qb, cscore[cc], jj,
-                                                       st[cc], kraw[nt], raw_bf16, nullptr, L);
+                                                       st[cc], kraw[nt], raw_bf16, ql, L);
             } else if (masked) {
               tile_step<CODE, D, BS, true, kKeyChannel>(t, nt, pos0, Lr[cc], qb, cscore[cc], jj,
                                                         st[cc], nullptr, false, ql, L, lo_r[cc],
