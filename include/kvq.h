@@ -343,7 +343,7 @@ kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const kvq_cach
                                         void* stream);
 
 /* Device workspace bytes kvq_prefill_attention needs for these sizes and this
- * split_blocks (>= 1, or 0 = the library's own choice), or a negative
+ * split_blocks (1..256, or 0 = the library's own choice), or a negative
  * kvq_status. */
 int64_t kvq_prefill_workspace_bytes(const kvq_layout* layout, int32_t batch,
                                     int32_t num_q_heads, int32_t max_query_len,
@@ -372,7 +372,7 @@ int64_t kvq_prefill_workspace_bytes(const kvq_layout* layout, int32_t batch,
  *                 ignored) is full causal attention. Positions no query
  *                 sees are never read, so their table entries may be -1
  *                 (kvq_blocks_trim).
- *  split_blocks   cache blocks per split-K chunk (>= 1); 0 lets the library
+ *  split_blocks   cache blocks per split-K chunk, 1..256; 0 lets the library
  *                 choose.
  *  out            device [Tq][num_q_heads][d] in out_dtype.
  * The other arguments are those of kvq_decode_attention; nq_b = 1 computes

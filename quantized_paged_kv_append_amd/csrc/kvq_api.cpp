@@ -431,7 +431,7 @@ int64_t kvq_prefill_workspace_bytes(const kvq_layout* L, int32_t batch, int32_t 
   kvq_status s = kvq_layout_check(L);
   if (s != KVQ_OK) return s;
   if (batch < 0 || num_q_heads < 1 || num_q_heads % L->num_kv_heads || max_query_len < 0 ||
-      max_context_len < max_query_len || split_blocks < 0)
+      max_context_len < max_query_len || split_blocks < 0 || split_blocks > kMaxSplitBlocks)
     return KVQ_ERR_INVALID_ARGUMENT;
   const PrefillShape sh = prefill_shape(L, batch, num_q_heads, max_query_len, max_context_len,
                                         split_blocks);
@@ -456,7 +456,7 @@ kvq_status kvq_prefill_attention(const kvq_layout* L, const kvq_cache* C, const 
   if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
     return KVQ_ERR_INVALID_ARGUMENT;
   if (max_query_len < 0 || max_context_len < max_query_len || split_blocks < 0 ||
-      max_blocks_per_seq < 1)
+      split_blocks > kMaxSplitBlocks || max_blocks_per_seq < 1)
     return KVQ_ERR_INVALID_ARGUMENT;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * L->block_size)
     return KVQ_ERR_INVALID_ARGUMENT;

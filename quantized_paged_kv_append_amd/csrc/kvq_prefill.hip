@@ -37,6 +37,7 @@ struct PrefillArgs {
   int32_t TW;   // column tiles per workgroup: 1, 2 or 4 (4 / TW waves per tile)
   int32_t window;   // > 0: each query sees its last `window` positions ...
   int32_t sink;     // ... and the first `sink` positions
+  int32_t bs_log2;  // log2 of the block size (the LDS-staged kernel)
 };
 
 // NC: 16-column tiles per wave. With NC = 2 a block's codes are loaded and
@@ -449,6 +450,392 @@ void prefill_split_kernel(PrefillArgs pa) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-query attention with the cache converted once per workgroup (8-bit
+// codes with per-token scales, no window). A workgroup takes one unit
+// (sequence b, split j, KV head g, column group) and streams the split in
+// chunks of kMqChunk tokens: its 256 threads load each chunk's key and value
+// codes once, 16 bytes per load, convert them to fp16 (exact for INT8 and
+// E4M3 codes) and store them with the per-token scales in one of two LDS
+// buffers; the waves then take their MFMA operands from LDS, so a block is
+// fetched and converted once for all the columns of the workgroup, not once
+// per wave. Wave w serves NCW column tiles (16 (query, head) columns each,
+// numbered as in prefill_split_kernel) and the (w / TW)-th of 4 / TW
+// interleaved shares of a chunk's 16-token tiles. The next two chunks are in
+// flight in registers while a chunk is computed. Rows past the split's last
+// visible position are stored as zeros, so every lane's mask needs only its
+// column's causal limit.
+// LDS rows hold D fp16 values and 8 halves of padding: the 16 lanes of a
+// 16-byte key read then start on 16 different 4-bank groups.
+// ---------------------------------------------------------------------------
+constexpr int kMqChunk = 64;      // tokens per LDS chunk
+constexpr int kMqMaxSplit = 256;  // blocks per split (the library's bound on split_blocks)
+
+template <int D>
+struct MqLds {
+  static constexpr int KSTR = D + 8;                      // halves per row
+  static constexpr int PLANE = kMqChunk * KSTR * 2;       // bytes: K or V of a chunk
+  static constexpr int BUF = 2 * PLANE + 2 * kMqChunk * 4;  // K, V, key and value scales
+  static constexpr int BYTES = 2 * BUF;                   // double buffer
+  static constexpr int IDS = BYTES;                       // then the split's block ids
+  static constexpr int TOTAL = IDS + kMqMaxSplit * 4;
+  static constexpr int RED = kNW * (D / 4 + 2) * kWave * 4;   // the waves' merge area
+  static_assert(RED <= BYTES, "the merge reuses the chunk buffers");
+};
+
+// One online-softmax step of a column tile over a wave's NT tiles of a
+// chunk: S[k] are the raw scores of tile k (token 4 jj + e of the tile in
+// element e), sk / sv the key / value scales of those tokens. One max over
+// the lane's 4 NT scores and at most one rescale per chunk, not per tile.
+// Writes the PV operands pop[k] = fp16(p sv). MASKED: token t counts for the
+// lane's column only if t < lim.
+template <int D, int NT, bool MASKED>
+__device__ __forceinline__ void mq_softmax(const float4v* S, const float4v* sk, const float4v* sv,
+                                           float cscore, int lim, const int* pos0, int jj,
+                                           SoftmaxState<D>& st, half4v* pop) {
+  constexpr int NPV = D / 16;
+  float s[NT][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NT; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[k][e] = S[k][e] * sk[k][e] * cscore;
+      if (MASKED && pos0[k] + 4 * jj + e >= lim) s[k][e] = -INFINITY;
+      mx = fmaxf(mx, s[k][e]);
+    }
+  const float mn = fmaxf(st.m, colmax4(mx));
+  const float msafe = mn == -INFINITY ? 0.0f : mn;
+  if (__any(mn > st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
+  }
+  st.m = mn;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[k][e] - msafe);   // masked: 0
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pop[k][e] = (half_t)(p[e] * sv[k][e]);
+  }
+  st.l += lsum;
+}
+
+// Multi-query kernel over LDS chunks. TW: column-tile groups per workgroup
+// (and tiles per wave per chunk: wave w takes tiles w / TW + k (4 / TW),
+// k < TW, one softmax step per two of them); NCW: column tiles per wave.
+template <int CODE, int D, int NCW, int TW>
+__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
+void mq_split_kernel(PrefillArgs pa) {
+  constexpr int NCH = D / 32;
+  constexpr int NPV = D / 16;
+  constexpr int NV = D / 4;
+  constexpr int CH = kMqChunk;
+  constexpr int NTC = CH / 16;        // 16-token tiles per chunk
+  constexpr int NSH = NTC / TW;       // waves sharing a column tile group (tile stride)
+  constexpr int SG = TW < 2 ? TW : 2; // tiles per softmax step
+  constexpr int PPT = D / 64;         // 16-byte code pieces per thread per plane and chunk
+  constexpr int KSTR = MqLds<D>::KSTR;
+  constexpr int DL = D == 128 ? 7 : 6;  // log2 D
+  constexpr int NPF = 2;              // chunks in flight in registers (the tail assumes 2)
+  static_assert(NTC == kNW && CH * D / 16 == PPT * 64 * kNW, "chunk shape");
+  __shared__ __align__(16) unsigned char smem[MqLds<D>::TOTAL];
+  const DecodeArgs& a = pa.a;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r = lane & 15, jj = lane >> 4;
+  const int bsl = pa.bs_log2, BS = 1 << bsl;   // block size 16 or 32
+
+  // ---- unit: workgroup x runs on XCD x % 8; the column groups of one
+  // (b, j, g) are consecutive there, so they share that XCD's L2 ----------
+  const int cts = (pa.CT + NCW - 1) / NCW;
+  const int CG = (cts + TW - 1) / TW;
+  const int64_t x = blockIdx.x;
+  const int64_t k8 = x >> 3;
+  const int cg = (int)(k8 % CG);
+  int64_t item = (k8 / CG) * 8 + (x & 7);
+  const int g = (int)(item % a.H);
+  item /= a.H;
+  const int j = (int)(item % pa.J);
+  const int b = (int)(item / pa.J);
+  if (b >= a.batch) return;
+  const int L = min(a.context_lens[b], a.max_len);
+  const int q0 = pa.qstart[b];
+  const int nq = min(min(pa.qstart[b + 1] - q0, L), pa.max_q);
+  const int ncol = nq * a.G;
+  const int nblk = (L + BS - 1) >> bsl;
+  const int s0 = j * pa.S;
+  const int cw0 = cg * TW * NCW * 16;   // the workgroup's first column
+  if (s0 >= nblk || cw0 >= ncol) return;   // workgroup-uniform
+  const int sh = wave / TW;
+  const int cbase = cw0 + (wave % TW) * NCW * 16;   // the wave's first column
+  const bool active = cbase < ncol;
+  // tokens [t0, t1) of the split that some column of the workgroup sees
+  const int Lmax = L - nq + (min(ncol, cw0 + TW * NCW * 16) - 1) / a.G + 1;
+  const int s1 = min(min(s0 + pa.S, nblk), (Lmax + BS - 1) >> bsl);
+  const int t0 = s0 << bsl, t1 = max(min(s1 << bsl, Lmax), t0);
+  // the wave's least limit (its first column's)
+  const int lim_lo = min(L - nq + cbase / a.G + 1, t1);
+
+  // ---- columns: lane (r, jj) serves columns cbase + 16 cc + r ---------------
+  int col[NCW], lim[NCW];
+  bool valid[NCW];
+  float cscore[NCW];
+  half8v qop[NCW][NCH];
+#pragma unroll
+  for (int cc = 0; cc < NCW; ++cc) {
+    col[cc] = cbase + 16 * cc + r;
+    valid[cc] = col[cc] < ncol;
+    lim[cc] = valid[cc] ? min(L - nq + col[cc] / a.G + 1, t1) : 0;
+    const int qi = valid[cc] ? col[cc] / a.G : 0;
+    const int hq = g * a.G + (valid[cc] ? col[cc] % a.G : 0);
+    const uint16_t* qp = a.q + ((int64_t)(q0 + qi) * a.Hq + hq) * D + jj * (D / 4);
+    float qf[D / 4];
+    if (a.q_bf16)
+      load_query<true, D>(qp, qf);
+    else
+      load_query<false, D>(qp, qf);
+    float qmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) qmax = fmaxf(qmax, fabsf(qf[e]));
+    qmax = colmax4(qmax);
+    int qe = qmax > 0.0f ? (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 : 0;
+    qe = max(qe, -126);
+    const float qdown = __uint_as_float((uint32_t)(127 - qe) << 23);
+    const float qup = __uint_as_float((uint32_t)(127 + qe) << 23);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qop[cc][c][e] = (half_t)(valid[cc] ? qf[8 * c + e] * qdown : 0.0f);
+    cscore[cc] = valid[cc] ? qup * a.sm_log2 : 0.0f;
+  }
+  SoftmaxState<D> st[NCW];
+#pragma unroll
+  for (int cc = 0; cc < NCW; ++cc) {
+    st[cc].m = -INFINITY;
+    st[cc].l = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NPV; ++k) st[cc].acc[k] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // ---- the split's block ids go to LDS first: a chunk's code loads then
+  // wait on no other vector load (those complete in order, so waiting on an
+  // id just loaded would also wait on the chunks already in flight). Ids
+  // outside the pool (a broken precondition) are read as block 0. --------
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + MqLds<D>::IDS);
+  {
+    const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
+    for (int i = tid; i < s1 - s0; i += kWave * kNW) {
+      const int32_t id = trow[s0 + i];
+      ids[i] = id >= 0 && id < a.num_blocks ? id : 0;
+    }
+    __syncthreads();
+  }
+  // ---- chunk loads: piece p of thread tid is code bytes [d0, d0 + 16) of
+  // token T of the chunk; threads 0..63 / 64..127 also load the key / value
+  // scale of token tid % 64 (threads 128.. load a key scale they do not
+  // store, so that every chunk is the same number of loads for the wait
+  // counts). Positions past t1 read a row of the split's last visible token
+  // (cached) and are stored as zeros. A wave's pieces p cover 8 (d 128) or
+  // 16 (d 64) consecutive positions of one block -- also when clamped to
+  // t1 - 1 -- so their block id and row base are wave-uniform. -----------
+  struct Regs {
+    u32x4 k[PPT], v[PPT];
+    float s;
+  };
+  auto load_chunk = [&](Regs& R, int c) {
+    const int tc = t0 + c * CH;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      const int q = tid + kWave * kNW * p;
+      const int T = q / (D / 16), d0 = (q % (D / 16)) * 16;
+      const int tok = min(tc + T, t1 - 1);
+      const int blk = __builtin_amdgcn_readfirstlane(tok >> bsl);
+      const int id = __builtin_amdgcn_readfirstlane(ids[blk - s0]);
+      const int64_t base = ((int64_t)id * a.H + g) << (bsl + DL);
+      const uint32_t off = ((uint32_t)(tok & (BS - 1)) << DL) + d0;
+      R.k[p] = *reinterpret_cast<const u32x4*>(a.k_codes + base + off);
+      R.v[p] = load_codes<true>(reinterpret_cast<const u32x4*>(a.v_codes + base + off));
+    }
+    const int tok = min(tc + (tid & (CH - 1)), t1 - 1);
+    const int64_t row = ((int64_t)ids[(tok >> bsl) - s0] * a.H + g) * BS + (tok & (BS - 1));
+    R.s = ((tid & CH) ? a.v_scale : a.k_scale)[row];
+  };
+  auto store_chunk = [&](const Regs& R, int c, unsigned char* buf) {
+    const int tc = t0 + c * CH;
+    const bool whole = tc + CH <= t1;   // no position past t1 in the chunk
+    half_t* K = reinterpret_cast<half_t*>(buf);
+    half_t* V = reinterpret_cast<half_t*>(buf + MqLds<D>::PLANE);
+    float* SC = reinterpret_cast<float*>(buf + 2 * MqLds<D>::PLANE);   // [2][CH]
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      const int q = tid + kWave * kNW * p;
+      const int T = q / (D / 16), d0 = (q % (D / 16)) * 16;
+      half8v k0 = codes8_to_h8<CODE>(R.k[p].x, R.k[p].y);
+      half8v k1 = codes8_to_h8<CODE>(R.k[p].z, R.k[p].w);
+      half8v v0 = codes8_to_h8<CODE>(R.v[p].x, R.v[p].y);
+      half8v v1 = codes8_to_h8<CODE>(R.v[p].z, R.v[p].w);
+      if (!whole && tc + T >= t1) {
+        const half8v z = {};
+        k0 = z; k1 = z; v0 = z; v1 = z;
+      }
+      *reinterpret_cast<half8v*>(K + T * KSTR + d0) = k0;
+      *reinterpret_cast<half8v*>(K + T * KSTR + d0 + 8) = k1;
+      *reinterpret_cast<half8v*>(V + T * KSTR + d0) = v0;
+      *reinterpret_cast<half8v*>(V + T * KSTR + d0 + 8) = v1;
+    }
+    if (tid < 2 * CH) SC[tid] = whole || tc + (tid & (CH - 1)) < t1 ? R.s : 0.0f;
+  };
+  // a wave's TW tiles of chunk c, in groups of SG: scores of the group, one
+  // softmax step per column tile, then PV tile by tile
+  auto compute_chunk = [&](int c, const unsigned char* buf) {
+    const int tc = t0 + c * CH;
+    if (tc + sh * 16 >= t1) return;   // none of the wave's tiles has a visible position
+    const half_t* K = reinterpret_cast<const half_t*>(buf);
+    const half_t* V = reinterpret_cast<const half_t*>(buf + MqLds<D>::PLANE);
+    const float* SK = reinterpret_cast<const float*>(buf + 2 * MqLds<D>::PLANE);
+    const float* SV = SK + CH;
+#pragma unroll
+    for (int k0 = 0; k0 < TW; k0 += SG) {
+      int pos0[SG];
+      float4v S[NCW][SG], sk[SG], sv[SG];
+#pragma unroll
+      for (int k = 0; k < SG; ++k) {
+        const int nt = sh + (k0 + k) * NSH;
+        pos0[k] = tc + nt * 16;
+        half8v kop[NCH];
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+          kop[ch] =
+              *reinterpret_cast<const half8v*>(K + (nt * 16 + r) * KSTR + jj * (D / 4) + 8 * ch);
+        sk[k] = *reinterpret_cast<const float4v*>(SK + nt * 16 + 4 * jj);
+        sv[k] = *reinterpret_cast<const float4v*>(SV + nt * 16 + 4 * jj);
+#pragma unroll
+        for (int cc = 0; cc < NCW; ++cc) {
+          float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ch], qop[cc][ch], acc, 0, 0, 0);
+          S[cc][k] = acc;
+        }
+      }
+      half4v pop[NCW][SG];
+      if (pos0[SG - 1] + 16 > lim_lo) {
+#pragma unroll
+        for (int cc = 0; cc < NCW; ++cc)
+          mq_softmax<D, SG, true>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < NCW; ++cc)
+          mq_softmax<D, SG, false>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
+      }
+#pragma unroll
+      for (int k = 0; k < SG; ++k) {
+        const int nt = sh + (k0 + k) * NSH;
+        uint32_t vw[4][D / 32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half_t* vr = V + (nt * 16 + 4 * jj + i) * KSTR + r * (D / 16);
+          if constexpr (D == 128) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(vr);
+            vw[i][0] = w.x; vw[i][1] = w.y; vw[i][2] = w.z; vw[i][3] = w.w;
+          } else {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(vr);
+            vw[i][0] = w.x; vw[i][1] = w.y;
+          }
+        }
+#pragma unroll
+        for (int cc = 0; cc < NCW; ++cc)
+#pragma unroll
+          for (int e = 0; e < NPV; ++e) {
+            const u32x2 v = raw_vop(vw[0][e / 2], vw[1][e / 2], vw[2][e / 2], vw[3][e / 2], e & 1);
+            st[cc].acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(half4v, v), pop[cc][k], st[cc].acc[e], 0, 0, 0);
+          }
+      }
+    }
+  };
+
+  // ---- the chunk loop: store chunk c, start loading chunk c + NPF into the
+  // registers it freed, then compute chunk c. One barrier per chunk: a wave
+  // stores chunk c + 1 into the buffer of chunk c - 1 only after every wave
+  // has passed chunk c's barrier, i.e. has finished computing chunk c - 1.
+  // Every step issues the same loads (chunks past the last one read its
+  // rows again, clamped, and are never stored), so that the wait before a
+  // store covers that chunk's loads only, not the ones in flight behind it.
+  const int nch = (t1 - t0 + CH - 1) / CH;
+  if (nch > 0) {
+    Regs R[NPF];
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) load_chunk(R[u], u);
+    auto step = [&](Regs& Ru, int c, unsigned char* buf) {
+      store_chunk(Ru, c, buf);
+      load_chunk(Ru, c + NPF);
+      __syncthreads();
+      if (active) compute_chunk(c, buf);
+    };
+    int c0 = 0;
+    for (; c0 + NPF <= nch; c0 += NPF) {
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) step(R[u], c0 + u, smem + u * MqLds<D>::BUF);
+    }
+    if (c0 < nch) step(R[0], c0, smem);   // at most one chunk left
+  }
+
+  // ---- merge the waves' states, then write one partial per column ---------
+  float (*red)[NV + 2][kWave] = reinterpret_cast<float (*)[NV + 2][kWave]>(smem);
+#pragma unroll
+  for (int cc = 0; cc < NCW; ++cc) {
+    const float lsum = colsum4(st[cc].l);
+    __syncthreads();   // every wave is done with the LDS area
+#pragma unroll
+    for (int k = 0; k < NPV; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][4 * k + e][lane] = st[cc].acc[k][e];
+    red[wave][NV][lane] = st[cc].m;
+    red[wave][NV + 1][lane] = lsum;
+    __syncthreads();
+    // waves w < TW merge the shares of their columns: waves w, w + TW, ...
+    if (wave < TW && valid[cc]) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = wave; w < kNW; w += TW) M = fmaxf(M, red[w][NV][lane]);
+      float acc[NV], l = 0.0f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
+#pragma unroll
+      for (int w = wave; w < kNW; w += TW) {
+        const float mw = red[w][NV][lane];
+        const float sc = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        l += sc * red[w][NV + 1][lane];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] += sc * red[w][v][lane];
+      }
+      const int64_t pidx = (((int64_t)b * pa.J + j) * a.H + g) * (pa.CT * 16) + col[cc];
+      if (jj == 0) *reinterpret_cast<float2*>(a.ws_ml + pidx * 2) = make_float2(M, l);
+      // acc[4 k + e] holds output element (d/16) (4 jj + e) + k of the column
+      float* dst = a.ws_acc + pidx * D + jj * (D / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (NPV == 8) {
+          float4v lo = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
+          float4v hi = {acc[16 + e], acc[20 + e], acc[24 + e], acc[28 + e]};
+          *reinterpret_cast<float4v*>(dst + 8 * e) = lo;
+          *reinterpret_cast<float4v*>(dst + 8 * e + 4) = hi;
+        } else {
+          float4v v4 = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
+          *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
+        }
+      }
+    }
+  }
+}
+
 // Cross-split merge for multi-query attention, as decode_reduce: one wave
 // per (query head, query i, sequence b), one or kReduceHeads heads per
 // workgroup;
@@ -569,6 +956,33 @@ hipError_t launch_prefill_shape(PrefillArgs pa, int d, int bs, int64_t units_per
   }
 }
 
+// The LDS-staged kernel: two column tiles per wave where there are two, and
+// 1, 2 or 4 waves' column tiles per workgroup (the other waves of a column
+// tile group share its token tiles). Grid: 8 x (column groups) x
+// ceil(units / 8), so that the column groups of a unit meet on one XCD.
+template <int CODE, int NCW, int TW>
+hipError_t launch_mq_shape(const PrefillArgs& pa, int d, hipStream_t stream) {
+  const int64_t cts = (pa.CT + NCW - 1) / NCW;
+  const int64_t cgs = (cts + TW - 1) / TW;
+  const int64_t items = (int64_t)pa.a.batch * pa.J * pa.a.H;
+  const dim3 grid((unsigned)(8 * cgs * ((items + 7) / 8)));
+  if (d == 128)
+    mq_split_kernel<CODE, 128, NCW, TW><<<grid, 64 * kNW, 0, stream>>>(pa);
+  else
+    mq_split_kernel<CODE, 64, NCW, TW><<<grid, 64 * kNW, 0, stream>>>(pa);
+  return hipGetLastError();
+}
+
+template <int CODE>
+hipError_t launch_mq(PrefillArgs pa, int d, int bs, hipStream_t stream) {
+  pa.bs_log2 = bs == 32 ? 5 : 4;
+  if (pa.CT < 2) return launch_mq_shape<CODE, 1, 1>(pa, d, stream);
+  const int cts = (pa.CT + 1) / 2;
+  if (cts >= 4) return launch_mq_shape<CODE, 2, 4>(pa, d, stream);
+  if (cts >= 2) return launch_mq_shape<CODE, 2, 2>(pa, d, stream);
+  return launch_mq_shape<CODE, 2, 1>(pa, d, stream);
+}
+
 }  // namespace
 
 bool prefill_supported(int32_t k_code, int32_t v_code, int32_t k_mode, int32_t v_mode) {
@@ -620,7 +1034,13 @@ hipError_t launch_prefill(const PrefillPlan& pp, hipStream_t stream) {
   const int64_t units = (int64_t)p.batch * pp.splits * p.num_kv_heads;
   const int d = p.head_dim, bs = p.block_size;
   hipError_t e;
-  if (p.k_code == KVQ_CODE_NONE16)
+  const bool tok8 = p.k_mode == KVQ_SCALE_TOKEN_SYM &&
+                    (p.k_code == KVQ_CODE_INT8 || p.k_code == KVQ_CODE_FP8_E4M3);
+  if (tok8 && pp.window == 0 && p.k_code == KVQ_CODE_FP8_E4M3)
+    e = launch_mq<KVQ_CODE_FP8_E4M3>(pa, d, bs, stream);
+  else if (tok8 && pp.window == 0)
+    e = launch_mq<KVQ_CODE_INT8>(pa, d, bs, stream);
+  else if (p.k_code == KVQ_CODE_NONE16)
     e = launch_prefill_shape<KVQ_CODE_NONE16, KVQ_SCALE_TOKEN_SYM>(pa, d, bs, units, stream);
   else if (p.k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM)
     e = launch_prefill_shape<KVQ_CODE_INT8, KVQ_SCALE_CHANNEL_BLOCK_SYM>(pa, d, bs, units, stream);

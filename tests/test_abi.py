@@ -243,6 +243,9 @@ def test_prefill_rejects_bad_arguments_on_host():
     assert pre(maxq=65) == kq.KVQ_ERR_INVALID_ARGUMENT          # more queries than context
     assert pre(maxlen=65) == kq.KVQ_ERR_INVALID_ARGUMENT        # > maxb * bs
     assert pre(split=-1) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert pre(split=257) == kq.KVQ_ERR_INVALID_ARGUMENT        # a split's ids fit in LDS
+    with pytest.raises(kq.KvqError):
+        kq.kvq_prefill_workspace_bytes(L, 2, 32, 8, 4096, 257)
     assert pre(qs=None) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert pre(q=C.c_void_p((1 << 21) + 2)) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert pre(wsb=16) == kq.KVQ_ERR_WORKSPACE_TOO_SMALL
