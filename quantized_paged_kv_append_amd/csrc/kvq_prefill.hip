@@ -485,40 +485,49 @@ struct MqLds {
 
 // One online-softmax step of a column tile over a wave's NT tiles of a
 // chunk: S[k] are the raw scores of tile k (token 4 jj + e of the tile in
-// element e), sk / sv the key / value scales of those tokens. One max over
-// the lane's 4 NT scores and at most one rescale per chunk, not per tile.
-// Writes the PV operands pop[k] = fp16(p sv). MASKED: token t counts for the
-// lane's column only if t < lim.
+// element e), sk / sv the key / value scales of those tokens, cscore > 0 the
+// column's score factor, so the largest scaled score is cscore times the
+// largest S sk. The reference st.m moves only when a score exceeds it, and
+// then to that score plus kMqHeadroom (log2 units): weights stay below
+// 2^-kMqHeadroom and the smaller increases that follow cost no rescale of
+// the accumulators (with 16 columns to a tile one of them reaches a new
+// maximum in almost every chunk). The merges need a common reference for l
+// and acc, not the maximum itself. Writes the PV operands pop[k] =
+// fp16(p sv). MASKED: token t counts for the lane's column only if t < lim.
+constexpr float kMqHeadroom = 2.0f;
+
 template <int D, int NT, bool MASKED>
 __device__ __forceinline__ void mq_softmax(const float4v* S, const float4v* sk, const float4v* sv,
                                            float cscore, int lim, const int* pos0, int jj,
                                            SoftmaxState<D>& st, half4v* pop) {
   constexpr int NPV = D / 16;
-  float s[NT][4];
+  float u[NT][4];
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NT; ++k)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      s[k][e] = S[k][e] * sk[k][e] * cscore;
-      if (MASKED && pos0[k] + 4 * jj + e >= lim) s[k][e] = -INFINITY;
-      mx = fmaxf(mx, s[k][e]);
+      u[k][e] = S[k][e] * sk[k][e];
+      if (MASKED && pos0[k] + 4 * jj + e >= lim) u[k][e] = -INFINITY;
+      mx = fmaxf(mx, u[k][e]);
     }
-  const float mn = fmaxf(st.m, colmax4(mx));
-  const float msafe = mn == -INFINITY ? 0.0f : mn;
-  if (__any(mn > st.m)) {
-    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+  const float mt = colmax4(mx) * cscore;
+  if (__any(mt > st.m)) {
+    const float mn = mt > st.m ? mt + kMqHeadroom : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);   // 1 where st.m stays
     st.l *= alpha;
 #pragma unroll
     for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
+    st.m = mn;
   }
-  st.m = mn;
+  const float msafe = st.m == -INFINITY ? 0.0f : st.m;
   float lsum = 0.0f;
 #pragma unroll
   for (int k = 0; k < NT; ++k) {
     float p[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[k][e] - msafe);   // masked: 0
+    for (int e = 0; e < 4; ++e)   // masked: exp2(-inf) = 0
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(u[k][e], cscore, -msafe));
     lsum += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) pop[k][e] = (half_t)(p[e] * sv[k][e]);
@@ -612,7 +621,9 @@ void mq_split_kernel(PrefillArgs pa) {
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qop[cc][c][e] = (half_t)(valid[cc] ? qf[8 * c + e] * qdown : 0.0f);
-    cscore[cc] = valid[cc] ? qup * a.sm_log2 : 0.0f;
+    // positive in every lane (mq_softmax takes the maximum through it);
+    // columns past the last have zero queries and are never written
+    cscore[cc] = valid[cc] ? qup * a.sm_log2 : 1.0f;
   }
   SoftmaxState<D> st[NCW];
 #pragma unroll
@@ -734,29 +745,49 @@ void mq_split_kernel(PrefillArgs pa) {
         for (int cc = 0; cc < NCW; ++cc)
           mq_softmax<D, SG, false>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
       }
+      // value words: lane (r, jj) reads elements [r d/16, (r+1) d/16) of
+      // tokens 4 jj + i of each tile of the group
+      uint32_t vw[SG][4][D / 32];
 #pragma unroll
       for (int k = 0; k < SG; ++k) {
         const int nt = sh + (k0 + k) * NSH;
-        uint32_t vw[4][D / 32];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const half_t* vr = V + (nt * 16 + 4 * jj + i) * KSTR + r * (D / 16);
           if constexpr (D == 128) {
             const u32x4 w = *reinterpret_cast<const u32x4*>(vr);
-            vw[i][0] = w.x; vw[i][1] = w.y; vw[i][2] = w.z; vw[i][3] = w.w;
+            vw[k][i][0] = w.x; vw[k][i][1] = w.y; vw[k][i][2] = w.z; vw[k][i][3] = w.w;
           } else {
             const u32x2 w = *reinterpret_cast<const u32x2*>(vr);
-            vw[i][0] = w.x; vw[i][1] = w.y;
+            vw[k][i][0] = w.x; vw[k][i][1] = w.y;
           }
         }
+      }
+      // PV MFMA e: output element r d/16 + e of every column. One tile: 16
+      // tokens (16x16x16). Two tiles: 32 tokens (16x16x32), contraction index
+      // 8 jj + i taking token 4 jj + i of the first tile for i < 4 and token
+      // 4 jj + i - 4 of the second for i >= 4 -- the order in which the lane
+      // already holds both the weights and the value words.
 #pragma unroll
-        for (int cc = 0; cc < NCW; ++cc)
+      for (int e = 0; e < NPV; ++e) {
+        const u32x2 v0 = raw_vop(vw[0][0][e / 2], vw[0][1][e / 2], vw[0][2][e / 2], vw[0][3][e / 2],
+                                 e & 1);
+        if constexpr (SG == 2) {
+          const u32x2 v1 = raw_vop(vw[1][0][e / 2], vw[1][1][e / 2], vw[1][2][e / 2],
+                                   vw[1][3][e / 2], e & 1);
+          const half8v va = __builtin_bit_cast(half8v, (u32x4){v0.x, v0.y, v1.x, v1.y});
 #pragma unroll
-          for (int e = 0; e < NPV; ++e) {
-            const u32x2 v = raw_vop(vw[0][e / 2], vw[1][e / 2], vw[2][e / 2], vw[3][e / 2], e & 1);
-            st[cc].acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                __builtin_bit_cast(half4v, v), pop[cc][k], st[cc].acc[e], 0, 0, 0);
+          for (int cc = 0; cc < NCW; ++cc) {
+            const half8v pb = __builtin_shufflevector(pop[cc][0], pop[cc][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            st[cc].acc[e] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st[cc].acc[e], 0, 0, 0);
           }
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < NCW; ++cc)
+            st[cc].acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(half4v, v0), pop[cc][0], st[cc].acc[e], 0, 0, 0);
+        }
       }
     }
   };
