@@ -402,23 +402,45 @@ kvq_status kvq_decode_attention_noalloc(const kvq_layout* L, const kvq_cache* C,
 
 namespace {
 
-// Multi-query splits: S blocks per split (the caller's, else a sixteenth of
-// the longest context within [32, 64]: four waves share a split, and longer
-// splits leave skewed batches waiting on their longest sequences), J =
-// splits of the longest context, CT = 16-column tiles of max_query_len
-// queries times G heads.
+// Multi-query splits: S blocks per split, J = splits of the longest context,
+// CT = 16-column tiles of max_query_len queries times G heads. S is the
+// caller's, else:
+//  - 8-bit codes with per-token scales (the LDS-staged kernel, whose
+//    workgroups each pay a fixed start -- block ids, first loads, queries --
+//    and a fixed merge): the launch's block visits, counted at the longest
+//    context (sequences x KV heads x groups of up to eight column tiles x
+//    blocks), over kPrefillUnits workgroups -- two rounds of two per CU --
+//    within [32, 256] blocks;
+//  - other layouts (register-streaming kernel): a sixteenth of the longest
+//    context within [32, 64], short enough that a batch of mostly short
+//    sequences still fills the GPU.
+constexpr int64_t kPrefillUnits = 1024;
+
 struct PrefillShape {
   int64_t S, J, CT, partials;
 };
+
+bool prefill_staged(const kvq_layout* L) {
+  return L->k_mode == KVQ_SCALE_TOKEN_SYM && L->v_mode == KVQ_SCALE_TOKEN_SYM &&
+         L->k_code == L->v_code &&
+         (L->k_code == KVQ_CODE_INT8 || L->k_code == KVQ_CODE_FP8_E4M3);
+}
 
 PrefillShape prefill_shape(const kvq_layout* L, int64_t batch, int64_t num_q_heads,
                            int64_t max_query_len, int64_t max_context_len, int64_t split_blocks) {
   PrefillShape sh;
   const int64_t maxblk = std::max<int64_t>(1, ceil_div(max_context_len, L->block_size));
-  sh.S = split_blocks > 0 ? split_blocks
-                         : std::min<int64_t>(64, std::max<int64_t>(32, ceil_div(maxblk, 16)));
-  sh.J = ceil_div(maxblk, sh.S);
   sh.CT = ceil_div(max_query_len * (num_q_heads / L->num_kv_heads), 16);
+  if (split_blocks > 0) {
+    sh.S = split_blocks;
+  } else if (prefill_staged(L)) {
+    const int64_t visits = batch * L->num_kv_heads * ceil_div(sh.CT, 8) * maxblk;
+    sh.S = std::min<int64_t>(kMaxSplitBlocks,
+                             std::max<int64_t>(32, ceil_div(visits, kPrefillUnits)));
+  } else {
+    sh.S = std::min<int64_t>(64, std::max<int64_t>(32, ceil_div(maxblk, 16)));
+  }
+  sh.J = ceil_div(maxblk, sh.S);
   sh.partials = batch * sh.J * L->num_kv_heads * sh.CT * 16;
   return sh;
 }

@@ -911,10 +911,13 @@ __global__ __launch_bounds__(64 * kReduceHeads) void prefill_reduce_kernel(Prefi
     const int cnt = min(KB, ns - s0);
     float2 ml = {-INFINITY, 0.0f};
     if (lane < cnt) ml = *reinterpret_cast<const float2*>(a.ws_ml + (base + (s0 + lane) * stride) * 2);
+    // a partial with m = -inf is empty (no position of the split seen): its
+    // accumulator is not read
+    const uint64_t full = __ballot(ml.x != -INFINITY);   // lanes past cnt hold -inf
     floatE v[KB];
 #pragma unroll
     for (int uu = 0; uu < KB; ++uu)
-      if (uu < cnt)
+      if ((full >> uu) & 1)
         v[uu] = *reinterpret_cast<const floatE*>(a.ws_acc + (base + (s0 + uu) * stride) * D + EPL * lane);
     const float mb = wave_reduce_f<true>(ml.x);
     const float Mn = fmaxf(M, mb);
@@ -926,7 +929,7 @@ __global__ __launch_bounds__(64 * kReduceHeads) void prefill_reduce_kernel(Prefi
     den += w * ml.y;
 #pragma unroll
     for (int uu = 0; uu < KB; ++uu)
-      if (uu < cnt) {
+      if ((full >> uu) & 1) {
         const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), uu));
         o += wu * v[uu];
       }

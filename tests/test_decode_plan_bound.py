@@ -96,12 +96,21 @@ def test_prefill_partial_index_stays_in_the_workspace():
     reach past the workspace. The rule is replayed here; the kernels' own
     expression is checked for the same cut."""
     src = (ROOT / "quantized_paged_kv_append_amd" / "csrc" / "kvq_prefill.hip").read_text()
-    assert src.count("min(min(pa.qstart[b + 1] - q0, L), pa.max_q)") == 1
+    # both split kernels (register-streaming and LDS-staged) cut the count
+    assert src.count("min(min(pa.qstart[b + 1] - q0, L), pa.max_q)") == 2
     assert src.count("min(min(a.qstart[b + 1] - q0, L), a.max_q)") == 1
     rng = np.random.default_rng(7)
-    for H, Hq, d, bs in ((8, 64, 128, 16), (2, 4, 64, 32), (8, 32, 128, 16)):
+    for H, Hq, d, bs, code, mode in ((8, 64, 128, 16, "int8", "token_sym"),
+                                     (2, 4, 64, 32, "fp8", "token_sym"),
+                                     (8, 32, 128, 16, "int8", "token_sym"),
+                                     (8, 64, 128, 32, "int4", "group_asym"),
+                                     (2, 16, 64, 16, "int8", "channel_block")):
         G = Hq // H
-        L = kq.make_layout(H, d, bs, "int8", src_dtype=torch.bfloat16)
+        staged = mode == "token_sym" and code in ("int8", "fp8")
+        L = kq.make_layout(H, d, bs, code, k_mode=mode,
+                           v_mode="token_sym" if mode == "channel_block" else mode,
+                           group_size=32 if mode == "group_asym" else 0,
+                           src_dtype=torch.bfloat16)
         for _ in range(200):
             B = int(rng.integers(1, 9))
             max_q = int(rng.integers(1, 40))
@@ -110,9 +119,13 @@ def test_prefill_partial_index_stays_in_the_workspace():
             # query counts up to 3x the bound: the clamp must hold them
             nq_raw = rng.integers(0, 3 * max_q + 1, B)
             total = kq.kvq_prefill_workspace_bytes(L, B, Hq, max_q, max_len)
-            S = min(64, max(32, -(-max(1, -(-max_len // bs)) // 16)))
-            J = -(-max(1, -(-max_len // bs)) // S)
+            maxblk = max(1, -(-max_len // bs))
             CT = -(-max_q * G // 16)
+            if staged:   # 8-bit per-token codes: split length from the block visits
+                S = min(256, max(32, -(-B * H * -(-CT // 8) * maxblk // 1024)))
+            else:
+                S = min(64, max(32, -(-maxblk // 16)))
+            J = -(-maxblk // S)
             partials = B * J * H * CT * 16
             need = -(-partials * d * 4 // 256) * 256 + -(-partials * 8 // 256) * 256
             assert need <= total
