@@ -410,7 +410,12 @@ namespace {
 //    and a fixed merge): the launch's block visits, counted at the longest
 //    context (sequences x KV heads x groups of up to eight column tiles x
 //    blocks), over kPrefillUnits workgroups -- two rounds of two per CU --
-//    within [32, 256] blocks;
+//    within [32, kPrefillMaxSplitBlocks] blocks (fewer, longer splits also
+//    mean fewer partials written and merged). Batches of 32 sequences or
+//    more take twice the workgroups: their lengths usually spread below the
+//    longest, so its visits overstate the work, and shorter splits balance
+//    the unequal sequences (a heuristic: the lengths stay on the device).
+//    S is a multiple of 32 blocks;
 //  - other layouts (register-streaming kernel): a sixteenth of the longest
 //    context within [32, 64], short enough that a batch of mostly short
 //    sequences still fills the GPU.
@@ -435,8 +440,10 @@ PrefillShape prefill_shape(const kvq_layout* L, int64_t batch, int64_t num_q_hea
     sh.S = split_blocks;
   } else if (prefill_staged(L)) {
     const int64_t visits = batch * L->num_kv_heads * ceil_div(sh.CT, 8) * maxblk;
-    sh.S = std::min<int64_t>(kMaxSplitBlocks,
-                             std::max<int64_t>(32, ceil_div(visits, kPrefillUnits)));
+    // rounded down to 32 blocks: a split is whole 64-token chunks
+    const int64_t units = batch >= 32 ? 2 * kPrefillUnits : kPrefillUnits;
+    sh.S = std::min<int64_t>(kvq::kPrefillMaxSplitBlocks,
+                             std::max<int64_t>(32, ceil_div(visits, units) / 32 * 32));
   } else {
     sh.S = std::min<int64_t>(64, std::max<int64_t>(32, ceil_div(maxblk, 16)));
   }

@@ -123,6 +123,10 @@ struct PrefillPlan {
   int32_t sink;                // sink positions kept next to the window
 };
 
+// Longest split the multi-query kernels take (the library's own choice for
+// 8-bit per-token caches may exceed the caller's bound on split_blocks).
+constexpr int kPrefillMaxSplitBlocks = 512;
+
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream);
 bool prefill_supported(int32_t k_code, int32_t v_code, int32_t k_mode, int32_t v_mode);
 

@@ -465,17 +465,22 @@ void prefill_split_kernel(PrefillArgs pa) {
 // flight in registers while a chunk is computed. Rows past the split's last
 // visible position are stored as zeros, so every lane's mask needs only its
 // column's causal limit.
-// LDS rows hold D fp16 values and 8 halves of padding: the 16 lanes of a
-// 16-byte key read then start on 16 different 4-bank groups.
+// LDS key rows hold D fp16 values and 8 halves of padding: the 16 lanes of
+// a 16-byte key read then start on 16 different 4-bank groups. Value rows
+// are not padded: the 16 lanes of a value read take one row, contiguous.
 // ---------------------------------------------------------------------------
 constexpr int kMqChunk = 64;      // tokens per LDS chunk
-constexpr int kMqMaxSplit = 256;  // blocks per split (the library's bound on split_blocks)
+constexpr int kMqMaxSplit = 512;  // blocks per split at most (the ids staged in LDS)
+static_assert(kMqMaxSplit >= kPrefillMaxSplitBlocks, "a split's ids fit in LDS");
 
 template <int D>
 struct MqLds {
-  static constexpr int KSTR = D + 8;                      // halves per row
-  static constexpr int PLANE = kMqChunk * KSTR * 2;       // bytes: K or V of a chunk
-  static constexpr int BUF = 2 * PLANE + 2 * kMqChunk * 4;  // K, V, key and value scales
+  static constexpr int KSTR = D + 8;                      // halves per key row
+  static constexpr int VSTR = D;                          // halves per value row
+  static constexpr int PLANE = kMqChunk * KSTR * 2;       // bytes: the keys of a chunk
+  static constexpr int VPLANE = kMqChunk * VSTR * 2;      // bytes: its values
+  static constexpr int SCALES = PLANE + VPLANE;           // then key and value scales
+  static constexpr int BUF = SCALES + 2 * kMqChunk * 4;
   static constexpr int BYTES = 2 * BUF;                   // double buffer
   static constexpr int IDS = BYTES;                       // then the split's block ids
   static constexpr int TOTAL = IDS + kMqMaxSplit * 4;
@@ -550,6 +555,7 @@ void mq_split_kernel(PrefillArgs pa) {
   constexpr int SG = TW < 2 ? TW : 2; // tiles per softmax step
   constexpr int PPT = D / 64;         // 16-byte code pieces per thread per plane and chunk
   constexpr int KSTR = MqLds<D>::KSTR;
+  constexpr int VSTR = MqLds<D>::VSTR;
   constexpr int DL = D == 128 ? 7 : 6;  // log2 D
   constexpr int NPF = 2;              // chunks in flight in registers (the tail assumes 2)
   static_assert(NTC == kNW && CH * D / 16 == PPT * 64 * kNW, "chunk shape");
@@ -682,7 +688,7 @@ void mq_split_kernel(PrefillArgs pa) {
     const bool whole = tc + CH <= t1;   // no position past t1 in the chunk
     half_t* K = reinterpret_cast<half_t*>(buf);
     half_t* V = reinterpret_cast<half_t*>(buf + MqLds<D>::PLANE);
-    float* SC = reinterpret_cast<float*>(buf + 2 * MqLds<D>::PLANE);   // [2][CH]
+    float* SC = reinterpret_cast<float*>(buf + MqLds<D>::SCALES);   // [2][CH]
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
       const int q = tid + kWave * kNW * p;
@@ -697,8 +703,8 @@ void mq_split_kernel(PrefillArgs pa) {
       }
       *reinterpret_cast<half8v*>(K + T * KSTR + d0) = k0;
       *reinterpret_cast<half8v*>(K + T * KSTR + d0 + 8) = k1;
-      *reinterpret_cast<half8v*>(V + T * KSTR + d0) = v0;
-      *reinterpret_cast<half8v*>(V + T * KSTR + d0 + 8) = v1;
+      *reinterpret_cast<half8v*>(V + T * VSTR + d0) = v0;
+      *reinterpret_cast<half8v*>(V + T * VSTR + d0 + 8) = v1;
     }
     if (tid < 2 * CH) SC[tid] = whole || tc + (tid & (CH - 1)) < t1 ? R.s : 0.0f;
   };
@@ -709,7 +715,7 @@ void mq_split_kernel(PrefillArgs pa) {
     if (tc + sh * 16 >= t1) return;   // none of the wave's tiles has a visible position
     const half_t* K = reinterpret_cast<const half_t*>(buf);
     const half_t* V = reinterpret_cast<const half_t*>(buf + MqLds<D>::PLANE);
-    const float* SK = reinterpret_cast<const float*>(buf + 2 * MqLds<D>::PLANE);
+    const float* SK = reinterpret_cast<const float*>(buf + MqLds<D>::SCALES);
     const float* SV = SK + CH;
 #pragma unroll
     for (int k0 = 0; k0 < TW; k0 += SG) {
@@ -753,7 +759,7 @@ void mq_split_kernel(PrefillArgs pa) {
         const int nt = sh + (k0 + k) * NSH;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const half_t* vr = V + (nt * 16 + 4 * jj + i) * KSTR + r * (D / 16);
+          const half_t* vr = V + (nt * 16 + 4 * jj + i) * VSTR + r * (D / 16);
           if constexpr (D == 128) {
             const u32x4 w = *reinterpret_cast<const u32x4*>(vr);
             vw[k][i][0] = w.x; vw[k][i][1] = w.y; vw[k][i][2] = w.z; vw[k][i][3] = w.w;

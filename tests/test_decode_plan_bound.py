@@ -112,7 +112,7 @@ def test_prefill_partial_index_stays_in_the_workspace():
                            group_size=32 if mode == "group_asym" else 0,
                            src_dtype=torch.bfloat16)
         for _ in range(200):
-            B = int(rng.integers(1, 9))
+            B = int(rng.choice([rng.integers(1, 9), rng.integers(30, 40)]))
             max_q = int(rng.integers(1, 40))
             max_len = int(rng.integers(max_q, 3000))
             lens = rng.integers(0, max_len + 1, B)
@@ -122,7 +122,8 @@ def test_prefill_partial_index_stays_in_the_workspace():
             maxblk = max(1, -(-max_len // bs))
             CT = -(-max_q * G // 16)
             if staged:   # 8-bit per-token codes: split length from the block visits
-                S = min(256, max(32, -(-B * H * -(-CT // 8) * maxblk // 1024)))
+                units = 2048 if B >= 32 else 1024
+                S = min(512, max(32, -(-B * H * -(-CT // 8) * maxblk // units) // 32 * 32))
             else:
                 S = min(64, max(32, -(-maxblk // 16)))
             J = -(-maxblk // S)
