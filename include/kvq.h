@@ -63,8 +63,10 @@
  *    Conditions only the device can see (pool exhaustion) are written to a
  *    caller-provided device status word. Values that the host cannot check
  *    (block ids, slots, lengths inside device arrays) are preconditions:
- *    breaking one gives unspecified results. Decode ignores block ids outside
- *    [0, num_blocks) instead of reading through them.
+ *    breaking one gives unspecified results. Decode and multi-query attention
+ *    never read outside the cache planes: a block id outside
+ *    [0, num_blocks) is read as block 0 (its positions then count with block
+ *    0's data), and no error is reported.
  *  - Alignment: every device pointer must be 16-byte aligned and every row
  *    stride must keep rows 16-byte aligned.
  *  - Inputs must be finite.
