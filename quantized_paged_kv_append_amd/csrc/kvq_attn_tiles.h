@@ -171,12 +171,15 @@ __device__ __forceinline__ half4v vpair_to_h4(uint32_t a01, uint32_t a23) {
 }
 
 // max over the four lanes {l, l^16, l^32, l^48} (one head column), with
-// the gfx950 lane-swap instructions instead of LDS permutes.
+// the gfx950 lane-swap instructions instead of LDS permutes. The NaN-
+// propagating maximum is one v_maximum3_f32 per level; the IEEE maxNum
+// would first quiet both swapped operands (two more instructions per
+// level). The callers' masked entries are -inf, never NaN.
 __device__ __forceinline__ float colmax4(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  x = __builtin_elementwise_maximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
   auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ float colsum4(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -465,10 +465,19 @@ void prefill_split_kernel(PrefillArgs pa) {
 // flight in registers while a chunk is computed. Rows past the split's last
 // visible position are stored as zeros, so every lane's mask needs only its
 // column's causal limit.
-// LDS key rows hold D fp16 values and 8 halves of padding: the 16 lanes of
-// a 16-byte key read then start on 16 different 4-bank groups. Value rows
-// are not padded: the 16 lanes of a value read take one row, contiguous.
+// LDS key and value rows hold D fp16 values and 8 halves of padding: the 16
+// lanes of a 16-byte key read then start on 16 different 4-bank groups, and
+// the 16 rows of a transposing value read (below) on 16 different ones.
 // ---------------------------------------------------------------------------
+// ds_read_b64_tr_b16 (gfx950): each lane gives the LDS address of 4 fp16
+// values; in each group of 16 lanes, lane i receives as its value k the
+// (i % 4)-th value of those that lane 4 k + i / 4 points at.
+__device__ __forceinline__ half4v lds_read_tr16(const half_t* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      half4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(p)));
+}
+
 constexpr int kMqChunk = 64;      // tokens per LDS chunk
 constexpr int kMqMaxSplit = 512;  // blocks per split at most (the ids staged in LDS)
 static_assert(kMqMaxSplit >= kPrefillMaxSplitBlocks, "a split's ids fit in LDS");
@@ -476,7 +485,7 @@ static_assert(kMqMaxSplit >= kPrefillMaxSplitBlocks, "a split's ids fit in LDS")
 template <int D>
 struct MqLds {
   static constexpr int KSTR = D + 8;                      // halves per key row
-  static constexpr int VSTR = D;                          // halves per value row
+  static constexpr int VSTR = D + 8;                      // halves per value row
   static constexpr int PLANE = kMqChunk * KSTR * 2;       // bytes: the keys of a chunk
   static constexpr int VPLANE = kMqChunk * VSTR * 2;      // bytes: its values
   static constexpr int SCALES = PLANE + VPLANE;           // then key and value scales
@@ -499,7 +508,11 @@ struct MqLds {
 // maximum in almost every chunk). The merges need a common reference for l
 // and acc, not the maximum itself. Writes the PV operands pop[k] =
 // fp16(p sv). MASKED: token t counts for the lane's column only if t < lim.
+// st.m starts at the finite kMqNone, below every real reference, so that no
+// step needs a guard for an infinite one: a masked score (-inf) gives
+// exp2(-inf) = 0 against it, and the first visible score replaces it.
 constexpr float kMqHeadroom = 2.0f;
+constexpr float kMqNone = -3.0e38f;
 
 template <int D, int NT, bool MASKED>
 __device__ __forceinline__ void mq_softmax(const float4v* S, const float4v* sk, const float4v* sv,
@@ -525,15 +538,15 @@ __device__ __forceinline__ void mq_softmax(const float4v* S, const float4v* sk, 
     for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
     st.m = mn;
   }
-  const float msafe = st.m == -INFINITY ? 0.0f : st.m;
-  float lsum = 0.0f;
+  float lsum;
 #pragma unroll
   for (int k = 0; k < NT; ++k) {
     float p[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)   // masked: exp2(-inf) = 0
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(u[k][e], cscore, -msafe));
-    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(u[k][e], cscore, -st.m));
+    const float ps = (p[0] + p[1]) + (p[2] + p[3]);
+    lsum = k == 0 ? ps : lsum + ps;
 #pragma unroll
     for (int e = 0; e < 4; ++e) pop[k][e] = (half_t)(p[e] * sv[k][e]);
   }
@@ -634,7 +647,7 @@ void mq_split_kernel(PrefillArgs pa) {
   SoftmaxState<D> st[NCW];
 #pragma unroll
   for (int cc = 0; cc < NCW; ++cc) {
-    st[cc].m = -INFINITY;
+    st[cc].m = kMqNone;
     st[cc].l = 0.0f;
 #pragma unroll
     for (int k = 0; k < NPV; ++k) st[cc].acc[k] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
@@ -751,37 +764,24 @@ void mq_split_kernel(PrefillArgs pa) {
         for (int cc = 0; cc < NCW; ++cc)
           mq_softmax<D, SG, false>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
       }
-      // value words: lane (r, jj) reads elements [r d/16, (r+1) d/16) of
-      // tokens 4 jj + i of each tile of the group
-      uint32_t vw[SG][4][D / 32];
-#pragma unroll
-      for (int k = 0; k < SG; ++k) {
-        const int nt = sh + (k0 + k) * NSH;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const half_t* vr = V + (nt * 16 + 4 * jj + i) * VSTR + r * (D / 16);
-          if constexpr (D == 128) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(vr);
-            vw[k][i][0] = w.x; vw[k][i][1] = w.y; vw[k][i][2] = w.z; vw[k][i][3] = w.w;
-          } else {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(vr);
-            vw[k][i][0] = w.x; vw[k][i][1] = w.y;
-          }
-        }
-      }
-      // PV MFMA e: output element r d/16 + e of every column. One tile: 16
-      // tokens (16x16x16). Two tiles: 32 tokens (16x16x32), contraction index
-      // 8 jj + i taking token 4 jj + i of the first tile for i < 4 and token
-      // 4 jj + i - 4 of the second for i >= 4 -- the order in which the lane
-      // already holds both the weights and the value words.
+      // PV MFMA e: output elements 16 e + 4 jj + i of every column (row 4 jj
+      // + i of the MFMA's output is element 16 e + 4 jj + i). Its value
+      // operand, the values of elements 16 e .. 16 e + 15 over the group's
+      // tokens, comes from one transposing LDS read per tile: in each 16-lane
+      // group, lane i receives as its value k the (i % 4)-th of the 4 values
+      // that lane 4 k + i / 4 points at. Lane (r, jj) points at elements 16 e
+      // + 4 (r % 4) .. + 3 of token 4 jj + r / 4, and so receives element 16 e
+      // + r of tokens 4 jj .. 4 jj + 3 -- the tokens whose weights it holds.
+      // One tile: 16 tokens (16x16x16). Two tiles: 32 tokens (16x16x32),
+      // contraction index 8 jj + i taking token 4 jj + i of the first tile for
+      // i < 4 and token 4 jj + i - 4 of the second for i >= 4.
+      const int vo = (4 * jj + (r >> 2)) * VSTR + 4 * (r & 3);
 #pragma unroll
       for (int e = 0; e < NPV; ++e) {
-        const u32x2 v0 = raw_vop(vw[0][0][e / 2], vw[0][1][e / 2], vw[0][2][e / 2], vw[0][3][e / 2],
-                                 e & 1);
+        const half4v v0 = lds_read_tr16(V + (sh + k0 * NSH) * 16 * VSTR + vo + 16 * e);
         if constexpr (SG == 2) {
-          const u32x2 v1 = raw_vop(vw[1][0][e / 2], vw[1][1][e / 2], vw[1][2][e / 2],
-                                   vw[1][3][e / 2], e & 1);
-          const half8v va = __builtin_bit_cast(half8v, (u32x4){v0.x, v0.y, v1.x, v1.y});
+          const half4v v1 = lds_read_tr16(V + (sh + (k0 + 1) * NSH) * 16 * VSTR + vo + 16 * e);
+          const half8v va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int cc = 0; cc < NCW; ++cc) {
             const half8v pb = __builtin_shufflevector(pop[cc][0], pop[cc][1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -791,8 +791,8 @@ void mq_split_kernel(PrefillArgs pa) {
         } else {
 #pragma unroll
           for (int cc = 0; cc < NCW; ++cc)
-            st[cc].acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                __builtin_bit_cast(half4v, v0), pop[cc][0], st[cc].acc[e], 0, 0, 0);
+            st[cc].acc[e] =
+                __builtin_amdgcn_mfma_f32_16x16x16f16(v0, pop[cc][0], st[cc].acc[e], 0, 0, 0);
         }
       }
     }
@@ -834,7 +834,7 @@ void mq_split_kernel(PrefillArgs pa) {
     for (int k = 0; k < NPV; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[wave][4 * k + e][lane] = st[cc].acc[k][e];
-    red[wave][NV][lane] = st[cc].m;
+    red[wave][NV][lane] = st[cc].m == kMqNone ? -INFINITY : st[cc].m;   // no visible score
     red[wave][NV + 1][lane] = lsum;
     __syncthreads();
     // waves w < TW merge the shares of their columns: waves w, w + TW, ...
@@ -855,20 +855,12 @@ void mq_split_kernel(PrefillArgs pa) {
       }
       const int64_t pidx = (((int64_t)b * pa.J + j) * a.H + g) * (pa.CT * 16) + col[cc];
       if (jj == 0) *reinterpret_cast<float2*>(a.ws_ml + pidx * 2) = make_float2(M, l);
-      // acc[4 k + e] holds output element (d/16) (4 jj + e) + k of the column
-      float* dst = a.ws_acc + pidx * D + jj * (D / 4);
+      // acc[4 k + e] holds output element 16 k + 4 jj + e of the column
+      float* dst = a.ws_acc + pidx * D + 4 * jj;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (NPV == 8) {
-          float4v lo = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
-          float4v hi = {acc[16 + e], acc[20 + e], acc[24 + e], acc[28 + e]};
-          *reinterpret_cast<float4v*>(dst + 8 * e) = lo;
-          *reinterpret_cast<float4v*>(dst + 8 * e + 4) = hi;
-        } else {
-          float4v v4 = {acc[0 + e], acc[4 + e], acc[8 + e], acc[12 + e]};
-          *reinterpret_cast<float4v*>(dst + 4 * e) = v4;
-        }
-      }
+      for (int k = 0; k < NPV; ++k)
+        *reinterpret_cast<float4v*>(dst + 16 * k) =
+            (float4v){acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
     }
   }
 }
