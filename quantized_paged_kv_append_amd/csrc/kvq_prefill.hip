@@ -570,7 +570,7 @@ void mq_split_kernel(PrefillArgs pa) {
   constexpr int KSTR = MqLds<D>::KSTR;
   constexpr int VSTR = MqLds<D>::VSTR;
   constexpr int DL = D == 128 ? 7 : 6;  // log2 D
-  constexpr int NPF = 2;              // chunks in flight in registers (the tail assumes 2)
+  constexpr int NPF = 2;              // chunks in flight in registers
   static_assert(NTC == kNW && CH * D / 16 == PPT * 64 * kNW, "chunk shape");
   __shared__ __align__(16) unsigned char smem[MqLds<D>::TOTAL];
   const DecodeArgs& a = pa.a;
@@ -667,13 +667,14 @@ void mq_split_kernel(PrefillArgs pa) {
     __syncthreads();
   }
   // ---- chunk loads: piece p of thread tid is code bytes [d0, d0 + 16) of
-  // token T of the chunk; threads 0..63 / 64..127 also load the key / value
-  // scale of token tid % 64 (threads 128.. load a key scale they do not
-  // store, so that every chunk is the same number of loads for the wait
-  // counts). Positions past t1 read a row of the split's last visible token
-  // (cached) and are stored as zeros. A wave's pieces p cover 8 (d 128) or
-  // 16 (d 64) consecutive positions of one block -- also when clamped to
-  // t1 - 1 -- so their block id and row base are wave-uniform. -----------
+  // token T of the chunk; threads tid and tid + 128 (tid < 128) also load
+  // the key (tid % 128 < 64) or value scale of token tid % 64. Positions
+  // past t1 read the codes of the split's last visible token (cached), a
+  // finite copy, and are stored with scale 0: every column's mask excludes
+  // them, so their weights are exactly 0. A wave's pieces p cover 8 (d 128)
+  // or 16 (d 64) consecutive positions of one block -- also when clamped to
+  // t1 - 1 -- so their block id and row base are wave-uniform. The store
+  // has no branch, so it can share a basic block with MFMAs. -------------
   struct Regs {
     u32x4 k[PPT], v[PPT];
     float s;
@@ -698,7 +699,6 @@ void mq_split_kernel(PrefillArgs pa) {
   };
   auto store_chunk = [&](const Regs& R, int c, unsigned char* buf) {
     const int tc = t0 + c * CH;
-    const bool whole = tc + CH <= t1;   // no position past t1 in the chunk
     half_t* K = reinterpret_cast<half_t*>(buf);
     half_t* V = reinterpret_cast<half_t*>(buf + MqLds<D>::PLANE);
     float* SC = reinterpret_cast<float*>(buf + MqLds<D>::SCALES);   // [2][CH]
@@ -706,122 +706,140 @@ void mq_split_kernel(PrefillArgs pa) {
     for (int p = 0; p < PPT; ++p) {
       const int q = tid + kWave * kNW * p;
       const int T = q / (D / 16), d0 = (q % (D / 16)) * 16;
-      half8v k0 = codes8_to_h8<CODE>(R.k[p].x, R.k[p].y);
-      half8v k1 = codes8_to_h8<CODE>(R.k[p].z, R.k[p].w);
-      half8v v0 = codes8_to_h8<CODE>(R.v[p].x, R.v[p].y);
-      half8v v1 = codes8_to_h8<CODE>(R.v[p].z, R.v[p].w);
-      if (!whole && tc + T >= t1) {
-        const half8v z = {};
-        k0 = z; k1 = z; v0 = z; v1 = z;
-      }
+      const half8v k0 = codes8_to_h8<CODE>(R.k[p].x, R.k[p].y);
+      const half8v k1 = codes8_to_h8<CODE>(R.k[p].z, R.k[p].w);
+      const half8v v0 = codes8_to_h8<CODE>(R.v[p].x, R.v[p].y);
+      const half8v v1 = codes8_to_h8<CODE>(R.v[p].z, R.v[p].w);
       *reinterpret_cast<half8v*>(K + T * KSTR + d0) = k0;
       *reinterpret_cast<half8v*>(K + T * KSTR + d0 + 8) = k1;
       *reinterpret_cast<half8v*>(V + T * VSTR + d0) = v0;
       *reinterpret_cast<half8v*>(V + T * VSTR + d0 + 8) = v1;
     }
-    if (tid < 2 * CH) SC[tid] = whole || tc + (tid & (CH - 1)) < t1 ? R.s : 0.0f;
+    // threads tid and tid + 128 write the same scale to the same place
+    SC[tid & (2 * CH - 1)] = tc + (tid & (CH - 1)) < t1 ? R.s : 0.0f;
   };
-  // a wave's TW tiles of chunk c, in groups of SG: scores of the group, one
-  // softmax step per column tile, then PV tile by tile
-  auto compute_chunk = [&](int c, const unsigned char* buf) {
-    const int tc = t0 + c * CH;
-    if (tc + sh * 16 >= t1) return;   // none of the wave's tiles has a visible position
+  // a wave's TW tiles of chunk c, in groups of SG: qk_group computes the
+  // group's raw scores, finish_group takes one softmax step per column tile
+  // and then the PV MFMAs
+  auto qk_group = [&](const unsigned char* buf, int k0, float4v (&S)[NCW][SG]) {
     const half_t* K = reinterpret_cast<const half_t*>(buf);
+#pragma unroll
+    for (int k = 0; k < SG; ++k) {
+      const int nt = sh + (k0 + k) * NSH;
+      half8v kop[NCH];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+        kop[ch] = *reinterpret_cast<const half8v*>(K + (nt * 16 + r) * KSTR + jj * (D / 4) + 8 * ch);
+#pragma unroll
+      for (int cc = 0; cc < NCW; ++cc) {
+        float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ch], qop[cc][ch], acc, 0, 0, 0);
+        S[cc][k] = acc;
+      }
+    }
+  };
+  auto finish_group = [&](int c, const unsigned char* buf, int k0, const float4v (&S)[NCW][SG]) {
+    const int tc = t0 + c * CH;
     const half_t* V = reinterpret_cast<const half_t*>(buf + MqLds<D>::PLANE);
     const float* SK = reinterpret_cast<const float*>(buf + MqLds<D>::SCALES);
     const float* SV = SK + CH;
+    int pos0[SG];
+    float4v sk[SG], sv[SG];
 #pragma unroll
-    for (int k0 = 0; k0 < TW; k0 += SG) {
-      int pos0[SG];
-      float4v S[NCW][SG], sk[SG], sv[SG];
+    for (int k = 0; k < SG; ++k) {
+      const int nt = sh + (k0 + k) * NSH;
+      pos0[k] = tc + nt * 16;
+      sk[k] = *reinterpret_cast<const float4v*>(SK + nt * 16 + 4 * jj);
+      sv[k] = *reinterpret_cast<const float4v*>(SV + nt * 16 + 4 * jj);
+    }
+    half4v pop[NCW][SG];
+    if (pos0[SG - 1] + 16 > lim_lo) {
 #pragma unroll
-      for (int k = 0; k < SG; ++k) {
-        const int nt = sh + (k0 + k) * NSH;
-        pos0[k] = tc + nt * 16;
-        half8v kop[NCH];
+      for (int cc = 0; cc < NCW; ++cc)
+        mq_softmax<D, SG, true>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
+    } else {
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-          kop[ch] =
-              *reinterpret_cast<const half8v*>(K + (nt * 16 + r) * KSTR + jj * (D / 4) + 8 * ch);
-        sk[k] = *reinterpret_cast<const float4v*>(SK + nt * 16 + 4 * jj);
-        sv[k] = *reinterpret_cast<const float4v*>(SV + nt * 16 + 4 * jj);
+      for (int cc = 0; cc < NCW; ++cc)
+        mq_softmax<D, SG, false>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
+    }
+    // PV MFMA e: output elements 16 e + 4 jj + i of every column (row 4 jj
+    // + i of the MFMA's output is element 16 e + 4 jj + i). Its value
+    // operand, the values of elements 16 e .. 16 e + 15 over the group's
+    // tokens, comes from one transposing LDS read per tile: in each 16-lane
+    // group, lane i receives as its value k the (i % 4)-th of the 4 values
+    // that lane 4 k + i / 4 points at. Lane (r, jj) points at elements 16 e
+    // + 4 (r % 4) .. + 3 of token 4 jj + r / 4, and so receives element 16 e
+    // + r of tokens 4 jj .. 4 jj + 3 -- the tokens whose weights it holds.
+    // One tile: 16 tokens (16x16x16). Two tiles: 32 tokens (16x16x32),
+    // contraction index 8 jj + i taking token 4 jj + i of the first tile for
+    // i < 4 and token 4 jj + i - 4 of the second for i >= 4.
+    const int vo = (4 * jj + (r >> 2)) * VSTR + 4 * (r & 3);
+#pragma unroll
+    for (int e = 0; e < NPV; ++e) {
+      const half4v v0 = lds_read_tr16(V + (sh + k0 * NSH) * 16 * VSTR + vo + 16 * e);
+      if constexpr (SG == 2) {
+        const half4v v1 = lds_read_tr16(V + (sh + (k0 + 1) * NSH) * 16 * VSTR + vo + 16 * e);
+        const half8v va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int cc = 0; cc < NCW; ++cc) {
-          float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ch], qop[cc][ch], acc, 0, 0, 0);
-          S[cc][k] = acc;
+          const half8v pb = __builtin_shufflevector(pop[cc][0], pop[cc][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          st[cc].acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st[cc].acc[e], 0, 0, 0);
         }
-      }
-      half4v pop[NCW][SG];
-      if (pos0[SG - 1] + 16 > lim_lo) {
-#pragma unroll
-        for (int cc = 0; cc < NCW; ++cc)
-          mq_softmax<D, SG, true>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
       } else {
 #pragma unroll
         for (int cc = 0; cc < NCW; ++cc)
-          mq_softmax<D, SG, false>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
-      }
-      // PV MFMA e: output elements 16 e + 4 jj + i of every column (row 4 jj
-      // + i of the MFMA's output is element 16 e + 4 jj + i). Its value
-      // operand, the values of elements 16 e .. 16 e + 15 over the group's
-      // tokens, comes from one transposing LDS read per tile: in each 16-lane
-      // group, lane i receives as its value k the (i % 4)-th of the 4 values
-      // that lane 4 k + i / 4 points at. Lane (r, jj) points at elements 16 e
-      // + 4 (r % 4) .. + 3 of token 4 jj + r / 4, and so receives element 16 e
-      // + r of tokens 4 jj .. 4 jj + 3 -- the tokens whose weights it holds.
-      // One tile: 16 tokens (16x16x16). Two tiles: 32 tokens (16x16x32),
-      // contraction index 8 jj + i taking token 4 jj + i of the first tile for
-      // i < 4 and token 4 jj + i - 4 of the second for i >= 4.
-      const int vo = (4 * jj + (r >> 2)) * VSTR + 4 * (r & 3);
-#pragma unroll
-      for (int e = 0; e < NPV; ++e) {
-        const half4v v0 = lds_read_tr16(V + (sh + k0 * NSH) * 16 * VSTR + vo + 16 * e);
-        if constexpr (SG == 2) {
-          const half4v v1 = lds_read_tr16(V + (sh + (k0 + 1) * NSH) * 16 * VSTR + vo + 16 * e);
-          const half8v va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int cc = 0; cc < NCW; ++cc) {
-            const half8v pb = __builtin_shufflevector(pop[cc][0], pop[cc][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            st[cc].acc[e] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st[cc].acc[e], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int cc = 0; cc < NCW; ++cc)
-            st[cc].acc[e] =
-                __builtin_amdgcn_mfma_f32_16x16x16f16(v0, pop[cc][0], st[cc].acc[e], 0, 0, 0);
-        }
+          st[cc].acc[e] =
+              __builtin_amdgcn_mfma_f32_16x16x16f16(v0, pop[cc][0], st[cc].acc[e], 0, 0, 0);
       }
     }
   };
 
-  // ---- the chunk loop: store chunk c, start loading chunk c + NPF into the
-  // registers it freed, then compute chunk c. One barrier per chunk: a wave
-  // stores chunk c + 1 into the buffer of chunk c - 1 only after every wave
-  // has passed chunk c's barrier, i.e. has finished computing chunk c - 1.
-  // Every step issues the same loads (chunks past the last one read its
-  // rows again, clamped, and are never stored), so that the wait before a
-  // store covers that chunk's loads only, not the ones in flight behind it.
+  // ---- the chunk loop. Step c: one barrier (chunk c is in LDS, and every
+  // wave has finished chunk c - 1, whose buffer chunk c + 1 takes next);
+  // the scores of the wave's first tile group of chunk c; chunk c + 1
+  // converted from registers into the other buffer; chunk c + 1 + NPF
+  // loads started into the registers that freed; then the rest of chunk c.
+  // The scores and the conversion sit in one basic block, so the
+  // conversion's vector instructions issue while the score MFMAs run. The
+  // score MFMAs run in every wave, also where none of its columns or tiles
+  // counts (the results are then unused). Every step issues the same loads
+  // (chunks past the last one read its rows again, clamped; stored past the
+  // end they are zeros and never computed), so that the wait before a
+  // conversion covers that chunk's loads only, not the ones behind it.
   const int nch = (t1 - t0 + CH - 1) / CH;
   if (nch > 0) {
+    // register set (c + 1) % 2 holds chunk c + 1 at step c
+    static_assert(NPF == 2, "two register sets alternate with the two buffers");
     Regs R[NPF];
-#pragma unroll
-    for (int u = 0; u < NPF; ++u) load_chunk(R[u], u);
-    auto step = [&](Regs& Ru, int c, unsigned char* buf) {
-      store_chunk(Ru, c, buf);
-      load_chunk(Ru, c + NPF);
+    load_chunk(R[0], 0);
+    load_chunk(R[1], 1);
+    store_chunk(R[0], 0, smem);
+    load_chunk(R[0], 2);
+    auto step = [&](Regs& Rn, int c, const unsigned char* buf, unsigned char* nbuf) {
       __syncthreads();
-      if (active) compute_chunk(c, buf);
-    };
-    int c0 = 0;
-    for (; c0 + NPF <= nch; c0 += NPF) {
+      float4v S[NCW][SG];
+      qk_group(buf, 0, S);
+      store_chunk(Rn, c + 1, nbuf);
+      load_chunk(Rn, c + 1 + NPF);
+      if (active && t0 + c * CH + sh * 16 < t1) {   // some tile of the wave has a visible position
+        finish_group(c, buf, 0, S);
 #pragma unroll
-      for (int u = 0; u < NPF; ++u) step(R[u], c0 + u, smem + u * MqLds<D>::BUF);
+        for (int k0 = SG; k0 < TW; k0 += SG) {
+          qk_group(buf, k0, S);
+          finish_group(c, buf, k0, S);
+        }
+      }
+    };
+    unsigned char* const b0 = smem;
+    unsigned char* const b1 = smem + MqLds<D>::BUF;
+    int c0 = 0;
+    for (; c0 + 2 <= nch; c0 += 2) {
+      step(R[1], c0, b0, b1);
+      step(R[0], c0 + 1, b1, b0);
     }
-    if (c0 < nch) step(R[0], c0, smem);   // at most one chunk left
+    if (c0 < nch) step(R[1], c0, b0, b1);   // at most one chunk left
   }
 
   // ---- merge the waves' states, then write one partial per column ---------
