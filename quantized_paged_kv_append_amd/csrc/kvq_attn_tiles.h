@@ -181,6 +181,20 @@ __device__ __forceinline__ float colmax4(float x) {
   auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __builtin_elementwise_maximum(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
+// colmax4 of two values at once. The first swap trades a's upper 32 lanes
+// for b's lower 32, so one maximum leaves a reduced over the lane pairs
+// {l, l^32} in lanes 0..31 and b in lanes 32..63; the row swap finishes
+// both; a last swap gives every lane both results. Seven instructions
+// instead of two colmax4 (twelve, with their copies).
+__device__ __forceinline__ void colmax4x2(float a, float b, float& ma, float& mb) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  float x = __builtin_elementwise_maximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  ma = __uint_as_float(t[0]);
+  mb = __uint_as_float(t[1]);
+}
 __device__ __forceinline__ float colsum4(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(p[0]) + __uint_as_float(p[1]);

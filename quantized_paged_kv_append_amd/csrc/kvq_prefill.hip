@@ -497,60 +497,85 @@ struct MqLds {
   static_assert(RED <= BYTES, "the merge reuses the chunk buffers");
 };
 
-// One online-softmax step of a column tile over a wave's NT tiles of a
-// chunk: S[k] are the raw scores of tile k (token 4 jj + e of the tile in
-// element e), sk / sv the key / value scales of those tokens, cscore > 0 the
-// column's score factor, so the largest scaled score is cscore times the
-// largest S sk. The reference st.m moves only when a score exceeds it, and
+// One online-softmax step of each of a wave's NCW column tiles over its NT
+// tiles of a chunk, in two parts: mq_scores (scaled scores and column
+// maxima) and mq_weights (rescale, then weights). S[cc][k] are the raw scores of tile k (token 4 jj + e of
+// the tile in element e), sk / sv the key / value scales of those tokens,
+// cscore[cc] > 0 the column's score factor, so the largest scaled score is
+// cscore times the largest S sk (the column maxima of both tiles in one
+// lane exchange when NCW = 2). The reference st.m moves only when a score exceeds it, and
 // then to that score plus kMqHeadroom (log2 units): weights stay below
 // 2^-kMqHeadroom and the smaller increases that follow cost no rescale of
 // the accumulators (with 16 columns to a tile one of them reaches a new
 // maximum in almost every chunk). The merges need a common reference for l
-// and acc, not the maximum itself. Writes the PV operands pop[k] =
-// fp16(p sv). MASKED: token t counts for the lane's column only if t < lim.
+// and acc, not the maximum itself. Writes the PV operands pop[cc][k] =
+// fp16(p sv). MASKED: token t counts for the lane's column only if t < lim[cc].
 // st.m starts at the finite kMqNone, below every real reference, so that no
 // step needs a guard for an infinite one: a masked score (-inf) gives
 // exp2(-inf) = 0 against it, and the first visible score replaces it.
 constexpr float kMqHeadroom = 2.0f;
 constexpr float kMqNone = -3.0e38f;
 
-template <int D, int NT, bool MASKED>
-__device__ __forceinline__ void mq_softmax(const float4v* S, const float4v* sk, const float4v* sv,
-                                           float cscore, int lim, const int* pos0, int jj,
-                                           SoftmaxState<D>& st, half4v* pop) {
+template <int NCW, int NT, bool MASKED>
+__device__ __forceinline__ void mq_scores(const float4v (&S)[NCW][NT], const float4v* sk,
+                                          const int* lim, const int* pos0, int jj,
+                                          float (&u)[NCW][NT][4], float (&mt)[NCW]) {
+  float mx[NCW];
+#pragma unroll
+  for (int cc = 0; cc < NCW; ++cc) {
+    mx[cc] = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NT; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u[cc][k][e] = S[cc][k][e] * sk[k][e];
+        if (MASKED && pos0[k] + 4 * jj + e >= lim[cc]) u[cc][k][e] = -INFINITY;
+        mx[cc] = fmaxf(mx[cc], u[cc][k][e]);
+      }
+  }
+  if constexpr (NCW == 2)
+    colmax4x2(mx[0], mx[1], mt[0], mt[1]);
+  else
+    mt[0] = colmax4(mx[0]);
+}
+
+template <int D, int NCW, int NT>
+__device__ __forceinline__ void mq_weights(const float (&u)[NCW][NT][4], const float (&mt)[NCW],
+                                           const float4v* sv, const float* cscore,
+                                           SoftmaxState<D>* st, half4v (&pop)[NCW][NT]) {
   constexpr int NPV = D / 16;
-  float u[NT][4];
-  float mx = -INFINITY;
+  // the rescales first (branches), then the weights of every column tile
+  // in one basic block
 #pragma unroll
-  for (int k = 0; k < NT; ++k)
+  for (int cc = 0; cc < NCW; ++cc) {
+    SoftmaxState<D>& s = st[cc];
+    const float m = mt[cc] * cscore[cc];
+    if (__any(m > s.m)) {
+      const float mn = m > s.m ? m + kMqHeadroom : s.m;
+      const float alpha = __builtin_amdgcn_exp2f(s.m - mn);   // 1 where s.m stays
+      s.l *= alpha;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u[k][e] = S[k][e] * sk[k][e];
-      if (MASKED && pos0[k] + 4 * jj + e >= lim) u[k][e] = -INFINITY;
-      mx = fmaxf(mx, u[k][e]);
+      for (int c = 0; c < NPV; ++c) s.acc[c] *= alpha;
+      s.m = mn;
     }
-  const float mt = colmax4(mx) * cscore;
-  if (__any(mt > st.m)) {
-    const float mn = mt > st.m ? mt + kMqHeadroom : st.m;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);   // 1 where st.m stays
-    st.l *= alpha;
-#pragma unroll
-    for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
-    st.m = mn;
   }
-  float lsum;
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    float p[4];
+  for (int cc = 0; cc < NCW; ++cc) {
+    SoftmaxState<D>& s = st[cc];
+    float lsum;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)   // masked: exp2(-inf) = 0
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(u[k][e], cscore, -st.m));
-    const float ps = (p[0] + p[1]) + (p[2] + p[3]);
-    lsum = k == 0 ? ps : lsum + ps;
+    for (int k = 0; k < NT; ++k) {
+      float p[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pop[k][e] = (half_t)(p[e] * sv[k][e]);
+      for (int e = 0; e < 4; ++e)   // masked: exp2(-inf) = 0
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(u[cc][k][e], cscore[cc], -s.m));
+      const float ps = (p[0] + p[1]) + (p[2] + p[3]);
+      lsum = k == 0 ? ps : lsum + ps;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pop[cc][k][e] = (half_t)(p[e] * sv[k][e]);
+    }
+    s.l += lsum;
   }
-  st.l += lsum;
 }
 
 // Multi-query kernel over LDS chunks. TW: column-tile groups per workgroup
@@ -740,41 +765,31 @@ void mq_split_kernel(PrefillArgs pa) {
       }
     }
   };
-  auto finish_group = [&](int c, const unsigned char* buf, int k0, const float4v (&S)[NCW][SG]) {
-    const int tc = t0 + c * CH;
-    const half_t* V = reinterpret_cast<const half_t*>(buf + MqLds<D>::PLANE);
+  auto group_scales = [&](int c, const unsigned char* buf, int k0, int (&pos0)[SG],
+                          float4v (&sk)[SG], float4v (&sv)[SG]) {
     const float* SK = reinterpret_cast<const float*>(buf + MqLds<D>::SCALES);
     const float* SV = SK + CH;
-    int pos0[SG];
-    float4v sk[SG], sv[SG];
 #pragma unroll
     for (int k = 0; k < SG; ++k) {
       const int nt = sh + (k0 + k) * NSH;
-      pos0[k] = tc + nt * 16;
+      pos0[k] = t0 + c * CH + nt * 16;
       sk[k] = *reinterpret_cast<const float4v*>(SK + nt * 16 + 4 * jj);
       sv[k] = *reinterpret_cast<const float4v*>(SV + nt * 16 + 4 * jj);
     }
-    half4v pop[NCW][SG];
-    if (pos0[SG - 1] + 16 > lim_lo) {
-#pragma unroll
-      for (int cc = 0; cc < NCW; ++cc)
-        mq_softmax<D, SG, true>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < NCW; ++cc)
-        mq_softmax<D, SG, false>(S[cc], sk, sv, cscore[cc], lim[cc], pos0, jj, st[cc], pop[cc]);
-    }
-    // PV MFMA e: output elements 16 e + 4 jj + i of every column (row 4 jj
-    // + i of the MFMA's output is element 16 e + 4 jj + i). Its value
-    // operand, the values of elements 16 e .. 16 e + 15 over the group's
-    // tokens, comes from one transposing LDS read per tile: in each 16-lane
-    // group, lane i receives as its value k the (i % 4)-th of the 4 values
-    // that lane 4 k + i / 4 points at. Lane (r, jj) points at elements 16 e
-    // + 4 (r % 4) .. + 3 of token 4 jj + r / 4, and so receives element 16 e
-    // + r of tokens 4 jj .. 4 jj + 3 -- the tokens whose weights it holds.
-    // One tile: 16 tokens (16x16x16). Two tiles: 32 tokens (16x16x32),
-    // contraction index 8 jj + i taking token 4 jj + i of the first tile for
-    // i < 4 and token 4 jj + i - 4 of the second for i >= 4.
+  };
+  // PV MFMA e: output elements 16 e + 4 jj + i of every column (row 4 jj
+  // + i of the MFMA's output is element 16 e + 4 jj + i). Its value
+  // operand, the values of elements 16 e .. 16 e + 15 over the group's
+  // tokens, comes from one transposing LDS read per tile: in each 16-lane
+  // group, lane i receives as its value k the (i % 4)-th of the 4 values
+  // that lane 4 k + i / 4 points at. Lane (r, jj) points at elements 16 e
+  // + 4 (r % 4) .. + 3 of token 4 jj + r / 4, and so receives element 16 e
+  // + r of tokens 4 jj .. 4 jj + 3 -- the tokens whose weights it holds.
+  // One tile: 16 tokens (16x16x16). Two tiles: 32 tokens (16x16x32),
+  // contraction index 8 jj + i taking token 4 jj + i of the first tile for
+  // i < 4 and token 4 jj + i - 4 of the second for i >= 4.
+  auto pv_group = [&](const unsigned char* buf, int k0, const half4v (&pop)[NCW][SG]) {
+    const half_t* V = reinterpret_cast<const half_t*>(buf + MqLds<D>::PLANE);
     const int vo = (4 * jj + (r >> 2)) * VSTR + 4 * (r & 3);
 #pragma unroll
     for (int e = 0; e < NPV; ++e) {
@@ -792,6 +807,31 @@ void mq_split_kernel(PrefillArgs pa) {
         for (int cc = 0; cc < NCW; ++cc)
           st[cc].acc[e] =
               __builtin_amdgcn_mfma_f32_16x16x16f16(v0, pop[cc][0], st[cc].acc[e], 0, 0, 0);
+      }
+    }
+  };
+  // the rest of chunk c for a wave whose first group's scores are S0: per
+  // group, the weights and PV MFMAs, then the next group's scores (between
+  // one group's rescale branches and the next's, one basic block). MASKED:
+  // the chunk holds a position at or past the wave's least column limit.
+  auto compute_rest = [&](auto masked, int c, const unsigned char* buf,
+                          const float4v (&S0)[NCW][SG]) {
+    constexpr bool MASKED = decltype(masked)::value;
+    int pos0[SG];
+    float4v sk[SG], sv[SG];
+    float u[NCW][SG][4], mt[NCW];
+    group_scales(c, buf, 0, pos0, sk, sv);
+    mq_scores<NCW, SG, MASKED>(S0, sk, lim, pos0, jj, u, mt);
+#pragma unroll
+    for (int k0 = 0; k0 < TW; k0 += SG) {
+      half4v pop[NCW][SG];
+      mq_weights<D, NCW, SG>(u, mt, sv, cscore, st, pop);
+      pv_group(buf, k0, pop);
+      if (k0 + SG < TW) {
+        float4v S[NCW][SG];
+        qk_group(buf, k0 + SG, S);
+        group_scales(c, buf, k0 + SG, pos0, sk, sv);
+        mq_scores<NCW, SG, MASKED>(S, sk, lim, pos0, jj, u, mt);
       }
     }
   };
@@ -823,13 +863,12 @@ void mq_split_kernel(PrefillArgs pa) {
       qk_group(buf, 0, S);
       store_chunk(Rn, c + 1, nbuf);
       load_chunk(Rn, c + 1 + NPF);
-      if (active && t0 + c * CH + sh * 16 < t1) {   // some tile of the wave has a visible position
-        finish_group(c, buf, 0, S);
-#pragma unroll
-        for (int k0 = SG; k0 < TW; k0 += SG) {
-          qk_group(buf, k0, S);
-          finish_group(c, buf, k0, S);
-        }
+      const int tc = t0 + c * CH;
+      if (active && tc + sh * 16 < t1) {   // some tile of the wave has a visible position
+        if (tc + (sh + (TW - 1) * NSH) * 16 + 16 > lim_lo)
+          compute_rest(std::true_type{}, c, buf, S);
+        else
+          compute_rest(std::false_type{}, c, buf, S);
       }
     };
     unsigned char* const b0 = smem;
