@@ -442,8 +442,17 @@ PrefillShape prefill_shape(const kvq_layout* L, int64_t batch, int64_t num_q_hea
     const int64_t visits = batch * L->num_kv_heads * ceil_div(sh.CT, 8) * maxblk;
     // rounded down to 32 blocks: a split is whole 64-token chunks
     const int64_t units = batch >= 32 ? 2 * kPrefillUnits : kPrefillUnits;
-    sh.S = std::min<int64_t>(kvq::kPrefillMaxSplitBlocks,
-                             std::max<int64_t>(32, ceil_div(visits, units) / 32 * 32));
+    int64_t S = std::min<int64_t>(kvq::kPrefillMaxSplitBlocks,
+                                  std::max<int64_t>(32, ceil_div(visits, units) / 32 * 32));
+    // a last split shorter than a quarter of the others is spread over them
+    // (whole chunks still, and no split past the LDS bound)
+    const int64_t J = ceil_div(maxblk, S);
+    if (J > 1 && maxblk - (J - 1) * S < S / 4) {
+      const int64_t per_chunk = std::max<int64_t>(1, 64 / L->block_size);
+      const int64_t S2 = round_up(ceil_div(maxblk, J - 1), per_chunk);
+      if (S2 <= kvq::kPrefillMaxSplitBlocks) S = S2;
+    }
+    sh.S = S;
   } else {
     sh.S = std::min<int64_t>(64, std::max<int64_t>(32, ceil_div(maxblk, 16)));
   }

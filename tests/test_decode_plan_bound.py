@@ -114,7 +114,7 @@ def test_prefill_partial_index_stays_in_the_workspace():
         for _ in range(200):
             B = int(rng.choice([rng.integers(1, 9), rng.integers(30, 40)]))
             max_q = int(rng.integers(1, 40))
-            max_len = int(rng.integers(max_q, 3000))
+            max_len = int(rng.choice([rng.integers(max_q, 3000), rng.integers(max_q, 40000)]))
             lens = rng.integers(0, max_len + 1, B)
             # query counts up to 3x the bound: the clamp must hold them
             nq_raw = rng.integers(0, 3 * max_q + 1, B)
@@ -124,12 +124,18 @@ def test_prefill_partial_index_stays_in_the_workspace():
             if staged:   # 8-bit per-token codes: split length from the block visits
                 units = 2048 if B >= 32 else 1024
                 S = min(512, max(32, -(-B * H * -(-CT // 8) * maxblk // units) // 32 * 32))
+                J0 = -(-maxblk // S)
+                if J0 > 1 and maxblk - (J0 - 1) * S < S // 4:   # short last split spread
+                    per_chunk = max(1, 64 // bs)
+                    S2 = -(-(-(-maxblk // (J0 - 1))) // per_chunk) * per_chunk
+                    if S2 <= 512:
+                        S = S2
             else:
                 S = min(64, max(32, -(-maxblk // 16)))
             J = -(-maxblk // S)
             partials = B * J * H * CT * 16
             need = -(-partials * d * 4 // 256) * 256 + -(-partials * 8 // 256) * 256
-            assert need <= total
+            assert need == total, (B, max_q, max_len, need, total)   # the rule replayed exactly
             worst = -1
             for b in range(B):
                 nq = min(int(nq_raw[b]), int(lens[b]), max_q)
@@ -139,3 +145,18 @@ def test_prefill_partial_index_stays_in_the_workspace():
                         continue
                     worst = max(worst, ((b * J + j) * H + (H - 1)) * CT * 16 + nq * G - 1)
             assert worst < partials, (B, max_q, max_len, worst, partials)
+
+
+def test_prefill_short_last_split_is_spread():
+    """A 32768-token context plus 8 new tokens is 2049 blocks of 16; the
+    visit rule asks for 256-block splits, which would leave a one-block
+    ninth split. It is spread: 8 splits of 260 blocks (whole 64-token
+    chunks). A 512-token chunk on the same context keeps 5 splits (4 x 520
+    would pass the 512-block bound)."""
+    L = kq.make_layout(8, 128, 16, "fp8", src_dtype=torch.bfloat16)
+    for B, max_q, J in ((16, 8, 8), (1, 512, 5)):
+        max_len = 32768 + max_q
+        CT = -(-max_q * 8 // 16)
+        partials = B * J * 8 * CT * 16
+        need = -(-partials * 128 * 4 // 256) * 256 + -(-partials * 8 // 256) * 256
+        assert kq.kvq_prefill_workspace_bytes(L, B, 64, max_q, max_len) == need, (B, max_q)
