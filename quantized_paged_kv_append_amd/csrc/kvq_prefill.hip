@@ -30,7 +30,7 @@ namespace {
 struct PrefillArgs {
   DecodeArgs a;
   const int32_t* qstart;
-  int32_t J;    // splits per sequence in the grid
+  int32_t J;    // splits per sequence (rows of partials in the workspace)
   int32_t S;    // blocks per split
   int32_t CT;   // column tiles per (sequence, KV head)
   int32_t max_q;  // bound on every sequence's query count (sizes CT and the grid)
@@ -38,6 +38,8 @@ struct PrefillArgs {
   int32_t window;   // > 0: each query sees its last `window` positions ...
   int32_t sink;     // ... and the first `sink` positions
   int32_t bs_log2;  // log2 of the block size (the LDS-staged kernel)
+  int32_t Jg;       // splits per sequence enumerated by the grid (J rounded up to
+                    // odd; splits j >= J start past every sequence and exit)
 };
 
 // NC: 16-column tiles per wave. With NC = 2 a block's codes are loaded and
@@ -150,8 +152,8 @@ void prefill_split_kernel(PrefillArgs pa) {
   u /= ctg;
   const int g = (int)(u % a.H);
   u /= a.H;
-  const int j = (int)(u % pa.J);
-  const int b = (int)(u / pa.J);
+  const int j = (int)(u % pa.Jg);
+  const int b = (int)(u / pa.Jg);
   if (b >= a.batch) return;
   const int L = min(a.context_lens[b], a.max_len);
   const int q0 = pa.qstart[b];
@@ -614,8 +616,8 @@ void mq_split_kernel(PrefillArgs pa) {
   int64_t item = (k8 / CG) * 8 + (x & 7);
   const int g = (int)(item % a.H);
   item /= a.H;
-  const int j = (int)(item % pa.J);
-  const int b = (int)(item / pa.J);
+  const int j = (int)(item % pa.Jg);
+  const int b = (int)(item / pa.Jg);
   if (b >= a.batch) return;
   const int L = min(a.context_lens[b], a.max_len);
   const int q0 = pa.qstart[b];
@@ -1053,7 +1055,7 @@ template <int CODE, int NCW, int TW>
 hipError_t launch_mq_shape(const PrefillArgs& pa, int d, hipStream_t stream) {
   const int64_t cts = (pa.CT + NCW - 1) / NCW;
   const int64_t cgs = (cts + TW - 1) / TW;
-  const int64_t items = (int64_t)pa.a.batch * pa.J * pa.a.H;
+  const int64_t items = (int64_t)pa.a.batch * pa.Jg * pa.a.H;
   const dim3 grid((unsigned)(8 * cgs * ((items + 7) / 8)));
   if (d == 128)
     mq_split_kernel<CODE, 128, NCW, TW><<<grid, 64 * kNW, 0, stream>>>(pa);
@@ -1062,6 +1064,12 @@ hipError_t launch_mq_shape(const PrefillArgs& pa, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Jg: the k-th workgroup of an XCD goes to its CUs in turn, so with the
+// split index cycling through the item order and J dividing 32, each CU
+// would keep one split index: with uneven lengths some CUs would take every
+// full first split and others the mostly empty last ones (8B layer, 8
+// queries: 4 splits 248 us, 5 splits 197 us). An odd split count in the
+// enumeration cycles every CU through all of them.
 template <int CODE>
 hipError_t launch_mq(PrefillArgs pa, int d, int bs, hipStream_t stream) {
   pa.bs_log2 = bs == 32 ? 5 : 4;
@@ -1120,7 +1128,8 @@ hipError_t launch_prefill(const PrefillPlan& pp, hipStream_t stream) {
   pa.window = pp.window;
   pa.sink = pp.sink;
   pa.TW = 1;   // set per launch shape
-  const int64_t units = (int64_t)p.batch * pp.splits * p.num_kv_heads;
+  pa.Jg = pp.splits | 1;   // odd, as for the LDS-staged kernel (see launch_mq)
+  const int64_t units = (int64_t)p.batch * pa.Jg * p.num_kv_heads;
   const int d = p.head_dim, bs = p.block_size;
   hipError_t e;
   const bool tok8 = p.k_mode == KVQ_SCALE_TOKEN_SYM &&
