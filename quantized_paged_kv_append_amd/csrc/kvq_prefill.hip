@@ -456,17 +456,17 @@ void prefill_split_kernel(PrefillArgs pa) {
 // Multi-query attention with the cache converted once per workgroup (8-bit
 // codes with per-token scales, no window). A workgroup takes one unit
 // (sequence b, split j, KV head g, column group) and streams the split in
-// chunks of kMqChunk tokens: its 256 threads load each chunk's key and value
-// codes once, 16 bytes per load, convert them to fp16 (exact for INT8 and
-// E4M3 codes) and store them with the per-token scales in one of two LDS
-// buffers; the waves then take their MFMA operands from LDS, so a block is
-// fetched and converted once for all the columns of the workgroup, not once
-// per wave. Wave w serves NCW column tiles (16 (query, head) columns each,
-// numbered as in prefill_split_kernel) and the (w / TW)-th of 4 / TW
-// interleaved shares of a chunk's 16-token tiles. The next two chunks are in
-// flight in registers while a chunk is computed. Rows past the split's last
-// visible position are stored as zeros, so every lane's mask needs only its
-// column's causal limit.
+// chunks of 16 tokens per wave (64 with four waves, 32 with two): its
+// threads load each chunk's key and value codes once, 16 bytes per load,
+// convert them to fp16 (exact for INT8 and E4M3 codes) and store them with
+// the per-token scales in one of two LDS buffers; the waves then take their
+// MFMA operands from LDS, so a block is fetched and converted once for all
+// the columns of the workgroup, not once per wave. Wave w serves NCW column
+// tiles (16 (query, head) columns each, numbered as in prefill_split_kernel)
+// and the (w / TW)-th of NW / TW interleaved shares of a chunk's 16-token
+// tiles. The next two chunks are in flight in registers while a chunk is
+// computed. Rows past the split's last visible position carry scale 0 and
+// every lane's mask excludes them (its column's causal limit).
 // LDS key and value rows hold D fp16 values and 8 halves of padding: the 16
 // lanes of a 16-byte key read then start on 16 different 4-bank groups, and
 // the 16 rows of a transposing value read (below) on 16 different ones.
@@ -480,22 +480,21 @@ __device__ __forceinline__ half4v lds_read_tr16(const half_t* p) {
       half4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(p)));
 }
 
-constexpr int kMqChunk = 64;      // tokens per LDS chunk
 constexpr int kMqMaxSplit = 512;  // blocks per split at most (the ids staged in LDS)
 static_assert(kMqMaxSplit >= kPrefillMaxSplitBlocks, "a split's ids fit in LDS");
 
-template <int D>
+template <int D, int CH, int NW>
 struct MqLds {
   static constexpr int KSTR = D + 8;                      // halves per key row
   static constexpr int VSTR = D + 8;                      // halves per value row
-  static constexpr int PLANE = kMqChunk * KSTR * 2;       // bytes: the keys of a chunk
-  static constexpr int VPLANE = kMqChunk * VSTR * 2;      // bytes: its values
+  static constexpr int PLANE = CH * KSTR * 2;             // bytes: the keys of a chunk
+  static constexpr int VPLANE = CH * VSTR * 2;            // bytes: its values
   static constexpr int SCALES = PLANE + VPLANE;           // then key and value scales
-  static constexpr int BUF = SCALES + 2 * kMqChunk * 4;
+  static constexpr int BUF = SCALES + 2 * CH * 4;
   static constexpr int BYTES = 2 * BUF;                   // double buffer
   static constexpr int IDS = BYTES;                       // then the split's block ids
   static constexpr int TOTAL = IDS + kMqMaxSplit * 4;
-  static constexpr int RED = kNW * (D / 4 + 2) * kWave * 4;   // the waves' merge area
+  static constexpr int RED = NW * (D / 4 + 2) * kWave * 4;   // the waves' merge area
   static_assert(RED <= BYTES, "the merge reuses the chunk buffers");
 };
 
@@ -580,26 +579,29 @@ __device__ __forceinline__ void mq_weights(const float (&u)[NCW][NT][4], const f
   }
 }
 
-// Multi-query kernel over LDS chunks. TW: column-tile groups per workgroup
-// (and tiles per wave per chunk: wave w takes tiles w / TW + k (4 / TW),
-// k < TW, one softmax step per two of them); NCW: column tiles per wave.
-template <int CODE, int D, int NCW, int TW>
-__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
+// Multi-query kernel over LDS chunks. NW waves per workgroup and CH = 16 NW
+// tokens per chunk (one 16-token tile per wave). TW: column-tile groups per
+// workgroup (and tiles per wave per chunk: wave w takes tiles w / TW + k
+// (NW / TW), k < TW, one softmax step per two of them); NCW: column tiles
+// per wave.
+template <int CODE, int D, int NCW, int TW, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_split_kernel(PrefillArgs pa) {
   constexpr int NCH = D / 32;
   constexpr int NPV = D / 16;
   constexpr int NV = D / 4;
-  constexpr int CH = kMqChunk;
+  constexpr int CH = 16 * NW;
   constexpr int NTC = CH / 16;        // 16-token tiles per chunk
   constexpr int NSH = NTC / TW;       // waves sharing a column tile group (tile stride)
   constexpr int SG = TW < 2 ? TW : 2; // tiles per softmax step
   constexpr int PPT = D / 64;         // 16-byte code pieces per thread per plane and chunk
-  constexpr int KSTR = MqLds<D>::KSTR;
-  constexpr int VSTR = MqLds<D>::VSTR;
+  using Lds = MqLds<D, CH, NW>;
+  constexpr int KSTR = Lds::KSTR;
+  constexpr int VSTR = Lds::VSTR;
   constexpr int DL = D == 128 ? 7 : 6;  // log2 D
   constexpr int NPF = 2;              // chunks in flight in registers
-  static_assert(NTC == kNW && CH * D / 16 == PPT * 64 * kNW, "chunk shape");
-  __shared__ __align__(16) unsigned char smem[MqLds<D>::TOTAL];
+  static_assert(NTC == NW && CH * D / 16 == PPT * 64 * NW, "chunk shape");
+  __shared__ __align__(16) unsigned char smem[Lds::TOTAL];
   const DecodeArgs& a = pa.a;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -684,10 +686,10 @@ void mq_split_kernel(PrefillArgs pa) {
   // wait on no other vector load (those complete in order, so waiting on an
   // id just loaded would also wait on the chunks already in flight). Ids
   // outside the pool (a broken precondition) are read as block 0. --------
-  int32_t* ids = reinterpret_cast<int32_t*>(smem + MqLds<D>::IDS);
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + Lds::IDS);
   {
     const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
-    for (int i = tid; i < s1 - s0; i += kWave * kNW) {
+    for (int i = tid; i < s1 - s0; i += kWave * NW) {
       const int32_t id = trow[s0 + i];
       ids[i] = id >= 0 && id < a.num_blocks ? id : 0;
     }
@@ -710,7 +712,7 @@ void mq_split_kernel(PrefillArgs pa) {
     const int tc = t0 + c * CH;
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
-      const int q = tid + kWave * kNW * p;
+      const int q = tid + kWave * NW * p;
       const int T = q / (D / 16), d0 = (q % (D / 16)) * 16;
       const int tok = min(tc + T, t1 - 1);
       const int blk = __builtin_amdgcn_readfirstlane(tok >> bsl);
@@ -727,11 +729,11 @@ void mq_split_kernel(PrefillArgs pa) {
   auto store_chunk = [&](const Regs& R, int c, unsigned char* buf) {
     const int tc = t0 + c * CH;
     half_t* K = reinterpret_cast<half_t*>(buf);
-    half_t* V = reinterpret_cast<half_t*>(buf + MqLds<D>::PLANE);
-    float* SC = reinterpret_cast<float*>(buf + MqLds<D>::SCALES);   // [2][CH]
+    half_t* V = reinterpret_cast<half_t*>(buf + Lds::PLANE);
+    float* SC = reinterpret_cast<float*>(buf + Lds::SCALES);   // [2][CH]
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
-      const int q = tid + kWave * kNW * p;
+      const int q = tid + kWave * NW * p;
       const int T = q / (D / 16), d0 = (q % (D / 16)) * 16;
       const half8v k0 = codes8_to_h8<CODE>(R.k[p].x, R.k[p].y);
       const half8v k1 = codes8_to_h8<CODE>(R.k[p].z, R.k[p].w);
@@ -769,7 +771,7 @@ void mq_split_kernel(PrefillArgs pa) {
   };
   auto group_scales = [&](int c, const unsigned char* buf, int k0, int (&pos0)[SG],
                           float4v (&sk)[SG], float4v (&sv)[SG]) {
-    const float* SK = reinterpret_cast<const float*>(buf + MqLds<D>::SCALES);
+    const float* SK = reinterpret_cast<const float*>(buf + Lds::SCALES);
     const float* SV = SK + CH;
 #pragma unroll
     for (int k = 0; k < SG; ++k) {
@@ -791,7 +793,7 @@ void mq_split_kernel(PrefillArgs pa) {
   // contraction index 8 jj + i taking token 4 jj + i of the first tile for
   // i < 4 and token 4 jj + i - 4 of the second for i >= 4.
   auto pv_group = [&](const unsigned char* buf, int k0, const half4v (&pop)[NCW][SG]) {
-    const half_t* V = reinterpret_cast<const half_t*>(buf + MqLds<D>::PLANE);
+    const half_t* V = reinterpret_cast<const half_t*>(buf + Lds::PLANE);
     const int vo = (4 * jj + (r >> 2)) * VSTR + 4 * (r & 3);
 #pragma unroll
     for (int e = 0; e < NPV; ++e) {
@@ -874,7 +876,7 @@ void mq_split_kernel(PrefillArgs pa) {
       }
     };
     unsigned char* const b0 = smem;
-    unsigned char* const b1 = smem + MqLds<D>::BUF;
+    unsigned char* const b1 = smem + Lds::BUF;
     int c0 = 0;
     for (; c0 + 2 <= nch; c0 += 2) {
       step(R[1], c0, b0, b1);
@@ -900,12 +902,12 @@ void mq_split_kernel(PrefillArgs pa) {
     if (wave < TW && valid[cc]) {
       float M = -INFINITY;
 #pragma unroll
-      for (int w = wave; w < kNW; w += TW) M = fmaxf(M, red[w][NV][lane]);
+      for (int w = wave; w < NW; w += TW) M = fmaxf(M, red[w][NV][lane]);
       float acc[NV], l = 0.0f;
 #pragma unroll
       for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
 #pragma unroll
-      for (int w = wave; w < kNW; w += TW) {
+      for (int w = wave; w < NW; w += TW) {
         const float mw = red[w][NV][lane];
         const float sc = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
         l += sc * red[w][NV + 1][lane];
@@ -1051,18 +1053,25 @@ hipError_t launch_prefill_shape(PrefillArgs pa, int d, int bs, int64_t units_per
 // 1, 2 or 4 waves' column tiles per workgroup (the other waves of a column
 // tile group share its token tiles). Grid: 8 x (column groups) x
 // ceil(units / 8), so that the column groups of a unit meet on one XCD.
-template <int CODE, int NCW, int TW>
+template <int CODE, int NCW, int TW, int NW>
 hipError_t launch_mq_shape(const PrefillArgs& pa, int d, hipStream_t stream) {
+  static_assert(TW <= NW, "a column-tile group has at least one wave");
   const int64_t cts = (pa.CT + NCW - 1) / NCW;
   const int64_t cgs = (cts + TW - 1) / TW;
   const int64_t items = (int64_t)pa.a.batch * pa.Jg * pa.a.H;
   const dim3 grid((unsigned)(8 * cgs * ((items + 7) / 8)));
   if (d == 128)
-    mq_split_kernel<CODE, 128, NCW, TW><<<grid, 64 * kNW, 0, stream>>>(pa);
+    mq_split_kernel<CODE, 128, NCW, TW, NW><<<grid, 64 * NW, 0, stream>>>(pa);
   else
-    mq_split_kernel<CODE, 64, NCW, TW><<<grid, 64 * kNW, 0, stream>>>(pa);
+    mq_split_kernel<CODE, 64, NCW, TW, NW><<<grid, 64 * NW, 0, stream>>>(pa);
   return hipGetLastError();
 }
+
+// Two column-tile groups per workgroup run as two waves over 32-token
+// chunks (about 37 KB of LDS, so four workgroups share a CU and each
+// barrier waits for two waves, not four): 70B shape, 8 queries per
+// sequence, 290-297 -> 281-291 us. One group keeps four waves (8B layer:
+// two waves were 1% slower).
 
 // Jg: the k-th workgroup of an XCD goes to its CUs in turn, so with the
 // split index cycling through the item order and J dividing 32, each CU
@@ -1073,11 +1082,11 @@ hipError_t launch_mq_shape(const PrefillArgs& pa, int d, hipStream_t stream) {
 template <int CODE>
 hipError_t launch_mq(PrefillArgs pa, int d, int bs, hipStream_t stream) {
   pa.bs_log2 = bs == 32 ? 5 : 4;
-  if (pa.CT < 2) return launch_mq_shape<CODE, 1, 1>(pa, d, stream);
+  if (pa.CT < 2) return launch_mq_shape<CODE, 1, 1, 4>(pa, d, stream);
   const int cts = (pa.CT + 1) / 2;
-  if (cts >= 4) return launch_mq_shape<CODE, 2, 4>(pa, d, stream);
-  if (cts >= 2) return launch_mq_shape<CODE, 2, 2>(pa, d, stream);
-  return launch_mq_shape<CODE, 2, 1>(pa, d, stream);
+  if (cts >= 4) return launch_mq_shape<CODE, 2, 4, 4>(pa, d, stream);
+  if (cts >= 2) return launch_mq_shape<CODE, 2, 2, 2>(pa, d, stream);
+  return launch_mq_shape<CODE, 2, 1, 4>(pa, d, stream);
 }
 
 }  // namespace
