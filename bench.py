@@ -359,12 +359,17 @@ def run(args, wname):
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
 
-    for _ in range(args.warmup):
+    # the last warm-up step runs right before the timed ones, with no idle gap
+    # between them (the first launch after the GPU idles for the host's
+    # reads runs ~30 us slower); the lengths are read before it, so the timed
+    # steps start from them plus one step's tokens
+    for _ in range(max(args.warmup - 1, 0)):
         step()
     torch.cuda.synchronize()
-    ctx_before = ctx.cpu().numpy().astype(np.int64)
+    ctx_before = ctx.cpu().numpy().astype(np.int64) + (new_per_step if args.warmup > 0 else 0)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    if args.warmup > 0:
+        step()
     t_start.record(stream)
     wall0 = time.perf_counter()
     for s_ in range(args.steps):
@@ -408,13 +413,15 @@ def run(args, wname):
                 step()
         stream.wait_stream(side)
         torch.cuda.synchronize()
-        for _ in range(args.warmup):
+        for _ in range(max(args.warmup - 1, 0)):   # the last one as in the eager steps
             g.replay()
         torch.cuda.synchronize()
-        ctx_g = ctx.cpu().numpy().astype(np.int64)
+        ctx_g = ctx.cpu().numpy().astype(np.int64) + (new_per_step if args.warmup > 0 else 0)
         gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.warmup > 0:
+            g.replay()
         g0.record(stream)
         for s_ in range(args.steps):
             if flush_buf is not None:

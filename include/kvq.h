@@ -414,18 +414,22 @@ kvq_status kvq_pool_init(int32_t* free_stack, int32_t* free_top,
  *  slot_mapping_out[o_b + k] (o_b = exclusive prefix sum of new_tokens) gets
  *  the slot of position L_b + k, k < n_b. context_lens_out (may be NULL or
  *  alias context_lens) gets L_b + n_b.
- * All or nothing: if sum(need) > top, or a sequence would exceed
- * max_blocks_per_seq blocks, nothing is written except *status_flag =
- * KVQ_ERR_OUT_OF_BLOCKS; on success *status_flag = KVQ_OK. All pointers are
- * device memory; pool_capacity is the length of free_stack. */
+ * All or nothing: if sum(new_tokens) > slot_capacity (the entries of
+ * slot_mapping_out), nothing is written except *status_flag =
+ * KVQ_ERR_INVALID_ARGUMENT; else if sum(need) > top, or a sequence would
+ * exceed max_blocks_per_seq blocks, nothing is written except *status_flag =
+ * KVQ_ERR_OUT_OF_BLOCKS; on success *status_flag = KVQ_OK. The token count
+ * is checked on the device, so the call reads nothing back to the host.
+ * All pointers are device memory; pool_capacity is the length of
+ * free_stack. A negative slot_capacity is KVQ_ERR_INVALID_ARGUMENT. */
 kvq_status kvq_blocks_reserve(int32_t* free_stack, int32_t* free_top,
                               int64_t pool_capacity, int32_t* block_tables,
                               int32_t max_blocks_per_seq,
                               const int32_t* context_lens,
                               const int32_t* new_tokens, int32_t batch,
                               int32_t block_size, int64_t* slot_mapping_out,
-                              int32_t* context_lens_out, int32_t* status_flag,
-                              void* stream);
+                              int64_t slot_capacity, int32_t* context_lens_out,
+                              int32_t* status_flag, void* stream);
 
 /* Return the blocks of every sequence b with release_mask[b] != 0 to the
  * pool: its ceil(context_lens[b] / bs) blocks are pushed in batch order and,
@@ -500,9 +504,10 @@ kvq_status kvq_blocks_reserve_shared(int32_t* free_stack, int32_t* free_top,
                                      const int32_t* context_lens,
                                      const int32_t* new_tokens, int32_t batch,
                                      int32_t block_size, int64_t* slot_mapping_out,
-                                     int32_t* context_lens_out, int32_t* cow_src,
-                                     int32_t* cow_dst, int32_t* cow_count,
-                                     int32_t* status_flag, void* stream);
+                                     int64_t slot_capacity, int32_t* context_lens_out,
+                                     int32_t* cow_src, int32_t* cow_dst,
+                                     int32_t* cow_count, int32_t* status_flag,
+                                     void* stream);
 
 /* kvq_blocks_release for a pool with counts: every table entry of a masked
  * row drops one reference (rows in batch order, entries in logical order)

@@ -572,16 +572,19 @@ kvq_status kvq_blocks_reserve(int32_t* free_stack, int32_t* free_top, int64_t po
                               int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, const int32_t* new_tokens,
                               int32_t batch, int32_t block_size, int64_t* slot_mapping_out,
-                              int32_t* context_lens_out, int32_t* status_flag, void* stream) {
+                              int64_t slot_capacity, int32_t* context_lens_out,
+                              int32_t* status_flag, void* stream) {
   if (!free_stack || !free_top || !status_flag || pool_capacity < 1 || pool_capacity > INT32_MAX)
     return KVQ_ERR_INVALID_ARGUMENT;
-  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1) return KVQ_ERR_INVALID_ARGUMENT;
-  if (batch > 0 && (!block_tables || !context_lens || !new_tokens || !slot_mapping_out))
+  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1 || slot_capacity < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (!block_tables || !context_lens || !new_tokens ||
+                    (!slot_mapping_out && slot_capacity > 0)))
     return KVQ_ERR_INVALID_ARGUMENT;
   return hip_status(kvq::launch_blocks_reserve(
       free_stack, free_top, pool_capacity, block_tables, max_blocks_per_seq, context_lens,
-      new_tokens, batch, block_size, slot_mapping_out, context_lens_out, status_flag,
-      static_cast<hipStream_t>(stream)));
+      new_tokens, batch, block_size, slot_mapping_out, slot_capacity, context_lens_out,
+      status_flag, static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_blocks_release(int32_t* free_stack, int32_t* free_top, int64_t pool_capacity,
@@ -635,20 +638,23 @@ kvq_status kvq_blocks_reserve_shared(int32_t* free_stack, int32_t* free_top,
                                      int32_t* block_tables, int32_t max_blocks_per_seq,
                                      const int32_t* context_lens, const int32_t* new_tokens,
                                      int32_t batch, int32_t block_size,
-                                     int64_t* slot_mapping_out, int32_t* context_lens_out,
-                                     int32_t* cow_src, int32_t* cow_dst, int32_t* cow_count,
+                                     int64_t* slot_mapping_out, int64_t slot_capacity,
+                                     int32_t* context_lens_out, int32_t* cow_src,
+                                     int32_t* cow_dst, int32_t* cow_count,
                                      int32_t* status_flag, void* stream) {
   if (!free_stack || !free_top || !status_flag || !refcount || !cow_count ||
       pool_capacity < 1 || pool_capacity > INT32_MAX)
     return KVQ_ERR_INVALID_ARGUMENT;
-  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1) return KVQ_ERR_INVALID_ARGUMENT;
-  if (batch > 0 && (!block_tables || !context_lens || !new_tokens || !slot_mapping_out ||
-                    !cow_src || !cow_dst))
+  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1 || slot_capacity < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (!block_tables || !context_lens || !new_tokens ||
+                    (!slot_mapping_out && slot_capacity > 0) || !cow_src || !cow_dst))
     return KVQ_ERR_INVALID_ARGUMENT;
   return hip_status(kvq::launch_blocks_reserve_shared(
       free_stack, free_top, pool_capacity, refcount, block_tables, max_blocks_per_seq,
-      context_lens, new_tokens, batch, block_size, slot_mapping_out, context_lens_out, cow_src,
-      cow_dst, cow_count, status_flag, static_cast<hipStream_t>(stream)));
+      context_lens, new_tokens, batch, block_size, slot_mapping_out, slot_capacity,
+      context_lens_out, cow_src, cow_dst, cow_count, status_flag,
+      static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_blocks_release_shared(int32_t* free_stack, int32_t* free_top,

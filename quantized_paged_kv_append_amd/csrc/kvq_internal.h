@@ -136,7 +136,7 @@ hipError_t launch_blocks_reserve(int32_t* stack, int32_t* top, int64_t capacity,
                                  int32_t* tables, int32_t max_blocks,
                                  const int32_t* lens, const int32_t* new_tokens,
                                  int32_t batch, int32_t bs, int64_t* slots,
-                                 int32_t* lens_out, int32_t* status,
+                                 int64_t slot_capacity, int32_t* lens_out, int32_t* status,
                                  hipStream_t stream);
 hipError_t launch_blocks_release(int32_t* stack, int32_t* top,
                                  int64_t capacity, const int32_t* tables,

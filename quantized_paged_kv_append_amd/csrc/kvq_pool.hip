@@ -76,7 +76,8 @@ __device__ __forceinline__ int64_t ceil_div(int64_t x, int64_t y) { return (x + 
 __global__ __launch_bounds__(kThreads) void reserve_kernel(
     int32_t* stack, int32_t* top, int32_t* tables, int32_t max_blocks,
     const int32_t* lens, const int32_t* new_tokens, int32_t batch, int32_t bs,
-    int64_t* slots, int32_t* lens_out, int32_t* status, int64_t capacity) {
+    int64_t* slots, int32_t* lens_out, int32_t* status, int64_t capacity,
+    int64_t slot_capacity) {
   __shared__ int64_t sh[kThreads];
   __shared__ int64_t s_bpre[kThreads], s_wpre[kThreads], s_tout[kThreads];
   __shared__ int32_t s_L[kThreads], s_n[kThreads];
@@ -84,24 +85,31 @@ __global__ __launch_bounds__(kThreads) void reserve_kernel(
   const int tid = threadIdx.x;
   // a top outside [0, capacity] (a broken precondition) is cut to it
   const int64_t top0 = min(max((int64_t)*top, (int64_t)0), capacity);
-  // pass 1: total need and table capacity check
+  // pass 1: total need, table capacity check, and the slots the call writes
   if (tid == 0) ok_sh = 1;
   __syncthreads();
-  int64_t total_need = 0;
+  int64_t total_need = 0, total_tok = 0;
   for (int base = 0; base < batch; base += kThreads) {
     const int b = base + tid;
-    int64_t need = 0;
+    int64_t need = 0, n = 0;
     if (b < batch) {
+      n = new_tokens[b];
       const int64_t have = ceil_div(lens[b], bs);
-      const int64_t want = ceil_div((int64_t)lens[b] + new_tokens[b], bs);
+      const int64_t want = ceil_div((int64_t)lens[b] + n, bs);
       if (want > max_blocks) ok_sh = 0;
       need = want - have;
     }
-    int64_t chunk_total;
+    int64_t chunk_total, chunk_tok;
     block_exclusive_scan(need, &chunk_total, sh);
+    block_exclusive_scan(n, &chunk_tok, sh);
     total_need += chunk_total;
+    total_tok += chunk_tok;
   }
   __syncthreads();
+  if (total_tok > slot_capacity) {   // slot_mapping_out is too short: a caller error
+    if (tid == 0) *status = KVQ_ERR_INVALID_ARGUMENT;
+    return;
+  }
   if (!ok_sh || total_need > top0) {
     if (tid == 0) *status = KVQ_ERR_OUT_OF_BLOCKS;
     return;
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void reserve_shared_kernel(
     int32_t* stack, int32_t* top, int64_t capacity, int32_t* refcount, int32_t* tables,
     int32_t max_blocks, const int32_t* lens, const int32_t* new_tokens, int32_t batch,
     int32_t bs, int64_t* slots, int32_t* lens_out, int32_t* cow_src, int32_t* cow_dst,
-    int32_t* cow_count, int32_t* status) {
+    int32_t* cow_count, int32_t* status, int64_t slot_capacity) {
   __shared__ int64_t sh[kThreads];
   __shared__ int64_t s_first[kThreads], s_gpre[kThreads], s_xpre[kThreads], s_tout[kThreads];
   __shared__ int32_t s_L[kThreads], s_n[kThreads], s_cow[kThreads];
@@ -280,22 +288,29 @@ __global__ __launch_bounds__(kThreads) void reserve_shared_kernel(
   const int64_t top0 = min(max((int64_t)*top, (int64_t)0), capacity);
   if (tid == 0) ok_sh = 1;
   __syncthreads();
-  int64_t total_need = 0;
+  int64_t total_need = 0, total_tok = 0;
   for (int base = 0; base < batch; base += kThreads) {
     const int b = base + tid;
-    int64_t need = 0;
+    int64_t need = 0, n = 0;
     if (b < batch) {
+      n = new_tokens[b];
       const int64_t have = ceil_div(lens[b], bs);
-      const int64_t want = ceil_div((int64_t)lens[b] + new_tokens[b], bs);
+      const int64_t want = ceil_div((int64_t)lens[b] + n, bs);
       if (want > max_blocks) ok_sh = 0;
       need = want - have +
              cow_needed(refcount, capacity, tables, max_blocks, b, lens[b], new_tokens[b], bs);
     }
-    int64_t chunk_total;
+    int64_t chunk_total, chunk_tok;
     block_exclusive_scan(need, &chunk_total, sh);
+    block_exclusive_scan(n, &chunk_tok, sh);
     total_need += chunk_total;
+    total_tok += chunk_tok;
   }
   __syncthreads();
+  if (total_tok > slot_capacity) {   // slot_mapping_out is too short: a caller error
+    if (tid == 0) *status = KVQ_ERR_INVALID_ARGUMENT;
+    return;
+  }
   if (!ok_sh || total_need > top0) {
     if (tid == 0) *status = KVQ_ERR_OUT_OF_BLOCKS;
     return;
@@ -635,11 +650,11 @@ hipError_t launch_blocks_reserve(int32_t* stack, int32_t* top, int64_t capacity,
                                  int32_t* tables, int32_t max_blocks,
                                  const int32_t* lens, const int32_t* new_tokens,
                                  int32_t batch, int32_t bs, int64_t* slots,
-                                 int32_t* lens_out, int32_t* status,
+                                 int64_t slot_capacity, int32_t* lens_out, int32_t* status,
                                  hipStream_t stream) {
   reserve_kernel<<<1, kThreads, 0, stream>>>(stack, top, tables, max_blocks, lens,
                                              new_tokens, batch, bs, slots, lens_out,
-                                             status, capacity);
+                                             status, capacity, slot_capacity);
   return hipGetLastError();
 }
 
@@ -676,13 +691,14 @@ hipError_t launch_blocks_reserve_shared(int32_t* stack, int32_t* top, int64_t ca
                                         int32_t* refcount, int32_t* tables, int32_t max_blocks,
                                         const int32_t* lens, const int32_t* new_tokens,
                                         int32_t batch, int32_t bs, int64_t* slots,
-                                        int32_t* lens_out, int32_t* cow_src, int32_t* cow_dst,
+                                        int64_t slot_capacity, int32_t* lens_out,
+                                        int32_t* cow_src, int32_t* cow_dst,
                                         int32_t* cow_count, int32_t* status,
                                         hipStream_t stream) {
   reserve_shared_kernel<<<1, kThreads, 0, stream>>>(stack, top, capacity, refcount, tables,
                                                     max_blocks, lens, new_tokens, batch, bs,
                                                     slots, lens_out, cow_src, cow_dst,
-                                                    cow_count, status);
+                                                    cow_count, status, slot_capacity);
   return hipGetLastError();
 }
 

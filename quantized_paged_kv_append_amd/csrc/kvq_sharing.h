@@ -17,7 +17,8 @@ hipError_t launch_blocks_reserve_shared(int32_t* stack, int32_t* top, int64_t ca
                                         int32_t* refcount, int32_t* tables, int32_t max_blocks,
                                         const int32_t* lens, const int32_t* new_tokens,
                                         int32_t batch, int32_t bs, int64_t* slots,
-                                        int32_t* lens_out, int32_t* cow_src, int32_t* cow_dst,
+                                        int64_t slot_capacity, int32_t* lens_out,
+                                        int32_t* cow_src, int32_t* cow_dst,
                                         int32_t* cow_count, int32_t* status,
                                         hipStream_t stream);
 hipError_t launch_blocks_release_shared(int32_t* stack, int32_t* top, int64_t capacity,

@@ -79,7 +79,7 @@ _SIGS = {
     "kvq_pool_init": (_i32, [_vp, _vp, _vp, _i64, _vp]),
     "kvq_blocks_fork": (_i32, [_vp, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _vp]),
     "kvq_blocks_reserve_shared": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
-                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+                                         _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kvq_blocks_release_shared": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                          _vp, _vp, _vp]),
     "kvq_copy_blocks": (_i32, [_LP, _CP, _vp, _vp, _vp, _i32, _vp]),
@@ -87,7 +87,7 @@ _SIGS = {
     "kvq_pack_blocks": (_i32, [_LP, _CP, _vp, _i32, _vp, _vp]),
     "kvq_unpack_blocks": (_i32, [_LP, _CP, _vp, _vp, _i32, _vp]),
     "kvq_blocks_reserve": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32,
-                                  _vp, _vp, _vp, _vp]),
+                                  _vp, _i64, _vp, _vp, _vp]),
     "kvq_blocks_release": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32,
                                   _vp, _vp, _vp]),
 }
@@ -199,10 +199,6 @@ def _need_rows(t, name, layout, T=None):
 
 def _nbytes(t):
     return t.numel() * t.element_size()
-
-
-def _capturing():
-    return torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
 
 
 def _stream(stream):
@@ -441,8 +437,11 @@ def kvq_pool_init(free_stack, free_top, initial_order=None, stream=None):
 def kvq_blocks_reserve(free_stack, free_top, block_tables, context_lens, new_tokens,
                        block_size, slot_mapping_out, status_flag,
                        context_lens_out=None, stream=None):
-    """slot_mapping_out: int64, at least sum(new_tokens) entries (checked on
-    the host when the stream is not being captured into a graph)."""
+    """slot_mapping_out: int64, at least sum(new_tokens) entries. Its length
+    goes to the library, which checks the count on the device: a short
+    buffer leaves everything unwritten and sets status_flag to
+    KVQ_ERR_INVALID_ARGUMENT (no host read of new_tokens, so no wait for the
+    device here)."""
     _need_pool(free_stack, free_top)
     _need(context_lens, "context_lens", torch.int32, ndim=1)
     B = context_lens.numel()
@@ -453,11 +452,6 @@ def kvq_blocks_reserve(free_stack, free_top, block_tables, context_lens, new_tok
     _need(slot_mapping_out, "slot_mapping_out", torch.int64, ndim=1)
     _need_status(status_flag)
     _need_lens_out(context_lens_out, B)
-    if B and not _capturing():
-        total = int(new_tokens.sum().item())
-        if slot_mapping_out.numel() < total:
-            raise ValueError(f"slot_mapping_out: {slot_mapping_out.numel()} entries, the "
-                             f"reservation writes {total}")
     _on_device(free_stack=free_stack, free_top=free_top, block_tables=block_tables,
                context_lens=context_lens, new_tokens=new_tokens,
                slot_mapping_out=slot_mapping_out, status_flag=status_flag,
@@ -465,7 +459,7 @@ def kvq_blocks_reserve(free_stack, free_top, block_tables, context_lens, new_tok
     _check("kvq_blocks_reserve", _lib.kvq_blocks_reserve(
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(new_tokens),
-        context_lens.numel(), block_size, _ptr(slot_mapping_out),
+        context_lens.numel(), block_size, _ptr(slot_mapping_out), slot_mapping_out.numel(),
         _ptr(context_lens_out), _ptr(status_flag), _stream(stream)))
 
 
@@ -525,11 +519,6 @@ def kvq_blocks_reserve_shared(free_stack, free_top, refcount, block_tables, cont
     _need(cow_count, "cow_count", torch.int32, min_numel=1)
     _need_status(status_flag)
     _need_lens_out(context_lens_out, B)
-    if B and not _capturing():
-        total = int(new_tokens.sum().item())
-        if slot_mapping_out.numel() < total:
-            raise ValueError(f"slot_mapping_out: {slot_mapping_out.numel()} entries, the "
-                             f"reservation writes {total}")
     _on_device(free_stack=free_stack, free_top=free_top, refcount=refcount,
                block_tables=block_tables, context_lens=context_lens, new_tokens=new_tokens,
                slot_mapping_out=slot_mapping_out, cow_src=cow_src, cow_dst=cow_dst,
@@ -537,8 +526,9 @@ def kvq_blocks_reserve_shared(free_stack, free_top, refcount, block_tables, cont
     _check("kvq_blocks_reserve_shared", _lib.kvq_blocks_reserve_shared(
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(refcount),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(new_tokens),
-        context_lens.numel(), block_size, _ptr(slot_mapping_out), _ptr(context_lens_out),
-        _ptr(cow_src), _ptr(cow_dst), _ptr(cow_count), _ptr(status_flag), _stream(stream)))
+        context_lens.numel(), block_size, _ptr(slot_mapping_out), slot_mapping_out.numel(),
+        _ptr(context_lens_out), _ptr(cow_src), _ptr(cow_dst), _ptr(cow_count),
+        _ptr(status_flag), _stream(stream)))
 
 
 def kvq_blocks_release_shared(free_stack, free_top, refcount, block_tables, context_lens,

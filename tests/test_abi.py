@@ -272,10 +272,12 @@ def test_sharing_calls_reject_bad_arguments_on_host():
     assert lib.kvq_blocks_fork(p, 64, p, 4, p, 2, p, p, 0, 16, None) == kq.KVQ_OK
     assert lib.kvq_blocks_fork(p, 64, None, 4, p, 2, p, p, 1, 16, None) == \
         kq.KVQ_ERR_INVALID_ARGUMENT
-    assert lib.kvq_blocks_reserve_shared(p, p, 64, p, p, 4, p, p, 2, 16, p, None, None, p, p, p,
-                                         None) == kq.KVQ_ERR_INVALID_ARGUMENT   # no copy pairs
-    assert lib.kvq_blocks_reserve_shared(p, p, 64, None, p, 4, p, p, 2, 16, p, None, p, p, p, p,
-                                         None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_blocks_reserve_shared(p, p, 64, p, p, 4, p, p, 2, 16, p, 8, None, None, p, p,
+                                         p, None) == kq.KVQ_ERR_INVALID_ARGUMENT   # no copy pairs
+    assert lib.kvq_blocks_reserve_shared(p, p, 64, None, p, 4, p, p, 2, 16, p, 8, None, p, p, p,
+                                         p, None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_blocks_reserve_shared(p, p, 64, p, p, 4, p, p, 2, 16, p, -1, None, p, p, p,
+                                         p, None) == kq.KVQ_ERR_INVALID_ARGUMENT   # slot count
     assert lib.kvq_blocks_release_shared(p, p, 0, p, p, 4, p, p, 2, 16, None, p, None) == \
         kq.KVQ_ERR_INVALID_ARGUMENT                                  # empty pool
     L = kq.make_layout(8, 128, 16, "int8")
@@ -309,9 +311,13 @@ def test_pool_calls_reject_bad_arguments_on_host():
     p = C.c_void_p(1 << 21)
     assert lib.kvq_pool_init(None, p, None, 16, None) == kq.KVQ_ERR_INVALID_ARGUMENT
     assert lib.kvq_pool_init(p, p, None, 0, None) == kq.KVQ_ERR_INVALID_ARGUMENT
-    assert lib.kvq_blocks_reserve(p, p, 16, p, 4, p, p, 2, 16, p, None, None,
+    assert lib.kvq_blocks_reserve(p, p, 16, p, 4, p, p, 2, 16, p, 8, None, None,
                                   None) == kq.KVQ_ERR_INVALID_ARGUMENT   # no status
-    assert lib.kvq_blocks_reserve(p, p, 16, None, 4, p, p, 2, 16, p, None, p,
+    assert lib.kvq_blocks_reserve(p, p, 16, None, 4, p, p, 2, 16, p, 8, None, p,
                                   None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_blocks_reserve(p, p, 16, p, 4, p, p, 2, 16, p, -1, None, p,
+                                  None) == kq.KVQ_ERR_INVALID_ARGUMENT   # negative slot count
+    assert lib.kvq_blocks_reserve(p, p, 16, p, 4, p, p, 2, 16, None, 8, None, p,
+                                  None) == kq.KVQ_ERR_INVALID_ARGUMENT   # slots without buffer
     assert lib.kvq_blocks_release(p, p, 16, p, 4, p, None, 2, 16, None, p,
                                   None) == kq.KVQ_ERR_INVALID_ARGUMENT

@@ -78,6 +78,72 @@ def test_pool_release_overflow_changes_nothing():
     assert int(gp.top.item()) == 4 and int(lens.item()) == 16
 
 
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("B", [7, 1500])
+def test_reserve_short_slot_buffer_changes_nothing(shared, B):
+    """A slot_mapping_out one entry short of sum(new_tokens) is refused on the
+    device: status KVQ_ERR_INVALID_ARGUMENT and no other byte written (stack,
+    top, tables, counts, lengths, slots, copy pairs), even when the pool is
+    also too small; the same call with the full buffer then matches the
+    oracle. B = 1500 spans two chunks of the kernel's scan."""
+    need_gpu()
+    rng = np.random.default_rng(B + 17 * shared)
+    bs, maxb, n = 16, 8, 4 * B
+    order = rng.permutation(n).astype(np.int32)
+    gp = GpuPool(n, B, maxb, order)
+    ostack, otop = ref.pool_init(n, order)
+    otab = np.full((B, maxb), -1, np.int32)
+    lens0 = np.zeros(B, np.int32)                    # empty sequences (valid tables)
+    new = rng.integers(1, 30, B).astype(np.int32)
+    total = int(new.sum())
+    glens = torch.from_numpy(lens0).to(DEV)
+    grc = torch.zeros(n, dtype=torch.int32, device=DEV)
+    cs = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    cd = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+
+    def call(slots, lens_dev, new_t):
+        if shared:
+            kq.kvq_blocks_reserve_shared(gp.stack, gp.top, grc, gp.tables, lens_dev, new_t, bs,
+                                         slots, cs, cd, cnt, gp.status, lens_dev)
+        else:
+            kq.kvq_blocks_reserve(gp.stack, gp.top, gp.tables, lens_dev, new_t, bs, slots,
+                                  gp.status, lens_dev)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.cpu().clone() for t in (gp.stack, gp.top, gp.tables, glens, grc, cs, cd, cnt)]
+
+    before = snapshot()
+    short = torch.full((total - 1,), -7, dtype=torch.int64, device=DEV)
+    call(short, glens, torch.from_numpy(new).to(DEV))
+    after = snapshot()
+    assert int(gp.status.item()) == kq.kvq.KVQ_ERR_INVALID_ARGUMENT
+    assert all(torch.equal(a, b) for a, b in zip(before, after))
+    assert (short.cpu() == -7).all()
+    # also too many blocks for the pool: the slot check still comes first
+    big = torch.full((B,), 64 * bs, dtype=torch.int32, device=DEV)
+    short2 = torch.full((64 * bs * B - 1,), -7, dtype=torch.int64, device=DEV)
+    call(short2, glens, big)
+    assert int(gp.status.item()) == kq.kvq.KVQ_ERR_INVALID_ARGUMENT
+    assert all(torch.equal(a, b) for a, b in zip(before, snapshot()))
+    # the full buffer: the reservation the oracle makes
+    olens = np.zeros(B, np.int32)
+    if shared:
+        orc = np.zeros(n, np.int32)
+        oslots, ost, _, _ = ref.blocks_reserve_shared(ostack, otop, orc, otab, lens0, new, bs,
+                                                      olens)
+    else:
+        oslots, ost = ref.blocks_reserve(ostack, otop, otab, lens0, new, bs, olens)
+    full = torch.full((total,), -7, dtype=torch.int64, device=DEV)
+    call(full, glens, torch.from_numpy(new).to(DEV))
+    torch.cuda.synchronize()
+    assert ost == 0 and int(gp.status.item()) == 0
+    assert np.array_equal(full.cpu().numpy(), oslots)
+    assert np.array_equal(gp.stack.cpu().numpy(), ostack)
+    assert int(gp.top.item()) == int(otop[0])
+
+
 @pytest.mark.parametrize("B,window,sink", [(1500, 40, 20), (3, 70, 0), (1100, 1, 33)])
 def test_trim_large_batches_match_oracle(B, window, sink):
     """Trim after placing long contexts: chunks of 1024 rows, many more
