@@ -113,6 +113,22 @@ def test_prefill_single_queries_match_decode(code, mode):
     assert torch.allclose(got, dec, atol=2e-3, rtol=1e-3)
 
 
+@pytest.mark.parametrize("code", ["fp8", "int8"])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("split", [0, 2])
+def test_prefill_checks_new_tokens_g8(code, bs, split):
+    """The shape of checking several new tokens at once on the 70B model: 8
+    queries per sequence, 8 query heads per KV head (4 column tiles, the
+    two-wave LDS kernel), d 128, lengths across many 32-token chunks and
+    the library's split rule or 2-block splits (an even split count, so the
+    grid's extra split is there)."""
+    need_gpu()
+    lens = (1000, 333, 8, 2049, 64, 517)
+    w, L, LL, s, q, qs = _setup(code, d=128, bs=bs, G=8, lens=lens, nq=(8,) * len(lens))
+    got, exp = _run(w, L, LL, s, q, qs, split_blocks=split)
+    assert_decode_close(got, exp, f"{code} bs{bs} split {split}")
+
+
 def test_prefill_chunk_of_a_long_prompt_sampled():
     """A 512-token prompt chunk at the end of a 4096-token context, 64 query /
     8 KV heads, d 128, FP8: the whole GPU output, checked against the oracle
