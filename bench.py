@@ -201,7 +201,7 @@ def append_bytes_per_token(w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

@@ -101,7 +101,7 @@ extern "C" {
 typedef int32_t kvq_status;
 #define KVQ_OK 0
 #define KVQ_ERR_INVALID_ARGUMENT (-1)    /* bad pointer, size, enum or shape     */
-#define KVQ_ERR_UNSUPPORTED (-2)         /* valid request this build lacks        */
+#define KVQ_ERR_UNSUPPORTED (-2)         /* valid request the library lacks       */
 #define KVQ_ERR_WORKSPACE_TOO_SMALL (-3) /* decode workspace below required size */
 #define KVQ_ERR_HIP (-4)                 /* a HIP launch or runtime call failed   */
 #define KVQ_ERR_OUT_OF_BLOCKS (-5)       /* pool cannot serve a reservation       */
@@ -198,7 +198,7 @@ const char* kvq_status_string(kvq_status status);
 
 /* Checks a layout without touching the device: KVQ_OK, or
  * KVQ_ERR_INVALID_ARGUMENT for malformed fields, or KVQ_ERR_UNSUPPORTED for a
- * well-formed combination this build does not implement. */
+ * well-formed combination the library does not implement. */
 kvq_status kvq_layout_check(const kvq_layout* layout);
 
 /* Cache bytes per token over num_layers layers ("KV Cache Optimization"
