@@ -220,7 +220,7 @@ def main():
         extras = {}
         for name in EXTRA_WORKLOADS:
             sub = argparse.Namespace(**vars(args))
-            sub.steps, sub.warmup, sub.no_cpu_baseline = min(args.steps, 10), 2, True
+            sub.steps, sub.warmup, sub.no_cpu_baseline = min(args.steps, 10), 4, True
             torch.cuda.empty_cache()
             r = run(sub, name)
             extras[name] = {k: r[k] for k in ("value", "ms_per_step", "pct_of_hbm_peak",
