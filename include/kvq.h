@@ -48,6 +48,9 @@
  *   kvq_copy_blocks       prefix sharing: reference-counted blocks, copy on
  *                         write of a shared, partly filled block (same
  *                         section, prefix caching).
+ *   kvq_check_block_tables / kvq_check_slots
+ *                         debugging aids: report block ids and slots outside
+ *                         the pool through a status word.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -66,7 +69,9 @@
  *    breaking one gives unspecified results. Decode and multi-query attention
  *    never read outside the cache planes: a block id outside
  *    [0, num_blocks) is read as block 0 (its positions then count with block
- *    0's data), and no error is reported.
+ *    0's data), and no error is reported. kvq_check_block_tables and
+ *    kvq_check_slots report such values (a debugging aid, run on the device
+ *    with no trap).
  *  - Alignment: every device pointer must be 16-byte aligned and every row
  *    stride must keep rows 16-byte aligned.
  *  - Inputs must be finite.
@@ -472,6 +477,33 @@ kvq_status kvq_blocks_trim(int32_t* free_stack, int32_t* free_top, int64_t pool_
                            int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t window, int32_t sink,
                            int32_t batch, int32_t block_size, int32_t* status_flag,
+                           void* stream);
+
+/* Debugging aids for the block map the attention calls read ("Dynamic KV
+ * Cache Quantization for Fast LLM Inference", section "Integrating Dynamic
+ * Quantization with PagedAttention": a table maps each sequence's logical
+ * blocks to physical ones). Block ids and slots live in device arrays that
+ * the host does not read; these calls check them on the device, with no
+ * trap, and report through device words.
+ *
+ * kvq_check_block_tables: every entry block_tables[b][k] with
+ * k < ceil(context_lens[b] / bs) must lie in [0, num_blocks), and every
+ * context_lens[b] in [0, max_blocks_per_seq * bs]. *first_bad (device int64)
+ * gets the smallest flat index b * max_blocks_per_seq + k of an entry that
+ * breaks this (a length outside its range counts at k = 0), or -1;
+ * *status_flag (device int32) gets KVQ_ERR_INVALID_ARGUMENT or KVQ_OK. One
+ * workgroup, so the answer does not depend on timing; intended for debug
+ * builds of a serving loop (it reads the whole table). */
+kvq_status kvq_check_block_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t batch,
+                                  int32_t block_size, int64_t num_blocks, int64_t* first_bad,
+                                  int32_t* status_flag, void* stream);
+
+/* kvq_check_slots: every slot_mapping[t], t < num_tokens, must be -1 (skip)
+ * or lie in [0, num_blocks * block_size). Reports as kvq_check_block_tables
+ * (first_bad = the smallest bad t, or -1). */
+kvq_status kvq_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                           int32_t block_size, int64_t* first_bad, int32_t* status_flag,
                            void* stream);
 
 /* Fork k (k < num_forks): row dst_rows[k] takes row src_rows[k]'s length and

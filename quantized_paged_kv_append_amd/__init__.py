@@ -10,7 +10,8 @@ from .kvq import (  # noqa: F401
     kvq_blocks_fork, kvq_blocks_release,
     kvq_block_pack_bytes, kvq_blocks_release_shared, kvq_blocks_reserve_shared, kvq_blocks_trim,
     kvq_copy_blocks, kvq_pack_blocks, kvq_unpack_blocks, kvq_blocks_reserve,
-    kvq_bytes_per_token, kvq_cache_plane_bytes, kvq_decode_attention,
+    kvq_bytes_per_token, kvq_cache_plane_bytes, kvq_check_block_tables, kvq_check_slots,
+    kvq_decode_attention,
     kvq_decode_attention_noalloc,
     kvq_decode_workspace_bytes, kvq_layout_check, kvq_pool_init, kvq_prefill_attention,
     kvq_prefill_workspace_bytes,

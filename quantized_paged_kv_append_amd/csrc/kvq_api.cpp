@@ -602,6 +602,31 @@ kvq_status kvq_blocks_release(int32_t* free_stack, int32_t* free_top, int64_t po
       static_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_check_block_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t batch,
+                                  int32_t block_size, int64_t num_blocks, int64_t* first_bad,
+                                  int32_t* status_flag, void* stream) {
+  if (!first_bad || !status_flag || batch < 0 || max_blocks_per_seq < 1 || block_size < 1 ||
+      num_blocks < 1)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (!block_tables || !context_lens)) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_check_tables(block_tables, max_blocks_per_seq, context_lens,
+                                             batch, block_size, num_blocks, first_bad,
+                                             status_flag, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                           int32_t block_size, int64_t* first_bad, int32_t* status_flag,
+                           void* stream) {
+  if (!first_bad || !status_flag || num_tokens < 0 || num_blocks < 1 || block_size < 1 ||
+      num_blocks > INT64_MAX / block_size)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 0 && !slot_mapping) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(kvq::launch_check_slots(slot_mapping, num_tokens, num_blocks, block_size,
+                                            first_bad, status_flag,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 kvq_status kvq_blocks_trim(int32_t* free_stack, int32_t* free_top, int64_t pool_capacity,
                            int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t window, int32_t sink,

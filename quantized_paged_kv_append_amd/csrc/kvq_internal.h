@@ -144,5 +144,10 @@ hipError_t launch_blocks_release(int32_t* stack, int32_t* top,
                                  const int32_t* mask, int32_t batch, int32_t bs,
                                  int32_t* lens_out, int32_t* status,
                                  hipStream_t stream);
+hipError_t launch_check_tables(const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                               int32_t batch, int32_t bs, int64_t num_blocks, int64_t* first_bad,
+                               int32_t* status, hipStream_t stream);
+hipError_t launch_check_slots(const int64_t* slots, int64_t n, int64_t num_blocks, int32_t bs,
+                              int64_t* first_bad, int32_t* status, hipStream_t stream);
 
 }  // namespace kvq

@@ -635,7 +635,77 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyPlanes cp, const i
   for (int64_t i = threadIdx.x; i < per / 16; i += blockDim.x) to[i] = from[i];
 }
 
+// Debug checks of the caller's tables and slots (one workgroup, so the
+// smallest offending index comes from a block-wide minimum: no atomics, the
+// same answer every run).
+__device__ int64_t block_min_i64(int64_t v, int64_t* sh) {
+  constexpr int kWaves = kThreads / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v = min(v, (int64_t)__shfl_xor(v, off));
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  int64_t m = lane < kWaves ? sh[lane] : INT64_MAX;
+#pragma unroll
+  for (int off = 1; off < kWaves; off <<= 1) m = min(m, (int64_t)__shfl_xor(m, off));
+  return m;
+}
+
+__global__ __launch_bounds__(kThreads) void check_tables_kernel(
+    const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t batch, int32_t bs,
+    int64_t num_blocks, int64_t* first_bad, int32_t* status) {
+  __shared__ int64_t sh[kThreads / kWave];
+  int64_t best = INT64_MAX;
+  const int64_t total = (int64_t)batch * max_blocks;
+  for (int64_t f = threadIdx.x; f < total; f += kThreads) {
+    const int64_t b = f / max_blocks, k = f % max_blocks;
+    const int64_t L = lens[b];
+    bool bad;
+    if (L < 0 || L > (int64_t)max_blocks * bs) {
+      bad = k == 0;   // the length itself: reported at the row's first entry
+    } else {
+      const int32_t id = tables[f];
+      bad = k < ceil_div(L, bs) && (id < 0 || id >= num_blocks);
+    }
+    if (bad) best = min(best, f);
+  }
+  best = block_min_i64(best, sh);
+  if (threadIdx.x == 0) {
+    *first_bad = best == INT64_MAX ? -1 : best;
+    *status = best == INT64_MAX ? KVQ_OK : KVQ_ERR_INVALID_ARGUMENT;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void check_slots_kernel(
+    const int64_t* slots, int64_t n, int64_t limit, int64_t* first_bad, int32_t* status) {
+  __shared__ int64_t sh[kThreads / kWave];
+  int64_t best = INT64_MAX;
+  for (int64_t t = threadIdx.x; t < n; t += kThreads) {
+    const int64_t s = slots[t];
+    if (s < -1 || s >= limit) best = min(best, t);
+  }
+  best = block_min_i64(best, sh);
+  if (threadIdx.x == 0) {
+    *first_bad = best == INT64_MAX ? -1 : best;
+    *status = best == INT64_MAX ? KVQ_OK : KVQ_ERR_INVALID_ARGUMENT;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_check_tables(const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                               int32_t batch, int32_t bs, int64_t num_blocks, int64_t* first_bad,
+                               int32_t* status, hipStream_t stream) {
+  check_tables_kernel<<<1, kThreads, 0, stream>>>(tables, max_blocks, lens, batch, bs,
+                                                  num_blocks, first_bad, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_slots(const int64_t* slots, int64_t n, int64_t num_blocks, int32_t bs,
+                              int64_t* first_bad, int32_t* status, hipStream_t stream) {
+  check_slots_kernel<<<1, kThreads, 0, stream>>>(slots, n, num_blocks * bs, first_bad, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_pool_init(int32_t* stack, int32_t* top, const int32_t* order,
                             int64_t n, hipStream_t stream) {

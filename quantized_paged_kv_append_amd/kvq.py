@@ -90,6 +90,8 @@ _SIGS = {
                                   _vp, _i64, _vp, _vp, _vp]),
     "kvq_blocks_release": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32,
                                   _vp, _vp, _vp]),
+    "kvq_check_block_tables": (_i32, [_vp, _i32, _vp, _i32, _i32, _i64, _vp, _vp, _vp]),
+    "kvq_check_slots": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -583,6 +585,39 @@ def kvq_blocks_trim(free_stack, free_top, block_tables, context_lens, window, si
         _ptr(free_stack), _ptr(free_top), free_stack.numel(), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), int(window), int(sink),
         context_lens.numel(), block_size, _ptr(status_flag), _stream(stream)))
+
+
+def kvq_check_block_tables(block_tables, context_lens, block_size, num_blocks, first_bad,
+                           status_flag, stream=None):
+    """Debugging aid: status_flag (device int32 [1]) gets KVQ_OK, or
+    KVQ_ERR_INVALID_ARGUMENT when a table entry a context uses lies outside
+    [0, num_blocks) or a length outside [0, max_blocks * block_size);
+    first_bad (device int64 [1]) gets the smallest flat index b * max_blocks
+    + k of such an entry, or -1."""
+    _need(context_lens, "context_lens", torch.int32, ndim=1)
+    _need(block_tables, "block_tables", torch.int32, ndim=2)
+    if block_tables.shape[0] < context_lens.numel():
+        raise ValueError("block_tables: fewer rows than context_lens")
+    _need(first_bad, "first_bad", torch.int64, numel=1)
+    _need_status(status_flag)
+    _on_device(block_tables=block_tables, context_lens=context_lens, first_bad=first_bad,
+               status_flag=status_flag)
+    _check("kvq_check_block_tables", _lib.kvq_check_block_tables(
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), context_lens.numel(),
+        block_size, int(num_blocks), _ptr(first_bad), _ptr(status_flag), _stream(stream)))
+
+
+def kvq_check_slots(slot_mapping, num_blocks, block_size, first_bad, status_flag, stream=None):
+    """Debugging aid: every slot must be -1 or lie in [0, num_blocks *
+    block_size); reports as kvq_check_block_tables (first_bad = the smallest
+    bad token index, or -1)."""
+    _need(slot_mapping, "slot_mapping", torch.int64, ndim=1)
+    _need(first_bad, "first_bad", torch.int64, numel=1)
+    _need_status(status_flag)
+    _on_device(slot_mapping=slot_mapping, first_bad=first_bad, status_flag=status_flag)
+    _check("kvq_check_slots", _lib.kvq_check_slots(
+        _ptr(slot_mapping), slot_mapping.numel(), int(num_blocks), block_size, _ptr(first_bad),
+        _ptr(status_flag), _stream(stream)))
 
 
 def kvq_block_pack_bytes(layout) -> int:

@@ -321,3 +321,18 @@ def test_pool_calls_reject_bad_arguments_on_host():
                                   None) == kq.KVQ_ERR_INVALID_ARGUMENT   # slots without buffer
     assert lib.kvq_blocks_release(p, p, 16, p, 4, p, None, 2, 16, None, p,
                                   None) == kq.KVQ_ERR_INVALID_ARGUMENT
+
+
+def test_check_calls_reject_bad_arguments_on_host():
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+    bad = kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_check_block_tables(p, 4, p, 2, 16, 100, None, p, None) == bad   # no first_bad
+    assert lib.kvq_check_block_tables(p, 4, p, 2, 16, 100, p, None, None) == bad   # no status
+    assert lib.kvq_check_block_tables(p, 4, p, 2, 16, 0, p, p, None) == bad        # empty pool
+    assert lib.kvq_check_block_tables(None, 4, p, 2, 16, 100, p, p, None) == bad
+    assert lib.kvq_check_block_tables(p, 0, p, 2, 16, 100, p, p, None) == bad
+    assert lib.kvq_check_slots(p, 8, 100, 16, p, None, None) == bad
+    assert lib.kvq_check_slots(None, 8, 100, 16, p, p, None) == bad
+    assert lib.kvq_check_slots(p, -1, 100, 16, p, p, None) == bad
+    assert lib.kvq_check_slots(p, 8, 100, 0, p, p, None) == bad
