@@ -591,7 +591,7 @@ def kvq_check_block_tables(block_tables, context_lens, block_size, num_blocks, f
                            status_flag, stream=None):
     """Debugging aid: status_flag (device int32 [1]) gets KVQ_OK, or
     KVQ_ERR_INVALID_ARGUMENT when a table entry a context uses lies outside
-    [0, num_blocks) or a length outside [0, max_blocks * block_size);
+    [0, num_blocks) or a length outside [0, max_blocks * block_size];
     first_bad (device int64 [1]) gets the smallest flat index b * max_blocks
     + k of such an entry, or -1."""
     _need(context_lens, "context_lens", torch.int32, ndim=1)
