@@ -233,13 +233,14 @@ __device__ __forceinline__ Nib4Consts nib4_consts() {
   return k;
 }
 
-// Per-token scores of one tile before the column scale: the score MFMAs
-// (chunk c = slice c; one accumulator per 32-element group for asymmetric
-// codes) and, for token 4j + e, the sum over groups c of S[c][e] times the
-// key scale of (token e, group c), held by lane SG e + c of the row.
-template <int D, int MODE>
-__device__ __forceinline__ void tile4_scores(const Tile4<D, MODE>& t, const half8v* qop,
-                                             const Nib4Consts& kc, float* v) {
+// Per-token scores of one tile before the column scale, for NC column sets
+// (qop[cc], v[cc]) that share the key conversion: the score MFMAs (chunk c =
+// slice c; one accumulator per 32-element group for asymmetric codes) and,
+// for token 4j + e, the sum over groups c of S[c][e] times the key scale of
+// (token e, group c), held by lane SG e + c of the row.
+template <int D, int MODE, int NC>
+__device__ __forceinline__ void tile4_scores(const Tile4<D, MODE>& t, const half8v (*qop)[D / 32],
+                                             const Nib4Consts& kc, float (*v)[4]) {
   constexpr int NS = D / 32;
   constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
   uint32_t g[4];
@@ -249,9 +250,11 @@ __device__ __forceinline__ void tile4_scores(const Tile4<D, MODE>& t, const half
     g[0] = __builtin_amdgcn_perm(t.k[1], t.k[0], 0x06040200u);
     g[1] = __builtin_amdgcn_perm(t.k[1], t.k[0], 0x07050301u);
   }
-  float4v S[ASYM ? NS : 1];
+  float4v S[NC][ASYM ? NS : 1];
 #pragma unroll
-  for (int c = 0; c < (ASYM ? NS : 1); ++c) S[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int c = 0; c < (ASYM ? NS : 1); ++c) S[cc][c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NS; ++c) {
     uint32_t gc = g[c];
@@ -268,15 +271,21 @@ __device__ __forceinline__ void tile4_scores(const Tile4<D, MODE>& t, const half
     half8v ka;
     ka[0] = h0[0]; ka[1] = h0[1]; ka[2] = h1[0]; ka[3] = h1[1];
     ka[4] = h2[0]; ka[5] = h2[1]; ka[6] = h3[0]; ka[7] = h3[1];
-    S[ASYM ? c : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[c], S[ASYM ? c : 0], 0, 0, 0);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      S[cc][ASYM ? c : 0] =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[cc][c], S[cc][ASYM ? c : 0], 0, 0, 0);
   }
-  if constexpr (ASYM) {
-    combine_groups(S, t.sk, v, std::integral_constant<int, NS>{});
-  } else {
-    static_for<0, 4>([&](auto E) {
-      constexpr int e = decltype(E)::value;
-      v[e] = row_bcast<e>(t.sk) * S[0][e];
-    });
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    if constexpr (ASYM) {
+      combine_groups(S[cc], t.sk, v[cc], std::integral_constant<int, NS>{});
+    } else {
+      static_for<0, 4>([&](auto E) {
+        constexpr int e = decltype(E)::value;
+        v[cc][e] = row_bcast<e>(t.sk) * S[cc][0][e];
+      });
+    }
   }
 }
 
@@ -347,107 +356,151 @@ __device__ __forceinline__ float softmax_update(const float* s, SoftmaxState<D>&
   return msafe;
 }
 
-// One 16-token tile. TAIL: token t of the tile counts for this lane's column
-// only if t < L and (t >= lo or t < sk) -- the causal limit, and the window
-// start and sink count of a windowed column (lo = sk = 0 without a window).
-template <int D, int MODE, bool TAIL>
-__device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, int L,
-                                           const half8v* qop, float cscore, int j,
-                                           SoftmaxState<D>& st, const Nib4Consts& kc,
-                                           int lo = 0, int sk = 0) {
+// One 16-token tile for NC column sets (cc: qop[cc], cscore[cc], st[cc],
+// limits L[cc], lo[cc]) sharing the code conversions. TAIL: token t of the
+// tile counts for this lane's column of set cc only if t < L[cc] and (t >=
+// lo[cc] or t < sk) -- the causal limit, and the window start and sink count
+// of a windowed column (lo = sk = 0 without a window).
+template <int D, int MODE, int NC, bool TAIL>
+__device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, const int* L,
+                                           const half8v (*qop)[D / 32], const float* cscore,
+                                           int j, SoftmaxState<D>* st, const Nib4Consts& kc,
+                                           const int* lo, int sk) {
   constexpr int NS = D / 32;
   constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
   constexpr int SG = Tile4<D, MODE>::SG;
-  float v[4], s[4];
-  tile4_scores(t, qop, kc, v);
+  float v[NC][4];
+  tile4_scores<D, MODE, NC>(t, qop, kc, v);
   // Masks that differ between the lanes of a row (per-column limits) must
   // not guard a row-broadcast read: the compiler would move the read under
   // the mask, and a lane whose source lane is masked off reads 0. The empty
   // barriers keep every broadcast ahead of the selects, under the full wave.
-  if constexpr (TAIL) asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
-  bool ok[4];
+  if constexpr (TAIL)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int tk = pos0 + 4 * j + e;
-    ok[e] = !TAIL || (tk < L && (tk >= lo || tk < sk));
+    for (int cc = 0; cc < NC; ++cc)
+      asm volatile("" : "+v"(v[cc][0]), "+v"(v[cc][1]), "+v"(v[cc][2]), "+v"(v[cc][3]));
+  bool ok[NC][4];
+  float p[NC][4];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    float s[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tk = pos0 + 4 * j + e;
+      ok[cc][e] = !TAIL || (tk < L[cc] && (tk >= lo[cc] || tk < sk));
+      s[e] = ok[cc][e] ? v[cc][e] * cscore[cc] : -INFINITY;
+    }
+    const float msafe = softmax_update<D, 4>(s, st[cc]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[cc][e] = ok[cc][e] ? __builtin_amdgcn_exp2f(s[e] - msafe) : 0.0f;
+    st[cc].l += (p[cc][0] + p[cc][1]) + (p[cc][2] + p[cc][3]);
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) s[e] = ok[e] ? v[e] * cscore : -INFINITY;
-  const float msafe = softmax_update<D, 4>(s, st);
-  float p[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) p[e] = ok[e] ? __builtin_amdgcn_exp2f(s[e] - msafe) : 0.0f;
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
   uint32_t G[4], Z[4] = {0u, 0u, 0u, 0u};
   tile4_vbytes(t, G, Z);
   static_for<0, NS>([&](auto I) {
     constexpr int i = decltype(I)::value;
-    float sb[4], pv[4];
+    float sb[4];
     static_for<0, 4>([&](auto E) {
       constexpr int e = decltype(E)::value;
       sb[e] = row_bcast<SG * e + (ASYM ? i : 0)>(t.sv);
     });
     if constexpr (TAIL) asm volatile("" : "+v"(sb[0]), "+v"(sb[1]), "+v"(sb[2]), "+v"(sb[3]));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = ok[e] ? sb[e] * p[e] : 0.0f;
-    half4v pop;
-    pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
     const VWords4 w = vgroup_words<ASYM>(G[i], Z[i], kc);
     const half4v va0 = __builtin_bit_cast(half4v, (u32x2){w.x[0], w.x[1]});
     const half4v va1 = __builtin_bit_cast(half4v, (u32x2){w.y[0], w.y[1]});
     const half4v corr = __builtin_bit_cast(half4v, (u32x2){w.c[0], w.c[1]});
-    st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va0, pop, st.acc[2 * i], 0, 0, 0);
-    st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(va1, pop, st.acc[2 * i + 1], 0, 0, 0);
-    st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(corr, pop, st.acc[2 * i], 0, 0, 0);
-    st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(corr, pop, st.acc[2 * i + 1], 0, 0, 0);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] = ok[cc][e] ? sb[e] * p[cc][e] : 0.0f;
+      half4v pop;
+      pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
+      float4v* acc = st[cc].acc;
+      acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va0, pop, acc[2 * i], 0, 0, 0);
+      acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(va1, pop, acc[2 * i + 1], 0, 0, 0);
+      acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(corr, pop, acc[2 * i], 0, 0, 0);
+      acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(corr, pop, acc[2 * i + 1], 0, 0, 0);
+    }
   });
 }
+// One column set (decode).
+template <int D, int MODE, bool TAIL>
+__device__ __forceinline__ void tile4_step(const Tile4<D, MODE>& t, int pos0, int L,
+                                           const half8v* qop, float cscore, int j,
+                                           SoftmaxState<D>& st, const Nib4Consts& kc,
+                                           int lo = 0, int sk = 0) {
+  tile4_step<D, MODE, 1, TAIL>(t, pos0, &L, reinterpret_cast<const half8v(*)[D / 32]>(qop),
+                               &cscore, j, &st, kc, &lo, sk);
+}
 
-// Two consecutive whole tiles (32 tokens) in one step: one softmax update
-// for both, and the PV products on 16x16x32 MFMAs whose contraction runs over
-// the 32 tokens (k = 8j + 4T + e' for tile T, token 4j + e' in the order
-// 0, 2, 1, 3, the same in the value and probability operands).
-template <int D, int MODE>
+// Two consecutive whole tiles (32 tokens) in one step, for NC column sets
+// sharing the code conversions: one softmax update per set for both tiles,
+// and the PV products on 16x16x32 MFMAs whose contraction runs over the 32
+// tokens (k = 8j + 4T + e' for tile T, token 4j + e' in the order 0, 2, 1, 3,
+// the same in the value and probability operands).
+template <int D, int MODE, int NC>
 __device__ __forceinline__ void tile4_pair_step(const Tile4<D, MODE>& t0, const Tile4<D, MODE>& t1,
-                                                const half8v* qop, float cscore,
-                                                SoftmaxState<D>& st, const Nib4Consts& kc) {
+                                                const half8v (*qop)[D / 32], const float* cscore,
+                                                SoftmaxState<D>* st, const Nib4Consts& kc) {
   constexpr int NS = D / 32;
   constexpr bool ASYM = MODE == KVQ_SCALE_GROUP_ASYM;
   constexpr int SG = Tile4<D, MODE>::SG;
-  float v[8], s[8];
-  tile4_scores(t0, qop, kc, v);
-  tile4_scores(t1, qop, kc, v + 4);
+  float v0[NC][4], v1[NC][4];
+  tile4_scores<D, MODE, NC>(t0, qop, kc, v0);
+  tile4_scores<D, MODE, NC>(t1, qop, kc, v1);
+  float p[NC][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = v[e] * cscore;
-  const float msafe = softmax_update<D, 8>(s, st);
-  float p[8];
+  for (int cc = 0; cc < NC; ++cc) {
+    float s[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - msafe);
-  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    for (int e = 0; e < 4; ++e) {
+      s[e] = v0[cc][e] * cscore[cc];
+      s[4 + e] = v1[cc][e] * cscore[cc];
+    }
+    const float msafe = softmax_update<D, 8>(s, st[cc]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[cc][e] = __builtin_amdgcn_exp2f(s[e] - msafe);
+    st[cc].l += ((p[cc][0] + p[cc][1]) + (p[cc][2] + p[cc][3])) +
+                ((p[cc][4] + p[cc][5]) + (p[cc][6] + p[cc][7]));
+  }
   uint32_t G0[4], Z0[4] = {0u, 0u, 0u, 0u}, G1[4], Z1[4] = {0u, 0u, 0u, 0u};
   tile4_vbytes(t0, G0, Z0);
   tile4_vbytes(t1, G1, Z1);
   static_for<0, NS>([&](auto I) {
     constexpr int i = decltype(I)::value;
-    float pv[8];
-    static_for<0, 4>([&](auto E) {
-      constexpr int e = decltype(E)::value;
-      pv[e] = row_bcast<SG * e + (ASYM ? i : 0)>(t0.sv) * p[e];
-      pv[4 + e] = row_bcast<SG * e + (ASYM ? i : 0)>(t1.sv) * p[4 + e];
-    });
-    half8v pop;
-    pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
-    pop[4] = (half_t)pv[4]; pop[5] = (half_t)pv[6]; pop[6] = (half_t)pv[5]; pop[7] = (half_t)pv[7];
     const VWords4 w0 = vgroup_words<ASYM>(G0[i], Z0[i], kc);
     const VWords4 w1 = vgroup_words<ASYM>(G1[i], Z1[i], kc);
     const half8v va0 = __builtin_bit_cast(half8v, (u32x4){w0.x[0], w0.x[1], w1.x[0], w1.x[1]});
     const half8v va1 = __builtin_bit_cast(half8v, (u32x4){w0.y[0], w0.y[1], w1.y[0], w1.y[1]});
     const half8v corr = __builtin_bit_cast(half8v, (u32x4){w0.c[0], w0.c[1], w1.c[0], w1.c[1]});
-    st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0, pop, st.acc[2 * i], 0, 0, 0);
-    st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va1, pop, st.acc[2 * i + 1], 0, 0, 0);
-    st.acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(corr, pop, st.acc[2 * i], 0, 0, 0);
-    st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(corr, pop, st.acc[2 * i + 1], 0, 0, 0);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      // the row broadcast folds into each multiply (v_mul_f32_dpp)
+      float pv[8];
+      static_for<0, 4>([&](auto E) {
+        constexpr int e = decltype(E)::value;
+        pv[e] = row_bcast<SG * e + (ASYM ? i : 0)>(t0.sv) * p[cc][e];
+        pv[4 + e] = row_bcast<SG * e + (ASYM ? i : 0)>(t1.sv) * p[cc][4 + e];
+      });
+      half8v pop;
+      pop[0] = (half_t)pv[0]; pop[1] = (half_t)pv[2]; pop[2] = (half_t)pv[1]; pop[3] = (half_t)pv[3];
+      pop[4] = (half_t)pv[4]; pop[5] = (half_t)pv[6]; pop[6] = (half_t)pv[5]; pop[7] = (half_t)pv[7];
+      float4v* acc = st[cc].acc;
+      acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0, pop, acc[2 * i], 0, 0, 0);
+      acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va1, pop, acc[2 * i + 1], 0, 0, 0);
+      acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(corr, pop, acc[2 * i], 0, 0, 0);
+      acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(corr, pop, acc[2 * i + 1], 0, 0, 0);
+    }
   });
+}
+// One column set (decode).
+template <int D, int MODE>
+__device__ __forceinline__ void tile4_pair_step(const Tile4<D, MODE>& t0, const Tile4<D, MODE>& t1,
+                                                const half8v* qop, float cscore,
+                                                SoftmaxState<D>& st, const Nib4Consts& kc) {
+  tile4_pair_step<D, MODE, 1>(t0, t1, reinterpret_cast<const half8v(*)[D / 32]>(qop), &cscore,
+                              &st, kc);
 }
 
 // Query operand for 4-bit keys: chunk c holds elements 32 c + 8 j + perm8[p]

@@ -45,19 +45,21 @@ struct PrefillArgs {
 // NC: 16-column tiles per wave. With NC = 2 a block's codes are loaded and
 // converted once for 32 columns (per-channel keys keep NC = 1: their
 // per-block query folding needs the fp32 query of every column).
-// A wave's share of a split over 4-bit codes for one column tile: the
+// A wave's share of a split over 4-bit codes for its NC column tiles: the
 // visible blocks as positions [x0, x1) in the sink blocks A = [s0, s0 + nA)
 // then the window's blocks from bstart. Blocks seen whole by every column
 // stream through a four-tile register ring in pairs of tiles; the others
 // (sink blocks, the window's first blocks, the context's last one or two)
 // go tile by tile with this lane's column masks (limit Lr, window start lo,
 // sink count).
-template <int D, int BS, int MODE>
+template <int D, int BS, int MODE, int NC>
 __device__ __forceinline__ void prefill_blocks_int4(const PrefillArgs& pa, int b, int g, int L,
                                                     int s0, int x0, int x1, int nA, int bstart,
                                                     int Lmin, int Lmax, int lo_min, int lo_max,
-                                                    int Lr, int lo, const half8v* qop,
-                                                    float cscore, int lane, SoftmaxState<D>& st) {
+                                                    const int* Lr, const int* lo,
+                                                    const half8v (*qop)[D / 32],
+                                                    const float* cscore, int lane,
+                                                    SoftmaxState<D>* st) {
   constexpr int TPB = BS / 16;  // tiles per block
   constexpr int NBUF = 4;       // tiles in the ring: two pairs
   const DecodeArgs& a = pa.a;
@@ -90,9 +92,9 @@ __device__ __forceinline__ void prefill_blocks_int4(const PrefillArgs& pa, int b
         Tile4<D, MODE> t;
         load_tile4<D, BS, MODE>(t, a, bh, nt, lo4);
         if (masked)
-          tile4_step<D, MODE, true>(t, pos0, Lr, qop, cscore, jj, st, kc, lo, SK);
+          tile4_step<D, MODE, NC, true>(t, pos0, Lr, qop, cscore, jj, st, kc, lo, SK);
         else
-          tile4_step<D, MODE, false>(t, pos0, Lr, qop, cscore, jj, st, kc);
+          tile4_step<D, MODE, NC, false>(t, pos0, Lr, qop, cscore, jj, st, kc, lo, SK);
       }
     }
   };
@@ -112,16 +114,17 @@ __device__ __forceinline__ void prefill_blocks_int4(const PrefillArgs& pa, int b
     for (int u = 0; u < NBUF; ++u) load(buf[u], T0 + u);
     int tt = T0;
     for (; tt + NBUF <= T1; tt += NBUF) {
-      tile4_pair_step<D, MODE>(buf[0], buf[1], qop, cscore, st, kc);
+      tile4_pair_step<D, MODE, NC>(buf[0], buf[1], qop, cscore, st, kc);
       load(buf[0], tt + NBUF);
       load(buf[1], tt + NBUF + 1);
-      tile4_pair_step<D, MODE>(buf[2], buf[3], qop, cscore, st, kc);
+      tile4_pair_step<D, MODE, NC>(buf[2], buf[3], qop, cscore, st, kc);
       load(buf[2], tt + NBUF + 2);
       load(buf[3], tt + NBUF + 3);
     }
 #pragma unroll
     for (int u = 0; u < NBUF; ++u)
-      if (tt + u < T1) tile4_step<D, MODE, false>(buf[u], (tt + u) * 16, L, qop, cscore, jj, st, kc);
+      if (tt + u < T1)
+        tile4_step<D, MODE, NC, false>(buf[u], (tt + u) * 16, Lr, qop, cscore, jj, st, kc, lo, SK);
   }
   edge_run(rb, b1);
 }
@@ -137,7 +140,6 @@ void prefill_split_kernel(PrefillArgs pa) {
   constexpr bool RAW = CODE == KVQ_CODE_NONE16;
   constexpr bool I4 = CODE == KVQ_CODE_INT4;
   static_assert(!KCH || NC == 1, "per-channel keys take one column tile per wave");
-  static_assert(!I4 || NC == 1, "4-bit codes take one column tile per wave");
   using TileT = typename std::conditional<RAW, TileRaw<D, BS>, Tile8<D, BS>>::type;
   __shared__ float red[kNW][NV + 2][kWave];
   const DecodeArgs& a = pa.a;
@@ -252,9 +254,9 @@ void prefill_split_kernel(PrefillArgs pa) {
   }
 
   if constexpr (I4) {
-    if (x0 < x1) prefill_blocks_int4<D, BS, MODE>(pa, b, g, L, s0, x0, x1, nA, bstart, Lmin, Lmax,
-                                                  lo_min, lo_max, Lr[0], lo_r[0], qop[0],
-                                                  cscore[0], lane, st[0]);
+    if (x0 < x1) prefill_blocks_int4<D, BS, MODE, NC>(pa, b, g, L, s0, x0, x1, nA, bstart, Lmin,
+                                                      Lmax, lo_min, lo_max, Lr, lo_r, qop, cscore,
+                                                      lane, st);
   } else if (x0 < x1) {
     // per-channel keys: a partly filled last block is read raw from stage row b
     const bool staged = KCH && (L % BS) != 0;
@@ -1028,20 +1030,19 @@ hipError_t launch_prefill_nc(const PrefillArgs& pa, int d, int bs, int64_t units
 
 // Two column tiles per wave whenever there are two and the second set of
 // accumulators fits in registers next to the ring without spilling (d 64;
-// d 128 with 16-token blocks of 8-bit codes); per-channel keys and 4-bit
-// codes: one.
+// d 128 with 16-token blocks of 8-bit codes; 4-bit codes, whose conversion
+// the two tiles then share); per-channel keys: one.
 template <int CODE, int MODE>
 hipError_t launch_prefill_shape(PrefillArgs pa, int d, int bs, int64_t units_per_tg,
                                 hipStream_t stream) {
-  const bool fits = d == 64 || (bs == 16 && CODE != KVQ_CODE_NONE16);
-  const int nc = (MODE != KVQ_SCALE_CHANNEL_BLOCK_SYM && CODE != KVQ_CODE_INT4 && pa.CT >= 2 &&
-                  fits) ? 2 : 1;
+  const bool fits = d == 64 || (bs == 16 && CODE != KVQ_CODE_NONE16) || CODE == KVQ_CODE_INT4;
+  const int nc = (MODE != KVQ_SCALE_CHANNEL_BLOCK_SYM && pa.CT >= 2 && fits) ? 2 : 1;
   const int cts = (pa.CT + nc - 1) / nc;
   // the column tiles of a split share a workgroup (one wave or pair of waves
   // each), so that their reads of the same blocks meet in L1
   pa.TW = cts >= 4 ? 4 : (cts >= 2 ? 2 : 1);
   const int64_t units = units_per_tg * ((cts + pa.TW - 1) / pa.TW);
-  if constexpr (MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM || CODE == KVQ_CODE_INT4) {
+  if constexpr (MODE == KVQ_SCALE_CHANNEL_BLOCK_SYM) {
     return launch_prefill_nc<CODE, MODE, 1>(pa, d, bs, units, stream);
   } else {
     if (nc == 2) return launch_prefill_nc<CODE, MODE, 2>(pa, d, bs, units, stream);
