@@ -123,6 +123,36 @@ def _check(w, P, sample=None, seed=0, layer=0):
     return assert_decode_close(got[torch.as_tensor(sample, device=DEV)], exp[sample], w.name)
 
 
+def _multi_query(w, P, sample, nq=8, seed=0):
+    """Multi-query attention over the populated layer, as `bench.py
+    --prefill-queries` launches it: the last nq positions of each sampled
+    sequence are its queries (the other sequences have none), compared with
+    the oracle's multi-query attention over its cache of the same sequences
+    (built by _check)."""
+    L = oracle_layout(w)
+    lens = P["lens"]
+    counts = np.zeros(w.batch, np.int64)
+    for b in sample:
+        counts[b] = min(nq, int(lens[b]))
+    qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    Tq, max_q, max_len = int(qs[-1]), int(counts.max()), int(lens.max())
+    q = workloads.query_rows(w, Tq, seed=seed, device=DEV)
+    ws = torch.empty(kq.kvq_prefill_workspace_bytes(P["LL"], w.batch, w.num_q_heads, max_q,
+                                                    max_len, 0),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.full((Tq, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32,
+                     device=DEV)
+    kq.kvq_prefill_attention(P["LL"], P["cache"], q, torch.from_numpy(qs).to(DEV), max_q,
+                             P["tables"], P["ctx"], max_len, out, ws)
+    torch.cuda.synchronize()
+    o = P["oracle"]
+    olens = np.zeros_like(lens)
+    olens[sample] = lens[sample]
+    exp = ref.prefill(L, o["hc"], bits(q), DT[w.src_dtype], qs, o["tables"], olens,
+                      threads=_threads())
+    return assert_decode_close(out, exp, f"{w.name} multi-query")
+
+
 def _other_layers(w, n=2, seed=0):
     """Layer 1 and n seeded layers among the rest of the workload's layers."""
     g = np.random.default_rng([seed, 80])
@@ -178,22 +208,29 @@ def test_llama3_8b_layer_int8():
 
 def test_int4_long_context_one_layer():
     """One layer of the INT4 long-context workload: one 131072-token sequence,
-    64 q / 8 KV heads, per-32-group scale and zero point, block 32."""
+    64 q / 8 KV heads, per-32-group scale and zero point, block 32; decode,
+    then 8 queries at its end (64 columns per KV head: four column tiles,
+    two per wave)."""
     need_gpu()
     w = workloads.get("int4_long")
     P = _populate(w)
     err = _check(w, P, sample=[0])
     print(f"int4_long layer: max err {err:.2e}")
+    err = _multi_query(w, P, [0])
+    print(f"int4_long layer, 8 queries: max err {err:.2e}")
 
 
 def test_int4_batch_one_layer():
     """One layer of the INT4 batch workload: all 32 sequences (log-normal
-    lengths, median 4096, cap 65536), then seeded sequences of other layers."""
+    lengths, median 4096, cap 65536), decode and 8 queries per sequence, then
+    seeded sequences of other layers."""
     need_gpu()
     w = workloads.get("int4_batch")
     P = _populate(w)
     err = _check(w, P)
     print(f"int4_batch layer 0, all 32 sequences: max err {err:.2e}")
+    err = _multi_query(w, P, list(range(w.batch)))
+    print(f"int4_batch layer 0, 8 queries per sequence: max err {err:.2e}")
     del P
     g = np.random.default_rng([0, 82])
     for layer in _other_layers(w, n=1):
