@@ -163,12 +163,17 @@ def _other_layers(w, n=2, seed=0):
 def test_llama3_70b_every_sequence_of_layer_0(name):
     """The 70B KV shape (16 x 32768 tokens, 64 q / 8 KV heads, block 16) with
     E4M3 or INT8 per-token codes: every sequence's planes and every query
-    head's output of layer 0."""
+    head's output of layer 0; then 8 queries at the end of three seeded
+    sequences (the LDS-staged multi-query kernel over the whole layer)."""
     need_gpu()
     w = workloads.get(name)
     P = _populate(w)
     err = _check(w, P)
     print(f"{name} layer 0, all 16 sequences: max err {err:.2e}")
+    sample = sorted(int(x) for x in np.random.default_rng([0, 83]).choice(w.batch, 3,
+                                                                           replace=False))
+    err = _multi_query(w, P, sample)
+    print(f"{name} layer 0, 8 queries on sequences {sample}: max err {err:.2e}")
 
 
 @pytest.mark.parametrize("name", ["llama3_70b", "llama3_70b_int8"])
