@@ -209,6 +209,8 @@ def test_llama3_8b_layer_int8():
     sample = [int(np.argmax(lens)), int(np.argmin(lens)), 7, 33]
     err = _check(w, P, sample=sample)
     print(f"llama3_8b: max err {err:.2e}")
+    err = _multi_query(w, P, sample)
+    print(f"llama3_8b, 8 queries: max err {err:.2e}")
 
 
 def test_int4_long_context_one_layer():
@@ -250,7 +252,8 @@ def test_mixed_continuous_step_one_layer():
     """The mixed workload at full size (256 sequences, log-normal lengths
     median 2048, cap 32768, INT8 per-channel-per-block keys with staging, INT8
     per-token values), then one continuous step: 8 new tokens per sequence
-    reserved, appended and decoded."""
+    reserved, appended and decoded, and the 8 tokens checked at once by
+    multi-query attention."""
     need_gpu()
     w = workloads.get("mixed")
     P = _populate(w)
@@ -288,3 +291,8 @@ def test_mixed_continuous_step_one_layer():
     exp = ref.decode(L, O["hc"], bits(q), DT[w.src_dtype], O["tables"], olens, threads=16)
     err = assert_decode_close(got[torch.as_tensor(sample, device=DEV)], exp[sample], "mixed step")
     print(f"mixed step: max err {err:.2e}")
+    # the step's 8 new tokens as queries, checked at once (partial last blocks
+    # read raw from the stage rows)
+    P["lens"] = lens2
+    err = _multi_query(w, P, sample)
+    print(f"mixed step, 8 queries: max err {err:.2e}")
