@@ -376,10 +376,11 @@ __device__ __forceinline__ void channel_query(const Tile8<D, BS>& t, float* x, c
     const float4v s1 = *reinterpret_cast<const float4v*>(src + 8 * c + 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float qp = qs[8 * c + e] * (e < 4 ? s0[e] : s1[e - 4]);
-      const half_t hi = (half_t)qp;
+      // hi and lo each in one mixed-precision FMA from the exact product
+      const float q = qs[8 * c + e], sc = e < 4 ? s0[e] : s1[e - 4];
+      const half_t hi = (half_t)__builtin_fmaf(q, sc, 0.0f);
       qop[c][e] = hi;
-      qlo[c][e] = (half_t)(qp - (float)hi);
+      qlo[c][e] = (half_t)__builtin_fmaf(q, sc, -(float)hi);
     }
   }
 }
