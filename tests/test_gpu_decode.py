@@ -199,10 +199,13 @@ def test_decode_gqa_equals_mha_with_duplicated_heads():
     """Query head h reads KV head h / G: GQA over H = 2 equals MHA over the
     KV heads duplicated G = 4 times. One-block ranges give both launches the
     same partials (the work partition otherwise depends on H, and with it the
-    fp16 rounding of the probabilities), so they agree to fp32 rounding."""
+    fp16 rounding of the probabilities), so they agree to fp32 rounding; each
+    also matches the oracle, whose GQA and MHA outputs agree to fp64
+    rounding."""
     need_gpu()
     w, L, LL, s, q = _setup("int8", G=4, H=2, lens=(90, 17, 300))
-    got_gqa, _ = _run(w, L, LL, s, q, split_blocks=1)
+    got_gqa, exp_gqa = _run(w, L, LL, s, q, split_blocks=1)
+    assert_decode_close(got_gqa, exp_gqa, "GQA")
     w8 = workloads.get("tiny", k_code="int8", v_code="int8", src_dtype="bfloat16",
                        head_dim=128, block_size=16, num_kv_heads=8, num_q_heads=8,
                        batch=3)
@@ -216,6 +219,10 @@ def test_decode_gqa_equals_mha_with_duplicated_heads():
     got_mha = decode_gpu(LL8, gc, q.to(DEV), torch.from_numpy(s8.tables).to(DEV),
                          torch.from_numpy(s8.lens).to(DEV), 300, split_blocks=1)
     assert torch.allclose(got_gqa, got_mha, atol=1e-6, rtol=1e-6)
+    exp_mha = ref.decode(L8, s8.cache, bits(q), DT[w8.src_dtype], s8.tables, s8.lens,
+                         threads=8)
+    assert np.allclose(exp_gqa, exp_mha, rtol=1e-12, atol=1e-12)
+    assert_decode_close(got_mha, exp_mha, "MHA")
 
 
 def test_decode_llama3_8b_workload_full():
