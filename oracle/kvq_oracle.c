@@ -734,8 +734,8 @@ static void* decode_worker(void* arg) {
 }
 
 /* Decode attention [P1, "Recap of KV Caching": attention of the current query
- * over the cached keys and values of its sequence; spec formula
- * softmax(q K^T / sqrt(d)) V]. out[b][h] = sum_t p_t v_t / sum_t p_t,
+ * over the cached keys and values of its sequence, scaled dot-product
+ * attention softmax(q K^T / sqrt(d)) V]. out[b][h] = sum_t p_t v_t / sum_t p_t,
  * p_t = exp(s_t - max s), over t < context_lens[b]; 0 tokens give 0. All in
  * binary64 from the binary32 dequantized rows. sm_scale = 0 means 1/sqrt(d).
  * (b, h) items are spread over num_threads threads; each item is computed

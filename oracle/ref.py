@@ -39,10 +39,15 @@ def _ptr(a):
 
 
 def _load():
-    path = _build.LIB
-    if not os.path.exists(path) or \
-            os.path.getmtime(path) < os.path.getmtime(_build.SRC):
-        _build.build()
+    # KVQ_ORACLE_LIB names another build of the oracle (the mutation test
+    # loads copies with planted mistakes this way); otherwise the oracle's
+    # own library, rebuilt when its source is newer
+    path = os.environ.get("KVQ_ORACLE_LIB")
+    if not path:
+        path = _build.LIB
+        if not os.path.exists(path) or \
+                os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
     lib = C.CDLL(path)
     vp, i32, i64, f32, f64 = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_double
     sig = {

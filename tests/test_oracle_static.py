@@ -97,6 +97,26 @@ def test_fp8_static_matches_torch_cast_in_range():
         assert (vals[~inside] == np.sign(y[~inside]) * 448.0).all()
 
 
+def test_fp8_static_quotient_near_every_midpoint():
+    # x placed at, and one float32 step either side of, m * s for every
+    # midpoint m between two positive E4M3 values, under scales that are not
+    # powers of two: the code is the cast of the correctly rounded quotient
+    # x / s, which near a midpoint decides the code (a product with 1 / s can
+    # land on the other side of it).
+    vals = np.array([ref.e4m3_value(c) for c in range(0x7F)], np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    for s in (0.3, 1.0 / 3.0, 0.7, 3.1, 0.05, 17.0):
+        s = float(np.float32(s))
+        base = f32(mids * s)
+        x = np.concatenate([np.nextafter(base, f32(-np.inf)), base, np.nextafter(base, f32(np.inf))])
+        x = np.concatenate([x, -x]).astype(np.float32)
+        y = f32(x / np.float32(s))
+        q = ref.quant_fp8_static(x, s)
+        got = np.array([ref.e4m3_value(c) for c in q.tolist()])
+        want = torch.from_numpy(y).to(torch.float8_e4m3fn).float().numpy()
+        assert (got == want).all(), s
+
+
 def test_asym4_static_bound_inside_and_clip_outside():
     for _ in range(300):
         s = float(np.float32(10.0 ** rng.uniform(-3, 1)))
