@@ -121,6 +121,33 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "repeats": 3}))
 
 
+def read_probe(nbytes=4 << 30, reps=10):
+    """The HBM read rate of a kernel that only reads (kvq_read_probe: one pass
+    over a 4 GiB buffer with 16-byte non-temporal loads over the whole GPU),
+    HIP events around each launch on the current stream: the ceiling the
+    decode's KV stream is compared with, measured in the same run."""
+    import quantized_paged_kv_append_amd as kq
+    dev = torch.device("cuda:0")
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        kq.kvq_read_probe(buf, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        kq.kvq_read_probe(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del buf
+    torch.cuda.empty_cache()
+    gbps = nbytes / (ms / 1e3) / 1e9
+    return {"GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBS, 4),
+            "bytes": nbytes, "launch_ms_median": round(ms, 4), "launches": reps}
+
+
 def offload_bench(args):
     """Offload of quantized blocks: kvq_pack_blocks into a device buffer,
     that buffer to pinned host memory and back (hipMemcpyAsync through torch),
@@ -233,6 +260,7 @@ def main():
                                       ("layers", "batch", "context", "num_q_heads",
                                        "k_code", "v_code", "k_mode", "v_mode", "block_size")}
         line["workloads"] = extras
+        line["hbm_read_probe"] = read_probe()
     print(json.dumps(line))
 
 

@@ -588,6 +588,21 @@ kvq_status kvq_unpack_blocks(const kvq_layout* layout, const kvq_cache* cache,
                              const void* src, const int32_t* ids, int32_t n,
                              void* stream);
 
+/* ---- measurement aid -------------------------------------------------- */
+/* Decode is bound by the memory stream ("KV Cache Optimization: Strategies
+ * for Faster LLM Inference", "Implementing KV Cache Optimization: A Practical
+ * Checklist": decode is memory-bound), so its rate is judged against what a
+ * kernel that only reads can reach on the device. kvq_read_probe reads
+ * `bytes` bytes of device memory at buf (16-byte aligned, a multiple of 16)
+ * once, with 16-byte non-temporal loads, each workgroup of up to 2048
+ * streaming one contiguous chunk, and
+ * stores nothing except, in the practically impossible case that the XOR of
+ * everything it read equals 0x9E3779B9, that value to sink[0] (device
+ * uint32). The launch's duration (events on `stream`) gives the read rate.
+ * Errors: KVQ_ERR_INVALID_ARGUMENT for a NULL pointer, misalignment or a size
+ * that is not a positive multiple of 16. */
+kvq_status kvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

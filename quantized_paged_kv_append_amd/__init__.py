@@ -14,5 +14,5 @@ from .kvq import (  # noqa: F401
     kvq_decode_attention,
     kvq_decode_attention_noalloc,
     kvq_decode_workspace_bytes, kvq_layout_check, kvq_pool_init, kvq_prefill_attention,
-    kvq_prefill_workspace_bytes,
+    kvq_prefill_workspace_bytes, kvq_read_probe,
     kvq_status_string, make_layout)

@@ -16,7 +16,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libkvq.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["kvq_append.hip", "kvq_decode.hip", "kvq_prefill.hip", "kvq_pool.hip", "kvq_api.cpp"]
+SOURCES = ["kvq_append.hip", "kvq_decode.hip", "kvq_prefill.hip", "kvq_pool.hip", "kvq_probe.hip",
+           "kvq_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -92,6 +92,7 @@ _SIGS = {
                                   _vp, _vp, _vp]),
     "kvq_check_block_tables": (_i32, [_vp, _i32, _vp, _i32, _i32, _i64, _vp, _vp, _vp]),
     "kvq_check_slots": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "kvq_read_probe": (_i32, [_vp, _i64, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -618,6 +619,19 @@ def kvq_check_slots(slot_mapping, num_blocks, block_size, first_bad, status_flag
     _check("kvq_check_slots", _lib.kvq_check_slots(
         _ptr(slot_mapping), slot_mapping.numel(), int(num_blocks), block_size, _ptr(first_bad),
         _ptr(status_flag), _stream(stream)))
+
+
+def kvq_read_probe(buf, sink, stream=None):
+    """Measurement aid: read every byte of buf (a device tensor, 16-byte
+    aligned, nbytes a multiple of 16) once with non-temporal loads; sink is a
+    device int32 [1] that is written only in a practically impossible case.
+    Time the call with events on the stream to get the read rate."""
+    _need(sink, "sink", torch.int32, numel=1)
+    _on_device(buf=buf, sink=sink)
+    if not buf.is_contiguous():
+        raise ValueError("buf: must be contiguous")
+    _check("kvq_read_probe", _lib.kvq_read_probe(_ptr(buf), _nbytes(buf), _ptr(sink),
+                                                 _stream(stream)))
 
 
 def kvq_block_pack_bytes(layout) -> int:

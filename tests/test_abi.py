@@ -336,3 +336,14 @@ def test_check_calls_reject_bad_arguments_on_host():
     assert lib.kvq_check_slots(None, 8, 100, 16, p, p, None) == bad
     assert lib.kvq_check_slots(p, -1, 100, 16, p, p, None) == bad
     assert lib.kvq_check_slots(p, 8, 100, 0, p, p, None) == bad
+
+
+def test_read_probe_rejects_bad_arguments_on_host():
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+    bad = kq.KVQ_ERR_INVALID_ARGUMENT
+    assert lib.kvq_read_probe(None, 1 << 20, p, None) == bad            # no buffer
+    assert lib.kvq_read_probe(p, 1 << 20, None, None) == bad            # no sink
+    assert lib.kvq_read_probe(p, 0, p, None) == bad                     # nothing to read
+    assert lib.kvq_read_probe(p, 24, p, None) == bad                    # not whole words
+    assert lib.kvq_read_probe(C.c_void_p((1 << 21) + 8), 64, p, None) == bad  # misaligned
