@@ -339,6 +339,92 @@ __device__ __forceinline__ void tile_step(const Tile8<D, BS>& t, int nt, int pos
   }
 }
 
+// Two whole 16-token tiles of 8-bit codes with per-token scales (tile na of
+// ta, then tile nb of tb: consecutive tokens of one block, or the tiles of
+// two consecutive blocks) in one step: their scores, one softmax update for
+// the 32 tokens, and the PV products on 16x16x32 MFMAs whose contraction
+// runs over both tiles (k = 8 j + 4 T + e for tile T, token 4 j + e; the
+// value and probability operands are each tile's 16x16x16 operands side by
+// side), half the MFMAs and one cross-lane max and rescale test per 32
+// tokens instead of per 16.
+template <int CODE, int D, int BS>
+__device__ __forceinline__ void tile_pair_step(const Tile8<D, BS>& ta, int na,
+                                               const Tile8<D, BS>& tb, int nb,
+                                               const half8v* qop, float cscore,
+                                               SoftmaxState<D>& st) {
+  constexpr int NCH = D / 32;
+  constexpr int NPV = D / 16;
+  float4v Sa = {0.0f, 0.0f, 0.0f, 0.0f}, Sb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const u32x4& ka = ta.k[na][c / 2];
+    const u32x4& kb = tb.k[nb][c / 2];
+    const half8v opa = codes8_to_h8<CODE>((c & 1) ? ka.z : ka.x, (c & 1) ? ka.w : ka.y);
+    const half8v opb = codes8_to_h8<CODE>((c & 1) ? kb.z : kb.x, (c & 1) ? kb.w : kb.y);
+    Sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(opa, qop[c], Sa, 0, 0, 0);
+    Sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(opb, qop[c], Sb, 0, 0, 0);
+  }
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s[e] = Sa[e] * ta.sk[na][e] * cscore;
+    s[4 + e] = Sb[e] * tb.sk[nb][e] * cscore;
+  }
+  const float mt = colmax4(fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                                 fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
+  const float mn = fmaxf(st.m, mt);
+  const float msafe = mn == -INFINITY ? 0.0f : mn;
+  if (__any(mn > st.m)) {  // a running max grew: rescale (rare after warm-up)
+    const float alpha = __builtin_amdgcn_exp2f(st.m - msafe);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) st.acc[c] *= alpha;
+  }
+  st.m = mn;
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - msafe);
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  half8v pop;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pop[e] = (half_t)(p[e] * ta.sv[na][e]);
+    pop[4 + e] = (half_t)(p[4 + e] * tb.sv[nb][e]);
+  }
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) {
+    const uint32_t a0 = ta.v[na][0][w], a1 = ta.v[na][1][w];
+    const uint32_t a2 = ta.v[na][2][w], a3 = ta.v[na][3][w];
+    const uint32_t b0 = tb.v[nb][0][w], b1 = tb.v[nb][1][w];
+    const uint32_t b2 = tb.v[nb][2][w], b3 = tb.v[nb][3][w];
+    // per tile: [t0.b0 t1.b0 t0.b1 t1.b1], [t0.b2 t1.b2 t0.b3 t1.b3]
+    const uint32_t a01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+    const uint32_t a01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+    const uint32_t a23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+    const uint32_t a23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+    const uint32_t b01l = __builtin_amdgcn_perm(b1, b0, 0x05010400u);
+    const uint32_t b01h = __builtin_amdgcn_perm(b1, b0, 0x07030602u);
+    const uint32_t b23l = __builtin_amdgcn_perm(b3, b2, 0x05010400u);
+    const uint32_t b23h = __builtin_amdgcn_perm(b3, b2, 0x07030602u);
+    auto cat = [](half4v x, half4v y) {
+      return (half8v){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    };
+    const int c0 = 4 * w;
+    st.acc[c0 + 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        cat(vpair_to_h4<CODE, false>(a01l, a23l), vpair_to_h4<CODE, false>(b01l, b23l)), pop,
+        st.acc[c0 + 0], 0, 0, 0);
+    st.acc[c0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        cat(vpair_to_h4<CODE, true>(a01l, a23l), vpair_to_h4<CODE, true>(b01l, b23l)), pop,
+        st.acc[c0 + 1], 0, 0, 0);
+    st.acc[c0 + 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        cat(vpair_to_h4<CODE, false>(a01h, a23h), vpair_to_h4<CODE, false>(b01h, b23h)), pop,
+        st.acc[c0 + 2], 0, 0, 0);
+    st.acc[c0 + 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        cat(vpair_to_h4<CODE, true>(a01h, a23h), vpair_to_h4<CODE, true>(b01h, b23h)), pop,
+        st.acc[c0 + 3], 0, 0, 0);
+  }
+}
+
 // A block whose BS tokens all lie before the sequence end.
 template <int CODE, int D, int BS, int KSRC = kKeyTokenScale>
 __device__ __forceinline__ void full_block_step(const Tile8<D, BS>& t, int i, int L,

@@ -37,9 +37,12 @@
 //  * The query is pre-scaled per head by a power of two into [1, 2) before
 //    its fp16 conversion (exact for bf16 values within 2^14 of the head's
 //    largest element); the factor returns in the score scale.
-//  * A ring of three register buffers keeps two cache blocks in flight while
-//    the wave computes on a third; block ids come from one vector load per 64
-//    blocks of the split and are read with v_readlane.
+//  * 8-bit codes with per-token scales take two 16-token tiles per softmax
+//    update, with PV on v_mfma_f32_16x16x32_f16 over both tiles' tokens.
+//  * A ring of register buffers (four 16-token blocks as two pairs, or three
+//    / two blocks) keeps the next blocks in flight while the wave computes;
+//    block ids come from one vector load per 64 blocks of the split and are
+//    read with v_readlane.
 //  * Partials (m, l, acc) per split go to the workspace; decode_reduce merges
 //    them with the log-sum-exp rule.
 #include <atomic>
@@ -400,8 +403,12 @@ __device__ __forceinline__ void plan_sequence(const PlanArgs& p, int b, int lane
 // Block ids of blocks [i0, ilast] of one sequence, 64 at a time: lane k of
 // `cur` holds the id of block base + k and lane k of `nxt` that of block
 // base + 64 + k (indices past ilast read ilast). A wave asks only for blocks
-// in [base, base + 128) and calls advance() once it has passed base + 64, so
-// each 64-id load is issued 64 blocks before its first use.
+// in [base, base + 128) and calls advance() once it has passed base + 64.
+// Each new window is waited for where it is loaded: vector loads retire in
+// order, and a window still in flight where id() reads it (the read of
+// `nxt` sits on every path) would make every ring turn wait for all of its
+// block loads, where this way only the turns that advance, one per 64
+// blocks, do.
 struct IdWindow {
   const int32_t* row;
   int base, ilast;
@@ -412,6 +419,7 @@ struct IdWindow {
     ilast = il;
     cur = row[min(i0 + lane, il)];
     nxt = row[min(i0 + kWave + lane, il)];
+    asm volatile("" ::"v"(cur), "v"(nxt));  // wait for both windows here
   }
   __device__ __forceinline__ int32_t id(int i) const {
     const int k = min(i, ilast) - base;
@@ -421,6 +429,7 @@ struct IdWindow {
     base += kWave;
     cur = nxt;
     nxt = row[min(base + kWave + lane, ilast)];
+    asm volatile("" ::"v"(nxt));  // wait for the new window here
   }
 };
 
@@ -434,7 +443,11 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
                                             int i0, int i1, int lane, SoftmaxState<D>& st,
                                             float* lds) {
   constexpr int NCH = D / 32;   // k-chunks of the score MFMA
-  constexpr int NBUF = BS == 16 ? 3 : 2;  // blocks in the register ring
+  constexpr bool RAW = CODE == KVQ_CODE_NONE16;
+  // Per-token 8-bit codes step two 16-token tiles at a time; 16-token
+  // blocks then ride a ring of two pairs.
+  constexpr bool PAIR = !RAW && !KCH;
+  constexpr int NBUF = BS == 16 ? (PAIR ? 4 : 3) : 2;  // blocks in the register ring
   const int r = lane & 15, j = lane >> 4;
   const int ilast = i1 - 1;
 
@@ -463,7 +476,6 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
 #pragma unroll
   for (int e = 0; e < D / 4; ++e) qf[e] = hcol ? qf[e] * qdown : 0.0f;
   const float* qs = qf;
-  constexpr bool RAW = CODE == KVQ_CODE_NONE16;
   const bool raw_bf16 = a.stage_bf16 != 0;
   half8v qop[NCH], qlo[NCH];
   auto make_qop = [&](bool pair) {
@@ -504,6 +516,9 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
       half8v qb[NCH], ql[NCH];
       channel_query<D, BS>(t, lds, qs, lane, qb, ql);
       full_block_step<CODE, D, BS, kKeyChannel>(t, i, L, qb, cscore, j, st, ql);
+    } else if constexpr (PAIR && BS >= 32) {
+#pragma unroll
+      for (int nt = 0; nt < BS / 16; nt += 2) tile_pair_step<CODE, D, BS>(t, nt, t, nt + 1, qop, cscore, st);
     } else {
       full_block_step<CODE, D, BS>(t, i, L, qop, cscore, j, st);
     }
@@ -521,10 +536,19 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
   int i = i0;
   for (; i + NBUF <= ifull; i += NBUF) {
     if (i - ids.base >= kWave) ids.advance(lane);
+    if constexpr (PAIR && BS == 16) {
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      block(buf[u], i + u);
-      load_tile<D, BS, KCH, true>(buf[u], a, bh_of(i + u + NBUF), lane);
+      for (int u = 0; u < NBUF; u += 2) {
+        tile_pair_step<CODE, D, BS>(buf[u], 0, buf[u + 1], 0, qop, cscore, st);
+        load_tile<D, BS, KCH, true>(buf[u], a, bh_of(i + u + NBUF), lane);
+        load_tile<D, BS, KCH, true>(buf[u + 1], a, bh_of(i + u + 1 + NBUF), lane);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        block(buf[u], i + u);
+        load_tile<D, BS, KCH, true>(buf[u], a, bh_of(i + u + NBUF), lane);
+      }
     }
   }
   // Remainder: fewer than NBUF complete blocks, already in buf[0 ..], then
@@ -543,8 +567,16 @@ __device__ __forceinline__ void wave_blocks(const DecodeArgs& a, int b, int g, i
       }
     }
   }
+  bool paired = false;  // the first two remaining 16-token blocks as one pair
+  if constexpr (PAIR && BS == 16) {
+    if (i + 1 < ifull) {
+      tile_pair_step<CODE, D, BS>(buf[0], 0, buf[1], 0, qop, cscore, st);
+      paired = true;
+    }
+  }
 #pragma unroll
   for (int u = 0; u < NBUF; ++u) {
+    if (u < 2 && paired) continue;
     if (i + u < ifull) {
       block(buf[u], i + u);
     } else if (i + u == ifull && partial) {

@@ -110,6 +110,22 @@ def test_decode_split_counts(split, code, mode, bs):
     assert_decode_close(got, exp, f"{code} split {split}")
 
 
+# Per-token 8-bit codes go two 16-token tiles per softmax update: shares of
+# 1, 2, 3 and 5 blocks leave every count of whole blocks after the ring (with
+# and without a partial block), and shares of 256 blocks take the ring through
+# several 64-block id windows.
+@pytest.mark.parametrize("split", [0, 1, 2, 3, 5, 256])
+@pytest.mark.parametrize("code", ["int8", "fp8"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 16), (128, 32), (64, 32)])
+def test_decode_paired_tiles_every_remainder(code, d, bs, split):
+    need_gpu()
+    lens = tuple(16 * k + r for k in range(9) for r in (0, 7)) + (1100, 2100, 4111)
+    w, L, LL, s, q = _setup(code, d, bs, G=4, lens=lens)
+    got, exp = _run(w, L, LL, s, q, split_blocks=split)
+    assert_decode_close(got, exp, f"{code} d{d} bs{bs} split {split}")
+    assert (got[0] == 0).all()           # empty context
+
+
 @pytest.mark.parametrize("split", [0, 21, 40])
 @pytest.mark.parametrize("mode", ["token_sym", "group_asym"])
 @pytest.mark.parametrize("d,bs", [(128, 16), (64, 16), (128, 32), (64, 32)])
