@@ -2,9 +2,11 @@
 
 One step is one pass of the whole hot path over a batch: the device pool
 reserves a slot for one new token per sequence, then for every layer the new
-token's K/V rows are quantized into the cache (kvq_append) and decode
-attention runs over the whole quantized context (kvq_decode_attention: split
-kernel + cross-split reduce). The default workload is the Llama-3-70B KV shape
+token's K/V rows are quantized into the cache and decode attention runs over
+the whole quantized context, the new token included: one
+kvq_append_decode_attention launch (split kernel, which also codes the new
+rows, + cross-split reduce) where the layout allows it, else kvq_append then
+kvq_decode_attention (--two-call forces the latter). The default workload is the Llama-3-70B KV shape
 with all 80 layers resident: 16 sequences x 32768 tokens, 64 query / 8 KV
 heads, d = 128, FP8 E4M3 codes with fp32 per-token-per-head scales, block 16,
 bf16 inputs (synthetic, seeded; see workloads.py).
@@ -35,6 +37,7 @@ PEAK_MFMA_F16_TFLOPS = 2500.0   # dense fp16 MFMA, MI355X
 HERE = os.path.dirname(os.path.abspath(__file__))
 # sources whose change invalidates committed decode counters
 DECODE_SOURCES = ("kvq_decode.hip", "kvq_attn_tiles.h", "kvq_int4_tiles.h", "kvq_device.h",
+                  "kvq_encode.h",
                   "kvq_internal.h", "kvq_api.cpp")
 
 
@@ -83,6 +86,9 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time the eager steps only (default: also one step captured in a "
                          "HIP graph, replayed; its time is the line's value)")
+    ap.add_argument("--two-call", action="store_true",
+                    help="append with kvq_append, then kvq_decode_attention, even where one "
+                         "kvq_append_decode_attention launch could do both")
     ap.add_argument("--identity-pool", action="store_true",
                     help="blocks in order instead of a seeded permutation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -363,10 +369,24 @@ def run(args, wname):
     dec_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(layers)] for _ in range(args.steps)]
 
+    # one launch appends and attends for byte codes with per-token scales and
+    # for 16-bit rows (the layouts kvq_append_decode_attention takes)
+    fused = not nq and not args.two_call and (
+        (w.k_code == w.v_code and w.k_code in ("int8", "fp8")
+         and w.k_mode == w.v_mode == "token_sym") or w.k_code == w.v_code == "none16")
+
     def step(evs=None):
         kq.kvq_blocks_reserve(stack, top, tables, ctx, new_tok, bs, slots, status, ctx)
         for layer in range(layers):
             k, v = new_kv[layer]
+            if fused:
+                if evs is not None:
+                    evs[layer][0].record(stream)
+                kq.kvq_append_decode_attention(LL, caches[layer], k, v, qs[layer], tables, ctx,
+                                               max_ctx, out, ws, split_blocks=args.split_blocks)
+                if evs is not None:
+                    evs[layer][1].record(stream)
+                continue
             kq.kvq_append(LL, caches[layer], k, v, slots, stage_rows)
             if evs is not None:
                 evs[layer][0].record(stream)
@@ -475,7 +495,9 @@ def run(args, wname):
         cpu = cpu_baseline(w, lens, args)
     roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": committed_traffic(w.name),
-            "kernel": "decode_split_kernel + decode_reduce_kernel (one kvq_decode_attention)",
+            "kernel": ("decode_split_kernel + decode_reduce_kernel (one "
+                       + ("kvq_append_decode_attention, which also codes the step's "
+                          "new rows)" if fused else "kvq_decode_attention)")),
             "bytes_per_launch": dec_bytes_launch}
     prefill = None
     if nq:
@@ -518,6 +540,8 @@ def run(args, wname):
             "split_blocks": args.split_blocks or "auto",
             "prefill_queries": nq or None,
             "step": "eager" if args.eager else "hip graph replay",
+            "step_calls": ("reserve, then per layer kvq_append_decode_attention" if fused
+                           else "reserve, then per layer kvq_append and the attention call"),
         },
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "kv_bytes_per_step": kv_bytes_step,

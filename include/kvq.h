@@ -324,6 +324,36 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache
                                 int32_t out_dtype, void* workspace,
                                 int64_t workspace_bytes, void* stream);
 
+/* kvq_append followed by kvq_decode_attention in one launch, for a decode
+ * step's one new token per sequence ("Dynamic KV Cache Quantization for Fast
+ * LLM Inference", section "Integrating Dynamic Quantization with
+ * PagedAttention": the new key and value are quantized as they enter their
+ * block, and the step's attention reads them from there).
+ *  k, v          device, src_dtype; the new row of sequence b, KV head h,
+ *                element e at k[b * k_row_stride + h * d + e] (strides in
+ *                elements, 16-byte aligned rows as for kvq_append).
+ * Row b is coded into position context_lens[b] - 1 of sequence b, the slot
+ * block_tables[b][(len - 1) / bs] * bs + (len - 1) % bs that
+ * kvq_blocks_reserve handed out for it, with kvq_append's arithmetic (same
+ * bytes); the decode then attends over all context_lens[b] tokens, the new
+ * one included. The other arguments, the result and the workspace are those
+ * of kvq_decode_attention. A sequence with no tokens takes no row; a table
+ * entry outside the pool receives nothing (the decode reads block 0 there).
+ * Supported: both sides INT8 or E4M3 under TOKEN_SYM, and both NONE16; other
+ * layouts return KVQ_ERR_UNSUPPORTED (use kvq_append, then decode).
+ * Errors: those of kvq_decode_attention, and KVQ_ERR_INVALID_ARGUMENT for a
+ * missing or misaligned k or v, a row stride below H * d or not a multiple of
+ * 8 elements, or max_context_len < 1 with batch > 0. */
+kvq_status kvq_append_decode_attention(const kvq_layout* layout, const kvq_cache* cache,
+                                       const void* k, const void* v, int64_t k_row_stride,
+                                       int64_t v_row_stride, const void* q, int32_t q_dtype,
+                                       int32_t batch, int32_t num_q_heads,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       float sm_scale, int32_t split_blocks, void* out,
+                                       int32_t out_dtype, void* workspace,
+                                       int64_t workspace_bytes, void* stream);
+
 /* kvq_decode_attention for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc. It takes no workspace: the partials go to a fixed array the

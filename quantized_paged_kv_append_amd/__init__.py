@@ -12,6 +12,7 @@ from .kvq import (  # noqa: F401
     kvq_copy_blocks, kvq_pack_blocks, kvq_unpack_blocks, kvq_blocks_reserve,
     kvq_bytes_per_token, kvq_cache_plane_bytes, kvq_check_block_tables, kvq_check_slots,
     kvq_decode_attention,
+    kvq_append_decode_attention,
     kvq_decode_attention_noalloc,
     kvq_decode_workspace_bytes, kvq_layout_check, kvq_pool_init, kvq_prefill_attention,
     kvq_prefill_workspace_bytes, kvq_read_probe,

@@ -320,7 +320,9 @@ kvq_status decode_launch(const kvq_layout* L, const kvq_cache* C, const void* q,
                          int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
                          int32_t max_blocks_per_seq, const int32_t* context_lens,
                          int32_t max_context_len, float sm_scale, int32_t split_blocks,
-                         void* out, int32_t out_dtype, void* workspace, void* stream) {
+                         void* out, int32_t out_dtype, void* workspace, void* stream,
+                         const void* new_k = nullptr, const void* new_v = nullptr,
+                         int64_t new_k_stride = 0, int64_t new_v_stride = 0) {
   const int64_t bound = decode_item_bound(L, batch, max_context_len, split_blocks);
   const int64_t items = bound * num_q_heads;
   kvq::DecodePlan p;
@@ -356,6 +358,10 @@ kvq_status decode_launch(const kvq_layout* L, const kvq_cache* C, const void* q,
   p.ws_acc = static_cast<float*>(workspace);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                      round_up(items * L->head_dim * 4, 256));
+  p.new_k = new_k;
+  p.new_v = new_v;
+  p.new_k_stride = new_k_stride;
+  p.new_v_stride = new_v_stride;
   return hip_status(kvq::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -378,6 +384,39 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* C, const v
   return decode_launch(L, C, q, q_dtype, batch, num_q_heads, block_tables, max_blocks_per_seq,
                        context_lens, max_context_len, sm_scale, split_blocks, out, out_dtype,
                        workspace, stream);
+}
+
+kvq_status kvq_append_decode_attention(const kvq_layout* L, const kvq_cache* C, const void* k,
+                                       const void* v, int64_t k_row_stride, int64_t v_row_stride,
+                                       const void* q, int32_t q_dtype, int32_t batch,
+                                       int32_t num_q_heads, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       int32_t max_context_len, float sm_scale,
+                                       int32_t split_blocks, void* out, int32_t out_dtype,
+                                       void* workspace, int64_t workspace_bytes, void* stream) {
+  int64_t need = 0;
+  kvq_status s = decode_check(L, C, q, q_dtype, batch, num_q_heads, block_tables,
+                              max_blocks_per_seq, context_lens, max_context_len, sm_scale,
+                              split_blocks, out, out_dtype, &need);
+  if (s != KVQ_OK) return s;
+  // byte codes with per-token scales, or 16-bit rows, on both sides
+  const bool bytes = L->k_code == L->v_code && L->k_mode == KVQ_SCALE_TOKEN_SYM &&
+                     L->v_mode == KVQ_SCALE_TOKEN_SYM &&
+                     (L->k_code == KVQ_CODE_INT8 || L->k_code == KVQ_CODE_FP8_E4M3);
+  const bool raw = L->k_code == KVQ_CODE_NONE16 && L->v_code == KVQ_CODE_NONE16;
+  if (!bytes && !raw) return KVQ_ERR_UNSUPPORTED;
+  if (batch == 0) return KVQ_OK;
+  // every context holds at least its new token
+  if (max_context_len < 1) return KVQ_ERR_INVALID_ARGUMENT;
+  const int64_t row = (int64_t)L->num_kv_heads * L->head_dim;
+  if (!k || !v || !aligned16(k) || !aligned16(v)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (k_row_stride < row || v_row_stride < row) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((k_row_stride * 2) % 16 || (v_row_stride * 2) % 16) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!workspace || !aligned16(workspace)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  return decode_launch(L, C, q, q_dtype, batch, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, sm_scale, split_blocks, out, out_dtype,
+                       workspace, stream, k, v, k_row_stride, v_row_stride);
 }
 
 kvq_status kvq_decode_attention_noalloc(const kvq_layout* L, const kvq_cache* C, const void* q,

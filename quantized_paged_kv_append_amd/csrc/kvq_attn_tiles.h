@@ -39,6 +39,19 @@ struct DecodeArgs {
   int32_t max_len;       // every context length is cut to this
   int32_t split_blocks;  // 0: planned from the lengths
   float sm_log2;  // sm_scale * log2(e)
+  // Append before attending (kvq_append_decode_attention): row b of new_k /
+  // new_v (16-bit, H*d per token, strides in elements) is coded into position
+  // context_lens[b] - 1 of sequence b, through the writable views of the
+  // planes. new_k == nullptr: decode only.
+  const uint16_t* new_k = nullptr;
+  const uint16_t* new_v = nullptr;
+  int64_t new_k_stride = 0;
+  int64_t new_v_stride = 0;
+  uint8_t* k_codes_w = nullptr;
+  uint8_t* v_codes_w = nullptr;
+  float* k_scale_w = nullptr;
+  float* v_scale_w = nullptr;
+  int32_t new_bf16 = 0;
 };
 
 // Max and sum of a float over the wave by the same DPP pattern, with -inf

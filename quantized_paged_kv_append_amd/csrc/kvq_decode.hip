@@ -49,6 +49,7 @@
 #include <mutex>
 
 #include "kvq_attn_tiles.h"
+#include "kvq_encode.h"
 #include "kvq_int4_tiles.h"
 
 // Partials of kvq_decode_attention_noalloc: a fixed array in device memory
@@ -733,6 +734,47 @@ __device__ __forceinline__ void split_write(const DecodeArgs& a, const PlanItem&
   }
 }
 
+// The step's new token of sequence b, KV head g, coded into the cache at
+// position L - 1 before the wave that owns the sequence's last block reads
+// it: quad 0 codes the key row and quad 1 the value row with the append's
+// own coder, so the bytes equal those kvq_append writes. The wave's stores
+// complete before its loads are issued; the block's other readers do not
+// exist in this launch (each block belongs to one wave's share).
+template <int CODE, int D, int BS>
+__device__ __forceinline__ void append_new_token(const DecodeArgs& a, int b, int g, int L,
+                                                 int lane) {
+  constexpr int NV = D / 32;   // 16-byte pieces per lane of a row
+  const int pos = L - 1;
+  const int32_t id = a.block_tables[(int64_t)b * a.max_blocks + pos / BS];
+  const int quad = lane >> 2, k = lane & 3;
+  const bool isv = quad == 1;
+  const bool live = quad < 2 && id >= 0 && id < a.num_blocks;
+  const int64_t rowi = ((int64_t)(live ? id : 0) * a.H + g) * BS + pos % BS;
+  const uint16_t* src = (isv ? a.new_v + (int64_t)b * a.new_v_stride
+                             : a.new_k + (int64_t)b * a.new_k_stride) + g * D + 8 * k;
+  u32x4 w[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+    w[u] = live ? *reinterpret_cast<const u32x4*>(src + 32 * u) : (u32x4){0u, 0u, 0u, 0u};
+  if constexpr (CODE == KVQ_CODE_NONE16) {
+    uint8_t* dst = (isv ? a.v_codes_w : a.k_codes_w) + rowi * (2 * D);
+    if (live) {
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        *reinterpret_cast<u32x4*>(dst + 2 * (32 * u + 8 * k)) = w[u];
+    }
+  } else {
+    uint8_t* dst = (isv ? a.v_codes_w : a.k_codes_w) + rowi * D;
+    float* sc = (isv ? a.v_scale_w : a.k_scale_w) + rowi;
+    if (a.new_bf16)
+      code_row8<CODE, D, true, false>(w, k, 0.0f, dst, sc, live);
+    else
+      code_row8<CODE, D, false, false>(w, k, 0.0f, dst, sc, live);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // One item of the plan: the split's S blocks are cut into kNW consecutive
 // shares, one per wave; the waves merge their softmax states through LDS and
 // wave 0 writes the split's partial. Every wave calls this (it holds
@@ -760,6 +802,9 @@ __device__ __forceinline__ void split_item(const DecodeArgs& a, const PlanItem& 
   st.l = 0.0f;
 #pragma unroll
   for (int c = 0; c < NPV; ++c) st.acc[c] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (!ROUNDS && MODE == KVQ_SCALE_TOKEN_SYM && CODE != KVQ_CODE_INT4) {
+    if (a.new_k != nullptr && i0 < i1 && i1 == nblk) append_new_token<CODE, D, BS>(a, b, g, L, lane);
+  }
   if (i0 < i1) {
     if constexpr (CODE == KVQ_CODE_INT4)
       wave_blocks_int4<D, BS, MODE>(a, b, g, L, nblk, i0, i1, lane, st);
@@ -909,9 +954,12 @@ __global__ __launch_bounds__(64 * kReduceHeads) void decode_reduce_kernel(Reduce
 template <int CODE, int MODE, int D, int BS>
 hipError_t launch_split(const DecodeArgs& a, int items, hipStream_t stream) {
   // whole runs of 16 workgroups (see workgroup_item); the extra ones find no
-  // item. Beyond kDecodeMaxGrid workgroups, the grid is capped and takes rounds.
+  // item. Beyond kDecodeMaxGrid workgroups, the grid is capped and takes
+  // rounds, except when the launch also appends the step's tokens: that code
+  // lives in the single-pass kernel only (it would cost the rounds kernel
+  // registers), whose surplus workgroups exit at once.
   const int64_t pairs = ((int64_t)items * a.H + 15) / 16 * 16;
-  if (pairs <= kDecodeMaxGrid)
+  if (pairs <= kDecodeMaxGrid || a.new_k != nullptr)
     decode_split_kernel<CODE, MODE, D, BS, false><<<dim3((unsigned)pairs), 64 * kNW, 0, stream>>>(a);
   else
     decode_split_kernel<CODE, MODE, D, BS, true><<<dim3(kDecodeMaxGrid), 64 * kNW, 0, stream>>>(a);
@@ -993,6 +1041,17 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
   a.v_zero = p.v_zero;
   a.k_stage = static_cast<const uint16_t*>(p.k_stage);
   a.stage_bf16 = p.src_bf16;
+  if (p.new_k != nullptr) {
+    a.new_k = static_cast<const uint16_t*>(p.new_k);
+    a.new_v = static_cast<const uint16_t*>(p.new_v);
+    a.new_k_stride = p.new_k_stride;
+    a.new_v_stride = p.new_v_stride;
+    a.k_codes_w = static_cast<uint8_t*>(const_cast<void*>(p.k_codes));
+    a.v_codes_w = static_cast<uint8_t*>(const_cast<void*>(p.v_codes));
+    a.k_scale_w = const_cast<float*>(p.k_scale);
+    a.v_scale_w = const_cast<float*>(p.v_scale);
+    a.new_bf16 = p.src_bf16;
+  }
   hipError_t e;
   const int d = p.head_dim, bs = p.block_size;
   if (p.k_code == KVQ_CODE_NONE16)

@@ -70,6 +70,11 @@ struct DecodePlan {
   int32_t out_dtype;
   float* ws_acc;  // [item_bound][Hq][d]
   float* ws_ml;   // [item_bound][Hq][2]
+  // kvq_append_decode_attention: the step's new rows, else nullptr
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  int64_t new_k_stride = 0;
+  int64_t new_v_stride = 0;
 };
 
 // Split planning constants, shared by the host (grid and workspace bounds)

@@ -68,6 +68,9 @@ _SIGS = {
     "kvq_decode_workspace_bytes": (_i64, [_LP, _i32, _i32, _i32, _i32]),
     "kvq_decode_attention": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
                                     _i32, _f32, _i32, _vp, _i32, _vp, _i64, _vp]),
+    "kvq_append_decode_attention": (_i32, [_LP, _CP, _vp, _vp, _i64, _i64, _vp, _i32, _i32,
+                                           _i32, _vp, _i32, _vp, _i32, _f32, _i32, _vp, _i32,
+                                           _vp, _i64, _vp]),
     "kvq_decode_attention_noalloc": (_i32, [_LP, _CP, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
                                             _i32, _f32, _i32, _vp, _i32, _vp]),
     "kvq_prefill_workspace_bytes": (_i64, [_LP, _i32, _i32, _i32, _i32, _i32]),
@@ -363,6 +366,28 @@ def kvq_decode_attention(layout, cache: PagedCache, q, block_tables, context_len
                workspace=workspace)
     _check("kvq_decode_attention", _lib.kvq_decode_attention(
         C.byref(layout), C.byref(cache.struct), _ptr(q), DTYPES[q.dtype], B, Hq,
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        int(max_context_len), float(sm_scale), int(split_blocks), _ptr(out),
+        DTYPES[out.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def kvq_append_decode_attention(layout, cache: PagedCache, k, v, q, block_tables,
+                                context_lens, max_context_len, out, workspace, sm_scale=0.0,
+                                split_blocks=0, stream=None):
+    """kvq_append of one new token per sequence (rows k[b], v[b]: device
+    [B][H][d] or [B][H*d] in the layout's source dtype) into position
+    context_lens[b] - 1, then kvq_decode_attention, in one launch. The other
+    arguments are kvq_decode_attention's."""
+    B, Hq = _decode_checks(layout, q, block_tables, context_lens, out, workspace)
+    _need_rows(k, "k", layout, B)
+    _need_rows(v, "v", layout, B)
+    _need_cache(layout, cache)
+    _on_device(cache=cache, k=k, v=v, q=q, block_tables=block_tables,
+               context_lens=context_lens, out=out, workspace=workspace)
+    _check("kvq_append_decode_attention", _lib.kvq_append_decode_attention(
+        C.byref(layout), C.byref(cache.struct), _ptr(k), _ptr(v),
+        k.stride(0) if B else 0, v.stride(0) if B else 0, _ptr(q), DTYPES[q.dtype], B, Hq,
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         int(max_context_len), float(sm_scale), int(split_blocks), _ptr(out),
         DTYPES[out.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),

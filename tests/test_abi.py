@@ -186,6 +186,41 @@ def test_decode_noalloc_rejects_bad_arguments_on_host():
     assert kq.kvq_decode_workspace_bytes(L, 256, 32, 33000) <= kq.KVQ_DECODE_SCRATCH_BYTES
 
 
+def test_append_decode_rejects_bad_arguments_on_host():
+    """The fused append + decode takes decode's checks, then its own: byte
+    codes with per-token scales or 16-bit rows only, aligned new rows with
+    strides of at least H * d elements, and room for the new token. Every
+    call here fails, or returns for an empty batch, before touching the
+    device."""
+    lib = kq._lib
+    p = C.c_void_p(1 << 21)
+
+    def fused(L, batch=2, k=p, v=p, ks=1024, vs=1024, maxlen=64, hq=32, ws_bytes=1 << 30):
+        cs = _fake_cache(L)
+        if L.k_mode == kq.KVQ_SCALE_GROUP_ASYM:
+            cs.k_zero, cs.v_zero = 1 << 22, 1 << 23
+        if L.k_mode == kq.KVQ_SCALE_CHANNEL_BLOCK_SYM:
+            cs.k_stage, cs.max_seqs = 1 << 24, 4
+        return lib.kvq_append_decode_attention(C.byref(L), C.byref(cs), k, v, ks, vs, p,
+                                               kq.KVQ_BF16, batch, hq, p, 4, p, maxlen, 0.0, 0,
+                                               p, kq.KVQ_F32, p, ws_bytes, None)
+    L8 = kq.make_layout(8, 128, 16, "int8")
+    assert fused(L8, batch=0) == kq.KVQ_OK
+    assert fused(L8, k=None) == kq.KVQ_ERR_INVALID_ARGUMENT
+    assert fused(L8, v=C.c_void_p((1 << 21) + 8)) == kq.KVQ_ERR_INVALID_ARGUMENT  # misaligned
+    assert fused(L8, ks=8 * 128 - 8) == kq.KVQ_ERR_INVALID_ARGUMENT     # stride below H*d
+    assert fused(L8, vs=1028) == kq.KVQ_ERR_INVALID_ARGUMENT            # not 16-byte rows
+    assert fused(L8, maxlen=0) == kq.KVQ_ERR_INVALID_ARGUMENT           # no new token fits
+    assert fused(L8, hq=30) == kq.KVQ_ERR_INVALID_ARGUMENT              # decode's own check
+    assert fused(L8, ws_bytes=16) == kq.KVQ_ERR_WORKSPACE_TOO_SMALL
+    # layouts the one-launch path does not code: 4-bit, per-channel keys
+    for L in (kq.make_layout(8, 128, 32, "int4", k_mode="group_asym", group_size=32),
+              kq.make_layout(8, 128, 16, "int4"),
+              kq.make_layout(8, 128, 16, "int8", k_mode="channel_block", v_mode="token_sym")):
+        assert kq.kvq_layout_check(L) == kq.KVQ_OK
+        assert fused(L) == kq.KVQ_ERR_UNSUPPORTED
+
+
 def test_append_static_rejects_bad_arguments_on_host():
     lib = kq._lib
     p = C.c_void_p(1 << 21)
