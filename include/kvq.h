@@ -25,6 +25,10 @@
  *                         stage 4 "fused dequantization attention kernel";
  *                         "Dynamic KV Cache Quantization ...", section "Recap
  *                         of KV Caching", the append-then-attend loop).
+ *   kvq_append_decode_attention
+ *                         a decode step's append of one token per sequence
+ *                         and its attention in one launch (byte codes with
+ *                         per-token scales, 16-bit rows).
  *   kvq_prefill_attention several causal queries per sequence at once
  *                         (prompt chunks, checking several new tokens).
  *   kvq_bytes_per_token   the cache-size closed form ("KV Cache Optimization"
