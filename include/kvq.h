@@ -341,8 +341,10 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache
  * kvq_blocks_reserve handed out for it, with kvq_append's arithmetic (same
  * bytes); the decode then attends over all context_lens[b] tokens, the new
  * one included. The other arguments, the result and the workspace are those
- * of kvq_decode_attention. A sequence with no tokens takes no row; a table
- * entry outside the pool receives nothing (the decode reads block 0 there).
+ * of kvq_decode_attention. A sequence with no tokens takes no row, nor does
+ * one whose length exceeds max_context_len (a broken precondition: the row
+ * would land on a cached token); a table entry outside the pool receives
+ * nothing (the decode reads block 0 there).
  * Supported: both sides INT8 or E4M3 under TOKEN_SYM, and both NONE16; other
  * layouts return KVQ_ERR_UNSUPPORTED (use kvq_append, then decode).
  * Errors: those of kvq_decode_attention, and KVQ_ERR_INVALID_ARGUMENT for a

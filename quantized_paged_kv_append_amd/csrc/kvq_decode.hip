@@ -744,6 +744,9 @@ template <int CODE, int D, int BS>
 __device__ __forceinline__ void append_new_token(const DecodeArgs& a, int b, int g, int L,
                                                  int lane) {
   constexpr int NV = D / 32;   // 16-byte pieces per lane of a row
+  // a length past max_context_len (a broken precondition) was cut to L: the
+  // row would land on a cached token, so the sequence takes none
+  if (a.context_lens[b] != L) return;
   const int pos = L - 1;
   const int32_t id = a.block_tables[(int64_t)b * a.max_blocks + pos / BS];
   const int quad = lane >> 2, k = lane & 3;

@@ -123,3 +123,31 @@ def test_fused_step_graph_replays_equal_eager():
         g.replay()
         torch.cuda.synchronize()
         _same(eager, graphed, f"graph step {s}")
+
+
+def test_fused_step_skips_a_length_past_max_context_len():
+    """A length above max_context_len (a broken precondition) is cut to it by
+    the decode; the fused call then codes no row for that sequence rather than
+    one over a cached token. Equal, bit for bit, to kvq_append with that
+    sequence's slot set to -1, then decode with the same cut."""
+    need_gpu()
+    w = _workload("int8", 128, 16, 4, "bfloat16")
+    LL = lib_layout(w)
+    fused = State(w, LL, LENS, 1, 1, 1)
+    ref = State(w, LL, LENS, 1, 1, 1)
+    long_b = int(np.argmax(LENS))
+    cut = int(LENS[long_b])          # after the reservation that sequence holds cut + 1
+    kv, q = _inputs(w, 0, 1)
+    k, v = kv[0]
+    for st in (fused, ref):
+        kq.kvq_blocks_reserve(st.stack, st.top, st.tables, st.ctx, st.new_tok, w.block_size,
+                              st.slots, st.status, st.ctx)
+    skip = ref.slots.clone()
+    skip[long_b] = -1
+    kq.kvq_append(LL, ref.caches[0], k, v, skip)
+    kq.kvq_decode_attention(LL, ref.caches[0], q[0], ref.tables, ref.ctx, cut, ref.out[0], ref.ws)
+    kq.kvq_append_decode_attention(LL, fused.caches[0], k, v, q[0], fused.tables, fused.ctx, cut,
+                                   fused.out[0], fused.ws)
+    torch.cuda.synchronize()
+    assert int(ref.status.item()) == 0
+    _same(ref, fused, "cut length")
