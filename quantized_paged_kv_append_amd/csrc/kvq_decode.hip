@@ -66,23 +66,27 @@ namespace {
 // same plan from context_lens alone, so neither a planning launch nor a host
 // synchronization is needed:
 //   n_b  = ceil(min(len_b, max_len) / BS)          blocks of sequence b
-//   S    = split_blocks, or kDecodeWaves * clamp(ceil(H sum_b n_b / 2^12),
-//          ceil(32 / BS), 32 or 64)                  blocks per split
+//   S    = split_blocks, or kDecodeWaves * clamp(ceil(H sum_b n_b / 2^lg),
+//          ceil(32 / BS), cap)                       blocks per split
+//          (lg, cap = 11, 256 for nearly equal lengths; otherwise 12, 32 for
+//          INT4, 12, 64 for per-channel keys, 11, 64 for other layouts)
 //   ns_b = ceil(n_b / S)                            splits of sequence b
 // Items (b, j), j < ns_b, are numbered sequence-major. The partial of item
 // (b, j) for query head h is row Hq off_b + h ns_b + j of the workspace, with
 // off_b = sum_{b' < b} ns_b', so one head's splits are adjacent. The host
 // bounds sum_b ns_b from batch and max_len alone (the grid and workspace
 // size). Short sequences thus get few splits and the total work is cut into
-// about 4096 wave shares whatever the length mix.
+// about 2^lg wave shares whatever the length mix.
 struct PlanArgs {
   const int32_t* lens;
   int32_t batch, max_len, bs, H, split_blocks;
   int32_t skew_cap;  // per-wave share cap for batches of unequal lengths
+  int32_t skew_lg;   // their wave target, log2
 };
 
 __device__ __forceinline__ PlanArgs plan_args(const int32_t* lens, int batch, int max_len,
-                                              int bs, int H, int split_blocks, int skew_cap) {
+                                              int bs, int H, int split_blocks, int skew_cap,
+                                              int skew_lg) {
   PlanArgs p;
   p.lens = lens;
   p.batch = batch;
@@ -91,6 +95,7 @@ __device__ __forceinline__ PlanArgs plan_args(const int32_t* lens, int batch, in
   p.H = H;
   p.split_blocks = split_blocks;
   p.skew_cap = skew_cap;
+  p.skew_lg = skew_lg;
   return p;
 }
 
@@ -172,8 +177,9 @@ __device__ __forceinline__ int wave_reduce_i(int x) {
 // is cut into one round of shares (2^kDecodeUniformWavesLog2 waves: two
 // workgroups per CU, up to kDecodeMaxWaveBlocks blocks each), since equal
 // items need no balancing and fewer, longer shares pay the start-up chain
-// less often; any other batch into twice as many shorter shares (at most
-// decode_skew_cap(key mode) blocks), which the dispatcher balances.
+// less often; any other batch into 2^decode_skew_lg shares of at most
+// decode_skew_cap blocks (twice as many, shorter ones for INT4 and
+// per-channel keys), which the dispatcher balances.
 __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, const int* len0,
                                                  bool& uniform) {
   // block counts fit in int32: the host bounds batch * ceil(max_len / bs)
@@ -194,7 +200,7 @@ __device__ __forceinline__ int plan_split_blocks(const PlanArgs& p, int lane, co
   nmin = wave_reduce_i<false>(nmin);
   uniform = (int64_t)nmax * 8 <= (int64_t)nmin * 9;
   if (p.split_blocks > 0) return p.split_blocks;
-  const int lg = uniform ? kDecodeUniformWavesLog2 : kDecodeTargetWavesLog2;
+  const int lg = uniform ? kDecodeUniformWavesLog2 : p.skew_lg;
   const int cap = uniform ? kDecodeMaxWaveBlocks : p.skew_cap;
   int64_t w = (tot * p.H + (int64_t(1) << lg) - 1) >> lg;
   const int wmin = (kDecodeMinWaveTokens + p.bs - 1) / p.bs;
@@ -849,7 +855,7 @@ void decode_split_kernel(DecodeArgs a) {
   // every wave derives the same plan, so every branch below is
   // workgroup-uniform
   const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, BS, a.H, a.split_blocks,
-                                decode_skew_cap(MODE));
+                                decode_skew_cap(CODE, MODE), decode_skew_lg(CODE, MODE));
   if constexpr (!ROUNDS) {
     int wg_item, g;
     workgroup_item(a.H, blockIdx.x, wg_item, g);
@@ -888,7 +894,8 @@ struct ReduceArgs {
   int32_t batch;
   int32_t max_len;
   int32_t split_blocks;
-  int32_t skew_cap;  // the split kernel's plan: decode_skew_cap of the key mode
+  int32_t skew_cap;  // the split kernel's plan: decode_skew_cap / _lg of the layout
+  int32_t skew_lg;
 };
 
 
@@ -906,7 +913,7 @@ __global__ __launch_bounds__(64 * kReduceHeads) void decode_reduce_kernel(Reduce
   const int h = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, b = blockIdx.y;
   if (h >= a.Hq) return;
   const PlanArgs pa = plan_args(a.context_lens, a.batch, a.max_len, a.BS, a.H, a.split_blocks,
-                                a.skew_cap);
+                                a.skew_cap, a.skew_lg);
   int off, ns;
   plan_sequence(pa, b, lane, off, ns);
   const int64_t base = (int64_t)a.Hq * off + (int64_t)h * ns;
@@ -1083,7 +1090,8 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t stream) {
   ra.batch = p.batch;
   ra.max_len = p.max_context_len;
   ra.split_blocks = p.split_blocks;
-  ra.skew_cap = decode_skew_cap(p.k_mode);
+  ra.skew_cap = decode_skew_cap(p.k_code, p.k_mode);
+  ra.skew_lg = decode_skew_lg(p.k_code, p.k_mode);
   const int hpg = reduce_heads_per_group((int64_t)p.num_q_heads * p.batch);
   dim3 grid((p.num_q_heads + hpg - 1) / hpg, p.batch);
   if (p.head_dim == 128)

@@ -95,11 +95,26 @@ constexpr int kDecodeMinWaveTokens = 32;
 // per-channel keys, whose items cost more to start (each block folds its
 // scales into the query); the host bound takes the smaller, which yields
 // more items.
+// Byte codes and 16-bit rows with per-token scales take longer shares, 64
+// blocks, over half as many waves (2^11): their blocks cost less to convert
+// than INT4 tiles, and a wave's fixed start (query, id window, first loads)
+// then weighs less (the 8B layer, 64 sequences of 1-8K tokens: 118 against
+// 124-129 us per launch at 128-block splits); INT4, whose loop is bound by
+// its instruction latency, measured slower with longer shares.
 constexpr int kDecodeSkewWaveBlocks = 32;
+constexpr int kDecodeSkewWaveBlocksBytes = 64;
 constexpr int kDecodeSkewWaveBlocksChannel = 64;
-__host__ __device__ constexpr int decode_skew_cap(int32_t k_mode) {
+constexpr int kDecodeSkewWavesLog2Bytes = 11;
+__host__ __device__ constexpr int decode_skew_cap(int32_t k_code, int32_t k_mode) {
   return k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM ? kDecodeSkewWaveBlocksChannel
-                                               : kDecodeSkewWaveBlocks;
+         : k_code == KVQ_CODE_INT4             ? kDecodeSkewWaveBlocks
+                                               : kDecodeSkewWaveBlocksBytes;
+}
+// the wave target (log2) of a batch of unequal lengths
+__host__ __device__ constexpr int decode_skew_lg(int32_t k_code, int32_t k_mode) {
+  return k_mode == KVQ_SCALE_CHANNEL_BLOCK_SYM || k_code == KVQ_CODE_INT4
+             ? kDecodeTargetWavesLog2
+             : kDecodeSkewWavesLog2Bytes;
 }
 
 // Largest decode split grid: sixteen workgroups of kDecodeWaves waves per
